@@ -1,0 +1,302 @@
+"""Pins of the CPU oracle to facts fixed outside itself (CPU only).
+
+Every pin here comes from a hand-worked golden value, a closed form, an
+invariant of the method, or a library routine (numpy / scipy) for a special
+case — never from the oracle's own arithmetic retyped.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+from scipy.special import logsumexp, softmax
+
+import oracle
+import synth
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def golden_e2m1():
+    table = {}
+    with open(os.path.join(GOLD, "e2m1_codes.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            c, v = line.split()
+            table[int(c)] = float(v)
+    return table
+
+
+E2M1 = golden_e2m1()
+
+
+def pack_hex(s):
+    """one hex e2m1 code per element, element 0 first -> packed bytes (even element low)"""
+    codes = [int(ch, 16) for ch in s]
+    return np.array([codes[2 * i] | (codes[2 * i + 1] << 4) for i in range(len(codes) // 2)], np.uint8)
+
+
+def decode_vec(packed, scales):
+    """MXFP4 vector -> float64 values via the golden code table (test-side decoding)."""
+    codes = np.empty(2 * packed.shape[-1], np.int64)
+    codes[0::2] = packed & 15
+    codes[1::2] = packed >> 4
+    vals = np.array([E2M1[int(c)] for c in codes])
+    sc = np.repeat(np.array([2.0 ** (int(e) - 127) for e in scales]), 32)
+    return vals * sc
+
+
+# ----------------------------------------------------------------------------
+# codec
+# ----------------------------------------------------------------------------
+def test_e2m1_matches_golden_table():
+    for code, val in E2M1.items():
+        got = oracle.e2m1_value(code)
+        assert got == val and math.copysign(1, got) == math.copysign(1, val), code
+
+
+def fp8_e4m3_values():
+    """All finite FP8 E4M3 (OCP 8-bit float) values, from the format definition."""
+    vals = set()
+    for b in range(256):
+        s, e, m = b >> 7, (b >> 3) & 15, b & 7
+        if e == 15 and m == 7:
+            continue  # NaN
+        mag = (m / 8.0) * 2.0 ** (1 - 7) if e == 0 else (1 + m / 8.0) * 2.0 ** (e - 7)
+        vals.add(-mag if s else mag)
+    return vals
+
+
+def test_fp4_to_fp8_dequant_is_lossless():
+    """The pages state FP4->FP8 dequantisation is lossless: every e2m1 value is an E4M3 value."""
+    e4m3 = fp8_e4m3_values()
+    for code in range(16):
+        assert oracle.e2m1_value(code) in e4m3
+
+
+def test_e8m0():
+    for e in (0, 1, 120, 125, 127, 129, 200, 254):
+        assert oracle.e8m0_value(e) == 2.0 ** (e - 127)
+    assert math.isnan(oracle.e8m0_value(255))
+
+
+# ----------------------------------------------------------------------------
+# pooling (compression)
+# ----------------------------------------------------------------------------
+def test_pool_golden_hand_cases():
+    cases = json.load(open(os.path.join(GOLD, "pool_hand.json")))["cases"]
+    for c in cases:
+        x = np.array(c["x"], np.float32).reshape(-1, 1)
+        z = np.array(c["z"], np.float32).reshape(-1, 1)
+        out = oracle.pool(x, z, c["m"])
+        assert out.shape == (1, 1)
+        assert abs(out[0, 0] - c["expected"]) < 1e-6, c["derivation"]
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_pool_m1_is_identity(dt):
+    x = synth.normal(1, 1, 64 * 16, dt).reshape(64, 16)
+    z = synth.normal(1, 2, 64 * 16, dt).reshape(64, 16)
+    out = oracle.pool(x, z, 1)
+    xf = x if dt == "f32" else synth.bf16_bits_to_f32(x)
+    assert np.array_equal(out, xf.astype(np.float64))
+
+
+def test_pool_equal_logits_is_mean_and_onehot_is_token():
+    rng = np.random.default_rng(0)
+    x = rng.standard_normal((40, 8)).astype(np.float32)
+    z = np.full((40, 8), 0.25, np.float32)
+    out = oracle.pool(x, z, 4)
+    assert np.allclose(out, x.astype(np.float64).reshape(10, 4, 8).mean(1), rtol=0, atol=1e-12)
+    # one logit 0, the rest -1e4: exp underflows to exactly 0, so the token itself comes out
+    pick = rng.integers(0, 4, size=(10, 8))
+    zz = np.full((40, 8), -1.0e4, np.float32)
+    for j in range(10):
+        for c in range(8):
+            zz[4 * j + pick[j, c], c] = 0.0
+    out = oracle.pool(x, zz, 4)
+    want = np.take_along_axis(x.reshape(10, 4, 8), pick[:, None, :], axis=1)[:, 0, :]
+    assert np.array_equal(out, want.astype(np.float64))
+
+
+def test_pool_shift_invariance_hull_and_locality():
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal((96, 6)).astype(np.float32)
+    z = (rng.integers(-16, 16, size=(96, 6)) / 8.0).astype(np.float32)  # dyadic: z+1 is exact
+    a = oracle.pool(x, z, 8)
+    b = oracle.pool(x, z + np.float32(1.0), 8)
+    assert np.allclose(a, b, rtol=1e-13, atol=1e-14)
+    xb = x.astype(np.float64).reshape(12, 8, 6)
+    assert np.all(a >= xb.min(1) - 1e-12) and np.all(a <= xb.max(1) + 1e-12)
+    # block locality: changing rows of block 5 only changes pooled row 5
+    x2 = x.copy()
+    x2[40:48] += 1.0
+    c = oracle.pool(x2, z, 8)
+    diff = np.any(c != a, axis=1)
+    assert diff[5] and diff.sum() == 1
+    # channel locality: changing logits of channel 2 only changes channel 2
+    z2 = z.copy()
+    z2[:, 2] = -z2[:, 2]
+    e = oracle.pool(x, z2, 8)
+    assert np.array_equal(np.delete(e, 2, axis=1), np.delete(a, 2, axis=1))
+    # tail rows that do not fill a block are not pooled
+    assert oracle.pool(x[:95], z[:95], 8).shape == (11, 6)
+
+
+def test_pool_matches_scipy_softmax():
+    rng = np.random.default_rng(2)
+    x = rng.standard_normal((12, 5)).astype(np.float32)
+    z = rng.standard_normal((12, 5)).astype(np.float32)
+    out = oracle.pool(x, z, 3)
+    xb = x.astype(np.float64).reshape(4, 3, 5)
+    wb = softmax(z.astype(np.float64).reshape(4, 3, 5), axis=1)
+    assert np.allclose(out, (wb * xb).sum(1), rtol=0, atol=1e-13)
+
+
+# ----------------------------------------------------------------------------
+# indexer score
+# ----------------------------------------------------------------------------
+def _case_arrays(c):
+    qc = np.stack([pack_hex(s) for s in c["q"]])
+    qs = np.array(c["qs"], np.uint8)
+    w = np.array(c["w"], np.float32)
+    kc = pack_hex(c["k"])[None, :]
+    ks = np.array(c["ks"], np.uint8)[None, :]
+    return qc, qs, w, kc, ks
+
+
+def test_index_golden_hand_cases():
+    cases = json.load(open(os.path.join(GOLD, "index_hand.json")))["cases"]
+    for c in cases:
+        S, ex = oracle.index_scores(*_case_arrays(c))
+        assert S[0] == c["expected"], c["derivation"]
+        assert ex[0]
+
+
+def _random_index(seed, n, codeset=synth.E2M1_ALL_CODES):
+    qc = synth.codes4(seed, synth.S_QCODE, 4 * 32, codeset).reshape(4, 32)
+    qs = synth.exp_bytes(seed, synth.S_QSCALE, 8, -2, 2).reshape(4, 2)
+    w = synth.pow2(seed, synth.S_W, 4, -1, 1)
+    kc = synth.codes4(seed, synth.S_KCODE, n * 32, codeset).reshape(n, 32)
+    ks = synth.exp_bytes(seed, synth.S_KSCALE, n * 2, -2, 2).reshape(n, 2)
+    return qc, qs, w, kc, ks
+
+
+def test_index_relu_identities_against_matmul():
+    """S(k) - S(-k) = sum_h w_h D_h and S(k) + S(-k) = sum_h w_h |D_h|, where
+    D = Q K^T is taken from a numpy matmul of test-decoded values."""
+    qc, qs, w, kc, ks = _random_index(3, 500)
+    S_pos, _ = oracle.index_scores(qc, qs, w, kc, ks)
+    S_neg, _ = oracle.index_scores(qc, qs, w, kc ^ np.uint8(0x88), ks)  # flip both sign bits
+    Q = np.stack([decode_vec(qc[h], qs[h]) for h in range(4)])
+    K = np.stack([decode_vec(kc[j], ks[j]) for j in range(kc.shape[0])])
+    D = K @ Q.T  # [n][4]
+    assert np.array_equal(S_pos - S_neg, D @ w.astype(np.float64))
+    assert np.array_equal(S_pos + S_neg, np.abs(D) @ w.astype(np.float64))
+    assert np.array_equal(S_pos, np.maximum(D, 0) @ w.astype(np.float64))
+
+
+def test_index_scale_doubling_and_head_weights():
+    qc, qs, w, kc, ks = _random_index(4, 200)
+    S, _ = oracle.index_scores(qc, qs, w, kc, ks)
+    # doubling every key scale doubles every head dot and hence S (ReLU is positively homogeneous)
+    S2, _ = oracle.index_scores(qc, qs, w, kc, ks + np.uint8(1))
+    assert np.array_equal(S2, 2 * S)
+    # doubling one head weight adds exactly that head's term again
+    w2 = w.copy()
+    w2[1] *= 2
+    S3, _ = oracle.index_scores(qc, qs, w2, kc, ks)
+    Q = decode_vec(qc[1], qs[1])
+    K = np.stack([decode_vec(kc[j], ks[j]) for j in range(kc.shape[0])])
+    assert np.array_equal(S3 - S, w[1] * np.maximum(K @ Q, 0))
+
+
+@pytest.mark.parametrize("codeset", [synth.E2M1_ALL_CODES, synth.E2M1_TIE_CODES])
+def test_index_fp32_exactness_precondition_holds_for_workload_distributions(codeset):
+    qc, qs, w, kc, ks = _random_index(5, 20000, codeset)
+    S, ex = oracle.index_scores(qc, qs, w, kc, ks)
+    assert ex.all()
+    assert S.max() < 2.0 ** 17 and np.all(S * 128 == np.round(S * 128))
+
+
+def test_index_exactness_flag_detects_wide_scale_spread():
+    qc = np.full((4, 32), 0x77, np.uint8)  # all 6.0
+    qs = np.array([[127 + 12, 127 - 12]] * 4, np.uint8)  # exact in fp64, not in fp32
+    w = np.ones(4, np.float32)
+    kc = np.full((1, 32), 0x77, np.uint8)
+    ks = np.array([[127, 127]], np.uint8)
+    S, ex = oracle.index_scores(qc, qs, w, kc, ks)
+    assert not ex[0]
+    assert S[0] == 4 * 32 * 36.0 * (2.0 ** 12 + 2.0 ** -12)
+
+
+# ----------------------------------------------------------------------------
+# top-k
+# ----------------------------------------------------------------------------
+def test_topk_matches_full_sort_exhaustively_on_tiny_inputs():
+    rng = np.random.default_rng(6)
+    for n in range(0, 11):
+        for trial in range(20):
+            S = rng.integers(0, 4, size=n).astype(np.float64) / 2.0  # many ties
+            for k in range(1, n + 3):
+                idx = oracle.topk(S, k)
+                order = sorted(range(n), key=lambda j: (-S[j], j))
+                want = sorted(order[:min(k, n)]) + [-1] * (k - min(k, n))
+                assert list(idx) == want, (S, k)
+
+
+def test_topk_properties_at_size():
+    rng = np.random.default_rng(7)
+    S = rng.integers(0, 50, size=20000).astype(np.float64)
+    k = 777
+    idx = oracle.topk(S, k)
+    assert np.all(np.diff(idx) > 0) and len(idx) == k
+    sel = np.zeros(S.shape[0], bool)
+    sel[idx] = True
+    # every selected entry beats every unselected one under (S desc, j asc)
+    worst_sel = min((S[j], -j) for j in idx)
+    best_rest = max((S[j], -j) for j in np.nonzero(~sel)[0])
+    assert worst_sel > best_rest
+
+
+# ----------------------------------------------------------------------------
+# attention with one softmax
+# ----------------------------------------------------------------------------
+def _scipy_attend(q, keys, vals, scale, bias=None):
+    lg = scale * (q @ keys.T)
+    if bias is not None:
+        lg = lg + bias[None, :]
+    p = softmax(lg, axis=1)
+    return p @ vals, logsumexp(lg, axis=1)
+
+
+def test_attend_matches_scipy_and_closed_forms():
+    rng = np.random.default_rng(8)
+    q, keys, vals = rng.standard_normal((8, 128)), rng.standard_normal((300, 128)), rng.standard_normal((300, 128))
+    s = 1 / math.sqrt(128)
+    out, lse = oracle.attend(q, keys, vals, s)
+    o2, l2 = _scipy_attend(q, keys, vals, s)
+    assert np.allclose(out, o2, atol=1e-12) and np.allclose(lse, l2, atol=1e-12)
+    # q = 0: uniform weights, the mean of the values, lse = log n
+    out, lse = oracle.attend(np.zeros((2, 128)), keys, vals, s)
+    assert np.allclose(out, vals.mean(0)[None], atol=1e-13) and np.allclose(lse, math.log(300), atol=1e-13)
+    # one key: its value, lse = its logit
+    out, lse = oracle.attend(q, keys[:1], vals[:1], s)
+    assert np.allclose(out, np.repeat(vals[:1], 8, 0), atol=1e-14)
+    assert np.allclose(lse, s * q @ keys[0], atol=1e-12)
+    # empty list: zero output, lse = -inf
+    out, lse = oracle.attend(q, keys[:0], vals[:0], s)
+    assert np.all(out == 0) and np.all(np.isneginf(lse))
+    # key order does not matter; a split merged by log-sum-exp equals the whole
+    perm = rng.permutation(300)
+    o3, l3 = oracle.attend(q, keys[perm], vals[perm], s)
+    o1, l1 = oracle.attend(q, keys, vals, s)
+    assert np.allclose(o3, o1, atol=1e-13) and np.allclose(l3, l1, atol=1e-13)
+    oa, la = oracle.attend(q, keys[:120], vals[:120], s)
+    ob, lb = oracle.attend(q, keys[120:], vals[120:], s)
+    L = np.logaddexp(la, lb)
+    merged = np.exp(la - L)[:, None] * oa + np.exp(lb - L)[:, None] * ob
+    assert np.allclose(merged, o1, atol=1e-13) and np.allclose(L, l1, atol=1e-13)
