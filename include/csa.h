@@ -1,0 +1,189 @@
+/*
+ * csa.h — C ABI of libcsa.so: compressed sparse attention (CSA) and heavily
+ * compressed attention (HCA) on AMD Instinct MI355X (gfx950).
+ *
+ * The method (pages on DeepSeek-V4):
+ *  - discuss.pytorch.kr, "DeepSeek-V4 series" summary, CSA/HCA section: CSA
+ *    compresses every m consecutive KV entries into one, lets each query
+ *    attend only to its top-k compressed entries (DeepSeek Sparse Attention
+ *    on the compressed sequence) and adds a sliding-window branch of recent
+ *    tokens; HCA compresses m' >> m entries into one and attends densely to
+ *    all of them, with no sparse selection.
+ *  - same page, FP4 QAT section: the indexer's QK path is MXFP4.
+ *  - sigco.tistory.com, "DeepSeek-V4 paper reading", CSA/HCA section: block
+ *    compression, an indexer that finds the blocks relevant to the current
+ *    token, attention over the top candidates, a sliding window of recent
+ *    tokens; HCA attends to every compressed entry.  KV-cache section: the
+ *    cache is split into compressed entries, the window, and the tail of
+ *    tokens not yet numerous enough to form a block.
+ *  - jyp-garden EP 95 notes, IDEAS: multi-query attention (one shared KV head).
+ *
+ * Conventions for every entry point
+ *  - Pointers are DEVICE pointers unless a comment says "host".  The caller
+ *    owns all memory, including workspaces; the library allocates and frees
+ *    nothing and keeps no pointer after a call returns.
+ *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
+ *    default stream).  The library never synchronises.  Calls on different
+ *    streams may run concurrently if they do not share a workspace.
+ *  - Return value: CSA_OK (0) or a negative csa_status.  Arguments are
+ *    validated on the host before anything is enqueued; a rejected call
+ *    enqueues nothing.  csa_last_error() returns a thread-local message for
+ *    the last failed call on the calling thread.
+ *  - Device data (offsets, positions, codes) is trusted: out-of-range values
+ *    there are undefined behaviour, not reported errors.
+ *  - Layouts: raw KV rows [sum L][2][d] (K half first, V half at element d);
+ *    pooled rows [sum P][2][d] in the same layout; queries [n_q][H][d];
+ *    outputs [n_q][H][d] in the KV dtype; lse [n_q][H] fp32.
+ *  - Supported shapes: d = 128; H <= 128 (bf16 needs H % 16 == 0); indexer
+ *    4 heads x 64 dims.  Everything else returns CSA_ERR_UNSUPPORTED.
+ */
+#ifndef CSA_H
+#define CSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  CSA_OK = 0,
+  CSA_ERR_INVALID = -1,     /* null pointer, negative size, inconsistent arguments */
+  CSA_ERR_UNSUPPORTED = -2, /* valid but not implemented (dtype, d, H, indexer shape) */
+  CSA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than the queried size   */
+  CSA_ERR_DEVICE = -4       /* no usable gfx950 device, or a HIP launch failed       */
+} csa_status;
+
+typedef enum { CSA_F32 = 0, CSA_BF16 = 1 } csa_dtype;
+
+/* A batch of sequences and the query rows that belong to them.
+ * Sequence b owns raw rows [tok_off[b], tok_off[b+1]) (length L_b) and query
+ * rows [q_off[b], q_off[b+1]); query i sits at position q_pos[i] inside its
+ * sequence, 0 <= q_pos[i] < L_b.  The host scalars bound the device arrays
+ * and size the launch grids; they must be >= the true values. */
+typedef struct {
+  int32_t n_seq;            /* host: number of sequences B >= 1                  */
+  int64_t n_q;              /* host: total query rows (= q_off[B])               */
+  int64_t max_len;          /* host: max_b L_b                                   */
+  int64_t max_q_per_seq;    /* host: max_b (q_off[b+1] - q_off[b])               */
+  const int64_t* tok_off;   /* device [B+1]                                      */
+  const int64_t* q_off;     /* device [B+1]                                      */
+  const int64_t* q_pos;     /* device [n_q]                                      */
+} csa_batch;
+
+/* Status code -> static string (host; never fails). */
+const char* csa_status_string(int status);
+
+/* Thread-local description of the last failed call on this thread (host). */
+const char* csa_last_error(void);
+
+/* ------------------------------------------------------------------------
+ * csa_compress — pooling of m consecutive raw rows into one row.
+ * Pages: pytorch.kr CSA/HCA section (m consecutive KV entries become one;
+ * m' >> m for HCA); sigco CSA/HCA section (blockwise compression).  Rule
+ * (the reading taken; the pages give none): for block j of sequence b and
+ * channel c, out[j][c] = sum_i softmax_i(z[jm+i][c]) * x[jm+i][c], i < m,
+ * computed in fp32 and rounded once to the KV dtype.
+ *
+ * Sequence b's rows [tok_off[b], tok_off[b+1]) are pooled in whole blocks of
+ * m starting at tok_off[b] (the start must sit on a block boundary of the
+ * sequence's absolute positions when appending a chunk); trailing rows that
+ * do not fill a block are not pooled (they stay visible through the window).
+ * Block j of sequence b is written to row pool_off[b] + j of `out`, for
+ * j < min(floor(L_b/m), pool_off[b+1] - pool_off[b]).
+ *   x, z      [sum L][width] in `dtype`  (width = 2d: the K and V channels
+ *             each with their own logits)
+ *   out       [sum P][width] in `dtype`
+ * Errors: CSA_ERR_INVALID for null pointers, m < 1, width < 1 or not a
+ * multiple of 8; CSA_ERR_UNSUPPORTED for other dtypes.
+ * ---------------------------------------------------------------------- */
+int csa_compress(int dtype, int32_t n_seq, const int64_t* tok_off, const int64_t* pool_off,
+                 int64_t max_len, int m, int width, const void* x, const void* z, void* out,
+                 void* stream);
+
+/* ------------------------------------------------------------------------
+ * csa_index_topk — lightning-indexer scores and per-query top-k.
+ * Pages: jyp-garden IDEAS (KV compressed to 1/4, the Lightning Indexer keeps
+ * only the top-k); sigco CSA/HCA section (the indexer finds relevant blocks,
+ * only the top candidates are used); pytorch.kr FP4 QAT section (MXFP4 on the
+ * indexer QK path).  Score of pooled entry j for query i (reading taken):
+ *     S = sum_h w[i][h] * max(0, sum_c qhat[i][h][c] * khat[j][c])
+ * with MXFP4 operands: e2m1 codes packed two per byte (even element in the
+ * low nibble) and one E8M0 scale byte per 32 elements.  Visible entries of a
+ * query at position t are j < min(floor((t+1)/m), P_b) (a block is visible
+ * once it ends at or before t).  The k entries first under (S descending,
+ * j ascending) are written to idx[i][0..k_eff) in ascending j, k_eff =
+ * min(k, visible), and idx[i][k_eff..k) = -1.  Indices are relative to the
+ * sequence's first pooled row pool_off[b].
+ *   q_codes  [n_q][n_heads][dim/2]   q_scales [n_q][n_heads][dim/32]
+ *   w        [n_q][n_heads] fp32, each an exact power of two
+ *   k_codes  [sum P][dim/2]          k_scales [sum P][dim/32]
+ *   idx      [n_q][k] int32 (output)
+ *   ws       workspace of >= csa_index_topk_workspace() bytes, ZERO-FILLED
+ *            before its first use; every successful call leaves it zero-filled
+ *            again (a failed launch may not: re-zero it then).
+ * Exactness: scores are formed in fp32 and compared as bit patterns.  They
+ * are exact, and the selection therefore matches exact arithmetic bit for
+ * bit, when every per-head dot and the head sum are representable, e.g. all
+ * partial sums stay below 2^24 units of their smallest block product, which
+ * holds for scale exponents within a few powers of two of each other.
+ * Errors: CSA_ERR_UNSUPPORTED unless n_heads = 4 and dim = 64;
+ * CSA_ERR_INVALID for null pointers, k < 1 or k > 4096, m < 1;
+ * CSA_ERR_WORKSPACE when ws_bytes is too small.
+ * ---------------------------------------------------------------------- */
+int csa_index_topk_workspace(const csa_batch* b, int64_t max_pool, int k, size_t* bytes);
+int csa_index_topk(const csa_batch* b, const int64_t* pool_off, int64_t max_pool, int m,
+                   int n_heads, int dim, int k, const uint8_t* q_codes, const uint8_t* q_scales,
+                   const float* w, const uint8_t* k_codes, const uint8_t* k_scales, int32_t* idx,
+                   void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * csa_sparse_attn — MQA attention over the selected pooled rows plus the
+ * sliding window, with ONE softmax.
+ * Pages: pytorch.kr CSA/HCA section (attend to the top-k compressed entries;
+ * a sliding-window branch keeps local detail); sigco CSA/HCA section (recent
+ * tokens kept by a sliding window); jyp-garden IDEAS (MQA).  For query i at
+ * position t in sequence b and head h the key list is
+ *     [pooled row pool_off[b] + idx[i][s] for s < k_eff]  ++
+ *     [raw row tok_off[b] + u for u = max(0, t-W+1) .. t]
+ * (concatenated, no de-duplication; entries with idx < 0 are padding and
+ * must come after the valid ones), and
+ *     out[i][h] = sum_n softmax_n(scale * q[i][h] . key_n) * value_n,
+ *     lse[i][h] = log sum_n exp(scale * q[i][h] . key_n).
+ * An empty list gives out = 0 and lse = -inf.
+ *   q [n_q][H][d], kv_pool [sum P][2][d], kv_raw [sum L][2][d], idx [n_q][k],
+ *   out [n_q][H][d] (KV dtype), lse [n_q][H] fp32 or NULL,
+ *   ws  >= csa_sparse_attn_workspace() bytes (no zero-fill needed).
+ * Errors: CSA_ERR_INVALID for null pointers, W < 0, k < 0; CSA_ERR_UNSUPPORTED
+ * for d != 128, H > 128, bf16 with H % 16 != 0; CSA_ERR_WORKSPACE.
+ * ---------------------------------------------------------------------- */
+int csa_sparse_attn_workspace(int dtype, const csa_batch* b, int H, int d, int W, int k,
+                              size_t* bytes);
+int csa_sparse_attn(int dtype, const csa_batch* b, const int64_t* pool_off, int H, int d,
+                    float scale, int W, int k, const void* q, const void* kv_pool,
+                    const void* kv_raw, const int32_t* idx, void* out, float* lse, void* ws,
+                    size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * hca_attn — dense MQA attention over every visible m'-pooled row.
+ * Pages: pytorch.kr CSA/HCA section (m' >> m, dense attention without
+ * sparse selection); sigco CSA/HCA section (attention over all compressed
+ * entries).  For query i at position t the key list is the pooled rows
+ * j < min(floor((t+1)/m_hca), P'_b) followed, when W_hca > 0, by the raw
+ * rows of the last W_hca tokens up to t (W_hca = 0: no window, the reading
+ * taken for pure HCA).  Same softmax, outputs and empty-list rule as
+ * csa_sparse_attn.
+ *   kv_pool_hca [sum P'][2][d]; kv_raw may be NULL iff W_hca == 0.
+ * ---------------------------------------------------------------------- */
+int hca_attn_workspace(int dtype, const csa_batch* b, int64_t max_hpool, int H, int d, int W_hca,
+                       size_t* bytes);
+int hca_attn(int dtype, const csa_batch* b, const int64_t* hpool_off, int64_t max_hpool,
+             int m_hca, int H, int d, float scale, int W_hca, const void* q,
+             const void* kv_pool_hca, const void* kv_raw, void* out, float* lse, void* ws,
+             size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CSA_H */

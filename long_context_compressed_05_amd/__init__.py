@@ -1,0 +1,237 @@
+"""Python binding of libcsa.so — compressed sparse attention (CSA) and heavily
+compressed attention (HCA) on MI355X.
+
+Argument marshalling only: every step runs in the HIP kernels behind the C ABI
+(include/csa.h).  PyTorch provides device memory and the stream.  There is no
+fallback: if libcsa.so is missing or a call fails, an exception is raised.
+The function names are those of the C ABI.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libcsa.so")
+
+CSA_OK, CSA_ERR_INVALID, CSA_ERR_UNSUPPORTED, CSA_ERR_WORKSPACE, CSA_ERR_DEVICE = 0, -1, -2, -3, -4
+CSA_F32, CSA_BF16 = 0, 1
+
+EXPORTS = ("csa_status_string", "csa_last_error", "csa_compress", "csa_index_topk_workspace",
+           "csa_index_topk", "csa_sparse_attn_workspace", "csa_sparse_attn", "hca_attn_workspace",
+           "hca_attn")
+
+
+class CsaBatch(ctypes.Structure):
+    _fields_ = [("n_seq", ctypes.c_int32), ("n_q", ctypes.c_int64), ("max_len", ctypes.c_int64),
+                ("max_q_per_seq", ctypes.c_int64), ("tok_off", ctypes.c_void_p),
+                ("q_off", ctypes.c_void_p), ("q_pos", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib():
+    """Load libcsa.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"libcsa.so not found at {LIB_PATH}; build it with "
+                           "`python -m long_context_compressed_05_amd.build` (hipcc, gfx950)")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, ci, i32, i64, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    bp = ctypes.POINTER(CsaBatch)
+    L.csa_status_string.restype = ctypes.c_char_p
+    L.csa_status_string.argtypes = [ci]
+    L.csa_last_error.restype = ctypes.c_char_p
+    L.csa_last_error.argtypes = []
+    L.csa_compress.argtypes = [ci, i32, vp, vp, i64, ci, ci, vp, vp, vp, vp]
+    L.csa_index_topk_workspace.argtypes = [bp, i64, ci, ctypes.POINTER(sz)]
+    L.csa_index_topk.argtypes = [bp, vp, i64, ci, ci, ci, ci, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.csa_sparse_attn_workspace.argtypes = [ci, bp, ci, ci, ci, ci, ctypes.POINTER(sz)]
+    L.csa_sparse_attn.argtypes = [ci, bp, vp, ci, ci, ctypes.c_float, ci, ci, vp, vp, vp, vp, vp, vp,
+                                  vp, sz, vp]
+    L.hca_attn_workspace.argtypes = [ci, bp, i64, ci, ci, ci, ctypes.POINTER(sz)]
+    L.hca_attn.argtypes = [ci, bp, vp, i64, ci, ci, ci, ctypes.c_float, ci, vp, vp, vp, vp, vp, vp,
+                           sz, vp]
+    for name in EXPORTS:
+        L[name].restype = L[name].restype if name in ("csa_status_string", "csa_last_error") else ci
+    _lib = L
+    return L
+
+
+class CsaError(RuntimeError):
+    def __init__(self, rc: int, what: str):
+        L = lib()
+        super().__init__(f"{what}: {L.csa_status_string(rc).decode()} ({L.csa_last_error().decode()})")
+        self.rc = rc
+
+
+def _check(rc: int, what: str):
+    if rc != CSA_OK:
+        raise CsaError(rc, what)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libcsa must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return CSA_F32
+    if t.dtype in (torch.bfloat16, torch.int16, torch.uint16):
+        return CSA_BF16
+    raise TypeError(f"KV dtype must be float32 or bfloat16, got {t.dtype}")
+
+
+@dataclass
+class Batch:
+    """Sequences and their query rows (device offset arrays + host bounds)."""
+    tok_off: torch.Tensor   # int64 [B+1] on the device
+    q_off: torch.Tensor     # int64 [B+1]
+    q_pos: torch.Tensor     # int64 [n_q]
+    n_q: int
+    max_len: int
+    max_q_per_seq: int
+
+    @property
+    def n_seq(self) -> int:
+        return self.tok_off.numel() - 1
+
+    def c(self) -> CsaBatch:
+        return CsaBatch(self.n_seq, self.n_q, self.max_len, self.max_q_per_seq, _ptr(self.tok_off),
+                        _ptr(self.q_off), _ptr(self.q_pos))
+
+    @staticmethod
+    def from_host(tok_off, q_off, q_pos, device="cuda") -> "Batch":
+        import numpy as np
+        tok_off = np.asarray(tok_off, dtype=np.int64)
+        q_off = np.asarray(q_off, dtype=np.int64)
+        q_pos = np.asarray(q_pos, dtype=np.int64)
+        lens = np.diff(tok_off)
+        qn = np.diff(q_off)
+        return Batch(torch.from_numpy(tok_off).to(device), torch.from_numpy(q_off).to(device),
+                     torch.from_numpy(q_pos).to(device), int(q_off[-1]),
+                     int(lens.max()) if lens.size else 0, int(qn.max()) if qn.size else 0)
+
+
+class Workspace:
+    """Reusable zero-initialised device workspace (the index workspace must be
+    zero-filled before first use; the library leaves it zero-filled)."""
+
+    def __init__(self, device="cuda"):
+        self.device = device
+        self.buf: Optional[torch.Tensor] = None
+
+    def get(self, nbytes: int) -> Optional[torch.Tensor]:
+        if nbytes == 0:
+            return None
+        if self.buf is None or self.buf.numel() < nbytes:
+            self.buf = torch.zeros(nbytes, dtype=torch.uint8, device=self.device)
+        return self.buf
+
+
+def csa_compress(x: torch.Tensor, z: torch.Tensor, tok_off: torch.Tensor, pool_off: torch.Tensor,
+                 max_len: int, m: int, out: torch.Tensor, stream=None) -> torch.Tensor:
+    """Pool whole blocks of m rows: x, z [rows][...] -> out [pooled rows][...] (same dtype)."""
+    width = x[0].numel() if x.shape[0] > 0 else out[0].numel()
+    _check(lib().csa_compress(_dtype_code(x), tok_off.numel() - 1, _ptr(tok_off), _ptr(pool_off),
+                              max_len, m, width, _ptr(x), _ptr(z), _ptr(out), _stream(stream)),
+           "csa_compress")
+    return out
+
+
+def csa_index_topk_workspace(batch: Batch, max_pool: int, k: int) -> int:
+    n = ctypes.c_size_t(0)
+    b = batch.c()
+    _check(lib().csa_index_topk_workspace(ctypes.byref(b), max_pool, k, ctypes.byref(n)),
+           "csa_index_topk_workspace")
+    return n.value
+
+
+def csa_index_topk(batch: Batch, pool_off: torch.Tensor, max_pool: int, m: int, k: int,
+                   q_codes: torch.Tensor, q_scales: torch.Tensor, w: torch.Tensor,
+                   k_codes: torch.Tensor, k_scales: torch.Tensor, idx: Optional[torch.Tensor] = None,
+                   ws: Optional[Workspace] = None, stream=None) -> torch.Tensor:
+    if idx is None:
+        idx = torch.empty((batch.n_q, k), dtype=torch.int32, device=q_codes.device)
+    ws = ws or Workspace(q_codes.device)
+    nbytes = csa_index_topk_workspace(batch, max_pool, k)
+    buf = ws.get(nbytes)
+    b = batch.c()
+    n_heads, dim = q_codes.shape[-2], 2 * q_codes.shape[-1]
+    _check(lib().csa_index_topk(ctypes.byref(b), _ptr(pool_off), max_pool, m, n_heads, dim, k,
+                                _ptr(q_codes), _ptr(q_scales), _ptr(w), _ptr(k_codes), _ptr(k_scales),
+                                _ptr(idx), _ptr(buf), nbytes, _stream(stream)), "csa_index_topk")
+    return idx
+
+
+def csa_sparse_attn_workspace(dtype_code: int, batch: Batch, H: int, d: int, W: int, k: int) -> int:
+    n = ctypes.c_size_t(0)
+    b = batch.c()
+    _check(lib().csa_sparse_attn_workspace(dtype_code, ctypes.byref(b), H, d, W, k, ctypes.byref(n)),
+           "csa_sparse_attn_workspace")
+    return n.value
+
+
+def csa_sparse_attn(batch: Batch, pool_off: torch.Tensor, q: torch.Tensor, kv_pool: torch.Tensor,
+                    kv_raw: torch.Tensor, idx: torch.Tensor, W: int, scale: float,
+                    out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                    ws: Optional[Workspace] = None, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    dt = _dtype_code(q)
+    H, d = q.shape[-2], q.shape[-1]
+    k = idx.shape[-1]
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((batch.n_q, H), dtype=torch.float32, device=q.device)
+    ws = ws or Workspace(q.device)
+    nbytes = csa_sparse_attn_workspace(dt, batch, H, d, W, k)
+    buf = ws.get(nbytes)
+    b = batch.c()
+    _check(lib().csa_sparse_attn(dt, ctypes.byref(b), _ptr(pool_off), H, d, scale, W, k, _ptr(q),
+                                 _ptr(kv_pool), _ptr(kv_raw), _ptr(idx), _ptr(out), _ptr(lse),
+                                 _ptr(buf), nbytes, _stream(stream)), "csa_sparse_attn")
+    return out, lse
+
+
+def hca_attn_workspace(dtype_code: int, batch: Batch, max_hpool: int, H: int, d: int, W_hca: int) -> int:
+    n = ctypes.c_size_t(0)
+    b = batch.c()
+    _check(lib().hca_attn_workspace(dtype_code, ctypes.byref(b), max_hpool, H, d, W_hca, ctypes.byref(n)),
+           "hca_attn_workspace")
+    return n.value
+
+
+def hca_attn(batch: Batch, hpool_off: torch.Tensor, max_hpool: int, m_hca: int, q: torch.Tensor,
+             kv_pool_hca: torch.Tensor, kv_raw: Optional[torch.Tensor], W_hca: int, scale: float,
+             out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+             ws: Optional[Workspace] = None, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    dt = _dtype_code(q)
+    H, d = q.shape[-2], q.shape[-1]
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((batch.n_q, H), dtype=torch.float32, device=q.device)
+    ws = ws or Workspace(q.device)
+    nbytes = hca_attn_workspace(dt, batch, max_hpool, H, d, W_hca)
+    buf = ws.get(nbytes)
+    b = batch.c()
+    _check(lib().hca_attn(dt, ctypes.byref(b), _ptr(hpool_off), max_hpool, m_hca, H, d, scale, W_hca,
+                          _ptr(q), _ptr(kv_pool_hca), _ptr(kv_raw), _ptr(out), _ptr(lse), _ptr(buf),
+                          nbytes, _stream(stream)), "hca_attn")
+    return out, lse

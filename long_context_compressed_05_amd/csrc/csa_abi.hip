@@ -1,0 +1,223 @@
+// C ABI of libcsa: host-side validation, workspace sizing and launches.
+// Declarations, argument meaning and error behaviour: include/csa.h.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/csa.h"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// 0 = unknown, 1 = gfx950, 2 = other / unusable
+std::atomic<int> g_dev_state[64];
+
+int check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return fail(CSA_ERR_DEVICE, "no HIP device available");
+  }
+  if (dev < 64) {
+    int s = g_dev_state[dev].load(std::memory_order_relaxed);
+    if (s == 1) return CSA_OK;
+    if (s == 2) return fail(CSA_ERR_DEVICE, "device %d is not gfx950", dev);
+  }
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(CSA_ERR_DEVICE, "hipGetDeviceProperties failed on device %d", dev);
+  }
+  const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev < 64) g_dev_state[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+  if (!ok) return fail(CSA_ERR_DEVICE, "device %d is %s, libcsa is built for gfx950", dev, prop.gcnArchName);
+  return CSA_OK;
+}
+
+int check_batch(const csa_batch* b) {
+  if (!b) return fail(CSA_ERR_INVALID, "batch descriptor is NULL");
+  if (b->n_seq < 1) return fail(CSA_ERR_INVALID, "n_seq must be >= 1 (got %d)", b->n_seq);
+  if (b->n_q < 0 || b->max_len < 0 || b->max_q_per_seq < 0)
+    return fail(CSA_ERR_INVALID, "negative batch sizes");
+  if (b->n_q > 0 && b->max_q_per_seq < 1)
+    return fail(CSA_ERR_INVALID, "max_q_per_seq must be >= 1 when n_q > 0");
+  if (b->n_q > (int64_t)b->n_seq * b->max_q_per_seq)
+    return fail(CSA_ERR_INVALID, "n_q exceeds n_seq * max_q_per_seq");
+  if (!b->tok_off || !b->q_off || (b->n_q > 0 && !b->q_pos))
+    return fail(CSA_ERR_INVALID, "batch offset arrays must not be NULL");
+  if (b->n_q > 0x7fffffffLL) return fail(CSA_ERR_UNSUPPORTED, "n_q too large");
+  return CSA_OK;
+}
+
+int launched(int rc) {
+  if (rc != 0) {
+    (void)hipGetLastError();
+    return fail(CSA_ERR_DEVICE, "kernel launch failed");
+  }
+  return CSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* csa_status_string(int status) {
+  switch (status) {
+    case CSA_OK: return "CSA_OK";
+    case CSA_ERR_INVALID: return "CSA_ERR_INVALID: invalid argument";
+    case CSA_ERR_UNSUPPORTED: return "CSA_ERR_UNSUPPORTED: unsupported shape or dtype";
+    case CSA_ERR_WORKSPACE: return "CSA_ERR_WORKSPACE: workspace missing or too small";
+    case CSA_ERR_DEVICE: return "CSA_ERR_DEVICE: no usable gfx950 device or launch failure";
+    default: return "unknown csa status";
+  }
+}
+
+const char* csa_last_error(void) { return g_err; }
+
+int csa_compress(int dtype, int32_t n_seq, const int64_t* tok_off, const int64_t* pool_off,
+                 int64_t max_len, int m, int width, const void* x, const void* z, void* out,
+                 void* stream) {
+  if (dtype != CSA_F32 && dtype != CSA_BF16) return fail(CSA_ERR_UNSUPPORTED, "dtype %d", dtype);
+  if (n_seq < 1) return fail(CSA_ERR_INVALID, "n_seq must be >= 1");
+  if (!tok_off || !pool_off || !x || !z || !out) return fail(CSA_ERR_INVALID, "NULL pointer argument");
+  if (m < 1) return fail(CSA_ERR_INVALID, "block size m must be >= 1 (got %d)", m);
+  if (width < 1 || width % 8 != 0) return fail(CSA_ERR_INVALID, "width must be a positive multiple of 8");
+  if (max_len < 0) return fail(CSA_ERR_INVALID, "max_len must be >= 0");
+  if (!aligned16(x) || !aligned16(z) || !aligned16(out))
+    return fail(CSA_ERR_INVALID, "x, z and out must be 16-byte aligned");
+  int rc = check_device();
+  if (rc) return rc;
+  return launched(csa::launch_compress(dtype == CSA_BF16, n_seq, tok_off, pool_off, max_len, m,
+                                       width, x, z, out, (hipStream_t)stream));
+}
+
+int csa_index_topk_workspace(const csa_batch* b, int64_t max_pool, int k, size_t* bytes) {
+  int rc = check_batch(b);
+  if (rc) return rc;
+  if (!bytes) return fail(CSA_ERR_INVALID, "bytes is NULL");
+  if (max_pool < 0) return fail(CSA_ERR_INVALID, "max_pool must be >= 0");
+  if (k < 1 || k > 4096) return fail(CSA_ERR_INVALID, "k must be in [1, 4096] (got %d)", k);
+  *bytes = csa::index_ws_bytes(b->n_q, max_pool, k);
+  return CSA_OK;
+}
+
+int csa_index_topk(const csa_batch* b, const int64_t* pool_off, int64_t max_pool, int m,
+                   int n_heads, int dim, int k, const uint8_t* q_codes, const uint8_t* q_scales,
+                   const float* w, const uint8_t* k_codes, const uint8_t* k_scales, int32_t* idx,
+                   void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_batch(b);
+  if (rc) return rc;
+  if (n_heads != 4 || dim != 64)
+    return fail(CSA_ERR_UNSUPPORTED, "indexer shape %d heads x %d dims (supported: 4 x 64)", n_heads, dim);
+  if (m < 1) return fail(CSA_ERR_INVALID, "block size m must be >= 1");
+  if (k < 1 || k > 4096) return fail(CSA_ERR_INVALID, "k must be in [1, 4096] (got %d)", k);
+  if (max_pool < 0 || max_pool > (1LL << 30)) return fail(CSA_ERR_INVALID, "max_pool out of range");
+  if (!pool_off || !q_codes || !q_scales || !w || !k_codes || !k_scales || !idx)
+    return fail(CSA_ERR_INVALID, "NULL pointer argument");
+  if (!aligned16(q_codes) || !aligned16(k_codes))
+    return fail(CSA_ERR_INVALID, "q_codes and k_codes must be 16-byte aligned");
+  const size_t need = csa::index_ws_bytes(b->n_q, max_pool, k);
+  if (!ws || ws_bytes < need)
+    return fail(CSA_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need, ws_bytes);
+  rc = check_device();
+  if (rc) return rc;
+  return launched(csa::launch_index_topk(b->n_seq, b->n_q, b->max_q_per_seq, b->q_off, b->q_pos,
+                                         pool_off, max_pool, m, k, q_codes, q_scales, w, k_codes,
+                                         k_scales, idx, ws, (hipStream_t)stream));
+}
+
+static int check_attn_shape(int dtype, int H, int d) {
+  if (dtype != CSA_F32 && dtype != CSA_BF16) return fail(CSA_ERR_UNSUPPORTED, "dtype %d", dtype);
+  if (d != 128) return fail(CSA_ERR_UNSUPPORTED, "head dim %d (supported: 128)", d);
+  if (H < 1 || H > 128) return fail(CSA_ERR_UNSUPPORTED, "H = %d (supported: 1..128)", H);
+  if (dtype == CSA_BF16 && H % 16 != 0) return fail(CSA_ERR_UNSUPPORTED, "bf16 needs H %% 16 == 0");
+  return CSA_OK;
+}
+
+int csa_sparse_attn_workspace(int dtype, const csa_batch* b, int H, int d, int W, int k,
+                              size_t* bytes) {
+  int rc = check_batch(b);
+  if (rc) return rc;
+  rc = check_attn_shape(dtype, H, d);
+  if (rc) return rc;
+  if (!bytes || W < 0 || k < 0) return fail(CSA_ERR_INVALID, "bytes NULL or negative W/k");
+  *bytes = csa::plan_attn(b->n_q, (int64_t)k + W, H).ws_bytes;
+  return CSA_OK;
+}
+
+int csa_sparse_attn(int dtype, const csa_batch* b, const int64_t* pool_off, int H, int d,
+                    float scale, int W, int k, const void* q, const void* kv_pool,
+                    const void* kv_raw, const int32_t* idx, void* out, float* lse, void* ws,
+                    size_t ws_bytes, void* stream) {
+  int rc = check_batch(b);
+  if (rc) return rc;
+  rc = check_attn_shape(dtype, H, d);
+  if (rc) return rc;
+  if (W < 0 || k < 0) return fail(CSA_ERR_INVALID, "W and k must be >= 0");
+  if (!pool_off || !q || !out || (k > 0 && (!kv_pool || !idx)) || (W > 0 && !kv_raw))
+    return fail(CSA_ERR_INVALID, "NULL pointer argument");
+  if (!aligned16(q) || !aligned16(kv_pool) || !aligned16(kv_raw) || !aligned16(out))
+    return fail(CSA_ERR_INVALID, "q, kv_pool, kv_raw and out must be 16-byte aligned");
+  const size_t need = csa::plan_attn(b->n_q, (int64_t)k + W, H).ws_bytes;
+  if (need > 0 && (!ws || ws_bytes < need))
+    return fail(CSA_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need, ws_bytes);
+  rc = check_device();
+  if (rc) return rc;
+  return launched(csa::launch_attn(dtype == CSA_BF16, false, b->n_seq, b->n_q, b->tok_off, b->q_off,
+                                   b->q_pos, pool_off, 1, k, W, H, scale, q, kv_pool, kv_raw, idx,
+                                   out, lse, ws, (hipStream_t)stream));
+}
+
+int hca_attn_workspace(int dtype, const csa_batch* b, int64_t max_hpool, int H, int d, int W_hca,
+                       size_t* bytes) {
+  int rc = check_batch(b);
+  if (rc) return rc;
+  rc = check_attn_shape(dtype, H, d);
+  if (rc) return rc;
+  if (!bytes || W_hca < 0 || max_hpool < 0 || max_hpool > 0x7fffffffLL)
+    return fail(CSA_ERR_INVALID, "bytes NULL or W_hca / max_hpool out of range");
+  *bytes = csa::plan_attn(b->n_q, max_hpool + W_hca, H).ws_bytes;
+  return CSA_OK;
+}
+
+int hca_attn(int dtype, const csa_batch* b, const int64_t* hpool_off, int64_t max_hpool,
+             int m_hca, int H, int d, float scale, int W_hca, const void* q,
+             const void* kv_pool_hca, const void* kv_raw, void* out, float* lse, void* ws,
+             size_t ws_bytes, void* stream) {
+  int rc = check_batch(b);
+  if (rc) return rc;
+  rc = check_attn_shape(dtype, H, d);
+  if (rc) return rc;
+  if (m_hca < 1) return fail(CSA_ERR_INVALID, "m_hca must be >= 1");
+  if (W_hca < 0 || max_hpool < 0 || max_hpool > 0x7fffffffLL)
+    return fail(CSA_ERR_INVALID, "W_hca / max_hpool out of range");
+  if (!hpool_off || !q || !out || (max_hpool > 0 && !kv_pool_hca) || (W_hca > 0 && !kv_raw))
+    return fail(CSA_ERR_INVALID, "NULL pointer argument");
+  if (!aligned16(q) || !aligned16(kv_pool_hca) || !aligned16(kv_raw) || !aligned16(out))
+    return fail(CSA_ERR_INVALID, "q, kv_pool_hca, kv_raw and out must be 16-byte aligned");
+  const size_t need = csa::plan_attn(b->n_q, max_hpool + W_hca, H).ws_bytes;
+  if (need > 0 && (!ws || ws_bytes < need))
+    return fail(CSA_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need, ws_bytes);
+  rc = check_device();
+  if (rc) return rc;
+  return launched(csa::launch_attn(dtype == CSA_BF16, true, b->n_seq, b->n_q, b->tok_off, b->q_off,
+                                   b->q_pos, hpool_off, m_hca, (int)max_hpool, W_hca, H, scale, q,
+                                   kv_pool_hca, kv_raw, nullptr, out, lse, ws, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,472 @@
+// MQA attention over a per-query key list with one softmax, used by both
+// CSA (selected pooled rows ++ sliding window of raw rows) and HCA (every
+// visible heavily-pooled row, optionally ++ a window).
+//
+// Pages: pytorch.kr DeepSeek-V4 summary, CSA/HCA section (top-k compressed
+// entries plus a sliding-window branch; HCA dense over all compressed
+// entries); sigco.tistory.com CSA/HCA section; jyp-garden IDEAS (MQA: one
+// KV head shared by all query heads).  The single softmax over the union of
+// both branches is the reading taken.
+//
+// Key list of query i (position t, sequence b), position p:
+//   p <  seg_a : CSA -> pooled row pool_off[b] + idx[i][p] (padding if < 0)
+//                HCA -> pooled row pool_off[b] + p (valid if p < n_vis)
+//   p >= seg_a : raw row tok_off[b] + t - W + 1 + (p - seg_a) (valid if >= 0)
+// Work item = (query, split of the list).  A split of more than one tile
+// runs an online softmax; with several splits per query, partial
+// (max, sum, unnormalised output) go to the workspace and k_attn_combine
+// merges them by log-sum-exp.
+//
+// bf16: one workgroup = 4 waves; a wave owns 16 query heads.  Per 64-key
+// tile, K rows are staged row-major and V transposed in LDS; S^T = K Q^T and
+// O^T += V^T P^T run on v_mfma_f32_16x16x32_bf16 with fp32 accumulation.
+// The key order inside the P^T operand is permuted so that each lane feeds
+// the MFMA with its own softmax outputs (no cross-lane shuffles).
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace csa {
+
+struct AttnArgs {
+  const int64_t* tok_off;
+  const int64_t* q_off;
+  const int64_t* q_pos;
+  const int64_t* pool_off;
+  int n_seq;
+  int hca;      // 0: CSA (segment A through idx), 1: HCA (segment A contiguous)
+  int m_pool;   // HCA block size
+  int seg_a;    // CSA: k; HCA: max pooled rows per sequence
+  int W;
+  int H;
+  float scale_log2;
+  const uint8_t* q;
+  const uint8_t* kv_pool;
+  const uint8_t* kv_raw;
+  const int32_t* idx;
+  uint8_t* out;
+  float* lse;
+  float* part_o;   // [n_q][splits][H][128]
+  float* part_ml;  // [n_q][splits][H][2]
+  int splits;
+  int ks;          // list positions per split (multiple of 64)
+};
+
+struct RowCtx {
+  int b;
+  int64_t t, n_vis_a, pool_base, tok_base;
+};
+
+__device__ __forceinline__ RowCtx row_ctx(const AttnArgs& a, int64_t row) {
+  RowCtx c;
+  c.b = seq_of_row(a.q_off, a.n_seq, row);
+  c.t = a.q_pos[row];
+  c.pool_base = a.pool_off[c.b];
+  c.tok_base = a.tok_off[c.b];
+  if (a.hca) {
+    const int64_t P = a.pool_off[c.b + 1] - c.pool_base;
+    const int64_t v = (c.t + 1) / a.m_pool;
+    c.n_vis_a = v < P ? v : P;
+  } else {
+    c.n_vis_a = a.seg_a;
+  }
+  return c;
+}
+
+// row pointer of list position p (nullptr = masked), row_bytes = bytes of one [2][d] row
+__device__ __forceinline__ const uint8_t* key_row(const AttnArgs& a, const RowCtx& c, int64_t row,
+                                                  int64_t p, size_t row_bytes) {
+  if (p < a.seg_a) {
+    if (a.hca) return p < c.n_vis_a ? a.kv_pool + (size_t)(c.pool_base + p) * row_bytes : nullptr;
+    const int32_t j = a.idx[row * a.seg_a + p];
+    return j >= 0 ? a.kv_pool + (size_t)(c.pool_base + j) * row_bytes : nullptr;
+  }
+  const int64_t u = c.t - a.W + 1 + (p - a.seg_a);
+  if (p >= (int64_t)a.seg_a + a.W || u < 0) return nullptr;
+  return a.kv_raw + (size_t)(c.tok_base + u) * row_bytes;
+}
+
+// ---------------------------------------------------------------------------
+// bf16, MFMA
+// ---------------------------------------------------------------------------
+constexpr int kKStride = 136;  // LDS row stride (elements) of the K tile
+constexpr int kVStride = 72;   // LDS row stride (elements) of the transposed V tile
+
+template <int GPW>
+__global__ __launch_bounds__(256) void k_attn_bf16(AttnArgs a) {
+  __shared__ __align__(16) uint16_t Ks[64 * kKStride];
+  __shared__ __align__(16) uint16_t Vt[128 * kVStride];
+  __shared__ const uint8_t* rowp[64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, g = lane >> 4;
+  const int64_t row = blockIdx.y;
+  const int split = blockIdx.x;
+  const RowCtx c = row_ctx(a, row);
+  const int64_t list_len = (int64_t)a.seg_a + a.W;
+  const int64_t p_begin = (int64_t)split * a.ks;
+  const int64_t p_end = p_begin + a.ks < list_len ? p_begin + a.ks : list_len;
+  const int HG = a.H >> 4;
+  constexpr size_t RB = 2 * 128 * 2;  // bytes per [2][128] bf16 row
+
+  // Q^T operand (B): column = head 16*hg + l16, K = dims 32*kstep + 8*g .. +7
+  v8bf qf[GPW][4];
+  float m_run[GPW], l_run[GPW];
+  v4f O[GPW][8];
+#pragma unroll
+  for (int gi = 0; gi < GPW; ++gi) {
+    const int hg = wave + 4 * gi;
+    m_run[gi] = -INFINITY;
+    l_run[gi] = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) O[gi][mt] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kq = 0; kq < 4; ++kq) {
+      if (hg < HG) {
+        const uint8_t* qp = a.q + ((size_t)(row * a.H + 16 * hg + l16) * 128 + 32 * kq + 8 * g) * 2;
+        qf[gi][kq] = *reinterpret_cast<const v8bf*>(qp);
+      } else {
+        qf[gi][kq] = v8bf{};
+      }
+    }
+  }
+
+  // staging assignment: 16-byte chunk ch of key pair kp in {tid/16, tid/16 + 16}
+  const int ch = tid & 15;
+  for (int64_t p0 = p_begin; p0 < p_end; p0 += 64) {
+    if (tid < 64) {
+      const int64_t p = p0 + tid;
+      rowp[tid] = p < p_end ? key_row(a, c, row, p, RB) : nullptr;
+    }
+    __syncthreads();
+    uint4 kr[2][2], vr[2][2];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int key = 2 * ((tid >> 4) + 16 * r) + e;
+        const uint8_t* rp = rowp[key];
+        if (rp) {
+          kr[r][e] = *reinterpret_cast<const uint4*>(rp + ch * 16);
+          vr[r][e] = *reinterpret_cast<const uint4*>(rp + 256 + ch * 16);
+        } else {
+          kr[r][e] = make_uint4(0, 0, 0, 0);
+          vr[r][e] = make_uint4(0, 0, 0, 0);
+        }
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int kp = (tid >> 4) + 16 * r;
+#pragma unroll
+      for (int e = 0; e < 2; ++e)
+        *reinterpret_cast<uint4*>(&Ks[(2 * kp + e) * kKStride + ch * 8]) = kr[r][e];
+      const uint32_t v0[4] = {vr[r][0].x, vr[r][0].y, vr[r][0].z, vr[r][0].w};
+      const uint32_t v1[4] = {vr[r][1].x, vr[r][1].y, vr[r][1].z, vr[r][1].w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        // dims ch*8 + 2q (low halves) and ch*8 + 2q + 1 (high halves) of keys 2kp, 2kp+1
+        const uint32_t lo = (v0[q] & 0xffffu) | (v1[q] << 16);
+        const uint32_t hi = (v0[q] >> 16) | (v1[q] & 0xffff0000u);
+        *reinterpret_cast<uint32_t*>(&Vt[(ch * 8 + 2 * q) * kVStride + 2 * kp]) = lo;
+        *reinterpret_cast<uint32_t*>(&Vt[(ch * 8 + 2 * q + 1) * kVStride + 2 * kp]) = hi;
+      }
+    }
+    __syncthreads();
+
+#pragma unroll
+    for (int gi = 0; gi < GPW; ++gi) {
+      const int hg = wave + 4 * gi;
+      if (hg >= HG) continue;
+      // S^T tile: rows = keys 16*mt + 4*g + v, column = head l16
+      float s[4][4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        v4f acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kq = 0; kq < 4; ++kq) {
+          const v8bf kf = *reinterpret_cast<const v8bf*>(&Ks[(16 * mt + l16) * kKStride + 32 * kq + 8 * g]);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[gi][kq], acc, 0, 0, 0);
+        }
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const bool valid = rowp[16 * mt + 4 * g + v] != nullptr;
+          s[mt][v] = valid ? acc[v] * a.scale_log2 : -INFINITY;
+        }
+      }
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) tmax = fmaxf(tmax, s[mt][v]);
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+      const float mnew = fmaxf(m_run[gi], tmax);
+      if (mnew == -INFINITY) continue;  // nothing valid so far (uniform per head)
+      const float alpha = fast_exp2(m_run[gi] - mnew);
+      m_run[gi] = mnew;
+      float psum = 0.f;
+      float pv[4][4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          pv[mt][v] = fast_exp2(s[mt][v] - mnew);
+          psum += pv[mt][v];
+        }
+      l_run[gi] = l_run[gi] * alpha + psum;
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt) O[gi][mt] *= alpha;
+      // O^T += V^T P^T over two 32-key steps; K slot 8g+i <-> key 32*kq + (i<4 ? 4g+i : 16+4g+i-4)
+#pragma unroll
+      for (int kq = 0; kq < 2; ++kq) {
+        v8bf pf;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          pf[i] = (__bf16)pv[2 * kq][i];
+          pf[4 + i] = (__bf16)pv[2 * kq + 1][i];
+        }
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt) {
+          const uint16_t* vrow = &Vt[(16 * mt + l16) * kVStride + 32 * kq + 4 * g];
+          const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
+          const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16);
+          uint4 u = make_uint4(lo.x, lo.y, hi.x, hi.y);
+          const v8bf vf = *reinterpret_cast<const v8bf*>(&u);
+          O[gi][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, O[gi][mt], 0, 0, 0);
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  // finish: lane (l16, g) holds head 16*hg + l16, dims 16*mt + 4*g + v
+#pragma unroll
+  for (int gi = 0; gi < GPW; ++gi) {
+    const int hg = wave + 4 * gi;
+    if (hg >= HG) continue;
+    float l = l_run[gi];
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    const int head = 16 * hg + l16;
+    if (a.splits == 1) {
+      const float inv = l > 0.f ? 1.f / l : 0.f;
+      uint8_t* op = a.out + ((size_t)(row * a.H + head) * 128) * 2;
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt) {
+        const int d0 = 16 * mt + 4 * g;
+        uint2 u;
+        u.x = f32_to_bf16(O[gi][mt][0] * inv) | (f32_to_bf16(O[gi][mt][1] * inv) << 16);
+        u.y = f32_to_bf16(O[gi][mt][2] * inv) | (f32_to_bf16(O[gi][mt][3] * inv) << 16);
+        *reinterpret_cast<uint2*>(op + d0 * 2) = u;
+      }
+      if (a.lse && g == 0)
+        a.lse[row * a.H + head] = l > 0.f ? (m_run[gi] + __log2f(l)) * kLn2 : -INFINITY;
+    } else {
+      const size_t base = ((size_t)(row * a.splits + split) * a.H + head);
+      float* op = a.part_o + base * 128;
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt)
+        *reinterpret_cast<v4f*>(op + 16 * mt + 4 * g) = O[gi][mt];
+      if (g == 0) {
+        a.part_ml[base * 2 + 0] = m_run[gi];
+        a.part_ml[base * 2 + 1] = l;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fp32, VALU (small head counts; exact fp32 FMAs)
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_attn_f32(AttnArgs a) {
+  __shared__ float Ks[64][129];
+  __shared__ float Vs[64][128];
+  __shared__ float Ps[128][65];
+  __shared__ float m_s[128], l_s[128], al_s[128];
+  __shared__ const uint8_t* rowp[64];
+  const int tid = threadIdx.x;
+  const int64_t row = blockIdx.y;
+  const int split = blockIdx.x;
+  const RowCtx c = row_ctx(a, row);
+  const int64_t list_len = (int64_t)a.seg_a + a.W;
+  const int64_t p_begin = (int64_t)split * a.ks;
+  const int64_t p_end = p_begin + a.ks < list_len ? p_begin + a.ks : list_len;
+  const int H = a.H;
+  constexpr size_t RB = 2 * 128 * 4;
+  const float* qrow = reinterpret_cast<const float*>(a.q) + (size_t)row * H * 128;
+  constexpr int MAXE = 64;  // H*128/256 outputs per thread at H = 128
+  const int n_el = (H * 128 + 255) / 256;
+  float O[MAXE];
+#pragma unroll
+  for (int e = 0; e < MAXE; ++e) O[e] = 0.f;
+  for (int h = tid; h < H; h += 256) { m_s[h] = -INFINITY; l_s[h] = 0.f; }
+
+  for (int64_t p0 = p_begin; p0 < p_end; p0 += 64) {
+    if (tid < 64) {
+      const int64_t p = p0 + tid;
+      rowp[tid] = p < p_end ? key_row(a, c, row, p, RB) : nullptr;
+    }
+    __syncthreads();
+    for (int i = tid; i < 64 * 64; i += 256) {  // 64 keys x 64 float4 (K then V)
+      const int key = i >> 6, q4 = i & 63;
+      const uint8_t* rp = rowp[key];
+      float4 v = rp ? *reinterpret_cast<const float4*>(rp + q4 * 16) : make_float4(0, 0, 0, 0);
+      if (q4 < 32) {
+        Ks[key][4 * q4 + 0] = v.x; Ks[key][4 * q4 + 1] = v.y;
+        Ks[key][4 * q4 + 2] = v.z; Ks[key][4 * q4 + 3] = v.w;
+      } else {
+        *reinterpret_cast<float4*>(&Vs[key][4 * (q4 - 32)]) = v;
+      }
+    }
+    __syncthreads();
+    for (int i = tid; i < H * 64; i += 256) {
+      const int h = i >> 6, j = i & 63;
+      float s = 0.f;
+      const float* qh = qrow + h * 128;
+      for (int d = 0; d < 128; ++d) s = fmaf(qh[d], Ks[j][d], s);
+      Ps[h][j] = rowp[j] ? s * a.scale_log2 : -INFINITY;
+    }
+    __syncthreads();
+    for (int h = tid; h < H; h += 256) {
+      float tmax = -INFINITY;
+      for (int j = 0; j < 64; ++j) tmax = fmaxf(tmax, Ps[h][j]);
+      const float mnew = fmaxf(m_s[h], tmax);
+      if (mnew == -INFINITY) { al_s[h] = 1.f; continue; }
+      const float alpha = fast_exp2(m_s[h] - mnew);
+      float sum = 0.f;
+      for (int j = 0; j < 64; ++j) {
+        const float pj = fast_exp2(Ps[h][j] - mnew);
+        Ps[h][j] = pj;
+        sum += pj;
+      }
+      m_s[h] = mnew;
+      l_s[h] = l_s[h] * alpha + sum;
+      al_s[h] = alpha;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < MAXE; ++e) {
+      const int o = tid + 256 * e;
+      if (e < n_el && o < H * 128) {
+        const int h = o >> 7, d = o & 127;
+        if (m_s[h] != -INFINITY) {
+          float acc = O[e] * al_s[h];
+          for (int j = 0; j < 64; ++j) acc = fmaf(Ps[h][j], Vs[j][d], acc);
+          O[e] = acc;
+        }
+      }
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int e = 0; e < MAXE; ++e) {
+    const int o = tid + 256 * e;
+    if (e >= n_el || o >= H * 128) continue;
+    const int h = o >> 7, d = o & 127;
+    const float l = l_s[h];
+    if (a.splits == 1) {
+      reinterpret_cast<float*>(a.out)[(size_t)row * H * 128 + o] = l > 0.f ? O[e] / l : 0.f;
+      if (a.lse && d == 0) a.lse[row * H + h] = l > 0.f ? (m_s[h] + __log2f(l)) * kLn2 : -INFINITY;
+    } else {
+      const size_t base = (size_t)(row * a.splits + split) * H + h;
+      a.part_o[base * 128 + d] = O[e];
+      if (d == 0) { a.part_ml[base * 2] = m_s[h]; a.part_ml[base * 2 + 1] = l; }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// log-sum-exp merge of split partials
+// ---------------------------------------------------------------------------
+template <bool BF16>
+__global__ __launch_bounds__(256) void k_attn_combine(const float* __restrict__ part_o,
+                                                      const float* __restrict__ part_ml, int splits,
+                                                      int H, uint8_t* __restrict__ out,
+                                                      float* __restrict__ lse) {
+  const int64_t row = blockIdx.x;
+  for (int o = threadIdx.x; o < H * 128; o += 256) {
+    const int h = o >> 7, d = o & 127;
+    float M = -INFINITY;
+    for (int s = 0; s < splits; ++s) M = fmaxf(M, part_ml[((row * splits + s) * H + h) * 2]);
+    float L = 0.f, acc = 0.f;
+    if (M != -INFINITY) {
+      for (int s = 0; s < splits; ++s) {
+        const size_t base = (size_t)(row * splits + s) * H + h;
+        const float ms = part_ml[base * 2];
+        if (ms == -INFINITY) continue;
+        const float wgt = fast_exp2(ms - M);
+        L = fmaf(wgt, part_ml[base * 2 + 1], L);
+        acc = fmaf(wgt, part_o[base * 128 + d], acc);
+      }
+    }
+    const float v = L > 0.f ? acc / L : 0.f;
+    if (BF16) {
+      reinterpret_cast<uint16_t*>(out)[(size_t)row * H * 128 + o] = (uint16_t)f32_to_bf16(v);
+    } else {
+      reinterpret_cast<float*>(out)[(size_t)row * H * 128 + o] = v;
+    }
+    if (lse && d == 0) lse[row * H + h] = L > 0.f ? (M + __log2f(L)) * kLn2 : -INFINITY;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+AttnPlan plan_attn(int64_t n_q, int64_t list_len, int H) {
+  AttnPlan p;
+  const int64_t max_splits_tile = (list_len + 63) / 64;
+  const int64_t max_splits_amort = (list_len + 255) / 256;  // >= 256 keys per partial
+  int64_t want = n_q > 0 ? (1024 + n_q - 1) / n_q : 1;
+  int64_t s = want;
+  if (s > max_splits_amort) s = max_splits_amort;
+  if (s > max_splits_tile) s = max_splits_tile;
+  if (s < 1) s = 1;
+  int64_t ks = (list_len + s - 1) / s;
+  ks = ((ks + 63) / 64) * 64;
+  if (ks < 64) ks = 64;
+  s = (list_len + ks - 1) / ks;
+  if (s < 1) s = 1;
+  p.splits = (int)s;
+  p.ks = (int)ks;
+  p.ws_bytes = s > 1 ? (size_t)n_q * s * H * (128 + 2) * 4 + 256 : 0;
+  return p;
+}
+
+int launch_attn(bool bf16, bool hca, int n_seq, int64_t n_q, const int64_t* tok_off,
+                const int64_t* q_off, const int64_t* q_pos, const int64_t* pool_off, int m_pool,
+                int seg_a, int W, int H, float scale, const void* q, const void* kv_pool,
+                const void* kv_raw, const int32_t* idx, void* out, float* lse, void* ws,
+                hipStream_t stream) {
+  if (n_q == 0) return 0;
+  const int64_t list_len = (int64_t)seg_a + W;
+  const AttnPlan pl = plan_attn(n_q, list_len, H);
+  AttnArgs a;
+  a.tok_off = tok_off; a.q_off = q_off; a.q_pos = q_pos; a.pool_off = pool_off;
+  a.n_seq = n_seq; a.hca = hca ? 1 : 0; a.m_pool = m_pool; a.seg_a = seg_a; a.W = W; a.H = H;
+  a.scale_log2 = scale * kLog2e;
+  a.q = (const uint8_t*)q; a.kv_pool = (const uint8_t*)kv_pool; a.kv_raw = (const uint8_t*)kv_raw;
+  a.idx = idx; a.out = (uint8_t*)out; a.lse = lse;
+  a.part_o = (float*)ws;
+  a.part_ml = pl.splits > 1 ? (float*)ws + (size_t)n_q * pl.splits * H * 128 : nullptr;
+  a.splits = pl.splits; a.ks = pl.ks;
+  if (list_len == 0) {  // every list is empty: the combine writes zeros and -inf
+    a.splits = 1;
+  }
+  dim3 grid((unsigned)a.splits, (unsigned)n_q);
+  if (bf16) {
+    if (H > 64) hipLaunchKernelGGL(k_attn_bf16<2>, grid, dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL(k_attn_bf16<1>, grid, dim3(256), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL(k_attn_f32, grid, dim3(256), 0, stream, a);
+  }
+  if (a.splits > 1) {
+    if (bf16)
+      hipLaunchKernelGGL(k_attn_combine<true>, dim3((unsigned)n_q), dim3(256), 0, stream, a.part_o,
+                         a.part_ml, a.splits, H, a.out, lse);
+    else
+      hipLaunchKernelGGL(k_attn_combine<false>, dim3((unsigned)n_q), dim3(256), 0, stream, a.part_o,
+                         a.part_ml, a.splits, H, a.out, lse);
+  }
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+}  // namespace csa

@@ -1,0 +1,394 @@
+// Lightning-indexer scoring and exact per-query top-k.
+//
+// Pages: jyp-garden EP 95 notes, IDEAS (KV compressed to 1/4, the Lightning
+// Indexer keeps only the top-k); sigco.tistory.com CSA/HCA section (the
+// indexer looks for the blocks most relevant to the current token and only
+// the top candidates are attended); pytorch.kr FP4 QAT section (the indexer
+// QK path is MXFP4).  Score (reading taken):
+//     S(i, j) = sum_h w[i][h] * max(0, qhat[i][h] . khat[j])
+// with MXFP4 operands, ties broken toward the lower j.
+//
+// Scoring runs on the gfx950 block-scaled MFMA (32x32x64, FP4 x FP4, one
+// E8M0 scale per lane per 32-element K block).  The A operand holds up to 8
+// queries x 4 heads (32 rows), the B operand 32 keys; the power-of-two head
+// weight is folded into the query block scale, so the MFMA output already
+// carries w_h.  Every product and partial sum is a small dyadic rational, so
+// the fp32 accumulation is exact and the score bit pattern is an exact sort
+// key (ReLU is an integer max on the bit pattern, which also maps -0 to +0).
+//
+// Selection is a radix select on those 32-bit keys:
+//   1. k_idx_score: keys to the workspace + a 4096-bin histogram of the top
+//      13 key bits per query (LDS, merged into global memory); the last
+//      workgroup of a query tile finds the threshold bin b1;
+//   2. k_idx_select: entries above b1 are selected outright, entries in b1
+//      become candidates;
+//   3. k_idx_final: exact k-th key K* among the candidates, then the lowest
+//      indices among entries equal to K*, then an ascending sort of the k
+//      selected indices.  It also returns the workspace to all-zero.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace csa {
+
+constexpr int kNBins = 4096;  // key >> 19: 8 exponent + 4 mantissa bits (sign is 0)
+constexpr int kBinShift = 19;
+constexpr int kScoreIter = 8;                       // 32-key MFMA groups per wave
+constexpr int kScoreChunk = 4 * 32 * kScoreIter;    // keys per score workgroup
+constexpr int kSelChunk = 4096;                     // keys per select workgroup
+constexpr uint32_t kNoBin = 0xffffffffu;
+
+__device__ __forceinline__ uint32_t ld_acquire(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ int64_t n_visible(int64_t t, int m, int64_t P) {
+  int64_t v = (t + 1) / m;
+  return v < P ? v : P;
+}
+
+// Threshold bin of one query: the bin b1 with count(bin > b1) < need <= count(bin >= b1).
+// Called by a whole 256-thread block; hist is read with device-coherent loads.
+__device__ void find_threshold(const uint32_t* hist, uint32_t need, uint32_t* info_out) {
+  __shared__ uint32_t part[256];
+  __shared__ uint32_t res[2];
+  const int t = threadIdx.x;
+  uint32_t loc[16];
+  uint32_t s = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) { loc[i] = ld_acquire(hist + t * 16 + i); s += loc[i]; }
+  part[t] = s;
+  __syncthreads();
+  if (t == 0) {
+    uint32_t cum = 0;
+    int tt = 255;
+    for (; tt >= 0; --tt) {
+      if (cum + part[tt] >= need) break;
+      cum += part[tt];
+    }
+    res[0] = (uint32_t)tt;  // thread holding the crossing (tt >= 0 since total >= need)
+    res[1] = cum;           // count above that thread's bins
+  }
+  __syncthreads();
+  if (t == (int)res[0]) {
+    uint32_t cum = res[1];
+    int bi = 15;
+    for (; bi > 0; --bi) {
+      if (cum + loc[bi] >= need) break;
+      cum += loc[bi];
+    }
+    info_out[0] = (uint32_t)(t * 16 + bi);
+    info_out[1] = cum;
+  }
+  __syncthreads();
+}
+
+struct ScoreArgs {
+  const int64_t* q_off;
+  const int64_t* q_pos;
+  const int64_t* pool_off;
+  int n_seq, tiles_per_seq, qt, m, k;
+  int64_t max_pool;
+  const uint8_t* q_codes;
+  const uint8_t* q_scales;
+  const float* w;
+  const uint8_t* k_codes;
+  const uint8_t* k_scales;
+  uint32_t* keys;
+  uint32_t* hist;
+  uint32_t* counts;
+  uint32_t* info;
+};
+
+__global__ __launch_bounds__(256) void k_idx_score(ScoreArgs a) {
+  extern __shared__ uint32_t lhist[];  // qt * kNBins/2 words, two 16-bit counters per word
+  __shared__ int64_t nvis_s[8];
+  __shared__ int is_last;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tile = blockIdx.y;
+  const int b = tile / a.tiles_per_seq;
+  const int64_t row0 = a.q_off[b] + (int64_t)(tile % a.tiles_per_seq) * a.qt;
+  const int64_t row_end_seq = a.q_off[b + 1];
+  const int nrows = (int)(row0 >= row_end_seq ? 0 : (row_end_seq - row0 < a.qt ? row_end_seq - row0 : a.qt));
+  if (nrows == 0) return;  // an empty tile: no query waits on it
+  const int64_t pbase = a.pool_off[b];
+  const int64_t P = a.pool_off[b + 1] - pbase;
+  if (tid < 8) nvis_s[tid] = tid < nrows ? n_visible(a.q_pos[row0 + tid], a.m, P) : 0;
+  for (int i = tid; i < a.qt * (kNBins / 2); i += 256) lhist[i] = 0;
+  __syncthreads();
+  int64_t nvis_max = 0;
+  for (int r = 0; r < nrows; ++r) nvis_max = nvis_s[r] > nvis_max ? nvis_s[r] : nvis_max;
+
+  // A operand: row (lane%32) = query slot * 4 + head, K block lane/32
+  const int slot_a = (lane & 31) >> 2, head_a = lane & 3, kb = lane >> 5;
+  v8i av = {0, 0, 0, 0, 0, 0, 0, 0};
+  int asc = 127;
+  if (slot_a < nrows) {
+    const int64_t qrow = (row0 + slot_a) * 4 + head_a;
+    uint4 u = *reinterpret_cast<const uint4*>(a.q_codes + qrow * 32 + kb * 16);
+    av[0] = (int)u.x; av[1] = (int)u.y; av[2] = (int)u.z; av[3] = (int)u.w;
+    const int we = (int)((__float_as_uint(a.w[qrow]) >> 23) & 255u) - 127;
+    asc = (int)a.q_scales[qrow * 2 + kb] + we;  // w_h = 2^we folded into the block scale
+  }
+
+  const int64_t jc0 = (int64_t)blockIdx.x * kScoreChunk;
+  if (jc0 < nvis_max) {
+    // issue all key loads of this wave first, then the MFMAs
+    uint4 kcv[kScoreIter];
+    int ksv[kScoreIter];
+#pragma unroll
+    for (int it = 0; it < kScoreIter; ++it) {
+      const int64_t j = jc0 + (int64_t)(wave * kScoreIter + it) * 32 + (lane & 31);
+      kcv[it] = make_uint4(0, 0, 0, 0);
+      ksv[it] = 127;
+      if (j < nvis_max) {
+        kcv[it] = *reinterpret_cast<const uint4*>(a.k_codes + (pbase + j) * 32 + kb * 16);
+        ksv[it] = a.k_scales[(pbase + j) * 2 + kb];
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < kScoreIter; ++it) {
+      const int64_t jbase = jc0 + (int64_t)(wave * kScoreIter + it) * 32;
+      if (jbase >= nvis_max) break;
+      v8i bv = {(int)kcv[it].x, (int)kcv[it].y, (int)kcv[it].z, (int)kcv[it].w, 0, 0, 0, 0};
+      v16f acc = {};
+      acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc, 4, 4, 0, asc, 0, ksv[it]);
+      const int64_t j = jbase + (lane & 31);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int slot = 2 * s + (lane >> 5);
+        if (slot < nrows && j < nvis_s[slot]) {
+          float r0 = __int_as_float(max(__float_as_int(acc[4 * s + 0]), 0));
+          float r1 = __int_as_float(max(__float_as_int(acc[4 * s + 1]), 0));
+          float r2 = __int_as_float(max(__float_as_int(acc[4 * s + 2]), 0));
+          float r3 = __int_as_float(max(__float_as_int(acc[4 * s + 3]), 0));
+          const uint32_t key = __float_as_uint((r0 + r1) + (r2 + r3));
+          a.keys[(row0 + slot) * a.max_pool + j] = key;
+          const uint32_t bin = key >> kBinShift;
+          atomicAdd(&lhist[slot * (kNBins / 2) + (bin >> 1)], 1u << ((bin & 1u) * 16));
+        }
+      }
+    }
+  }
+  __syncthreads();
+  for (int r = 0; r < nrows; ++r) {
+    uint32_t* gh = a.hist + (row0 + r) * kNBins;
+    for (int wi = tid; wi < kNBins / 2; wi += 256) {
+      const uint32_t v = lhist[r * (kNBins / 2) + wi];
+      if (v & 0xffffu) atomicAdd(gh + 2 * wi, v & 0xffffu);
+      if (v >> 16) atomicAdd(gh + 2 * wi + 1, v >> 16);
+    }
+  }
+  // the last workgroup of this query tile computes the threshold bins
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) is_last = (atomicAdd(a.counts + row0 * 4 + 2, 1u) == gridDim.x - 1);
+  __syncthreads();
+  if (!is_last) return;
+  __threadfence();
+  for (int r = 0; r < nrows; ++r) {
+    const int64_t kk = nvis_s[r] < a.k ? nvis_s[r] : a.k;
+    uint32_t* info = a.info + (row0 + r) * 2;
+    if (kk == 0) {
+      if (tid == 0) { info[0] = kNoBin; info[1] = 0; }
+      continue;
+    }
+    find_threshold(a.hist + (row0 + r) * kNBins, (uint32_t)kk, info);
+  }
+  if (tid == 0) a.counts[row0 * 4 + 2] = 0;
+}
+
+struct SelectArgs {
+  const int64_t* q_off;
+  const int64_t* q_pos;
+  const int64_t* pool_off;
+  int n_seq, m, k;
+  int64_t max_pool;
+  const uint32_t* keys;
+  const uint32_t* info;
+  uint32_t* counts;
+  int32_t* def;
+  uint2* cand;
+};
+
+__global__ __launch_bounds__(256) void k_idx_select(SelectArgs a) {
+  const int64_t row = blockIdx.y;
+  const uint32_t b1 = a.info[row * 2];
+  if (b1 == kNoBin) return;
+  const int b = seq_of_row(a.q_off, a.n_seq, row);
+  const int64_t P = a.pool_off[b + 1] - a.pool_off[b];
+  const int64_t nvis = n_visible(a.q_pos[row], a.m, P);
+  const int64_t j0 = (int64_t)blockIdx.x * kSelChunk;
+  if (j0 >= nvis) return;
+  const int lane = threadIdx.x & 63;
+  const uint32_t* keys = a.keys + row * a.max_pool;
+  for (int i = 0; i < kSelChunk / 256; ++i) {
+    const int64_t j = j0 + i * 256 + threadIdx.x;
+    uint32_t key = 0, bin = 0;
+    const bool ok = j < nvis;
+    if (ok) { key = keys[j]; bin = key >> kBinShift; }
+    const bool gt = ok && bin > b1, eq = ok && bin == b1;
+    const uint64_t mg = __ballot(gt), me = __ballot(eq);
+    const int first = __ffsll((unsigned long long)(mg | me)) - 1;
+    if (first < 0) continue;
+    uint32_t base_g = 0, base_e = 0;
+    if (lane == first) {
+      if (mg) base_g = atomicAdd(a.counts + row * 4 + 0, (uint32_t)__popcll(mg));
+      if (me) base_e = atomicAdd(a.counts + row * 4 + 1, (uint32_t)__popcll(me));
+    }
+    base_g = __shfl(base_g, first);
+    base_e = __shfl(base_e, first);
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    if (gt) a.def[row * a.k + base_g + __popcll(mg & below)] = (int32_t)j;
+    if (eq) a.cand[row * a.max_pool + base_e + __popcll(me & below)] = make_uint2(key, (uint32_t)j);
+  }
+}
+
+struct FinalArgs {
+  const int64_t* q_off;
+  const int64_t* q_pos;
+  const int64_t* pool_off;
+  int n_seq, m, k;
+  int64_t max_pool;
+  uint32_t* counts;
+  uint32_t* hist;
+  const int32_t* def;
+  const uint2* cand;
+  int32_t* idx;
+};
+
+// need-th largest value among the active candidates, 8 bits per round.
+// Returns the exact value; *need_left = how many entries equal to it are to be taken.
+template <typename ValueFn, typename ActiveFn>
+__device__ uint32_t radix_select_desc(int64_t n, uint32_t need, ValueFn val, ActiveFn active,
+                                      uint32_t* need_left) {
+  __shared__ uint32_t bins[256];
+  __shared__ uint32_t sh[2];
+  uint32_t prefix = 0, pmask = 0;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    for (int i = threadIdx.x; i < 256; i += blockDim.x) bins[i] = 0;
+    __syncthreads();
+    for (int64_t i = threadIdx.x; i < n; i += blockDim.x) {
+      if (!active(i)) continue;
+      const uint32_t v = val(i);
+      if ((v & pmask) == prefix) atomicAdd(&bins[(v >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      uint32_t cum = 0;
+      int d = 255;
+      for (; d > 0; --d) {
+        if (cum + bins[d] >= need) break;
+        cum += bins[d];
+      }
+      sh[0] = (uint32_t)d;
+      sh[1] = need - cum;
+    }
+    __syncthreads();
+    prefix |= sh[0] << shift;
+    pmask |= 255u << shift;
+    need = sh[1];
+    __syncthreads();
+  }
+  *need_left = need;
+  return prefix;
+}
+
+__global__ __launch_bounds__(1024) void k_idx_final(FinalArgs a) {
+  __shared__ int32_t outj[4096];
+  __shared__ uint32_t n_out;
+  const int64_t row = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int b = seq_of_row(a.q_off, a.n_seq, row);
+  const int64_t P = a.pool_off[b + 1] - a.pool_off[b];
+  const int64_t nvis = n_visible(a.q_pos[row], a.m, P);
+  const int k_eff = (int)(nvis < a.k ? nvis : a.k);
+  int32_t* idx = a.idx + row * a.k;
+  if (k_eff > 0) {
+    const uint32_t n_def = a.counts[row * 4 + 0];
+    const uint32_t n_c = a.counts[row * 4 + 1];
+    const uint32_t need = (uint32_t)k_eff - n_def;  // >= 1 by the choice of b1
+    const uint2* cand = a.cand + row * a.max_pool;
+    uint32_t r;
+    const uint32_t kstar = radix_select_desc(
+        n_c, need, [&](int64_t i) { return cand[i].x; }, [&](int64_t) { return true; }, &r);
+    uint32_t r2;
+    const uint32_t jstar = radix_select_desc(
+        n_c, r, [&](int64_t i) { return ~cand[i].y; }, [&](int64_t i) { return cand[i].x == kstar; },
+        &r2);
+    if (tid == 0) n_out = n_def;
+    for (uint32_t i = tid; i < n_def; i += blockDim.x) outj[i] = a.def[row * a.k + i];
+    __syncthreads();
+    for (uint32_t i = tid; i < n_c; i += blockDim.x) {
+      const uint2 c = cand[i];
+      if (c.x > kstar || (c.x == kstar && ~c.y >= jstar)) outj[atomicAdd(&n_out, 1u)] = (int32_t)c.y;
+    }
+    __syncthreads();
+    // bitonic sort of outj[0..k_eff) ascending, padded to a power of two
+    int N = 1;
+    while (N < k_eff) N <<= 1;
+    for (int i = k_eff + tid; i < N; i += blockDim.x) outj[i] = 0x7fffffff;
+    __syncthreads();
+    for (int size = 2; size <= N; size <<= 1) {
+      for (int stride = size >> 1; stride > 0; stride >>= 1) {
+        for (int i = tid; i < N / 2; i += blockDim.x) {
+          const int lo = 2 * i - (i & (stride - 1));
+          const int hi = lo + stride;
+          const bool up = ((lo & size) == 0);
+          const int32_t x = outj[lo], y = outj[hi];
+          if ((x > y) == up) { outj[lo] = y; outj[hi] = x; }
+        }
+        __syncthreads();
+      }
+    }
+    for (int i = tid; i < k_eff; i += blockDim.x) idx[i] = outj[i];
+  }
+  for (int i = k_eff + tid; i < a.k; i += blockDim.x) idx[i] = -1;
+  // return this query's workspace rows to zero for the next call
+  for (int i = tid; i < kNBins; i += blockDim.x) a.hist[row * kNBins + i] = 0;
+  if (tid < 2) a.counts[row * 4 + tid] = 0;
+}
+
+size_t index_ws_bytes(int64_t n_q, int64_t max_pool, int k) {
+  size_t s = 0;
+  auto add = [&](size_t bytes) { s += (bytes + 255) & ~(size_t)255; };
+  add((size_t)n_q * kNBins * 4);        // hist (zero invariant)
+  add((size_t)n_q * 4 * 4);             // counts (zero invariant)
+  add((size_t)n_q * 2 * 4);             // info
+  add((size_t)n_q * max_pool * 4);      // keys
+  add((size_t)n_q * k * 4);             // def
+  add((size_t)n_q * max_pool * 8);      // cand
+  return s;
+}
+
+int launch_index_topk(int n_seq, int64_t n_q, int64_t max_q_per_seq, const int64_t* q_off,
+                      const int64_t* q_pos, const int64_t* pool_off, int64_t max_pool, int m,
+                      int k, const uint8_t* q_codes, const uint8_t* q_scales, const float* w,
+                      const uint8_t* k_codes, const uint8_t* k_scales, int32_t* idx, void* ws,
+                      hipStream_t stream) {
+  uint8_t* p = (uint8_t*)ws;
+  auto take = [&](size_t bytes) { uint8_t* r = p; p += (bytes + 255) & ~(size_t)255; return r; };
+  uint32_t* hist = (uint32_t*)take((size_t)n_q * kNBins * 4);
+  uint32_t* counts = (uint32_t*)take((size_t)n_q * 4 * 4);
+  uint32_t* info = (uint32_t*)take((size_t)n_q * 2 * 4);
+  uint32_t* keys = (uint32_t*)take((size_t)n_q * max_pool * 4);
+  int32_t* def = (int32_t*)take((size_t)n_q * k * 4);
+  uint2* cand = (uint2*)take((size_t)n_q * max_pool * 8);
+  if (n_q == 0) return 0;
+
+  const int qt = max_q_per_seq > 1 ? 8 : 1;
+  const int tiles_per_seq = (int)((max_q_per_seq + qt - 1) / qt);
+  ScoreArgs sa{q_off, q_pos, pool_off, n_seq, tiles_per_seq, qt, m, k, max_pool, q_codes,
+               q_scales, w, k_codes, k_scales, keys, hist, counts, info};
+  dim3 g1((unsigned)((max_pool + kScoreChunk - 1) / kScoreChunk), (unsigned)(n_seq * tiles_per_seq));
+  if (g1.x == 0) g1.x = 1;
+  hipLaunchKernelGGL(k_idx_score, g1, dim3(256), (size_t)qt * (kNBins / 2) * 4, stream, sa);
+  SelectArgs se{q_off, q_pos, pool_off, n_seq, m, k, max_pool, keys, info, counts, def, cand};
+  dim3 g2((unsigned)((max_pool + kSelChunk - 1) / kSelChunk), (unsigned)n_q);
+  if (g2.x == 0) g2.x = 1;
+  hipLaunchKernelGGL(k_idx_select, g2, dim3(256), 0, stream, se);
+  FinalArgs fa{q_off, q_pos, pool_off, n_seq, m, k, max_pool, counts, hist, def, cand, idx};
+  hipLaunchKernelGGL(k_idx_final, dim3((unsigned)n_q), dim3(1024), 0, stream, fa);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+}  // namespace csa

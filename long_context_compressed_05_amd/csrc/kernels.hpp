@@ -1,0 +1,32 @@
+// Host-side launchers of the libcsa kernels (internal to the library).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace csa {
+
+int launch_compress(bool bf16, int n_seq, const int64_t* tok_off, const int64_t* pool_off,
+                    int64_t max_len, int m, int width, const void* x, const void* z, void* out,
+                    hipStream_t stream);
+
+size_t index_ws_bytes(int64_t n_q, int64_t max_pool, int k);
+int launch_index_topk(int n_seq, int64_t n_q, int64_t max_q_per_seq, const int64_t* q_off,
+                      const int64_t* q_pos, const int64_t* pool_off, int64_t max_pool, int m,
+                      int k, const uint8_t* q_codes, const uint8_t* q_scales, const float* w,
+                      const uint8_t* k_codes, const uint8_t* k_scales, int32_t* idx, void* ws,
+                      hipStream_t stream);
+
+struct AttnPlan {
+  int splits;
+  int ks;
+  size_t ws_bytes;
+};
+AttnPlan plan_attn(int64_t n_q, int64_t list_len, int H);
+int launch_attn(bool bf16, bool hca, int n_seq, int64_t n_q, const int64_t* tok_off,
+                const int64_t* q_off, const int64_t* q_pos, const int64_t* pool_off, int m_pool,
+                int seg_a, int W, int H, float scale, const void* q, const void* kv_pool,
+                const void* kv_raw, const int32_t* idx, void* out, float* lse, void* ws,
+                hipStream_t stream);
+
+}  // namespace csa

@@ -1,0 +1,203 @@
+"""GPU parity of the HIP path (through the C ABI) against the CPU oracle on
+the same seeded inputs, at sizes the oracle finishes in seconds that still
+span several tiles, ragged batches and tails, and the degenerate cases
+(no visible block, k above the visible count, k = 1, window clipped at the
+sequence start, empty HCA list)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests import _parity as P
+
+pytestmark = pytest.mark.gpu
+
+
+def _lib():
+    import long_context_compressed_05_amd as csa
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    csa.lib()  # raises if libcsa.so is missing: no fallback
+    return csa
+
+
+def small_wl(name, lengths, q_counts, H=64, dtype="bf16", k=64, W=128, m=4, m_hca=128, W_hca=0,
+             codeset=synth.E2M1_ALL_CODES, seed=77):
+    return synth.Workload(name, list(lengths), [L - c for L, c in zip(lengths, q_counts)], H=H,
+                          dtype=dtype, k=k, W=W, m=m, m_hca=m_hca, W_hca=W_hca, codeset=codeset, seed=seed)
+
+
+WORKLOADS = {
+    "decode_fp32_t4096_h8": lambda: synth.decode_t4096_fp32(),
+    "decode_bf16_ragged": lambda: small_wl("decode_bf16_ragged", [1, 3, 130, 517, 1030, 2049, 4099],
+                                           [1] * 7, k=64, seed=11),
+    "prefill_bf16_chunks": lambda: small_wl("prefill_bf16_chunks", [700, 1500], [37, 100], k=32,
+                                            W=64, seed=12),
+    "decode_bf16_ties": lambda: small_wl("decode_bf16_ties", [3001, 2998, 4097, 5003], [1] * 4, k=50,
+                                         codeset=synth.E2M1_TIE_CODES, seed=13),
+    "decode_fp32_k1_h24": lambda: small_wl("decode_fp32_k1_h24", [333, 1024], [2, 3], H=24,
+                                           dtype="f32", k=1, W=5, m=3, m_hca=16, seed=14),
+    "decode_bf16_kbig_whca": lambda: small_wl("decode_bf16_kbig_whca", [200, 900], [1, 4], H=32, k=4000,
+                                              W=200, m=4, m_hca=64, W_hca=64, seed=15),
+}
+
+
+def _params(wl):
+    from long_context_compressed_05_amd.step import Params
+    return Params(H=wl.H, d=wl.d, m=wl.m, k=wl.k, W=wl.W, m_hca=wl.m_hca, W_hca=wl.W_hca)
+
+
+def _run_path(wl, host):
+    from long_context_compressed_05_amd.step import Layer, to_device
+    layer = Layer.from_host(_params(wl), host)
+    layer.build_caches()
+    dq = to_device({k: host[k] for k in ("q", "qc", "qs", "w")})
+    idx, co, cl, ho, hl = layer.attend(dq["q"], dq["qc"], dq["qs"], dq["w"])
+    torch.cuda.synchronize()
+    return layer, (P.torch_to_np(idx), P.torch_to_np(co), P.torch_to_np(cl), P.torch_to_np(ho),
+                   P.torch_to_np(hl))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("m", [1, 3, 4, 128])
+def test_compress_parity(dtype, m):
+    csa = _lib()
+    wl = small_wl("compress", [5, 130, 517, 1030, 2049], [1] * 5, dtype=dtype, m=m, seed=21)
+    host = synth.make_inputs(wl)
+    from long_context_compressed_05_amd.step import to_device
+    d = to_device({k: host[k] for k in ("kv", "z", "tok_off")})
+    P_b = [L // m for L in wl.lengths]
+    pool_off = synth.offsets(P_b)
+    out = torch.empty((int(pool_off[-1]), 2, wl.d), dtype=d["kv"].dtype, device="cuda")
+    csa.csa_compress(d["kv"], d["z"], d["tok_off"], torch.from_numpy(pool_off).cuda(), max(wl.lengths), m, out)
+    torch.cuda.synchronize()
+    got = P.torch_to_np(out)
+    for b in range(wl.B):
+        t0, t1 = int(host["tok_off"][b]), int(host["tok_off"][b + 1])
+        want = oracle.pool(host["kv"][t0:t1], host["z"][t0:t1], m).reshape(-1, 2, wl.d)
+        P.check_close(got[pool_off[b]:pool_off[b + 1]], want, dtype, f"pooled rows of sequence {b}")
+        # one rounding of an fp32 result: within 2^-8 relative (+ tiny) of the exact value
+        g = P.as_f64(got[pool_off[b]:pool_off[b + 1]])
+        bound = (2.0 ** -8 if dtype == "bf16" else 2.0 ** -20) * np.abs(want) + 1e-6
+        assert np.all(np.abs(g - want) <= bound)
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_index_topk_bit_exact(name):
+    csa = _lib()
+    wl = WORKLOADS[name]()
+    host = synth.make_inputs(wl, raw=False)
+    from long_context_compressed_05_amd.step import to_device
+    d = to_device({k: host[k] for k in ("qc", "qs", "w", "kc", "ks", "pool_off")})
+    batch = csa.Batch.from_host(host["tok_off"], host["q_off"], host["q_pos"])
+    max_pool = int(np.diff(host["pool_off"]).max())
+    ws = csa.Workspace()
+    idx = csa.csa_index_topk(batch, d["pool_off"], max_pool, wl.m, wl.k, d["qc"], d["qs"], d["w"], d["kc"],
+                             d["ks"], ws=ws)
+    got = P.torch_to_np(idx)
+    seqs = P.row_seq(host)
+    for row in range(wl.n_q):
+        want = P.oracle_topk_row(host, wl, row, seqs[row], wl.k, wl.m)
+        assert np.array_equal(got[row], want), f"row {row} (seq {seqs[row]}, t={host['q_pos'][row]})"
+    # the library leaves its workspace zero-filled; a second call is bit-identical
+    assert int(torch.count_nonzero(ws.buf[:4096 * 4 * wl.n_q])) == 0
+    idx2 = csa.csa_index_topk(batch, d["pool_off"], max_pool, wl.m, wl.k, d["qc"], d["qs"], d["w"], d["kc"],
+                              d["ks"], ws=ws)
+    assert torch.equal(idx, idx2)
+
+
+@pytest.mark.parametrize("name", ["decode_fp32_t4096_h8", "decode_bf16_ragged", "prefill_bf16_chunks",
+                                  "decode_fp32_k1_h24", "decode_bf16_kbig_whca"])
+def test_sparse_attn_stagewise(name):
+    """Attention on given inputs: a generated pooled cache and the oracle's indices."""
+    csa = _lib()
+    wl = WORKLOADS[name]()
+    host = synth.make_inputs(wl)
+    pooled = synth.pooled_like(wl, wl.m)
+    seqs = P.row_seq(host)
+    idx = np.stack([P.oracle_topk_row(host, wl, r, seqs[r], wl.k, wl.m) for r in range(wl.n_q)])
+    from long_context_compressed_05_amd.step import to_device
+    d = to_device({"kv": host["kv"], "q": host["q"], "pooled": pooled, "idx": idx,
+                   "pool_off": host["pool_off"]})
+    batch = csa.Batch.from_host(host["tok_off"], host["q_off"], host["q_pos"])
+    scale = 1 / math.sqrt(wl.d)
+    out, lse = csa.csa_sparse_attn(batch, d["pool_off"], d["q"], d["pooled"], d["kv"], d["idx"], wl.W, scale)
+    got, gl = P.torch_to_np(out), P.torch_to_np(lse)
+    want = np.zeros(got.shape)
+    wl_ = np.zeros(gl.shape)
+    for r in range(wl.n_q):
+        b = seqs[r]
+        (t0, t1), (p0, p1), _ = P.seq_slices(host, b)
+        want[r], wl_[r] = oracle.csa_attend_given(host["kv"][t0:t1], pooled[p0:p1], idx[r], host["q"][r],
+                                                 int(host["q_pos"][r]), wl.W, scale)
+    P.check_close(got, want, wl.dtype, "csa output")
+    P.check_close(gl, wl_, "f32" if wl.dtype == "f32" else "bf16", "csa lse")
+
+
+@pytest.mark.parametrize("name", ["decode_fp32_t4096_h8", "decode_bf16_ragged", "prefill_bf16_chunks",
+                                  "decode_fp32_k1_h24", "decode_bf16_kbig_whca"])
+def test_hca_attn_stagewise(name):
+    csa = _lib()
+    wl = WORKLOADS[name]()
+    host = synth.make_inputs(wl)
+    hpooled = synth.pooled_like(wl, wl.m_hca)
+    seqs = P.row_seq(host)
+    from long_context_compressed_05_amd.step import to_device
+    d = to_device({"kv": host["kv"], "q": host["q"], "hpooled": hpooled, "hpool_off": host["hpool_off"]})
+    batch = csa.Batch.from_host(host["tok_off"], host["q_off"], host["q_pos"])
+    scale = 1 / math.sqrt(wl.d)
+    max_hpool = int(np.diff(host["hpool_off"]).max())
+    out, lse = csa.hca_attn(batch, d["hpool_off"], max_hpool, wl.m_hca, d["q"], d["hpooled"], d["kv"], wl.W_hca,
+                            scale)
+    got, gl = P.torch_to_np(out), P.torch_to_np(lse)
+    want = np.zeros(got.shape)
+    wl_ = np.zeros(gl.shape)
+    for r in range(wl.n_q):
+        b = seqs[r]
+        t0, t1 = int(host["tok_off"][b]), int(host["tok_off"][b + 1])
+        h0, h1 = int(host["hpool_off"][b]), int(host["hpool_off"][b + 1])
+        want[r], wl_[r] = oracle.hca_attend_given(host["kv"][t0:t1], hpooled[h0:h1], host["q"][r],
+                                                 int(host["q_pos"][r]), wl.m_hca, wl.W_hca, scale)
+    P.check_close(got, want, wl.dtype, "hca output")
+    P.check_close(gl, wl_, "f32" if wl.dtype == "f32" else "bf16", "hca lse")
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_end_to_end(name):
+    """Raw rows -> compress -> index/top-k -> CSA and HCA, against the oracle
+    pooling in fp64 from the same raw rows."""
+    _lib()
+    wl = WORKLOADS[name]()
+    host = synth.make_inputs(wl)
+    _, (idx, co, cl, ho, hl) = _run_path(wl, host)
+    seqs = P.row_seq(host)
+    scale = 1 / math.sqrt(wl.d)
+    want_co, want_cl = np.zeros(co.shape), np.zeros(cl.shape)
+    want_ho, want_hl = np.zeros(ho.shape), np.zeros(hl.shape)
+    for r in range(wl.n_q):
+        b = seqs[r]
+        (t0, t1), (p0, p1), _ = P.seq_slices(host, b)
+        t = int(host["q_pos"][r])
+        o, l, i = oracle.csa_query(host["kv"][t0:t1], host["z"][t0:t1], host["q"][r], t, wl.m, wl.W, wl.k, scale,
+                                   host["qc"][r], host["qs"][r], host["w"][r], host["kc"][p0:p1],
+                                   host["ks"][p0:p1])
+        assert np.array_equal(idx[r], i), f"top-k of row {r}"
+        want_co[r], want_cl[r] = o, l
+        want_ho[r], want_hl[r] = oracle.hca_query(host["kv"][t0:t1], host["z"][t0:t1], host["q"][r], t, wl.m_hca,
+                                                  wl.W_hca, scale)
+    P.check_close(co, want_co, wl.dtype, "csa output")
+    P.check_close(cl, want_cl, "f32" if wl.dtype == "f32" else "bf16", "csa lse")
+    P.check_close(ho, want_ho, wl.dtype, "hca output")
+    P.check_close(hl, want_hl, "f32" if wl.dtype == "f32" else "bf16", "hca lse")
+
+
+def test_deterministic_repeat():
+    _lib()
+    wl = WORKLOADS["decode_bf16_ties"]()
+    host = synth.make_inputs(wl)
+    _, a = _run_path(wl, host)
+    _, b = _run_path(wl, host)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
