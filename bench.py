@@ -1,0 +1,326 @@
+#!/usr/bin/env python3
+"""CSA + HCA decode benchmark on one MI355X (gfx950).
+
+One step = one pass of the whole decode hot path over one batch: indexer
+scoring + exact top-k (csa_index_topk), CSA sparse attention over the top-k
+pooled rows plus the sliding window (csa_sparse_attn), and HCA dense attention
+(hca_attn), for every sequence's query at position T-1.  Pooled caches are
+built once with csa_compress before timing (its throughput is reported apart).
+
+Default workload: 4 sequences x 1,048,576 tokens, 64 query heads on one bf16
+KV head, d = 128, m = 4 (262,144 pooled entries), top-k 1024, window 128,
+m' = 128 (8192 entries), indexer 4 heads x 64 in MXFP4.  Inputs are seeded
+synthetic data already resident in HBM; R input sets are rotated so that
+consecutive steps do not hit the 256 MB Infinity Cache.
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+T0 = time.time()
+METRIC = "CSA+HCA decode queries/s & HBM GB/s at 1M ctx; prefill indexer TFLOP/s"
+HBM_PEAK_GBS = 8000.0
+FP4_PEAK_TFLOPS = 10100.0
+
+
+def log(msg: str):
+    print(f"[bench {time.time() - T0:7.1f}s] {msg}", file=sys.stderr, flush=True)
+
+
+def decode_bytes_per_query(n_vis, k, W, L, n_hvis, H, d, es):
+    """Algorithmic HBM bytes of one decode query: indexer keys + scales, the
+    gathered pooled rows, the window rows, the HCA rows, q and out for both
+    branches, the indices, and the indexer query codes, scales and weights."""
+    k_eff = min(k, n_vis)
+    return (34 * n_vis + k_eff * 2 * d * es + min(W, L) * 2 * d * es + n_hvis * 2 * d * es
+            + 4 * H * d * es + 4 * k + (4 * 34 + 4 * 4))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="decode_b4_t1m")
+    ap.add_argument("--rotate", type=int, default=20, help="input sets cycled through the timed steps")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--eager", action="store_true", help="time eager launches instead of a captured HIP graph")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(decode shards by sequence with no exchange; see the design notes). Run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    import long_context_compressed_05_amd as csa
+    from long_context_compressed_05_amd.step import Layer, Params, to_device
+
+    assert torch.cuda.is_available(), "bench.py needs a ROCm GPU"
+    csa.lib()
+    dev = "cuda"
+    torch.cuda.init()
+
+    wl = synth.WORKLOADS[args.workload]()
+    log(f"workload {wl.name}: B={wl.B} max_len={max(wl.lengths)} n_q={wl.n_q}; generating inputs")
+    host = synth.make_inputs(wl)
+    es = 2 if wl.dtype == "bf16" else 4
+    p = Params(H=wl.H, d=wl.d, m=wl.m, k=wl.k, W=wl.W, m_hca=wl.m_hca, W_hca=wl.W_hca)
+    layer = Layer.from_host(p, host, dev)
+    log("inputs resident on the GPU; building pooled caches")
+
+    # ---- compress (cache build), timed apart ----------------------------------
+    n_pool, n_hpool = int(host["pool_off"][-1]), int(host["hpool_off"][-1])
+    layer.pooled = torch.empty((n_pool, 2, wl.d), dtype=layer.kv.dtype, device=dev)
+    layer.hpooled = torch.empty((n_hpool, 2, wl.d), dtype=layer.kv.dtype, device=dev)
+    compress = {}
+    for name, m, off, out in (("csa", wl.m, layer.pool_off, layer.pooled), ("hca", wl.m_hca, layer.hpool_off, layer.hpooled)):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        csa.csa_compress(layer.kv, layer.z, layer.tok_off, off, layer.batch.max_len, m, out)  # warm
+        torch.cuda.synchronize()
+        e0.record()
+        csa.csa_compress(layer.kv, layer.z, layer.tok_off, off, layer.batch.max_len, m, out)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        rows = sum((L // m) * m for L in wl.lengths)
+        nbytes = 2 * rows * 2 * wl.d * es + (rows // m) * 2 * wl.d * es
+        compress[name] = {"m": m, "ms": round(ms, 4), "GB/s": round(nbytes / ms / 1e6, 1)}
+    log(f"compress: {compress}")
+
+    # ---- rotation sets ---------------------------------------------------------
+    R = max(1, args.rotate)
+    sets = []
+    P_tot = int(host["pool_off"][-1])
+    for r in range(R):
+        if r == 0:
+            hs = {k: host[k] for k in ("q", "qc", "qs", "w", "kc", "ks")}
+        else:
+            s = wl.seed + 7919 * r
+            hs = {
+                "q": synth.normal(s, synth.S_Q, wl.n_q * wl.H * wl.d, wl.dtype).reshape(wl.n_q, wl.H, wl.d),
+                "qc": synth.codes4(s, synth.S_QCODE, wl.n_q * 128, wl.codeset).reshape(wl.n_q, 4, 32),
+                "qs": synth.exp_bytes(s, synth.S_QSCALE, wl.n_q * 8, *wl.scale_exp).reshape(wl.n_q, 4, 2),
+                "w": synth.pow2(s, synth.S_W, wl.n_q * 4, *wl.w_exp).reshape(wl.n_q, 4),
+                "kc": synth.codes4(s, synth.S_KCODE, P_tot * 32, wl.codeset).reshape(P_tot, 32),
+                "ks": synth.exp_bytes(s, synth.S_KSCALE, P_tot * 2, *wl.scale_exp).reshape(P_tot, 2),
+            }
+        d = to_device(hs, dev)
+        d["hpooled"] = layer.hpooled if r == 0 else layer.hpooled.clone()
+        d["idx"] = torch.empty((wl.n_q, wl.k), dtype=torch.int32, device=dev)
+        d["co"] = torch.empty((wl.n_q, wl.H, wl.d), dtype=layer.kv.dtype, device=dev)
+        d["cl"] = torch.empty((wl.n_q, wl.H), dtype=torch.float32, device=dev)
+        d["ho"] = torch.empty_like(d["co"])
+        d["hl"] = torch.empty_like(d["cl"])
+        sets.append(d)
+    log(f"{R} rotation sets resident")
+
+    batch = layer.batch
+    scale = 1.0 / math.sqrt(wl.d)
+
+    def step(r):
+        d = sets[r % R]
+        csa.csa_index_topk(batch, layer.pool_off, layer.max_pool, wl.m, wl.k, d["qc"], d["qs"], d["w"], d["kc"],
+                           d["ks"], idx=d["idx"], ws=layer.ws_idx)
+        csa.csa_sparse_attn(batch, layer.pool_off, d["q"], layer.pooled, layer.kv, d["idx"], wl.W, scale,
+                            out=d["co"], lse=d["cl"], ws=layer.ws_csa)
+        csa.hca_attn(batch, layer.hpool_off, layer.max_hpool, wl.m_hca, d["q"], d["hpooled"], layer.kv, wl.W_hca,
+                     scale, out=d["ho"], lse=d["hl"], ws=layer.ws_hca)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} steps done; timing {args.steps} steps")
+
+    K = args.steps
+    # dominant kernel: HIP events around every launch of the indexer scoring kernel
+    # (eager steps, same inputs and rotation)
+    ev = [(csa.HipEvent(), csa.HipEvent()) for _ in range(K)]
+    torch.cuda.synchronize()
+    for i in range(K):
+        csa.csa_profile_events(csa.CSA_K_IDX_SCORE, ev[i][0], ev[i][1])
+        step(i)
+    torch.cuda.synchronize()
+    csa.csa_profile_events(csa.CSA_K_IDX_SCORE)
+    score_ms = float(np.mean([a.elapsed_ms(b) for a, b in ev]))
+
+    graph = None
+    if not args.eager:
+        try:
+            graph = torch.cuda.CUDAGraph()
+            cap = torch.cuda.Stream()
+            cap.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(cap):
+                with torch.cuda.graph(graph, stream=cap):
+                    for r in range(R):
+                        step(r)
+            torch.cuda.current_stream().wait_stream(cap)
+            for _ in range(max(1, args.warmup // R)):
+                graph.replay()
+            torch.cuda.synchronize()
+        except Exception as e:
+            log(f"graph capture unavailable ({e!r}); timing eager launches")
+            graph = None
+    reps = max(1, K // R) if graph is not None else K
+    t_start, t_stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    if graph is not None:
+        for _ in range(reps):
+            graph.replay()
+    else:
+        for i in range(K):
+            step(i)
+    t_stop.record()
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_stop)
+    K = reps * R if graph is not None else K
+    ms_step = total_ms / K
+    log(f"timed ({'graph' if graph is not None else 'eager'}): {ms_step * 1e3:.2f} us/step; "
+        f"indexer scoring kernel {score_ms * 1e3:.2f} us/launch")
+
+    # algorithmic bytes
+    m_, mh = wl.m, wl.m_hca
+    q_pos = host["q_pos"]
+    q_seq = np.repeat(np.arange(wl.B), np.diff(host["q_off"]))
+    P_b = np.diff(host["pool_off"])
+    Ph_b = np.diff(host["hpool_off"])
+    step_bytes = 0
+    score_bytes = 0
+    for i in range(wl.n_q):
+        b = q_seq[i]
+        t = int(q_pos[i])
+        n_vis = min((t + 1) // m_, int(P_b[b]))
+        n_hvis = min((t + 1) // mh, int(Ph_b[b]))
+        step_bytes += decode_bytes_per_query(n_vis, wl.k, wl.W, t + 1, n_hvis, wl.H, wl.d, es)
+        score_bytes += 34 * n_vis + 4 * 34 + 4 * 4
+    qps = wl.n_q / (ms_step * 1e-3)
+    gbs = step_bytes / (ms_step * 1e-3) / 1e9
+    achieved = score_bytes / (score_ms * 1e-3) / 1e9
+
+    result = {
+        "metric": METRIC,
+        "value": round(qps, 1),
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {**wl.describe(), "indexer": "mxfp4 4x64", "rotate_sets": R,
+                   "timing": "hip graph of the rotated steps, replayed" if graph is not None else "eager launches"},
+        "hbm_gbps": round(gbs, 1),
+        "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "step_bytes": int(step_bytes),
+        "roofline": {"bound": "hbm", "kernel": "k_idx_score", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None, "bytes_per_launch": int(score_bytes),
+                     "avg_launch_us": round(score_ms * 1e3, 3)},
+        "compress": compress,
+    }
+
+    # ---- prefill indexer (4096-token chunk on a 64K cache) ----------------------
+    if not args.no_prefill:
+        try:
+            result["prefill_indexer"] = bench_prefill_indexer(torch, csa, synth, to_device, log)
+        except Exception as e:  # reported, never silently replaced
+            result["prefill_indexer"] = {"error": repr(e)}
+
+    # ---- CPU oracle baseline --------------------------------------------------
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wl, host, log)
+
+    print(json.dumps(result), flush=True)
+
+
+def bench_prefill_indexer(torch, csa, synth, to_device, log, reps: int = 10):
+    wl = synth.prefill_4k_on_64k()
+    host = synth.make_inputs(wl, raw=False)
+    d = to_device({k: host[k] for k in ("qc", "qs", "w", "kc", "ks", "pool_off")})
+    batch = csa.Batch.from_host(host["tok_off"], host["q_off"], host["q_pos"])
+    max_pool = int(np.diff(host["pool_off"]).max())
+    ws = csa.Workspace()
+    idx = torch.empty((wl.n_q, wl.k), dtype=torch.int32, device="cuda")
+    call = lambda: csa.csa_index_topk(batch, d["pool_off"], max_pool, wl.m, wl.k, d["qc"], d["qs"], d["w"],
+                                      d["kc"], d["ks"], idx=idx, ws=ws)
+    call()
+    torch.cuda.synchronize()
+    ev = [(csa.HipEvent(), csa.HipEvent()) for _ in range(reps)]
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(reps):
+        csa.csa_profile_events(csa.CSA_K_IDX_SCORE, ev[i][0], ev[i][1])
+        call()
+    t1.record()
+    torch.cuda.synchronize()
+    csa.csa_profile_events(csa.CSA_K_IDX_SCORE)
+    score_ms = float(np.mean([a.elapsed_ms(b) for a, b in ev]))
+    call_ms = t0.elapsed_time(t1) / reps
+    n_vis = np.minimum((host["q_pos"] + 1) // wl.m, int(host["pool_off"][-1]))
+    flops = 2.0 * 4 * 64 * float(n_vis.sum())
+    tf = flops / (score_ms * 1e-3) / 1e12
+    log(f"prefill indexer: scoring {score_ms * 1e3:.1f} us ({tf:.1f} TFLOP/s), whole index_topk {call_ms * 1e3:.1f} us")
+    return {"workload": wl.name, "scoring_kernel_us": round(score_ms * 1e3, 2),
+            "algorithmic_flop": flops, "tflops": round(tf, 2), "peak_tflops": FP4_PEAK_TFLOPS,
+            "frac": round(tf / FP4_PEAK_TFLOPS, 5), "index_topk_us": round(call_ms * 1e3, 2),
+            "queries_per_s": round(wl.n_q / (call_ms * 1e-3), 1)}
+
+
+def cpu_baseline(wl, host, log):
+    """The oracle, as it stands, on the decode queries of the same workload
+    (one thread per query).  The oracle's fp64 HCA caches are built first and
+    not timed, as the GPU's pooled caches are not."""
+    import oracle
+    n = wl.n_q
+    seqs = np.repeat(np.arange(wl.B), np.diff(host["q_off"]))
+    scale = 1.0 / math.sqrt(wl.d)
+
+    def seq_rows(b):
+        t0, t1 = int(host["tok_off"][b]), int(host["tok_off"][b + 1])
+        return host["kv"][t0:t1], host["z"][t0:t1]
+
+    log(f"cpu baseline: building oracle HCA caches for {n} queries")
+    with ThreadPoolExecutor(max_workers=n) as ex:
+        hp = list(ex.map(lambda r: oracle.pool(*seq_rows(seqs[r]), wl.m_hca), range(n)))
+
+    def one(r):
+        b = seqs[r]
+        kv, z = seq_rows(b)
+        p0, p1 = int(host["pool_off"][b]), int(host["pool_off"][b + 1])
+        t = int(host["q_pos"][r])
+        oracle.csa_query(kv, z, host["q"][r], t, wl.m, wl.W, wl.k, scale, host["qc"][r], host["qs"][r],
+                         host["w"][r], host["kc"][p0:p1], host["ks"][p0:p1])
+        oracle.hca_query(kv, z, host["q"][r], t, wl.m_hca, wl.W_hca, scale, hpooled=hp[r])
+
+    log(f"cpu baseline: timing the oracle on {n} queries with {n} threads")
+    t = time.time()
+    with ThreadPoolExecutor(max_workers=n) as ex:
+        list(ex.map(one, range(n)))
+    dt = time.time() - t
+    log(f"cpu baseline: {dt:.2f} s")
+    return {"value": round(n / dt, 4), "unit": "queries/s", "cores": n, "kind": "oracle",
+            "sample": f"all {n} decode queries of {wl.name} (CSA: exact MXFP4 scores of every visible "
+                      f"pooled entry, full-sort top-{wl.k}, fp64 pooling of the selected blocks, attention; "
+                      f"HCA: attention over the oracle's prebuilt fp64 cache), one thread per query",
+            "seconds": round(dt, 3), "host_cpus": os.cpu_count()}
+
+
+if __name__ == "__main__":
+    main()

@@ -183,6 +183,28 @@ int hca_attn(int dtype, const csa_batch* b, const int64_t* hpool_off, int64_t ma
              const void* kv_pool_hca, const void* kv_raw, void* out, float* lse, void* ws,
              size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------------------------------
+ * csa_profile_events — tracing hook (host).  Until cleared, every launch of
+ * internal kernel `kernel_id` made by the calling thread is bracketed by
+ * hipEventRecord(start) / hipEventRecord(stop) on the launch stream, so a
+ * caller can time one kernel of a multi-kernel call with its own events.
+ * start/stop are hipEvent_t handles owned by the caller; pass NULL, NULL to
+ * clear.  Kernel ids: CSA_K_IDX_SCORE (indexer scoring), CSA_K_IDX_SELECT,
+ * CSA_K_IDX_FINAL (top-k passes), CSA_K_ATTN (attention main kernel, CSA or
+ * HCA), CSA_K_ATTN_COMBINE (split merge), CSA_K_COMPRESS.
+ * Errors: CSA_ERR_INVALID for an unknown id or exactly one NULL event.
+ * ---------------------------------------------------------------------- */
+enum {
+  CSA_K_IDX_SCORE = 0,
+  CSA_K_IDX_SELECT = 1,
+  CSA_K_IDX_FINAL = 2,
+  CSA_K_ATTN = 3,
+  CSA_K_ATTN_COMBINE = 4,
+  CSA_K_COMPRESS = 5,
+  CSA_K_COUNT = 6
+};
+int csa_profile_events(int kernel_id, void* start, void* stop);
+
 #ifdef __cplusplus
 }
 #endif

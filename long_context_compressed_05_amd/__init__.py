@@ -23,7 +23,8 @@ CSA_F32, CSA_BF16 = 0, 1
 
 EXPORTS = ("csa_status_string", "csa_last_error", "csa_compress", "csa_index_topk_workspace",
            "csa_index_topk", "csa_sparse_attn_workspace", "csa_sparse_attn", "hca_attn_workspace",
-           "hca_attn")
+           "hca_attn", "csa_profile_events")
+CSA_K_IDX_SCORE, CSA_K_IDX_SELECT, CSA_K_IDX_FINAL, CSA_K_ATTN, CSA_K_ATTN_COMBINE, CSA_K_COMPRESS = range(6)
 
 
 class CsaBatch(ctypes.Structure):
@@ -59,6 +60,7 @@ def lib():
     L.hca_attn_workspace.argtypes = [ci, bp, i64, ci, ci, ci, ctypes.POINTER(sz)]
     L.hca_attn.argtypes = [ci, bp, vp, i64, ci, ci, ci, ctypes.c_float, ci, vp, vp, vp, vp, vp, vp,
                            sz, vp]
+    L.csa_profile_events.argtypes = [ci, vp, vp]
     for name in EXPORTS:
         L[name].restype = L[name].restype if name in ("csa_status_string", "csa_last_error") else ci
     _lib = L
@@ -235,3 +237,48 @@ def hca_attn(batch: Batch, hpool_off: torch.Tensor, max_hpool: int, m_hca: int, 
                           _ptr(q), _ptr(kv_pool_hca), _ptr(kv_raw), _ptr(out), _ptr(lse), _ptr(buf),
                           nbytes, _stream(stream)), "hca_attn")
     return out, lse
+
+
+_hip = None
+
+
+def _hiplib():
+    global _hip
+    if _hip is None:
+        _hip = ctypes.CDLL("libamdhip64.so")
+        _hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        _hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        _hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        _hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+    return _hip
+
+
+class HipEvent:
+    """A plain hipEvent_t (timing enabled) for the tracing hook."""
+
+    def __init__(self):
+        h = ctypes.c_void_p()
+        rc = _hiplib().hipEventCreateWithFlags(ctypes.byref(h), 0)
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+        self.handle = h
+
+    def elapsed_ms(self, end: "HipEvent") -> float:
+        ms = ctypes.c_float()
+        _hiplib().hipEventSynchronize(end.handle)
+        rc = _hiplib().hipEventElapsedTime(ctypes.byref(ms), self.handle, end.handle)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return ms.value
+
+    def __del__(self):
+        if _hip is not None and self.handle:
+            _hip.hipEventDestroy(self.handle)
+
+
+def csa_profile_events(kernel_id: int, start: Optional[HipEvent] = None, stop: Optional[HipEvent] = None) -> None:
+    """Bracket every launch of one internal kernel (this thread) with the given
+    HipEvent pair; csa_profile_events(id) clears."""
+    sp = start.handle if start is not None else None
+    ep = stop.handle if stop is not None else None
+    _check(lib().csa_profile_events(kernel_id, sp, ep), "csa_profile_events")

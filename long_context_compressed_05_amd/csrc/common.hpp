@@ -40,4 +40,34 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// Block-wide search from the top.  Thread t holds the count c of its bin
+// range; ranges ascend with t.  Returns in *found (on every thread) the
+// thread t* whose range contains the need-th element counted from the top
+// (sum over t > t* of c < need <= sum over t >= t*), and in *above that sum
+// over t > t*.  Requires blockDim.x % 64 == 0 and total >= need.  `scratch`
+// holds at least blockDim.x / 64 + 2 words of LDS.
+__device__ __forceinline__ void block_find_from_top(uint32_t c, uint32_t need, uint32_t* scratch,
+                                                    int* found, uint32_t* above) {
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6, nw = blockDim.x >> 6;
+  uint32_t s = c;  // inclusive suffix sum within the wave
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t v = __shfl_down(s, off);
+    if (lane + off < 64) s += v;
+  }
+  if (lane == 0) scratch[wave] = s;
+  __syncthreads();
+  uint32_t higher = 0;
+  for (int w = wave + 1; w < nw; ++w) higher += scratch[w];
+  const uint32_t incl = s + higher, excl = incl - c;
+  if (excl < need && incl >= need) {
+    scratch[nw] = (uint32_t)t;
+    scratch[nw + 1] = excl;
+  }
+  __syncthreads();
+  *found = (int)scratch[nw];
+  *above = scratch[nw + 1];
+  __syncthreads();
+}
+
 }  // namespace csa

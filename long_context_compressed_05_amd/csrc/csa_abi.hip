@@ -13,6 +13,7 @@
 namespace {
 
 thread_local char g_err[512] = "";
+thread_local hipEvent_t g_prof[CSA_K_COUNT][2] = {};
 
 int fail(int status, const char* fmt, ...) {
   va_list ap;
@@ -74,7 +75,25 @@ int launched(int rc) {
 
 }  // namespace
 
+namespace csa {
+void prof_begin(int id, hipStream_t stream) {
+  if (g_prof[id][0]) (void)hipEventRecord(g_prof[id][0], stream);
+}
+void prof_end(int id, hipStream_t stream) {
+  if (g_prof[id][1]) (void)hipEventRecord(g_prof[id][1], stream);
+}
+}  // namespace csa
+
 extern "C" {
+
+int csa_profile_events(int kernel_id, void* start, void* stop) {
+  if (kernel_id < 0 || kernel_id >= CSA_K_COUNT) return fail(CSA_ERR_INVALID, "unknown kernel id %d", kernel_id);
+  if ((start == nullptr) != (stop == nullptr)) return fail(CSA_ERR_INVALID, "pass both events or neither");
+  g_prof[kernel_id][0] = (hipEvent_t)start;
+  g_prof[kernel_id][1] = (hipEvent_t)stop;
+  return CSA_OK;
+}
+
 
 const char* csa_status_string(int status) {
   switch (status) {

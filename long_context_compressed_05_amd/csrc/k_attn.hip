@@ -90,12 +90,14 @@ __device__ __forceinline__ const uint8_t* key_row(const AttnArgs& a, const RowCt
 // ---------------------------------------------------------------------------
 constexpr int kKStride = 136;  // LDS row stride (elements) of the K tile
 constexpr int kVStride = 72;   // LDS row stride (elements) of the transposed V tile
+constexpr int kMaxSplitKeys = 1024;
 
 template <int GPW>
 __global__ __launch_bounds__(256) void k_attn_bf16(AttnArgs a) {
   __shared__ __align__(16) uint16_t Ks[64 * kKStride];
   __shared__ __align__(16) uint16_t Vt[128 * kVStride];
-  __shared__ const uint8_t* rowp[64];
+  __shared__ int32_t idx_s[kMaxSplitKeys];
+  __shared__ uint8_t valid_s[64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g = lane >> 4;
   const int64_t row = blockIdx.y;
@@ -106,6 +108,23 @@ __global__ __launch_bounds__(256) void k_attn_bf16(AttnArgs a) {
   const int64_t p_end = p_begin + a.ks < list_len ? p_begin + a.ks : list_len;
   const int HG = a.H >> 4;
   constexpr size_t RB = 2 * 128 * 2;  // bytes per [2][128] bf16 row
+
+  // this split's slice of the index row, staged once
+  if (!a.hca) {
+    for (int64_t p = p_begin + tid; p < p_end && p < a.seg_a; p += 256)
+      idx_s[p - p_begin] = a.idx[row * a.seg_a + p];
+  }
+  __syncthreads();
+  auto rowptr = [&](int64_t p) -> const uint8_t* {
+    if (p >= p_end) return nullptr;
+    if (p < a.seg_a) {
+      if (a.hca) return p < c.n_vis_a ? a.kv_pool + (size_t)(c.pool_base + p) * RB : nullptr;
+      const int32_t j = idx_s[p - p_begin];
+      return j >= 0 ? a.kv_pool + (size_t)(c.pool_base + j) * RB : nullptr;
+    }
+    const int64_t u = c.t - a.W + 1 + (p - a.seg_a);
+    return u >= 0 ? a.kv_raw + (size_t)(c.tok_base + u) * RB : nullptr;
+  };
 
   // Q^T operand (B): column = head 16*hg + l16, K = dims 32*kstep + 8*g .. +7
   v8bf qf[GPW][4];
@@ -129,21 +148,17 @@ __global__ __launch_bounds__(256) void k_attn_bf16(AttnArgs a) {
     }
   }
 
-  // staging assignment: 16-byte chunk ch of key pair kp in {tid/16, tid/16 + 16}
+  // staging: 16-byte chunk ch of keys 2*kp, 2*kp+1 for kp in {tid/16, tid/16 + 16}
   const int ch = tid & 15;
-  for (int64_t p0 = p_begin; p0 < p_end; p0 += 64) {
-    if (tid < 64) {
-      const int64_t p = p0 + tid;
-      rowp[tid] = p < p_end ? key_row(a, c, row, p, RB) : nullptr;
-    }
-    __syncthreads();
-    uint4 kr[2][2], vr[2][2];
+  uint4 kr[2][2], vr[2][2];
+  bool vl[2][2];
+  auto load_tile = [&](int64_t p0) {
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
+    for (int r = 0; r < 2; ++r)
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
-        const int key = 2 * ((tid >> 4) + 16 * r) + e;
-        const uint8_t* rp = rowp[key];
+        const uint8_t* rp = rowptr(p0 + 2 * ((tid >> 4) + 16 * r) + e);
+        vl[r][e] = rp != nullptr;
         if (rp) {
           kr[r][e] = *reinterpret_cast<const uint4*>(rp + ch * 16);
           vr[r][e] = *reinterpret_cast<const uint4*>(rp + 256 + ch * 16);
@@ -152,13 +167,19 @@ __global__ __launch_bounds__(256) void k_attn_bf16(AttnArgs a) {
           vr[r][e] = make_uint4(0, 0, 0, 0);
         }
       }
-    }
+  };
+  if (p_begin < p_end) load_tile(p_begin);
+
+  for (int64_t p0 = p_begin; p0 < p_end; p0 += 64) {
+    __syncthreads();  // the previous tile's LDS reads are done
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
       const int kp = (tid >> 4) + 16 * r;
 #pragma unroll
-      for (int e = 0; e < 2; ++e)
+      for (int e = 0; e < 2; ++e) {
         *reinterpret_cast<uint4*>(&Ks[(2 * kp + e) * kKStride + ch * 8]) = kr[r][e];
+        if (ch == 0) valid_s[2 * kp + e] = vl[r][e] ? 1 : 0;
+      }
       const uint32_t v0[4] = {vr[r][0].x, vr[r][0].y, vr[r][0].z, vr[r][0].w};
       const uint32_t v1[4] = {vr[r][1].x, vr[r][1].y, vr[r][1].z, vr[r][1].w};
 #pragma unroll
@@ -171,6 +192,7 @@ __global__ __launch_bounds__(256) void k_attn_bf16(AttnArgs a) {
       }
     }
     __syncthreads();
+    if (p0 + 64 < p_end) load_tile(p0 + 64);  // next tile's loads fly during this tile's math
 
 #pragma unroll
     for (int gi = 0; gi < GPW; ++gi) {
@@ -187,10 +209,8 @@ __global__ __launch_bounds__(256) void k_attn_bf16(AttnArgs a) {
           acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[gi][kq], acc, 0, 0, 0);
         }
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const bool valid = rowp[16 * mt + 4 * g + v] != nullptr;
-          s[mt][v] = valid ? acc[v] * a.scale_log2 : -INFINITY;
-        }
+        for (int v = 0; v < 4; ++v)
+          s[mt][v] = valid_s[16 * mt + 4 * g + v] ? acc[v] * a.scale_log2 : -INFINITY;
       }
       float tmax = -INFINITY;
 #pragma unroll
@@ -200,7 +220,7 @@ __global__ __launch_bounds__(256) void k_attn_bf16(AttnArgs a) {
       tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
       const float mnew = fmaxf(m_run[gi], tmax);
-      if (mnew == -INFINITY) continue;  // nothing valid so far (uniform per head)
+      if (mnew == -INFINITY) continue;  // nothing valid so far (uniform: validity is per key)
       const float alpha = fast_exp2(m_run[gi] - mnew);
       m_run[gi] = mnew;
       float psum = 0.f;
@@ -235,7 +255,6 @@ __global__ __launch_bounds__(256) void k_attn_bf16(AttnArgs a) {
         }
       }
     }
-    __syncthreads();
   }
 
   // finish: lane (l16, g) holds head 16*hg + l16, dims 16*mt + 4*g + v
@@ -375,54 +394,83 @@ __global__ __launch_bounds__(256) void k_attn_f32(AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// log-sum-exp merge of split partials
+// log-sum-exp merge of split partials: one workgroup per (query, head), one
+// thread per output dim
 // ---------------------------------------------------------------------------
 template <bool BF16>
-__global__ __launch_bounds__(256) void k_attn_combine(const float* __restrict__ part_o,
+__global__ __launch_bounds__(128) void k_attn_combine(const float* __restrict__ part_o,
                                                       const float* __restrict__ part_ml, int splits,
                                                       int H, uint8_t* __restrict__ out,
                                                       float* __restrict__ lse) {
+  __shared__ float wsh[128];
+  __shared__ float red[2];
   const int64_t row = blockIdx.x;
-  for (int o = threadIdx.x; o < H * 128; o += 256) {
-    const int h = o >> 7, d = o & 127;
-    float M = -INFINITY;
-    for (int s = 0; s < splits; ++s) M = fmaxf(M, part_ml[((row * splits + s) * H + h) * 2]);
-    float L = 0.f, acc = 0.f;
-    if (M != -INFINITY) {
-      for (int s = 0; s < splits; ++s) {
-        const size_t base = (size_t)(row * splits + s) * H + h;
-        const float ms = part_ml[base * 2];
-        if (ms == -INFINITY) continue;
-        const float wgt = fast_exp2(ms - M);
-        L = fmaf(wgt, part_ml[base * 2 + 1], L);
-        acc = fmaf(wgt, part_o[base * 128 + d], acc);
+  const int h = blockIdx.y, d = threadIdx.x, lane = d & 63, wave = d >> 6;
+  const float* ml = part_ml + ((size_t)row * splits * H + h) * 2;  // split s at ml[s * H * 2]
+  float M = -INFINITY;
+  for (int s = d; s < splits; s += 128) M = fmaxf(M, ml[(size_t)s * H * 2]);
+  M = wave_max(M);
+  if (lane == 0) red[wave] = M;
+  __syncthreads();
+  M = fmaxf(red[0], red[1]);
+  __syncthreads();
+  float Lp = 0.f, acc = 0.f;
+  if (M != -INFINITY) {
+    for (int c0 = 0; c0 < splits; c0 += 128) {
+      const int s = c0 + d;
+      float wgt = 0.f;
+      if (s < splits) {
+        const float ms = ml[(size_t)s * H * 2];
+        wgt = ms == -INFINITY ? 0.f : fast_exp2(ms - M);
+        Lp = fmaf(wgt, ml[(size_t)s * H * 2 + 1], Lp);
       }
+      wsh[d] = wgt;
+      __syncthreads();
+      const int n = splits - c0 < 128 ? splits - c0 : 128;
+      const float* po = part_o + (((size_t)row * splits + c0) * H + h) * 128 + d;
+      const size_t stride = (size_t)H * 128;
+      int i = 0;
+      for (; i + 8 <= n; i += 8) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = po[(size_t)(i + u) * stride];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc = fmaf(wsh[i + u], v[u], acc);
+      }
+      for (; i < n; ++i) acc = fmaf(wsh[i], po[(size_t)i * stride], acc);
+      __syncthreads();
     }
-    const float v = L > 0.f ? acc / L : 0.f;
-    if (BF16) {
-      reinterpret_cast<uint16_t*>(out)[(size_t)row * H * 128 + o] = (uint16_t)f32_to_bf16(v);
-    } else {
-      reinterpret_cast<float*>(out)[(size_t)row * H * 128 + o] = v;
-    }
-    if (lse && d == 0) lse[row * H + h] = L > 0.f ? (M + __log2f(L)) * kLn2 : -INFINITY;
   }
+  // L = sum of the per-thread partial sums
+  for (int o = 32; o >= 1; o >>= 1) Lp += __shfl_xor(Lp, o);
+  if (lane == 0) red[wave] = Lp;
+  __syncthreads();
+  const float L = red[0] + red[1];
+  const float v = L > 0.f ? acc / L : 0.f;
+  const size_t o = ((size_t)row * H + h) * 128 + d;
+  if (BF16) reinterpret_cast<uint16_t*>(out)[o] = (uint16_t)f32_to_bf16(v);
+  else reinterpret_cast<float*>(out)[o] = v;
+  if (lse && d == 0) lse[row * H + h] = L > 0.f ? (M + __log2f(L)) * kLn2 : -INFINITY;
 }
 
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
 AttnPlan plan_attn(int64_t n_q, int64_t list_len, int H) {
+  // aim for ~256 workgroups, at least 128 list positions per split (the
+  // partial (m, l, o) of a split costs as much as 64 bf16 KV rows), and at
+  // most kMaxSplitKeys positions per split (the staged index slice)
   AttnPlan p;
-  const int64_t max_splits_tile = (list_len + 63) / 64;
-  const int64_t max_splits_amort = (list_len + 255) / 256;  // >= 256 keys per partial
-  int64_t want = n_q > 0 ? (1024 + n_q - 1) / n_q : 1;
-  int64_t s = want;
-  if (s > max_splits_amort) s = max_splits_amort;
-  if (s > max_splits_tile) s = max_splits_tile;
+  const int64_t s_min = (list_len + kMaxSplitKeys - 1) / kMaxSplitKeys;
+  const int64_t s_max = (list_len + 127) / 128;
+  int64_t s = n_q > 0 ? (256 + n_q - 1) / n_q : 1;
+  if (s > s_max) s = s_max;
+  if (s < s_min) s = s_min;
   if (s < 1) s = 1;
   int64_t ks = (list_len + s - 1) / s;
   ks = ((ks + 63) / 64) * 64;
   if (ks < 64) ks = 64;
+  if (ks > kMaxSplitKeys) ks = kMaxSplitKeys;
   s = (list_len + ks - 1) / ks;
   if (s < 1) s = 1;
   p.splits = (int)s;
@@ -452,19 +500,24 @@ int launch_attn(bool bf16, bool hca, int n_seq, int64_t n_q, const int64_t* tok_
     a.splits = 1;
   }
   dim3 grid((unsigned)a.splits, (unsigned)n_q);
+  prof_begin(3, stream);
   if (bf16) {
     if (H > 64) hipLaunchKernelGGL(k_attn_bf16<2>, grid, dim3(256), 0, stream, a);
     else hipLaunchKernelGGL(k_attn_bf16<1>, grid, dim3(256), 0, stream, a);
   } else {
     hipLaunchKernelGGL(k_attn_f32, grid, dim3(256), 0, stream, a);
   }
+  prof_end(3, stream);
   if (a.splits > 1) {
+    prof_begin(4, stream);
+    dim3 gc((unsigned)n_q, (unsigned)H);
     if (bf16)
-      hipLaunchKernelGGL(k_attn_combine<true>, dim3((unsigned)n_q), dim3(256), 0, stream, a.part_o,
-                         a.part_ml, a.splits, H, a.out, lse);
+      hipLaunchKernelGGL(k_attn_combine<true>, gc, dim3(128), 0, stream, a.part_o, a.part_ml, a.splits, H,
+                         a.out, lse);
     else
-      hipLaunchKernelGGL(k_attn_combine<false>, dim3((unsigned)n_q), dim3(256), 0, stream, a.part_o,
-                         a.part_ml, a.splits, H, a.out, lse);
+      hipLaunchKernelGGL(k_attn_combine<false>, gc, dim3(128), 0, stream, a.part_o, a.part_ml, a.splits, H,
+                         a.out, lse);
+    prof_end(4, stream);
   }
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }

@@ -18,13 +18,15 @@
 //
 // Selection is a radix select on those 32-bit keys:
 //   1. k_idx_score: keys to the workspace + a 4096-bin histogram of the top
-//      13 key bits per query (LDS, merged into global memory); the last
+//      13 key bits per query (LDS, merged into one of `nrep` global replicas
+//      picked by workgroup id, i.e. per XCD, to spread the atomics); the last
 //      workgroup of a query tile finds the threshold bin b1;
 //   2. k_idx_select: entries above b1 are selected outright, entries in b1
 //      become candidates;
 //   3. k_idx_final: exact k-th key K* among the candidates, then the lowest
-//      indices among entries equal to K*, then an ascending sort of the k
-//      selected indices.  It also returns the workspace to all-zero.
+//      indices among entries equal to K*, then the ascending index order
+//      (an LDS bitmap of the visible range, or a bitonic sort when the range
+//      is too large for LDS).  It also returns the workspace to all-zero.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -35,42 +37,36 @@ constexpr int kBinShift = 19;
 constexpr int kScoreIter = 8;                       // 32-key MFMA groups per wave
 constexpr int kScoreChunk = 4 * 32 * kScoreIter;    // keys per score workgroup
 constexpr int kSelChunk = 4096;                     // keys per select workgroup
+constexpr int kSelPerThread = kSelChunk / 256;
 constexpr uint32_t kNoBin = 0xffffffffu;
-
-__device__ __forceinline__ uint32_t ld_acquire(const uint32_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
+constexpr int kBitmapMaxBytes = 64 * 1024;         // LDS bitmap of the visible range
+constexpr int kCandLds = 4096;                     // candidates staged in LDS (else read from L2)
 
 __device__ __forceinline__ int64_t n_visible(int64_t t, int m, int64_t P) {
   int64_t v = (t + 1) / m;
   return v < P ? v : P;
 }
 
-// Threshold bin of one query: the bin b1 with count(bin > b1) < need <= count(bin >= b1).
-// Called by a whole 256-thread block; hist is read with device-coherent loads.
-__device__ void find_threshold(const uint32_t* hist, uint32_t need, uint32_t* info_out) {
-  __shared__ uint32_t part[256];
-  __shared__ uint32_t res[2];
+// Threshold bin of one query over `nrep` histogram replicas: the bin b1 with
+// count(bin > b1) < need <= count(bin >= b1).  Whole 256-thread block.
+__device__ void find_threshold(const uint32_t* hist, int nrep, uint32_t need, uint32_t* info_out) {
+  __shared__ uint32_t scratch[8];
   const int t = threadIdx.x;
   uint32_t loc[16];
-  uint32_t s = 0;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) { loc[i] = ld_acquire(hist + t * 16 + i); s += loc[i]; }
-  part[t] = s;
-  __syncthreads();
-  if (t == 0) {
-    uint32_t cum = 0;
-    int tt = 255;
-    for (; tt >= 0; --tt) {
-      if (cum + part[tt] >= need) break;
-      cum += part[tt];
-    }
-    res[0] = (uint32_t)tt;  // thread holding the crossing (tt >= 0 since total >= need)
-    res[1] = cum;           // count above that thread's bins
+  for (int i = 0; i < 16; ++i) loc[i] = 0;
+  for (int r = 0; r < nrep; ++r) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) loc[i] += hist[r * kNBins + t * 16 + i];
   }
-  __syncthreads();
-  if (t == (int)res[0]) {
-    uint32_t cum = res[1];
+  uint32_t c = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) c += loc[i];
+  int tstar;
+  uint32_t above;
+  block_find_from_top(c, need, scratch, &tstar, &above);
+  if (t == tstar) {
+    uint32_t cum = above;
     int bi = 15;
     for (; bi > 0; --bi) {
       if (cum + loc[bi] >= need) break;
@@ -86,7 +82,7 @@ struct ScoreArgs {
   const int64_t* q_off;
   const int64_t* q_pos;
   const int64_t* pool_off;
-  int n_seq, tiles_per_seq, qt, m, k;
+  int n_seq, tiles_per_seq, qt, m, nrep;
   int64_t max_pool;
   const uint8_t* q_codes;
   const uint8_t* q_scales;
@@ -95,14 +91,11 @@ struct ScoreArgs {
   const uint8_t* k_scales;
   uint32_t* keys;
   uint32_t* hist;
-  uint32_t* counts;
-  uint32_t* info;
 };
 
 __global__ __launch_bounds__(256) void k_idx_score(ScoreArgs a) {
   extern __shared__ uint32_t lhist[];  // qt * kNBins/2 words, two 16-bit counters per word
   __shared__ int64_t nvis_s[8];
-  __shared__ int is_last;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int tile = blockIdx.y;
   const int b = tile / a.tiles_per_seq;
@@ -170,31 +163,32 @@ __global__ __launch_bounds__(256) void k_idx_score(ScoreArgs a) {
     }
   }
   __syncthreads();
+  const int rep = (int)((blockIdx.x + (int64_t)gridDim.x * blockIdx.y) % a.nrep);
   for (int r = 0; r < nrows; ++r) {
-    uint32_t* gh = a.hist + (row0 + r) * kNBins;
+    uint32_t* gh = a.hist + ((row0 + r) * a.nrep + rep) * kNBins;
     for (int wi = tid; wi < kNBins / 2; wi += 256) {
       const uint32_t v = lhist[r * (kNBins / 2) + wi];
       if (v & 0xffffu) atomicAdd(gh + 2 * wi, v & 0xffffu);
       if (v >> 16) atomicAdd(gh + 2 * wi + 1, v >> 16);
     }
   }
-  // the last workgroup of this query tile computes the threshold bins
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) is_last = (atomicAdd(a.counts + row0 * 4 + 2, 1u) == gridDim.x - 1);
-  __syncthreads();
-  if (!is_last) return;
-  __threadfence();
-  for (int r = 0; r < nrows; ++r) {
-    const int64_t kk = nvis_s[r] < a.k ? nvis_s[r] : a.k;
-    uint32_t* info = a.info + (row0 + r) * 2;
-    if (kk == 0) {
-      if (tid == 0) { info[0] = kNoBin; info[1] = 0; }
-      continue;
-    }
-    find_threshold(a.hist + (row0 + r) * kNBins, (uint32_t)kk, info);
+}
+
+// threshold bin of every query (one workgroup per query); runs after the
+// scoring kernel so its histogram merges are complete and visible
+__global__ __launch_bounds__(256) void k_idx_threshold(const int64_t* q_off, const int64_t* q_pos,
+                                                       const int64_t* pool_off, int n_seq, int m, int k,
+                                                       int nrep, const uint32_t* hist, uint32_t* info) {
+  const int64_t row = blockIdx.x;
+  const int b = seq_of_row(q_off, n_seq, row);
+  const int64_t P = pool_off[b + 1] - pool_off[b];
+  const int64_t nvis = n_visible(q_pos[row], m, P);
+  const int64_t kk = nvis < k ? nvis : k;
+  if (kk == 0) {
+    if (threadIdx.x == 0) { info[row * 2] = kNoBin; info[row * 2 + 1] = 0; }
+    return;
   }
-  if (tid == 0) a.counts[row0 * 4 + 2] = 0;
+  find_threshold(hist + row * nrep * kNBins, nrep, (uint32_t)kk, info + row * 2);
 }
 
 struct SelectArgs {
@@ -221,25 +215,47 @@ __global__ __launch_bounds__(256) void k_idx_select(SelectArgs a) {
   if (j0 >= nvis) return;
   const int lane = threadIdx.x & 63;
   const uint32_t* keys = a.keys + row * a.max_pool;
-  for (int i = 0; i < kSelChunk / 256; ++i) {
+  uint32_t kv[kSelPerThread];
+#pragma unroll
+  for (int i = 0; i < kSelPerThread; ++i) {  // all loads first
     const int64_t j = j0 + i * 256 + threadIdx.x;
-    uint32_t key = 0, bin = 0;
+    kv[i] = j < nvis ? keys[j] : 0u;
+  }
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  // pass 1: per-wave counts; one atomic per list per workgroup
+  __shared__ uint32_t wcount[2][4], wbase[2];
+  uint32_t ng = 0, ne = 0;
+#pragma unroll
+  for (int i = 0; i < kSelPerThread; ++i) {
+    const int64_t j = j0 + i * 256 + threadIdx.x;
     const bool ok = j < nvis;
-    if (ok) { key = keys[j]; bin = key >> kBinShift; }
+    const uint32_t bin = kv[i] >> kBinShift;
+    ng += (uint32_t)__popcll(__ballot(ok && bin > b1));
+    ne += (uint32_t)__popcll(__ballot(ok && bin == b1));
+  }
+  const int wave = threadIdx.x >> 6;
+  if (lane == 0) { wcount[0][wave] = ng; wcount[1][wave] = ne; }
+  __syncthreads();
+  if (threadIdx.x < 2) {
+    const uint32_t tot = wcount[threadIdx.x][0] + wcount[threadIdx.x][1] + wcount[threadIdx.x][2] +
+                         wcount[threadIdx.x][3];
+    wbase[threadIdx.x] = tot ? atomicAdd(a.counts + row * 4 + threadIdx.x, tot) : 0u;
+  }
+  __syncthreads();
+  uint32_t pg = wbase[0], pe = wbase[1];
+  for (int w = 0; w < wave; ++w) { pg += wcount[0][w]; pe += wcount[1][w]; }
+  // pass 2: write in the same order
+#pragma unroll
+  for (int i = 0; i < kSelPerThread; ++i) {
+    const int64_t j = j0 + i * 256 + threadIdx.x;
+    const bool ok = j < nvis;
+    const uint32_t bin = kv[i] >> kBinShift;
     const bool gt = ok && bin > b1, eq = ok && bin == b1;
     const uint64_t mg = __ballot(gt), me = __ballot(eq);
-    const int first = __ffsll((unsigned long long)(mg | me)) - 1;
-    if (first < 0) continue;
-    uint32_t base_g = 0, base_e = 0;
-    if (lane == first) {
-      if (mg) base_g = atomicAdd(a.counts + row * 4 + 0, (uint32_t)__popcll(mg));
-      if (me) base_e = atomicAdd(a.counts + row * 4 + 1, (uint32_t)__popcll(me));
-    }
-    base_g = __shfl(base_g, first);
-    base_e = __shfl(base_e, first);
-    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    if (gt) a.def[row * a.k + base_g + __popcll(mg & below)] = (int32_t)j;
-    if (eq) a.cand[row * a.max_pool + base_e + __popcll(me & below)] = make_uint2(key, (uint32_t)j);
+    if (gt) a.def[row * a.k + pg + __popcll(mg & below)] = (int32_t)j;
+    if (eq) a.cand[row * a.max_pool + pe + __popcll(me & below)] = make_uint2(kv[i], (uint32_t)j);
+    pg += (uint32_t)__popcll(mg);
+    pe += (uint32_t)__popcll(me);
   }
 }
 
@@ -247,7 +263,7 @@ struct FinalArgs {
   const int64_t* q_off;
   const int64_t* q_pos;
   const int64_t* pool_off;
-  int n_seq, m, k;
+  int n_seq, m, k, nrep, use_bitmap;
   int64_t max_pool;
   uint32_t* counts;
   uint32_t* hist;
@@ -256,48 +272,44 @@ struct FinalArgs {
   int32_t* idx;
 };
 
-// need-th largest value among the active candidates, 8 bits per round.
-// Returns the exact value; *need_left = how many entries equal to it are to be taken.
+// need-th largest value among the active candidates, 8 bits per round, all
+// threads of the block.  Returns the exact value; *need_left = how many of the
+// entries equal to it are to be taken.
 template <typename ValueFn, typename ActiveFn>
-__device__ uint32_t radix_select_desc(int64_t n, uint32_t need, ValueFn val, ActiveFn active,
+__device__ uint32_t radix_select_desc(uint32_t n, uint32_t need, ValueFn val, ActiveFn active,
                                       uint32_t* need_left) {
   __shared__ uint32_t bins[256];
-  __shared__ uint32_t sh[2];
+  __shared__ uint32_t scratch[24];
   uint32_t prefix = 0, pmask = 0;
   for (int shift = 24; shift >= 0; shift -= 8) {
     for (int i = threadIdx.x; i < 256; i += blockDim.x) bins[i] = 0;
     __syncthreads();
-    for (int64_t i = threadIdx.x; i < n; i += blockDim.x) {
+    for (uint32_t i = threadIdx.x; i < n; i += blockDim.x) {
       if (!active(i)) continue;
       const uint32_t v = val(i);
       if ((v & pmask) == prefix) atomicAdd(&bins[(v >> shift) & 255u], 1u);
     }
     __syncthreads();
-    if (threadIdx.x == 0) {
-      uint32_t cum = 0;
-      int d = 255;
-      for (; d > 0; --d) {
-        if (cum + bins[d] >= need) break;
-        cum += bins[d];
-      }
-      sh[0] = (uint32_t)d;
-      sh[1] = need - cum;
-    }
-    __syncthreads();
-    prefix |= sh[0] << shift;
+    const uint32_t c = threadIdx.x < 256 ? bins[threadIdx.x] : 0u;
+    int d;
+    uint32_t above;
+    block_find_from_top(c, need, scratch, &d, &above);
+    prefix |= (uint32_t)d << shift;
     pmask |= 255u << shift;
-    need = sh[1];
-    __syncthreads();
+    need -= above;
   }
   *need_left = need;
   return prefix;
 }
 
 __global__ __launch_bounds__(1024) void k_idx_final(FinalArgs a) {
+  extern __shared__ uint32_t bitmap[];  // ceil(max_pool / 32) words when use_bitmap
   __shared__ int32_t outj[4096];
+  __shared__ uint2 cand_s[kCandLds];
   __shared__ uint32_t n_out;
+  __shared__ uint32_t scan_scratch[24];
   const int64_t row = blockIdx.x;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int b = seq_of_row(a.q_off, a.n_seq, row);
   const int64_t P = a.pool_off[b + 1] - a.pool_off[b];
   const int64_t nvis = n_visible(a.q_pos[row], a.m, P);
@@ -308,55 +320,110 @@ __global__ __launch_bounds__(1024) void k_idx_final(FinalArgs a) {
     const uint32_t n_c = a.counts[row * 4 + 1];
     const uint32_t need = (uint32_t)k_eff - n_def;  // >= 1 by the choice of b1
     const uint2* cand = a.cand + row * a.max_pool;
+    if (n_c <= (uint32_t)kCandLds) {  // stage the candidates once
+      for (uint32_t i = tid; i < n_c; i += blockDim.x) cand_s[i] = cand[i];
+      __syncthreads();
+      cand = cand_s;
+    }
     uint32_t r;
     const uint32_t kstar = radix_select_desc(
-        n_c, need, [&](int64_t i) { return cand[i].x; }, [&](int64_t) { return true; }, &r);
+        n_c, need, [&](uint32_t i) { return cand[i].x; }, [&](uint32_t) { return true; }, &r);
     uint32_t r2;
     const uint32_t jstar = radix_select_desc(
-        n_c, r, [&](int64_t i) { return ~cand[i].y; }, [&](int64_t i) { return cand[i].x == kstar; },
+        n_c, r, [&](uint32_t i) { return ~cand[i].y; }, [&](uint32_t i) { return cand[i].x == kstar; },
         &r2);
-    if (tid == 0) n_out = n_def;
-    for (uint32_t i = tid; i < n_def; i += blockDim.x) outj[i] = a.def[row * a.k + i];
-    __syncthreads();
-    for (uint32_t i = tid; i < n_c; i += blockDim.x) {
-      const uint2 c = cand[i];
-      if (c.x > kstar || (c.x == kstar && ~c.y >= jstar)) outj[atomicAdd(&n_out, 1u)] = (int32_t)c.y;
-    }
-    __syncthreads();
-    // bitonic sort of outj[0..k_eff) ascending, padded to a power of two
-    int N = 1;
-    while (N < k_eff) N <<= 1;
-    for (int i = k_eff + tid; i < N; i += blockDim.x) outj[i] = 0x7fffffff;
-    __syncthreads();
-    for (int size = 2; size <= N; size <<= 1) {
-      for (int stride = size >> 1; stride > 0; stride >>= 1) {
-        for (int i = tid; i < N / 2; i += blockDim.x) {
-          const int lo = 2 * i - (i & (stride - 1));
-          const int hi = lo + stride;
-          const bool up = ((lo & size) == 0);
-          const int32_t x = outj[lo], y = outj[hi];
-          if ((x > y) == up) { outj[lo] = y; outj[hi] = x; }
-        }
-        __syncthreads();
+    auto chosen = [&](uint2 c) { return c.x > kstar || (c.x == kstar && ~c.y >= jstar); };
+    if (a.use_bitmap) {
+      // ascending order from a bitmap of the visible range
+      const int nwords = (int)((nvis + 31) >> 5);
+      for (int i = tid; i < nwords; i += blockDim.x) bitmap[i] = 0;
+      __syncthreads();
+      for (uint32_t i = tid; i < n_def; i += blockDim.x) {
+        const int32_t j = a.def[row * a.k + i];
+        atomicOr(&bitmap[j >> 5], 1u << (j & 31));
       }
+      for (uint32_t i = tid; i < n_c; i += blockDim.x) {
+        const uint2 c = cand[i];
+        if (chosen(c)) atomicOr(&bitmap[c.y >> 5], 1u << (c.y & 31));
+      }
+      __syncthreads();
+      const int wpt = (nwords + (int)blockDim.x - 1) / (int)blockDim.x;
+      const int w0 = tid * wpt;
+      uint32_t cnt = 0;
+      for (int i = 0; i < wpt; ++i)
+        if (w0 + i < nwords) cnt += __popc(bitmap[w0 + i]);
+      // block exclusive prefix of cnt
+      uint32_t incl = cnt;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t v = __shfl_up(incl, off);
+        if (lane >= off) incl += v;
+      }
+      if (lane == 63) scan_scratch[wave] = incl;
+      __syncthreads();
+      uint32_t lower = 0;
+      for (int w = 0; w < wave; ++w) lower += scan_scratch[w];
+      uint32_t pos = lower + incl - cnt;
+      for (int i = 0; i < wpt; ++i) {
+        if (w0 + i >= nwords) break;
+        uint32_t bits = bitmap[w0 + i];
+        while (bits) {
+          const int bpos = __ffs(bits) - 1;
+          bits &= bits - 1;
+          idx[pos++] = (w0 + i) * 32 + bpos;
+        }
+      }
+    } else {
+      if (tid == 0) n_out = n_def;
+      for (uint32_t i = tid; i < n_def; i += blockDim.x) outj[i] = a.def[row * a.k + i];
+      __syncthreads();
+      for (uint32_t i = tid; i < n_c; i += blockDim.x) {
+        const uint2 c = cand[i];
+        if (chosen(c)) outj[atomicAdd(&n_out, 1u)] = (int32_t)c.y;
+      }
+      __syncthreads();
+      // bitonic sort of outj[0..k_eff) ascending, padded to a power of two
+      int N = 1;
+      while (N < k_eff) N <<= 1;
+      for (int i = k_eff + tid; i < N; i += blockDim.x) outj[i] = 0x7fffffff;
+      __syncthreads();
+      for (int size = 2; size <= N; size <<= 1) {
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+          for (int i = tid; i < N / 2; i += blockDim.x) {
+            const int lo = 2 * i - (i & (stride - 1));
+            const int hi = lo + stride;
+            const bool up = ((lo & size) == 0);
+            const int32_t x = outj[lo], y = outj[hi];
+            if ((x > y) == up) { outj[lo] = y; outj[hi] = x; }
+          }
+          __syncthreads();
+        }
+      }
+      for (int i = tid; i < k_eff; i += blockDim.x) idx[i] = outj[i];
     }
-    for (int i = tid; i < k_eff; i += blockDim.x) idx[i] = outj[i];
   }
   for (int i = k_eff + tid; i < a.k; i += blockDim.x) idx[i] = -1;
   // return this query's workspace rows to zero for the next call
-  for (int i = tid; i < kNBins; i += blockDim.x) a.hist[row * kNBins + i] = 0;
+  uint32_t* h = a.hist + row * a.nrep * kNBins;
+  for (int i = tid; i < a.nrep * kNBins; i += blockDim.x) h[i] = 0;
   if (tid < 2) a.counts[row * 4 + tid] = 0;
 }
 
+static int hist_replicas(int64_t n_q, int64_t max_pool) {
+  const int64_t chunks = (max_pool + kScoreChunk - 1) / kScoreChunk;
+  return (chunks >= 32 && n_q <= 256) ? 8 : 1;
+}
+
 size_t index_ws_bytes(int64_t n_q, int64_t max_pool, int k) {
+  const int nrep = hist_replicas(n_q, max_pool);
   size_t s = 0;
   auto add = [&](size_t bytes) { s += (bytes + 255) & ~(size_t)255; };
-  add((size_t)n_q * kNBins * 4);        // hist (zero invariant)
-  add((size_t)n_q * 4 * 4);             // counts (zero invariant)
-  add((size_t)n_q * 2 * 4);             // info
-  add((size_t)n_q * max_pool * 4);      // keys
-  add((size_t)n_q * k * 4);             // def
-  add((size_t)n_q * max_pool * 8);      // cand
+  add((size_t)n_q * nrep * kNBins * 4);  // hist replicas (zero invariant)
+  add((size_t)n_q * 4 * 4);              // counts (zero invariant)
+  add((size_t)n_q * 2 * 4);              // info
+  add((size_t)n_q * max_pool * 4);       // keys
+  add((size_t)n_q * k * 4);              // def
+  add((size_t)n_q * max_pool * 8);       // cand
   return s;
 }
 
@@ -365,9 +432,10 @@ int launch_index_topk(int n_seq, int64_t n_q, int64_t max_q_per_seq, const int64
                       int k, const uint8_t* q_codes, const uint8_t* q_scales, const float* w,
                       const uint8_t* k_codes, const uint8_t* k_scales, int32_t* idx, void* ws,
                       hipStream_t stream) {
+  const int nrep = hist_replicas(n_q, max_pool);
   uint8_t* p = (uint8_t*)ws;
   auto take = [&](size_t bytes) { uint8_t* r = p; p += (bytes + 255) & ~(size_t)255; return r; };
-  uint32_t* hist = (uint32_t*)take((size_t)n_q * kNBins * 4);
+  uint32_t* hist = (uint32_t*)take((size_t)n_q * nrep * kNBins * 4);
   uint32_t* counts = (uint32_t*)take((size_t)n_q * 4 * 4);
   uint32_t* info = (uint32_t*)take((size_t)n_q * 2 * 4);
   uint32_t* keys = (uint32_t*)take((size_t)n_q * max_pool * 4);
@@ -377,17 +445,33 @@ int launch_index_topk(int n_seq, int64_t n_q, int64_t max_q_per_seq, const int64
 
   const int qt = max_q_per_seq > 1 ? 8 : 1;
   const int tiles_per_seq = (int)((max_q_per_seq + qt - 1) / qt);
-  ScoreArgs sa{q_off, q_pos, pool_off, n_seq, tiles_per_seq, qt, m, k, max_pool, q_codes,
-               q_scales, w, k_codes, k_scales, keys, hist, counts, info};
+  ScoreArgs sa{q_off, q_pos, pool_off, n_seq, tiles_per_seq, qt, m, nrep, max_pool, q_codes,
+               q_scales, w, k_codes, k_scales, keys, hist};
   dim3 g1((unsigned)((max_pool + kScoreChunk - 1) / kScoreChunk), (unsigned)(n_seq * tiles_per_seq));
   if (g1.x == 0) g1.x = 1;
+  prof_begin(0, stream);
   hipLaunchKernelGGL(k_idx_score, g1, dim3(256), (size_t)qt * (kNBins / 2) * 4, stream, sa);
+  prof_end(0, stream);
+  hipLaunchKernelGGL(k_idx_threshold, dim3((unsigned)n_q), dim3(256), 0, stream, q_off, q_pos, pool_off,
+                     n_seq, m, k, nrep, (const uint32_t*)hist, info);
   SelectArgs se{q_off, q_pos, pool_off, n_seq, m, k, max_pool, keys, info, counts, def, cand};
   dim3 g2((unsigned)((max_pool + kSelChunk - 1) / kSelChunk), (unsigned)n_q);
   if (g2.x == 0) g2.x = 1;
+  prof_begin(1, stream);
   hipLaunchKernelGGL(k_idx_select, g2, dim3(256), 0, stream, se);
-  FinalArgs fa{q_off, q_pos, pool_off, n_seq, m, k, max_pool, counts, hist, def, cand, idx};
-  hipLaunchKernelGGL(k_idx_final, dim3((unsigned)n_q), dim3(1024), 0, stream, fa);
+  prof_end(1, stream);
+  const size_t bm_bytes = (size_t)((max_pool + 31) / 32) * 4;
+  const int use_bitmap = bm_bytes <= (size_t)kBitmapMaxBytes ? 1 : 0;
+  FinalArgs fa{q_off, q_pos, pool_off, n_seq, m, k, nrep, use_bitmap, max_pool, counts, hist, def, cand, idx};
+  static bool lds_attr_set = false;  // allow the bitmap beyond the default dynamic LDS limit
+  if (!lds_attr_set) {
+    (void)hipFuncSetAttribute((const void*)k_idx_final, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              kBitmapMaxBytes);
+    lds_attr_set = true;
+  }
+  prof_begin(2, stream);
+  hipLaunchKernelGGL(k_idx_final, dim3((unsigned)n_q), dim3(1024), use_bitmap ? bm_bytes : 0, stream, fa);
+  prof_end(2, stream);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

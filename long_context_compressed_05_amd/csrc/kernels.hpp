@@ -6,6 +6,10 @@
 
 namespace csa {
 
+// tracing hook: events recorded around one internal kernel (thread-local)
+void prof_begin(int kernel_id, hipStream_t stream);
+void prof_end(int kernel_id, hipStream_t stream);
+
 int launch_compress(bool bf16, int n_seq, const int64_t* tok_off, const int64_t* pool_off,
                     int64_t max_len, int m, int width, const void* x, const void* z, void* out,
                     hipStream_t stream);

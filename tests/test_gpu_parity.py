@@ -201,3 +201,24 @@ def test_deterministic_repeat():
     _, b = _run_path(wl, host)
     for x, y in zip(a, b):
         assert np.array_equal(x, y)
+
+
+@pytest.mark.parametrize("lengths,k,codeset", [
+    ([160001, 200003, 150002], 1000, synth.E2M1_ALL_CODES),   # 8 histogram replicas, bitmap ordering
+    ([160001, 200003], 777, synth.E2M1_TIE_CODES),             # the same with heavy ties
+    ([3200003], 4096, synth.E2M1_ALL_CODES),                   # visible range beyond the LDS bitmap: bitonic
+])
+def test_index_topk_large_ranges(lengths, k, codeset):
+    csa = _lib()
+    wl = small_wl("index_large", lengths, [1] * len(lengths), k=k, codeset=codeset, seed=31)
+    host = synth.make_inputs(wl, raw=False)
+    from long_context_compressed_05_amd.step import to_device
+    d = to_device({kk: host[kk] for kk in ("qc", "qs", "w", "kc", "ks", "pool_off")})
+    batch = csa.Batch.from_host(host["tok_off"], host["q_off"], host["q_pos"])
+    max_pool = int(np.diff(host["pool_off"]).max())
+    idx = csa.csa_index_topk(batch, d["pool_off"], max_pool, wl.m, wl.k, d["qc"], d["qs"], d["w"], d["kc"], d["ks"])
+    got = P.torch_to_np(idx)
+    seqs = P.row_seq(host)
+    for row in range(wl.n_q):
+        want = P.oracle_topk_row(host, wl, row, seqs[row], wl.k, wl.m)
+        assert np.array_equal(got[row], want), f"row {row}"
