@@ -184,6 +184,41 @@ int hca_attn(int dtype, const csa_batch* b, const int64_t* hpool_off, int64_t ma
              size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * csa_hca_decode — one decode step of a CSA + HCA layer in ONE launch:
+ * csa_index_topk, csa_sparse_attn and hca_attn of the same arguments, fused
+ * into a single persistent (cooperatively launched) kernel so that the HCA
+ * stream overlaps the top-k chain and no launch gaps separate the stages.
+ * Same definitions and outputs as the three separate calls (pages as cited
+ * there); bit-identical top-k.  Decode batches only: one query per sequence
+ * (n_q == n_seq, q_off[b] == b), bf16, H % 16 == 0 and H <= 64, d = 128,
+ * indexer 4 x 64, max_pool <= 262144, at most 64 queries; otherwise
+ * CSA_ERR_UNSUPPORTED (use the separate calls).
+ *   kv_pool [sum P][2][d] (block m), kv_pool_hca [sum P'][2][d] (block m_hca),
+ *   kv_raw [sum L][2][d]; idx [n_q][k]; csa_out/hca_out [n_q][H][d] bf16;
+ *   csa_lse/hca_lse [n_q][H] fp32 or NULL.
+ *   ws: >= csa_hca_decode_workspace() bytes, ZERO-FILLED before first use and
+ *       left zero-filled by every launch; re-zero it when the shapes change.
+ * The kernel's internal waits are bounded: if one ever times out (not seen
+ * with co-resident workgroups) the step's outputs are invalid and an error
+ * word in ws is set, which csa_hca_decode_check() reports.
+ * ---------------------------------------------------------------------- */
+int csa_hca_decode_workspace(const csa_batch* b, int64_t max_pool, int64_t max_hpool, int H, int d,
+                             int k, int W, int W_hca, size_t* bytes);
+int csa_hca_decode(const csa_batch* b, const int64_t* pool_off, int64_t max_pool,
+                   const int64_t* hpool_off, int64_t max_hpool, int m, int m_hca, int H, int d,
+                   float scale, int k, int W, int W_hca, const uint8_t* q_codes,
+                   const uint8_t* q_scales, const float* w, const uint8_t* k_codes,
+                   const uint8_t* k_scales, const void* q, const void* kv_pool,
+                   const void* kv_pool_hca, const void* kv_raw, int32_t* idx, void* csa_out,
+                   float* csa_lse, void* hca_out, float* hca_lse, void* ws, size_t ws_bytes,
+                   void* stream);
+
+/* Synchronises `stream`, then returns CSA_OK if no csa_hca_decode launch on
+ * workspace `ws` hit its wait bound since the last check, else
+ * CSA_ERR_DEVICE; clears the word.  (The only synchronising call.) */
+int csa_hca_decode_check(const csa_batch* b, const void* ws, void* stream);
+
+/* ------------------------------------------------------------------------
  * csa_profile_events — tracing hook (host).  Until cleared, every launch of
  * internal kernel `kernel_id` made by the calling thread is bracketed by
  * hipEventRecord(start) / hipEventRecord(stop) on the launch stream, so a
@@ -191,7 +226,7 @@ int hca_attn(int dtype, const csa_batch* b, const int64_t* hpool_off, int64_t ma
  * start/stop are hipEvent_t handles owned by the caller; pass NULL, NULL to
  * clear.  Kernel ids: CSA_K_IDX_SCORE (indexer scoring), CSA_K_IDX_SELECT,
  * CSA_K_IDX_FINAL (top-k passes), CSA_K_ATTN (attention main kernel, CSA or
- * HCA), CSA_K_ATTN_COMBINE (split merge), CSA_K_COMPRESS.
+ * HCA), CSA_K_ATTN_COMBINE (split merge), CSA_K_COMPRESS, CSA_K_FUSED.
  * Errors: CSA_ERR_INVALID for an unknown id or exactly one NULL event.
  * ---------------------------------------------------------------------- */
 enum {
@@ -201,7 +236,8 @@ enum {
   CSA_K_ATTN = 3,
   CSA_K_ATTN_COMBINE = 4,
   CSA_K_COMPRESS = 5,
-  CSA_K_COUNT = 6
+  CSA_K_FUSED = 6,
+  CSA_K_COUNT = 7
 };
 int csa_profile_events(int kernel_id, void* start, void* stop);
 

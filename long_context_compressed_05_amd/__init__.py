@@ -23,8 +23,10 @@ CSA_F32, CSA_BF16 = 0, 1
 
 EXPORTS = ("csa_status_string", "csa_last_error", "csa_compress", "csa_index_topk_workspace",
            "csa_index_topk", "csa_sparse_attn_workspace", "csa_sparse_attn", "hca_attn_workspace",
-           "hca_attn", "csa_profile_events")
-CSA_K_IDX_SCORE, CSA_K_IDX_SELECT, CSA_K_IDX_FINAL, CSA_K_ATTN, CSA_K_ATTN_COMBINE, CSA_K_COMPRESS = range(6)
+           "hca_attn", "csa_hca_decode_workspace", "csa_hca_decode", "csa_hca_decode_check",
+           "csa_profile_events")
+(CSA_K_IDX_SCORE, CSA_K_IDX_SELECT, CSA_K_IDX_FINAL, CSA_K_ATTN, CSA_K_ATTN_COMBINE, CSA_K_COMPRESS,
+ CSA_K_FUSED) = range(7)
 
 
 class CsaBatch(ctypes.Structure):
@@ -60,6 +62,10 @@ def lib():
     L.hca_attn_workspace.argtypes = [ci, bp, i64, ci, ci, ci, ctypes.POINTER(sz)]
     L.hca_attn.argtypes = [ci, bp, vp, i64, ci, ci, ci, ctypes.c_float, ci, vp, vp, vp, vp, vp, vp,
                            sz, vp]
+    L.csa_hca_decode_workspace.argtypes = [bp, i64, i64, ci, ci, ci, ci, ci, ctypes.POINTER(sz)]
+    L.csa_hca_decode.argtypes = [bp, vp, i64, vp, i64, ci, ci, ci, ci, ctypes.c_float, ci, ci, ci, vp, vp, vp, vp,
+                                 vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.csa_hca_decode_check.argtypes = [bp, vp, vp]
     L.csa_profile_events.argtypes = [ci, vp, vp]
     for name in EXPORTS:
         L[name].restype = L[name].restype if name in ("csa_status_string", "csa_last_error") else ci
@@ -282,3 +288,47 @@ def csa_profile_events(kernel_id: int, start: Optional[HipEvent] = None, stop: O
     sp = start.handle if start is not None else None
     ep = stop.handle if stop is not None else None
     _check(lib().csa_profile_events(kernel_id, sp, ep), "csa_profile_events")
+
+
+def csa_hca_decode_workspace(batch: Batch, max_pool: int, max_hpool: int, H: int, d: int, k: int, W: int,
+                             W_hca: int) -> int:
+    n = ctypes.c_size_t(0)
+    b = batch.c()
+    _check(lib().csa_hca_decode_workspace(ctypes.byref(b), max_pool, max_hpool, H, d, k, W, W_hca, ctypes.byref(n)),
+           "csa_hca_decode_workspace")
+    return n.value
+
+
+def csa_hca_decode(batch: Batch, pool_off, max_pool: int, hpool_off, max_hpool: int, m: int, m_hca: int,
+                   k: int, W: int, W_hca: int, scale: float, q_codes, q_scales, w, k_codes, k_scales, q, kv_pool,
+                   kv_pool_hca, kv_raw, idx=None, csa_out=None, csa_lse=None, hca_out=None, hca_lse=None,
+                   ws: Optional[Workspace] = None, stream=None):
+    """One fused decode step (index + top-k + CSA + HCA) in a single launch."""
+    H, d = q.shape[-2], q.shape[-1]
+    dev = q.device
+    if idx is None:
+        idx = torch.empty((batch.n_q, k), dtype=torch.int32, device=dev)
+    if csa_out is None:
+        csa_out = torch.empty_like(q)
+    if hca_out is None:
+        hca_out = torch.empty_like(q)
+    if csa_lse is None:
+        csa_lse = torch.empty((batch.n_q, H), dtype=torch.float32, device=dev)
+    if hca_lse is None:
+        hca_lse = torch.empty((batch.n_q, H), dtype=torch.float32, device=dev)
+    ws = ws or Workspace(dev)
+    nbytes = csa_hca_decode_workspace(batch, max_pool, max_hpool, H, d, k, W, W_hca)
+    buf = ws.get(nbytes)
+    b = batch.c()
+    _check(lib().csa_hca_decode(ctypes.byref(b), _ptr(pool_off), max_pool, _ptr(hpool_off), max_hpool, m, m_hca, H, d,
+                                scale, k, W, W_hca, _ptr(q_codes), _ptr(q_scales), _ptr(w), _ptr(k_codes),
+                                _ptr(k_scales), _ptr(q), _ptr(kv_pool), _ptr(kv_pool_hca), _ptr(kv_raw), _ptr(idx),
+                                _ptr(csa_out), _ptr(csa_lse), _ptr(hca_out), _ptr(hca_lse), _ptr(buf), nbytes,
+                                _stream(stream)), "csa_hca_decode")
+    return idx, csa_out, csa_lse, hca_out, hca_lse
+
+
+def csa_hca_decode_check(batch: Batch, ws: Workspace, stream=None) -> None:
+    """Synchronise and raise if a fused decode launch on `ws` hit its wait bound."""
+    b = batch.c()
+    _check(lib().csa_hca_decode_check(ctypes.byref(b), _ptr(ws.buf), _stream(stream)), "csa_hca_decode")

@@ -86,6 +86,79 @@ void prof_end(int id, hipStream_t stream) {
 
 extern "C" {
 
+int csa_hca_decode_workspace(const csa_batch* b, int64_t max_pool, int64_t max_hpool, int H, int d,
+                             int k, int W, int W_hca, size_t* bytes) {
+  int rc = check_batch(b);
+  if (rc) return rc;
+  if (!bytes || k < 1 || k > 4096 || W < 0 || W_hca < 0 || max_pool < 0 || max_hpool < 0)
+    return fail(CSA_ERR_INVALID, "bytes NULL or k / W / W_hca / sizes out of range");
+  if (d != 128 || !csa::fused_supported(b->n_q, max_pool, H))
+    return fail(CSA_ERR_UNSUPPORTED, "fused decode needs d = 128, H %% 16 == 0, H <= 64, max_pool <= 262144, "
+                                     "1..64 queries");
+  *bytes = csa::plan_fused(b->n_q, max_pool, max_hpool, H, k, W, W_hca).ws_bytes;
+  return CSA_OK;
+}
+
+int csa_hca_decode(const csa_batch* b, const int64_t* pool_off, int64_t max_pool,
+                   const int64_t* hpool_off, int64_t max_hpool, int m, int m_hca, int H, int d,
+                   float scale, int k, int W, int W_hca, const uint8_t* q_codes,
+                   const uint8_t* q_scales, const float* w, const uint8_t* k_codes,
+                   const uint8_t* k_scales, const void* q, const void* kv_pool,
+                   const void* kv_pool_hca, const void* kv_raw, int32_t* idx, void* csa_out,
+                   float* csa_lse, void* hca_out, float* hca_lse, void* ws, size_t ws_bytes,
+                   void* stream) {
+  int rc = check_batch(b);
+  if (rc) return rc;
+  if (b->n_q != b->n_seq || b->max_q_per_seq != 1)
+    return fail(CSA_ERR_UNSUPPORTED, "fused decode needs exactly one query per sequence");
+  if (m < 1 || m_hca < 1) return fail(CSA_ERR_INVALID, "block sizes must be >= 1");
+  if (k < 1 || k > 4096 || W < 0 || W_hca < 0) return fail(CSA_ERR_INVALID, "k / W / W_hca out of range");
+  if (max_pool < 0 || max_hpool < 0 || max_hpool > 0x7fffffffLL) return fail(CSA_ERR_INVALID, "sizes out of range");
+  if (d != 128 || !csa::fused_supported(b->n_q, max_pool, H))
+    return fail(CSA_ERR_UNSUPPORTED, "fused decode needs d = 128, H %% 16 == 0, H <= 64, max_pool <= 262144, "
+                                     "1..64 queries");
+  if (!pool_off || !hpool_off || !q_codes || !q_scales || !w || !k_codes || !k_scales || !q || !kv_pool ||
+      (max_hpool > 0 && !kv_pool_hca) || ((W > 0 || W_hca > 0) && !kv_raw) || !idx || !csa_out || !hca_out)
+    return fail(CSA_ERR_INVALID, "NULL pointer argument");
+  if (!aligned16(q_codes) || !aligned16(k_codes) || !aligned16(q) || !aligned16(kv_pool) ||
+      !aligned16(kv_pool_hca) || !aligned16(kv_raw) || !aligned16(csa_out) || !aligned16(hca_out))
+    return fail(CSA_ERR_INVALID, "codes, q, caches and outputs must be 16-byte aligned");
+  const size_t need = csa::plan_fused(b->n_q, max_pool, max_hpool, H, k, W, W_hca).ws_bytes;
+  if (!ws || ws_bytes < need)
+    return fail(CSA_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need, ws_bytes);
+  rc = check_device();
+  if (rc) return rc;
+  if (csa::launch_fused((int)b->n_q, b->tok_off, b->q_pos, pool_off, hpool_off, max_pool, max_hpool, m, m_hca, H,
+                        scale, k, W, W_hca, q_codes, q_scales, w, k_codes, k_scales, q, kv_pool, kv_pool_hca,
+                        kv_raw, idx, csa_out, csa_lse, hca_out, hca_lse, ws, (hipStream_t)stream) != 0) {
+    (void)hipGetLastError();
+    return fail(CSA_ERR_DEVICE, "cooperative launch of the fused decode kernel failed");
+  }
+  return CSA_OK;
+}
+
+int csa_hca_decode_check(const csa_batch* b, const void* ws, void* stream) {
+  int rc = check_batch(b);
+  if (rc) return rc;
+  if (!ws) return fail(CSA_ERR_INVALID, "ws is NULL");
+  rc = check_device();
+  if (rc) return rc;
+  // the error word follows the per-row control words at the start of the workspace
+  uint32_t* errp = (uint32_t*)ws + b->n_q * 16 + 1;
+  uint32_t err = 0;
+  if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess ||
+      hipMemcpy(&err, errp, 4, hipMemcpyDeviceToHost) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(CSA_ERR_DEVICE, "could not read the decode status word");
+  }
+  if (err) {
+    const uint32_t zero = 0;
+    (void)hipMemcpy(errp, &zero, 4, hipMemcpyHostToDevice);
+    return fail(CSA_ERR_DEVICE, "a fused decode launch hit its internal wait bound; its outputs are invalid");
+  }
+  return CSA_OK;
+}
+
 int csa_profile_events(int kernel_id, void* start, void* stop) {
   if (kernel_id < 0 || kernel_id >= CSA_K_COUNT) return fail(CSA_ERR_INVALID, "unknown kernel id %d", kernel_id);
   if ((start == nullptr) != (stop == nullptr)) return fail(CSA_ERR_INVALID, "pass both events or neither");

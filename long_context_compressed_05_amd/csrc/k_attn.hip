@@ -22,6 +22,7 @@
 // O^T += V^T P^T run on v_mfma_f32_16x16x32_bf16 with fp32 accumulation.
 // The key order inside the P^T operand is permuted so that each lane feeds
 // the MFMA with its own softmax outputs (no cross-lane shuffles).
+#include "attn_core.hpp"
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -86,27 +87,21 @@ __device__ __forceinline__ const uint8_t* key_row(const AttnArgs& a, const RowCt
 }
 
 // ---------------------------------------------------------------------------
-// bf16, MFMA
+// bf16, MFMA (tile loop in attn_core.hpp)
 // ---------------------------------------------------------------------------
-constexpr int kKStride = 136;  // LDS row stride (elements) of the K tile
-constexpr int kVStride = 72;   // LDS row stride (elements) of the transposed V tile
 constexpr int kMaxSplitKeys = 1024;
 
 template <int GPW>
 __global__ __launch_bounds__(256) void k_attn_bf16(AttnArgs a) {
-  __shared__ __align__(16) uint16_t Ks[64 * kKStride];
-  __shared__ __align__(16) uint16_t Vt[128 * kVStride];
+  __shared__ __align__(16) uint8_t lds[kAttnLdsBytes];
   __shared__ int32_t idx_s[kMaxSplitKeys];
-  __shared__ uint8_t valid_s[64];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int l16 = lane & 15, g = lane >> 4;
+  const int tid = threadIdx.x;
   const int64_t row = blockIdx.y;
   const int split = blockIdx.x;
   const RowCtx c = row_ctx(a, row);
   const int64_t list_len = (int64_t)a.seg_a + a.W;
   const int64_t p_begin = (int64_t)split * a.ks;
   const int64_t p_end = p_begin + a.ks < list_len ? p_begin + a.ks : list_len;
-  const int HG = a.H >> 4;
   constexpr size_t RB = 2 * 128 * 2;  // bytes per [2][128] bf16 row
 
   // this split's slice of the index row, staged once
@@ -116,7 +111,6 @@ __global__ __launch_bounds__(256) void k_attn_bf16(AttnArgs a) {
   }
   __syncthreads();
   auto rowptr = [&](int64_t p) -> const uint8_t* {
-    if (p >= p_end) return nullptr;
     if (p < a.seg_a) {
       if (a.hca) return p < c.n_vis_a ? a.kv_pool + (size_t)(c.pool_base + p) * RB : nullptr;
       const int32_t j = idx_s[p - p_begin];
@@ -125,172 +119,13 @@ __global__ __launch_bounds__(256) void k_attn_bf16(AttnArgs a) {
     const int64_t u = c.t - a.W + 1 + (p - a.seg_a);
     return u >= 0 ? a.kv_raw + (size_t)(c.tok_base + u) * RB : nullptr;
   };
-
-  // Q^T operand (B): column = head 16*hg + l16, K = dims 32*kstep + 8*g .. +7
-  v8bf qf[GPW][4];
-  float m_run[GPW], l_run[GPW];
-  v4f O[GPW][8];
-#pragma unroll
-  for (int gi = 0; gi < GPW; ++gi) {
-    const int hg = wave + 4 * gi;
-    m_run[gi] = -INFINITY;
-    l_run[gi] = 0.f;
-#pragma unroll
-    for (int mt = 0; mt < 8; ++mt) O[gi][mt] = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kq = 0; kq < 4; ++kq) {
-      if (hg < HG) {
-        const uint8_t* qp = a.q + ((size_t)(row * a.H + 16 * hg + l16) * 128 + 32 * kq + 8 * g) * 2;
-        qf[gi][kq] = *reinterpret_cast<const v8bf*>(qp);
-      } else {
-        qf[gi][kq] = v8bf{};
-      }
-    }
-  }
-
-  // staging: 16-byte chunk ch of keys 2*kp, 2*kp+1 for kp in {tid/16, tid/16 + 16}
-  const int ch = tid & 15;
-  uint4 kr[2][2], vr[2][2];
-  bool vl[2][2];
-  auto load_tile = [&](int64_t p0) {
-#pragma unroll
-    for (int r = 0; r < 2; ++r)
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const uint8_t* rp = rowptr(p0 + 2 * ((tid >> 4) + 16 * r) + e);
-        vl[r][e] = rp != nullptr;
-        if (rp) {
-          kr[r][e] = *reinterpret_cast<const uint4*>(rp + ch * 16);
-          vr[r][e] = *reinterpret_cast<const uint4*>(rp + 256 + ch * 16);
-        } else {
-          kr[r][e] = make_uint4(0, 0, 0, 0);
-          vr[r][e] = make_uint4(0, 0, 0, 0);
-        }
-      }
-  };
-  if (p_begin < p_end) load_tile(p_begin);
-
-  for (int64_t p0 = p_begin; p0 < p_end; p0 += 64) {
-    __syncthreads();  // the previous tile's LDS reads are done
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const int kp = (tid >> 4) + 16 * r;
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        *reinterpret_cast<uint4*>(&Ks[(2 * kp + e) * kKStride + ch * 8]) = kr[r][e];
-        if (ch == 0) valid_s[2 * kp + e] = vl[r][e] ? 1 : 0;
-      }
-      const uint32_t v0[4] = {vr[r][0].x, vr[r][0].y, vr[r][0].z, vr[r][0].w};
-      const uint32_t v1[4] = {vr[r][1].x, vr[r][1].y, vr[r][1].z, vr[r][1].w};
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        // dims ch*8 + 2q (low halves) and ch*8 + 2q + 1 (high halves) of keys 2kp, 2kp+1
-        const uint32_t lo = (v0[q] & 0xffffu) | (v1[q] << 16);
-        const uint32_t hi = (v0[q] >> 16) | (v1[q] & 0xffff0000u);
-        *reinterpret_cast<uint32_t*>(&Vt[(ch * 8 + 2 * q) * kVStride + 2 * kp]) = lo;
-        *reinterpret_cast<uint32_t*>(&Vt[(ch * 8 + 2 * q + 1) * kVStride + 2 * kp]) = hi;
-      }
-    }
-    __syncthreads();
-    if (p0 + 64 < p_end) load_tile(p0 + 64);  // next tile's loads fly during this tile's math
-
-#pragma unroll
-    for (int gi = 0; gi < GPW; ++gi) {
-      const int hg = wave + 4 * gi;
-      if (hg >= HG) continue;
-      // S^T tile: rows = keys 16*mt + 4*g + v, column = head l16
-      float s[4][4];
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        v4f acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kq = 0; kq < 4; ++kq) {
-          const v8bf kf = *reinterpret_cast<const v8bf*>(&Ks[(16 * mt + l16) * kKStride + 32 * kq + 8 * g]);
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[gi][kq], acc, 0, 0, 0);
-        }
-#pragma unroll
-        for (int v = 0; v < 4; ++v)
-          s[mt][v] = valid_s[16 * mt + 4 * g + v] ? acc[v] * a.scale_log2 : -INFINITY;
-      }
-      float tmax = -INFINITY;
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) tmax = fmaxf(tmax, s[mt][v]);
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-      const float mnew = fmaxf(m_run[gi], tmax);
-      if (mnew == -INFINITY) continue;  // nothing valid so far (uniform: validity is per key)
-      const float alpha = fast_exp2(m_run[gi] - mnew);
-      m_run[gi] = mnew;
-      float psum = 0.f;
-      float pv[4][4];
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          pv[mt][v] = fast_exp2(s[mt][v] - mnew);
-          psum += pv[mt][v];
-        }
-      l_run[gi] = l_run[gi] * alpha + psum;
-#pragma unroll
-      for (int mt = 0; mt < 8; ++mt) O[gi][mt] *= alpha;
-      // O^T += V^T P^T over two 32-key steps; K slot 8g+i <-> key 32*kq + (i<4 ? 4g+i : 16+4g+i-4)
-#pragma unroll
-      for (int kq = 0; kq < 2; ++kq) {
-        v8bf pf;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          pf[i] = (__bf16)pv[2 * kq][i];
-          pf[4 + i] = (__bf16)pv[2 * kq + 1][i];
-        }
-#pragma unroll
-        for (int mt = 0; mt < 8; ++mt) {
-          const uint16_t* vrow = &Vt[(16 * mt + l16) * kVStride + 32 * kq + 4 * g];
-          const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
-          const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16);
-          uint4 u = make_uint4(lo.x, lo.y, hi.x, hi.y);
-          const v8bf vf = *reinterpret_cast<const v8bf*>(&u);
-          O[gi][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, O[gi][mt], 0, 0, 0);
-        }
-      }
-    }
-  }
-
-  // finish: lane (l16, g) holds head 16*hg + l16, dims 16*mt + 4*g + v
-#pragma unroll
-  for (int gi = 0; gi < GPW; ++gi) {
-    const int hg = wave + 4 * gi;
-    if (hg >= HG) continue;
-    float l = l_run[gi];
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
-    const int head = 16 * hg + l16;
-    if (a.splits == 1) {
-      const float inv = l > 0.f ? 1.f / l : 0.f;
-      uint8_t* op = a.out + ((size_t)(row * a.H + head) * 128) * 2;
-#pragma unroll
-      for (int mt = 0; mt < 8; ++mt) {
-        const int d0 = 16 * mt + 4 * g;
-        uint2 u;
-        u.x = f32_to_bf16(O[gi][mt][0] * inv) | (f32_to_bf16(O[gi][mt][1] * inv) << 16);
-        u.y = f32_to_bf16(O[gi][mt][2] * inv) | (f32_to_bf16(O[gi][mt][3] * inv) << 16);
-        *reinterpret_cast<uint2*>(op + d0 * 2) = u;
-      }
-      if (a.lse && g == 0)
-        a.lse[row * a.H + head] = l > 0.f ? (m_run[gi] + __log2f(l)) * kLn2 : -INFINITY;
-    } else {
-      const size_t base = ((size_t)(row * a.splits + split) * a.H + head);
-      float* op = a.part_o + base * 128;
-#pragma unroll
-      for (int mt = 0; mt < 8; ++mt)
-        *reinterpret_cast<v4f*>(op + 16 * mt + 4 * g) = O[gi][mt];
-      if (g == 0) {
-        a.part_ml[base * 2 + 0] = m_run[gi];
-        a.part_ml[base * 2 + 1] = l;
-      }
-    }
-  }
+  AttnState<GPW> st;
+  attn_init<GPW>(st, a.q + (size_t)row * a.H * 128 * 2, a.H);
+  attn_run<GPW>(st, a.H, a.scale_log2, p_begin, p_end, rowptr, lds);
+  const size_t pbase = (size_t)(row * a.splits + split) * a.H;
+  attn_finish<GPW>(st, a.H, a.out + (size_t)row * a.H * 128 * 2, a.lse ? a.lse + row * a.H : nullptr,
+                   a.part_o ? a.part_o + pbase * 128 : nullptr, a.part_ml ? a.part_ml + pbase * 2 : nullptr,
+                   a.splits > 1, false);
 }
 
 // ---------------------------------------------------------------------------

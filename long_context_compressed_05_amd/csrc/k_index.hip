@@ -29,6 +29,7 @@
 //      is too large for LDS).  It also returns the workspace to all-zero.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "select_core.hpp"
 
 namespace csa {
 
@@ -272,44 +273,15 @@ struct FinalArgs {
   int32_t* idx;
 };
 
-// need-th largest value among the active candidates, 8 bits per round, all
-// threads of the block.  Returns the exact value; *need_left = how many of the
-// entries equal to it are to be taken.
-template <typename ValueFn, typename ActiveFn>
-__device__ uint32_t radix_select_desc(uint32_t n, uint32_t need, ValueFn val, ActiveFn active,
-                                      uint32_t* need_left) {
-  __shared__ uint32_t bins[256];
-  __shared__ uint32_t scratch[24];
-  uint32_t prefix = 0, pmask = 0;
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int i = threadIdx.x; i < 256; i += blockDim.x) bins[i] = 0;
-    __syncthreads();
-    for (uint32_t i = threadIdx.x; i < n; i += blockDim.x) {
-      if (!active(i)) continue;
-      const uint32_t v = val(i);
-      if ((v & pmask) == prefix) atomicAdd(&bins[(v >> shift) & 255u], 1u);
-    }
-    __syncthreads();
-    const uint32_t c = threadIdx.x < 256 ? bins[threadIdx.x] : 0u;
-    int d;
-    uint32_t above;
-    block_find_from_top(c, need, scratch, &d, &above);
-    prefix |= (uint32_t)d << shift;
-    pmask |= 255u << shift;
-    need -= above;
-  }
-  *need_left = need;
-  return prefix;
-}
-
 __global__ __launch_bounds__(1024) void k_idx_final(FinalArgs a) {
   extern __shared__ uint32_t bitmap[];  // ceil(max_pool / 32) words when use_bitmap
   __shared__ int32_t outj[4096];
   __shared__ uint2 cand_s[kCandLds];
+  __shared__ uint32_t bins[256];
+  __shared__ uint32_t scratch[24];
   __shared__ uint32_t n_out;
-  __shared__ uint32_t scan_scratch[24];
   const int64_t row = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x;
   const int b = seq_of_row(a.q_off, a.n_seq, row);
   const int64_t P = a.pool_off[b + 1] - a.pool_off[b];
   const int64_t nvis = n_visible(a.q_pos[row], a.m, P);
@@ -327,11 +299,11 @@ __global__ __launch_bounds__(1024) void k_idx_final(FinalArgs a) {
     }
     uint32_t r;
     const uint32_t kstar = radix_select_desc(
-        n_c, need, [&](uint32_t i) { return cand[i].x; }, [&](uint32_t) { return true; }, &r);
+        n_c, need, [&](uint32_t i) { return cand[i].x; }, [&](uint32_t) { return true; }, &r, bins, scratch);
     uint32_t r2;
     const uint32_t jstar = radix_select_desc(
-        n_c, r, [&](uint32_t i) { return ~cand[i].y; }, [&](uint32_t i) { return cand[i].x == kstar; },
-        &r2);
+        n_c, r, [&](uint32_t i) { return ~cand[i].y; }, [&](uint32_t i) { return cand[i].x == kstar; }, &r2,
+        bins, scratch);
     auto chosen = [&](uint2 c) { return c.x > kstar || (c.x == kstar && ~c.y >= jstar); };
     if (a.use_bitmap) {
       // ascending order from a bitmap of the visible range
@@ -347,32 +319,7 @@ __global__ __launch_bounds__(1024) void k_idx_final(FinalArgs a) {
         if (chosen(c)) atomicOr(&bitmap[c.y >> 5], 1u << (c.y & 31));
       }
       __syncthreads();
-      const int wpt = (nwords + (int)blockDim.x - 1) / (int)blockDim.x;
-      const int w0 = tid * wpt;
-      uint32_t cnt = 0;
-      for (int i = 0; i < wpt; ++i)
-        if (w0 + i < nwords) cnt += __popc(bitmap[w0 + i]);
-      // block exclusive prefix of cnt
-      uint32_t incl = cnt;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t v = __shfl_up(incl, off);
-        if (lane >= off) incl += v;
-      }
-      if (lane == 63) scan_scratch[wave] = incl;
-      __syncthreads();
-      uint32_t lower = 0;
-      for (int w = 0; w < wave; ++w) lower += scan_scratch[w];
-      uint32_t pos = lower + incl - cnt;
-      for (int i = 0; i < wpt; ++i) {
-        if (w0 + i >= nwords) break;
-        uint32_t bits = bitmap[w0 + i];
-        while (bits) {
-          const int bpos = __ffs(bits) - 1;
-          bits &= bits - 1;
-          idx[pos++] = (w0 + i) * 32 + bpos;
-        }
-      }
+      bitmap_emit_ascending(bitmap, nwords, scratch, [&](uint32_t pos, int32_t j) { idx[pos] = j; });
     } else {
       if (tid == 0) n_out = n_def;
       for (uint32_t i = tid; i < n_def; i += blockDim.x) outj[i] = a.def[row * a.k + i];

@@ -33,4 +33,17 @@ int launch_attn(bool bf16, bool hca, int n_seq, int64_t n_q, const int64_t* tok_
                 const void* kv_raw, const int32_t* idx, void* out, float* lse, void* ws,
                 hipStream_t stream);
 
+struct FusedPlan {
+  int n_sc, n_cs, cs, n_hs, hs;
+  size_t ws_bytes;
+};
+FusedPlan plan_fused(int64_t R, int64_t max_pool, int64_t max_hpool, int H, int k, int W, int W_hca);
+int fused_supported(int64_t R, int64_t max_pool, int H);
+int launch_fused(int R, const int64_t* tok_off, const int64_t* q_pos, const int64_t* pool_off,
+                 const int64_t* hpool_off, int64_t max_pool, int64_t max_hpool, int m, int m_hca, int H,
+                 float scale, int k, int W, int W_hca, const uint8_t* q_codes, const uint8_t* q_scales,
+                 const float* w, const uint8_t* k_codes, const uint8_t* k_scales, const void* q,
+                 const void* kv_pool, const void* kv_hpool, const void* kv_raw, int32_t* idx, void* csa_out,
+                 float* csa_lse, void* hca_out, float* hca_lse, void* ws, hipStream_t stream);
+
 }  // namespace csa

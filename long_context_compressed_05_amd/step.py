@@ -15,7 +15,8 @@ from typing import Dict, Optional
 import numpy as np
 import torch
 
-from . import (Batch, Workspace, csa_compress, csa_index_topk, csa_sparse_attn, hca_attn)
+from . import (Batch, Workspace, csa_compress, csa_hca_decode, csa_hca_decode_check, csa_index_topk,
+               csa_sparse_attn, hca_attn)
 
 
 @dataclass
@@ -64,6 +65,7 @@ class Layer:
     ws_idx: Workspace = field(default_factory=Workspace)
     ws_csa: Workspace = field(default_factory=Workspace)
     ws_hca: Workspace = field(default_factory=Workspace)
+    ws_fused: Workspace = field(default_factory=Workspace)
 
     @staticmethod
     def from_host(p: Params, host: Dict[str, np.ndarray], device="cuda") -> "Layer":
@@ -75,7 +77,7 @@ class Layer:
                      hpool_off=dev["hpool_off"], max_pool=int(np.diff(pool_off).max()),
                      max_hpool=int(np.diff(hpool_off).max()), kv=dev["kv"], kc=dev["kc"], ks=dev["ks"],
                      z=dev.get("z"), ws_idx=Workspace(device), ws_csa=Workspace(device),
-                     ws_hca=Workspace(device))
+                     ws_hca=Workspace(device), ws_fused=Workspace(device))
 
     def build_caches(self, stream=None):
         """Pool the raw rows into the CSA (m) and HCA (m') caches."""
@@ -104,3 +106,16 @@ class Layer:
                                     self.kv, p.W_hca, p.sm_scale, out=hca_out, lse=hca_lse,
                                     ws=self.ws_hca, stream=hca_stream if hca_stream is not None else stream)
         return idx, csa_out, csa_lse, hca_out, hca_lse
+
+    def decode_fused(self, q, qc, qs, w, idx=None, csa_out=None, csa_lse=None, hca_out=None, hca_lse=None,
+                     stream=None, kc=None, ks=None, hpooled=None):
+        """The same step as attend() in one fused launch (decode batches: one query per sequence)."""
+        p = self.p
+        return csa_hca_decode(self.batch, self.pool_off, self.max_pool, self.hpool_off, self.max_hpool, p.m, p.m_hca,
+                              p.k, p.W, p.W_hca, p.sm_scale, qc, qs, w, self.kc if kc is None else kc,
+                              self.ks if ks is None else ks, q, self.pooled,
+                              self.hpooled if hpooled is None else hpooled, self.kv, idx=idx, csa_out=csa_out,
+                              csa_lse=csa_lse, hca_out=hca_out, hca_lse=hca_lse, ws=self.ws_fused, stream=stream)
+
+    def check_fused(self, stream=None):
+        csa_hca_decode_check(self.batch, self.ws_fused, stream)

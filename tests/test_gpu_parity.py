@@ -222,3 +222,55 @@ def test_index_topk_large_ranges(lengths, k, codeset):
     for row in range(wl.n_q):
         want = P.oracle_topk_row(host, wl, row, seqs[row], wl.k, wl.m)
         assert np.array_equal(got[row], want), f"row {row}"
+
+
+FUSED_CASES = {
+    "decode_bf16_ragged": lambda: small_wl("decode_bf16_ragged", [1, 3, 130, 517, 1030, 2049, 4099], [1] * 7,
+                                           k=64, seed=11),
+    "decode_bf16_ties": lambda: small_wl("decode_bf16_ties", [3001, 2998, 4097, 5003], [1] * 4, k=50,
+                                         codeset=synth.E2M1_TIE_CODES, seed=13),
+    "decode_bf16_h32_whca": lambda: small_wl("decode_bf16_h32_whca", [200, 900, 70001], [1] * 3, H=32, k=700,
+                                             W=200, m=4, m_hca=64, W_hca=64, seed=15),
+    "decode_bf16_long": lambda: small_wl("decode_bf16_long", [160001, 200003, 150002, 99999], [1] * 4, k=1024,
+                                         seed=16),
+}
+
+
+@pytest.mark.parametrize("name", list(FUSED_CASES))
+def test_fused_decode_matches_oracle_and_separate_calls(name):
+    """The one-launch decode step gives the oracle's top-k bit for bit, outputs
+    within tolerance, and the separate calls' top-k; repeated launches on the
+    same workspace are bit-identical."""
+    _lib()
+    wl = FUSED_CASES[name]()
+    host = synth.make_inputs(wl)
+    layer, (idx_s, co_s, cl_s, ho_s, hl_s) = _run_path(wl, host)
+    from long_context_compressed_05_amd.step import to_device
+    dq = to_device({k: host[k] for k in ("q", "qc", "qs", "w")})
+    outs = [layer.decode_fused(dq["q"], dq["qc"], dq["qs"], dq["w"]) for _ in range(3)]
+    layer.check_fused()
+    torch.cuda.synchronize()
+    res = [[P.torch_to_np(t) for t in o] for o in outs]
+    idx, co, cl, ho, hl = res[0]
+    for other in res[1:]:
+        for x, y in zip(res[0], other):
+            assert np.array_equal(x, y), "fused decode is not deterministic"
+    assert np.array_equal(idx, idx_s), "fused top-k differs from csa_index_topk"
+    seqs = P.row_seq(host)
+    scale = 1 / math.sqrt(wl.d)
+    want_co, want_cl = np.zeros(co.shape), np.zeros(cl.shape)
+    want_ho, want_hl = np.zeros(ho.shape), np.zeros(hl.shape)
+    for r in range(wl.n_q):
+        b = seqs[r]
+        (t0, t1), (p0, p1), _ = P.seq_slices(host, b)
+        t = int(host["q_pos"][r])
+        o, l, i = oracle.csa_query(host["kv"][t0:t1], host["z"][t0:t1], host["q"][r], t, wl.m, wl.W, wl.k, scale,
+                                   host["qc"][r], host["qs"][r], host["w"][r], host["kc"][p0:p1], host["ks"][p0:p1])
+        assert np.array_equal(idx[r], i), f"top-k of row {r}"
+        want_co[r], want_cl[r] = o, l
+        want_ho[r], want_hl[r] = oracle.hca_query(host["kv"][t0:t1], host["z"][t0:t1], host["q"][r], t, wl.m_hca,
+                                                  wl.W_hca, scale)
+    P.check_close(co, want_co, wl.dtype, "fused csa output")
+    P.check_close(cl, want_cl, "bf16", "fused csa lse")
+    P.check_close(ho, want_ho, wl.dtype, "fused hca output")
+    P.check_close(hl, want_hl, "bf16", "fused hca lse")
