@@ -2,21 +2,46 @@
 //
 // One workgroup of 4 waves; wave w owns query-head groups w, w+4, ... (16
 // heads each, GPW groups per wave).  A list of key rows ([2][128] bf16: K then
-// V) is walked in 64-key tiles: K staged row-major and V transposed in LDS,
-// S^T = K Q^T and O^T += V^T P^T on v_mfma_f32_16x16x32_bf16 with fp32
-// accumulation and an online softmax in base 2.  The P^T operand uses the key
-// order 8g+i <-> 32*kq + (i < 4 ? 4g+i : 16+4g+i-4), which is exactly the set
-// of keys each lane already holds in the S^T output, so no shuffles are
-// needed.  The next tile's rows are loaded into registers while the current
-// tile is computed.
+// V, 512 B) is walked in 64-key tiles.  Tiles go from memory straight into LDS
+// (global_load_lds_dwordx4, no register staging) through NST stages: while
+// tile t is computed, tiles t+1 .. t+NST-1 are in flight.
+//
+// LDS stage layout (32 KB): row r (key), 16-byte chunk c (0..15 K, 16..31 V)
+// lives at ((c/4)*4 + r/16) KB + (r%16)*64 + (c%4)*16.  One DMA instruction of
+// wave w writes 1 KB: lane L carries row 16w + L/4, chunk 4i + L%4 of
+// instruction i, so each lane needs one row address per tile.  With this
+// layout both the K fragment reads and the V transpose reads stay inside one
+// 1 KB block per instruction.
+//
+// Per tile and head group: S^T = K Q^T (v_mfma_f32_16x16x32_bf16, K rows as
+// the A operand), an online softmax in base 2, then O^T += V^T P^T.  The V^T
+// operand comes from the row-major V chunks through ds_read_b64_tr_b16: in
+// each 16-lane group, lane a addresses row (key0 + a/4), dims dim0 + 4(a%4)
+// and lane j receives dims dim0 + j of keys key0 .. key0+3.  The P^T operand
+// uses the key order 8g+i <-> 32*kq + (i < 4 ? 4g+i : 16+4g+i-4), exactly the
+// keys each lane already holds in the S^T output, so P needs no shuffles; the
+// head-wise max and sum over the four lane groups use v_permlane16_swap and
+// v_permlane32_swap.  The running max is only raised (and O, l rescaled) when
+// a tile's max exceeds it by more than 2^8, so most tiles skip the rescale;
+// the normalised result does not depend on which max is used.  Masked keys
+// read a zero row and are excluded through one 64-bit validity word per tile.
 #pragma once
 #include "common.hpp"
 
 namespace csa {
 
-constexpr int kKStride = 136;  // LDS row stride (elements) of the K tile
-constexpr int kVStride = 72;   // LDS row stride (elements) of the transposed V tile
-constexpr int kAttnLdsBytes = 64 * kKStride * 2 + 128 * kVStride * 2 + 64;  // K, V^T, valid flags
+constexpr int kTileKeys = 64;
+constexpr int kStageBytes = kTileKeys * 512;
+constexpr int kLazyRescale = 8;  // log2 headroom before the running max is raised
+
+template <int NST>
+constexpr int attn_lds_bytes() { return NST * kStageBytes + 8 * NST; }
+constexpr int kAttnStages = 2;
+constexpr int kAttnLdsBytes = attn_lds_bytes<kAttnStages>();
+
+// A 512-byte row of zeros in device memory (never written): the source of
+// masked key rows.
+static __device__ __align__(256) uint8_t g_zero_row[512];
 
 template <int GPW>
 struct AttnState {
@@ -24,6 +49,43 @@ struct AttnState {
   float m_run[GPW], l_run[GPW];
   v4f O[GPW][8];
 };
+
+typedef short v4s_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float xor16_max(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor16_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor32_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// 16 bytes per lane from global memory to LDS address m0 + 16*lane + OFF
+// (and global address + OFF).  The compiler does not see this write: callers
+// order it with attn_wait_dma and a barrier.
+template <int OFF>
+__device__ __forceinline__ void dma16(const uint8_t* gaddr, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off offset:%2"
+               :
+               : "s"(m0), "v"(gaddr), "i"(OFF)
+               : "memory");
+}
+// at most N of this wave's memory operations still outstanding
+template <int N>
+__device__ __forceinline__ void attn_wait_dma() {
+  if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  else if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+}
 
 // q_row: this query's [H][128] bf16 heads.
 template <int GPW>
@@ -50,101 +112,127 @@ __device__ __forceinline__ void attn_init(AttnState<GPW>& st, const uint8_t* q_r
 }
 
 // Walk list positions [p_begin, p_end); rowptr(p) gives the [2][128] bf16 row
-// of position p or nullptr when masked.  lds: kAttnLdsBytes bytes, 16-aligned.
-template <int GPW, class RowPtr>
+// of position p or nullptr when masked.  lds: attn_lds_bytes<NST>() bytes,
+// 16-aligned.  Must be called by the whole workgroup; no memory operation of
+// the calling thread may be outstanding on entry (the DMA count relies on it).
+template <int GPW, int NST = kAttnStages, class RowPtr>
 __device__ __forceinline__ void attn_run(AttnState<GPW>& st, int H, float scale_log2, int64_t p_begin,
                                          int64_t p_end, RowPtr rowptr, uint8_t* lds) {
-  uint16_t* Ks = reinterpret_cast<uint16_t*>(lds);
-  uint16_t* Vt = Ks + 64 * kKStride;
-  uint8_t* valid_s = reinterpret_cast<uint8_t*>(Vt + 128 * kVStride);
+  static_assert(NST == 2 || NST == 3, "two or three stages");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g = lane >> 4;
   const int HG = H >> 4;
-  const int ch = tid & 15;  // staging: 16-byte chunk ch of keys 2*kp, 2*kp+1, kp in {tid/16, tid/16+16}
-  uint4 kr[2][2], vr[2][2];
-  bool vl[2][2];
-  auto load_tile = [&](int64_t p0) {
-#pragma unroll
-    for (int r = 0; r < 2; ++r)
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int64_t p = p0 + 2 * ((tid >> 4) + 16 * r) + e;
-        const uint8_t* rp = p < p_end ? rowptr(p) : nullptr;
-        vl[r][e] = rp != nullptr;
-        if (rp) {
-          kr[r][e] = *reinterpret_cast<const uint4*>(rp + ch * 16);
-          vr[r][e] = *reinterpret_cast<const uint4*>(rp + 256 + ch * 16);
-        } else {
-          kr[r][e] = make_uint4(0, 0, 0, 0);
-          vr[r][e] = make_uint4(0, 0, 0, 0);
-        }
-      }
-  };
-  if (p_begin < p_end) load_tile(p_begin);
+  if (p_begin >= p_end) return;
+  const int64_t n_tiles = (p_end - p_begin + kTileKeys - 1) / kTileKeys;
+  const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
+  uint64_t* masks = reinterpret_cast<uint64_t*>(lds + NST * kStageBytes);
 
-  for (int64_t p0 = p_begin; p0 < p_end; p0 += 64) {
-    __syncthreads();  // the previous tile's LDS reads are done
+  // DMA of tile t into stage s: row 16*wave + lane/4, chunks 4i + lane%4
+  auto issue = [&](int64_t t, int s) {
+    const int row = 16 * wave + (lane >> 2);
+    const int64_t p = p_begin + t * kTileKeys + row;
+    const uint8_t* rp = p < p_end ? rowptr(p) : nullptr;
+    const uint64_t vb = __ballot(rp != nullptr);
+    const uint8_t* src = (rp ? rp : g_zero_row) + 16 * (lane & 3);
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_base + (uint32_t)(s * kStageBytes + wave * 1024));
+    dma16<0>(src, m0);
+    dma16<64>(src, m0 + 4 * 1024 - 64);
+    dma16<128>(src, m0 + 8 * 1024 - 128);
+    dma16<192>(src, m0 + 12 * 1024 - 192);
+    dma16<256>(src, m0 + 16 * 1024 - 256);
+    dma16<320>(src, m0 + 20 * 1024 - 320);
+    dma16<384>(src, m0 + 24 * 1024 - 384);
+    dma16<448>(src, m0 + 28 * 1024 - 448);
+    // rows 16w .. 16w+15 valid bits: lanes 4j
+    uint32_t m16 = 0;
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const int kp = (tid >> 4) + 16 * r;
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        *reinterpret_cast<uint4*>(&Ks[(2 * kp + e) * kKStride + ch * 8]) = kr[r][e];
-        if (ch == 0) valid_s[2 * kp + e] = vl[r][e] ? 1 : 0;
-      }
-      const uint32_t v0[4] = {vr[r][0].x, vr[r][0].y, vr[r][0].z, vr[r][0].w};
-      const uint32_t v1[4] = {vr[r][1].x, vr[r][1].y, vr[r][1].z, vr[r][1].w};
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint32_t lo = (v0[q] & 0xffffu) | (v1[q] << 16);
-        const uint32_t hi = (v0[q] >> 16) | (v1[q] & 0xffff0000u);
-        *reinterpret_cast<uint32_t*>(&Vt[(ch * 8 + 2 * q) * kVStride + 2 * kp]) = lo;
-        *reinterpret_cast<uint32_t*>(&Vt[(ch * 8 + 2 * q + 1) * kVStride + 2 * kp]) = hi;
-      }
-    }
-    __syncthreads();
-    if (p0 + 64 < p_end) load_tile(p0 + 64);  // next tile's loads fly during this tile's math
+    for (int j = 0; j < 16; ++j) m16 |= (uint32_t)((vb >> (4 * j)) & 1ull) << j;
+    if (lane == 0) reinterpret_cast<uint16_t*>(masks + s)[wave] = (uint16_t)m16;
+  };
+
+  issue(0, 0);
+  if (n_tiles > 1) issue(1, 1);
+  if (NST == 3 && n_tiles > 2) issue(2, 2);
+
+  for (int64_t t = 0; t < n_tiles; ++t) {
+    const int s = (int)(t % NST);
+    const int64_t ahead = n_tiles - 1 - t < NST - 1 ? n_tiles - 1 - t : NST - 1;  // tiles issued after t
+    if (ahead >= 2) attn_wait_dma<16>();
+    else if (ahead == 1) attn_wait_dma<8>();
+    else attn_wait_dma<0>();
+    __syncthreads();  // every wave's part of tile t is in LDS (with its validity word)
+    const uint8_t* cur = lds + s * kStageBytes;
+    const uint64_t vmask = masks[s];
 
 #pragma unroll
     for (int gi = 0; gi < GPW; ++gi) {
       const int hg = wave + 4 * gi;
       if (hg >= HG) continue;
-      float s[4][4];
+      // S^T: 64 keys x 16 heads; lane holds keys 16 mt + 4 g + v of head l16
+      v8bf kf[4][4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int kq = 0; kq < 4; ++kq)
+          kf[mt][kq] = *reinterpret_cast<const v8bf*>(cur + (kq * 4 + mt) * 1024 + l16 * 64 + g * 16);
+      float s_[4][4];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         v4f acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kq = 0; kq < 4; ++kq) {
-          const v8bf kf = *reinterpret_cast<const v8bf*>(&Ks[(16 * mt + l16) * kKStride + 32 * kq + 8 * g]);
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, st.qf[gi][kq], acc, 0, 0, 0);
-        }
+        for (int kq = 0; kq < 4; ++kq)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[mt][kq], st.qf[gi][kq], acc, 0, 0, 0);
 #pragma unroll
-        for (int v = 0; v < 4; ++v)
-          s[mt][v] = valid_s[16 * mt + 4 * g + v] ? acc[v] * scale_log2 : -INFINITY;
+        for (int v = 0; v < 4; ++v) s_[mt][v] = acc[v];
+      }
+      // V^T fragments, requested before the softmax math
+      v4s_t vt[8][2][2];
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+        for (int kq = 0; kq < 2; ++kq)
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            const int a3 = l16 & 3;
+            const int off = ((4 + (mt >> 1)) * 4 + 2 * kq + hh) * 1024 + (4 * g + (l16 >> 2)) * 64 +
+                            (2 * (mt & 1) + (a3 >> 1)) * 16 + (a3 & 1) * 8;
+            vt[mt][kq][hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) v4s_t*)(const_cast<uint8_t*>(cur) + off));
+          }
+      if (vmask != ~0ull) {
+        const uint64_t my = vmask >> (4 * g);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            if (!((my >> (16 * mt + v)) & 1ull)) s_[mt][v] = -INFINITY;
       }
       float tmax = -INFINITY;
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) tmax = fmaxf(tmax, s[mt][v]);
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-      const float mnew = fmaxf(st.m_run[gi], tmax);
-      if (mnew == -INFINITY) continue;  // nothing valid so far (uniform: validity is per key)
-      const float alpha = fast_exp2(st.m_run[gi] - mnew);
-      st.m_run[gi] = mnew;
+        for (int v = 0; v < 4; ++v) tmax = fmaxf(tmax, s_[mt][v]);
+      tmax = xor32_max(xor16_max(tmax)) * scale_log2;
+      if (__ballot(tmax > st.m_run[gi] + (float)kLazyRescale) != 0ull) {
+        const float mnew = fmaxf(st.m_run[gi], tmax);
+        const float alpha = fast_exp2(st.m_run[gi] - mnew);  // 0 while nothing was valid
+        st.m_run[gi] = mnew;
+        st.l_run[gi] *= alpha;
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt) st.O[gi][mt] *= alpha;
+      }
+      if (st.m_run[gi] == -INFINITY) continue;  // nothing valid so far (uniform: validity is per key)
+      const float mneg = -st.m_run[gi];
       float psum = 0.f;
       float pv[4][4];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          pv[mt][v] = fast_exp2(s[mt][v] - mnew);
+          pv[mt][v] = fast_exp2(fmaf(s_[mt][v], scale_log2, mneg));
           psum += pv[mt][v];
         }
-      st.l_run[gi] = st.l_run[gi] * alpha + psum;
-#pragma unroll
-      for (int mt = 0; mt < 8; ++mt) st.O[gi][mt] *= alpha;
+      st.l_run[gi] += psum;
 #pragma unroll
       for (int kq = 0; kq < 2; ++kq) {
         v8bf pf;
@@ -155,16 +243,18 @@ __device__ __forceinline__ void attn_run(AttnState<GPW>& st, int H, float scale_
         }
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt) {
-          const uint16_t* vrow = &Vt[(16 * mt + l16) * kVStride + 32 * kq + 4 * g];
-          const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
-          const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16);
-          uint4 u = make_uint4(lo.x, lo.y, hi.x, hi.y);
-          const v8bf vf = *reinterpret_cast<const v8bf*>(&u);
+          const v4s_t both[2] = {vt[mt][kq][0], vt[mt][kq][1]};
+          const v8bf vf = *reinterpret_cast<const v8bf*>(both);
           st.O[gi][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, st.O[gi][mt], 0, 0, 0);
         }
       }
     }
+    if (t + NST < n_tiles) {
+      __syncthreads();  // stage s is read out by every wave
+      issue(t + NST, s);
+    }
   }
+  __syncthreads();  // LDS free for the caller
 }
 
 // Finish: normalised bf16 output [H][128] and lse (natural log), or, when
@@ -181,9 +271,7 @@ __device__ __forceinline__ void attn_finish(AttnState<GPW>& st, int H, uint8_t* 
   for (int gi = 0; gi < GPW; ++gi) {
     const int hg = wave + 4 * gi;
     if (hg >= HG) continue;
-    float l = st.l_run[gi];
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
+    const float l = xor32_sum(xor16_sum(st.l_run[gi]));
     const int head = 16 * hg + l16;
     if (!partial) {
       const float inv = l > 0.f ? 1.f / l : 0.f;

@@ -92,9 +92,12 @@ int csa_hca_decode_workspace(const csa_batch* b, int64_t max_pool, int64_t max_h
   if (rc) return rc;
   if (!bytes || k < 1 || k > 4096 || W < 0 || W_hca < 0 || max_pool < 0 || max_hpool < 0)
     return fail(CSA_ERR_INVALID, "bytes NULL or k / W / W_hca / sizes out of range");
-  if (d != 128 || !csa::fused_supported(b->n_q, max_pool, H))
-    return fail(CSA_ERR_UNSUPPORTED, "fused decode needs d = 128, H %% 16 == 0, H <= 64, max_pool <= 262144, "
-                                     "1..64 queries");
+  rc = check_device();
+  if (rc) return rc;
+  if (d != 128 || !csa::fused_supported(b->n_q, max_pool, max_hpool, H, k, W, W_hca))
+    return fail(CSA_ERR_UNSUPPORTED, "fused decode needs d = 128, 16 <= H <= 64 with H %% 16 == 0, "
+                                     "max_pool <= 262144, 1..64 queries and n_q * max_pool <= 3072 * (resident "
+                                     "workgroups)");
   *bytes = csa::plan_fused(b->n_q, max_pool, max_hpool, H, k, W, W_hca).ws_bytes;
   return CSA_OK;
 }
@@ -114,9 +117,12 @@ int csa_hca_decode(const csa_batch* b, const int64_t* pool_off, int64_t max_pool
   if (m < 1 || m_hca < 1) return fail(CSA_ERR_INVALID, "block sizes must be >= 1");
   if (k < 1 || k > 4096 || W < 0 || W_hca < 0) return fail(CSA_ERR_INVALID, "k / W / W_hca out of range");
   if (max_pool < 0 || max_hpool < 0 || max_hpool > 0x7fffffffLL) return fail(CSA_ERR_INVALID, "sizes out of range");
-  if (d != 128 || !csa::fused_supported(b->n_q, max_pool, H))
-    return fail(CSA_ERR_UNSUPPORTED, "fused decode needs d = 128, H %% 16 == 0, H <= 64, max_pool <= 262144, "
-                                     "1..64 queries");
+  rc = check_device();
+  if (rc) return rc;
+  if (d != 128 || !csa::fused_supported(b->n_q, max_pool, max_hpool, H, k, W, W_hca))
+    return fail(CSA_ERR_UNSUPPORTED, "fused decode needs d = 128, 16 <= H <= 64 with H %% 16 == 0, "
+                                     "max_pool <= 262144, 1..64 queries and n_q * max_pool <= 3072 * (resident "
+                                     "workgroups)");
   if (!pool_off || !hpool_off || !q_codes || !q_scales || !w || !k_codes || !k_scales || !q || !kv_pool ||
       (max_hpool > 0 && !kv_pool_hca) || ((W > 0 || W_hca > 0) && !kv_raw) || !idx || !csa_out || !hca_out)
     return fail(CSA_ERR_INVALID, "NULL pointer argument");
@@ -126,8 +132,6 @@ int csa_hca_decode(const csa_batch* b, const int64_t* pool_off, int64_t max_pool
   const size_t need = csa::plan_fused(b->n_q, max_pool, max_hpool, H, k, W, W_hca).ws_bytes;
   if (!ws || ws_bytes < need)
     return fail(CSA_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need, ws_bytes);
-  rc = check_device();
-  if (rc) return rc;
   if (csa::launch_fused((int)b->n_q, b->tok_off, b->q_pos, pool_off, hpool_off, max_pool, max_hpool, m, m_hca, H,
                         scale, k, W, W_hca, q_codes, q_scales, w, k_codes, k_scales, q, kv_pool, kv_pool_hca,
                         kv_raw, idx, csa_out, csa_lse, hca_out, hca_lse, ws, (hipStream_t)stream) != 0) {
@@ -143,8 +147,8 @@ int csa_hca_decode_check(const csa_batch* b, const void* ws, void* stream) {
   if (!ws) return fail(CSA_ERR_INVALID, "ws is NULL");
   rc = check_device();
   if (rc) return rc;
-  // the error word follows the per-row control words at the start of the workspace
-  uint32_t* errp = (uint32_t*)ws + b->n_q * 16 + 1;
+  // the error word sits among the control words at the start of the workspace
+  uint32_t* errp = (uint32_t*)((uint8_t*)ws + csa::fused_error_word_offset());
   uint32_t err = 0;
   if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess ||
       hipMemcpy(&err, errp, 4, hipMemcpyDeviceToHost) != hipSuccess) {

@@ -34,11 +34,16 @@ int launch_attn(bool bf16, bool hca, int n_seq, int64_t n_q, const int64_t* tok_
                 hipStream_t stream);
 
 struct FusedPlan {
-  int n_sc, n_cs, cs, n_hs, hs;
+  int grid;                     // co-resident workgroups of the cooperative launch
+  int C, n_sc;                  // score entries per chunk, chunks per row
+  int cs, n_cs_sel, n_cs_win;   // CSA split size, selected and window splits per row
+  int hs, n_hs;                 // HCA split size, splits per row
+  int def_cap;
   size_t ws_bytes;
 };
 FusedPlan plan_fused(int64_t R, int64_t max_pool, int64_t max_hpool, int H, int k, int W, int W_hca);
-int fused_supported(int64_t R, int64_t max_pool, int H);
+int fused_supported(int64_t R, int64_t max_pool, int64_t max_hpool, int H, int k, int W, int W_hca);
+size_t fused_error_word_offset();
 int launch_fused(int R, const int64_t* tok_off, const int64_t* q_pos, const int64_t* pool_off,
                  const int64_t* hpool_off, int64_t max_pool, int64_t max_hpool, int m, int m_hca, int H,
                  float scale, int k, int W, int W_hca, const uint8_t* q_codes, const uint8_t* q_scales,
