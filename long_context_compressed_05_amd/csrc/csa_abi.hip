@@ -149,16 +149,19 @@ int csa_hca_decode_check(const csa_batch* b, const void* ws, void* stream) {
   if (rc) return rc;
   // the error word sits among the control words at the start of the workspace
   uint32_t* errp = (uint32_t*)((uint8_t*)ws + csa::fused_error_word_offset());
-  uint32_t err = 0;
+  uint32_t ctl[4] = {0, 0, 0, 0};  // epoch, exit count, error word, work counter
   if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess ||
-      hipMemcpy(&err, errp, 4, hipMemcpyDeviceToHost) != hipSuccess) {
+      hipMemcpy(ctl, ws, sizeof(ctl), hipMemcpyDeviceToHost) != hipSuccess) {
     (void)hipGetLastError();
     return fail(CSA_ERR_DEVICE, "could not read the decode status word");
   }
-  if (err) {
+  if (ctl[2]) {
     const uint32_t zero = 0;
     (void)hipMemcpy(errp, &zero, 4, hipMemcpyHostToDevice);
-    return fail(CSA_ERR_DEVICE, "a fused decode launch hit its internal wait bound; its outputs are invalid");
+    return fail(CSA_ERR_DEVICE,
+                "a fused decode launch hit its internal wait bound (code 0x%x; epoch %u, exit %u, work %u); its outputs "
+                "are invalid",
+                ctl[2], ctl[0], ctl[1], ctl[3]);
   }
   return CSA_OK;
 }

@@ -1,4 +1,4 @@
-// Fused CSA + HCA decode step: one cooperative launch per step.
+// Fused CSA + HCA decode step: one launch per step.
 //
 // The whole decode hot path runs in one persistent kernel whose workgroups
 // are all co-resident.  Every workgroup w runs, in order:
@@ -41,35 +41,32 @@ namespace csa {
 constexpr int kFMaxC = 3072;         // score entries per workgroup (keys in LDS)
 constexpr int kFBins = 4096;         // key >> 19
 constexpr int kFMaxSplit = 256;      // list positions per attention item
-constexpr int kFCandLds = 4096;      // candidates staged in LDS
+constexpr int kFEntLds = 6144;       // emitted entries of a row staged in LDS
 constexpr int kFMaxVisible = 262144;  // visible pooled entries per query (18-bit indices)
 constexpr int kFMaxRows = 64;
 constexpr int kFMaxSlots = 512;      // score chunks per row
-constexpr int kFRankMax = 1024;      // candidates ranked by direct comparison (< kFCandLds - 16)
+constexpr int kFRankMax = 2032;      // threshold-bin entries ranked by direct comparison
 constexpr uint32_t kSpinLimit = 1u << 20;
-constexpr int kTopPairs = 16;       // summary pairs per chunk read in the first round
-constexpr int kThrStride = 64;      // threshold words 512 bytes apart (no shared line among pollers)
 
 // control words at the start of the workspace
-enum { W_EPOCH = 0, W_EXIT = 1, W_ERROR = 2, W_CTL = 64 };
+enum { W_EPOCH = 0, W_EXIT = 1, W_ERROR = 2, W_TICKET = 3, W_CTL = 64 };
 
 // LDS layout (dynamic)
-constexpr int kOffKeys = 0;                                 // uint32 [kFMaxC]; later slot prefix sums
+constexpr int kOffKeys = 0;                                 // uint32 [kFMaxC]; later per-chunk arrays
 constexpr int kOffIdx = kOffKeys + kFMaxC * 4;              // int32 [kFMaxSplit]
 constexpr int kOffScr = kOffIdx + kFMaxSplit * 4;           // uint32 [64]
 constexpr int kOffU = kOffScr + 64 * 4;                     // union region
-constexpr int kOffCand = kOffU;                             // uint2 [kFCandLds]
-constexpr int kOffRadix = kOffCand + kFCandLds * 8;         // uint32 [1024] radix bins
-constexpr int kOffComp = kOffRadix + 1024 * 4;             // uint64 [kFRankMax + 16] order keys
-constexpr int kSelEnd = kOffComp + (1024 + 16) * 8;
+constexpr int kOffEnt = kOffU;                              // uint64 [kFEntLds] order keys of emitted entries
+constexpr int kOffHist = kOffEnt + kFEntLds * 8;            // uint32 [kFBins]; then uint64 [kFRankMax + 16]
+constexpr int kSelEnd = kOffHist + kFBins * 4;
 constexpr int kAttnEnd = kOffU + kAttnLdsBytes;
 constexpr int kFusedLds = kSelEnd > kAttnEnd ? kSelEnd : kAttnEnd;
-static_assert((kFMaxSlots + 1) * 3 * 4 <= kFMaxC * 4, "slot prefix sums alias the key region");
+static_assert((kFMaxSlots + 1) * 3 * 4 <= kFMaxC * 4, "per-chunk arrays alias the key region");
 static_assert(kOffU % 16 == 0, "attention LDS must be 16-byte aligned");
-static_assert(kFBins * 4 <= kFCandLds * 8, "histogram fits the union region");
+static_assert((kFRankMax + 16) * 8 <= kFBins * 4, "ranked entries reuse the histogram");
 
 // scratch word indices (0..39 are used by the block scans)
-enum { S_TAG = 40, S_FLAG, S_B1, S_ABOVE, S_FLOOR, S_KSTAR, S_JSTAR };
+enum { S_TAG = 40, S_FLAG, S_B1, S_ABOVE, S_NB1, S_CSTAR_LO, S_CSTAR_HI, S_BAD, S_TICKET };
 
 struct FusedArgs {
   const int64_t* tok_off;
@@ -96,16 +93,15 @@ struct FusedArgs {
   // plan
   int C, n_sc;                 // entries per score chunk, chunks per row
   int cs, n_cs_sel, n_cs_win;  // CSA split size, selected splits, window splits (per row)
+  int rounds;                  // work units taken per workgroup (rounds * grid >= all units)
   int hs, n_hs;                // HCA split size, splits per row
-  int def_cap;                 // definite slots per chunk = min(C, k)
+  int emit_q, emit_max;        // per chunk: entries at or above the local emit_q-th bin, at most emit_max
+  int64_t key_stride;          // keys row stride (multiple of 4)
   // workspace
   uint32_t* ctl;
-  uint64_t* sum_hdr;   // [R*n_sc]
-  uint64_t* sum;       // [R*n_sc][k]
-  uint64_t* thr;       // [R][kThrStride], word 0 used
-  uint64_t* emit_hdr;  // [R*n_sc]
-  uint64_t* defw;      // [R*n_sc][def_cap]
-  uint64_t* candw;     // [R*n_sc][2*C]
+  uint32_t* keys;      // [R][key_stride] sort keys (read only by the exact fallback)
+  uint64_t* ent_hdr;   // [R*n_sc] tagged: count | bin << 12 | truncated << 25
+  uint64_t* ent;       // [R*n_sc][emit_max] (key << 32) | index, ascending index
   uint64_t* part_hdr;  // [R][n_cs_sel + n_cs_win + n_hs]
   float* csa_po;       // [R][n_cs][H][128]
   float* csa_pml;      // [R][n_cs][H][2]
@@ -178,6 +174,11 @@ __device__ __forceinline__ void coh_st128(const Coh& c, void* p, v4u_t v) {
   __builtin_amdgcn_raw_buffer_store_b128(v, c.r, coh_off(c, p), 0, kSc1);
 }
 
+__device__ __forceinline__ uint32_t n_vis_u32(const FRow& f) { return (uint32_t)f.n_vis; }
+// A value every lane holds identically (an LDS broadcast): made scalar so that
+// the compiler sees control flow on it as uniform (barriers inside stay aligned).
+__device__ __forceinline__ uint32_t uni(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
+
 struct FCtx {
   const FusedArgs* a;
   uint8_t* smem;
@@ -186,19 +187,20 @@ struct FCtx {
   Coh coh;
 };
 
-__device__ __forceinline__ void set_error(const FCtx& x) { atomicOr(x.a->ctl + W_ERROR, 1u); }
+// error word: bit 0 = a wait hit its bound, bits 1.. = which wait (see the callers)
+__device__ __forceinline__ void set_error(const FCtx& x, uint32_t code) { atomicOr(x.a->ctl + W_ERROR, 1u | code); }
 __device__ __forceinline__ bool error_seen(const FCtx& x) { return ld_dev(x.a->ctl + W_ERROR) != 0; }
 
 // this thread spins until the tagged word at p carries the launch's tag and
 // returns its payload; after the bound (or once an error was reported) it
 // sets *fail and returns 0
-__device__ __forceinline__ uint32_t poll_word(const FCtx& x, const uint64_t* p, bool* fail) {
+__device__ __forceinline__ uint32_t poll_word(const FCtx& x, const uint64_t* p, bool* fail, uint32_t code = 0) {
   uint64_t v = coh_ld64(x.coh, p);
   uint32_t n = 0;
   while ((uint32_t)(v >> 32) != x.tag) {
     ++n;
     if (n >= kSpinLimit || ((n & 1023u) == 0 && error_seen(x))) {
-      if (n >= kSpinLimit) set_error(x);
+      if (n >= kSpinLimit) set_error(x, code);
       *fail = true;
       return 0;
     }
@@ -223,7 +225,7 @@ __device__ __forceinline__ void read_tagged(const FCtx& x, const uint64_t* const
     for (int i = 0; i < N; ++i) late |= (uint32_t)(v[i] >> 32) != x.tag;
     if (!late) break;
     if (++n >= kSpinLimit || ((n & 1023u) == 0 && error_seen(x))) {
-      if (n >= kSpinLimit) set_error(x);
+      if (n >= kSpinLimit) set_error(x, 0);
       *fail = true;
       break;
     }
@@ -284,7 +286,7 @@ __device__ __forceinline__ bool all_ok(const FCtx& x, bool fail) {
   __syncthreads();
   if (fail) x.scr[S_FLAG] = 1;
   __syncthreads();
-  const bool ok = x.scr[S_FLAG] == 0;
+  const bool ok = uni(x.scr[S_FLAG]) == 0;
   __syncthreads();
   return ok;
 }
@@ -305,7 +307,7 @@ __device__ __forceinline__ uint32_t kth_bin(const uint32_t* hist, uint32_t need,
   int tstar;
   uint32_t ab;
   block_find_from_top(tot, need, scr, &tstar, &ab);
-  if (tstar < 0) {
+  if ((int)uni((uint32_t)tstar) < 0) {
     *above = 0;
     return kFBins + 1;
   }
@@ -331,8 +333,8 @@ __device__ __forceinline__ uint32_t kth_bin(const uint32_t* hist, uint32_t need,
     scr[S_ABOVE] = asel;
   }
   __syncthreads();
-  const uint32_t b = scr[S_B1];
-  *above = scr[S_ABOVE];
+  const uint32_t b = uni(scr[S_B1]);
+  *above = uni(scr[S_ABOVE]);
   __syncthreads();
   return b;
 }
@@ -394,133 +396,32 @@ __device__ __forceinline__ void phase_score(const FCtx& x, int r, int c, const F
     }
   }
   __syncthreads();
-  // local k-th bin: report the nonzero bins at or above it
-  int bw = 0;
-  const uint32_t need = n < a.k ? (uint32_t)n : (uint32_t)a.k;
-  if (need > 0) {
-    uint32_t ab;
-    bw = (int)kth_bin(hist, need, x.scr, &ab);
-  }
-  uint32_t cnt[16], mine = 0;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    cnt[i] = hist[tid * 16 + i];
-    mine += (tid * 16 + i >= bw && cnt[i] != 0) ? 1u : 0u;
-  }
-  // output position: pairs of higher threads come first (descending bins)
-  uint32_t s = mine;  // inclusive suffix sum within the wave
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t v = __shfl_down(s, off);
-    if (lane + off < 64) s += v;
-  }
-  if (lane == 0) x.scr[8 + wave] = s;
-  __syncthreads();
-  uint32_t higher = 0;
-  for (int w2 = wave + 1; w2 < 4; ++w2) higher += x.scr[8 + w2];
-  uint32_t pos = s - mine + higher;
-  const uint32_t npairs = x.scr[8] + x.scr[9] + x.scr[10] + x.scr[11];
-  const size_t slot = (size_t)r * a.n_sc + c;
-  uint64_t* dst = a.sum + slot * a.k;
-  for (int i = 15; i >= 0; --i) {
-    const int bin = tid * 16 + i;
-    if (bin >= bw && cnt[i] != 0) st_dev64(dst + pos++, tagged(x.tag, ((uint32_t)bin << 20) | cnt[i]));
-  }
-  if (tid == 0) st_dev64(a.sum_hdr + slot, tagged(x.tag, npairs));
-  __syncthreads();
-}
-
-// ---------------------------------------------------------------------------
-// reduce (chunk 0 of row r): threshold bin of the row
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ bool phase_reduce(const FCtx& x, int r, const FRow& f) {
-  const FusedArgs& a = *x.a;
-  const int tid = threadIdx.x;
-  uint32_t* hist = reinterpret_cast<uint32_t*>(x.smem + kOffU);
-  uint32_t* np = hist + kFBins;  // pairs per chunk
-  for (int i = tid; i < kFBins; i += 256) hist[i] = 0;
-  if (tid == 0) x.scr[S_FLOOR] = 0;
-  bool fail = false;
-  for (int sl = tid; sl < a.n_sc && !fail; sl += 256) np[sl] = poll_word(x, a.sum_hdr + (size_t)r * a.n_sc + sl, &fail);
-  if (!all_ok(x, fail)) return false;
-  const uint64_t* rowsum = a.sum + (size_t)r * a.n_sc * a.k;
-  // Round 1: the top kTopPairs pairs of every chunk.  The counts are then complete at and
-  // above the highest last-read bin of the truncated chunks (the floor).
-  const int nq = a.n_sc * kTopPairs;
-  for (int base = 0; base < nq && !fail; base += 256 * 8) {
-    const uint64_t* pp[8];
-    bool use[8];
-    uint32_t v[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int i = base + tid + 256 * u, sl = i / kTopPairs, j = i % kTopPairs;
-      use[u] = i < nq && (uint32_t)j < np[sl < a.n_sc ? sl : 0];
-      pp[u] = rowsum + (size_t)(use[u] ? sl : 0) * a.k + (use[u] ? j : 0);
-    }
-    read_tagged<8>(x, pp, use, v, &fail);
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      if (!use[u] || fail) continue;
-      const int i = base + tid + 256 * u, sl = i / kTopPairs, j = i % kTopPairs;
-      atomicAdd(&hist[v[u] >> 20], v[u] & 0xfffffu);
-      if (j == kTopPairs - 1 && np[sl] > (uint32_t)kTopPairs) atomicMax(&x.scr[S_FLOOR], v[u] >> 20);
-    }
-  }
-  if (!all_ok(x, fail)) return false;
-  const uint32_t k_eff = (uint32_t)(f.n_vis < a.k ? f.n_vis : a.k);
-  uint32_t b1 = kFBins, above = 0;  // k_eff == 0: nothing is selected
-  if (k_eff > 0) {
-    const uint32_t floor_bin = x.scr[S_FLOOR];
-    b1 = kth_bin(hist, k_eff, x.scr, &above);
-    if (b1 > kFBins || b1 < floor_bin) {
-      // Round 2 (rare): the rest of the truncated chunks' pairs, one chunk per thread
-      for (int sl = tid; sl < a.n_sc && !fail; sl += 256) {
-        const uint32_t n = np[sl];
-        for (uint32_t j0 = kTopPairs; j0 < n && !fail; j0 += 8) {
-          const uint64_t* pp[8];
-          bool use[8];
-          uint32_t v[8];
-#pragma unroll
-          for (int u = 0; u < 8; ++u) {
-            use[u] = j0 + u < n;
-            pp[u] = rowsum + (size_t)sl * a.k + (use[u] ? j0 + u : 0);
-          }
-          read_tagged<8>(x, pp, use, v, &fail);
-#pragma unroll
-          for (int u = 0; u < 8; ++u)
-            if (use[u] && !fail) atomicAdd(&hist[v[u] >> 20], v[u] & 0xfffffu);
-        }
+  // keys -> workspace (read only by the exact fallback), 16 bytes per store
+  {
+    uint32_t* gk = a.keys + (size_t)r * a.key_stride + j0;
+    for (int i = 4 * tid; i < n; i += 1024) {
+      if (i + 3 < n) {
+        const v4u_t u = {keys_s[i], keys_s[i + 1], keys_s[i + 2], keys_s[i + 3]};
+        coh_st128(x.coh, gk + i, u);
+      } else {
+        for (int e = i; e < n; ++e)
+          __builtin_amdgcn_raw_buffer_store_b32(keys_s[e], x.coh.r, coh_off(x.coh, gk + e), 0, kSc1);
       }
-      if (!all_ok(x, fail)) return false;
-      b1 = kth_bin(hist, k_eff, x.scr, &above);
     }
   }
-  if (tid == 0) st_dev64(a.thr + (size_t)r * kThrStride, tagged(x.tag, (above << 13) | b1));
-  __syncthreads();
-  return true;
-}
-
-// ---------------------------------------------------------------------------
-// emit: definite indices and candidates of chunk c, ascending
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ bool phase_emit(const FCtx& x, int r, int c, int n) {
-  const FusedArgs& a = *x.a;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  bool fail = false;
-  if (tid == 0) x.scr[S_B1] = poll_word(x, a.thr + (size_t)r * kThrStride, &fail) & 0x1fffu;
-  if (!all_ok(x, fail)) return false;
-  const uint32_t b1 = x.scr[S_B1];
-  const uint32_t* keys_s = reinterpret_cast<const uint32_t*>(x.smem + kOffKeys);
-  // thread t owns local entries [t*E, t*E + E)
-  const int E = (n + 255) / 256;
+  // local emit_q-th bin bq: every entry above it, and entries in it while room remains
+  const uint32_t q = n < a.emit_q ? (uint32_t)n : (uint32_t)a.emit_q;
+  uint32_t bq = 0, ab = 0;
+  if (q > 0) bq = kth_bin(hist, q, x.scr, &ab);
+  const int E = (n + 255) / 256;  // thread t owns local entries [t*E, t*E + E)
   const int e0 = tid * E;
   uint32_t ng = 0, ne = 0;
   for (int i = 0; i < E; ++i) {
     const int jl = e0 + i;
     if (jl < n) {
       const uint32_t bin = keys_s[jl] >> 19;
-      ng += bin > b1 ? 1u : 0u;
-      ne += bin == b1 ? 1u : 0u;
+      ng += bin > bq ? 1u : 0u;
+      ne += bin == bq ? 1u : 0u;
     }
   }
   uint32_t sg = ng, se = ne;  // inclusive prefix within the wave
@@ -544,27 +445,29 @@ __device__ __forceinline__ bool phase_emit(const FCtx& x, int r, int c, int n) {
   }
   const uint32_t tg = x.scr[0] + x.scr[1] + x.scr[2] + x.scr[3];
   const uint32_t te = x.scr[4] + x.scr[5] + x.scr[6] + x.scr[7];
+  const uint32_t cap_eq = (uint32_t)a.emit_max - tg;  // tg < q <= emit_q < emit_max
+  const uint32_t n_emit = tg + (te < cap_eq ? te : cap_eq);
   const size_t slot = (size_t)r * a.n_sc + c;
-  uint64_t* dd = a.defw + slot * a.def_cap;
-  uint64_t* cd = a.candw + slot * 2 * a.C;
+  uint64_t* dst = a.ent + slot * a.emit_max;
   const uint32_t jbase = (uint32_t)c * (uint32_t)a.C;
+  uint32_t pos = pg + (pe < cap_eq ? pe : cap_eq);
   for (int i = 0; i < E; ++i) {
     const int jl = e0 + i;
     if (jl < n) {
-      const uint32_t key = keys_s[jl];
-      const uint32_t bin = key >> 19;
-      if (bin > b1) {
-        st_dev64(dd + pg++, tagged(x.tag, jbase + (uint32_t)jl));
-      } else if (bin == b1) {
-        st_dev64(cd + 2 * pe, tagged(x.tag, jbase + (uint32_t)jl));
-        st_dev64(cd + 2 * pe + 1, tagged(x.tag, key));
-        ++pe;
+      const uint32_t key = keys_s[jl], bin = key >> 19;
+      bool take = bin > bq;
+      if (bin == bq) take = pe++ < cap_eq;
+      if (take) {
+        const uint64_t w64 = ((uint64_t)key << 32) | (jbase + (uint32_t)jl);
+        __builtin_amdgcn_raw_buffer_store_b64(v2u_t{(uint32_t)w64, (uint32_t)(w64 >> 32)}, x.coh.r,
+                                              coh_off(x.coh, dst + pos), 0, kSc1);
+        ++pos;
       }
     }
   }
-  if (tid == 0) st_dev64(a.emit_hdr + slot, tagged(x.tag, (tg << 12) | te));
+  vm_drain();
   __syncthreads();
-  return true;
+  if (tid == 0) st_dev64(a.ent_hdr + slot, tagged(x.tag, n_emit | (bq << 12) | ((te > cap_eq ? 1u : 0u) << 25)));
 }
 
 // ---------------------------------------------------------------------------
@@ -609,15 +512,17 @@ __device__ __forceinline__ void write_partial(const FCtx& x, AttnState<1>& st, i
 // selected list -> idx_s (and, for split 0, the whole row -> idx).  false on a
 // failed wait.
 //
-// The row's selected set is every definite index plus the candidates (keys in
-// the threshold bin) that come first in (key descending, index ascending)
-// order, need = k_eff - definites of them.  The need-th candidate (K*, j*) is
-// found by ranking every candidate against all others (at most kFRankMax
-// candidates) or by a radix select; candidate (key, j) is chosen when
-// key > K* or (key == K* and j <= j*).  Chunks cover ascending index ranges,
-// so the position of a selected index is the selected count of the earlier
-// chunks plus its rank among its own chunk's definites and chosen candidates,
-// both of which are stored in ascending order.
+// The selected set is the k_eff first entries in (key descending, index
+// ascending) order, i.e. the entries whose order key (key << 32 | ~index) is
+// at least that of the k_eff-th one, c*.  Each score chunk emitted every entry
+// above its local emit_q-th bin bq (and that bin's entries up to emit_max,
+// else it is marked truncated).  From the emitted entries of the row: b1 = the
+// bin of the k_eff-th largest, and c* = the need-th largest order key in bin
+// b1.  This is exact when every chunk emitted all its entries in bins >= b1:
+// bq <= b1 (bq < b1 when truncated).  Otherwise c* comes from an exact radix
+// select over the row's stored keys.  Chunks cover ascending index ranges and
+// emit in index order, so the position of a selected index is the selected
+// count of the earlier chunks plus its rank within its chunk.
 __device__ __forceinline__ bool select_split(const FCtx& x, int r, int s, const FRow& f) {
   const FusedArgs& a = *x.a;
   const int tid = threadIdx.x;
@@ -629,170 +534,166 @@ __device__ __forceinline__ bool select_split(const FCtx& x, int r, int s, const 
   for (int i = tid; i < a.cs; i += 256) idx_s[i] = -1;
   const bool needs_sel = (s == 0) || (p_begin < k_eff);
   if (needs_sel && k_eff > 0) {
-    // per-chunk counts -> exclusive prefix sums (LDS, over the key region)
-    uint32_t* def_off = reinterpret_cast<uint32_t*>(x.smem + kOffKeys);
-    uint32_t* cand_off = def_off + (kFMaxSlots + 1);
-    uint32_t* sel_off = cand_off + (kFMaxSlots + 1);
+    uint32_t* e_off = reinterpret_cast<uint32_t*>(x.smem + kOffKeys);  // per chunk, LDS
+    uint32_t* e_bq = e_off + (kFMaxSlots + 1);
+    uint32_t* sel_off = e_bq + (kFMaxSlots + 1);
+    uint64_t* ent_s = reinterpret_cast<uint64_t*>(x.smem + kOffEnt);
+    uint32_t* hist = reinterpret_cast<uint32_t*>(x.smem + kOffHist);
+    const uint64_t* rowent = a.ent + (size_t)r * a.n_sc * a.emit_max;
+    const uint32_t* rowkeys = a.keys + (size_t)r * a.key_stride;
     bool fail = false;
-    if (tid == 0) x.scr[S_B1] = poll_word(x, a.thr + (size_t)r * kThrStride, &fail) & 0x1fffu;
     for (int sl = tid; sl < a.n_sc && !fail; sl += 256) {
-      const uint32_t v = poll_word(x, a.emit_hdr + (size_t)r * a.n_sc + sl, &fail);
-      def_off[sl] = v >> 12;
-      cand_off[sl] = v & 0xfffu;
+      const uint32_t v = poll_word(x, a.ent_hdr + (size_t)r * a.n_sc + sl, &fail, 2u);
+      e_off[sl] = v & 0xfffu;
+      e_bq[sl] = v >> 12;  // bin | truncated << 13
     }
+    for (int i = tid; i < kFBins; i += 256) hist[i] = 0;
+    if (tid == 0) x.scr[S_BAD] = 0;
     if (!all_ok(x, fail)) return false;
-    const uint32_t b1 = x.scr[S_B1];
-    block_exscan(def_off, a.n_sc, x.scr);
-    block_exscan(cand_off, a.n_sc, x.scr);
-    const uint32_t n_def = def_off[a.n_sc], n_c = cand_off[a.n_sc];
-    const uint32_t need = (uint32_t)k_eff - n_def;
-    uint2* cand_s = reinterpret_cast<uint2*>(x.smem + kOffCand);
-    const bool in_lds = n_c <= (uint32_t)kFCandLds;
-    auto cand_src = [&](uint32_t i) -> const uint64_t* {
-      const int sl = upper_slot(cand_off, a.n_sc, i);
-      return a.candw + ((size_t)r * a.n_sc + sl) * 2 * a.C + 2 * (i - cand_off[sl]);
-    };
-    // candidate i of the row: (key, index)
-    auto cand_global = [&](uint32_t i, bool* fl) -> uint2 {
-      const uint64_t* src = cand_src(i);
-      const uint32_t j = poll_word(x, src, fl);
-      const uint32_t key = poll_word(x, src + 1, fl);
-      return make_uint2(key, j);
-    };
-    if (in_lds) {  // one chunk per thread, 8 candidates (16 words) per round
-      for (int sl = tid; sl < a.n_sc && !fail; sl += 256) {
-        const uint32_t c0 = cand_off[sl], nc = cand_off[sl + 1] - c0;
-        const uint64_t* src = a.candw + ((size_t)r * a.n_sc + sl) * 2 * a.C;
-        for (uint32_t i0 = 0; i0 < nc && !fail; i0 += 8) {
-          const uint64_t* pp[16];
-          bool use[16];
-          uint32_t v[16];
+    block_exscan(e_off, a.n_sc, x.scr);
+    const uint32_t n_ent = uni(e_off[a.n_sc]);
+    bool exact = n_ent <= (uint32_t)kFEntLds && n_ent >= (uint32_t)k_eff;
+    if (exact) {
+      // emitted entries -> LDS order keys, in global index order: wave w takes chunks
+      // w, w+4, ..., lane = entry within the chunk, 16 chunks in flight
+      const int lane = tid & 63, wave = tid >> 6;
+      for (int i0 = 0; i0 < a.emit_max; i0 += 64) {
+        const uint32_t i = (uint32_t)(i0 + lane);
+        for (int sb = wave; sb < a.n_sc; sb += 64) {
+          uint64_t v[16];
 #pragma unroll
           for (int u = 0; u < 16; ++u) {
-            use[u] = i0 + (u >> 1) < nc;
-            pp[u] = src + (use[u] ? 2 * (i0 + (u >> 1)) + (u & 1) : 0);
+            const int sl = sb + 4 * u;
+            v[u] = (sl < a.n_sc && i < e_off[sl + 1] - e_off[sl]) ? coh_ld64(x.coh, rowent + (size_t)sl * a.emit_max + i)
+                                                                  : 0ull;
           }
-          read_tagged<16>(x, pp, use, v, &fail);
 #pragma unroll
-          for (int u = 0; u < 8; ++u)
-            if (use[2 * u]) cand_s[c0 + i0 + u] = make_uint2(v[2 * u + 1], v[2 * u]);
+          for (int u = 0; u < 16; ++u) {
+            const int sl = sb + 4 * u;
+            if (sl < a.n_sc && i < e_off[sl + 1] - e_off[sl]) {
+              const uint32_t key = (uint32_t)(v[u] >> 32), j = (uint32_t)v[u];
+              ent_s[e_off[sl] + i] = ((uint64_t)key << 32) | (uint32_t)~j;
+              atomicAdd(&hist[key >> 19], 1u);
+            }
+          }
         }
       }
-    }
-    if (!all_ok(x, fail)) return false;
-    // the need-th candidate (K*, j*)
-    if (tid == 0) {
-      x.scr[S_KSTAR] = 0xffffffffu;  // need == 0: no candidate is chosen
-      x.scr[S_JSTAR] = 0;
-    }
-    __syncthreads();
-    if (need > 0) {
-      if (in_lds && n_c <= (uint32_t)kFRankMax) {
-        // order key (key, ~index): larger ranks first.  Padded to a multiple of 16 with
-        // zero keys, which rank after every candidate.
-        uint64_t* comp = reinterpret_cast<uint64_t*>(x.smem + kOffComp);
-        const uint32_t n_pad = (n_c + 15) & ~15u;
-        for (uint32_t i = tid; i < n_pad; i += 256)
-          comp[i] = i < n_c ? ((uint64_t)cand_s[i].x << 32) | (uint32_t)~cand_s[i].y : 0ull;
+      __syncthreads();
+      uint32_t above = 0;
+      const uint32_t b1 = kth_bin(hist, (uint32_t)k_eff, x.scr, &above);
+      // every chunk must have emitted all of its entries in bins >= b1
+      for (int sl = tid; sl < a.n_sc; sl += 256) {
+        const uint32_t bq = e_bq[sl] & 0x1fffu, trunc = e_bq[sl] >> 13;
+        if (trunc ? bq >= b1 : bq > b1) x.scr[S_BAD] = 1;
+      }
+      if (tid == 0) x.scr[S_NB1] = 0;
+      __syncthreads();
+      exact = uni(x.scr[S_BAD]) == 0;
+      if (exact) {
+        // the bin-b1 entries, ranked by order key (the histogram area is free now)
+        uint64_t* comp = reinterpret_cast<uint64_t*>(x.smem + kOffHist);
+        for (uint32_t i0 = 0; i0 < n_ent; i0 += 256) {
+          const uint32_t i = i0 + tid;
+          const uint64_t e = i < n_ent ? ent_s[i] : 0ull;
+          const bool hit = i < n_ent && (uint32_t)(e >> 51) == b1;
+          const uint64_t m = __ballot(hit);
+          uint32_t base = 0;
+          if ((tid & 63) == 0 && m) base = atomicAdd(&x.scr[S_NB1], (uint32_t)__popcll(m));
+          base = __shfl(base, 0);
+          const uint32_t slot_i = base + (uint32_t)__popcll(m & ((1ull << (tid & 63)) - 1ull));
+          if (hit && slot_i < (uint32_t)kFRankMax) comp[slot_i] = e;
+        }
         __syncthreads();
-        for (uint32_t i = tid; i < n_c; i += 256) {
-          const uint64_t ci = comp[i];
-          uint32_t rank = 0;
-          for (uint32_t j0 = 0; j0 < n_pad; j0 += 16) {
-            uint64_t q[16];
+        const uint32_t nb = uni(x.scr[S_NB1]);
+        exact = nb <= (uint32_t)kFRankMax;
+        if (exact) {
+          const uint32_t need = (uint32_t)k_eff - above;  // >= 1
+          const uint32_t n_pad = (nb + 15) & ~15u;
+          for (uint32_t i = nb + tid; i < n_pad; i += 256) comp[i] = 0ull;
+          __syncthreads();
+          for (uint32_t i = tid; i < nb; i += 256) {
+            const uint64_t ci = comp[i];
+            uint32_t rank = 0;
+            for (uint32_t j0 = 0; j0 < n_pad; j0 += 16) {
+              uint64_t qv[16];
 #pragma unroll
-            for (int u = 0; u < 16; ++u) q[u] = comp[j0 + u];
+              for (int u = 0; u < 16; ++u) qv[u] = comp[j0 + u];
 #pragma unroll
-            for (int u = 0; u < 16; ++u) rank += q[u] > ci ? 1u : 0u;
+              for (int u = 0; u < 16; ++u) rank += qv[u] > ci ? 1u : 0u;
+            }
+            if (rank == need - 1) {
+              x.scr[S_CSTAR_LO] = (uint32_t)ci;
+              x.scr[S_CSTAR_HI] = (uint32_t)(ci >> 32);
+            }
           }
-          if (rank == need - 1) {
-            x.scr[S_KSTAR] = (uint32_t)(ci >> 32);
-            x.scr[S_JSTAR] = ~(uint32_t)ci;
-          }
+          __syncthreads();
         }
-      } else {
-        // every candidate key shares its top 13 bits (bin b1); every index < 2^18, so ~index
-        // starts with 14 ones.  A tie class too large for LDS is re-read from the workspace.
-        bool fl = false;
-        uint32_t* bins = reinterpret_cast<uint32_t*>(x.smem + kOffRadix);
-        auto cand = [&](uint32_t i) -> uint2 { return in_lds ? cand_s[i] : cand_global(i, &fl); };
-        uint32_t rr, r2;
-        const uint32_t ks = radix_select_desc_low(n_c, need, 19, b1 << 19, [&](uint32_t i) { return cand(i).x; },
-                                                  [&](uint32_t) { return true; }, &rr, bins, x.scr);
-        const uint32_t js = radix_select_desc_low(n_c, rr, 18, 0xfffc0000u, [&](uint32_t i) { return ~cand(i).y; },
-                                                  [&](uint32_t i) { return cand(i).x == ks; }, &r2, bins, x.scr);
-        if (tid == 0) {
-          x.scr[S_KSTAR] = ks;
-          x.scr[S_JSTAR] = ~js;
+      }
+    }
+    if (!exact) {
+      // exact radix select over the row's stored keys: the k_eff-th largest key K*, then
+      // the (need_left)-th smallest index among keys equal to K* (indices < 2^18)
+      uint32_t* bins = hist;
+      uint32_t nl;
+      const uint32_t n_vis = (uint32_t)f.n_vis;
+      const uint32_t kstar = radix_select_desc(
+          n_vis, (uint32_t)k_eff, [&](uint32_t i) { return coh_ld32(x.coh, rowkeys + i); },
+          [&](uint32_t) { return true; }, &nl, bins, x.scr);
+      uint32_t nl2;
+      const uint32_t njstar = radix_select_desc_low(
+          n_vis, nl, 18, 0xfffc0000u, [&](uint32_t i) { return ~i; },
+          [&](uint32_t i) { return coh_ld32(x.coh, rowkeys + i) == kstar; }, &nl2, bins, x.scr);
+      if (tid == 0) {
+        x.scr[S_CSTAR_LO] = njstar;
+        x.scr[S_CSTAR_HI] = kstar;
+      }
+      __syncthreads();
+    }
+    const uint64_t cstar = ((uint64_t)uni(x.scr[S_CSTAR_HI]) << 32) | uni(x.scr[S_CSTAR_LO]);
+    auto emit_at = [&](uint32_t pos, uint32_t j) {
+      if ((int64_t)pos >= p_begin && (int64_t)pos < p_end) idx_s[pos - p_begin] = (int32_t)j;
+      if (s == 0 && pos < (uint32_t)a.k) idx_out[pos] = (int32_t)j;
+    };
+    if (exact) {
+      // the entries are in index order: position = selected entries before it.  Thread t
+      // owns entries [t*M, t*M + M); one block scan of the per-thread counts.
+      const uint32_t M = (n_ent + 255) / 256, m0 = tid * M;
+      uint32_t cnt = 0;
+      for (uint32_t i = m0; i < m0 + M && i < n_ent; ++i) cnt += ent_s[i] >= cstar ? 1u : 0u;
+      sel_off[tid] = cnt;
+      __syncthreads();
+      block_exscan(sel_off, 256, x.scr);
+      uint32_t pos = sel_off[tid];
+      const uint32_t pend = sel_off[tid + 1];
+      if (pos < pend && (s == 0 || ((int64_t)pos < p_end && (int64_t)pend > p_begin))) {
+        for (uint32_t i = m0; i < m0 + M && i < n_ent; ++i) {
+          const uint64_t e = ent_s[i];
+          if (e >= cstar) emit_at(pos++, ~(uint32_t)e);
         }
+      }
+    } else {
+      const int C = a.C;
+      const uint32_t nv = n_vis_u32(f);
+      // selected count per chunk -> offsets, then the chunks in index order
+      for (int sl = tid; sl < a.n_sc; sl += 256) {
+        uint32_t cnt = 0;
+        const uint32_t jb = (uint32_t)sl * C, je = jb + C < nv ? jb + C : nv;
+        for (uint32_t j = jb; j < je; ++j)
+          cnt += (((uint64_t)coh_ld32(x.coh, rowkeys + j) << 32) | (uint32_t)~j) >= cstar ? 1u : 0u;
+        sel_off[sl] = cnt;
+      }
+      __syncthreads();
+      block_exscan(sel_off, a.n_sc, x.scr);
+      for (int sl = tid; sl < a.n_sc; sl += 256) {
+        uint32_t pos = sel_off[sl];
+        const uint32_t pend = sel_off[sl + 1];
+        if (pos == pend || (s != 0 && ((int64_t)pos >= p_end || (int64_t)pend <= p_begin))) continue;
+        const uint32_t jb = (uint32_t)sl * C, je = jb + C < nv ? jb + C : nv;
+        for (uint32_t j = jb; j < je; ++j)
+          if ((((uint64_t)coh_ld32(x.coh, rowkeys + j) << 32) | (uint32_t)~j) >= cstar) emit_at(pos++, j);
       }
     }
     __syncthreads();
-    const uint32_t kstar = x.scr[S_KSTAR], jstar = x.scr[S_JSTAR];
-    auto chosen = [&](uint2 c) { return c.x > kstar || (c.x == kstar && c.y <= jstar); };
-    // selected count per chunk -> offsets
-    for (int sl = tid; sl < a.n_sc; sl += 256) {
-      uint32_t cnt = def_off[sl + 1] - def_off[sl];
-      const uint32_t c0 = cand_off[sl], c1 = cand_off[sl + 1];
-      for (uint32_t i = c0; i < c1; ++i) {
-        bool fl = false;
-        cnt += chosen(in_lds ? cand_s[i] : cand_global(i, &fl)) ? 1u : 0u;
-      }
-      sel_off[sl] = cnt;
-    }
-    __syncthreads();
-    block_exscan(sel_off, a.n_sc, x.scr);
-    // chunks overlapping this split's positions (every chunk for split 0): ordered merge
-    for (int sl = tid; sl < a.n_sc && !fail; sl += 256) {
-      uint32_t pos = sel_off[sl];
-      const uint32_t pend = sel_off[sl + 1];
-      if (pos == pend || (s != 0 && ((int64_t)pos >= p_end || (int64_t)pend <= p_begin))) continue;
-      auto emit = [&](uint32_t j) {
-        if ((int64_t)pos >= p_begin && (int64_t)pos < p_end) idx_s[pos - p_begin] = (int32_t)j;
-        if (s == 0 && pos < (uint32_t)a.k) idx_out[pos] = (int32_t)j;
-        ++pos;
-      };
-      const uint32_t nd = def_off[sl + 1] - def_off[sl];
-      const uint32_t c1 = cand_off[sl + 1];
-      uint32_t m = cand_off[sl];
-      auto next_chosen = [&]() -> uint32_t {  // index of the next chosen candidate, or ~0
-        for (; m < c1; ++m) {
-          bool fl = false;
-          const uint2 c = in_lds ? cand_s[m] : cand_global(m, &fl);
-          if (chosen(c)) return c.y;
-        }
-        return 0xffffffffu;
-      };
-      uint32_t cn = next_chosen();
-      const uint64_t* src = a.defw + ((size_t)r * a.n_sc + sl) * a.def_cap;
-      for (uint32_t i0 = 0; i0 < nd && !fail; i0 += 16) {
-        const uint64_t* pp[16];
-        bool use[16];
-        uint32_t v[16];
-#pragma unroll
-        for (int u = 0; u < 16; ++u) {
-          use[u] = i0 + u < nd;
-          pp[u] = src + (use[u] ? i0 + u : 0);
-        }
-        read_tagged<16>(x, pp, use, v, &fail);
-#pragma unroll
-        for (int u = 0; u < 16; ++u) {
-          if (!use[u]) continue;
-          while (cn < v[u]) {
-            emit(cn);
-            ++m;
-            cn = next_chosen();
-          }
-          emit(v[u]);
-        }
-      }
-      while (cn != 0xffffffffu) {
-        emit(cn);
-        ++m;
-        cn = next_chosen();
-      }
-    }
-    if (!all_ok(x, fail)) return false;
   }
   if (s == 0)
     for (int i = k_eff + tid; i < a.k; i += 256) idx_out[i] = -1;
@@ -847,7 +748,7 @@ __device__ __forceinline__ void item_merge(const FCtx& x, bool hca, int r, int h
   const int n = hca ? a.n_hs : n_cs;
   const uint64_t* hdr = a.part_hdr + (size_t)r * (n_cs + a.n_hs) + (hca ? n_cs : 0);
   bool fail = false;
-  for (int s = tid; s < n && !fail; s += 256) (void)poll_word(x, hdr + s, &fail);
+  for (int s = tid; s < n && !fail; s += 256) (void)poll_word(x, hdr + s, &fail, hca ? 8u : 4u);
   if (!all_ok(x, fail)) return;
   const float* po = hca ? a.hca_po : a.csa_po;
   const float* pml = hca ? a.hca_pml : a.csa_pml;
@@ -913,41 +814,46 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     scr[S_TAG] = tag;
   }
   __syncthreads();
-  const FCtx x{&a, smem, scr, scr[S_TAG], make_coh(a.ctl)};
+  const FCtx x{&a, smem, scr, uni(scr[S_TAG]), make_coh(a.ctl)};
   __syncthreads();
-  const int G = (int)gridDim.x, w = (int)blockIdx.x;
-  bool ok = true;
-  // ---- score / reduce / emit: chunk w
-  if (w < a.R * a.n_sc) {
-    const int r = w / a.n_sc, c = w % a.n_sc;
-    const FRow f = row_info(a, r);
-    int64_t j0 = (int64_t)c * a.C, j1 = j0 + a.C;
-    if (j1 > f.n_vis) j1 = f.n_vis;
-    if (j0 > j1) j0 = j1;
-    phase_score(x, r, c, f, j0, j1);
-    if (c == 0) ok = phase_reduce(x, r, f);
-    if (ok) ok = phase_emit(x, r, c, (int)(j1 - j0));
-  }
-  // ---- items
-  if (ok) {
-    const int R = a.R, nM = a.H / 4;
-    const int64_t e1 = (int64_t)R * a.n_cs_sel, e2 = e1 + (int64_t)R * a.n_cs_win,
-                  e3 = e2 + (int64_t)R * a.n_hs, e4 = e3 + (int64_t)R * nM, total = e4 + (int64_t)R * nM;
-    for (int64_t it = w; it < total; it += G) {
-      __syncthreads();
-      if (error_seen(x)) break;
-      if (it >= e3) {
-        const bool hca = it >= e4;
-        const int64_t m = it - (hca ? e4 : e3);
-        item_merge(x, hca, (int)(m / nM), (int)(m % nM) * 4);
-        continue;
-      }
+  const int G = (int)gridDim.x;
+  // Work units in dependency order: the R * n_sc score chunks, then the items
+  // [CSA selected splits | CSA window splits | HCA splits | CSA merges | HCA
+  // merges].  Units are handed out in that order through one returning atomic,
+  // and a unit only waits for units of lower number, whose holders are already
+  // running: every wait ends whatever the residency of the grid.
+  const int R = a.R, nM = a.H / 4;
+  const int64_t nS = (int64_t)R * a.n_sc;
+  const int64_t e1 = nS + (int64_t)R * a.n_cs_sel, e2 = e1 + (int64_t)R * a.n_cs_win,
+                e3 = e2 + (int64_t)R * a.n_hs, e4 = e3 + (int64_t)R * nM, total = e4 + (int64_t)R * nM;
+  // Every workgroup runs the same number of rounds (rounds * grid >= total), so
+  // the loop bound is uniform; a round whose unit number is past the end (or
+  // that follows a reported error) does nothing.
+  for (int round = 0; round < a.rounds; ++round) {
+    if (threadIdx.x == 0) scr[S_TICKET] = error_seen(x) ? 0xffffffffu : atomicAdd(a.ctl + W_TICKET, 1u);
+    __syncthreads();
+    const int64_t it = uni(scr[S_TICKET]);
+    __syncthreads();
+    if (it >= total) {
+      // nothing to do this round
+    } else if (it < nS) {
+      const int r = (int)(it / a.n_sc), c = (int)(it % a.n_sc);
+      const FRow f = row_info(a, r);
+      int64_t j0 = (int64_t)c * a.C, j1 = j0 + a.C;
+      if (j1 > f.n_vis) j1 = f.n_vis;
+      if (j0 > j1) j0 = j1;
+      phase_score(x, r, c, f, j0, j1);
+    } else if (it >= e3) {
+      const bool hca = it >= e4;
+      const int64_t m = it - (hca ? e4 : e3);
+      item_merge(x, hca, (int)(m / nM), (int)(m % nM) * 4);
+    } else {
       const int kind = it < e1 ? 0 : it < e2 ? 1 : 2;
-      const int64_t q = it - (kind == 0 ? 0 : kind == 1 ? e1 : e2);
+      const int64_t q = it - (kind == 0 ? nS : kind == 1 ? e1 : e2);
       const int r = (int)(q % R), s = (int)(q / R);
       const FRow f = row_info(a, r);
-      if (kind == 0 && !select_split(x, r, s, f)) continue;
-      attend_item(x, r, kind, s, f);
+      const bool ok = kind != 0 || select_split(x, r, s, f);
+      if (ok) attend_item(x, r, kind, s, f);
     }
   }
   // ---- the last workgroup out advances the epoch
@@ -956,6 +862,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     vm_drain();
     if (atomicAdd(a.ctl + W_EXIT, 1u) == (uint32_t)G - 1) {
       st_dev(a.ctl + W_EXIT, 0u);
+      st_dev(a.ctl + W_TICKET, 0u);
       st_dev(a.ctl + W_EPOCH, x.tag);
     }
   }
@@ -1002,18 +909,23 @@ FusedPlan plan_fused(int64_t R, int64_t max_pool, int64_t max_hpool, int H, int 
   p.hs = 128;
   p.n_hs = split_count(max_hpool + W_hca, p.hs);
   if (p.n_hs == 0) p.n_hs = 1;
-  p.def_cap = (int)(p.C < k ? p.C : k);
+  // emitted per chunk: about twice a chunk's expected share of the top-k, plus slack
+  const int64_t share = p.n_sc > 0 ? ((int64_t)k + p.n_sc - 1) / p.n_sc : k;
+  int64_t q = 2 * share + 16;
+  if (q > p.C) q = p.C;
+  int64_t qm = q + 16;
+  if (qm > p.C) qm = p.C;
+  p.emit_q = (int)q;
+  p.emit_max = (int)qm;
+  p.key_stride = (max_pool + 3) & ~(int64_t)3;
   auto al = [](size_t b) { return (b + 255) & ~(size_t)255; };
   const size_t slots = (size_t)R * p.n_sc;
   const int n_cs = p.n_cs_sel + p.n_cs_win;
   size_t s = 0;
   s += al(W_CTL * 4);
+  s += al((size_t)R * p.key_stride * 4);
   s += al(slots * 8);
-  s += al(slots * k * 8);
-  s += al((size_t)R * kThrStride * 8);
-  s += al(slots * 8);
-  s += al(slots * p.def_cap * 8);
-  s += al(slots * 2 * p.C * 8);
+  s += al(slots * p.emit_max * 8);
   s += al((size_t)R * (n_cs + p.n_hs) * 8);
   s += al((size_t)R * n_cs * H * 128 * 4);
   s += al((size_t)R * n_cs * H * 2 * 4);
@@ -1058,14 +970,17 @@ int launch_fused(int R, const int64_t* tok_off, const int64_t* q_pos, const int6
   a.kv_raw = (const uint8_t*)kv_raw;
   a.idx = idx; a.csa_out = (uint8_t*)csa_out; a.csa_lse = csa_lse; a.hca_out = (uint8_t*)hca_out; a.hca_lse = hca_lse;
   a.C = pl.C; a.n_sc = pl.n_sc; a.cs = pl.cs; a.n_cs_sel = pl.n_cs_sel; a.n_cs_win = pl.n_cs_win;
-  a.hs = pl.hs; a.n_hs = pl.n_hs; a.def_cap = pl.def_cap;
+  a.hs = pl.hs; a.n_hs = pl.n_hs;
+  a.emit_q = pl.emit_q; a.emit_max = pl.emit_max; a.key_stride = pl.key_stride;
+  {
+    const int64_t units = (int64_t)R * pl.n_sc + (int64_t)R * (pl.n_cs_sel + pl.n_cs_win + pl.n_hs) +
+                          2 * (int64_t)R * (H / 4);
+    a.rounds = (int)((units + pl.grid - 1) / pl.grid);
+  }
   a.ctl = (uint32_t*)take(W_CTL * 4);
-  a.sum_hdr = (uint64_t*)take(slots * 8);
-  a.sum = (uint64_t*)take(slots * k * 8);
-  a.thr = (uint64_t*)take((size_t)R * kThrStride * 8);
-  a.emit_hdr = (uint64_t*)take(slots * 8);
-  a.defw = (uint64_t*)take(slots * pl.def_cap * 8);
-  a.candw = (uint64_t*)take(slots * 2 * pl.C * 8);
+  a.keys = (uint32_t*)take((size_t)R * pl.key_stride * 4);
+  a.ent_hdr = (uint64_t*)take(slots * 8);
+  a.ent = (uint64_t*)take(slots * pl.emit_max * 8);
   a.part_hdr = (uint64_t*)take((size_t)R * (n_cs + pl.n_hs) * 8);
   a.csa_po = (float*)take((size_t)R * n_cs * H * 128 * 4);
   a.csa_pml = (float*)take((size_t)R * n_cs * H * 2 * 4);
@@ -1073,8 +988,9 @@ int launch_fused(int R, const int64_t* tok_off, const int64_t* q_pos, const int6
   a.hca_pml = (float*)take((size_t)R * pl.n_hs * H * 2 * 4);
   void* args[] = {&a};
   prof_begin(6, stream);
-  const hipError_t e = hipLaunchCooperativeKernel((const void*)k_decode_fused, dim3((unsigned)pl.grid), dim3(256),
-                                                  args, kFusedLds, stream);
+  // an ordinary launch: correctness does not depend on all workgroups being resident
+  const hipError_t e =
+      hipLaunchKernel((const void*)k_decode_fused, dim3((unsigned)pl.grid), dim3(256), args, kFusedLds, stream);
   prof_end(6, stream);
   if (e != hipSuccess) return -1;
   return hipGetLastError() == hipSuccess ? 0 : -1;

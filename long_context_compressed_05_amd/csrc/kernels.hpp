@@ -38,7 +38,8 @@ struct FusedPlan {
   int C, n_sc;                  // score entries per chunk, chunks per row
   int cs, n_cs_sel, n_cs_win;   // CSA split size, selected and window splits per row
   int hs, n_hs;                 // HCA split size, splits per row
-  int def_cap;
+  int emit_q, emit_max;         // per score chunk: local bin rank emitted, entry capacity
+  int64_t key_stride;
   size_t ws_bytes;
 };
 FusedPlan plan_fused(int64_t R, int64_t max_pool, int64_t max_hpool, int H, int k, int W, int W_hca);
