@@ -2,10 +2,13 @@
 """CSA + HCA decode benchmark on one MI355X (gfx950).
 
 One step = one pass of the whole decode hot path over one batch: indexer
-scoring + exact top-k (csa_index_topk), CSA sparse attention over the top-k
-pooled rows plus the sliding window (csa_sparse_attn), and HCA dense attention
-(hca_attn), for every sequence's query at position T-1.  Pooled caches are
-built once with csa_compress before timing (its throughput is reported apart).
+scoring, exact top-k, CSA sparse attention over the top-k pooled rows plus the
+sliding window, and HCA dense attention, for every sequence's query at
+position T-1.  By default the step is the single-launch csa_hca_decode call;
+--path separate times csa_index_topk + csa_sparse_attn + hca_attn instead.
+Pooled caches are built once with csa_compress before timing (its throughput
+is reported apart).  --copy-calibration runs only a 1 GiB device copy, the
+scale reference for the HBM byte counters.
 
 Default workload: 4 sequences x 1,048,576 tokens, 64 query heads on one bf16
 KV head, d = 128, m = 4 (262,144 pooled entries), top-k 1024, window 128,
@@ -56,8 +59,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of a captured HIP graph")
-    ap.add_argument("--path", choices=["fused", "separate"], default="separate",
+    ap.add_argument("--path", choices=["fused", "separate"], default="fused",
                     help="fused: one csa_hca_decode launch per step; separate: csa_index_topk + csa_sparse_attn + hca_attn")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain device-to-device copy of known size (the HBM counter calibration)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -72,6 +77,9 @@ def main():
     from long_context_compressed_05_amd.step import Layer, Params, to_device
 
     assert torch.cuda.is_available(), "bench.py needs a ROCm GPU"
+    if args.copy_calibration:
+        copy_calibration(torch)
+        return
     csa.lib()
     dev = "cuda"
     torch.cuda.init()
@@ -150,6 +158,7 @@ def main():
     step = step_fused if args.path == "fused" else step_separate
     # the kernel whose duration is the roofline figure: the fused step kernel, or the indexer scoring kernel
     prof_id = csa.CSA_K_FUSED if args.path == "fused" else csa.CSA_K_IDX_SCORE
+    prof_name = "k_decode_fused" if args.path == "fused" else "k_idx_score"
 
     for i in range(args.warmup):
         step(i)
@@ -245,9 +254,10 @@ def main():
         "hbm_gbps": round(gbs, 1),
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         "step_bytes": int(step_bytes),
-        "roofline": {"bound": "hbm", "kernel": "k_decode_fused" if args.path == "fused" else "k_idx_score",
+        "roofline": {"bound": "hbm", "kernel": prof_name,
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": counted_traffic(prof_name, wl.name),
                      "bytes_per_launch": int(kernel_bytes), "avg_launch_us": round(score_ms * 1e3, 3)},
         "compress": compress,
     }
@@ -264,6 +274,54 @@ def main():
         result["cpu_baseline"] = cpu_baseline(wl, host, log)
 
     print(json.dumps(result), flush=True)
+
+
+COPY_BYTES = 1 << 30
+# the device sources each kernel is built from: a stored counter reading is
+# used only while these are unchanged
+KERNEL_SOURCES = {
+    "k_decode_fused": ["k_fused.hip", "attn_core.hpp", "common.hpp", "kernels.hpp", "select_core.hpp"],
+    "k_idx_score": ["k_index.hip", "common.hpp", "kernels.hpp", "select_core.hpp"],
+}
+
+
+def copy_calibration(torch):
+    """A plain device copy of COPY_BYTES: under rocprofv3 --pmc its FETCH_SIZE
+    and WRITE_SIZE readings give the counters' scale (reads = writes = COPY_BYTES)."""
+    src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": COPY_BYTES, "launches": 5}), flush=True)
+
+
+def kernel_source_digest(kernel: str) -> str:
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)), "long_context_compressed_05_amd", "csrc")
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def counted_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` on `workload` from the committed
+    rocprofv3 counter summary (FETCH_SIZE + WRITE_SIZE, each scaled by the
+    copy-kernel calibration), or None when there is none or the kernel's
+    sources changed since the counters were taken."""
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", f"{kernel}_{workload}_pmc.md")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        for line in fh:
+            if line.startswith("traffic-json: "):
+                rec = json.loads(line[len("traffic-json: "):])
+                if rec.get("source_sha256") != kernel_source_digest(kernel):
+                    return None
+                return int(rec["traffic_bytes_per_launch"])
+    return None
 
 
 def bench_prefill_indexer(torch, csa, synth, to_device, log, reps: int = 10):
@@ -299,7 +357,7 @@ def bench_prefill_indexer(torch, csa, synth, to_device, log, reps: int = 10):
             "queries_per_s": round(wl.n_q / (call_ms * 1e-3), 1)}
 
 
-def cpu_baseline(wl, host, log):
+def cpu_baseline(wl, host, log, min_seconds: float = 12.0):
     """The oracle, as it stands, on the decode queries of the same workload
     (one thread per query).  The oracle's fp64 HCA caches are built first and
     not timed, as the GPU's pooled caches are not."""
@@ -325,15 +383,18 @@ def cpu_baseline(wl, host, log):
                          host["w"][r], host["kc"][p0:p1], host["ks"][p0:p1])
         oracle.hca_query(kv, z, host["q"][r], t, wl.m_hca, wl.W_hca, scale, hpooled=hp[r])
 
-    log(f"cpu baseline: timing the oracle on {n} queries with {n} threads")
+    log(f"cpu baseline: timing the oracle on {n} queries with {n} threads, repeated for at least {min_seconds} s")
     t = time.time()
+    passes = 0
     with ThreadPoolExecutor(max_workers=n) as ex:
-        list(ex.map(one, range(n)))
+        while passes == 0 or time.time() - t < min_seconds:
+            list(ex.map(one, range(n)))
+            passes += 1
     dt = time.time() - t
-    log(f"cpu baseline: {dt:.2f} s")
-    return {"value": round(n / dt, 4), "unit": "queries/s", "cores": n, "kind": "oracle",
-            "sample": f"all {n} decode queries of {wl.name} (CSA: exact MXFP4 scores of every visible "
-                      f"pooled entry, full-sort top-{wl.k}, fp64 pooling of the selected blocks, attention; "
+    log(f"cpu baseline: {passes} passes in {dt:.2f} s")
+    return {"value": round(passes * n / dt, 4), "unit": "queries/s", "cores": n, "kind": "oracle",
+            "sample": f"{passes} passes over all {n} decode queries of {wl.name} (CSA: exact MXFP4 scores of every "
+                      f"visible pooled entry, full-sort top-{wl.k}, fp64 pooling of the selected blocks, attention; "
                       f"HCA: attention over the oracle's prebuilt fp64 cache), one thread per query",
             "seconds": round(dt, 3), "host_cpus": os.cpu_count()}
 
