@@ -90,7 +90,7 @@ __device__ __forceinline__ void attn_wait_dma() {
 // q_row: this query's [H][128] bf16 heads.
 template <int GPW>
 __device__ __forceinline__ void attn_init(AttnState<GPW>& st, const uint8_t* q_row, int H) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, l16 = lane & 15, g = lane >> 4;
+  const int lane = lane_tid() & 63, wave = lane_tid() >> 6, l16 = lane & 15, g = lane >> 4;
   const int HG = H >> 4;
 #pragma unroll
   for (int gi = 0; gi < GPW; ++gi) {
@@ -119,7 +119,7 @@ template <int GPW, int NST = kAttnStages, class RowPtr>
 __device__ __forceinline__ void attn_run(AttnState<GPW>& st, int H, float scale_log2, int64_t p_begin,
                                          int64_t p_end, RowPtr rowptr, uint8_t* lds) {
   static_assert(NST == 2 || NST == 3, "two or three stages");
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = lane_tid(), lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g = lane >> 4;
   const int HG = H >> 4;
   if (p_begin >= p_end) return;
@@ -265,7 +265,7 @@ __device__ __forceinline__ void attn_run(AttnState<GPW>& st, int H, float scale_
 template <int GPW>
 __device__ __forceinline__ void attn_finish(AttnState<GPW>& st, int H, uint8_t* out_row, float* lse_row,
                                             float* part_o, float* part_ml, bool partial, bool coherent) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, l16 = lane & 15, g = lane >> 4;
+  const int lane = lane_tid() & 63, wave = lane_tid() >> 6, l16 = lane & 15, g = lane >> 4;
   const int HG = H >> 4;
 #pragma unroll
   for (int gi = 0; gi < GPW; ++gi) {

@@ -13,6 +13,15 @@ typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
+// threadIdx.x behind an opaque move: values derived from it are formed where
+// they are used instead of being hoisted out of a long outer loop and held in
+// registers across all of it
+__device__ __forceinline__ int lane_tid() {
+  int t = (int)threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t;
+}
+
 __device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
 
 // fp32 -> bf16 bits, round to nearest even; NaN stays NaN.

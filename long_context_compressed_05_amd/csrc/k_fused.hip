@@ -109,11 +109,16 @@ struct FusedArgs {
   float* hca_pml;
 };
 
+// The arguments are read through a kernarg-segment pointer that is laundered
+// at the top of every work round, so each field is re-read with a scalar load
+// where it is used instead of being held in registers across the whole loop.
+using KArgs = const __attribute__((address_space(4))) FusedArgs;
+
 struct FRow {
   int64_t t, n_vis, n_vis_h, pbase, hbase, tok_base;
 };
 
-__device__ __forceinline__ FRow row_info(const FusedArgs& a, int r) {
+__device__ __forceinline__ FRow row_info(KArgs& a, int r) {
   FRow f;
   f.t = a.q_pos[r];
   f.pbase = a.pool_off[r];
@@ -180,7 +185,7 @@ __device__ __forceinline__ uint32_t n_vis_u32(const FRow& f) { return (uint32_t)
 __device__ __forceinline__ uint32_t uni(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
 
 struct FCtx {
-  const FusedArgs* a;
+  KArgs* a;
   uint8_t* smem;
   uint32_t* scr;
   uint32_t tag;
@@ -240,7 +245,7 @@ __device__ __forceinline__ void read_tagged(const FCtx& x, const uint64_t* const
 
 // exclusive scan of cnt[0..n) in place (LDS, n <= 1024), total at cnt[n]
 __device__ __forceinline__ void block_exscan(uint32_t* cnt, int n, uint32_t* scr) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = lane_tid(), lane = tid & 63, wave = tid >> 6;
   uint32_t v[4], tot = 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -282,7 +287,7 @@ __device__ __forceinline__ int upper_slot(const uint32_t* off, int n, uint32_t i
 
 // workgroup-wide: true when no thread's wait failed
 __device__ __forceinline__ bool all_ok(const FCtx& x, bool fail) {
-  if (threadIdx.x == 0) x.scr[S_FLAG] = 0;
+  if (lane_tid() == 0) x.scr[S_FLAG] = 0;
   __syncthreads();
   if (fail) x.scr[S_FLAG] = 1;
   __syncthreads();
@@ -295,7 +300,7 @@ __device__ __forceinline__ bool all_ok(const FCtx& x, bool fail) {
 // returns the bin, *above = entries in higher bins.  need >= 1 and <= total.
 // Returns kFBins + 1 when the histogram holds fewer than need entries.
 __device__ __forceinline__ uint32_t kth_bin(const uint32_t* hist, uint32_t need, uint32_t* scr, uint32_t* above) {
-  const int tid = threadIdx.x;
+  const int tid = lane_tid();
   uint32_t cnt[16], tot = 0;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
@@ -343,8 +348,8 @@ __device__ __forceinline__ uint32_t kth_bin(const uint32_t* hist, uint32_t need,
 // score: chunk c of row r -> keys in LDS, local histogram, published summary
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void phase_score(const FCtx& x, int r, int c, const FRow& f, int64_t j0, int64_t j1) {
-  const FusedArgs& a = *x.a;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, kb = lane >> 5;
+  KArgs& a = *x.a;
+  const int tid = lane_tid(), lane = tid & 63, wave = tid >> 6, kb = lane >> 5;
   uint32_t* keys_s = reinterpret_cast<uint32_t*>(x.smem + kOffKeys);
   uint32_t* hist = reinterpret_cast<uint32_t*>(x.smem + kOffU);
   for (int i = tid; i < kFBins; i += 256) hist[i] = 0;
@@ -475,9 +480,9 @@ __device__ __forceinline__ void phase_score(const FCtx& x, int r, int c, const F
 // ---------------------------------------------------------------------------
 // unnormalised partial (O, m in log2 units, l) of one split, then its tagged header
 __device__ __forceinline__ void write_partial(const FCtx& x, AttnState<1>& st, int r, int pi, bool hca) {
-  const FusedArgs& a = *x.a;
+  KArgs& a = *x.a;
   const int n_cs = a.n_cs_sel + a.n_cs_win;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, l16 = lane & 15, g = lane >> 4;
+  const int lane = lane_tid() & 63, wave = lane_tid() >> 6, l16 = lane & 15, g = lane >> 4;
   float* po;
   float* pml;
   if (hca) {
@@ -504,7 +509,7 @@ __device__ __forceinline__ void write_partial(const FCtx& x, AttnState<1>& st, i
   }
   vm_drain();
   __syncthreads();
-  if (threadIdx.x == 0)
+  if (lane_tid() == 0)
     st_dev64(a.part_hdr + (size_t)r * (n_cs + a.n_hs) + (hca ? n_cs : 0) + pi, tagged(x.tag, 1u));
 }
 
@@ -524,8 +529,8 @@ __device__ __forceinline__ void write_partial(const FCtx& x, AttnState<1>& st, i
 // emit in index order, so the position of a selected index is the selected
 // count of the earlier chunks plus its rank within its chunk.
 __device__ __forceinline__ bool select_split(const FCtx& x, int r, int s, const FRow& f) {
-  const FusedArgs& a = *x.a;
-  const int tid = threadIdx.x;
+  KArgs& a = *x.a;
+  const int tid = lane_tid();
   const int64_t p_begin = (int64_t)s * a.cs;
   const int64_t p_end = p_begin + a.cs < a.k ? p_begin + a.cs : a.k;
   const int k_eff = (int)(f.n_vis < a.k ? f.n_vis : a.k);
@@ -704,7 +709,7 @@ __device__ __forceinline__ bool select_split(const FCtx& x, int r, int s, const 
 // Attention item: CSA selected split (kind 0, rows through idx_s), CSA window
 // split (kind 1) or HCA split (kind 2) of row r, then its partial.
 __device__ __forceinline__ void attend_item(const FCtx& x, int r, int kind, int s, const FRow& f) {
-  const FusedArgs& a = *x.a;
+  KArgs& a = *x.a;
   int64_t p_begin, p_end;
   int pi = s;
   if (kind == 0) {
@@ -720,19 +725,25 @@ __device__ __forceinline__ void attend_item(const FCtx& x, int r, int kind, int 
     p_end = p_begin + a.hs < list_len ? p_begin + a.hs : list_len;
   }
   const int32_t* idx_s = reinterpret_cast<const int32_t*>(x.smem + kOffIdx);
-  constexpr size_t RB = 2 * 128 * 2;
-  auto rowptr = [&](int64_t p) -> const uint8_t* {
+  constexpr uint64_t RB = 2 * 128 * 2;
+  // Row addresses from 32-bit offsets against per-row bases: list positions
+  // below `split` are pooled rows (selected ones for kind 0, HCA rows for
+  // kind 2), the rest are window tokens t - W + 1 + (p - split).
+  const uint8_t* pool_base = kind == 0 ? a.kv_pool + (size_t)f.pbase * RB : a.kv_hpool + (size_t)f.hbase * RB;
+  const uint8_t* raw_base = a.kv_raw + (size_t)f.tok_base * RB;
+  const int32_t pb32 = (int32_t)p_begin;
+  const int32_t split = kind == 1 ? 0 : (int32_t)a.max_hpool;
+  const int32_t hi_pool = (int32_t)f.n_vis_h;
+  const int32_t win_off = (int32_t)(f.t + 1 - (kind == 1 ? a.W : a.W_hca)) - split;
+  auto rowptr = [&](int64_t p64) -> const uint8_t* {
+    const int32_t p = (int32_t)p64;
     if (kind == 0) {
-      const int32_t j = idx_s[p - p_begin];
-      return j >= 0 ? a.kv_pool + (size_t)(f.pbase + j) * RB : nullptr;
+      const int32_t j = idx_s[p - pb32];
+      return j >= 0 ? pool_base + (uint64_t)(uint32_t)j * RB : nullptr;
     }
-    if (kind == 1) {
-      const int64_t u = f.t - a.W + 1 + p;
-      return u >= 0 ? a.kv_raw + (size_t)(f.tok_base + u) * RB : nullptr;
-    }
-    if (p < a.max_hpool) return p < f.n_vis_h ? a.kv_hpool + (size_t)(f.hbase + p) * RB : nullptr;
-    const int64_t u = f.t - a.W_hca + 1 + (p - a.max_hpool);
-    return u >= 0 ? a.kv_raw + (size_t)(f.tok_base + u) * RB : nullptr;
+    if (p < split) return p < hi_pool ? pool_base + (uint64_t)(uint32_t)p * RB : nullptr;
+    const int32_t u = p + win_off;
+    return u >= 0 ? raw_base + (uint64_t)(uint32_t)u * RB : nullptr;
   };
   AttnState<1> st;
   attn_init<1>(st, a.q + (size_t)r * a.H * 128 * 2, a.H);
@@ -742,8 +753,8 @@ __device__ __forceinline__ void attend_item(const FCtx& x, int r, int kind, int 
 
 // merge of 4 heads (h0 .. h0+3) of one row: thread = (head, 2 dims)
 __device__ __forceinline__ void item_merge(const FCtx& x, bool hca, int r, int h0) {
-  const FusedArgs& a = *x.a;
-  const int tid = threadIdx.x;
+  KArgs& a = *x.a;
+  const int tid = lane_tid();
   const int n_cs = a.n_cs_sel + a.n_cs_win;
   const int n = hca ? a.n_hs : n_cs;
   const uint64_t* hdr = a.part_hdr + (size_t)r * (n_cs + a.n_hs) + (hca ? n_cs : 0);
@@ -808,38 +819,42 @@ __device__ __forceinline__ void item_merge(const FCtx& x, bool hca, int r, int h
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_decode_fused(FusedArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
   uint32_t* scr = reinterpret_cast<uint32_t*>(smem + kOffScr);
-  if (threadIdx.x == 0) {
+  if (lane_tid() == 0) {
     uint32_t tag = ld_dev(a.ctl + W_EPOCH) + 1u;
     if (tag == 0) tag = 1;
     scr[S_TAG] = tag;
   }
   __syncthreads();
-  const FCtx x{&a, smem, scr, uni(scr[S_TAG]), make_coh(a.ctl)};
+  const uint32_t tag = uni(scr[S_TAG]);
   __syncthreads();
-  const int G = (int)gridDim.x;
+  const int rounds = a.rounds;
   // Work units in dependency order: the R * n_sc score chunks, then the items
   // [CSA selected splits | CSA window splits | HCA splits | CSA merges | HCA
   // merges].  Units are handed out in that order through one returning atomic,
   // and a unit only waits for units of lower number, whose holders are already
   // running: every wait ends whatever the residency of the grid.
-  const int R = a.R, nM = a.H / 4;
-  const int64_t nS = (int64_t)R * a.n_sc;
-  const int64_t e1 = nS + (int64_t)R * a.n_cs_sel, e2 = e1 + (int64_t)R * a.n_cs_win,
-                e3 = e2 + (int64_t)R * a.n_hs, e4 = e3 + (int64_t)R * nM, total = e4 + (int64_t)R * nM;
   // Every workgroup runs the same number of rounds (rounds * grid >= total), so
   // the loop bound is uniform; a round whose unit number is past the end (or
   // that follows a reported error) does nothing.
-  for (int round = 0; round < a.rounds; ++round) {
-    if (threadIdx.x == 0) scr[S_TICKET] = error_seen(x) ? 0xffffffffu : atomicAdd(a.ctl + W_TICKET, 1u);
+  for (int round = 0; round < rounds; ++round) {
+    KArgs* ap = (KArgs*)__builtin_amdgcn_kernarg_segment_ptr();
+    asm volatile("" : "+s"(ap));
+    KArgs& A = *ap;
+    const FCtx x{ap, smem, scr, tag, make_coh(A.ctl)};
+    const int R = A.R, nM = A.H / 4;
+    const int64_t nS = (int64_t)R * A.n_sc;
+    const int64_t e1 = nS + (int64_t)R * A.n_cs_sel, e2 = e1 + (int64_t)R * A.n_cs_win,
+                  e3 = e2 + (int64_t)R * A.n_hs, e4 = e3 + (int64_t)R * nM, total = e4 + (int64_t)R * nM;
+    if (lane_tid() == 0) scr[S_TICKET] = error_seen(x) ? 0xffffffffu : atomicAdd(A.ctl + W_TICKET, 1u);
     __syncthreads();
     const int64_t it = uni(scr[S_TICKET]);
     __syncthreads();
     if (it >= total) {
       // nothing to do this round
     } else if (it < nS) {
-      const int r = (int)(it / a.n_sc), c = (int)(it % a.n_sc);
-      const FRow f = row_info(a, r);
-      int64_t j0 = (int64_t)c * a.C, j1 = j0 + a.C;
+      const int r = (int)(it / A.n_sc), c = (int)(it % A.n_sc);
+      const FRow f = row_info(A, r);
+      int64_t j0 = (int64_t)c * A.C, j1 = j0 + A.C;
       if (j1 > f.n_vis) j1 = f.n_vis;
       if (j0 > j1) j0 = j1;
       phase_score(x, r, c, f, j0, j1);
@@ -851,19 +866,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
       const int kind = it < e1 ? 0 : it < e2 ? 1 : 2;
       const int64_t q = it - (kind == 0 ? nS : kind == 1 ? e1 : e2);
       const int r = (int)(q % R), s = (int)(q / R);
-      const FRow f = row_info(a, r);
+      const FRow f = row_info(A, r);
       const bool ok = kind != 0 || select_split(x, r, s, f);
       if (ok) attend_item(x, r, kind, s, f);
     }
   }
+  const int G = (int)gridDim.x;
   // ---- the last workgroup out advances the epoch
   __syncthreads();
-  if (threadIdx.x == 0) {
+  if (lane_tid() == 0) {
     vm_drain();
     if (atomicAdd(a.ctl + W_EXIT, 1u) == (uint32_t)G - 1) {
       st_dev(a.ctl + W_EXIT, 0u);
       st_dev(a.ctl + W_TICKET, 0u);
-      st_dev(a.ctl + W_EPOCH, x.tag);
+      st_dev(a.ctl + W_EPOCH, tag);
     }
   }
 }

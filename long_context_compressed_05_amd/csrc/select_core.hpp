@@ -13,19 +13,19 @@ __device__ uint32_t radix_select_desc(uint32_t n, uint32_t need, ValueFn val, Ac
                                       uint32_t* need_left, uint32_t* bins, uint32_t* scratch) {
   uint32_t prefix = 0, pmask = 0;
   for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int i = threadIdx.x; i < 256; i += blockDim.x) bins[i] = 0;
+    for (int i = lane_tid(); i < 256; i += blockDim.x) bins[i] = 0;
     __syncthreads();
-    for (uint32_t i = threadIdx.x; i < n; i += blockDim.x) {
+    for (uint32_t i = lane_tid(); i < n; i += blockDim.x) {
       if (!active(i)) continue;
       const uint32_t v = val(i);
       if ((v & pmask) == prefix) atomicAdd(&bins[(v >> shift) & 255u], 1u);
     }
     __syncthreads();
     uint32_t c = 0;
-    for (int b = threadIdx.x; b < 256; b += blockDim.x) c += bins[b];  // one bin per thread (blockDim >= 256)
+    for (int b = lane_tid(); b < 256; b += blockDim.x) c += bins[b];  // one bin per thread (blockDim >= 256)
     int d;
     uint32_t above;
-    block_find_from_top(threadIdx.x < 256 ? c : 0u, need, scratch, &d, &above);
+    block_find_from_top(lane_tid() < 256 ? c : 0u, need, scratch, &d, &above);
     prefix |= (uint32_t)d << shift;
     pmask |= 255u << shift;
     need -= above;
@@ -49,9 +49,9 @@ __device__ uint32_t radix_select_desc_low(uint32_t n, uint32_t need, int top, ui
     const int width = hi < (top + rounds - 1) / rounds ? hi : (top + rounds - 1) / rounds;
     const int shift = hi - width;
     const int nb = 1 << width;
-    for (int i = threadIdx.x; i < nb; i += nt) bins[i] = 0;
+    for (int i = lane_tid(); i < nb; i += nt) bins[i] = 0;
     __syncthreads();
-    for (uint32_t i = threadIdx.x; i < n; i += nt) {
+    for (uint32_t i = lane_tid(); i < n; i += nt) {
       if (!active(i)) continue;
       const uint32_t v = val(i);
       if ((v & pmask) == prefix) atomicAdd(&bins[(v >> shift) & (uint32_t)(nb - 1)], 1u);
@@ -61,22 +61,22 @@ __device__ uint32_t radix_select_desc_low(uint32_t n, uint32_t need, int top, ui
     const int bpt = (nb + nt - 1) / nt;
     uint32_t c = 0;
     for (int b = 0; b < bpt; ++b) {
-      const int bi = threadIdx.x * bpt + b;
+      const int bi = lane_tid() * bpt + b;
       if (bi < nb) c += bins[bi];
     }
     int tstar;
     uint32_t above;
     block_find_from_top(c, need, scratch, &tstar, &above);
-    if ((int)threadIdx.x == tstar) {
+    if ((int)lane_tid() == tstar) {
       uint32_t cum = above;
       int b = bpt - 1;
       for (; b > 0; --b) {
-        const int bi = threadIdx.x * bpt + b;
+        const int bi = lane_tid() * bpt + b;
         const uint32_t cb = bi < nb ? bins[bi] : 0u;
         if (cum + cb >= need) break;
         cum += cb;
       }
-      scratch[30] = (uint32_t)(threadIdx.x * bpt + b);
+      scratch[30] = (uint32_t)(lane_tid() * bpt + b);
       scratch[31] = cum;
     }
     __syncthreads();
@@ -94,7 +94,7 @@ __device__ uint32_t radix_select_desc_low(uint32_t n, uint32_t need, int top, ui
 // ascending j, rank counting from 0.  scratch: blockDim.x/64 words of LDS.
 template <typename EmitFn>
 __device__ void bitmap_emit_ascending(const uint32_t* bitmap, int nwords, uint32_t* scratch, EmitFn emit) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = lane_tid(), lane = tid & 63, wave = tid >> 6;
   const int wpt = (nwords + (int)blockDim.x - 1) / (int)blockDim.x;
   const int w0 = tid * wpt;
   uint32_t cnt = 0;
