@@ -218,6 +218,13 @@ int csa_hca_decode(const csa_batch* b, const int64_t* pool_off, int64_t max_pool
  * CSA_ERR_DEVICE; clears the word.  (The only synchronising call.) */
 int csa_hca_decode_check(const csa_batch* b, const void* ws, void* stream);
 
+/* Synchronises `stream`, then stores in *rows how many row selections of the
+ * csa_hca_decode launches on `ws` (since it was zero-filled) could not be
+ * proved exact from the score chunks' candidate lists and took the exact
+ * radix select over all of the row's keys instead (same result, slower).
+ * ws and rows non-NULL (rows is a host pointer), else CSA_ERR_INVALID. */
+int csa_hca_decode_fallbacks(const void* ws, void* stream, uint32_t* rows);
+
 /* ------------------------------------------------------------------------
  * csa_profile_events — tracing hook (host).  Until cleared, every launch of
  * internal kernel `kernel_id` made by the calling thread is bracketed by

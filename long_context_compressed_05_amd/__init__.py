@@ -24,7 +24,7 @@ CSA_F32, CSA_BF16 = 0, 1
 EXPORTS = ("csa_status_string", "csa_last_error", "csa_compress", "csa_index_topk_workspace",
            "csa_index_topk", "csa_sparse_attn_workspace", "csa_sparse_attn", "hca_attn_workspace",
            "hca_attn", "csa_hca_decode_workspace", "csa_hca_decode", "csa_hca_decode_check",
-           "csa_profile_events")
+           "csa_hca_decode_fallbacks", "csa_profile_events")
 (CSA_K_IDX_SCORE, CSA_K_IDX_SELECT, CSA_K_IDX_FINAL, CSA_K_ATTN, CSA_K_ATTN_COMBINE, CSA_K_COMPRESS,
  CSA_K_FUSED) = range(7)
 
@@ -66,6 +66,7 @@ def lib():
     L.csa_hca_decode.argtypes = [bp, vp, i64, vp, i64, ci, ci, ci, ci, ctypes.c_float, ci, ci, ci, vp, vp, vp, vp,
                                  vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.csa_hca_decode_check.argtypes = [bp, vp, vp]
+    L.csa_hca_decode_fallbacks.argtypes = [vp, vp, ctypes.POINTER(ctypes.c_uint32)]
     L.csa_profile_events.argtypes = [ci, vp, vp]
     for name in EXPORTS:
         L[name].restype = L[name].restype if name in ("csa_status_string", "csa_last_error") else ci
@@ -326,6 +327,13 @@ def csa_hca_decode(batch: Batch, pool_off, max_pool: int, hpool_off, max_hpool: 
                                 _ptr(csa_out), _ptr(csa_lse), _ptr(hca_out), _ptr(hca_lse), _ptr(buf), nbytes,
                                 _stream(stream)), "csa_hca_decode")
     return idx, csa_out, csa_lse, hca_out, hca_lse
+
+
+def csa_hca_decode_fallbacks(ws: Workspace, stream=None) -> int:
+    """Synchronise and return how many row selections on `ws` took the exact fallback."""
+    n = ctypes.c_uint32(0)
+    _check(lib().csa_hca_decode_fallbacks(_ptr(ws.buf), _stream(stream), ctypes.byref(n)), "csa_hca_decode_fallbacks")
+    return int(n.value)
 
 
 def csa_hca_decode_check(batch: Batch, ws: Workspace, stream=None) -> None:

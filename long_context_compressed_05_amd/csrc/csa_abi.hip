@@ -166,6 +166,19 @@ int csa_hca_decode_check(const csa_batch* b, const void* ws, void* stream) {
   return CSA_OK;
 }
 
+int csa_hca_decode_fallbacks(const void* ws, void* stream, uint32_t* rows) {
+  if (!ws || !rows) return fail(CSA_ERR_INVALID, "ws and rows must not be NULL");
+  int rc = check_device();
+  if (rc) return rc;
+  if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess ||
+      hipMemcpy(rows, (const uint8_t*)ws + csa::fused_fallback_word_offset(), 4, hipMemcpyDeviceToHost) !=
+          hipSuccess) {
+    (void)hipGetLastError();
+    return fail(CSA_ERR_DEVICE, "could not read the decode fallback count");
+  }
+  return CSA_OK;
+}
+
 int csa_profile_events(int kernel_id, void* start, void* stop) {
   if (kernel_id < 0 || kernel_id >= CSA_K_COUNT) return fail(CSA_ERR_INVALID, "unknown kernel id %d", kernel_id);
   if ((start == nullptr) != (stop == nullptr)) return fail(CSA_ERR_INVALID, "pass both events or neither");

@@ -1,21 +1,19 @@
 // Fused CSA + HCA decode step: one launch per step.
 //
-// The whole decode hot path runs in one persistent kernel whose workgroups
-// are all co-resident.  Every workgroup w runs, in order:
-//   score   chunk w of the (row, chunk) list: C pooled entries of one query's
-//           visible range, MXFP4 MFMA scores -> sort keys kept in LDS, and an
-//           LDS histogram of key >> 19; then it publishes a summary: the
-//           nonzero bins at or above its local k-th bin (at most k pairs, and
-//           every bin at or above the row's threshold bin is complete in it)
-//   reduce  (chunk 0 of each row) merge the row's summaries, find the
-//           threshold bin b1 and the count above it, publish them
-//   emit    keys above bin b1 -> the chunk's list of definite indices, keys
-//           in bin b1 -> its candidate list, both in ascending index order
-//   items   taken from [CSA selected splits | CSA window splits | HCA splits |
-//           CSA merges | HCA merges], item i on workgroup i mod G:
-//     CSA selected split: the exact k-th key and lowest-index ties among the
-//           row's candidates (in LDS), the row's selected set as an LDS
-//           bitmap, the split's slice of the ascending list, attention over it
+// The whole decode hot path runs in one kernel whose workgroups take work
+// units from a device-wide ticket, in dependency order:
+//   score   chunk c of row r: C pooled entries of the query's visible range,
+//           MXFP4 MFMA scores -> u32 sort keys (in LDS, and in the workspace
+//           for the fallback); the chunk's list: its L largest entries by
+//           (key desc, index asc), in ascending index order, then the list's
+//           tagged header
+//   select  row r: K* = the k_eff-th largest listed key (radix select in LDS),
+//           the per-chunk counts above and equal to K*, the tie cut in chunk
+//           (= index) order, an exactness check (else an exact radix select
+//           over the stored keys), the selection -> idx, the row's header
+//   items   [CSA selected splits | CSA window splits | HCA splits | CSA merges |
+//           HCA merges]:
+//     CSA selected split: its 64 positions of idx, attention over those rows
 //     window / HCA split: attention over raw window rows / pooled HCA rows
 //     merge: log-sum-exp merge of the row's split partials, 4 heads per item
 //
@@ -39,34 +37,39 @@
 namespace csa {
 
 constexpr int kFMaxC = 3072;         // score entries per workgroup (keys in LDS)
-constexpr int kFBins = 4096;         // key >> 19
-constexpr int kFMaxSplit = 256;      // list positions per attention item
-constexpr int kFEntLds = 6144;       // emitted entries of a row staged in LDS
+constexpr int kFKPT = kFMaxC / 256;  // keys per thread in a chunk
+constexpr int kFHist = 2048;         // radix digit bins (11 bits)
+constexpr int kFEntLds = 6144;       // listed keys of a row staged in LDS
+constexpr int kFEPT = kFEntLds / 256;  // listed keys per thread in the row selection
+constexpr int kFMaxSel = 1024;       // selected rows of one CSA group (k <= kFMaxSel)
 constexpr int kFMaxVisible = 262144;  // visible pooled entries per query (18-bit indices)
 constexpr int kFMaxRows = 64;
 constexpr int kFMaxSlots = 512;      // score chunks per row
-constexpr int kFRankMax = 2032;      // threshold-bin entries ranked by direct comparison
 constexpr uint32_t kSpinLimit = 1u << 20;
 
 // control words at the start of the workspace
-enum { W_EPOCH = 0, W_EXIT = 1, W_ERROR = 2, W_TICKET = 3, W_CTL = 64 };
+enum { W_EPOCH = 0, W_EXIT = 1, W_ERROR = 2, W_TICKET = 3, W_FALLBACK = 4, W_CTL = 64 };
 
-// LDS layout (dynamic)
-constexpr int kOffKeys = 0;                                 // uint32 [kFMaxC]; later per-chunk arrays
-constexpr int kOffIdx = kOffKeys + kFMaxC * 4;              // int32 [kFMaxSplit]
-constexpr int kOffScr = kOffIdx + kFMaxSplit * 4;           // uint32 [64]
+// LDS layout (dynamic).  The key region holds a score chunk's keys, or the
+// per-chunk arrays of a row (offsets, counts, thresholds) and a CSA group's
+// selected rows; the union region holds the attention stages, or a row's
+// listed keys and the radix histograms, or a CSA group's listed entries.
+constexpr int kOffKeys = 0;                                 // uint32 [kFMaxC]
+constexpr int kOffSel = kOffKeys + 3 * (kFMaxSlots + 8) * 4;  // int32 [kFMaxSel] (aliases the chunk keys)
+constexpr int kOffScr = kOffKeys + kFMaxC * 4;              // uint32 [64]
 constexpr int kOffU = kOffScr + 64 * 4;                     // union region
-constexpr int kOffEnt = kOffU;                              // uint64 [kFEntLds] order keys of emitted entries
-constexpr int kOffHist = kOffEnt + kFEntLds * 8;            // uint32 [kFBins]; then uint64 [kFRankMax + 16]
-constexpr int kSelEnd = kOffHist + kFBins * 4;
+constexpr int kOffLst = kOffU;                              // uint32 [kFEntLds] listed keys / uint64 entries
+constexpr int kOffHist = kOffU + kFEntLds * 4;              // uint32 [2][kFHist] + [64] lane trash words
+constexpr int kSelEnd = kOffHist + (2 * kFHist + 64) * 4;
 constexpr int kAttnEnd = kOffU + kAttnLdsBytes;
 constexpr int kFusedLds = kSelEnd > kAttnEnd ? kSelEnd : kAttnEnd;
-static_assert((kFMaxSlots + 1) * 3 * 4 <= kFMaxC * 4, "per-chunk arrays alias the key region");
-static_assert(kOffU % 16 == 0, "attention LDS must be 16-byte aligned");
-static_assert((kFRankMax + 16) * 8 <= kFBins * 4, "ranked entries reuse the histogram");
+static_assert(kOffSel + kFMaxSel * 4 <= kOffScr, "a group's selected rows fit the key region");
+static_assert(kOffU % 16 == 0 && kOffHist % 16 == 0, "LDS regions must be 16-byte aligned");
+static_assert(kFEntLds * 8 <= kAttnLdsBytes, "a group's listed entries fit the union region");
+static_assert(kFusedLds <= 80 * 1024, "two workgroups per CU");
 
-// scratch word indices (0..39 are used by the block scans)
-enum { S_TAG = 40, S_FLAG, S_B1, S_ABOVE, S_NB1, S_CSTAR_LO, S_CSTAR_HI, S_BAD, S_TICKET };
+// scratch word indices (0..19 are used by the block scans and searches)
+enum { S_TAG = 40, S_FLAG, S_DIGIT, S_ABOVE, S_CNT, S_BAD, S_TICKET, S_KEY, S_CUT };
 
 struct FusedArgs {
   const int64_t* tok_off;
@@ -92,16 +95,22 @@ struct FusedArgs {
   float* hca_lse;
   // plan
   int C, n_sc;                 // entries per score chunk, chunks per row
-  int cs, n_cs_sel, n_cs_win;  // CSA split size, selected splits, window splits (per row)
+  int cs, n_cs_sel, n_cs_win;  // window split size; CSA groups and window splits per row
+  int cg;                      // score chunks per CSA group
   int rounds;                  // work units taken per workgroup (rounds * grid >= all units)
   int hs, n_hs;                // HCA split size, splits per row
-  int emit_q, emit_max;        // per chunk: entries at or above the local emit_q-th bin, at most emit_max
+  int lst_min, lst;            // per chunk: listed entries, at least lst_min (when it has them), at most lst (4 | lst)
   int64_t key_stride;          // keys row stride (multiple of 4)
   // workspace
   uint32_t* ctl;
   uint32_t* keys;      // [R][key_stride] sort keys (read only by the exact fallback)
-  uint64_t* ent_hdr;   // [R*n_sc] tagged: count | bin << 12 | truncated << 25
-  uint64_t* ent;       // [R*n_sc][emit_max] (key << 32) | index, ascending index
+  uint64_t* ent_hdr;   // [R*n_sc] tagged: listed count | truncated << 16
+  uint64_t* ent;       // [R*n_sc][lst] (key << 32) | index, ascending index
+  uint32_t* lkey;      // [R*n_sc][lst] the listed keys alone, same order
+  uint32_t* ltau;      // [R*n_sc] listing threshold: every entry of the chunk with key >= it is listed
+  uint64_t* row_k;     // [R] tagged: K*
+  uint64_t* row_cut;   // [R] tagged: listed position of the last taken tie; or 1 << 31 | index (fallback)
+  uint64_t* grp_off;   // [R][n_cs_sel] tagged: output position of the group's first selected entry
   uint64_t* part_hdr;  // [R][n_cs_sel + n_cs_win + n_hs]
   float* csa_po;       // [R][n_cs][H][128]
   float* csa_pml;      // [R][n_cs][H][2]
@@ -296,37 +305,128 @@ __device__ __forceinline__ bool all_ok(const FCtx& x, bool fail) {
   return ok;
 }
 
-// k-th largest bin over a 4096-bin LDS histogram (thread t owns bins 16t..16t+15):
-// returns the bin, *above = entries in higher bins.  need >= 1 and <= total.
-// Returns kFBins + 1 when the histogram holds fewer than need entries.
-__device__ __forceinline__ uint32_t kth_bin(const uint32_t* hist, uint32_t need, uint32_t* scr, uint32_t* above) {
-  const int tid = lane_tid();
-  uint32_t cnt[16], tot = 0;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    cnt[i] = hist[tid * 16 + i];
-    tot += cnt[i];
+// Wave-wide inclusive scans on DPP lane moves (row shifts within 16-lane rows,
+// then the row broadcasts of lanes 15 and 31): a few VALU operations instead
+// of LDS permutes.  Lanes whose source is outside the row take the identity.
+template <int CTRL, int ROWS = 0xf>
+__device__ __forceinline__ uint32_t dpp_mov(uint32_t identity, uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)identity, (int)x, CTRL, ROWS, 0xf, false);
+}
+__device__ __forceinline__ uint32_t wave_incl_add(uint32_t x) {
+  x += dpp_mov<0x111>(0u, x);        // row_shr:1
+  x += dpp_mov<0x112>(0u, x);        // row_shr:2
+  x += dpp_mov<0x114>(0u, x);        // row_shr:4
+  x += dpp_mov<0x118>(0u, x);        // row_shr:8
+  x += dpp_mov<0x142, 0xa>(0u, x);   // row_bcast:15 -> rows 1, 3
+  x += dpp_mov<0x143, 0xc>(0u, x);   // row_bcast:31 -> rows 2, 3
+  return x;
+}
+// wave-wide min and max of x, on every lane
+__device__ __forceinline__ void wave_minmax(uint32_t& mn, uint32_t& mx) {
+#define CSA_MM_STEP(CTRL, ROWS)                                    \
+  {                                                                \
+    const uint32_t a_ = dpp_mov<CTRL, ROWS>(0xffffffffu, mn);      \
+    const uint32_t b_ = dpp_mov<CTRL, ROWS>(0u, mx);               \
+    mn = a_ < mn ? a_ : mn;                                        \
+    mx = b_ > mx ? b_ : mx;                                        \
   }
-  if (tid == 0) scr[4] = 0xffffffffu;  // block_find_from_top's result word for 4 waves
+  CSA_MM_STEP(0x111, 0xf) CSA_MM_STEP(0x112, 0xf) CSA_MM_STEP(0x114, 0xf) CSA_MM_STEP(0x118, 0xf)
+  CSA_MM_STEP(0x142, 0xa) CSA_MM_STEP(0x143, 0xc)
+#undef CSA_MM_STEP
+  mn = (uint32_t)__builtin_amdgcn_readlane((int)mn, 63);
+  mx = (uint32_t)__builtin_amdgcn_readlane((int)mx, 63);
+}
+
+// exclusive prefix of v over the workgroup (thread order); *total = the sum
+__device__ __forceinline__ uint32_t block_exscan_val(uint32_t v, uint32_t* scr, uint32_t* total) {
+  const int tid = lane_tid(), lane = tid & 63, wave = tid >> 6;
+  const uint32_t incl = wave_incl_add(v);
+  if (lane == 63) scr[16 + wave] = incl;
   __syncthreads();
-  int tstar;
-  uint32_t ab;
-  block_find_from_top(tot, need, scr, &tstar, &ab);
-  if ((int)uni((uint32_t)tstar) < 0) {
-    *above = 0;
-    return kFBins + 1;
+  uint32_t run = incl - v;
+  for (int w2 = 0; w2 < wave; ++w2) run += scr[16 + w2];
+  *total = uni(scr[16] + scr[17] + scr[18] + scr[19]);
+  __syncthreads();
+  return run;
+}
+
+// [lo, hi] = the range of the workgroup's valid keys (each thread holds NK in
+// registers, the first nv valid; at least one valid key in the workgroup).
+// Also clears the two 2048-bin histograms at hist (16-byte aligned).
+template <int NK>
+__device__ __forceinline__ void key_range(const uint32_t (&kv)[NK], int nv, uint32_t* hist, uint32_t* scr,
+                                          uint32_t* lo, uint32_t* hi) {
+  const int tid = lane_tid(), lane = tid & 63, wave = tid >> 6;
+  uint32_t mn = 0xffffffffu, mx = 0u;
+#pragma unroll
+  for (int i = 0; i < NK; ++i)
+    if (i < nv) {
+      mn = kv[i] < mn ? kv[i] : mn;
+      mx = kv[i] > mx ? kv[i] : mx;
+    }
+  wave_minmax(mn, mx);
+  if (lane == 0) {
+    scr[8 + wave] = mn;
+    scr[12 + wave] = mx;
   }
-  if (tid == tstar) {  // walk this thread's bins downwards (unrolled: no dynamic register indexing)
-    uint32_t cum = ab, asel = 0;
+  for (int i = tid; i < 2 * kFHist / 4; i += 256) reinterpret_cast<uint4*>(hist)[i] = make_uint4(0u, 0u, 0u, 0u);
+  __syncthreads();
+  uint32_t l = scr[8], h = scr[12];
+  for (int w2 = 1; w2 < 4; ++w2) {
+    l = scr[8 + w2] < l ? scr[8 + w2] : l;
+    h = scr[12 + w2] > h ? scr[12 + w2] : h;
+  }
+  *lo = uni(l);
+  *hi = uni(h);
+}
+
+// One radix pass over the keys in [lo, hi] (lo < hi), cut into at most 2048
+// bins of width 2^shift: the bin that holds the need-th largest of them
+// (need <= their count) -> [*blo, *bhi], *above = keys above that bin, *cnt =
+// keys in it.  hist: 2048 zeroed words, left zeroed; trash: 64 words that
+// take the counts of keys outside the range (one per lane: the count loop
+// has no branches and no colliding atomics on them).
+template <int NK>
+__device__ __forceinline__ void radix_pass(const uint32_t (&kv)[NK], int nv, uint32_t need, uint32_t* hist,
+                                           uint32_t* trash, uint32_t* scr, uint32_t lo, uint32_t hi, uint32_t* blo,
+                                           uint32_t* bhi, uint32_t* above, uint32_t* cnt) {
+  const int tid = lane_tid(), lane = tid & 63, wave = tid >> 6;
+  const uint32_t span = hi - lo;
+  const int nbits = 32 - __clz((int)span);
+  const int shift = nbits > 11 ? nbits - 11 : 0;
+#pragma unroll
+  for (int i = 0; i < NK; ++i) {
+    const bool in = i < nv && kv[i] >= lo && kv[i] <= hi;
+    atomicAdd(in ? hist + ((kv[i] - lo) >> shift) : trash + lane, 1u);
+  }
+  __syncthreads();
+  uint32_t c[8], tot = 0;
+#pragma unroll
+  for (int b = 0; b < 8; ++b) {
+    c[b] = hist[8 * tid + b];
+    hist[8 * tid + b] = 0u;
+    tot += c[b];
+  }
+  const uint32_t incl = wave_incl_add(tot);
+  if (lane == 63) scr[wave] = incl;
+  __syncthreads();
+  uint32_t below = incl - tot, all = 0;
+  for (int w2 = 0; w2 < 4; ++w2) {
+    all += scr[w2];
+    below += w2 < wave ? scr[w2] : 0u;
+  }
+  const uint32_t sup = all - below - tot;  // keys in bins above this thread's 8
+  if (sup < need && sup + tot >= need) {  // walk this thread's bins downwards (unrolled)
+    uint32_t cum = sup, asel = 0;
     int bsel = -1;
 #pragma unroll
-    for (int bi = 15; bi >= 1; --bi) {
+    for (int b = 7; b >= 1; --b) {
       if (bsel < 0) {
-        if (cum + cnt[bi] >= need) {
-          bsel = bi;
+        if (cum + c[b] >= need) {
+          bsel = b;
           asel = cum;
         } else {
-          cum += cnt[bi];
+          cum += c[b];
         }
       }
     }
@@ -334,25 +434,68 @@ __device__ __forceinline__ uint32_t kth_bin(const uint32_t* hist, uint32_t need,
       bsel = 0;
       asel = cum;
     }
-    scr[S_B1] = (uint32_t)(tid * 16 + bsel);
+    uint32_t cb = c[0];
+#pragma unroll
+    for (int b = 1; b < 8; ++b) cb = b == bsel ? c[b] : cb;
+    scr[S_DIGIT] = (uint32_t)(8 * tid + bsel);
     scr[S_ABOVE] = asel;
+    scr[S_CNT] = cb;
   }
   __syncthreads();
-  const uint32_t b = uni(scr[S_B1]);
+  const uint32_t digit = uni(scr[S_DIGIT]);
   *above = uni(scr[S_ABOVE]);
-  __syncthreads();
-  return b;
+  *cnt = uni(scr[S_CNT]);
+  const uint32_t nlo = lo + (digit << shift);
+  const uint32_t width_m1 = (uint32_t)(((uint64_t)1 << shift) - 1u);
+  *blo = nlo;
+  *bhi = hi - nlo > width_m1 ? nlo + width_m1 : hi;
+}
+
+// The need-th largest key (1 <= need <= number of valid keys) among the
+// workgroup's keys, each thread holding NK of them in registers (the first nv
+// valid): radix select over the keys' own range, each pass narrowing it to one
+// of at most 2048 bins (so keys spread over the bins whatever their
+// magnitude), at most 3 passes.  Returns the key; *gt = the keys above it.
+// A pass that leaves one key in the range ends the search.  hist: 2 x 2048 +
+// 64 words of LDS, 16-byte aligned.
+template <int NK>
+__device__ __forceinline__ uint32_t kth_key(const uint32_t (&kv)[NK], int nv, uint32_t need, uint32_t* hist,
+                                            uint32_t* scr, uint32_t* gt) {
+  uint32_t lo, hi;
+  key_range<NK>(kv, nv, hist, scr, &lo, &hi);
+  uint32_t above_all = 0;
+#pragma unroll 1
+  for (int pass = 0; pass < 3 && lo != hi; ++pass) {
+    uint32_t blo, bhi, above, cnt;
+    radix_pass<NK>(kv, nv, need, hist + (pass & 1) * kFHist, hist + 2 * kFHist, scr, lo, hi, &blo, &bhi, &above,
+                   &cnt);
+    need -= above;
+    above_all += above;
+    lo = blo;
+    hi = bhi;
+    if (cnt == 1u && lo != hi) {  // the one key in [lo, hi]
+#pragma unroll
+      for (int i = 0; i < NK; ++i)
+        if (i < nv && kv[i] >= lo && kv[i] <= hi) scr[S_KEY] = kv[i];
+      __syncthreads();
+      lo = hi = uni(scr[S_KEY]);
+      __syncthreads();
+    }
+  }
+  *gt = above_all;
+  return lo;
 }
 
 // ---------------------------------------------------------------------------
-// score: chunk c of row r -> keys in LDS, local histogram, published summary
+// score: chunk c of row r -> keys in LDS and in the workspace, then the
+// chunk's list: its lst largest entries in (key descending, index ascending)
+// order, stored in ascending index order, and the list's tagged header
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void phase_score(const FCtx& x, int r, int c, const FRow& f, int64_t j0, int64_t j1) {
   KArgs& a = *x.a;
   const int tid = lane_tid(), lane = tid & 63, wave = tid >> 6, kb = lane >> 5;
   uint32_t* keys_s = reinterpret_cast<uint32_t*>(x.smem + kOffKeys);
-  uint32_t* hist = reinterpret_cast<uint32_t*>(x.smem + kOffU);
-  for (int i = tid; i < kFBins; i += 256) hist[i] = 0;
+  uint32_t* hist = reinterpret_cast<uint32_t*>(x.smem + kOffHist);
   // A operand: rows 0..3 = the query's 4 heads, K block lane/32
   v8i av = {0, 0, 0, 0, 0, 0, 0, 0};
   int asc = 127;
@@ -363,7 +506,6 @@ __device__ __forceinline__ void phase_score(const FCtx& x, int r, int c, const F
     const int we = (int)((__float_as_uint(a.w[qrow]) >> 23) & 255u) - 127;
     asc = (int)a.q_scales[qrow * 2 + kb] + we;  // w_h = 2^we folded into the block scale
   }
-  __syncthreads();  // histogram zeroed
   // 32-entry MFMA tiles; wave w takes tiles w, w+4, ...; 16 tiles per wave per batch of loads
   const int n = (int)(j1 - j0);
   const int ntiles = (n + 31) >> 5;
@@ -390,13 +532,12 @@ __device__ __forceinline__ void phase_score(const FCtx& x, int r, int c, const F
       acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc, 4, 4, 0, asc, 0, ksv[u]);
       const int jl = tile * 32 + lane;  // local index
       if (lane < 32 && jl < n) {
+        // ReLU on the bit pattern (also maps -0 to +0), then the head sum
         const float r0 = __int_as_float(max(__float_as_int(acc[0]), 0));
         const float r1 = __int_as_float(max(__float_as_int(acc[1]), 0));
         const float r2 = __int_as_float(max(__float_as_int(acc[2]), 0));
         const float r3 = __int_as_float(max(__float_as_int(acc[3]), 0));
-        const uint32_t key = __float_as_uint((r0 + r1) + (r2 + r3));
-        keys_s[jl] = key;
-        atomicAdd(&hist[key >> 19], 1u);
+        keys_s[jl] = __float_as_uint((r0 + r1) + (r2 + r3));
       }
     }
   }
@@ -414,65 +555,53 @@ __device__ __forceinline__ void phase_score(const FCtx& x, int r, int c, const F
       }
     }
   }
-  // local emit_q-th bin bq: every entry above it, and entries in it while room remains
-  const uint32_t q = n < a.emit_q ? (uint32_t)n : (uint32_t)a.emit_q;
-  uint32_t bq = 0, ab = 0;
-  if (q > 0) bq = kth_bin(hist, q, x.scr, &ab);
-  const int E = (n + 255) / 256;  // thread t owns local entries [t*E, t*E + E)
-  const int e0 = tid * E;
-  uint32_t ng = 0, ne = 0;
-  for (int i = 0; i < E; ++i) {
-    const int jl = e0 + i;
-    if (jl < n) {
-      const uint32_t bin = keys_s[jl] >> 19;
-      ng += bin > bq ? 1u : 0u;
-      ne += bin == bq ? 1u : 0u;
-    }
-  }
-  uint32_t sg = ng, se = ne;  // inclusive prefix within the wave
+  // thread t owns the local entries [t*M, t*M + M)
+  const int M = (n + 255) >> 8;
+  const int e0 = tid * M;
+  const int nv = n - e0 < 0 ? 0 : (n - e0 < M ? n - e0 : M);
+  uint32_t kv[kFKPT];
 #pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t vg = __shfl_up(sg, off), ve = __shfl_up(se, off);
-    if (lane >= off) {
-      sg += vg;
-      se += ve;
+  for (int i = 0; i < kFKPT; ++i) kv[i] = i < nv ? keys_s[e0 + i] : 0u;
+  // The list: every entry with key >= tau, where tau is the lower edge of the
+  // histogram bin holding the chunk's lst_min-th largest key, or of the bin
+  // above it when listing that bin would pass lst entries (one radix pass over
+  // the chunk's own key range).  Chunks with at most lst entries list them all.
+  const uint32_t L = (uint32_t)a.lst;
+  const bool trunc = (uint32_t)n > L;
+  uint32_t tau = 0;
+  if (trunc) {
+    uint32_t lo, hi;
+    key_range<kFKPT>(kv, nv, hist, x.scr, &lo, &hi);
+    if (lo != hi) {
+      uint32_t blo, bhi, above, cnt;
+      radix_pass<kFKPT>(kv, nv, (uint32_t)a.lst_min, hist, hist + 2 * kFHist, x.scr, lo, hi, &blo, &bhi, &above, &cnt);
+      tau = above + cnt <= L ? blo : bhi + 1u;
+    } else {
+      tau = lo + 1u;  // n > L equal keys: list none (the row then takes the exact fallback)
     }
   }
-  if (lane == 63) {
-    x.scr[wave] = sg;
-    x.scr[4 + wave] = se;
-  }
-  __syncthreads();
-  uint32_t pg = sg - ng, pe = se - ne;
-  for (int w2 = 0; w2 < wave; ++w2) {
-    pg += x.scr[w2];
-    pe += x.scr[4 + w2];
-  }
-  const uint32_t tg = x.scr[0] + x.scr[1] + x.scr[2] + x.scr[3];
-  const uint32_t te = x.scr[4] + x.scr[5] + x.scr[6] + x.scr[7];
-  const uint32_t cap_eq = (uint32_t)a.emit_max - tg;  // tg < q <= emit_q < emit_max
-  const uint32_t n_emit = tg + (te < cap_eq ? te : cap_eq);
+  uint32_t cg = 0;
+#pragma unroll
+  for (int i = 0; i < kFKPT; ++i) cg += (i < nv && kv[i] >= tau) ? 1u : 0u;
+  uint32_t n_list;
+  uint32_t pos = block_exscan_val(cg, x.scr, &n_list);
   const size_t slot = (size_t)r * a.n_sc + c;
-  uint64_t* dst = a.ent + slot * a.emit_max;
-  const uint32_t jbase = (uint32_t)c * (uint32_t)a.C;
-  uint32_t pos = pg + (pe < cap_eq ? pe : cap_eq);
-  for (int i = 0; i < E; ++i) {
-    const int jl = e0 + i;
-    if (jl < n) {
-      const uint32_t key = keys_s[jl], bin = key >> 19;
-      bool take = bin > bq;
-      if (bin == bq) take = pe++ < cap_eq;
-      if (take) {
-        const uint64_t w64 = ((uint64_t)key << 32) | (jbase + (uint32_t)jl);
-        __builtin_amdgcn_raw_buffer_store_b64(v2u_t{(uint32_t)w64, (uint32_t)(w64 >> 32)}, x.coh.r,
-                                              coh_off(x.coh, dst + pos), 0, kSc1);
-        ++pos;
-      }
+  uint64_t* dst = a.ent + slot * a.lst;
+  uint32_t* dk = a.lkey + slot * a.lst;
+  const uint32_t jbase = (uint32_t)c * (uint32_t)a.C + (uint32_t)e0;
+#pragma unroll
+  for (int i = 0; i < kFKPT; ++i) {
+    if (i < nv && kv[i] >= tau) {
+      __builtin_amdgcn_raw_buffer_store_b64(v2u_t{jbase + (uint32_t)i, kv[i]}, x.coh.r,
+                                            coh_off(x.coh, dst + pos), 0, kSc1);
+      __builtin_amdgcn_raw_buffer_store_b32(kv[i], x.coh.r, coh_off(x.coh, dk + pos), 0, kSc1);
+      ++pos;
     }
   }
+  if (tid == 0) __builtin_amdgcn_raw_buffer_store_b32(tau, x.coh.r, coh_off(x.coh, a.ltau + slot), 0, kSc1);
   vm_drain();
   __syncthreads();
-  if (tid == 0) st_dev64(a.ent_hdr + slot, tagged(x.tag, n_emit | (bq << 12) | ((te > cap_eq ? 1u : 0u) << 25)));
+  if (tid == 0) st_dev64(a.ent_hdr + slot, tagged(x.tag, n_list | ((n_list < (uint32_t)n ? 1u : 0u) << 16)));
 }
 
 // ---------------------------------------------------------------------------
@@ -513,208 +642,304 @@ __device__ __forceinline__ void write_partial(const FCtx& x, AttnState<1>& st, i
     st_dev64(a.part_hdr + (size_t)r * (n_cs + a.n_hs) + (hca ? n_cs : 0) + pi, tagged(x.tag, 1u));
 }
 
-// Selection for CSA split s of row r: the split's slice of the ascending
-// selected list -> idx_s (and, for split 0, the whole row -> idx).  false on a
-// failed wait.
-//
-// The selected set is the k_eff first entries in (key descending, index
-// ascending) order, i.e. the entries whose order key (key << 32 | ~index) is
-// at least that of the k_eff-th one, c*.  Each score chunk emitted every entry
-// above its local emit_q-th bin bq (and that bin's entries up to emit_max,
-// else it is marked truncated).  From the emitted entries of the row: b1 = the
-// bin of the k_eff-th largest, and c* = the need-th largest order key in bin
-// b1.  This is exact when every chunk emitted all its entries in bins >= b1:
-// bq <= b1 (bq < b1 when truncated).  Otherwise c* comes from an exact radix
-// select over the row's stored keys.  Chunks cover ascending index ranges and
-// emit in index order, so the position of a selected index is the selected
-// count of the earlier chunks plus its rank within its chunk.
-__device__ __forceinline__ bool select_split(const FCtx& x, int r, int s, const FRow& f) {
+// Per-chunk arrays of a row in LDS (key region): list offsets (exclusive
+// prefix of the listed counts, total at [n_sc]), headers, thresholds.
+__device__ __forceinline__ uint32_t* row_off(const FCtx& x) { return reinterpret_cast<uint32_t*>(x.smem + kOffKeys); }
+__device__ __forceinline__ uint32_t* row_hdrs(const FCtx& x) { return row_off(x) + (kFMaxSlots + 8); }
+__device__ __forceinline__ uint32_t* row_taus(const FCtx& x) { return row_off(x) + 2 * (kFMaxSlots + 8); }
+
+// Wait for the list headers of every score chunk of row r -> LDS (counts,
+// offsets).  false on a failed wait.
+__device__ __forceinline__ bool row_lists(const FCtx& x, int r) {
   KArgs& a = *x.a;
-  const int tid = lane_tid();
-  const int64_t p_begin = (int64_t)s * a.cs;
-  const int64_t p_end = p_begin + a.cs < a.k ? p_begin + a.cs : a.k;
-  const int k_eff = (int)(f.n_vis < a.k ? f.n_vis : a.k);
-  int32_t* idx_s = reinterpret_cast<int32_t*>(x.smem + kOffIdx);
-  int32_t* idx_out = a.idx + (size_t)r * a.k;
-  for (int i = tid; i < a.cs; i += 256) idx_s[i] = -1;
-  const bool needs_sel = (s == 0) || (p_begin < k_eff);
-  if (needs_sel && k_eff > 0) {
-    uint32_t* e_off = reinterpret_cast<uint32_t*>(x.smem + kOffKeys);  // per chunk, LDS
-    uint32_t* e_bq = e_off + (kFMaxSlots + 1);
-    uint32_t* sel_off = e_bq + (kFMaxSlots + 1);
-    uint64_t* ent_s = reinterpret_cast<uint64_t*>(x.smem + kOffEnt);
-    uint32_t* hist = reinterpret_cast<uint32_t*>(x.smem + kOffHist);
-    const uint64_t* rowent = a.ent + (size_t)r * a.n_sc * a.emit_max;
-    const uint32_t* rowkeys = a.keys + (size_t)r * a.key_stride;
-    bool fail = false;
-    for (int sl = tid; sl < a.n_sc && !fail; sl += 256) {
-      const uint32_t v = poll_word(x, a.ent_hdr + (size_t)r * a.n_sc + sl, &fail, 2u);
-      e_off[sl] = v & 0xfffu;
-      e_bq[sl] = v >> 12;  // bin | truncated << 13
-    }
-    for (int i = tid; i < kFBins; i += 256) hist[i] = 0;
-    if (tid == 0) x.scr[S_BAD] = 0;
-    if (!all_ok(x, fail)) return false;
-    block_exscan(e_off, a.n_sc, x.scr);
-    const uint32_t n_ent = uni(e_off[a.n_sc]);
-    bool exact = n_ent <= (uint32_t)kFEntLds && n_ent >= (uint32_t)k_eff;
-    if (exact) {
-      // emitted entries -> LDS order keys, in global index order: wave w takes chunks
-      // w, w+4, ..., lane = entry within the chunk, 16 chunks in flight
-      const int lane = tid & 63, wave = tid >> 6;
-      for (int i0 = 0; i0 < a.emit_max; i0 += 64) {
-        const uint32_t i = (uint32_t)(i0 + lane);
-        for (int sb = wave; sb < a.n_sc; sb += 64) {
-          uint64_t v[16];
-#pragma unroll
-          for (int u = 0; u < 16; ++u) {
-            const int sl = sb + 4 * u;
-            v[u] = (sl < a.n_sc && i < e_off[sl + 1] - e_off[sl]) ? coh_ld64(x.coh, rowent + (size_t)sl * a.emit_max + i)
-                                                                  : 0ull;
-          }
-#pragma unroll
-          for (int u = 0; u < 16; ++u) {
-            const int sl = sb + 4 * u;
-            if (sl < a.n_sc && i < e_off[sl + 1] - e_off[sl]) {
-              const uint32_t key = (uint32_t)(v[u] >> 32), j = (uint32_t)v[u];
-              ent_s[e_off[sl] + i] = ((uint64_t)key << 32) | (uint32_t)~j;
-              atomicAdd(&hist[key >> 19], 1u);
-            }
-          }
-        }
-      }
-      __syncthreads();
-      uint32_t above = 0;
-      const uint32_t b1 = kth_bin(hist, (uint32_t)k_eff, x.scr, &above);
-      // every chunk must have emitted all of its entries in bins >= b1
-      for (int sl = tid; sl < a.n_sc; sl += 256) {
-        const uint32_t bq = e_bq[sl] & 0x1fffu, trunc = e_bq[sl] >> 13;
-        if (trunc ? bq >= b1 : bq > b1) x.scr[S_BAD] = 1;
-      }
-      if (tid == 0) x.scr[S_NB1] = 0;
-      __syncthreads();
-      exact = uni(x.scr[S_BAD]) == 0;
-      if (exact) {
-        // the bin-b1 entries, ranked by order key (the histogram area is free now)
-        uint64_t* comp = reinterpret_cast<uint64_t*>(x.smem + kOffHist);
-        for (uint32_t i0 = 0; i0 < n_ent; i0 += 256) {
-          const uint32_t i = i0 + tid;
-          const uint64_t e = i < n_ent ? ent_s[i] : 0ull;
-          const bool hit = i < n_ent && (uint32_t)(e >> 51) == b1;
-          const uint64_t m = __ballot(hit);
-          uint32_t base = 0;
-          if ((tid & 63) == 0 && m) base = atomicAdd(&x.scr[S_NB1], (uint32_t)__popcll(m));
-          base = __shfl(base, 0);
-          const uint32_t slot_i = base + (uint32_t)__popcll(m & ((1ull << (tid & 63)) - 1ull));
-          if (hit && slot_i < (uint32_t)kFRankMax) comp[slot_i] = e;
-        }
-        __syncthreads();
-        const uint32_t nb = uni(x.scr[S_NB1]);
-        exact = nb <= (uint32_t)kFRankMax;
-        if (exact) {
-          const uint32_t need = (uint32_t)k_eff - above;  // >= 1
-          const uint32_t n_pad = (nb + 15) & ~15u;
-          for (uint32_t i = nb + tid; i < n_pad; i += 256) comp[i] = 0ull;
-          __syncthreads();
-          for (uint32_t i = tid; i < nb; i += 256) {
-            const uint64_t ci = comp[i];
-            uint32_t rank = 0;
-            for (uint32_t j0 = 0; j0 < n_pad; j0 += 16) {
-              uint64_t qv[16];
-#pragma unroll
-              for (int u = 0; u < 16; ++u) qv[u] = comp[j0 + u];
-#pragma unroll
-              for (int u = 0; u < 16; ++u) rank += qv[u] > ci ? 1u : 0u;
-            }
-            if (rank == need - 1) {
-              x.scr[S_CSTAR_LO] = (uint32_t)ci;
-              x.scr[S_CSTAR_HI] = (uint32_t)(ci >> 32);
-            }
-          }
-          __syncthreads();
-        }
-      }
-    }
-    if (!exact) {
-      // exact radix select over the row's stored keys: the k_eff-th largest key K*, then
-      // the (need_left)-th smallest index among keys equal to K* (indices < 2^18)
-      uint32_t* bins = hist;
-      uint32_t nl;
-      const uint32_t n_vis = (uint32_t)f.n_vis;
-      const uint32_t kstar = radix_select_desc(
-          n_vis, (uint32_t)k_eff, [&](uint32_t i) { return coh_ld32(x.coh, rowkeys + i); },
-          [&](uint32_t) { return true; }, &nl, bins, x.scr);
-      uint32_t nl2;
-      const uint32_t njstar = radix_select_desc_low(
-          n_vis, nl, 18, 0xfffc0000u, [&](uint32_t i) { return ~i; },
-          [&](uint32_t i) { return coh_ld32(x.coh, rowkeys + i) == kstar; }, &nl2, bins, x.scr);
-      if (tid == 0) {
-        x.scr[S_CSTAR_LO] = njstar;
-        x.scr[S_CSTAR_HI] = kstar;
-      }
-      __syncthreads();
-    }
-    const uint64_t cstar = ((uint64_t)uni(x.scr[S_CSTAR_HI]) << 32) | uni(x.scr[S_CSTAR_LO]);
-    auto emit_at = [&](uint32_t pos, uint32_t j) {
-      if ((int64_t)pos >= p_begin && (int64_t)pos < p_end) idx_s[pos - p_begin] = (int32_t)j;
-      if (s == 0 && pos < (uint32_t)a.k) idx_out[pos] = (int32_t)j;
-    };
-    if (exact) {
-      // the entries are in index order: position = selected entries before it.  Thread t
-      // owns entries [t*M, t*M + M); one block scan of the per-thread counts.
-      const uint32_t M = (n_ent + 255) / 256, m0 = tid * M;
-      uint32_t cnt = 0;
-      for (uint32_t i = m0; i < m0 + M && i < n_ent; ++i) cnt += ent_s[i] >= cstar ? 1u : 0u;
-      sel_off[tid] = cnt;
-      __syncthreads();
-      block_exscan(sel_off, 256, x.scr);
-      uint32_t pos = sel_off[tid];
-      const uint32_t pend = sel_off[tid + 1];
-      if (pos < pend && (s == 0 || ((int64_t)pos < p_end && (int64_t)pend > p_begin))) {
-        for (uint32_t i = m0; i < m0 + M && i < n_ent; ++i) {
-          const uint64_t e = ent_s[i];
-          if (e >= cstar) emit_at(pos++, ~(uint32_t)e);
-        }
-      }
-    } else {
-      const int C = a.C;
-      const uint32_t nv = n_vis_u32(f);
-      // selected count per chunk -> offsets, then the chunks in index order
-      for (int sl = tid; sl < a.n_sc; sl += 256) {
-        uint32_t cnt = 0;
-        const uint32_t jb = (uint32_t)sl * C, je = jb + C < nv ? jb + C : nv;
-        for (uint32_t j = jb; j < je; ++j)
-          cnt += (((uint64_t)coh_ld32(x.coh, rowkeys + j) << 32) | (uint32_t)~j) >= cstar ? 1u : 0u;
-        sel_off[sl] = cnt;
-      }
-      __syncthreads();
-      block_exscan(sel_off, a.n_sc, x.scr);
-      for (int sl = tid; sl < a.n_sc; sl += 256) {
-        uint32_t pos = sel_off[sl];
-        const uint32_t pend = sel_off[sl + 1];
-        if (pos == pend || (s != 0 && ((int64_t)pos >= p_end || (int64_t)pend <= p_begin))) continue;
-        const uint32_t jb = (uint32_t)sl * C, je = jb + C < nv ? jb + C : nv;
-        for (uint32_t j = jb; j < je; ++j)
-          if ((((uint64_t)coh_ld32(x.coh, rowkeys + j) << 32) | (uint32_t)~j) >= cstar) emit_at(pos++, j);
-      }
-    }
-    __syncthreads();
+  const int tid = lane_tid(), nsc = a.n_sc;
+  uint32_t* e_off = row_off(x);
+  uint32_t* e_n = row_hdrs(x);
+  bool fail = false;
+  for (int sl = tid; sl < nsc && !fail; sl += 256) {
+    const uint32_t v = poll_word(x, a.ent_hdr + (size_t)r * nsc + sl, &fail, 2u);
+    e_n[sl] = v;
+    e_off[sl] = v & 0xffffu;
   }
-  if (s == 0)
-    for (int i = k_eff + tid; i < a.k; i += 256) idx_out[i] = -1;
-  __syncthreads();
+  if (!all_ok(x, fail)) return false;
+  block_exscan(e_off, nsc, x.scr);
   return true;
 }
 
-// Attention item: CSA selected split (kind 0, rows through idx_s), CSA window
-// split (kind 1) or HCA split (kind 2) of row r, then its partial.
-__device__ __forceinline__ void attend_item(const FCtx& x, int r, int kind, int s, const FRow& f) {
+// Selection threshold of row r, one workgroup.  The row takes the k_eff first
+// entries in (key descending, index ascending) order.  Each score chunk listed
+// every entry whose key is at least its threshold tau (all of its entries when
+// it has at most lst).  K* = the k_eff-th largest listed key; the row takes
+// every listed entry above K* and the r_eq = k_eff - (listed keys above K*)
+// listed entries equal to K* of lowest index.  Chunks cover ascending index
+// ranges and list in index order, so the lists concatenated in chunk order
+// are in index order, and the taken ties are the first r_eq equal keys of that
+// concatenation: those at or before position `cut`.  This is the exact
+// selection when every truncated chunk has tau <= K* (it then listed all of
+// its entries >= K*, ties included).  Otherwise an exact radix select over the
+// row's stored keys gives the order key (K*, j*) of the k_eff-th entry.
+// Published: row_k = K*, row_cut = cut (or 1 << 31 | j*), then each CSA
+// group's output offset; idx positions [k_eff, k) are set to -1.  The
+// selected entries themselves are taken and written by the CSA groups.
+__device__ __forceinline__ bool select_row(const FCtx& x, int r, const FRow& f) {
+  KArgs& a = *x.a;
+  const int tid = lane_tid();
+  const int k_eff = (int)(f.n_vis < a.k ? f.n_vis : a.k);
+  const int nsc = a.n_sc, ngrp = a.n_cs_sel, cgs = a.cg;
+  int32_t* idx_out = a.idx + (size_t)r * a.k;
+  for (int i = k_eff + tid; i < a.k; i += 256) idx_out[i] = -1;
+  uint64_t* gout = a.grp_off + (size_t)r * ngrp;
+  if (k_eff == 0) {  // nothing visible: every list is empty
+    if (tid == 0) {
+      st_dev64(a.row_k + r, tagged(x.tag, 0u));
+      st_dev64(a.row_cut + r, tagged(x.tag, 0u));
+    }
+    for (int g = tid; g < ngrp; g += 256) st_dev64(gout + g, tagged(x.tag, 0u));
+    return true;
+  }
+  if (!row_lists(x, r)) return false;
+  uint32_t* e_off = row_off(x);
+  uint32_t* e_n = row_hdrs(x);
+  uint32_t* e_tau = row_taus(x);
+  uint32_t* lk_s = reinterpret_cast<uint32_t*>(x.smem + kOffLst);
+  uint32_t* hist = reinterpret_cast<uint32_t*>(x.smem + kOffHist);
+  const uint32_t n_ent = uni(e_off[nsc]);
+  bool exact = n_ent <= (uint32_t)kFEntLds && n_ent >= (uint32_t)k_eff;
+  if (tid == 0) x.scr[S_BAD] = exact ? 0u : 1u;
+  if (exact) {
+    // thresholds, and the listed keys -> LDS in chunk order (16-byte loads, 8 per thread in flight)
+    for (int sl = tid; sl < nsc; sl += 256) e_tau[sl] = coh_ld32(x.coh, a.ltau + (size_t)r * nsc + sl);
+    const uint32_t* rowk = a.lkey + (size_t)r * nsc * a.lst;
+    const int L4 = a.lst >> 2;
+    const int nq = nsc * L4;
+    for (int q0 = 0; q0 < nq; q0 += 256 * 8) {
+      v4u_t v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int q = q0 + tid + 256 * u;
+        const int sl = q / L4, i = 4 * (q - sl * L4);
+        const bool use = q < nq && (uint32_t)i < (e_n[q < nq ? sl : 0] & 0xffffu);
+        v[u] = use ? coh_ld128(x.coh, rowk + (size_t)sl * a.lst + i) : v4u_t{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int q = q0 + tid + 256 * u;
+        if (q >= nq) continue;
+        const int sl = q / L4, i = 4 * (q - sl * L4);
+        const uint32_t cnt = e_n[sl] & 0xffffu;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if ((uint32_t)(i + e) < cnt) lk_s[e_off[sl] + i + e] = v[u][e];
+      }
+    }
+    __syncthreads();
+    // K* over the listed keys, thread t holding positions [t*M, t*M + M)
+    const int M = (int)((n_ent + 255) >> 8);
+    const int m0 = tid * M;
+    const int nv = (int)n_ent - m0 < 0 ? 0 : ((int)n_ent - m0 < M ? (int)n_ent - m0 : M);
+    uint32_t kv[kFEPT];
+#pragma unroll
+    for (int i = 0; i < kFEPT; ++i) kv[i] = i < nv ? lk_s[m0 + i] : 0u;
+    uint32_t gt_all;
+    const uint32_t kstar = kth_key<kFEPT>(kv, nv, (uint32_t)k_eff, hist, x.scr, &gt_all);
+    const uint32_t r_eq = (uint32_t)k_eff - gt_all;  // >= 1
+    for (int sl = tid; sl < nsc; sl += 256)
+      if ((e_n[sl] >> 16) != 0u && e_tau[sl] > kstar) x.scr[S_BAD] = 1;
+    uint32_t cgt = 0, ceq = 0;
+#pragma unroll
+    for (int i = 0; i < kFEPT; ++i) {
+      cgt += (i < nv && kv[i] > kstar) ? 1u : 0u;
+      ceq += (i < nv && kv[i] == kstar) ? 1u : 0u;
+    }
+    uint32_t tot;
+    const uint32_t pre = block_exscan_val(cgt | (ceq << 16), x.scr, &tot);
+    const uint32_t pre_gt = pre & 0xffffu, pre_eq = pre >> 16;
+    if (pre_eq < r_eq && pre_eq + ceq >= r_eq) {  // this thread holds the r_eq-th tie
+      uint32_t e = pre_eq, cut = 0;
+#pragma unroll
+      for (int i = 0; i < kFEPT; ++i)
+        if (i < nv && kv[i] == kstar) {
+          ++e;
+          if (e == r_eq) cut = (uint32_t)(m0 + i);
+        }
+      x.scr[S_CUT] = cut;
+    }
+    __syncthreads();
+    exact = uni(x.scr[S_BAD]) == 0u;
+    if (exact) {
+      const uint32_t cut = uni(x.scr[S_CUT]);
+      if (tid == 0) {
+        st_dev64(a.row_k + r, tagged(x.tag, kstar));
+        st_dev64(a.row_cut + r, tagged(x.tag, cut));
+      }
+      // group g starts at listed position P = e_off[g * cg]: its output offset is the
+      // count of taken entries before P
+      for (int g = 0; g < ngrp; ++g) {
+        const uint32_t P = e_off[g * cgs < nsc ? g * cgs : nsc];
+        if (P >= n_ent) {
+          if (tid == 0) st_dev64(gout + g, tagged(x.tag, (uint32_t)k_eff));
+        } else if (P >= (uint32_t)m0 && P < (uint32_t)(m0 + M)) {
+          uint32_t gb = pre_gt, eb = pre_eq;
+#pragma unroll
+          for (int i = 0; i < kFEPT; ++i)
+            if ((uint32_t)(m0 + i) < P) {
+              gb += kv[i] > kstar ? 1u : 0u;
+              eb += kv[i] == kstar ? 1u : 0u;
+            }
+          st_dev64(gout + g, tagged(x.tag, gb + (eb < r_eq ? eb : r_eq)));
+        }
+      }
+      return true;
+    }
+  }
+  // exact radix select over the row's stored keys: the k_eff-th largest key K*, then
+  // the (need_left)-th smallest index among keys equal to K* (indices < 2^18)
+  if (tid == 0) atomicAdd(a.ctl + W_FALLBACK, 1u);
+  const uint32_t* rowkeys = a.keys + (size_t)r * a.key_stride;
+  uint32_t nl;
+  const uint32_t n_vis = n_vis_u32(f);
+  const uint32_t kstar = radix_select_desc(
+      n_vis, (uint32_t)k_eff, [&](uint32_t i) { return coh_ld32(x.coh, rowkeys + i); }, [&](uint32_t) { return true; },
+      &nl, hist, x.scr);
+  uint32_t nl2;
+  const uint32_t njstar = radix_select_desc_low(
+      n_vis, nl, 18, 0xfffc0000u, [&](uint32_t i) { return ~i; },
+      [&](uint32_t i) { return coh_ld32(x.coh, rowkeys + i) == kstar; }, &nl2, hist, x.scr);
+  if (tid == 0) {
+    st_dev64(a.row_k + r, tagged(x.tag, kstar));
+    st_dev64(a.row_cut + r, tagged(x.tag, 0x80000000u | (~njstar & 0x3ffffu)));
+  }
+  const uint64_t cstar = ((uint64_t)kstar << 32) | njstar;
+  // selected count per chunk -> offsets at the group starts
+  const uint32_t C = (uint32_t)a.C;
+  uint32_t* e_sel = row_taus(x);
+  for (int sl = tid; sl < nsc; sl += 256) {
+    uint32_t cnt = 0;
+    const uint32_t jb = (uint32_t)sl * C, je = jb + C < n_vis ? jb + C : n_vis;
+    for (uint32_t j = jb; j < je; ++j)
+      cnt += (((uint64_t)coh_ld32(x.coh, rowkeys + j) << 32) | (uint32_t)~j) >= cstar ? 1u : 0u;
+    e_sel[sl] = cnt;
+  }
+  __syncthreads();
+  block_exscan(e_sel, nsc, x.scr);
+  for (int g = tid; g < ngrp; g += 256)
+    st_dev64(gout + g, tagged(x.tag, e_sel[g * cgs < nsc ? g * cgs : nsc]));
+  return true;
+}
+
+// CSA group g of row r (score chunks [g*cg, g*cg + cg)): its selected entries,
+// in ascending index order -> LDS (returns how many, or -1 on a failed wait).
+// The group's lists are loaded before the row's threshold is published.
+__device__ __forceinline__ int group_select(const FCtx& x, int r, int g, const FRow& f) {
+  KArgs& a = *x.a;
+  const int tid = lane_tid(), nsc = a.n_sc;
+  const int c0 = g * a.cg < nsc ? g * a.cg : nsc, c1 = c0 + a.cg < nsc ? c0 + a.cg : nsc;
+  int32_t* sel_s = reinterpret_cast<int32_t*>(x.smem + kOffSel);
+  if (!row_lists(x, r)) return -1;
+  uint32_t* e_off = row_off(x);
+  uint32_t* e_n = row_hdrs(x);
+  uint64_t* ent_s = reinterpret_cast<uint64_t*>(x.smem + kOffLst);
+  const uint32_t base = e_off[c0], n_loc = e_off[c1] - base;
+  {  // the group's lists -> LDS (16-byte loads, 8 per thread in flight)
+    const uint64_t* gent = a.ent + ((size_t)r * nsc + c0) * a.lst;
+    const int L2 = a.lst >> 1;
+    const int npairs = (c1 - c0) * L2;
+    for (int q0 = 0; q0 < npairs; q0 += 256 * 8) {
+      v4u_t v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int q = q0 + tid + 256 * u;
+        const int sl = q / L2, i = 2 * (q - sl * L2);
+        const bool use = q < npairs && (uint32_t)i < (e_n[c0 + (q < npairs ? sl : 0)] & 0xffffu);
+        v[u] = use ? coh_ld128(x.coh, gent + (size_t)sl * a.lst + i) : v4u_t{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int q = q0 + tid + 256 * u;
+        if (q >= npairs) continue;
+        const int sl = q / L2, i = 2 * (q - sl * L2);
+        const uint32_t cnt = e_n[c0 + sl] & 0xffffu, o = e_off[c0 + sl] - base;
+        if ((uint32_t)i < cnt) ent_s[o + i] = (uint64_t)v[u][0] | ((uint64_t)v[u][1] << 32);
+        if ((uint32_t)i + 1 < cnt) ent_s[o + i + 1] = (uint64_t)v[u][2] | ((uint64_t)v[u][3] << 32);
+      }
+    }
+  }
+  // the row's threshold
+  bool fail = false;
+  if (tid == 0) {
+    x.scr[S_KEY] = poll_word(x, a.row_k + r, &fail, 16u);
+    if (!fail) x.scr[S_CUT] = poll_word(x, a.row_cut + r, &fail, 16u);
+  }
+  if (!all_ok(x, fail)) return -1;
+  const uint32_t kstar = uni(x.scr[S_KEY]), cut = uni(x.scr[S_CUT]);
+  uint32_t tot;
+  if ((cut >> 31) == 0u) {
+    // listed entries above K*, and ties at listed positions up to cut
+    const uint32_t M = (n_loc + 255) >> 8, m0 = (uint32_t)tid * M;
+    uint32_t cnt = 0;
+    for (uint32_t i = 0; i < M; ++i) {
+      const uint32_t p = m0 + i;
+      if (p < n_loc) {
+        const uint32_t key = (uint32_t)(ent_s[p] >> 32);
+        cnt += (key > kstar || (key == kstar && base + p <= cut)) ? 1u : 0u;
+      }
+    }
+    uint32_t pos = block_exscan_val(cnt, x.scr, &tot);
+    for (uint32_t i = 0; i < M; ++i) {
+      const uint32_t p = m0 + i;
+      if (p < n_loc) {
+        const uint64_t e = ent_s[p];
+        const uint32_t key = (uint32_t)(e >> 32);
+        if (key > kstar || (key == kstar && base + p <= cut)) sel_s[pos++] = (int32_t)(uint32_t)e;
+      }
+    }
+  } else {
+    // fallback: the order key (key, ~index) of every visible entry of the group's chunks
+    const uint64_t cstar = ((uint64_t)kstar << 32) | (uint32_t)~(cut & 0x3ffffu);
+    const uint32_t* rowkeys = a.keys + (size_t)r * a.key_stride;
+    const uint32_t C = (uint32_t)a.C, nvis = n_vis_u32(f);
+    const uint32_t jb = (uint32_t)c0 * C, je = (uint32_t)c1 * C < nvis ? (uint32_t)c1 * C : nvis;
+    const uint32_t n = je > jb ? je - jb : 0u;
+    const uint32_t M = (n + 255) >> 8, m0 = (uint32_t)tid * M;
+    uint32_t cnt = 0;
+    for (uint32_t i = 0; i < M; ++i) {
+      const uint32_t j = jb + m0 + i;
+      if (m0 + i < n) cnt += (((uint64_t)coh_ld32(x.coh, rowkeys + j) << 32) | (uint32_t)~j) >= cstar ? 1u : 0u;
+    }
+    uint32_t pos = block_exscan_val(cnt, x.scr, &tot);
+    for (uint32_t i = 0; i < M; ++i) {
+      const uint32_t j = jb + m0 + i;
+      if (m0 + i < n && (((uint64_t)coh_ld32(x.coh, rowkeys + j) << 32) | (uint32_t)~j) >= cstar)
+        sel_s[pos++] = (int32_t)j;
+    }
+  }
+  __syncthreads();
+  return (int)tot;
+}
+
+// the group's selected indices -> idx at the offset the row selection published
+__device__ __forceinline__ bool group_write_idx(const FCtx& x, int r, int g, int n_sel) {
+  KArgs& a = *x.a;
+  const int tid = lane_tid();
+  bool fail = false;
+  if (tid == 0) x.scr[S_KEY] = poll_word(x, a.grp_off + (size_t)r * a.n_cs_sel + g, &fail, 32u);
+  if (!all_ok(x, fail)) return false;
+  const uint32_t off = uni(x.scr[S_KEY]);
+  const int32_t* sel_s = reinterpret_cast<const int32_t*>(x.smem + kOffSel);
+  int32_t* dst = a.idx + (size_t)r * a.k + off;
+  for (int i = tid; i < n_sel && off + (uint32_t)i < (uint32_t)a.k; i += 256) dst[i] = sel_s[i];
+  return true;
+}
+
+// Attention item: CSA group (kind 0, its n_sel selected rows in LDS), CSA
+// window split (kind 1) or HCA split (kind 2) of row r, then its partial.
+__device__ __forceinline__ void attend_item(const FCtx& x, int r, int kind, int s, const FRow& f, int n_sel) {
   KArgs& a = *x.a;
   int64_t p_begin, p_end;
   int pi = s;
   if (kind == 0) {
-    p_begin = (int64_t)s * a.cs;
-    p_end = p_begin + a.cs < a.k ? p_begin + a.cs : a.k;
+    p_begin = 0;
+    p_end = n_sel;
   } else if (kind == 1) {
     p_begin = (int64_t)s * a.cs;
     p_end = p_begin + a.cs < a.W ? p_begin + a.cs : a.W;
@@ -724,7 +949,7 @@ __device__ __forceinline__ void attend_item(const FCtx& x, int r, int kind, int 
     p_begin = (int64_t)s * a.hs;
     p_end = p_begin + a.hs < list_len ? p_begin + a.hs : list_len;
   }
-  const int32_t* idx_s = reinterpret_cast<const int32_t*>(x.smem + kOffIdx);
+  const int32_t* idx_s = reinterpret_cast<const int32_t*>(x.smem + kOffSel);
   constexpr uint64_t RB = 2 * 128 * 2;
   // Row addresses from 32-bit offsets against per-row bases: list positions
   // below `split` are pooled rows (selected ones for kind 0, HCA rows for
@@ -819,20 +1044,19 @@ __device__ __forceinline__ void item_merge(const FCtx& x, bool hca, int r, int h
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_decode_fused(FusedArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
   uint32_t* scr = reinterpret_cast<uint32_t*>(smem + kOffScr);
-  if (lane_tid() == 0) {
-    uint32_t tag = ld_dev(a.ctl + W_EPOCH) + 1u;
-    if (tag == 0) tag = 1;
-    scr[S_TAG] = tag;
-  }
-  __syncthreads();
-  const uint32_t tag = uni(scr[S_TAG]);
-  __syncthreads();
+  // the launch's tag: every thread loads the epoch word; the load is waited for
+  // at the tag's first use (a first-round score chunk: when it publishes)
+  const uint32_t tag0 = ld_dev(a.ctl + W_EPOCH) + 1u;
+  const uint32_t tag = tag0 == 0u ? 1u : tag0;
   const int rounds = a.rounds;
-  // Work units in dependency order: the R * n_sc score chunks, then the items
-  // [CSA selected splits | CSA window splits | HCA splits | CSA merges | HCA
-  // merges].  Units are handed out in that order through one returning atomic,
-  // and a unit only waits for units of lower number, whose holders are already
-  // running: every wait ends whatever the residency of the grid.
+  // Work units in dependency order: [score chunks | row selections | CSA groups
+  // | CSA window splits | HCA splits | HCA merges | CSA merges].  The score
+  // chunks stream first on every workgroup; the HCA stream then runs beside the
+  // latency-bound selection chain on a limited number of workgroups.  Units
+  // are handed out in that order, the first grid-size ones by workgroup id
+  // (workgroups are dispatched in id order) and the rest through one returning
+  // atomic, and a unit only waits for units of lower number, whose holders are
+  // already running: every wait ends whatever the residency of the grid.
   // Every workgroup runs the same number of rounds (rounds * grid >= total), so
   // the loop bound is uniform; a round whose unit number is past the end (or
   // that follows a reported error) does nothing.
@@ -842,33 +1066,49 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     KArgs& A = *ap;
     const FCtx x{ap, smem, scr, tag, make_coh(A.ctl)};
     const int R = A.R, nM = A.H / 4;
-    const int64_t nS = (int64_t)R * A.n_sc;
-    const int64_t e1 = nS + (int64_t)R * A.n_cs_sel, e2 = e1 + (int64_t)R * A.n_cs_win,
-                  e3 = e2 + (int64_t)R * A.n_hs, e4 = e3 + (int64_t)R * nM, total = e4 + (int64_t)R * nM;
-    if (lane_tid() == 0) scr[S_TICKET] = error_seen(x) ? 0xffffffffu : atomicAdd(A.ctl + W_TICKET, 1u);
-    __syncthreads();
-    const int64_t it = uni(scr[S_TICKET]);
-    __syncthreads();
+    const int64_t u_sel = (int64_t)R * A.n_sc, u_grp = u_sel + R;
+    const int64_t u_win = u_grp + (int64_t)R * A.n_cs_sel, u_hca = u_win + (int64_t)R * A.n_cs_win;
+    const int64_t u_mh = u_hca + (int64_t)R * A.n_hs, u_mc = u_mh + (int64_t)R * nM;
+    const int64_t total = u_mc + (int64_t)R * nM;
+    int64_t it = (int64_t)blockIdx.x;
+    if (round > 0) {
+      if (lane_tid() == 0)
+        scr[S_TICKET] = error_seen(x) ? 0xffffffffu : (uint32_t)gridDim.x + atomicAdd(A.ctl + W_TICKET, 1u);
+      __syncthreads();
+      it = uni(scr[S_TICKET]);
+      __syncthreads();
+    }
     if (it >= total) {
       // nothing to do this round
-    } else if (it < nS) {
+    } else if (it < u_sel) {
       const int r = (int)(it / A.n_sc), c = (int)(it % A.n_sc);
       const FRow f = row_info(A, r);
       int64_t j0 = (int64_t)c * A.C, j1 = j0 + A.C;
       if (j1 > f.n_vis) j1 = f.n_vis;
       if (j0 > j1) j0 = j1;
       phase_score(x, r, c, f, j0, j1);
-    } else if (it >= e3) {
-      const bool hca = it >= e4;
-      const int64_t m = it - (hca ? e4 : e3);
+    } else if (it < u_grp) {
+      const int r = (int)(it - u_sel);
+      (void)select_row(x, r, row_info(A, r));
+    } else if (it >= u_mh) {
+      const bool hca = it < u_mc;
+      const int64_t m = it - (hca ? u_mh : u_mc);
       item_merge(x, hca, (int)(m / nM), (int)(m % nM) * 4);
-    } else {
-      const int kind = it < e1 ? 0 : it < e2 ? 1 : 2;
-      const int64_t q = it - (kind == 0 ? nS : kind == 1 ? e1 : e2);
-      const int r = (int)(q % R), s = (int)(q / R);
+    } else if (it < u_win) {
+      const int64_t q = it - u_grp;
+      const int r = (int)(q % R), g = (int)(q / R);
       const FRow f = row_info(A, r);
-      const bool ok = kind != 0 || select_split(x, r, s, f);
-      if (ok) attend_item(x, r, kind, s, f);
+      const int n_sel = group_select(x, r, g, f);
+      if (n_sel >= 0) {
+        attend_item(x, r, 0, g, f, n_sel);
+        (void)group_write_idx(x, r, g, n_sel);
+      }
+    } else {
+      // attention: kind 1 = CSA window split, 2 = HCA split
+      const int kind = it < u_hca ? 1 : 2;
+      const int64_t q = it - (kind == 1 ? u_win : u_hca);
+      const int r = (int)(q % R), s = (int)(q / R);
+      attend_item(x, r, kind, s, row_info(A, r), 0);
     }
   }
   const int G = (int)gridDim.x;
@@ -910,29 +1150,40 @@ FusedPlan plan_fused(int64_t R, int64_t max_pool, int64_t max_hpool, int H, int 
   FusedPlan p{};
   const int G = fused_grid();
   p.grid = G;
-  // score chunk: the smallest multiple of 256 (>= 1024) that gives every chunk its own workgroup
+  p.cs = 64;
+  p.n_cs_win = split_count(W, p.cs);
+  p.hs = 512;
+  p.n_hs = split_count(max_hpool + W_hca, p.hs);
+  if (p.n_hs == 0) p.n_hs = 1;
+  // score chunk: the smallest multiple of 256 (>= 1024) that gives every chunk a
+  // workgroup of its own (more chunks than workgroups: later rounds take the rest)
   int64_t C = 1024;
   if (G > 0) {
     const int64_t per = (R * max_pool + G - 1) / G;
     if (per > C) C = ((per + 255) / 256) * 256;
   }
-  p.C = (int)(C > kFMaxC ? kFMaxC + 1 : C);
-  p.n_sc = max_pool > 0 ? (int)((max_pool + C - 1) / C) : 1;
-  p.cs = 64;
-  p.n_cs_sel = split_count(k, p.cs);
-  p.n_cs_win = split_count(W, p.cs);
-  if (p.n_cs_sel + p.n_cs_win == 0) p.n_cs_win = 1;
-  p.hs = 128;
-  p.n_hs = split_count(max_hpool + W_hca, p.hs);
-  if (p.n_hs == 0) p.n_hs = 1;
-  // emitted per chunk: about twice a chunk's expected share of the top-k, plus slack
+  p.C = (int)(C > kFMaxC ? kFMaxC : C);
+  p.n_sc = max_pool > 0 ? (int)((max_pool + p.C - 1) / p.C) : 1;
+  // CSA groups: consecutive chunks holding about 64 selected entries each
+  const int64_t want = split_count(k, 64) > 0 ? split_count(k, 64) : 1;
+  p.cg = (int)((p.n_sc + want - 1) / want);
+  if (p.cg < 1) p.cg = 1;
+  p.n_cs_sel = (p.n_sc + p.cg - 1) / p.cg;
+  // listed per chunk: about twice a chunk's expected share of the top-k plus
+  // slack, and room for 16 more (a threshold bin's worth); the stride is a
+  // multiple of 4, so lists are read 16 bytes at a time, and the row's listed
+  // keys fit its LDS staging.  Short lists only make the exact fallback more
+  // likely.
   const int64_t share = p.n_sc > 0 ? ((int64_t)k + p.n_sc - 1) / p.n_sc : k;
-  int64_t q = 2 * share + 16;
-  if (q > p.C) q = p.C;
-  int64_t qm = q + 16;
-  if (qm > p.C) qm = p.C;
-  p.emit_q = (int)q;
-  p.emit_max = (int)qm;
+  int64_t Lm = 2 * share + 16;
+  int64_t L = Lm + 16;
+  if (L * p.n_sc > kFEntLds) L = kFEntLds / p.n_sc;
+  L &= ~(int64_t)3;
+  if (L < 4) L = 4;
+  if (L > p.C) L = p.C;
+  if (Lm > L) Lm = L;
+  p.lst_min = (int)Lm;
+  p.lst = (int)L;
   p.key_stride = (max_pool + 3) & ~(int64_t)3;
   auto al = [](size_t b) { return (b + 255) & ~(size_t)255; };
   const size_t slots = (size_t)R * p.n_sc;
@@ -941,7 +1192,12 @@ FusedPlan plan_fused(int64_t R, int64_t max_pool, int64_t max_hpool, int H, int 
   s += al(W_CTL * 4);
   s += al((size_t)R * p.key_stride * 4);
   s += al(slots * 8);
-  s += al(slots * p.emit_max * 8);
+  s += al(slots * p.lst * 8);
+  s += al(slots * p.lst * 4);
+  s += al(slots * 4);
+  s += al((size_t)R * 8);
+  s += al((size_t)R * 8);
+  s += al((size_t)R * p.n_cs_sel * 8);
   s += al((size_t)R * (n_cs + p.n_hs) * 8);
   s += al((size_t)R * n_cs * H * 128 * 4);
   s += al((size_t)R * n_cs * H * 2 * 4);
@@ -952,13 +1208,15 @@ FusedPlan plan_fused(int64_t R, int64_t max_pool, int64_t max_hpool, int H, int 
 }
 
 int fused_supported(int64_t R, int64_t max_pool, int64_t max_hpool, int H, int k, int W, int W_hca) {
-  if (R < 1 || R > kFMaxRows || max_pool > (int64_t)kFMaxVisible || H % 16 != 0 || H > 64 || H < 16) return 0;
+  if (R < 1 || R > kFMaxRows || max_pool > (int64_t)kFMaxVisible || H % 16 != 0 || H > 64 || H < 16 || k > kFMaxSel)
+    return 0;
   const FusedPlan p = plan_fused(R, max_pool, max_hpool, H, k, W, W_hca);
-  if (p.grid <= 0 || p.C > kFMaxC || p.n_sc > kFMaxSlots || (int64_t)R * p.n_sc > p.grid) return 0;
+  if (p.grid <= 0 || p.C > kFMaxC || p.n_sc > kFMaxSlots) return 0;
   return 1;
 }
 
 size_t fused_error_word_offset() { return W_ERROR * 4; }
+size_t fused_fallback_word_offset() { return W_FALLBACK * 4; }
 
 int launch_fused(int R, const int64_t* tok_off, const int64_t* q_pos, const int64_t* pool_off,
                  const int64_t* hpool_off, int64_t max_pool, int64_t max_hpool, int m, int m_hca, int H,
@@ -967,7 +1225,7 @@ int launch_fused(int R, const int64_t* tok_off, const int64_t* q_pos, const int6
                  const void* kv_pool, const void* kv_hpool, const void* kv_raw, int32_t* idx, void* csa_out,
                  float* csa_lse, void* hca_out, float* hca_lse, void* ws, hipStream_t stream) {
   const FusedPlan pl = plan_fused(R, max_pool, max_hpool, H, k, W, W_hca);
-  if (pl.grid <= 0 || pl.C > kFMaxC || (int64_t)R * pl.n_sc > pl.grid) return -1;
+  if (pl.grid <= 0 || pl.C > kFMaxC || pl.n_sc > kFMaxSlots) return -1;
   uint8_t* p = (uint8_t*)ws;
   auto take = [&](size_t bytes) {
     uint8_t* q0 = p;
@@ -985,18 +1243,23 @@ int launch_fused(int R, const int64_t* tok_off, const int64_t* q_pos, const int6
   a.q = (const uint8_t*)q; a.kv_pool = (const uint8_t*)kv_pool; a.kv_hpool = (const uint8_t*)kv_hpool;
   a.kv_raw = (const uint8_t*)kv_raw;
   a.idx = idx; a.csa_out = (uint8_t*)csa_out; a.csa_lse = csa_lse; a.hca_out = (uint8_t*)hca_out; a.hca_lse = hca_lse;
-  a.C = pl.C; a.n_sc = pl.n_sc; a.cs = pl.cs; a.n_cs_sel = pl.n_cs_sel; a.n_cs_win = pl.n_cs_win;
+  a.C = pl.C; a.n_sc = pl.n_sc; a.cs = pl.cs; a.n_cs_sel = pl.n_cs_sel; a.n_cs_win = pl.n_cs_win; a.cg = pl.cg;
   a.hs = pl.hs; a.n_hs = pl.n_hs;
-  a.emit_q = pl.emit_q; a.emit_max = pl.emit_max; a.key_stride = pl.key_stride;
+  a.lst_min = pl.lst_min; a.lst = pl.lst; a.key_stride = pl.key_stride;
   {
-    const int64_t units = (int64_t)R * pl.n_sc + (int64_t)R * (pl.n_cs_sel + pl.n_cs_win + pl.n_hs) +
+    const int64_t units = (int64_t)R * pl.n_sc + R + (int64_t)R * (pl.n_cs_sel + pl.n_cs_win + pl.n_hs) +
                           2 * (int64_t)R * (H / 4);
     a.rounds = (int)((units + pl.grid - 1) / pl.grid);
   }
   a.ctl = (uint32_t*)take(W_CTL * 4);
   a.keys = (uint32_t*)take((size_t)R * pl.key_stride * 4);
   a.ent_hdr = (uint64_t*)take(slots * 8);
-  a.ent = (uint64_t*)take(slots * pl.emit_max * 8);
+  a.ent = (uint64_t*)take(slots * pl.lst * 8);
+  a.lkey = (uint32_t*)take(slots * pl.lst * 4);
+  a.ltau = (uint32_t*)take(slots * 4);
+  a.row_k = (uint64_t*)take((size_t)R * 8);
+  a.row_cut = (uint64_t*)take((size_t)R * 8);
+  a.grp_off = (uint64_t*)take((size_t)R * pl.n_cs_sel * 8);
   a.part_hdr = (uint64_t*)take((size_t)R * (n_cs + pl.n_hs) * 8);
   a.csa_po = (float*)take((size_t)R * n_cs * H * 128 * 4);
   a.csa_pml = (float*)take((size_t)R * n_cs * H * 2 * 4);

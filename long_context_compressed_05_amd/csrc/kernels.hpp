@@ -34,17 +34,19 @@ int launch_attn(bool bf16, bool hca, int n_seq, int64_t n_q, const int64_t* tok_
                 hipStream_t stream);
 
 struct FusedPlan {
-  int grid;                     // co-resident workgroups of the cooperative launch
+  int grid;                     // workgroups of the launch (CUs x workgroups per CU)
   int C, n_sc;                  // score entries per chunk, chunks per row
-  int cs, n_cs_sel, n_cs_win;   // CSA split size, selected and window splits per row
+  int cs, n_cs_sel, n_cs_win;   // window split size; CSA groups and window splits per row
+  int cg;                       // score chunks per CSA group
   int hs, n_hs;                 // HCA split size, splits per row
-  int emit_q, emit_max;         // per score chunk: local bin rank emitted, entry capacity
+  int lst_min, lst;             // per score chunk: entries listed, at least lst_min, at most lst
   int64_t key_stride;
   size_t ws_bytes;
 };
 FusedPlan plan_fused(int64_t R, int64_t max_pool, int64_t max_hpool, int H, int k, int W, int W_hca);
 int fused_supported(int64_t R, int64_t max_pool, int64_t max_hpool, int H, int k, int W, int W_hca);
 size_t fused_error_word_offset();
+size_t fused_fallback_word_offset();
 int launch_fused(int R, const int64_t* tok_off, const int64_t* q_pos, const int64_t* pool_off,
                  const int64_t* hpool_off, int64_t max_pool, int64_t max_hpool, int m, int m_hca, int H,
                  float scale, int k, int W, int W_hca, const uint8_t* q_codes, const uint8_t* q_scales,
