@@ -36,7 +36,7 @@
 
 namespace csa {
 
-constexpr int kFMaxC = 3072;         // score entries per workgroup (keys in LDS)
+constexpr int kFMaxC = 4096;         // score entries per workgroup (keys in LDS)
 constexpr int kFKPT = kFMaxC / 256;  // keys per thread in a chunk
 constexpr int kFHist = 2048;         // radix digit bins (11 bits)
 constexpr int kFEntLds = 6144;       // listed keys of a row staged in LDS
@@ -66,7 +66,7 @@ constexpr int kFusedLds = kSelEnd > kAttnEnd ? kSelEnd : kAttnEnd;
 static_assert(kOffSel + kFMaxSel * 4 <= kOffScr, "a group's selected rows fit the key region");
 static_assert(kOffU % 16 == 0 && kOffHist % 16 == 0, "LDS regions must be 16-byte aligned");
 static_assert(kFEntLds * 8 <= kAttnLdsBytes, "a group's listed entries fit the union region");
-static_assert(kFusedLds <= 80 * 1024, "two workgroups per CU");
+static_assert(kFusedLds <= 160 * 1024, "one workgroup per CU");
 
 // scratch word indices (0..19 are used by the block scans and searches)
 enum { S_TAG = 40, S_FLAG, S_DIGIT, S_ABOVE, S_CNT, S_BAD, S_TICKET, S_KEY, S_CUT };
@@ -104,6 +104,7 @@ struct FusedArgs {
   // workspace
   uint32_t* ctl;
   uint32_t* keys;      // [R][key_stride] sort keys (read only by the exact fallback)
+  uint64_t* key_hdr;   // [R*n_sc] tagged: the chunk's keys are in keys
   uint64_t* ent_hdr;   // [R*n_sc] tagged: listed count | truncated << 16
   uint64_t* ent;       // [R*n_sc][lst] (key << 32) | index, ascending index
   uint32_t* lkey;      // [R*n_sc][lst] the listed keys alone, same order
@@ -351,19 +352,20 @@ __device__ __forceinline__ uint32_t block_exscan_val(uint32_t v, uint32_t* scr, 
 }
 
 // [lo, hi] = the range of the workgroup's valid keys (each thread holds NK in
-// registers, the first nv valid; at least one valid key in the workgroup).
+// registers, key i valid when bit i of vm is set; at least one valid key in
+// the workgroup).
 // Also clears the two 2048-bin histograms at hist (16-byte aligned).
 template <int NK>
-__device__ __forceinline__ void key_range(const uint32_t (&kv)[NK], int nv, uint32_t* hist, uint32_t* scr,
+__device__ __forceinline__ void key_range(const uint32_t (&kv)[NK], uint32_t vm, uint32_t* hist, uint32_t* scr,
                                           uint32_t* lo, uint32_t* hi) {
   const int tid = lane_tid(), lane = tid & 63, wave = tid >> 6;
   uint32_t mn = 0xffffffffu, mx = 0u;
 #pragma unroll
-  for (int i = 0; i < NK; ++i)
-    if (i < nv) {
-      mn = kv[i] < mn ? kv[i] : mn;
-      mx = kv[i] > mx ? kv[i] : mx;
-    }
+  for (int i = 0; i < NK; ++i) {
+    const bool v = (vm >> i) & 1u;
+    mn = v && kv[i] < mn ? kv[i] : mn;
+    mx = v && kv[i] > mx ? kv[i] : mx;
+  }
   wave_minmax(mn, mx);
   if (lane == 0) {
     scr[8 + wave] = mn;
@@ -387,7 +389,7 @@ __device__ __forceinline__ void key_range(const uint32_t (&kv)[NK], int nv, uint
 // take the counts of keys outside the range (one per lane: the count loop
 // has no branches and no colliding atomics on them).
 template <int NK>
-__device__ __forceinline__ void radix_pass(const uint32_t (&kv)[NK], int nv, uint32_t need, uint32_t* hist,
+__device__ __forceinline__ void radix_pass(const uint32_t (&kv)[NK], uint32_t vm, uint32_t need, uint32_t* hist,
                                            uint32_t* trash, uint32_t* scr, uint32_t lo, uint32_t hi, uint32_t* blo,
                                            uint32_t* bhi, uint32_t* above, uint32_t* cnt) {
   const int tid = lane_tid(), lane = tid & 63, wave = tid >> 6;
@@ -396,7 +398,7 @@ __device__ __forceinline__ void radix_pass(const uint32_t (&kv)[NK], int nv, uin
   const int shift = nbits > 11 ? nbits - 11 : 0;
 #pragma unroll
   for (int i = 0; i < NK; ++i) {
-    const bool in = i < nv && kv[i] >= lo && kv[i] <= hi;
+    const bool in = ((vm >> i) & 1u) && kv[i] >= lo && kv[i] <= hi;
     atomicAdd(in ? hist + ((kv[i] - lo) >> shift) : trash + lane, 1u);
   }
   __syncthreads();
@@ -452,22 +454,22 @@ __device__ __forceinline__ void radix_pass(const uint32_t (&kv)[NK], int nv, uin
 }
 
 // The need-th largest key (1 <= need <= number of valid keys) among the
-// workgroup's keys, each thread holding NK of them in registers (the first nv
-// valid): radix select over the keys' own range, each pass narrowing it to one
+// workgroup's keys, each thread holding NK of them in registers (key i valid
+// when bit i of vm is set): radix select over the keys' own range, each pass narrowing it to one
 // of at most 2048 bins (so keys spread over the bins whatever their
 // magnitude), at most 3 passes.  Returns the key; *gt = the keys above it.
 // A pass that leaves one key in the range ends the search.  hist: 2 x 2048 +
 // 64 words of LDS, 16-byte aligned.
 template <int NK>
-__device__ __forceinline__ uint32_t kth_key(const uint32_t (&kv)[NK], int nv, uint32_t need, uint32_t* hist,
+__device__ __forceinline__ uint32_t kth_key(const uint32_t (&kv)[NK], uint32_t vm, uint32_t need, uint32_t* hist,
                                             uint32_t* scr, uint32_t* gt) {
   uint32_t lo, hi;
-  key_range<NK>(kv, nv, hist, scr, &lo, &hi);
+  key_range<NK>(kv, vm, hist, scr, &lo, &hi);
   uint32_t above_all = 0;
 #pragma unroll 1
   for (int pass = 0; pass < 3 && lo != hi; ++pass) {
     uint32_t blo, bhi, above, cnt;
-    radix_pass<NK>(kv, nv, need, hist + (pass & 1) * kFHist, hist + 2 * kFHist, scr, lo, hi, &blo, &bhi, &above,
+    radix_pass<NK>(kv, vm, need, hist + (pass & 1) * kFHist, hist + 2 * kFHist, scr, lo, hi, &blo, &bhi, &above,
                    &cnt);
     need -= above;
     above_all += above;
@@ -476,7 +478,7 @@ __device__ __forceinline__ uint32_t kth_key(const uint32_t (&kv)[NK], int nv, ui
     if (cnt == 1u && lo != hi) {  // the one key in [lo, hi]
 #pragma unroll
       for (int i = 0; i < NK; ++i)
-        if (i < nv && kv[i] >= lo && kv[i] <= hi) scr[S_KEY] = kv[i];
+        if (((vm >> i) & 1u) && kv[i] >= lo && kv[i] <= hi) scr[S_KEY] = kv[i];
       __syncthreads();
       lo = hi = uni(scr[S_KEY]);
       __syncthreads();
@@ -542,19 +544,6 @@ __device__ __forceinline__ void phase_score(const FCtx& x, int r, int c, const F
     }
   }
   __syncthreads();
-  // keys -> workspace (read only by the exact fallback), 16 bytes per store
-  {
-    uint32_t* gk = a.keys + (size_t)r * a.key_stride + j0;
-    for (int i = 4 * tid; i < n; i += 1024) {
-      if (i + 3 < n) {
-        const v4u_t u = {keys_s[i], keys_s[i + 1], keys_s[i + 2], keys_s[i + 3]};
-        coh_st128(x.coh, gk + i, u);
-      } else {
-        for (int e = i; e < n; ++e)
-          __builtin_amdgcn_raw_buffer_store_b32(keys_s[e], x.coh.r, coh_off(x.coh, gk + e), 0, kSc1);
-      }
-    }
-  }
   // thread t owns the local entries [t*M, t*M + M)
   const int M = (n + 255) >> 8;
   const int e0 = tid * M;
@@ -571,10 +560,11 @@ __device__ __forceinline__ void phase_score(const FCtx& x, int r, int c, const F
   uint32_t tau = 0;
   if (trunc) {
     uint32_t lo, hi;
-    key_range<kFKPT>(kv, nv, hist, x.scr, &lo, &hi);
+    const uint32_t vm = (1u << nv) - 1u;
+    key_range<kFKPT>(kv, vm, hist, x.scr, &lo, &hi);
     if (lo != hi) {
       uint32_t blo, bhi, above, cnt;
-      radix_pass<kFKPT>(kv, nv, (uint32_t)a.lst_min, hist, hist + 2 * kFHist, x.scr, lo, hi, &blo, &bhi, &above, &cnt);
+      radix_pass<kFKPT>(kv, vm, (uint32_t)a.lst_min, hist, hist + 2 * kFHist, x.scr, lo, hi, &blo, &bhi, &above, &cnt);
       tau = above + cnt <= L ? blo : bhi + 1u;
     } else {
       tau = lo + 1u;  // n > L equal keys: list none (the row then takes the exact fallback)
@@ -602,6 +592,23 @@ __device__ __forceinline__ void phase_score(const FCtx& x, int r, int c, const F
   vm_drain();
   __syncthreads();
   if (tid == 0) st_dev64(a.ent_hdr + slot, tagged(x.tag, n_list | ((n_list < (uint32_t)n ? 1u : 0u) << 16)));
+  // then all the keys -> workspace, read only by the exact fallback: stored after the
+  // list is published (their drain would hold the list back), with a header of their own
+  {
+    uint32_t* gk = a.keys + (size_t)r * a.key_stride + j0;
+    for (int i = 4 * tid; i < n; i += 1024) {
+      if (i + 3 < n) {
+        const v4u_t u = {keys_s[i], keys_s[i + 1], keys_s[i + 2], keys_s[i + 3]};
+        coh_st128(x.coh, gk + i, u);
+      } else {
+        for (int e = i; e < n; ++e)
+          __builtin_amdgcn_raw_buffer_store_b32(keys_s[e], x.coh.r, coh_off(x.coh, gk + e), 0, kSc1);
+      }
+    }
+  }
+  vm_drain();
+  __syncthreads();
+  if (tid == 0) st_dev64(a.key_hdr + slot, tagged(x.tag, 1u));
 }
 
 // ---------------------------------------------------------------------------
@@ -642,50 +649,32 @@ __device__ __forceinline__ void write_partial(const FCtx& x, AttnState<1>& st, i
     st_dev64(a.part_hdr + (size_t)r * (n_cs + a.n_hs) + (hca ? n_cs : 0) + pi, tagged(x.tag, 1u));
 }
 
-// Per-chunk arrays of a row in LDS (key region): list offsets (exclusive
-// prefix of the listed counts, total at [n_sc]), headers, thresholds.
-__device__ __forceinline__ uint32_t* row_off(const FCtx& x) { return reinterpret_cast<uint32_t*>(x.smem + kOffKeys); }
-__device__ __forceinline__ uint32_t* row_hdrs(const FCtx& x) { return row_off(x) + (kFMaxSlots + 8); }
-__device__ __forceinline__ uint32_t* row_taus(const FCtx& x) { return row_off(x) + 2 * (kFMaxSlots + 8); }
-
-// Wait for the list headers of every score chunk of row r -> LDS (counts,
-// offsets).  false on a failed wait.
-__device__ __forceinline__ bool row_lists(const FCtx& x, int r) {
-  KArgs& a = *x.a;
-  const int tid = lane_tid(), nsc = a.n_sc;
-  uint32_t* e_off = row_off(x);
-  uint32_t* e_n = row_hdrs(x);
-  bool fail = false;
-  for (int sl = tid; sl < nsc && !fail; sl += 256) {
-    const uint32_t v = poll_word(x, a.ent_hdr + (size_t)r * nsc + sl, &fail, 2u);
-    e_n[sl] = v;
-    e_off[sl] = v & 0xffffu;
-  }
-  if (!all_ok(x, fail)) return false;
-  block_exscan(e_off, nsc, x.scr);
-  return true;
-}
+// Per-chunk arrays of a row in LDS (key region): list headers (count |
+// truncated << 16) and thresholds.  A listed entry's position is its list
+// slot: chunk * lst + rank in the chunk's list, so positions ascend with the
+// index.
+__device__ __forceinline__ uint32_t* row_hdrs(const FCtx& x) { return reinterpret_cast<uint32_t*>(x.smem + kOffKeys); }
+__device__ __forceinline__ uint32_t* row_taus(const FCtx& x) { return row_hdrs(x) + (kFMaxSlots + 8); }
 
 // Selection threshold of row r, one workgroup.  The row takes the k_eff first
 // entries in (key descending, index ascending) order.  Each score chunk listed
 // every entry whose key is at least its threshold tau (all of its entries when
 // it has at most lst).  K* = the k_eff-th largest listed key; the row takes
 // every listed entry above K* and the r_eq = k_eff - (listed keys above K*)
-// listed entries equal to K* of lowest index.  Chunks cover ascending index
-// ranges and list in index order, so the lists concatenated in chunk order
-// are in index order, and the taken ties are the first r_eq equal keys of that
-// concatenation: those at or before position `cut`.  This is the exact
-// selection when every truncated chunk has tau <= K* (it then listed all of
-// its entries >= K*, ties included).  Otherwise an exact radix select over the
-// row's stored keys gives the order key (K*, j*) of the k_eff-th entry.
-// Published: row_k = K*, row_cut = cut (or 1 << 31 | j*), then each CSA
-// group's output offset; idx positions [k_eff, k) are set to -1.  The
-// selected entries themselves are taken and written by the CSA groups.
+// listed entries equal to K* of lowest index: those at or before position
+// `cut`.  This is the exact selection when every truncated chunk has tau <= K*
+// (it then listed all of its entries >= K*, ties included).  Otherwise an
+// exact radix select over the row's stored keys gives the order key (K*, j*)
+// of the k_eff-th entry.  Published: row_k = K*, row_cut = cut (or 1 << 31 |
+// j*), then each CSA group's output offset; idx positions [k_eff, k) are set
+// to -1.  The selected entries themselves are taken and written by the CSA
+// groups.  Each chunk's listed keys are loaded as soon as its header is seen,
+// while later chunks are still being scored.
 __device__ __forceinline__ bool select_row(const FCtx& x, int r, const FRow& f) {
   KArgs& a = *x.a;
   const int tid = lane_tid();
   const int k_eff = (int)(f.n_vis < a.k ? f.n_vis : a.k);
-  const int nsc = a.n_sc, ngrp = a.n_cs_sel, cgs = a.cg;
+  const int nsc = a.n_sc, ngrp = a.n_cs_sel, cgs = a.cg, L = a.lst;
   int32_t* idx_out = a.idx + (size_t)r * a.k;
   for (int i = k_eff + tid; i < a.k; i += 256) idx_out[i] = -1;
   uint64_t* gout = a.grp_off + (size_t)r * ngrp;
@@ -697,70 +686,81 @@ __device__ __forceinline__ bool select_row(const FCtx& x, int r, const FRow& f) 
     for (int g = tid; g < ngrp; g += 256) st_dev64(gout + g, tagged(x.tag, 0u));
     return true;
   }
-  if (!row_lists(x, r)) return false;
-  uint32_t* e_off = row_off(x);
   uint32_t* e_n = row_hdrs(x);
   uint32_t* e_tau = row_taus(x);
   uint32_t* lk_s = reinterpret_cast<uint32_t*>(x.smem + kOffLst);
   uint32_t* hist = reinterpret_cast<uint32_t*>(x.smem + kOffHist);
-  const uint32_t n_ent = uni(e_off[nsc]);
-  bool exact = n_ent <= (uint32_t)kFEntLds && n_ent >= (uint32_t)k_eff;
-  if (tid == 0) x.scr[S_BAD] = exact ? 0u : 1u;
-  if (exact) {
-    // thresholds, and the listed keys -> LDS in chunk order (16-byte loads, 8 per thread in flight)
-    for (int sl = tid; sl < nsc; sl += 256) e_tau[sl] = coh_ld32(x.coh, a.ltau + (size_t)r * nsc + sl);
-    const uint32_t* rowk = a.lkey + (size_t)r * nsc * a.lst;
-    const int L4 = a.lst >> 2;
-    const int nq = nsc * L4;
-    for (int q0 = 0; q0 < nq; q0 += 256 * 8) {
-      v4u_t v[8];
+  const uint32_t* rowk = a.lkey + (size_t)r * nsc * L;
+  // per chunk: wait for its header, then load its threshold and listed keys (16 bytes per load)
+  bool fail = false;
+  uint32_t listed = 0;
+  for (int sl = tid; sl < nsc && !fail; sl += 256) {
+    const uint32_t v = poll_word(x, a.ent_hdr + (size_t)r * nsc + sl, &fail, 2u);
+    const uint32_t cnt = v & 0xffffu;
+    e_n[sl] = v;
+    listed += cnt;
+    e_tau[sl] = coh_ld32(x.coh, a.ltau + (size_t)r * nsc + sl);
+    for (uint32_t i0 = 0; i0 < cnt; i0 += 64) {  // 16 loads in flight
+      v4u_t q[16];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int q = q0 + tid + 256 * u;
-        const int sl = q / L4, i = 4 * (q - sl * L4);
-        const bool use = q < nq && (uint32_t)i < (e_n[q < nq ? sl : 0] & 0xffffu);
-        v[u] = use ? coh_ld128(x.coh, rowk + (size_t)sl * a.lst + i) : v4u_t{0u, 0u, 0u, 0u};
-      }
+      for (int u = 0; u < 16; ++u)
+        q[u] = i0 + 4u * u < cnt ? coh_ld128(x.coh, rowk + (size_t)sl * L + i0 + 4u * u) : v4u_t{0u, 0u, 0u, 0u};
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int q = q0 + tid + 256 * u;
-        if (q >= nq) continue;
-        const int sl = q / L4, i = 4 * (q - sl * L4);
-        const uint32_t cnt = e_n[sl] & 0xffffu;
+      for (int u = 0; u < 16; ++u)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          if ((uint32_t)(i + e) < cnt) lk_s[e_off[sl] + i + e] = v[u][e];
+          if (i0 + 4u * u + e < cnt) lk_s[sl * L + i0 + 4u * u + e] = q[u][e];
+    }
+  }
+  if (tid == 0) x.scr[S_BAD] = 0;
+  if (!all_ok(x, fail)) return false;
+  uint32_t n_ent;
+  (void)block_exscan_val(listed, x.scr, &n_ent);
+  bool exact = n_ent >= (uint32_t)k_eff;
+  if (exact) {
+    // K* over the listed keys, thread t holding slot positions [t*M, t*M + M)
+    const int npos = nsc * L;
+    const int M = (npos + 255) >> 8;
+    const int m0 = tid * M;
+    uint32_t kv[kFEPT];
+    uint32_t vm = 0;
+    {
+      int sl = m0 / L, i = m0 - sl * L;
+      uint32_t cnt = sl < nsc ? (e_n[sl] & 0xffffu) : 0u;
+#pragma unroll
+      for (int e = 0; e < kFEPT; ++e) {
+        const bool v = e < M && m0 + e < npos && (uint32_t)i < cnt;
+        kv[e] = v ? lk_s[m0 + e] : 0u;
+        vm |= v ? (1u << e) : 0u;
+        if (++i == L) {
+          i = 0;
+          ++sl;
+          cnt = sl < nsc ? (e_n[sl] & 0xffffu) : 0u;
+        }
       }
     }
-    __syncthreads();
-    // K* over the listed keys, thread t holding positions [t*M, t*M + M)
-    const int M = (int)((n_ent + 255) >> 8);
-    const int m0 = tid * M;
-    const int nv = (int)n_ent - m0 < 0 ? 0 : ((int)n_ent - m0 < M ? (int)n_ent - m0 : M);
-    uint32_t kv[kFEPT];
-#pragma unroll
-    for (int i = 0; i < kFEPT; ++i) kv[i] = i < nv ? lk_s[m0 + i] : 0u;
     uint32_t gt_all;
-    const uint32_t kstar = kth_key<kFEPT>(kv, nv, (uint32_t)k_eff, hist, x.scr, &gt_all);
+    const uint32_t kstar = kth_key<kFEPT>(kv, vm, (uint32_t)k_eff, hist, x.scr, &gt_all);
     const uint32_t r_eq = (uint32_t)k_eff - gt_all;  // >= 1
     for (int sl = tid; sl < nsc; sl += 256)
       if ((e_n[sl] >> 16) != 0u && e_tau[sl] > kstar) x.scr[S_BAD] = 1;
     uint32_t cgt = 0, ceq = 0;
 #pragma unroll
-    for (int i = 0; i < kFEPT; ++i) {
-      cgt += (i < nv && kv[i] > kstar) ? 1u : 0u;
-      ceq += (i < nv && kv[i] == kstar) ? 1u : 0u;
+    for (int e = 0; e < kFEPT; ++e) {
+      const bool v = (vm >> e) & 1u;
+      cgt += (v && kv[e] > kstar) ? 1u : 0u;
+      ceq += (v && kv[e] == kstar) ? 1u : 0u;
     }
     uint32_t tot;
     const uint32_t pre = block_exscan_val(cgt | (ceq << 16), x.scr, &tot);
     const uint32_t pre_gt = pre & 0xffffu, pre_eq = pre >> 16;
     if (pre_eq < r_eq && pre_eq + ceq >= r_eq) {  // this thread holds the r_eq-th tie
-      uint32_t e = pre_eq, cut = 0;
+      uint32_t e2 = pre_eq, cut = 0;
 #pragma unroll
-      for (int i = 0; i < kFEPT; ++i)
-        if (i < nv && kv[i] == kstar) {
-          ++e;
-          if (e == r_eq) cut = (uint32_t)(m0 + i);
+      for (int e = 0; e < kFEPT; ++e)
+        if (((vm >> e) & 1u) && kv[e] == kstar) {
+          ++e2;
+          if (e2 == r_eq) cut = (uint32_t)(m0 + e);
         }
       x.scr[S_CUT] = cut;
     }
@@ -772,19 +772,17 @@ __device__ __forceinline__ bool select_row(const FCtx& x, int r, const FRow& f) 
         st_dev64(a.row_k + r, tagged(x.tag, kstar));
         st_dev64(a.row_cut + r, tagged(x.tag, cut));
       }
-      // group g starts at listed position P = e_off[g * cg]: its output offset is the
-      // count of taken entries before P
+      // group g starts at position P = g * cg * lst: its output offset is the count of
+      // taken entries before P
       for (int g = 0; g < ngrp; ++g) {
-        const uint32_t P = e_off[g * cgs < nsc ? g * cgs : nsc];
-        if (P >= n_ent) {
-          if (tid == 0) st_dev64(gout + g, tagged(x.tag, (uint32_t)k_eff));
-        } else if (P >= (uint32_t)m0 && P < (uint32_t)(m0 + M)) {
+        const uint32_t P = (uint32_t)(g * cgs * L);
+        if (P >= (uint32_t)m0 && P < (uint32_t)(m0 + M)) {
           uint32_t gb = pre_gt, eb = pre_eq;
 #pragma unroll
-          for (int i = 0; i < kFEPT; ++i)
-            if ((uint32_t)(m0 + i) < P) {
-              gb += kv[i] > kstar ? 1u : 0u;
-              eb += kv[i] == kstar ? 1u : 0u;
+          for (int e = 0; e < kFEPT; ++e)
+            if ((uint32_t)(m0 + e) < P && ((vm >> e) & 1u)) {
+              gb += kv[e] > kstar ? 1u : 0u;
+              eb += kv[e] == kstar ? 1u : 0u;
             }
           st_dev64(gout + g, tagged(x.tag, gb + (eb < r_eq ? eb : r_eq)));
         }
@@ -795,6 +793,11 @@ __device__ __forceinline__ bool select_row(const FCtx& x, int r, const FRow& f) 
   // exact radix select over the row's stored keys: the k_eff-th largest key K*, then
   // the (need_left)-th smallest index among keys equal to K* (indices < 2^18)
   if (tid == 0) atomicAdd(a.ctl + W_FALLBACK, 1u);
+  {
+    bool kfail = false;
+    for (int sl = tid; sl < nsc && !kfail; sl += 256) (void)poll_word(x, a.key_hdr + (size_t)r * nsc + sl, &kfail, 64u);
+    if (!all_ok(x, kfail)) return false;
+  }
   const uint32_t* rowkeys = a.keys + (size_t)r * a.key_stride;
   uint32_t nl;
   const uint32_t n_vis = n_vis_u32(f);
@@ -829,20 +832,21 @@ __device__ __forceinline__ bool select_row(const FCtx& x, int r, const FRow& f) 
 
 // CSA group g of row r (score chunks [g*cg, g*cg + cg)): its selected entries,
 // in ascending index order -> LDS (returns how many, or -1 on a failed wait).
-// The group's lists are loaded before the row's threshold is published.
+// Its chunks' lists are loaded before the row's threshold is published.
 __device__ __forceinline__ int group_select(const FCtx& x, int r, int g, const FRow& f) {
   KArgs& a = *x.a;
-  const int tid = lane_tid(), nsc = a.n_sc;
+  const int tid = lane_tid(), nsc = a.n_sc, L = a.lst;
   const int c0 = g * a.cg < nsc ? g * a.cg : nsc, c1 = c0 + a.cg < nsc ? c0 + a.cg : nsc;
   int32_t* sel_s = reinterpret_cast<int32_t*>(x.smem + kOffSel);
-  if (!row_lists(x, r)) return -1;
-  uint32_t* e_off = row_off(x);
   uint32_t* e_n = row_hdrs(x);
-  uint64_t* ent_s = reinterpret_cast<uint64_t*>(x.smem + kOffLst);
-  const uint32_t base = e_off[c0], n_loc = e_off[c1] - base;
+  uint64_t* ent_s = reinterpret_cast<uint64_t*>(x.smem + kOffLst);  // [chunk - c0][lst]
+  bool fail = false;
+  for (int sl = c0 + tid; sl < c1 && !fail; sl += 256)
+    e_n[sl - c0] = poll_word(x, a.ent_hdr + (size_t)r * nsc + sl, &fail, 2u) & 0xffffu;
+  if (!all_ok(x, fail)) return -1;
   {  // the group's lists -> LDS (16-byte loads, 8 per thread in flight)
-    const uint64_t* gent = a.ent + ((size_t)r * nsc + c0) * a.lst;
-    const int L2 = a.lst >> 1;
+    const uint64_t* gent = a.ent + ((size_t)r * nsc + c0) * L;
+    const int L2 = L >> 1;
     const int npairs = (c1 - c0) * L2;
     for (int q0 = 0; q0 < npairs; q0 += 256 * 8) {
       v4u_t v[8];
@@ -850,22 +854,21 @@ __device__ __forceinline__ int group_select(const FCtx& x, int r, int g, const F
       for (int u = 0; u < 8; ++u) {
         const int q = q0 + tid + 256 * u;
         const int sl = q / L2, i = 2 * (q - sl * L2);
-        const bool use = q < npairs && (uint32_t)i < (e_n[c0 + (q < npairs ? sl : 0)] & 0xffffu);
-        v[u] = use ? coh_ld128(x.coh, gent + (size_t)sl * a.lst + i) : v4u_t{0u, 0u, 0u, 0u};
+        const bool use = q < npairs && (uint32_t)i < e_n[q < npairs ? sl : 0];
+        v[u] = use ? coh_ld128(x.coh, gent + (size_t)sl * L + i) : v4u_t{0u, 0u, 0u, 0u};
       }
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const int q = q0 + tid + 256 * u;
         if (q >= npairs) continue;
         const int sl = q / L2, i = 2 * (q - sl * L2);
-        const uint32_t cnt = e_n[c0 + sl] & 0xffffu, o = e_off[c0 + sl] - base;
-        if ((uint32_t)i < cnt) ent_s[o + i] = (uint64_t)v[u][0] | ((uint64_t)v[u][1] << 32);
-        if ((uint32_t)i + 1 < cnt) ent_s[o + i + 1] = (uint64_t)v[u][2] | ((uint64_t)v[u][3] << 32);
+        const uint32_t cnt = e_n[sl];
+        if ((uint32_t)i < cnt) ent_s[sl * L + i] = (uint64_t)v[u][0] | ((uint64_t)v[u][1] << 32);
+        if ((uint32_t)i + 1 < cnt) ent_s[sl * L + i + 1] = (uint64_t)v[u][2] | ((uint64_t)v[u][3] << 32);
       }
     }
   }
   // the row's threshold
-  bool fail = false;
   if (tid == 0) {
     x.scr[S_KEY] = poll_word(x, a.row_k + r, &fail, 16u);
     if (!fail) x.scr[S_CUT] = poll_word(x, a.row_cut + r, &fail, 16u);
@@ -874,27 +877,32 @@ __device__ __forceinline__ int group_select(const FCtx& x, int r, int g, const F
   const uint32_t kstar = uni(x.scr[S_KEY]), cut = uni(x.scr[S_CUT]);
   uint32_t tot;
   if ((cut >> 31) == 0u) {
-    // listed entries above K*, and ties at listed positions up to cut
-    const uint32_t M = (n_loc + 255) >> 8, m0 = (uint32_t)tid * M;
+    // listed entries above K*, and ties at positions up to cut
+    const uint32_t npos = (uint32_t)((c1 - c0) * L), base = (uint32_t)(c0 * L);
+    const uint32_t M = (npos + 255) >> 8, m0 = (uint32_t)tid * M;
+    auto take = [&](uint32_t p, uint64_t* e) {
+      if (p >= npos) return false;
+      const uint32_t sl = p / (uint32_t)L;
+      if (p - sl * (uint32_t)L >= e_n[sl]) return false;
+      *e = ent_s[p];
+      const uint32_t key = (uint32_t)(*e >> 32);
+      return key > kstar || (key == kstar && base + p <= cut);
+    };
     uint32_t cnt = 0;
     for (uint32_t i = 0; i < M; ++i) {
-      const uint32_t p = m0 + i;
-      if (p < n_loc) {
-        const uint32_t key = (uint32_t)(ent_s[p] >> 32);
-        cnt += (key > kstar || (key == kstar && base + p <= cut)) ? 1u : 0u;
-      }
+      uint64_t e;
+      cnt += take(m0 + i, &e) ? 1u : 0u;
     }
     uint32_t pos = block_exscan_val(cnt, x.scr, &tot);
     for (uint32_t i = 0; i < M; ++i) {
-      const uint32_t p = m0 + i;
-      if (p < n_loc) {
-        const uint64_t e = ent_s[p];
-        const uint32_t key = (uint32_t)(e >> 32);
-        if (key > kstar || (key == kstar && base + p <= cut)) sel_s[pos++] = (int32_t)(uint32_t)e;
-      }
+      uint64_t e;
+      if (take(m0 + i, &e)) sel_s[pos++] = (int32_t)(uint32_t)e;
     }
   } else {
     // fallback: the order key (key, ~index) of every visible entry of the group's chunks
+    bool kfail = false;
+    for (int sl = c0 + tid; sl < c1 && !kfail; sl += 256) (void)poll_word(x, a.key_hdr + (size_t)r * nsc + sl, &kfail, 64u);
+    if (!all_ok(x, kfail)) return -1;
     const uint64_t cstar = ((uint64_t)kstar << 32) | (uint32_t)~(cut & 0x3ffffu);
     const uint32_t* rowkeys = a.keys + (size_t)r * a.key_stride;
     const uint32_t C = (uint32_t)a.C, nvis = n_vis_u32(f);
@@ -1140,7 +1148,10 @@ static int fused_grid() {
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)k_decode_fused, 256, kFusedLds) != hipSuccess)
     return 0;
   if (per_cu < 1) return 0;
-  g_fused_grid = cus * per_cu;
+  // One workgroup per CU: two score workgroups sharing a CU's memory pipeline
+  // finish far apart (the second one's stores drain late), and the selection
+  // waits for the last chunk of every row.
+  g_fused_grid = cus;
   return g_fused_grid;
 }
 
@@ -1152,7 +1163,7 @@ FusedPlan plan_fused(int64_t R, int64_t max_pool, int64_t max_hpool, int H, int 
   p.grid = G;
   p.cs = 64;
   p.n_cs_win = split_count(W, p.cs);
-  p.hs = 512;
+  p.hs = 256;
   p.n_hs = split_count(max_hpool + W_hca, p.hs);
   if (p.n_hs == 0) p.n_hs = 1;
   // score chunk: the smallest multiple of 256 (>= 1024) that gives every chunk a
@@ -1191,6 +1202,7 @@ FusedPlan plan_fused(int64_t R, int64_t max_pool, int64_t max_hpool, int H, int 
   size_t s = 0;
   s += al(W_CTL * 4);
   s += al((size_t)R * p.key_stride * 4);
+  s += al(slots * 8);
   s += al(slots * 8);
   s += al(slots * p.lst * 8);
   s += al(slots * p.lst * 4);
@@ -1254,6 +1266,7 @@ int launch_fused(int R, const int64_t* tok_off, const int64_t* q_pos, const int6
   a.ctl = (uint32_t*)take(W_CTL * 4);
   a.keys = (uint32_t*)take((size_t)R * pl.key_stride * 4);
   a.ent_hdr = (uint64_t*)take(slots * 8);
+  a.key_hdr = (uint64_t*)take(slots * 8);
   a.ent = (uint64_t*)take(slots * pl.lst * 8);
   a.lkey = (uint32_t*)take(slots * pl.lst * 4);
   a.ltau = (uint32_t*)take(slots * 4);

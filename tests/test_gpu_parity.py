@@ -236,20 +236,64 @@ FUSED_CASES = {
 }
 
 
-@pytest.mark.parametrize("name", list(FUSED_CASES))
+def _concentrate(host, n_top=2600):
+    """Gives the first n_top pooled entries of every sequence one and the same
+    indexer key aligned with that sequence's query (code +-6 with the sign of
+    the w-weighted head sum of q, scale 2^2), so that they are equal and hold
+    the whole top-k: single score chunks then hold more selected entries than
+    their candidate lists can, and the equal keys are ranked by index."""
+    kc, ks = host["kc"].copy(), host["ks"].copy()
+    for b in range(len(host["pool_off"]) - 1):
+        row = int(host["q_off"][b])
+        qv = np.zeros(64)
+        for h in range(4):
+            for c in range(64):
+                byte = int(host["qc"][row, h, c // 2])
+                code = byte & 15 if c % 2 == 0 else byte >> 4
+                qv[c] += (float(host["w"][row, h]) * oracle.e2m1_value(code)
+                          * oracle.e8m0_value(int(host["qs"][row, h, c // 32])))
+        nib = np.where(qv >= 0, 0x7, 0xF).astype(np.uint8)
+        packed = (nib[0::2] | (nib[1::2] << 4)).astype(np.uint8)
+        p0, p1 = int(host["pool_off"][b]), int(host["pool_off"][b + 1])
+        e = min(p0 + n_top, p1)
+        kc[p0:e] = packed
+        ks[p0:e] = 127 + 2
+    host["kc"], host["ks"] = kc, ks
+    return host
+
+
+# name -> (workload, host post-processing or None, whether the exact fallback must be taken)
+FUSED_EXTRA = {
+    "decode_bf16_concentrated": (lambda: small_wl("decode_bf16_concentrated", [40001, 30002], [1, 1], k=1024,
+                                                  seed=17), _concentrate, True),
+}
+
+
+@pytest.mark.parametrize("name", list(FUSED_CASES) + list(FUSED_EXTRA))
 def test_fused_decode_matches_oracle_and_separate_calls(name):
     """The one-launch decode step gives the oracle's top-k bit for bit, outputs
     within tolerance, and the separate calls' top-k; repeated launches on the
-    same workspace are bit-identical."""
-    _lib()
-    wl = FUSED_CASES[name]()
+    same workspace are bit-identical.  The concentrated case drives the
+    selection into its exact fallback and checks that it was taken."""
+    csa = _lib()
+    post, want_fallback = None, False
+    if name in FUSED_EXTRA:
+        make, post, want_fallback = FUSED_EXTRA[name]
+        wl = make()
+    else:
+        wl = FUSED_CASES[name]()
     host = synth.make_inputs(wl)
+    if post is not None:
+        host = post(host)
     layer, (idx_s, co_s, cl_s, ho_s, hl_s) = _run_path(wl, host)
     from long_context_compressed_05_amd.step import to_device
     dq = to_device({k: host[k] for k in ("q", "qc", "qs", "w")})
     outs = [layer.decode_fused(dq["q"], dq["qc"], dq["qs"], dq["w"]) for _ in range(3)]
     layer.check_fused()
     torch.cuda.synchronize()
+    n_fallback = csa.csa_hca_decode_fallbacks(layer.ws_fused)
+    if want_fallback:
+        assert n_fallback == 3 * wl.n_q, f"expected every row of every launch to take the fallback, got {n_fallback}"
     res = [[P.torch_to_np(t) for t in o] for o in outs]
     idx, co, cl, ho, hl = res[0]
     for other in res[1:]:
