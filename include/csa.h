@@ -232,8 +232,10 @@ int csa_hca_decode_fallbacks(const void* ws, void* stream, uint32_t* rows);
  * caller can time one kernel of a multi-kernel call with its own events.
  * start/stop are hipEvent_t handles owned by the caller; pass NULL, NULL to
  * clear.  Kernel ids: CSA_K_IDX_SCORE (indexer scoring), CSA_K_IDX_SELECT,
- * CSA_K_IDX_FINAL (top-k passes), CSA_K_ATTN (attention main kernel, CSA or
- * HCA), CSA_K_ATTN_COMBINE (split merge), CSA_K_COMPRESS, CSA_K_FUSED.
+ * CSA_K_IDX_FINAL (top-k passes of decode batches), CSA_K_ATTN (attention
+ * main kernel, CSA or HCA), CSA_K_ATTN_COMBINE (split merge), CSA_K_COMPRESS,
+ * CSA_K_FUSED, CSA_K_PF_THRESH and CSA_K_PF_SELECT (threshold and selection
+ * kernels of prefill batches; their scoring kernel is CSA_K_IDX_SCORE).
  * Errors: CSA_ERR_INVALID for an unknown id or exactly one NULL event.
  * ---------------------------------------------------------------------- */
 enum {
@@ -244,7 +246,9 @@ enum {
   CSA_K_ATTN_COMBINE = 4,
   CSA_K_COMPRESS = 5,
   CSA_K_FUSED = 6,
-  CSA_K_COUNT = 7
+  CSA_K_PF_THRESH = 7,
+  CSA_K_PF_SELECT = 8,
+  CSA_K_COUNT = 9
 };
 int csa_profile_events(int kernel_id, void* start, void* stop);
 

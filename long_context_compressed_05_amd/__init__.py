@@ -26,7 +26,7 @@ EXPORTS = ("csa_status_string", "csa_last_error", "csa_compress", "csa_index_top
            "hca_attn", "csa_hca_decode_workspace", "csa_hca_decode", "csa_hca_decode_check",
            "csa_hca_decode_fallbacks", "csa_profile_events")
 (CSA_K_IDX_SCORE, CSA_K_IDX_SELECT, CSA_K_IDX_FINAL, CSA_K_ATTN, CSA_K_ATTN_COMBINE, CSA_K_COMPRESS,
- CSA_K_FUSED) = range(7)
+ CSA_K_FUSED, CSA_K_PF_THRESH, CSA_K_PF_SELECT) = range(9)
 
 
 class CsaBatch(ctypes.Structure):

@@ -224,7 +224,7 @@ int csa_index_topk_workspace(const csa_batch* b, int64_t max_pool, int k, size_t
   if (!bytes) return fail(CSA_ERR_INVALID, "bytes is NULL");
   if (max_pool < 0) return fail(CSA_ERR_INVALID, "max_pool must be >= 0");
   if (k < 1 || k > 4096) return fail(CSA_ERR_INVALID, "k must be in [1, 4096] (got %d)", k);
-  *bytes = csa::index_ws_bytes(b->n_q, max_pool, k);
+  *bytes = csa::index_ws_bytes(b->n_q, b->max_q_per_seq, max_pool, k);
   return CSA_OK;
 }
 
@@ -243,7 +243,7 @@ int csa_index_topk(const csa_batch* b, const int64_t* pool_off, int64_t max_pool
     return fail(CSA_ERR_INVALID, "NULL pointer argument");
   if (!aligned16(q_codes) || !aligned16(k_codes))
     return fail(CSA_ERR_INVALID, "q_codes and k_codes must be 16-byte aligned");
-  const size_t need = csa::index_ws_bytes(b->n_q, max_pool, k);
+  const size_t need = csa::index_ws_bytes(b->n_q, b->max_q_per_seq, max_pool, k);
   if (!ws || ws_bytes < need)
     return fail(CSA_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need, ws_bytes);
   rc = check_device();

@@ -306,38 +306,6 @@ __device__ __forceinline__ bool all_ok(const FCtx& x, bool fail) {
   return ok;
 }
 
-// Wave-wide inclusive scans on DPP lane moves (row shifts within 16-lane rows,
-// then the row broadcasts of lanes 15 and 31): a few VALU operations instead
-// of LDS permutes.  Lanes whose source is outside the row take the identity.
-template <int CTRL, int ROWS = 0xf>
-__device__ __forceinline__ uint32_t dpp_mov(uint32_t identity, uint32_t x) {
-  return (uint32_t)__builtin_amdgcn_update_dpp((int)identity, (int)x, CTRL, ROWS, 0xf, false);
-}
-__device__ __forceinline__ uint32_t wave_incl_add(uint32_t x) {
-  x += dpp_mov<0x111>(0u, x);        // row_shr:1
-  x += dpp_mov<0x112>(0u, x);        // row_shr:2
-  x += dpp_mov<0x114>(0u, x);        // row_shr:4
-  x += dpp_mov<0x118>(0u, x);        // row_shr:8
-  x += dpp_mov<0x142, 0xa>(0u, x);   // row_bcast:15 -> rows 1, 3
-  x += dpp_mov<0x143, 0xc>(0u, x);   // row_bcast:31 -> rows 2, 3
-  return x;
-}
-// wave-wide min and max of x, on every lane
-__device__ __forceinline__ void wave_minmax(uint32_t& mn, uint32_t& mx) {
-#define CSA_MM_STEP(CTRL, ROWS)                                    \
-  {                                                                \
-    const uint32_t a_ = dpp_mov<CTRL, ROWS>(0xffffffffu, mn);      \
-    const uint32_t b_ = dpp_mov<CTRL, ROWS>(0u, mx);               \
-    mn = a_ < mn ? a_ : mn;                                        \
-    mx = b_ > mx ? b_ : mx;                                        \
-  }
-  CSA_MM_STEP(0x111, 0xf) CSA_MM_STEP(0x112, 0xf) CSA_MM_STEP(0x114, 0xf) CSA_MM_STEP(0x118, 0xf)
-  CSA_MM_STEP(0x142, 0xa) CSA_MM_STEP(0x143, 0xc)
-#undef CSA_MM_STEP
-  mn = (uint32_t)__builtin_amdgcn_readlane((int)mn, 63);
-  mx = (uint32_t)__builtin_amdgcn_readlane((int)mx, 63);
-}
-
 // exclusive prefix of v over the workgroup (thread order); *total = the sum
 __device__ __forceinline__ uint32_t block_exscan_val(uint32_t v, uint32_t* scr, uint32_t* total) {
   const int tid = lane_tid(), lane = tid & 63, wave = tid >> 6;

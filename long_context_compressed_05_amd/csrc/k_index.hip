@@ -16,7 +16,9 @@
 // the fp32 accumulation is exact and the score bit pattern is an exact sort
 // key (ReLU is an integer max on the bit pattern, which also maps -0 to +0).
 //
-// Selection is a radix select on those 32-bit keys:
+// This is the path for decode batches (few queries per sequence); batches with
+// many queries per sequence take the prefill path (k_prefill.hip), which keeps
+// no score matrix.  Selection is a radix select on those 32-bit keys:
 //   1. k_idx_score: keys to the workspace + a 4096-bin histogram of the top
 //      13 key bits per query (LDS, merged into one of `nrep` global replicas
 //      picked by workgroup id, i.e. per XCD, to spread the atomics); the last
@@ -361,7 +363,8 @@ static int hist_replicas(int64_t n_q, int64_t max_pool) {
   return (chunks >= 32 && n_q <= 256) ? 8 : 1;
 }
 
-size_t index_ws_bytes(int64_t n_q, int64_t max_pool, int k) {
+size_t index_ws_bytes(int64_t n_q, int64_t max_q_per_seq, int64_t max_pool, int k) {
+  if (prefill_path(max_q_per_seq)) return prefill_ws_bytes(n_q, max_pool);
   const int nrep = hist_replicas(n_q, max_pool);
   size_t s = 0;
   auto add = [&](size_t bytes) { s += (bytes + 255) & ~(size_t)255; };
@@ -379,6 +382,9 @@ int launch_index_topk(int n_seq, int64_t n_q, int64_t max_q_per_seq, const int64
                       int k, const uint8_t* q_codes, const uint8_t* q_scales, const float* w,
                       const uint8_t* k_codes, const uint8_t* k_scales, int32_t* idx, void* ws,
                       hipStream_t stream) {
+  if (prefill_path(max_q_per_seq))
+    return launch_prefill_topk(n_seq, n_q, max_q_per_seq, q_off, q_pos, pool_off, max_pool, m, k, q_codes, q_scales,
+                               w, k_codes, k_scales, idx, ws, stream);
   const int nrep = hist_replicas(n_q, max_pool);
   uint8_t* p = (uint8_t*)ws;
   auto take = [&](size_t bytes) { uint8_t* r = p; p += (bytes + 255) & ~(size_t)255; return r; };

@@ -1,0 +1,548 @@
+// Lightning-indexer top-k for prefill batches (many queries per sequence),
+// without materialising the score matrix.
+//
+// Pages: jyp-garden EP 95 notes, IDEAS (the Lightning Indexer keeps only the
+// top-k compressed blocks); sigco.tistory.com CSA/HCA section (the indexer
+// picks the blocks most relevant to each query); pytorch.kr FP4 QAT section
+// (the indexer QK path is MXFP4).  Same score and order as the decode path:
+//     S(i, j) = sum_h w[i][h] * max(0, qhat[i][h] . khat[j]),
+// the k largest under (S descending, j ascending), indices in ascending order.
+//
+// Three kernels:
+//  1. k_pf_thresh: per block of 16 queries of one sequence, the scores of a
+//     strided sample of the visible keys (every stride-th) -> LDS; per query
+//     (one wave) the need_s-th largest sample score tau, need_s = ceil(2 k /
+//     stride), so that about 2 k keys are >= tau; tau = 0 when the query sees
+//     at most k keys or too few samples.
+//  2. k_pf_score: every visible score exactly once on the block-scaled FP4
+//     MFMA (8 queries x 4 heads x 32 keys per MFMA, two MFMAs per key tile),
+//     compared with its query's tau: the output is a candidate bitmap, one bit
+//     per (query, visible key).  This is the scoring pass; no score is stored.
+//  3. k_pf_select: one wave per query: the candidates from its bitmap (in
+//     ascending index order), their scores again (MFMA on the gathered keys),
+//     K* = the k_eff-th largest by a radix select in the wave's LDS, then the
+//     selected indices, in order.  Exact whenever at least k_eff keys are >=
+//     tau (then K* >= tau and every key >= K* is a candidate); otherwise, or
+//     when the candidates overflow the wave's LDS, the wave runs an exact
+//     radix select over all of the query's visible keys, scored again on each
+//     pass (slow, and only for such queries).  It also returns the query's
+//     threshold and bitmap words to zero, so the workspace is left zero-filled.
+//
+// MFMA operands: A rows (lane & 31) = query slot (lane & 31) >> 2 and head
+// lane & 3, K half lane >> 5; the power-of-two head weight is folded into the
+// query's block scale.  B: key lane & 31, K half lane >> 5.  Output register
+// 4s + h of lane l holds query slot 2s + (l >> 5), head h, key l & 31.  Every
+// product and partial sum is a small dyadic rational, so the fp32 sums are
+// exact and the score bit pattern (ReLU as an integer max, which also maps -0
+// to +0) is an exact sort key.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace csa {
+
+constexpr int kPfRows = 16;        // queries per score block (two MFMA A operands)
+constexpr int kPfKeysWG = 2048;    // keys per scoring workgroup
+constexpr int kPfSampleMax = 2048;  // sample keys per query
+constexpr int kPfCand = 2048;      // candidates per query held in a wave's LDS
+constexpr int kPfBins = 1024;      // wave radix-select bins
+constexpr int kPfWaveHist = kPfBins + 64;  // + one trash word per lane
+constexpr int kPfMinQ = 16;        // queries per sequence from which this path is used
+
+struct PfArgs {
+  const int64_t* q_off;
+  const int64_t* q_pos;
+  const int64_t* pool_off;
+  int n_seq, bps, m, k, stride, ns_max, bw;
+  int64_t n_q, max_pool;
+  const uint8_t* q_codes;
+  const uint8_t* q_scales;
+  const float* w;
+  const uint8_t* k_codes;
+  const uint8_t* k_scales;
+  uint32_t* tau;     // [n_q]
+  uint32_t* bitmap;  // [n_q][bw]
+  int32_t* idx;      // [n_q][k]
+};
+
+__device__ __forceinline__ int64_t pf_nvis(int64_t t, int m, int64_t P) {
+  const int64_t v = (t + 1) / m;
+  return v < P ? v : P;
+}
+
+// A operand: query slots [0, nslots) are rows row0 + slot, the others zero
+__device__ __forceinline__ void pf_load_a(const PfArgs& a, int64_t row0, int nslots, int lane, v8i& av, int& asc) {
+  const int slot = (lane & 31) >> 2, head = lane & 3, kb = lane >> 5;
+  av = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+  asc = 127;
+  if (slot < nslots) {
+    const int64_t qrow = (row0 + slot) * 4 + head;
+    const uint4 u = *reinterpret_cast<const uint4*>(a.q_codes + qrow * 32 + kb * 16);
+    av[0] = (int)u.x; av[1] = (int)u.y; av[2] = (int)u.z; av[3] = (int)u.w;
+    const int we = (int)((__float_as_uint(a.w[qrow]) >> 23) & 255u) - 127;
+    asc = (int)a.q_scales[qrow * 2 + kb] + we;  // w_h = 2^we folded into the block scale
+  }
+}
+
+// B operand of pooled row gj (codes half lane >> 5), or zero
+__device__ __forceinline__ void pf_load_b(const PfArgs& a, int64_t gj, bool ok, int kb, uint4& kc, int& ks) {
+  kc = make_uint4(0u, 0u, 0u, 0u);
+  ks = 127;
+  if (ok) {
+    kc = *reinterpret_cast<const uint4*>(a.k_codes + gj * 32 + kb * 16);
+    ks = a.k_scales[gj * 2 + kb];
+  }
+}
+
+__device__ __forceinline__ v16f pf_mfma(const v8i& av, int asc, const uint4& kc, int ks) {
+  const v8i bv = {(int)kc.x, (int)kc.y, (int)kc.z, (int)kc.w, 0, 0, 0, 0};
+  v16f acc = {};
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc, 4, 4, 0, asc, 0, ks);
+}
+
+// sort key of score index s of this lane (query slot 2s + lane/32)
+__device__ __forceinline__ uint32_t pf_key(const v16f& acc, int s) {
+  const float r0 = __int_as_float(max(__float_as_int(acc[4 * s + 0]), 0));
+  const float r1 = __int_as_float(max(__float_as_int(acc[4 * s + 1]), 0));
+  const float r2 = __int_as_float(max(__float_as_int(acc[4 * s + 2]), 0));
+  const float r3 = __int_as_float(max(__float_as_int(acc[4 * s + 3]), 0));
+  return __float_as_uint((r0 + r1) + (r2 + r3));
+}
+
+// The need-th largest (1 <= need <= valid count) of the wave's keys, lane l
+// holding kv[i] (valid when bit i of vm is set): radix select over the keys'
+// own range in at most 1024 bins per pass, in the wave's LDS (hist: 1024
+// zeroed words, left zeroed, + 64 trash words).  No barriers.  *gt = the keys
+// above the result.
+template <int NK>
+__device__ __forceinline__ uint32_t wave_kth(const uint32_t (&kv)[NK], uint32_t vm, uint32_t need, uint32_t* hist,
+                                             uint32_t* gt) {
+  const int lane = lane_tid() & 63;
+  uint32_t lo = 0xffffffffu, hi = 0u;
+#pragma unroll
+  for (int i = 0; i < NK; ++i) {
+    const bool v = (vm >> i) & 1u;
+    lo = v && kv[i] < lo ? kv[i] : lo;
+    hi = v && kv[i] > hi ? kv[i] : hi;
+  }
+  wave_minmax(lo, hi);
+  uint32_t above_all = 0;
+#pragma unroll 1
+  for (int pass = 0; pass < 4 && lo != hi; ++pass) {
+    const uint32_t span = hi - lo;
+    const int nbits = 32 - __clz((int)span);
+    const int shift = nbits > 10 ? nbits - 10 : 0;
+#pragma unroll
+    for (int i = 0; i < NK; ++i) {
+      const bool in = ((vm >> i) & 1u) && kv[i] >= lo && kv[i] <= hi;
+      atomicAdd(in ? hist + ((kv[i] - lo) >> shift) : hist + kPfBins + lane, 1u);
+    }
+    // lane l owns bins [1024 - 16 (l + 1), 1024 - 16 l): lane 0 the top ones
+    const int base = kPfBins - 16 * (lane + 1);
+    uint32_t c[16], tot = 0;
+#pragma unroll
+    for (int b = 0; b < 16; ++b) {
+      c[b] = hist[base + b];
+      hist[base + b] = 0u;
+      tot += c[b];
+    }
+    const uint32_t incl = wave_incl_add(tot), excl = incl - tot;
+    uint32_t cum = excl, asel = 0, cb = 0;
+    int bsel = -1;
+#pragma unroll
+    for (int b = 15; b >= 0; --b) {
+      if (bsel < 0) {
+        if (cum + c[b] >= need || b == 0) {
+          bsel = b;
+          asel = cum;
+          cb = c[b];
+        } else {
+          cum += c[b];
+        }
+      }
+    }
+    const uint64_t fl = __ballot(excl < need && incl >= need);
+    const int src = (int)__builtin_ctzll(fl);
+    const uint32_t digit = (uint32_t)__builtin_amdgcn_readlane(base + bsel, src);
+    const uint32_t above = (uint32_t)__builtin_amdgcn_readlane((int)asel, src);
+    const uint32_t cnt = (uint32_t)__builtin_amdgcn_readlane((int)cb, src);
+    need -= above;
+    above_all += above;
+    const uint32_t nlo = lo + (digit << shift);
+    const uint32_t width_m1 = (uint32_t)(((uint64_t)1 << shift) - 1u);
+    hi = hi - nlo > width_m1 ? nlo + width_m1 : hi;
+    lo = nlo;
+    if (cnt == 1u && lo != hi) {  // the one key in [lo, hi]
+      uint32_t v = 0u;
+#pragma unroll
+      for (int i = 0; i < NK; ++i) v = (((vm >> i) & 1u) && kv[i] >= lo && kv[i] <= hi) ? kv[i] : v;
+      uint32_t dummy = 0xffffffffu;
+      wave_minmax(dummy, v);
+      lo = hi = v;
+    }
+  }
+  *gt = above_all;
+  return lo;
+}
+
+// ---------------------------------------------------------------------------
+// 1. thresholds from a strided sample
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_pf_thresh(PfArgs a) {
+  extern __shared__ __align__(16) uint32_t pf_sm[];
+  uint32_t* ss = pf_sm;                                          // [kPfRows][ns_max]
+  uint32_t* wh = pf_sm + (size_t)kPfRows * a.ns_max;             // [4][kPfWaveHist]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, kb = lane >> 5;
+  const int b = blockIdx.x / a.bps, t = blockIdx.x % a.bps;
+  const int64_t row0 = a.q_off[b] + (int64_t)t * kPfRows, row_end = a.q_off[b + 1];
+  const int nrows = (int)(row0 >= row_end ? 0 : (row_end - row0 < kPfRows ? row_end - row0 : kPfRows));
+  if (nrows == 0) return;
+  const int64_t pbase = a.pool_off[b], P = a.pool_off[b + 1] - pbase;
+  int64_t nvis_max = 0;
+  for (int q = 0; q < nrows; ++q) {
+    const int64_t v = pf_nvis(a.q_pos[row0 + q], a.m, P);
+    nvis_max = v > nvis_max ? v : nvis_max;
+  }
+  for (int i = tid; i < 4 * kPfWaveHist; i += 256) wh[i] = 0u;
+  v8i a0, a1;
+  int s0, s1;
+  pf_load_a(a, row0, nrows, lane, a0, s0);
+  pf_load_a(a, row0 + 8, nrows - 8, lane, a1, s1);
+  const int64_t st = a.stride;
+  const int ns = (int)((nvis_max + st - 1) / st);  // <= ns_max
+  const int ntiles = (ns + 31) >> 5;
+  for (int tile = wave; tile < ntiles; tile += 4) {
+    const int i = tile * 32 + (lane & 31);
+    const int64_t j = (int64_t)i * st;
+    uint4 kc;
+    int ks;
+    pf_load_b(a, pbase + j, j < nvis_max, kb, kc, ks);
+    const v16f c0 = pf_mfma(a0, s0, kc, ks), c1 = pf_mfma(a1, s1, kc, ks);
+    if (i < ns) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int q0 = 2 * s + (lane >> 5), q1 = 8 + q0;
+        if (q0 < nrows) ss[(size_t)q0 * a.ns_max + i] = pf_key(c0, s);
+        if (q1 < nrows) ss[(size_t)q1 * a.ns_max + i] = pf_key(c1, s);
+      }
+    }
+  }
+  __syncthreads();
+  uint32_t* hist = wh + wave * kPfWaveHist;
+  for (int q = wave; q < nrows; q += 4) {
+    const int64_t row = row0 + q;
+    const int64_t nvis = pf_nvis(a.q_pos[row], a.m, P);
+    const int64_t k_eff = nvis < a.k ? nvis : a.k;
+    const int nsq = (int)((nvis + st - 1) / st);
+    const int64_t need_s = (2 * k_eff + st - 1) / st;
+    uint32_t tau = 0u;
+    if (k_eff < nvis && need_s >= 1 && need_s <= nsq) {
+      uint32_t kv[kPfSampleMax / 64];
+      uint32_t vm = 0;
+#pragma unroll
+      for (int e = 0; e < kPfSampleMax / 64; ++e) {
+        const int c = e * 64 + lane;
+        const bool v = c < nsq;
+        kv[e] = v ? ss[(size_t)q * a.ns_max + c] : 0u;
+        vm |= v ? (1u << e) : 0u;
+      }
+      uint32_t gt;
+      tau = wave_kth<kPfSampleMax / 64>(kv, vm, (uint32_t)need_s, hist, &gt);
+    }
+    if (lane == 0) a.tau[row] = tau;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 2. every visible score once -> candidate bitmap
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_pf_score(PfArgs a) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, kb = lane >> 5;
+  const int b = blockIdx.y / a.bps, t = blockIdx.y % a.bps;
+  const int64_t row0 = a.q_off[b] + (int64_t)t * kPfRows, row_end = a.q_off[b + 1];
+  const int nrows = (int)(row0 >= row_end ? 0 : (row_end - row0 < kPfRows ? row_end - row0 : kPfRows));
+  if (nrows == 0) return;
+  const int64_t pbase = a.pool_off[b], P = a.pool_off[b + 1] - pbase;
+  const int64_t jr0 = (int64_t)blockIdx.x * kPfKeysWG;
+  // this lane's 8 queries: slot 8u + 2s + lane/32 for MFMA u, score index s
+  uint32_t tq[8];
+  int64_t nq[8];
+  int64_t nvis_max = 0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int q = 8 * (e >> 2) + 2 * (e & 3) + (lane >> 5);
+    const bool v = q < nrows;
+    tq[e] = v ? a.tau[row0 + q] : 0xffffffffu;
+    nq[e] = v ? pf_nvis(a.q_pos[row0 + q], a.m, P) : 0;
+    nvis_max = nq[e] > nvis_max ? nq[e] : nvis_max;
+  }
+  nvis_max = (int64_t)__builtin_amdgcn_readfirstlane((int)nvis_max) > (int64_t)__builtin_amdgcn_readlane((int)nvis_max, 32)
+                 ? (int64_t)__builtin_amdgcn_readfirstlane((int)nvis_max)
+                 : (int64_t)__builtin_amdgcn_readlane((int)nvis_max, 32);
+  if (jr0 >= nvis_max) return;
+  v8i a0, a1;
+  int s0, s1;
+  pf_load_a(a, row0, nrows, lane, a0, s0);
+  pf_load_a(a, row0 + 8, nrows - 8, lane, a1, s1);
+  constexpr int kT = kPfKeysWG / 32 / 4;  // tiles per wave
+  uint4 kc[kT];
+  int ks[kT];
+#pragma unroll
+  for (int u = 0; u < kT; ++u) {  // all key loads of the wave first
+    const int64_t j = jr0 + (int64_t)(wave + 4 * u) * 32 + (lane & 31);
+    pf_load_b(a, pbase + j, j < nvis_max, kb, kc[u], ks[u]);
+  }
+  const int wq = lane & 15;  // word lane: query 8 (wq >> 3) + 2 ((wq >> 1) & 3) + (wq & 1)
+  const int qw = 8 * (wq >> 3) + 2 * ((wq >> 1) & 3) + (wq & 1);
+  uint32_t* bm_row = a.bitmap + (size_t)(row0 + (qw < nrows ? qw : 0)) * a.bw;
+#pragma unroll
+  for (int u = 0; u < kT; ++u) {
+    const int64_t jt = jr0 + (int64_t)(wave + 4 * u) * 32;
+    if (jt >= nvis_max) break;
+    const int64_t j = jt + (lane & 31);
+    const v16f c0 = pf_mfma(a0, s0, kc[u], ks[u]), c1 = pf_mfma(a1, s1, kc[u], ks[u]);
+    uint32_t word = 0u;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t key = pf_key(e < 4 ? c0 : c1, e & 3);
+      const uint64_t m = __ballot(j < nq[e] && key >= tq[e]);
+      word = lane == 2 * e ? (uint32_t)m : word;
+      word = lane == 2 * e + 1 ? (uint32_t)(m >> 32) : word;
+    }
+    if (lane < 16 && qw < nrows) bm_row[jt >> 5] = word;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 3. per query: exact top-k among the candidates (or over all keys)
+// ---------------------------------------------------------------------------
+// exact radix select over all visible keys of one query, scored again on
+// every pass, then the selection in ascending index order
+__device__ void pf_select_all(const PfArgs& a, int64_t row, int64_t pbase, int64_t nvis, uint32_t k_eff,
+                              uint32_t* hist, int32_t* idx) {
+  const int lane = lane_tid() & 63, kb = lane >> 5;
+  v8i av;
+  int asc;
+  pf_load_a(a, row, 1, lane, av, asc);
+  const int64_t ntiles = (nvis + 31) >> 5;
+  uint32_t prefix = 0, pmask = 0, need = k_eff;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    for (int64_t tt = 0; tt < ntiles; ++tt) {
+      const int64_t j = tt * 32 + (lane & 31);
+      uint4 kc;
+      int ks;
+      pf_load_b(a, pbase + j, j < nvis, kb, kc, ks);
+      const uint32_t key = pf_key(pf_mfma(av, asc, kc, ks), 0);
+      const bool in = lane < 32 && j < nvis && (key & pmask) == prefix;
+      atomicAdd(in ? hist + ((key >> shift) & 255u) : hist + kPfBins + lane, 1u);
+    }
+    // 256 bins: lane l owns bins [252 - 4 l, 256 - 4 l)
+    const int base = 252 - 4 * lane;
+    uint32_t c[4], tot = 0;
+#pragma unroll
+    for (int bb = 0; bb < 4; ++bb) {
+      c[bb] = hist[base + bb];
+      hist[base + bb] = 0u;
+      tot += c[bb];
+    }
+    const uint32_t incl = wave_incl_add(tot), excl = incl - tot;
+    uint32_t cum = excl, asel = 0;
+    int bsel = -1;
+#pragma unroll
+    for (int bb = 3; bb >= 0; --bb) {
+      if (bsel < 0) {
+        if (cum + c[bb] >= need || bb == 0) {
+          bsel = bb;
+          asel = cum;
+        } else {
+          cum += c[bb];
+        }
+      }
+    }
+    const uint64_t fl = __ballot(excl < need && incl >= need);
+    const int src = (int)__builtin_ctzll(fl);
+    const uint32_t digit = (uint32_t)__builtin_amdgcn_readlane(base + bsel, src);
+    need -= (uint32_t)__builtin_amdgcn_readlane((int)asel, src);
+    prefix |= digit << shift;
+    pmask |= 255u << shift;
+  }
+  // prefix = K*; take every key above it and the first `need` keys equal to it
+  uint32_t n_sel = 0, n_tie = 0;
+  const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+  for (int64_t tt = 0; tt < ntiles; ++tt) {
+    const int64_t j = tt * 32 + (lane & 31);
+    uint4 kc;
+    int ks;
+    pf_load_b(a, pbase + j, j < nvis, kb, kc, ks);
+    const uint32_t key = pf_key(pf_mfma(av, asc, kc, ks), 0);
+    const bool ok = lane < 32 && j < nvis;
+    const bool eq = ok && key == prefix;
+    const uint64_t me = __ballot(eq);
+    const uint32_t tie_rank = n_tie + (uint32_t)__popcll(me & below);
+    const bool sel = ok && (key > prefix || (eq && tie_rank < need));
+    const uint64_t ms = __ballot(sel);
+    if (sel) idx[n_sel + (uint32_t)__popcll(ms & below)] = (int32_t)j;
+    n_sel += (uint32_t)__popcll(ms);
+    n_tie += (uint32_t)__popcll(me);
+  }
+}
+
+__global__ __launch_bounds__(128) void k_pf_select(PfArgs a) {
+  extern __shared__ __align__(16) uint32_t pf_sm[];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, kb = lane >> 5;
+  uint32_t* cand_j = pf_sm + (size_t)wave * (2 * kPfCand + kPfWaveHist);
+  uint32_t* cand_k = cand_j + kPfCand;
+  uint32_t* hist = cand_k + kPfCand;
+  for (int i = lane; i < kPfWaveHist; i += 64) hist[i] = 0u;
+  const int64_t row = (int64_t)blockIdx.x * 2 + wave;
+  if (row >= a.n_q) return;  // wave-level work only: no block barriers below
+  const int b = seq_of_row(a.q_off, a.n_seq, row);
+  const int64_t pbase = a.pool_off[b], P = a.pool_off[b + 1] - pbase;
+  const int64_t nvis = pf_nvis(a.q_pos[row], a.m, P);
+  const uint32_t k_eff = (uint32_t)(nvis < a.k ? nvis : a.k);
+  int32_t* idx = a.idx + row * a.k;
+  for (int i = (int)k_eff + lane; i < a.k; i += 64) idx[i] = -1;
+  if (k_eff == 0) {
+    if (lane == 0) a.tau[row] = 0u;
+    return;
+  }
+  // candidates: the bitmap's set bits, lane l owning words [l * wpl, l * wpl + wpl)
+  const uint32_t* bm = a.bitmap + (size_t)row * a.bw;
+  const int nw = (int)((nvis + 31) >> 5), wpl = (nw + 63) >> 6, w0 = lane * wpl;
+  uint32_t cnt = 0;
+  for (int i = 0; i < wpl; ++i)
+    if (w0 + i < nw) cnt += (uint32_t)__popc(bm[w0 + i]);
+  const uint32_t incl = wave_incl_add(cnt);
+  const uint32_t n_c = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+  // the workspace is left zero-filled: this query's bitmap words and threshold
+  if (lane == 0) a.tau[row] = 0u;
+  uint32_t* bmw = a.bitmap + (size_t)row * a.bw;
+  if (n_c < k_eff || n_c > (uint32_t)kPfCand) {
+    for (int i = 0; i < wpl; ++i)
+      if (w0 + i < nw) bmw[w0 + i] = 0u;
+    pf_select_all(a, row, pbase, nvis, k_eff, hist, idx);
+    return;
+  }
+  uint32_t pos = incl - cnt;
+  for (int i = 0; i < wpl; ++i) {
+    if (w0 + i >= nw) break;
+    uint32_t bits = bm[w0 + i];
+    bmw[w0 + i] = 0u;
+    while (bits) {
+      const int bpos = __ffs(bits) - 1;
+      bits &= bits - 1u;
+      cand_j[pos++] = (uint32_t)((w0 + i) * 32 + bpos);
+    }
+  }
+  // the candidates' scores again: 32 per MFMA (query slot 0), 8 tiles in flight
+  v8i av;
+  int asc;
+  pf_load_a(a, row, 1, lane, av, asc);
+  const int ntile = (int)((n_c + 31) >> 5);
+  for (int t0 = 0; t0 < ntile; t0 += 8) {
+    uint4 kc[8];
+    int ks[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const uint32_t c = (uint32_t)(t0 + u) * 32u + (uint32_t)(lane & 31);
+      const bool ok = c < n_c;
+      pf_load_b(a, pbase + (ok ? (int64_t)cand_j[c] : 0), ok, kb, kc[u], ks[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const uint32_t c = (uint32_t)(t0 + u) * 32u + (uint32_t)(lane & 31);
+      const uint32_t key = pf_key(pf_mfma(av, asc, kc[u], ks[u]), 0);
+      if (lane < 32 && c < n_c) cand_k[c] = key;
+    }
+  }
+  constexpr int NK = kPfCand / 64;
+  uint32_t kv[NK];
+  uint32_t vm = 0;
+#pragma unroll
+  for (int e = 0; e < NK; ++e) {
+    const uint32_t c = (uint32_t)(e * 64 + lane);
+    const bool v = c < n_c;
+    kv[e] = v ? cand_k[c] : 0u;
+    vm |= v ? (1u << e) : 0u;
+  }
+  uint32_t gt;
+  const uint32_t kstar = wave_kth<NK>(kv, vm, k_eff, hist, &gt);
+  const uint32_t r_eq = k_eff - gt;
+  // candidates are in ascending index order: a selected one goes to the count of
+  // selected ones before it
+  uint32_t n_sel = 0, n_tie = 0;
+  const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+#pragma unroll
+  for (int e = 0; e < NK; ++e) {
+    const bool v = (vm >> e) & 1u;
+    const bool eq = v && kv[e] == kstar;
+    const uint64_t me = __ballot(eq);
+    const uint32_t tie_rank = n_tie + (uint32_t)__popcll(me & below);
+    const bool sel = v && (kv[e] > kstar || (eq && tie_rank < r_eq));
+    const uint64_t ms = __ballot(sel);
+    if (sel) idx[n_sel + (uint32_t)__popcll(ms & below)] = (int32_t)cand_j[e * 64 + lane];
+    n_sel += (uint32_t)__popcll(ms);
+    n_tie += (uint32_t)__popcll(me);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+int prefill_path(int64_t max_q_per_seq) { return max_q_per_seq >= kPfMinQ ? 1 : 0; }
+
+static int pf_stride(int64_t max_pool) {
+  int64_t s = (max_pool + kPfSampleMax - 1) / kPfSampleMax;
+  return (int)(s < 16 ? 16 : s);
+}
+
+size_t prefill_ws_bytes(int64_t n_q, int64_t max_pool) {
+  const size_t bw = (size_t)((max_pool + 31) / 32);
+  return (((size_t)n_q * 4 + 255) & ~(size_t)255) + (size_t)n_q * (bw ? bw : 1) * 4;
+}
+
+int launch_prefill_topk(int n_seq, int64_t n_q, int64_t max_q_per_seq, const int64_t* q_off,
+                        const int64_t* q_pos, const int64_t* pool_off, int64_t max_pool, int m, int k,
+                        const uint8_t* q_codes, const uint8_t* q_scales, const float* w,
+                        const uint8_t* k_codes, const uint8_t* k_scales, int32_t* idx, void* ws,
+                        hipStream_t stream) {
+  if (n_q == 0) return 0;
+  PfArgs a{};
+  a.q_off = q_off; a.q_pos = q_pos; a.pool_off = pool_off;
+  a.n_seq = n_seq;
+  a.bps = (int)((max_q_per_seq + kPfRows - 1) / kPfRows);
+  a.m = m; a.k = k;
+  a.stride = pf_stride(max_pool);
+  a.ns_max = (int)((max_pool + a.stride - 1) / a.stride);
+  if (a.ns_max < 1) a.ns_max = 1;
+  a.bw = (int)((max_pool + 31) / 32);
+  a.n_q = n_q; a.max_pool = max_pool;
+  a.q_codes = q_codes; a.q_scales = q_scales; a.w = w; a.k_codes = k_codes; a.k_scales = k_scales;
+  uint8_t* p = (uint8_t*)ws;
+  a.tau = (uint32_t*)p;
+  a.bitmap = (uint32_t*)(p + (((size_t)n_q * 4 + 255) & ~(size_t)255));
+  a.idx = idx;
+  const size_t lds1 = ((size_t)kPfRows * a.ns_max + 4 * kPfWaveHist) * 4;
+  const size_t lds3 = (size_t)2 * (2 * kPfCand + kPfWaveHist) * 4;
+  static bool attr = false;
+  if (!attr) {
+    (void)hipFuncSetAttribute((const void*)k_pf_thresh, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)(((size_t)kPfRows * kPfSampleMax + 4 * kPfWaveHist) * 4));
+    (void)hipFuncSetAttribute((const void*)k_pf_select, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds3);
+    attr = true;
+  }
+  const unsigned nblk = (unsigned)(n_seq * a.bps);
+  prof_begin(7, stream);
+  hipLaunchKernelGGL(k_pf_thresh, dim3(nblk), dim3(256), lds1, stream, a);
+  prof_end(7, stream);
+  dim3 g2((unsigned)((max_pool + kPfKeysWG - 1) / kPfKeysWG), nblk);
+  if (g2.x == 0) g2.x = 1;
+  prof_begin(0, stream);
+  hipLaunchKernelGGL(k_pf_score, g2, dim3(256), 0, stream, a);
+  prof_end(0, stream);
+  prof_begin(8, stream);
+  hipLaunchKernelGGL(k_pf_select, dim3((unsigned)((n_q + 1) / 2)), dim3(128), lds3, stream, a);
+  prof_end(8, stream);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+}  // namespace csa

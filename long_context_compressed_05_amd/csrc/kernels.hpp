@@ -14,7 +14,14 @@ int launch_compress(bool bf16, int n_seq, const int64_t* tok_off, const int64_t*
                     int64_t max_len, int m, int width, const void* x, const void* z, void* out,
                     hipStream_t stream);
 
-size_t index_ws_bytes(int64_t n_q, int64_t max_pool, int k);
+size_t index_ws_bytes(int64_t n_q, int64_t max_q_per_seq, int64_t max_pool, int k);
+int prefill_path(int64_t max_q_per_seq);
+size_t prefill_ws_bytes(int64_t n_q, int64_t max_pool);
+int launch_prefill_topk(int n_seq, int64_t n_q, int64_t max_q_per_seq, const int64_t* q_off,
+                        const int64_t* q_pos, const int64_t* pool_off, int64_t max_pool, int m, int k,
+                        const uint8_t* q_codes, const uint8_t* q_scales, const float* w,
+                        const uint8_t* k_codes, const uint8_t* k_scales, int32_t* idx, void* ws,
+                        hipStream_t stream);
 int launch_index_topk(int n_seq, int64_t n_q, int64_t max_q_per_seq, const int64_t* q_off,
                       const int64_t* q_pos, const int64_t* pool_off, int64_t max_pool, int m,
                       int k, const uint8_t* q_codes, const uint8_t* q_scales, const float* w,

@@ -41,6 +41,8 @@ WORKLOADS = {
                                            dtype="f32", k=1, W=5, m=3, m_hca=16, seed=14),
     "decode_bf16_kbig_whca": lambda: small_wl("decode_bf16_kbig_whca", [200, 900], [1, 4], H=32, k=4000,
                                               W=200, m=4, m_hca=64, W_hca=64, seed=15),
+    "prefill_bf16_ties": lambda: small_wl("prefill_bf16_ties", [5000, 9001], [64, 200], k=128,
+                                          codeset=synth.E2M1_TIE_CODES, seed=18),
 }
 
 
@@ -222,6 +224,47 @@ def test_index_topk_large_ranges(lengths, k, codeset):
     for row in range(wl.n_q):
         want = P.oracle_topk_row(host, wl, row, seqs[row], wl.k, wl.m)
         assert np.array_equal(got[row], want), f"row {row}"
+
+
+def _index_rows(wl, host, rows):
+    csa = _lib()
+    from long_context_compressed_05_amd.step import to_device
+    d = to_device({kk: host[kk] for kk in ("qc", "qs", "w", "kc", "ks", "pool_off")})
+    batch = csa.Batch.from_host(host["tok_off"], host["q_off"], host["q_pos"])
+    max_pool = int(np.diff(host["pool_off"]).max())
+    ws = csa.Workspace()
+    idx = csa.csa_index_topk(batch, d["pool_off"], max_pool, wl.m, wl.k, d["qc"], d["qs"], d["w"], d["kc"],
+                             d["ks"], ws=ws)
+    got = P.torch_to_np(idx)
+    seqs = P.row_seq(host)
+    for row in rows:
+        want = P.oracle_topk_row(host, wl, row, seqs[row], wl.k, wl.m)
+        assert np.array_equal(got[row], want), f"row {row} (seq {seqs[row]}, t={host['q_pos'][row]})"
+    assert int(torch.count_nonzero(ws.buf)) == 0, "the workspace is not left zero-filled"
+    return got
+
+
+def test_prefill_topk_equal_keys():
+    """Every indexer key equal: every visible score of a query ties, the
+    sampled threshold passes all of them, the candidates overflow the per-query
+    buffer and the exact path over all keys runs; the top-k is the first k
+    visible indices."""
+    wl = small_wl("prefill_equal_keys", [12001, 3000], [40, 17], k=256, seed=19)
+    host = synth.make_inputs(wl, raw=False)
+    host["kc"][:] = 0x22
+    host["ks"][:] = 127
+    got = _index_rows(wl, host, range(wl.n_q))
+    assert np.array_equal(got[0], np.arange(wl.k))
+
+
+def test_prefill_topk_full_size_sampled():
+    """The 4096-query chunk on a 65,536-token cache (17,408 pooled keys, top-512)
+    in the launch configuration the benchmark times; 96 sampled rows (first,
+    last and spread) against the oracle, bit for bit."""
+    wl = synth.prefill_4k_on_64k()
+    host = synth.make_inputs(wl, raw=False)
+    rows = sorted(set([0, 1, wl.n_q - 1] + list(np.random.default_rng(7).choice(wl.n_q, 93, replace=False))))
+    _index_rows(wl, host, rows)
 
 
 FUSED_CASES = {
