@@ -9,11 +9,12 @@
 // the k largest under (S descending, j ascending), indices in ascending order.
 //
 // Three kernels:
-//  1. k_pf_thresh: per block of 16 queries of one sequence, the scores of a
+//  1. k_pf_thresh: per block of 8 queries of one sequence, the scores of a
 //     strided sample of the visible keys (every stride-th) -> LDS; per query
-//     (one wave) the need_s-th largest sample score tau, need_s = ceil(2 k /
-//     stride), so that about 2 k keys are >= tau; tau = 0 when the query sees
-//     at most k keys or too few samples.
+//     (one wave, two radix passes over the sample's own range) tau = the lower
+//     edge of the bin holding the need_s-th largest sample score, need_s =
+//     ceil(2 k / stride), so that about 2 k keys are >= tau; tau = 0 when the
+//     query sees at most k keys or too few samples.
 //  2. k_pf_score: every visible score exactly once on the block-scaled FP4
 //     MFMA (8 queries x 4 heads x 32 keys per MFMA, two MFMAs per key tile),
 //     compared with its query's tau: the output is a candidate bitmap, one bit
@@ -40,6 +41,7 @@
 
 namespace csa {
 
+constexpr int kPfRowsT = 8;        // queries per threshold block (one MFMA A operand)
 constexpr int kPfRows = 16;        // queries per score block (two MFMA A operands)
 constexpr int kPfKeysWG = 2048;    // keys per scoring workgroup
 constexpr int kPfSampleMax = 2048;  // sample keys per query
@@ -52,7 +54,7 @@ struct PfArgs {
   const int64_t* q_off;
   const int64_t* q_pos;
   const int64_t* pool_off;
-  int n_seq, bps, m, k, stride, ns_max, bw;
+  int n_seq, bps, bps_t, m, k, stride, ns_max, bw;
   int64_t n_q, max_pool;
   const uint8_t* q_codes;
   const uint8_t* q_scales;
@@ -108,18 +110,56 @@ __device__ __forceinline__ uint32_t pf_key(const v16f& acc, int s) {
   return __float_as_uint((r0 + r1) + (r2 + r3));
 }
 
+// candidate bits of score index E & 3 of MFMA output c (this lane's query
+// E = 4 o + s) -> lanes 2E (the query of lanes 0-31) and 2E + 1 of word;
+// WHOLE: every query sees the tile's 32 keys
+template <int E, bool WHOLE>
+__device__ __forceinline__ void pf_word(uint32_t& word, const v16f& c, int j, const int (&nq)[kPfRows / 2],
+                                        const uint32_t (&tq)[kPfRows / 2]) {
+  const uint32_t key = pf_key(c, E & 3);
+  const uint64_t m = __builtin_amdgcn_ballot_w64(WHOLE ? key >= tq[E] : (j < nq[E] && key >= tq[E]));
+  const int lane = lane_tid() & 63;
+  word = lane == 2 * E ? (uint32_t)m : word;
+  word = lane == 2 * E + 1 ? (uint32_t)(m >> 32) : word;
+}
+
+template <bool WHOLE>
+__device__ __forceinline__ uint32_t pf_tile_word(const v8i (&av)[2], const int (&asc)[2], const uint4& kc, int ks,
+                                                 int j, const int (&nq)[kPfRows / 2],
+                                                 const uint32_t (&tq)[kPfRows / 2]) {
+  uint32_t word = 0u;
+  {
+    const v16f c = pf_mfma(av[0], asc[0], kc, ks);
+    pf_word<0, WHOLE>(word, c, j, nq, tq);
+    pf_word<1, WHOLE>(word, c, j, nq, tq);
+    pf_word<2, WHOLE>(word, c, j, nq, tq);
+    pf_word<3, WHOLE>(word, c, j, nq, tq);
+  }
+  {
+    const v16f c = pf_mfma(av[1], asc[1], kc, ks);
+    pf_word<4, WHOLE>(word, c, j, nq, tq);
+    pf_word<5, WHOLE>(word, c, j, nq, tq);
+    pf_word<6, WHOLE>(word, c, j, nq, tq);
+    pf_word<7, WHOLE>(word, c, j, nq, tq);
+  }
+  return word;
+}
+
 // The need-th largest (1 <= need <= valid count) of the wave's keys, lane l
 // holding kv[i] (valid when bit i of vm is set): radix select over the keys'
 // own range in at most 1024 bins per pass, in the wave's LDS (hist: 1024
-// zeroed words, left zeroed, + 64 trash words).  No barriers.  *gt = the keys
-// above the result.
-template <int NK>
-__device__ __forceinline__ uint32_t wave_kth(const uint32_t (&kv)[NK], uint32_t vm, uint32_t need, uint32_t* hist,
-                                             uint32_t* gt) {
+// zeroed words, left zeroed, + 64 trash words); only slots i < nk (uniform)
+// are looked at.  No barriers.  *gt = the keys above the result.  With
+// MAXPASS < 4 the result is the lower edge of the last bin found, a value
+// with at least `need` keys at or above it.
+template <int NK, int MAXPASS = 4>
+__device__ __forceinline__ uint32_t wave_kth(const uint32_t (&kv)[NK], uint32_t vm, int nk, uint32_t need,
+                                             uint32_t* hist, uint32_t* gt) {
   const int lane = lane_tid() & 63;
   uint32_t lo = 0xffffffffu, hi = 0u;
 #pragma unroll
   for (int i = 0; i < NK; ++i) {
+    if (i >= nk) break;  // uniform: only the slots in use
     const bool v = (vm >> i) & 1u;
     lo = v && kv[i] < lo ? kv[i] : lo;
     hi = v && kv[i] > hi ? kv[i] : hi;
@@ -127,12 +167,13 @@ __device__ __forceinline__ uint32_t wave_kth(const uint32_t (&kv)[NK], uint32_t 
   wave_minmax(lo, hi);
   uint32_t above_all = 0;
 #pragma unroll 1
-  for (int pass = 0; pass < 4 && lo != hi; ++pass) {
+  for (int pass = 0; pass < MAXPASS && lo != hi; ++pass) {
     const uint32_t span = hi - lo;
     const int nbits = 32 - __clz((int)span);
     const int shift = nbits > 10 ? nbits - 10 : 0;
 #pragma unroll
     for (int i = 0; i < NK; ++i) {
+      if (i >= nk) break;
       const bool in = ((vm >> i) & 1u) && kv[i] >= lo && kv[i] <= hi;
       atomicAdd(in ? hist + ((kv[i] - lo) >> shift) : hist + kPfBins + lane, 1u);
     }
@@ -189,12 +230,13 @@ __device__ __forceinline__ uint32_t wave_kth(const uint32_t (&kv)[NK], uint32_t 
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_pf_thresh(PfArgs a) {
   extern __shared__ __align__(16) uint32_t pf_sm[];
-  uint32_t* ss = pf_sm;                                          // [kPfRows][ns_max]
-  uint32_t* wh = pf_sm + (size_t)kPfRows * a.ns_max;             // [4][kPfWaveHist]
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, kb = lane >> 5;
-  const int b = blockIdx.x / a.bps, t = blockIdx.x % a.bps;
-  const int64_t row0 = a.q_off[b] + (int64_t)t * kPfRows, row_end = a.q_off[b + 1];
-  const int nrows = (int)(row0 >= row_end ? 0 : (row_end - row0 < kPfRows ? row_end - row0 : kPfRows));
+  uint32_t* ss = pf_sm;                                          // [kPfRowsT][ns_max]
+  uint32_t* wh = pf_sm + (size_t)kPfRowsT * a.ns_max;            // [4][kPfWaveHist]
+  const int tid = threadIdx.x, lane = tid & 63, kb = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int b = blockIdx.x / a.bps_t, t = blockIdx.x % a.bps_t;
+  const int64_t row0 = a.q_off[b] + (int64_t)t * kPfRowsT, row_end = a.q_off[b + 1];
+  const int nrows = (int)(row0 >= row_end ? 0 : (row_end - row0 < kPfRowsT ? row_end - row0 : kPfRowsT));
   if (nrows == 0) return;
   const int64_t pbase = a.pool_off[b], P = a.pool_off[b + 1] - pbase;
   int64_t nvis_max = 0;
@@ -203,26 +245,32 @@ __global__ __launch_bounds__(256) void k_pf_thresh(PfArgs a) {
     nvis_max = v > nvis_max ? v : nvis_max;
   }
   for (int i = tid; i < 4 * kPfWaveHist; i += 256) wh[i] = 0u;
-  v8i a0, a1;
-  int s0, s1;
+  v8i a0;
+  int s0;
   pf_load_a(a, row0, nrows, lane, a0, s0);
-  pf_load_a(a, row0 + 8, nrows - 8, lane, a1, s1);
   const int64_t st = a.stride;
   const int ns = (int)((nvis_max + st - 1) / st);  // <= ns_max
   const int ntiles = (ns + 31) >> 5;
-  for (int tile = wave; tile < ntiles; tile += 4) {
-    const int i = tile * 32 + (lane & 31);
-    const int64_t j = (int64_t)i * st;
-    uint4 kc;
-    int ks;
-    pf_load_b(a, pbase + j, j < nvis_max, kb, kc, ks);
-    const v16f c0 = pf_mfma(a0, s0, kc, ks), c1 = pf_mfma(a1, s1, kc, ks);
-    if (i < ns) {
+  for (int tb = wave; tb < ntiles; tb += 4 * 8) {  // 8 tiles per wave in flight
+    uint4 kc[8];
+    int ks[8];
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const int q0 = 2 * s + (lane >> 5), q1 = 8 + q0;
-        if (q0 < nrows) ss[(size_t)q0 * a.ns_max + i] = pf_key(c0, s);
-        if (q1 < nrows) ss[(size_t)q1 * a.ns_max + i] = pf_key(c1, s);
+    for (int u = 0; u < 8; ++u) {
+      const int64_t j = (int64_t)((tb + 4 * u) * 32 + (lane & 31)) * st;
+      pf_load_b(a, pbase + j, tb + 4 * u < ntiles && j < nvis_max, kb, kc[u], ks[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int tile = tb + 4 * u;
+      if (tile >= ntiles) break;
+      const int i = tile * 32 + (lane & 31);
+      const v16f c0 = pf_mfma(a0, s0, kc[u], ks[u]);
+      if (i < ns) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const int q = 2 * s + (lane >> 5);
+          if (q < nrows) ss[(size_t)q * a.ns_max + i] = pf_key(c0, s);
+        }
       }
     }
   }
@@ -245,8 +293,10 @@ __global__ __launch_bounds__(256) void k_pf_thresh(PfArgs a) {
         kv[e] = v ? ss[(size_t)q * a.ns_max + c] : 0u;
         vm |= v ? (1u << e) : 0u;
       }
+      // two radix passes: the lower edge of the sample bin holding the need_s-th largest
+      // (at least need_s samples are >= it; the exact order statistic is not needed)
       uint32_t gt;
-      tau = wave_kth<kPfSampleMax / 64>(kv, vm, (uint32_t)need_s, hist, &gt);
+      tau = wave_kth<kPfSampleMax / 64, 2>(kv, vm, (nsq + 63) >> 6, (uint32_t)need_s, hist, &gt);
     }
     if (lane == 0) a.tau[row] = tau;
   }
@@ -256,59 +306,64 @@ __global__ __launch_bounds__(256) void k_pf_thresh(PfArgs a) {
 // 2. every visible score once -> candidate bitmap
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_pf_score(PfArgs a) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, kb = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, kb = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int b = blockIdx.y / a.bps, t = blockIdx.y % a.bps;
   const int64_t row0 = a.q_off[b] + (int64_t)t * kPfRows, row_end = a.q_off[b + 1];
   const int nrows = (int)(row0 >= row_end ? 0 : (row_end - row0 < kPfRows ? row_end - row0 : kPfRows));
   if (nrows == 0) return;
   const int64_t pbase = a.pool_off[b], P = a.pool_off[b + 1] - pbase;
   const int64_t jr0 = (int64_t)blockIdx.x * kPfKeysWG;
-  // this lane's 8 queries: slot 8u + 2s + lane/32 for MFMA u, score index s
-  uint32_t tq[8];
-  int64_t nq[8];
-  int64_t nvis_max = 0;
+  // this lane's 16 queries: slot 8u + 2s + lane/32 of A operand u, score index s
+  constexpr int kE = kPfRows / 2;
+  uint32_t tq[kE];
+  int nq[kE];
+  int nmax = 0, nmin = 0x7fffffff;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
+  for (int e = 0; e < kE; ++e) {
     const int q = 8 * (e >> 2) + 2 * (e & 3) + (lane >> 5);
     const bool v = q < nrows;
     tq[e] = v ? a.tau[row0 + q] : 0xffffffffu;
-    nq[e] = v ? pf_nvis(a.q_pos[row0 + q], a.m, P) : 0;
-    nvis_max = nq[e] > nvis_max ? nq[e] : nvis_max;
+    nq[e] = v ? (int)pf_nvis(a.q_pos[row0 + q], a.m, P) : 0;
+    nmax = nq[e] > nmax ? nq[e] : nmax;
+    nmin = v && nq[e] < nmin ? nq[e] : nmin;
   }
-  nvis_max = (int64_t)__builtin_amdgcn_readfirstlane((int)nvis_max) > (int64_t)__builtin_amdgcn_readlane((int)nvis_max, 32)
-                 ? (int64_t)__builtin_amdgcn_readfirstlane((int)nvis_max)
-                 : (int64_t)__builtin_amdgcn_readlane((int)nvis_max, 32);
+  {  // over the wave (lanes 0-31 and 32-63 hold different queries)
+    uint32_t mn = (uint32_t)nmin, mx = (uint32_t)nmax;
+    wave_minmax(mn, mx);
+    nmin = (int)mn;
+    nmax = (int)mx;
+  }
+  const int64_t nvis_max = nmax;
   if (jr0 >= nvis_max) return;
-  v8i a0, a1;
-  int s0, s1;
-  pf_load_a(a, row0, nrows, lane, a0, s0);
-  pf_load_a(a, row0 + 8, nrows - 8, lane, a1, s1);
+  v8i av[kPfRows / 8];
+  int asc[kPfRows / 8];
+#pragma unroll
+  for (int u = 0; u < kPfRows / 8; ++u) pf_load_a(a, row0 + 8 * u, nrows - 8 * u, lane, av[u], asc[u]);
+  // word lane L < kPfRows holds the bits of query L (= 8u + 2s + h for ballot (u, s), half h)
+  uint32_t* bm_row = a.bitmap + (size_t)(row0 + ((lane & 31) < nrows ? (lane & 31) : 0)) * a.bw;
   constexpr int kT = kPfKeysWG / 32 / 4;  // tiles per wave
-  uint4 kc[kT];
-  int ks[kT];
+  constexpr int kB = 8;                   // tiles per wave in flight
+#pragma unroll 1
+  for (int ub = 0; ub < kT; ub += kB) {
+    uint4 kc[kB];
+    int ks[kB];
 #pragma unroll
-  for (int u = 0; u < kT; ++u) {  // all key loads of the wave first
-    const int64_t j = jr0 + (int64_t)(wave + 4 * u) * 32 + (lane & 31);
-    pf_load_b(a, pbase + j, j < nvis_max, kb, kc[u], ks[u]);
-  }
-  const int wq = lane & 15;  // word lane: query 8 (wq >> 3) + 2 ((wq >> 1) & 3) + (wq & 1)
-  const int qw = 8 * (wq >> 3) + 2 * ((wq >> 1) & 3) + (wq & 1);
-  uint32_t* bm_row = a.bitmap + (size_t)(row0 + (qw < nrows ? qw : 0)) * a.bw;
-#pragma unroll
-  for (int u = 0; u < kT; ++u) {
-    const int64_t jt = jr0 + (int64_t)(wave + 4 * u) * 32;
-    if (jt >= nvis_max) break;
-    const int64_t j = jt + (lane & 31);
-    const v16f c0 = pf_mfma(a0, s0, kc[u], ks[u]), c1 = pf_mfma(a1, s1, kc[u], ks[u]);
-    uint32_t word = 0u;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint32_t key = pf_key(e < 4 ? c0 : c1, e & 3);
-      const uint64_t m = __ballot(j < nq[e] && key >= tq[e]);
-      word = lane == 2 * e ? (uint32_t)m : word;
-      word = lane == 2 * e + 1 ? (uint32_t)(m >> 32) : word;
+    for (int u = 0; u < kB; ++u) {
+      const int64_t j = jr0 + (int64_t)(wave + 4 * (ub + u)) * 32 + (lane & 31);
+      pf_load_b(a, pbase + j, j < nvis_max, kb, kc[u], ks[u]);
     }
-    if (lane < 16 && qw < nrows) bm_row[jt >> 5] = word;
+#pragma unroll
+    for (int u = 0; u < kB; ++u) {
+      const int64_t jt = jr0 + (int64_t)(wave + 4 * (ub + u)) * 32;
+      if (jt >= nvis_max) break;
+      const int j = (int)jt + (lane & 31);
+      const bool whole = jt + 32 <= (int64_t)nmin;  // every query sees the whole tile
+      static_assert(kPfRows == 16, "two MFMA A operands");
+      const uint32_t word = whole ? pf_tile_word<true>(av, asc, kc[u], ks[u], j, nq, tq)
+                                  : pf_tile_word<false>(av, asc, kc[u], ks[u], j, nq, tq);
+      if (lane < nrows && lane < kPfRows) bm_row[jt >> 5] = word;
+    }
   }
 }
 
@@ -388,10 +443,10 @@ __device__ void pf_select_all(const PfArgs& a, int64_t row, int64_t pbase, int64
 
 __global__ __launch_bounds__(128) void k_pf_select(PfArgs a) {
   extern __shared__ __align__(16) uint32_t pf_sm[];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, kb = lane >> 5;
-  uint32_t* cand_j = pf_sm + (size_t)wave * (2 * kPfCand + kPfWaveHist);
-  uint32_t* cand_k = cand_j + kPfCand;
-  uint32_t* hist = cand_k + kPfCand;
+  const int tid = threadIdx.x, lane = tid & 63, kb = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  uint32_t* cand_j = pf_sm + (size_t)wave * (kPfCand + kPfWaveHist);
+  uint32_t* hist = cand_j + kPfCand;
   for (int i = lane; i < kPfWaveHist; i += 64) hist[i] = 0u;
   const int64_t row = (int64_t)blockIdx.x * 2 + wave;
   if (row >= a.n_q) return;  // wave-level work only: no block barriers below
@@ -405,17 +460,24 @@ __global__ __launch_bounds__(128) void k_pf_select(PfArgs a) {
     if (lane == 0) a.tau[row] = 0u;
     return;
   }
-  // candidates: the bitmap's set bits, lane l owning words [l * wpl, l * wpl + wpl)
+  // candidates: the bitmap's set bits, lane l owning words [l * wpl, l * wpl + wpl),
+  // read 16 at a time (all loads of a batch in flight)
   const uint32_t* bm = a.bitmap + (size_t)row * a.bw;
+  uint32_t* bmw = a.bitmap + (size_t)row * a.bw;
   const int nw = (int)((nvis + 31) >> 5), wpl = (nw + 63) >> 6, w0 = lane * wpl;
+  constexpr int kWB = 16;
+  uint32_t wv[kWB];
   uint32_t cnt = 0;
-  for (int i = 0; i < wpl; ++i)
-    if (w0 + i < nw) cnt += (uint32_t)__popc(bm[w0 + i]);
+  for (int b0 = 0; b0 < wpl; b0 += kWB) {
+#pragma unroll
+    for (int i = 0; i < kWB; ++i) wv[i] = (b0 + i < wpl && w0 + b0 + i < nw) ? bm[w0 + b0 + i] : 0u;
+#pragma unroll
+    for (int i = 0; i < kWB; ++i) cnt += (uint32_t)__popc(wv[i]);
+  }
   const uint32_t incl = wave_incl_add(cnt);
   const uint32_t n_c = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
-  // the workspace is left zero-filled: this query's bitmap words and threshold
+  // the workspace is left zero-filled: this query's threshold and bitmap words
   if (lane == 0) a.tau[row] = 0u;
-  uint32_t* bmw = a.bitmap + (size_t)row * a.bw;
   if (n_c < k_eff || n_c > (uint32_t)kPfCand) {
     for (int i = 0; i < wpl; ++i)
       if (w0 + i < nw) bmw[w0 + i] = 0u;
@@ -423,49 +485,56 @@ __global__ __launch_bounds__(128) void k_pf_select(PfArgs a) {
     return;
   }
   uint32_t pos = incl - cnt;
-  for (int i = 0; i < wpl; ++i) {
-    if (w0 + i >= nw) break;
-    uint32_t bits = bm[w0 + i];
-    bmw[w0 + i] = 0u;
-    while (bits) {
-      const int bpos = __ffs(bits) - 1;
-      bits &= bits - 1u;
-      cand_j[pos++] = (uint32_t)((w0 + i) * 32 + bpos);
+  for (int b0 = 0; b0 < wpl; b0 += kWB) {
+    if (wpl > kWB) {  // more than one batch: read this one again
+#pragma unroll
+      for (int i = 0; i < kWB; ++i) wv[i] = (b0 + i < wpl && w0 + b0 + i < nw) ? bm[w0 + b0 + i] : 0u;
+    }
+#pragma unroll
+    for (int i = 0; i < kWB; ++i) {
+      if (b0 + i < wpl && w0 + b0 + i < nw) bmw[w0 + b0 + i] = 0u;
+      uint32_t bits = wv[i];
+      while (bits) {
+        const int bpos = __ffs(bits) - 1;
+        bits &= bits - 1u;
+        cand_j[pos++] = (uint32_t)((w0 + b0 + i) * 32 + bpos);
+      }
     }
   }
-  // the candidates' scores again: 32 per MFMA (query slot 0), 8 tiles in flight
+  // the candidates' scores again: query slot 0 of the MFMA, 32 candidates per tile;
+  // tiles 2e and 2e + 1 fill register slot e (lanes 0-31 and 32-63)
   v8i av;
   int asc;
   pf_load_a(a, row, 1, lane, av, asc);
-  const int ntile = (int)((n_c + 31) >> 5);
-  for (int t0 = 0; t0 < ntile; t0 += 8) {
+  constexpr int NK = kPfCand / 64;
+  uint32_t kv[NK];
+  uint32_t vm = 0;
+  const int nk = (int)((n_c + 63) >> 6);
+#pragma unroll
+  for (int e0 = 0; e0 < NK; e0 += 4) {  // 8 tiles (4 register slots) in flight
+    if (e0 >= nk) break;
     uint4 kc[8];
     int ks[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const uint32_t c = (uint32_t)(t0 + u) * 32u + (uint32_t)(lane & 31);
+      const uint32_t c = (uint32_t)(2 * e0 + u) * 32u + (uint32_t)(lane & 31);
       const bool ok = c < n_c;
       pf_load_b(a, pbase + (ok ? (int64_t)cand_j[c] : 0), ok, kb, kc[u], ks[u]);
     }
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const uint32_t c = (uint32_t)(t0 + u) * 32u + (uint32_t)(lane & 31);
-      const uint32_t key = pf_key(pf_mfma(av, asc, kc[u], ks[u]), 0);
-      if (lane < 32 && c < n_c) cand_k[c] = key;
+    for (int u = 0; u < 8; u += 2) {
+      const uint32_t k_even = pf_key(pf_mfma(av, asc, kc[u], ks[u]), 0);
+      const uint32_t k_odd = pf_key(pf_mfma(av, asc, kc[u + 1], ks[u + 1]), 0);
+      // lanes 0-31 of k_odd -> lanes 32-63 of the slot
+      const uint32_t hi_half = (uint32_t)__shfl_xor((int)k_odd, 32);
+      const int e = e0 + u / 2;
+      kv[e] = lane < 32 ? k_even : hi_half;
+      const bool v = (uint32_t)(e * 64 + lane) < n_c;
+      vm |= v ? (1u << e) : 0u;
     }
   }
-  constexpr int NK = kPfCand / 64;
-  uint32_t kv[NK];
-  uint32_t vm = 0;
-#pragma unroll
-  for (int e = 0; e < NK; ++e) {
-    const uint32_t c = (uint32_t)(e * 64 + lane);
-    const bool v = c < n_c;
-    kv[e] = v ? cand_k[c] : 0u;
-    vm |= v ? (1u << e) : 0u;
-  }
   uint32_t gt;
-  const uint32_t kstar = wave_kth<NK>(kv, vm, k_eff, hist, &gt);
+  const uint32_t kstar = wave_kth<NK>(kv, vm, nk, k_eff, hist, &gt);
   const uint32_t r_eq = k_eff - gt;
   // candidates are in ascending index order: a selected one goes to the count of
   // selected ones before it
@@ -473,6 +542,7 @@ __global__ __launch_bounds__(128) void k_pf_select(PfArgs a) {
   const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
 #pragma unroll
   for (int e = 0; e < NK; ++e) {
+    if (e >= nk) break;
     const bool v = (vm >> e) & 1u;
     const bool eq = v && kv[e] == kstar;
     const uint64_t me = __ballot(eq);
@@ -510,6 +580,7 @@ int launch_prefill_topk(int n_seq, int64_t n_q, int64_t max_q_per_seq, const int
   a.q_off = q_off; a.q_pos = q_pos; a.pool_off = pool_off;
   a.n_seq = n_seq;
   a.bps = (int)((max_q_per_seq + kPfRows - 1) / kPfRows);
+  a.bps_t = (int)((max_q_per_seq + kPfRowsT - 1) / kPfRowsT);
   a.m = m; a.k = k;
   a.stride = pf_stride(max_pool);
   a.ns_max = (int)((max_pool + a.stride - 1) / a.stride);
@@ -521,18 +592,18 @@ int launch_prefill_topk(int n_seq, int64_t n_q, int64_t max_q_per_seq, const int
   a.tau = (uint32_t*)p;
   a.bitmap = (uint32_t*)(p + (((size_t)n_q * 4 + 255) & ~(size_t)255));
   a.idx = idx;
-  const size_t lds1 = ((size_t)kPfRows * a.ns_max + 4 * kPfWaveHist) * 4;
-  const size_t lds3 = (size_t)2 * (2 * kPfCand + kPfWaveHist) * 4;
+  const size_t lds1 = ((size_t)kPfRowsT * a.ns_max + 4 * kPfWaveHist) * 4;
+  const size_t lds3 = (size_t)2 * (kPfCand + kPfWaveHist) * 4;
   static bool attr = false;
   if (!attr) {
     (void)hipFuncSetAttribute((const void*)k_pf_thresh, hipFuncAttributeMaxDynamicSharedMemorySize,
-                              (int)(((size_t)kPfRows * kPfSampleMax + 4 * kPfWaveHist) * 4));
+                              (int)(((size_t)kPfRowsT * kPfSampleMax + 4 * kPfWaveHist) * 4));
     (void)hipFuncSetAttribute((const void*)k_pf_select, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds3);
     attr = true;
   }
   const unsigned nblk = (unsigned)(n_seq * a.bps);
   prof_begin(7, stream);
-  hipLaunchKernelGGL(k_pf_thresh, dim3(nblk), dim3(256), lds1, stream, a);
+  hipLaunchKernelGGL(k_pf_thresh, dim3((unsigned)(n_seq * a.bps_t)), dim3(256), lds1, stream, a);
   prof_end(7, stream);
   dim3 g2((unsigned)((max_pool + kPfKeysWG - 1) / kPfKeysWG), nblk);
   if (g2.x == 0) g2.x = 1;
