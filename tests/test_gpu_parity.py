@@ -361,3 +361,66 @@ def test_fused_decode_matches_oracle_and_separate_calls(name):
     P.check_close(cl, want_cl, "bf16", "fused csa lse")
     P.check_close(ho, want_ho, wl.dtype, "fused hca output")
     P.check_close(hl, want_hl, "bf16", "fused hca lse")
+
+
+def _full_size_decode(wl, rows, hca_rows):
+    """Runs the benchmark's one-launch decode step on a full-size workload and
+    the separate calls on the same inputs; checks the top-k of `rows` and the
+    CSA outputs of `rows` against the oracle, the HCA outputs of `hca_rows`,
+    and that both paths agree on every row."""
+    csa = _lib()
+    host = synth.make_inputs(wl)
+    from long_context_compressed_05_amd.step import Layer, to_device
+    layer = Layer.from_host(_params(wl), host)
+    layer.build_caches()
+    dq = to_device({k: host[k] for k in ("q", "qc", "qs", "w")})
+    idx, co, cl, ho, hl = [P.torch_to_np(t) for t in layer.decode_fused(dq["q"], dq["qc"], dq["qs"], dq["w"])]
+    layer.check_fused()
+    idx_s, co_s, cl_s, ho_s, hl_s = [P.torch_to_np(t) for t in layer.attend(dq["q"], dq["qc"], dq["qs"], dq["w"])]
+    torch.cuda.synchronize()
+    assert np.array_equal(idx, idx_s), "fused and separate top-k differ"
+    P.check_close(co, P.as_f64(co_s), wl.dtype, "fused vs separate csa output")
+    P.check_close(ho, P.as_f64(ho_s), wl.dtype, "fused vs separate hca output")
+    seqs = P.row_seq(host)
+    scale = 1 / math.sqrt(wl.d)
+    for r in rows:
+        b = seqs[r]
+        (t0, t1), (p0, p1), _ = P.seq_slices(host, b)
+        t = int(host["q_pos"][r])
+        o, l, i = oracle.csa_query(host["kv"][t0:t1], host["z"][t0:t1], host["q"][r], t, wl.m, wl.W, wl.k, scale,
+                                   host["qc"][r], host["qs"][r], host["w"][r], host["kc"][p0:p1], host["ks"][p0:p1])
+        assert np.array_equal(idx[r], i), f"top-k of row {r}"
+        P.check_close(co[r], o, wl.dtype, f"csa output of row {r}")
+        P.check_close(cl[r], l, "bf16", f"csa lse of row {r}")
+    for r in hca_rows:
+        b = seqs[r]
+        (t0, t1), _, _ = P.seq_slices(host, b)
+        t = int(host["q_pos"][r])
+        o, l = oracle.hca_query(host["kv"][t0:t1], host["z"][t0:t1], host["q"][r], t, wl.m_hca, wl.W_hca, scale)
+        P.check_close(ho[r], o, wl.dtype, f"hca output of row {r}")
+        P.check_close(hl[r], l, "bf16", f"hca lse of row {r}")
+
+
+def test_decode_full_size_b4_t1m():
+    """The benchmark workload: 4 sequences of 2^20 tokens, top-1024 of 262,144
+    pooled entries, 8192 HCA entries, in the launch configuration bench.py
+    times; every row against the oracle."""
+    wl = synth.decode_b4_t1m()
+    _full_size_decode(wl, range(wl.n_q), range(wl.n_q))
+
+
+def test_decode_full_size_b16_t64k():
+    """16 sequences of 65,536 tokens, top-512 of 16,384; every row's top-k and
+    CSA output, HCA outputs of four rows."""
+    wl = synth.decode_b16_t64k()
+    _full_size_decode(wl, range(wl.n_q), [0, 5, 10, 15])
+
+
+def test_decode_full_size_ragged_b32_sampled():
+    """32 ragged sequences (log-uniform lengths up to 2^20, tails not a
+    multiple of m) with tie-heavy indexer codes; sampled rows against the
+    oracle, and the fused and separate paths agree on every row."""
+    wl = synth.decode_ragged_b32()
+    lens = np.array(wl.lengths)
+    rows = sorted(set([int(np.argmin(lens)), int(np.argmax(lens)), 0, 7, 19, 31]))
+    _full_size_decode(wl, rows, rows[:3])
