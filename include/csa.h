@@ -186,21 +186,26 @@ int hca_attn(int dtype, const csa_batch* b, const int64_t* hpool_off, int64_t ma
 /* ------------------------------------------------------------------------
  * csa_hca_decode — one decode step of a CSA + HCA layer in ONE launch:
  * csa_index_topk, csa_sparse_attn and hca_attn of the same arguments, fused
- * into a single persistent (cooperatively launched) kernel so that the HCA
- * stream overlaps the top-k chain and no launch gaps separate the stages.
- * Same definitions and outputs as the three separate calls (pages as cited
- * there); bit-identical top-k.  Decode batches only: one query per sequence
- * (n_q == n_seq, q_off[b] == b), bf16, H % 16 == 0 and H <= 64, d = 128,
- * indexer 4 x 64, max_pool <= 262144, at most 64 queries; otherwise
- * CSA_ERR_UNSUPPORTED (use the separate calls).
+ * into a single persistent kernel (one workgroup per compute unit, work units
+ * handed out in dependency order) so that the HCA stream overlaps the top-k
+ * chain and no launch gaps separate the stages.  Same definitions and
+ * outputs as the three separate calls (pages as cited there); bit-identical
+ * top-k.  Decode batches only: one query per sequence (n_q == n_seq,
+ * q_off[b] == b), bf16, H % 16 == 0 and 16 <= H <= 64, d = 128, indexer
+ * 4 x 64, k <= 1024, max_pool <= 262144, at most 64 queries, and a plan whose
+ * score chunks fit (at most 4096 entries per chunk, 512 chunks per row);
+ * otherwise CSA_ERR_UNSUPPORTED (use the separate calls).
  *   kv_pool [sum P][2][d] (block m), kv_pool_hca [sum P'][2][d] (block m_hca),
  *   kv_raw [sum L][2][d]; idx [n_q][k]; csa_out/hca_out [n_q][H][d] bf16;
  *   csa_lse/hca_lse [n_q][H] fp32 or NULL.
  *   ws: >= csa_hca_decode_workspace() bytes, ZERO-FILLED before first use and
- *       left zero-filled by every launch; re-zero it when the shapes change.
- * The kernel's internal waits are bounded: if one ever times out (not seen
- * with co-resident workgroups) the step's outputs are invalid and an error
- * word in ws is set, which csa_hca_decode_check() reports.
+ *       reusable by later launches of the same shapes (a launch-epoch tag in
+ *       ws tells one launch's words from another's); re-zero it when the
+ *       shapes change.  Launches sharing a ws must be ordered (one stream).
+ * The kernel's internal waits are bounded: if one ever times out (a wait only
+ * depends on work units handed out before it, so it is not expected) the
+ * step's outputs are invalid and an error word in ws is set, which
+ * csa_hca_decode_check() reports.
  * ---------------------------------------------------------------------- */
 int csa_hca_decode_workspace(const csa_batch* b, int64_t max_pool, int64_t max_hpool, int H, int d,
                              int k, int W, int W_hca, size_t* bytes);

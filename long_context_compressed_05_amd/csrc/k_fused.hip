@@ -1,21 +1,26 @@
 // Fused CSA + HCA decode step: one launch per step.
 //
-// The whole decode hot path runs in one kernel whose workgroups take work
-// units from a device-wide ticket, in dependency order:
+// The whole decode hot path runs in one kernel whose workgroups (one per CU)
+// take work units in dependency order:
 //   score   chunk c of row r: C pooled entries of the query's visible range,
-//           MXFP4 MFMA scores -> u32 sort keys (in LDS, and in the workspace
-//           for the fallback); the chunk's list: its L largest entries by
-//           (key desc, index asc), in ascending index order, then the list's
-//           tagged header
-//   select  row r: K* = the k_eff-th largest listed key (radix select in LDS),
-//           the per-chunk counts above and equal to K*, the tie cut in chunk
-//           (= index) order, an exactness check (else an exact radix select
-//           over the stored keys), the selection -> idx, the row's header
-//   items   [CSA selected splits | CSA window splits | HCA splits | CSA merges |
-//           HCA merges]:
-//     CSA selected split: its 64 positions of idx, attention over those rows
-//     window / HCA split: attention over raw window rows / pooled HCA rows
-//     merge: log-sum-exp merge of the row's split partials, 4 heads per item
+//           MXFP4 MFMA scores -> u32 sort keys in LDS; one adaptive radix pass
+//           finds a threshold tau so that about lst entries have key >= tau;
+//           every entry with key >= tau (at most lst of them) is listed in
+//           ascending index order with its key, then the list's tagged header;
+//           the chunk's keys are then stored for the exact fallback
+//   select  row r: the listed keys of all its chunks, staged in LDS as their
+//           headers arrive; K* = the k_eff-th largest listed key (radix select),
+//           the tie cut in list (= index) order, an exactness check (every
+//           truncated chunk must have tau <= K*; else an exact radix select over
+//           the stored keys), then K*, the cut and each CSA group's output
+//           offset are published
+//   group   CSA group g of row r (cg consecutive chunks, about 64 selected
+//           entries): its chunks' lists filtered by (K*, cut) into LDS,
+//           attention over those pooled rows, its partial, its slice of idx
+//   window / HCA split: attention over raw window rows / pooled HCA rows
+//   merge   log-sum-exp merge of a row's split partials, 4 heads per unit
+// (units: [score chunks | row selects | CSA groups | window splits | HCA
+// splits | HCA merges | CSA merges]).
 //
 // Synchronisation.  Cross-workgroup words are 64 bits: the launch's tag in
 // the high half, the payload in the low half, written with device-coherent
