@@ -5,22 +5,22 @@
 //   score   chunk c of row r: C pooled entries of the query's visible range,
 //           MXFP4 MFMA scores -> u32 sort keys in LDS; one adaptive radix pass
 //           finds a threshold tau so that about lst entries have key >= tau;
-//           every entry with key >= tau (at most lst of them) is listed in
-//           ascending index order with its key, then the list's tagged header;
-//           the chunk's keys are then stored for the exact fallback
-//   select  row r: the listed keys of all its chunks, staged in LDS as their
-//           headers arrive; K* = the k_eff-th largest listed key (radix select),
-//           the tie cut in list (= index) order, an exactness check (every
-//           truncated chunk must have tau <= K*; else an exact radix select over
-//           the stored keys), then K*, the cut and each CSA group's output
-//           offset are published
+//           every entry with key >= tau (at most lst of them) is written to the
+//           chunk's lst list positions in ascending index order, each position
+//           a tagged entry (empty ones included), with tau beside them; then
+//           the chunk's keys are stored for the exact fallback
 //   group   CSA group g of row r (cg consecutive chunks, about 64 selected
-//           entries): its chunks' lists filtered by (K*, cut) into LDS,
-//           attention over those pooled rows, its partial, its slice of idx
+//           entries): reads the whole row's lists (one round of loads), finds
+//           K* = the k_eff-th largest listed key (radix select in LDS), checks
+//           that every truncated chunk has tau <= K* (else the row's first
+//           group runs an exact radix select over the stored keys and
+//           publishes it), cuts the ties in list (= index) order, takes its own
+//           chunks' selected entries, attends over those pooled rows, writes
+//           its partial and its slice of idx
 //   window / HCA split: attention over raw window rows / pooled HCA rows
 //   merge   log-sum-exp merge of a row's split partials, 4 heads per unit
-// (units: [score chunks | row selects | CSA groups | window splits | HCA
-// splits | HCA merges | CSA merges]).
+// (units: [score chunks | CSA groups | window splits | HCA splits | HCA
+// merges | CSA merges]).
 //
 // Synchronisation.  Cross-workgroup words are 64 bits: the launch's tag in
 // the high half, the payload in the low half, written with device-coherent
@@ -44,8 +44,8 @@ namespace csa {
 constexpr int kFMaxC = 4096;         // score entries per workgroup (keys in LDS)
 constexpr int kFKPT = kFMaxC / 256;  // keys per thread in a chunk
 constexpr int kFHist = 2048;         // radix digit bins (11 bits)
-constexpr int kFEntLds = 6144;       // listed keys of a row staged in LDS
-constexpr int kFEPT = kFEntLds / 256;  // listed keys per thread in the row selection
+constexpr int kFEntLds = 6144;       // list positions of a row (n_sc * lst)
+constexpr int kFEPT = kFEntLds / 256;  // list positions per thread in a group's selection
 constexpr int kFMaxSel = 1024;       // selected rows of one CSA group (k <= kFMaxSel)
 constexpr int kFMaxVisible = 262144;  // visible pooled entries per query (18-bit indices)
 constexpr int kFMaxRows = 64;
@@ -56,25 +56,30 @@ constexpr uint32_t kSpinLimit = 1u << 20;
 enum { W_EPOCH = 0, W_EXIT = 1, W_ERROR = 2, W_TICKET = 3, W_FALLBACK = 4, W_CTL = 64 };
 
 // LDS layout (dynamic).  The key region holds a score chunk's keys, or the
-// per-chunk arrays of a row (offsets, counts, thresholds) and a CSA group's
-// selected rows; the union region holds the attention stages, or a row's
-// listed keys and the radix histograms, or a CSA group's listed entries.
+// per-chunk arrays of a row (counts, thresholds) and a CSA group's selected
+// rows; the union region holds the attention stages, or the radix histograms,
+// or a score chunk's staged list.
 constexpr int kOffKeys = 0;                                 // uint32 [kFMaxC]
 constexpr int kOffSel = kOffKeys + 3 * (kFMaxSlots + 8) * 4;  // int32 [kFMaxSel] (aliases the chunk keys)
 constexpr int kOffScr = kOffKeys + kFMaxC * 4;              // uint32 [64]
 constexpr int kOffU = kOffScr + 64 * 4;                     // union region
-constexpr int kOffLst = kOffU;                              // uint32 [kFEntLds] listed keys / uint64 entries
 constexpr int kOffHist = kOffU + kFEntLds * 4;              // uint32 [2][kFHist] + [64] lane trash words
 constexpr int kSelEnd = kOffHist + (2 * kFHist + 64) * 4;
 constexpr int kAttnEnd = kOffU + kAttnLdsBytes;
 constexpr int kFusedLds = kSelEnd > kAttnEnd ? kSelEnd : kAttnEnd;
 static_assert(kOffSel + kFMaxSel * 4 <= kOffScr, "a group's selected rows fit the key region");
 static_assert(kOffU % 16 == 0 && kOffHist % 16 == 0, "LDS regions must be 16-byte aligned");
-static_assert(kFEntLds * 8 <= kAttnLdsBytes, "a group's listed entries fit the union region");
+static_assert(kFMaxC * 8 <= kAttnLdsBytes, "a score chunk's staged list fits the union region");
+static_assert(2 * kFEntLds * 4 <= kAttnLdsBytes, "a row's keys and indices by position fit the union region");
+static_assert(kFEPT % 4 == 0 && kFEntLds % 4 == 0, "positions are read 16 bytes at a time");
 static_assert(kFusedLds <= 160 * 1024, "one workgroup per CU");
 
+typedef unsigned int v2u_t __attribute__((ext_vector_type(2)));
+typedef unsigned int v4u_t __attribute__((ext_vector_type(4)));
+constexpr uint32_t kNoKey = 0xffffffffu;  // empty list position (scores are finite and >= 0)
+
 // scratch word indices (0..19 are used by the block scans and searches)
-enum { S_TAG = 40, S_FLAG, S_DIGIT, S_ABOVE, S_CNT, S_BAD, S_TICKET, S_KEY, S_CUT };
+enum { S_TAG = 40, S_FLAG, S_DIGIT, S_ABOVE, S_CNT, S_BAD, S_TICKET, S_KEY, S_CUT, S_OFF, S_END };
 
 struct FusedArgs {
   const int64_t* tok_off;
@@ -110,13 +115,12 @@ struct FusedArgs {
   uint32_t* ctl;
   uint32_t* keys;      // [R][key_stride] sort keys (read only by the exact fallback)
   uint64_t* key_hdr;   // [R*n_sc] tagged: the chunk's keys are in keys
-  uint64_t* ent_hdr;   // [R*n_sc] tagged: listed count | truncated << 16
-  uint64_t* ent;       // [R*n_sc][lst] (key << 32) | index, ascending index
-  uint32_t* lkey;      // [R*n_sc][lst] the listed keys alone, same order
-  uint32_t* ltau;      // [R*n_sc] listing threshold: every entry of the chunk with key >= it is listed
-  uint64_t* row_k;     // [R] tagged: K*
-  uint64_t* row_cut;   // [R] tagged: listed position of the last taken tie; or 1 << 31 | index (fallback)
-  uint64_t* grp_off;   // [R][n_cs_sel] tagged: output position of the group's first selected entry
+  v4u_t* lent;         // [R*n_sc][lst] list entries {tag, key, tag, index}, ascending index;
+                       // positions past the chunk's count hold kNoKey
+  uint64_t* ltau;      // [R*n_sc] tagged: the chunk's listing threshold (0 when it listed all)
+  uint64_t* row_k;     // [R] tagged: K* (exact selection over the stored keys only)
+  uint64_t* row_cut;   // [R] tagged: index of the last taken entry equal to K* (same)
+  uint64_t* grp_off;   // [R][n_cs_sel] tagged: output position of the group's first selected entry (same)
   uint64_t* part_hdr;  // [R][n_cs_sel + n_cs_win + n_hs]
   float* csa_po;       // [R][n_cs][H][128]
   float* csa_pml;      // [R][n_cs][H][2]
@@ -166,8 +170,6 @@ __device__ __forceinline__ uint64_t tagged(uint32_t tag, uint32_t payload) {
 // Device-coherent (sc1) loads and stores through a buffer descriptor over the
 // workspace: ordinary (non-atomic) memory operations, so the compiler keeps
 // many of them in flight, with the same cache policy as agent-scope atomics.
-typedef unsigned int v2u_t __attribute__((ext_vector_type(2)));
-typedef unsigned int v4u_t __attribute__((ext_vector_type(4)));
 constexpr int kSc1 = 16;  // cache-policy operand: sc1
 struct Coh {
   __amdgpu_buffer_rsrc_t r;
@@ -268,17 +270,12 @@ __device__ __forceinline__ void block_exscan(uint32_t* cnt, int n, uint32_t* scr
     v[i] = j < n ? cnt[j] : 0u;
     tot += v[i];
   }
-  uint32_t incl = tot;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t u = __shfl_up(incl, off);
-    if (lane >= off) incl += u;
-  }
+  const uint32_t incl = wave_incl_add(tot);
   if (lane == 63) scr[wave] = incl;
   __syncthreads();
-  uint32_t run = incl - tot;
-  for (int w2 = 0; w2 < wave; ++w2) run += scr[w2];
-  const uint32_t all = scr[0] + scr[1] + scr[2] + scr[3];
+  const uint4 wt = *reinterpret_cast<const uint4*>(scr);
+  uint32_t run = incl - tot + (wave > 0 ? wt.x : 0u) + (wave > 1 ? wt.y : 0u) + (wave > 2 ? wt.z : 0u);
+  const uint32_t all = wt.x + wt.y + wt.z + wt.w;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int j = 4 * tid + i;
@@ -317,9 +314,9 @@ __device__ __forceinline__ uint32_t block_exscan_val(uint32_t v, uint32_t* scr, 
   const uint32_t incl = wave_incl_add(v);
   if (lane == 63) scr[16 + wave] = incl;
   __syncthreads();
-  uint32_t run = incl - v;
-  for (int w2 = 0; w2 < wave; ++w2) run += scr[16 + w2];
-  *total = uni(scr[16] + scr[17] + scr[18] + scr[19]);
+  const uint4 w = *reinterpret_cast<const uint4*>(scr + 16);  // one LDS read for the four wave totals
+  const uint32_t run = incl - v + (wave > 0 ? w.x : 0u) + (wave > 1 ? w.y : 0u) + (wave > 2 ? w.z : 0u);
+  *total = uni(w.x + w.y + w.z + w.w);
   __syncthreads();
   return run;
 }
@@ -346,13 +343,11 @@ __device__ __forceinline__ void key_range(const uint32_t (&kv)[NK], uint32_t vm,
   }
   for (int i = tid; i < 2 * kFHist / 4; i += 256) reinterpret_cast<uint4*>(hist)[i] = make_uint4(0u, 0u, 0u, 0u);
   __syncthreads();
-  uint32_t l = scr[8], h = scr[12];
-  for (int w2 = 1; w2 < 4; ++w2) {
-    l = scr[8 + w2] < l ? scr[8 + w2] : l;
-    h = scr[12 + w2] > h ? scr[12 + w2] : h;
-  }
-  *lo = uni(l);
-  *hi = uni(h);
+  const uint4 l4 = *reinterpret_cast<const uint4*>(scr + 8), h4 = *reinterpret_cast<const uint4*>(scr + 12);
+  const uint32_t l01 = l4.x < l4.y ? l4.x : l4.y, l23 = l4.z < l4.w ? l4.z : l4.w;
+  const uint32_t h01 = h4.x > h4.y ? h4.x : h4.y, h23 = h4.z > h4.w ? h4.z : h4.w;
+  *lo = uni(l01 < l23 ? l01 : l23);
+  *hi = uni(h01 > h23 ? h01 : h23);
 }
 
 // One radix pass over the keys in [lo, hi] (lo < hi), cut into at most 2048
@@ -376,20 +371,22 @@ __device__ __forceinline__ void radix_pass(const uint32_t (&kv)[NK], uint32_t vm
   }
   __syncthreads();
   uint32_t c[8], tot = 0;
-#pragma unroll
-  for (int b = 0; b < 8; ++b) {
-    c[b] = hist[8 * tid + b];
-    hist[8 * tid + b] = 0u;
-    tot += c[b];
+  {
+    uint4* h4 = reinterpret_cast<uint4*>(hist + 8 * tid);
+    const uint4 a0 = h4[0], a1 = h4[1];
+    h4[0] = make_uint4(0u, 0u, 0u, 0u);
+    h4[1] = make_uint4(0u, 0u, 0u, 0u);
+    c[0] = a0.x; c[1] = a0.y; c[2] = a0.z; c[3] = a0.w;
+    c[4] = a1.x; c[5] = a1.y; c[6] = a1.z; c[7] = a1.w;
   }
+#pragma unroll
+  for (int b = 0; b < 8; ++b) tot += c[b];
   const uint32_t incl = wave_incl_add(tot);
   if (lane == 63) scr[wave] = incl;
   __syncthreads();
-  uint32_t below = incl - tot, all = 0;
-  for (int w2 = 0; w2 < 4; ++w2) {
-    all += scr[w2];
-    below += w2 < wave ? scr[w2] : 0u;
-  }
+  const uint4 wt = *reinterpret_cast<const uint4*>(scr);
+  const uint32_t all = wt.x + wt.y + wt.z + wt.w;
+  const uint32_t below = incl - tot + (wave > 0 ? wt.x : 0u) + (wave > 1 ? wt.y : 0u) + (wave > 2 ? wt.z : 0u);
   const uint32_t sup = all - below - tot;  // keys in bins above this thread's 8
   if (sup < need && sup + tot >= need) {  // walk this thread's bins downwards (unrolled)
     uint32_t cum = sup, asel = 0;
@@ -548,23 +545,21 @@ __device__ __forceinline__ void phase_score(const FCtx& x, int r, int c, const F
   for (int i = 0; i < kFKPT; ++i) cg += (i < nv && kv[i] >= tau) ? 1u : 0u;
   uint32_t n_list;
   uint32_t pos = block_exscan_val(cg, x.scr, &n_list);
-  const size_t slot = (size_t)r * a.n_sc + c;
-  uint64_t* dst = a.ent + slot * a.lst;
-  uint32_t* dk = a.lkey + slot * a.lst;
+  // the listed (key, index) pairs in ascending index order -> LDS (the
+  // histograms are no longer needed), then every list position -> workspace
+  uint2* lst_s = reinterpret_cast<uint2*>(x.smem + kOffU);
   const uint32_t jbase = (uint32_t)c * (uint32_t)a.C + (uint32_t)e0;
 #pragma unroll
-  for (int i = 0; i < kFKPT; ++i) {
-    if (i < nv && kv[i] >= tau) {
-      __builtin_amdgcn_raw_buffer_store_b64(v2u_t{jbase + (uint32_t)i, kv[i]}, x.coh.r,
-                                            coh_off(x.coh, dst + pos), 0, kSc1);
-      __builtin_amdgcn_raw_buffer_store_b32(kv[i], x.coh.r, coh_off(x.coh, dk + pos), 0, kSc1);
-      ++pos;
-    }
-  }
-  if (tid == 0) __builtin_amdgcn_raw_buffer_store_b32(tau, x.coh.r, coh_off(x.coh, a.ltau + slot), 0, kSc1);
-  vm_drain();
+  for (int i = 0; i < kFKPT; ++i)
+    if (i < nv && kv[i] >= tau) lst_s[pos++] = make_uint2(kv[i], jbase + (uint32_t)i);
   __syncthreads();
-  if (tid == 0) st_dev64(a.ent_hdr + slot, tagged(x.tag, n_list | ((n_list < (uint32_t)n ? 1u : 0u) << 16)));
+  const size_t slot = (size_t)r * a.n_sc + c;
+  v4u_t* dst = a.lent + slot * L;
+  for (uint32_t t = (uint32_t)tid; t < L; t += 256) {
+    const uint2 e = t < n_list ? lst_s[t] : make_uint2(kNoKey, kNoKey);
+    coh_st128(x.coh, dst + t, v4u_t{x.tag, e.x, x.tag, e.y});
+  }
+  if (tid == 0) st_dev64(a.ltau + slot, tagged(x.tag, n_list < (uint32_t)n ? tau : 0u));
   // then all the keys -> workspace, read only by the exact fallback: stored after the
   // list is published (their drain would hold the list back), with a header of their own
   {
@@ -622,149 +617,24 @@ __device__ __forceinline__ void write_partial(const FCtx& x, AttnState<1>& st, i
     st_dev64(a.part_hdr + (size_t)r * (n_cs + a.n_hs) + (hca ? n_cs : 0) + pi, tagged(x.tag, 1u));
 }
 
-// Per-chunk arrays of a row in LDS (key region): list headers (count |
-// truncated << 16) and thresholds.  A listed entry's position is its list
-// slot: chunk * lst + rank in the chunk's list, so positions ascend with the
-// index.
-__device__ __forceinline__ uint32_t* row_hdrs(const FCtx& x) { return reinterpret_cast<uint32_t*>(x.smem + kOffKeys); }
-__device__ __forceinline__ uint32_t* row_taus(const FCtx& x) { return row_hdrs(x) + (kFMaxSlots + 8); }
+// Per-chunk thresholds of a row, or per-chunk counts, in LDS (key region).
+__device__ __forceinline__ uint32_t* row_cnts(const FCtx& x) { return reinterpret_cast<uint32_t*>(x.smem + kOffKeys); }
+__device__ __forceinline__ uint32_t* row_taus(const FCtx& x) { return row_cnts(x) + (kFMaxSlots + 8); }
 
-// Selection threshold of row r, one workgroup.  The row takes the k_eff first
-// entries in (key descending, index ascending) order.  Each score chunk listed
-// every entry whose key is at least its threshold tau (all of its entries when
-// it has at most lst).  K* = the k_eff-th largest listed key; the row takes
-// every listed entry above K* and the r_eq = k_eff - (listed keys above K*)
-// listed entries equal to K* of lowest index: those at or before position
-// `cut`.  This is the exact selection when every truncated chunk has tau <= K*
-// (it then listed all of its entries >= K*, ties included).  Otherwise an
-// exact radix select over the row's stored keys gives the order key (K*, j*)
-// of the k_eff-th entry.  Published: row_k = K*, row_cut = cut (or 1 << 31 |
-// j*), then each CSA group's output offset; idx positions [k_eff, k) are set
-// to -1.  The selected entries themselves are taken and written by the CSA
-// groups.  Each chunk's listed keys are loaded as soon as its header is seen,
-// while later chunks are still being scored.
-__device__ __forceinline__ bool select_row(const FCtx& x, int r, const FRow& f) {
+__device__ __forceinline__ uint32_t lanes_below(uint64_t b) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0u));
+}
+
+// Exact selection of row r over all of its stored keys, when its chunks' lists
+// cannot decide it (run by the row's first CSA group).  The k_eff-th entry in
+// (key descending, index ascending) order is found by a radix select over the
+// keys and then over the indices of the entries equal to its key; published:
+// row_k = K*, row_cut = its index, and each CSA group's output offset.
+__device__ __forceinline__ bool row_fallback(const FCtx& x, int r, const FRow& f, int k_eff) {
   KArgs& a = *x.a;
   const int tid = lane_tid();
-  const int k_eff = (int)(f.n_vis < a.k ? f.n_vis : a.k);
-  const int nsc = a.n_sc, ngrp = a.n_cs_sel, cgs = a.cg, L = a.lst;
-  int32_t* idx_out = a.idx + (size_t)r * a.k;
-  for (int i = k_eff + tid; i < a.k; i += 256) idx_out[i] = -1;
-  uint64_t* gout = a.grp_off + (size_t)r * ngrp;
-  if (k_eff == 0) {  // nothing visible: every list is empty
-    if (tid == 0) {
-      st_dev64(a.row_k + r, tagged(x.tag, 0u));
-      st_dev64(a.row_cut + r, tagged(x.tag, 0u));
-    }
-    for (int g = tid; g < ngrp; g += 256) st_dev64(gout + g, tagged(x.tag, 0u));
-    return true;
-  }
-  uint32_t* e_n = row_hdrs(x);
-  uint32_t* e_tau = row_taus(x);
-  uint32_t* lk_s = reinterpret_cast<uint32_t*>(x.smem + kOffLst);
+  const int nsc = a.n_sc, ngrp = a.n_cs_sel, cgs = a.cg;
   uint32_t* hist = reinterpret_cast<uint32_t*>(x.smem + kOffHist);
-  const uint32_t* rowk = a.lkey + (size_t)r * nsc * L;
-  // per chunk: wait for its header, then load its threshold and listed keys (16 bytes per load)
-  bool fail = false;
-  uint32_t listed = 0;
-  for (int sl = tid; sl < nsc && !fail; sl += 256) {
-    const uint32_t v = poll_word(x, a.ent_hdr + (size_t)r * nsc + sl, &fail, 2u);
-    const uint32_t cnt = v & 0xffffu;
-    e_n[sl] = v;
-    listed += cnt;
-    e_tau[sl] = coh_ld32(x.coh, a.ltau + (size_t)r * nsc + sl);
-    for (uint32_t i0 = 0; i0 < cnt; i0 += 64) {  // 16 loads in flight
-      v4u_t q[16];
-#pragma unroll
-      for (int u = 0; u < 16; ++u)
-        q[u] = i0 + 4u * u < cnt ? coh_ld128(x.coh, rowk + (size_t)sl * L + i0 + 4u * u) : v4u_t{0u, 0u, 0u, 0u};
-#pragma unroll
-      for (int u = 0; u < 16; ++u)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (i0 + 4u * u + e < cnt) lk_s[sl * L + i0 + 4u * u + e] = q[u][e];
-    }
-  }
-  if (tid == 0) x.scr[S_BAD] = 0;
-  if (!all_ok(x, fail)) return false;
-  uint32_t n_ent;
-  (void)block_exscan_val(listed, x.scr, &n_ent);
-  bool exact = n_ent >= (uint32_t)k_eff;
-  if (exact) {
-    // K* over the listed keys, thread t holding slot positions [t*M, t*M + M)
-    const int npos = nsc * L;
-    const int M = (npos + 255) >> 8;
-    const int m0 = tid * M;
-    uint32_t kv[kFEPT];
-    uint32_t vm = 0;
-    {
-      int sl = m0 / L, i = m0 - sl * L;
-      uint32_t cnt = sl < nsc ? (e_n[sl] & 0xffffu) : 0u;
-#pragma unroll
-      for (int e = 0; e < kFEPT; ++e) {
-        const bool v = e < M && m0 + e < npos && (uint32_t)i < cnt;
-        kv[e] = v ? lk_s[m0 + e] : 0u;
-        vm |= v ? (1u << e) : 0u;
-        if (++i == L) {
-          i = 0;
-          ++sl;
-          cnt = sl < nsc ? (e_n[sl] & 0xffffu) : 0u;
-        }
-      }
-    }
-    uint32_t gt_all;
-    const uint32_t kstar = kth_key<kFEPT>(kv, vm, (uint32_t)k_eff, hist, x.scr, &gt_all);
-    const uint32_t r_eq = (uint32_t)k_eff - gt_all;  // >= 1
-    for (int sl = tid; sl < nsc; sl += 256)
-      if ((e_n[sl] >> 16) != 0u && e_tau[sl] > kstar) x.scr[S_BAD] = 1;
-    uint32_t cgt = 0, ceq = 0;
-#pragma unroll
-    for (int e = 0; e < kFEPT; ++e) {
-      const bool v = (vm >> e) & 1u;
-      cgt += (v && kv[e] > kstar) ? 1u : 0u;
-      ceq += (v && kv[e] == kstar) ? 1u : 0u;
-    }
-    uint32_t tot;
-    const uint32_t pre = block_exscan_val(cgt | (ceq << 16), x.scr, &tot);
-    const uint32_t pre_gt = pre & 0xffffu, pre_eq = pre >> 16;
-    if (pre_eq < r_eq && pre_eq + ceq >= r_eq) {  // this thread holds the r_eq-th tie
-      uint32_t e2 = pre_eq, cut = 0;
-#pragma unroll
-      for (int e = 0; e < kFEPT; ++e)
-        if (((vm >> e) & 1u) && kv[e] == kstar) {
-          ++e2;
-          if (e2 == r_eq) cut = (uint32_t)(m0 + e);
-        }
-      x.scr[S_CUT] = cut;
-    }
-    __syncthreads();
-    exact = uni(x.scr[S_BAD]) == 0u;
-    if (exact) {
-      const uint32_t cut = uni(x.scr[S_CUT]);
-      if (tid == 0) {
-        st_dev64(a.row_k + r, tagged(x.tag, kstar));
-        st_dev64(a.row_cut + r, tagged(x.tag, cut));
-      }
-      // group g starts at position P = g * cg * lst: its output offset is the count of
-      // taken entries before P
-      for (int g = 0; g < ngrp; ++g) {
-        const uint32_t P = (uint32_t)(g * cgs * L);
-        if (P >= (uint32_t)m0 && P < (uint32_t)(m0 + M)) {
-          uint32_t gb = pre_gt, eb = pre_eq;
-#pragma unroll
-          for (int e = 0; e < kFEPT; ++e)
-            if ((uint32_t)(m0 + e) < P && ((vm >> e) & 1u)) {
-              gb += kv[e] > kstar ? 1u : 0u;
-              eb += kv[e] == kstar ? 1u : 0u;
-            }
-          st_dev64(gout + g, tagged(x.tag, gb + (eb < r_eq ? eb : r_eq)));
-        }
-      }
-      return true;
-    }
-  }
-  // exact radix select over the row's stored keys: the k_eff-th largest key K*, then
-  // the (need_left)-th smallest index among keys equal to K* (indices < 2^18)
   if (tid == 0) atomicAdd(a.ctl + W_FALLBACK, 1u);
   {
     bool kfail = false;
@@ -783,7 +653,7 @@ __device__ __forceinline__ bool select_row(const FCtx& x, int r, const FRow& f) 
       [&](uint32_t i) { return coh_ld32(x.coh, rowkeys + i) == kstar; }, &nl2, hist, x.scr);
   if (tid == 0) {
     st_dev64(a.row_k + r, tagged(x.tag, kstar));
-    st_dev64(a.row_cut + r, tagged(x.tag, 0x80000000u | (~njstar & 0x3ffffu)));
+    st_dev64(a.row_cut + r, tagged(x.tag, ~njstar & 0x3ffffu));
   }
   const uint64_t cstar = ((uint64_t)kstar << 32) | njstar;
   // selected count per chunk -> offsets at the group starts
@@ -799,122 +669,227 @@ __device__ __forceinline__ bool select_row(const FCtx& x, int r, const FRow& f) 
   __syncthreads();
   block_exscan(e_sel, nsc, x.scr);
   for (int g = tid; g < ngrp; g += 256)
-    st_dev64(gout + g, tagged(x.tag, e_sel[g * cgs < nsc ? g * cgs : nsc]));
+    st_dev64(a.grp_off + (size_t)r * ngrp + g, tagged(x.tag, e_sel[g * cgs < nsc ? g * cgs : nsc]));
+  __syncthreads();
   return true;
 }
 
-// CSA group g of row r (score chunks [g*cg, g*cg + cg)): its selected entries,
-// in ascending index order -> LDS (returns how many, or -1 on a failed wait).
-// Its chunks' lists are loaded before the row's threshold is published.
-__device__ __forceinline__ int group_select(const FCtx& x, int r, int g, const FRow& f) {
+// CSA group g of row r: score chunks [c0, c1) = [g*cg, g*cg + cg).  The row
+// takes the k_eff first entries in (key descending, index ascending) order.
+// Each score chunk listed every entry whose key is at least its threshold tau
+// (all of its entries when it has at most lst), in ascending index order, at
+// list positions chunk * lst + rank, so positions ascend with the index.  The
+// group reads the whole row's lists and thresholds (every group of the row
+// computes the same result): K* = the k_eff-th largest listed key; the row
+// takes every listed entry above K* and the r_eq = k_eff - (listed keys above
+// K*) listed entries equal to K* of lowest position.  This is the exact
+// selection when every truncated chunk has tau <= K*: each entry of the row
+// with key >= K* is then listed, so the listed keys >= K* are all of the
+// row's, ties included.  Otherwise the row's first group runs the exact
+// selection over the stored keys (row_fallback) and every group takes its
+// entries from the stored keys.  Result: the group's selected indices in
+// ascending order -> LDS, their count (or -1 on a failed wait), and their
+// output offset in the row's idx -> *off_out; the entries sit at
+// sel_s[*base_out ..] (the exact path stores them at their output rank).
+__device__ __forceinline__ int group_select(const FCtx& x, int r, int g, const FRow& f, uint32_t* off_out,
+                                            uint32_t* base_out) {
   KArgs& a = *x.a;
-  const int tid = lane_tid(), nsc = a.n_sc, L = a.lst;
-  const int c0 = g * a.cg < nsc ? g * a.cg : nsc, c1 = c0 + a.cg < nsc ? c0 + a.cg : nsc;
+  const int tid = lane_tid();
+  const int nsc = a.n_sc, L = a.lst, cgs = a.cg;
+  const int k_eff = (int)(f.n_vis < a.k ? f.n_vis : a.k);
+  const int c0 = g * cgs < nsc ? g * cgs : nsc, c1 = c0 + cgs < nsc ? c0 + cgs : nsc;
+  const uint32_t P0 = (uint32_t)(c0 * L), P1 = (uint32_t)(c1 * L), npos = (uint32_t)(nsc * L);
   int32_t* sel_s = reinterpret_cast<int32_t*>(x.smem + kOffSel);
-  uint32_t* e_n = row_hdrs(x);
-  uint64_t* ent_s = reinterpret_cast<uint64_t*>(x.smem + kOffLst);  // [chunk - c0][lst]
+  uint32_t* e_tau = row_taus(x);
+  uint32_t* hist = reinterpret_cast<uint32_t*>(x.smem + kOffHist);
+  if (g == 0) {
+    int32_t* idx_out = a.idx + (size_t)r * a.k;
+    for (int i = k_eff + tid; i < a.k; i += 256) idx_out[i] = -1;
+  }
+  *base_out = 0;
+  if (k_eff == 0) {  // nothing visible: every list is empty
+    *off_out = 0;
+    return 0;
+  }
+  // the row's lists: thread t holds positions u * 256 + t (keys and indices in
+  // registers), and the chunks' thresholds -> LDS
+  const v4u_t* lrow = a.lent + (size_t)r * npos;
+  const uint64_t* trow = a.ltau + (size_t)r * nsc;
+  uint32_t kv[kFEPT], ix[kFEPT];
+  uint32_t vm = 0;
   bool fail = false;
-  for (int sl = c0 + tid; sl < c1 && !fail; sl += 256)
-    e_n[sl - c0] = poll_word(x, a.ent_hdr + (size_t)r * nsc + sl, &fail, 2u) & 0xffffu;
+  {
+    v4u_t e[kFEPT];
+#pragma unroll
+    for (int u = 0; u < kFEPT; ++u) {
+      const uint32_t p = (uint32_t)(u * 256 + tid);
+      e[u] = p < npos ? coh_ld128(x.coh, lrow + p) : v4u_t{x.tag, kNoKey, x.tag, kNoKey};
+    }
+    uint64_t tw0 = tid < nsc ? coh_ld64(x.coh, trow + tid) : tagged(x.tag, 0u);
+    uint64_t tw1 = tid + 256 < nsc ? coh_ld64(x.coh, trow + tid + 256) : tagged(x.tag, 0u);
+    // entries not written yet are all read again together (one bounded retry loop)
+    for (uint32_t n = 0;;) {
+      bool late = (uint32_t)(tw0 >> 32) != x.tag || (uint32_t)(tw1 >> 32) != x.tag;
+#pragma unroll
+      for (int u = 0; u < kFEPT; ++u) late |= e[u][0] != x.tag || e[u][2] != x.tag;
+      if (!late) break;
+      if (++n >= kSpinLimit || ((n & 1023u) == 0 && error_seen(x))) {
+        if (n >= kSpinLimit) set_error(x, 2u);
+        fail = true;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+#pragma unroll
+      for (int u = 0; u < kFEPT; ++u)
+        if (e[u][0] != x.tag || e[u][2] != x.tag) e[u] = coh_ld128(x.coh, lrow + u * 256 + tid);
+      if ((uint32_t)(tw0 >> 32) != x.tag) tw0 = coh_ld64(x.coh, trow + tid);
+      if ((uint32_t)(tw1 >> 32) != x.tag) tw1 = coh_ld64(x.coh, trow + tid + 256);
+    }
+#pragma unroll
+    for (int u = 0; u < kFEPT; ++u) {
+      kv[u] = fail ? kNoKey : e[u][1];
+      ix[u] = e[u][3];
+      vm |= kv[u] != kNoKey ? (1u << u) : 0u;
+    }
+    if (tid < nsc) e_tau[tid] = (uint32_t)tw0;
+    if (tid + 256 < nsc) e_tau[tid + 256] = (uint32_t)tw1;
+  }
+  if (tid == 0) x.scr[S_BAD] = 0;
   if (!all_ok(x, fail)) return -1;
-  {  // the group's lists -> LDS (16-byte loads, 8 per thread in flight)
-    const uint64_t* gent = a.ent + ((size_t)r * nsc + c0) * L;
-    const int L2 = L >> 1;
-    const int npairs = (c1 - c0) * L2;
-    for (int q0 = 0; q0 < npairs; q0 += 256 * 8) {
-      v4u_t v[8];
+  uint32_t n_ent;
+  (void)block_exscan_val((uint32_t)__builtin_popcount(vm), x.scr, &n_ent);
+  bool exact = n_ent >= (uint32_t)k_eff;
+  uint32_t kstar = 0, gt_all = 0;
+  uint32_t* lk = reinterpret_cast<uint32_t*>(x.smem + kOffU);  // [npos] keys by position
+  uint32_t* li = lk + kFEntLds;                                 // [npos] indices by position
+  if (exact) {
+    if (npos <= 16u * 256u) {
+      uint32_t kv16[16];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int q = q0 + tid + 256 * u;
-        const int sl = q / L2, i = 2 * (q - sl * L2);
-        const bool use = q < npairs && (uint32_t)i < e_n[q < npairs ? sl : 0];
-        v[u] = use ? coh_ld128(x.coh, gent + (size_t)sl * L + i) : v4u_t{0u, 0u, 0u, 0u};
-      }
+      for (int u = 0; u < 16; ++u) kv16[u] = kv[u];
+      kstar = kth_key<16>(kv16, vm & 0xffffu, (uint32_t)k_eff, hist, x.scr, &gt_all);
+    } else {
+      kstar = kth_key<kFEPT>(kv, vm, (uint32_t)k_eff, hist, x.scr, &gt_all);
+    }
+    for (int sl = tid; sl < nsc; sl += 256)
+      if (e_tau[sl] > kstar) x.scr[S_BAD] = 1;
+    // to contiguous ownership (the histograms are free again): thread t takes
+    // positions [t*M, t*M + M), so position order is thread order
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int q = q0 + tid + 256 * u;
-        if (q >= npairs) continue;
-        const int sl = q / L2, i = 2 * (q - sl * L2);
-        const uint32_t cnt = e_n[sl];
-        if ((uint32_t)i < cnt) ent_s[sl * L + i] = (uint64_t)v[u][0] | ((uint64_t)v[u][1] << 32);
-        if ((uint32_t)i + 1 < cnt) ent_s[sl * L + i + 1] = (uint64_t)v[u][2] | ((uint64_t)v[u][3] << 32);
+    for (int u = 0; u < kFEPT; ++u) {
+      const uint32_t p = (uint32_t)(u * 256 + tid);
+      if (p < npos) {
+        lk[p] = kv[u];
+        li[p] = ix[u];
       }
+    }
+    __syncthreads();
+    exact = uni(x.scr[S_BAD]) == 0u;
+  }
+  if (exact) {
+    const uint32_t r_eq = (uint32_t)k_eff - gt_all;  // >= 1
+    constexpr uint32_t M = kFEPT;  // positions per thread (16-byte aligned runs)
+    const uint32_t m0 = (uint32_t)tid * M;
+    uint32_t ck[kFEPT], ci[kFEPT];
+#pragma unroll
+    for (int e4 = 0; e4 < kFEPT / 4; ++e4) {
+      const uint32_t q = m0 + 4u * (uint32_t)e4;
+      const uint4 kk = q < npos ? *reinterpret_cast<const uint4*>(lk + q) : make_uint4(kNoKey, kNoKey, kNoKey, kNoKey);
+      const uint4 ii = q < npos ? *reinterpret_cast<const uint4*>(li + q) : make_uint4(0u, 0u, 0u, 0u);
+      ck[4 * e4] = kk.x; ck[4 * e4 + 1] = kk.y; ck[4 * e4 + 2] = kk.z; ck[4 * e4 + 3] = kk.w;
+      ci[4 * e4] = ii.x; ci[4 * e4 + 1] = ii.y; ci[4 * e4 + 2] = ii.z; ci[4 * e4 + 3] = ii.w;
+    }
+    uint32_t cgt = 0, ceq = 0;
+#pragma unroll
+    for (int e = 0; e < kFEPT; ++e) {
+      cgt += ck[e] != kNoKey && ck[e] > kstar ? 1u : 0u;
+      ceq += ck[e] == kstar ? 1u : 0u;
+    }
+    uint32_t tot;
+    const uint32_t pre = block_exscan_val(cgt | (ceq << 16), x.scr, &tot);
+    const uint32_t pre_gt = pre & 0xffffu, pre_eq = pre >> 16;
+    if (pre_eq < r_eq && pre_eq + ceq >= r_eq) {  // this thread holds the r_eq-th entry equal to K*
+      uint32_t e2 = pre_eq, cut = 0;
+#pragma unroll
+      for (int e = 0; e < kFEPT; ++e)
+        if (ck[e] == kstar && ++e2 == r_eq) cut = m0 + (uint32_t)e;
+      x.scr[S_CUT] = cut;
+    }
+    __syncthreads();
+    const uint32_t pcut = uni(x.scr[S_CUT]);
+    // each taken entry's output rank: the taken entries before this thread,
+    // then its own in position order; the group's entries go to sel_s[rank]
+    uint32_t rank = pre_gt + (pre_eq < r_eq ? pre_eq : r_eq);
+#pragma unroll
+    for (int e = 0; e < kFEPT; ++e) {
+      const uint32_t p = m0 + (uint32_t)e;
+      if (p == P0) x.scr[S_OFF] = rank;
+      if (p == P1) x.scr[S_END] = rank;
+      const bool tk = ck[e] != kNoKey && (ck[e] > kstar || (ck[e] == kstar && p <= pcut));
+      if (tk && p >= P0 && p < P1) sel_s[rank] = (int32_t)ci[e];
+      rank += tk ? 1u : 0u;
+    }
+    if (tid == 0 && P1 >= npos) x.scr[S_END] = (uint32_t)k_eff;
+    __syncthreads();
+    const uint32_t off = uni(x.scr[S_OFF]);
+    *off_out = off;
+    *base_out = off;
+    return (int)(uni(x.scr[S_END]) - off);
+  }
+  // not decidable from the lists: the exact selection over the stored keys
+  if (g == 0 && !row_fallback(x, r, f, k_eff)) return -1;
+  uint32_t w3[3];
+  {
+    const uint64_t* const pw[3] = {a.row_k + r, a.row_cut + r, a.grp_off + (size_t)r * a.n_cs_sel + g};
+    const bool use[3] = {true, true, true};
+    if (tid == 0) {
+      read_tagged<3>(x, pw, use, w3, &fail);
+      x.scr[S_KEY] = w3[0];
+      x.scr[S_CUT] = w3[1];
+      x.scr[S_DIGIT] = w3[2];
     }
   }
-  // the row's threshold
-  if (tid == 0) {
-    x.scr[S_KEY] = poll_word(x, a.row_k + r, &fail, 16u);
-    if (!fail) x.scr[S_CUT] = poll_word(x, a.row_cut + r, &fail, 16u);
-  }
   if (!all_ok(x, fail)) return -1;
-  const uint32_t kstar = uni(x.scr[S_KEY]), cut = uni(x.scr[S_CUT]);
-  uint32_t tot;
-  if ((cut >> 31) == 0u) {
-    // listed entries above K*, and ties at positions up to cut
-    const uint32_t npos = (uint32_t)((c1 - c0) * L), base = (uint32_t)(c0 * L);
-    const uint32_t M = (npos + 255) >> 8, m0 = (uint32_t)tid * M;
-    auto take = [&](uint32_t p, uint64_t* e) {
-      if (p >= npos) return false;
-      const uint32_t sl = p / (uint32_t)L;
-      if (p - sl * (uint32_t)L >= e_n[sl]) return false;
-      *e = ent_s[p];
-      const uint32_t key = (uint32_t)(*e >> 32);
-      return key > kstar || (key == kstar && base + p <= cut);
-    };
-    uint32_t cnt = 0;
-    for (uint32_t i = 0; i < M; ++i) {
-      uint64_t e;
-      cnt += take(m0 + i, &e) ? 1u : 0u;
-    }
-    uint32_t pos = block_exscan_val(cnt, x.scr, &tot);
-    for (uint32_t i = 0; i < M; ++i) {
-      uint64_t e;
-      if (take(m0 + i, &e)) sel_s[pos++] = (int32_t)(uint32_t)e;
-    }
-  } else {
-    // fallback: the order key (key, ~index) of every visible entry of the group's chunks
-    bool kfail = false;
-    for (int sl = c0 + tid; sl < c1 && !kfail; sl += 256) (void)poll_word(x, a.key_hdr + (size_t)r * nsc + sl, &kfail, 64u);
-    if (!all_ok(x, kfail)) return -1;
-    const uint64_t cstar = ((uint64_t)kstar << 32) | (uint32_t)~(cut & 0x3ffffu);
-    const uint32_t* rowkeys = a.keys + (size_t)r * a.key_stride;
-    const uint32_t C = (uint32_t)a.C, nvis = n_vis_u32(f);
-    const uint32_t jb = (uint32_t)c0 * C, je = (uint32_t)c1 * C < nvis ? (uint32_t)c1 * C : nvis;
-    const uint32_t n = je > jb ? je - jb : 0u;
-    const uint32_t M = (n + 255) >> 8, m0 = (uint32_t)tid * M;
-    uint32_t cnt = 0;
-    for (uint32_t i = 0; i < M; ++i) {
-      const uint32_t j = jb + m0 + i;
-      if (m0 + i < n) cnt += (((uint64_t)coh_ld32(x.coh, rowkeys + j) << 32) | (uint32_t)~j) >= cstar ? 1u : 0u;
-    }
-    uint32_t pos = block_exscan_val(cnt, x.scr, &tot);
-    for (uint32_t i = 0; i < M; ++i) {
-      const uint32_t j = jb + m0 + i;
-      if (m0 + i < n && (((uint64_t)coh_ld32(x.coh, rowkeys + j) << 32) | (uint32_t)~j) >= cstar)
-        sel_s[pos++] = (int32_t)j;
-    }
+  const uint32_t kstar_f = uni(x.scr[S_KEY]), jstar = uni(x.scr[S_CUT]);
+  *off_out = uni(x.scr[S_DIGIT]);
+  // the order key (key, ~index) of every visible entry of the group's chunks
+  bool kfail = false;
+  for (int sl = c0 + tid; sl < c1 && !kfail; sl += 256) (void)poll_word(x, a.key_hdr + (size_t)r * nsc + sl, &kfail, 64u);
+  if (!all_ok(x, kfail)) return -1;
+  const uint64_t cstar = ((uint64_t)kstar_f << 32) | (uint32_t)~jstar;
+  const uint32_t* rowkeys = a.keys + (size_t)r * a.key_stride;
+  const uint32_t C = (uint32_t)a.C, nvis = n_vis_u32(f);
+  const uint32_t jb = (uint32_t)c0 * C, je = (uint32_t)c1 * C < nvis ? (uint32_t)c1 * C : nvis;
+  const uint32_t n = je > jb ? je - jb : 0u;
+  const uint32_t M = (n + 255) >> 8, m0 = (uint32_t)tid * M;
+  uint32_t cntf = 0, tot;
+  for (uint32_t i = 0; i < M; ++i) {
+    const uint32_t j = jb + m0 + i;
+    if (m0 + i < n) cntf += (((uint64_t)coh_ld32(x.coh, rowkeys + j) << 32) | (uint32_t)~j) >= cstar ? 1u : 0u;
+  }
+  uint32_t pos = block_exscan_val(cntf, x.scr, &tot);
+  for (uint32_t i = 0; i < M; ++i) {
+    const uint32_t j = jb + m0 + i;
+    if (m0 + i < n && (((uint64_t)coh_ld32(x.coh, rowkeys + j) << 32) | (uint32_t)~j) >= cstar)
+      sel_s[pos++] = (int32_t)j;
   }
   __syncthreads();
   return (int)tot;
 }
 
-// the group's selected indices -> idx at the offset the row selection published
-__device__ __forceinline__ bool group_write_idx(const FCtx& x, int r, int g, int n_sel) {
+// the group's selected indices -> idx at its output offset
+__device__ __forceinline__ void group_write_idx(const FCtx& x, int r, uint32_t off, int n_sel, uint32_t base) {
   KArgs& a = *x.a;
   const int tid = lane_tid();
-  bool fail = false;
-  if (tid == 0) x.scr[S_KEY] = poll_word(x, a.grp_off + (size_t)r * a.n_cs_sel + g, &fail, 32u);
-  if (!all_ok(x, fail)) return false;
-  const uint32_t off = uni(x.scr[S_KEY]);
-  const int32_t* sel_s = reinterpret_cast<const int32_t*>(x.smem + kOffSel);
+  const int32_t* sel_s = reinterpret_cast<const int32_t*>(x.smem + kOffSel) + base;
   int32_t* dst = a.idx + (size_t)r * a.k + off;
   for (int i = tid; i < n_sel && off + (uint32_t)i < (uint32_t)a.k; i += 256) dst[i] = sel_s[i];
-  return true;
 }
 
 // Attention item: CSA group (kind 0, its n_sel selected rows in LDS), CSA
 // window split (kind 1) or HCA split (kind 2) of row r, then its partial.
-__device__ __forceinline__ void attend_item(const FCtx& x, int r, int kind, int s, const FRow& f, int n_sel) {
+__device__ __forceinline__ void attend_item(const FCtx& x, int r, int kind, int s, const FRow& f, int n_sel,
+                                            uint32_t sel_base = 0) {
   KArgs& a = *x.a;
   int64_t p_begin, p_end;
   int pi = s;
@@ -930,7 +905,7 @@ __device__ __forceinline__ void attend_item(const FCtx& x, int r, int kind, int 
     p_begin = (int64_t)s * a.hs;
     p_end = p_begin + a.hs < list_len ? p_begin + a.hs : list_len;
   }
-  const int32_t* idx_s = reinterpret_cast<const int32_t*>(x.smem + kOffSel);
+  const int32_t* idx_s = reinterpret_cast<const int32_t*>(x.smem + kOffSel) + sel_base;
   constexpr uint64_t RB = 2 * 128 * 2;
   // Row addresses from 32-bit offsets against per-row bases: list positions
   // below `split` are pooled rows (selected ones for kind 0, HCA rows for
@@ -971,49 +946,37 @@ __device__ __forceinline__ void item_merge(const FCtx& x, bool hca, int r, int h
   const float* pml = hca ? a.hca_pml : a.csa_pml;
   uint8_t* out = hca ? a.hca_out : a.csa_out;
   float* lse = hca ? a.hca_lse : a.csa_lse;
-  // (m, l) of every split for the 4 heads -> LDS [4][n]
-  uint2* ml_s = reinterpret_cast<uint2*>(x.smem + kOffU);
-  for (int q0 = 0; q0 < 4 * n; q0 += 256 * 8) {
-    uint64_t v[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int q = q0 + tid + 256 * u;
-      v[u] = q < 4 * n ? coh_ld64(x.coh, pml + (((size_t)r * n + (q >> 2)) * a.H + h0 + (q & 3)) * 2) : 0ull;
-    }
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int q = q0 + tid + 256 * u;
-      if (q < 4 * n) ml_s[(q & 3) * n + (q >> 2)] = make_uint2((uint32_t)v[u], (uint32_t)(v[u] >> 32));
-    }
-  }
-  __syncthreads();
+  // every split's (m, l) of this thread's head and its two output values, all
+  // loaded at once (one round of loads per 24 splits), merged online
   const int hh = tid >> 6, h = h0 + hh, d = (tid & 63) * 2;
-  const uint2* mlh = ml_s + hh * n;
-  float M = -INFINITY;
-  for (int s = 0; s < n; ++s) M = fmaxf(M, __uint_as_float(mlh[s].x));
-  float L = 0.f, acc0 = 0.f, acc1 = 0.f;
-  if (M != -INFINITY) {
-    for (int s0 = 0; s0 < n; s0 += 32) {
-      uint64_t ov[32];
+  constexpr int SB = 24;
+  float M = -INFINITY, L = 0.f, acc0 = 0.f, acc1 = 0.f;
+  for (int s0 = 0; s0 < n; s0 += SB) {
+    uint64_t mlv[SB], ov[SB];
 #pragma unroll
-      for (int u = 0; u < 32; ++u) {
-        const int s = s0 + u;
-        ov[u] = s < n && __uint_as_float(mlh[s].x) != -INFINITY
-                    ? coh_ld64(x.coh, po + (((size_t)r * n + s) * a.H + h) * 128 + d)
-                    : 0ull;
-      }
-#pragma unroll
-      for (int u = 0; u < 32; ++u) {
-        const int s = s0 + u;
-        if (s >= n) continue;
-        const float ms = __uint_as_float(mlh[s].x);
-        if (ms == -INFINITY) continue;
-        const float wgt = fast_exp2(ms - M);
-        L = fmaf(wgt, __uint_as_float(mlh[s].y), L);
-        acc0 = fmaf(wgt, __uint_as_float((uint32_t)ov[u]), acc0);
-        acc1 = fmaf(wgt, __uint_as_float((uint32_t)(ov[u] >> 32)), acc1);
-      }
+    for (int u = 0; u < SB; ++u) {
+      const int s = s0 + u;
+      const size_t pb = ((size_t)r * n + s) * a.H + h;
+      mlv[u] = s < n ? coh_ld64(x.coh, pml + pb * 2) : (uint64_t)__float_as_uint(-INFINITY);
+      ov[u] = s < n ? coh_ld64(x.coh, po + pb * 128 + d) : 0ull;
     }
+    float Mc = M;
+#pragma unroll
+    for (int u = 0; u < SB; ++u) Mc = fmaxf(Mc, __uint_as_float((uint32_t)mlv[u]));
+    if (Mc == -INFINITY) continue;
+    const float sc = M == -INFINITY ? 0.f : fast_exp2(M - Mc);
+    L *= sc;
+    acc0 *= sc;
+    acc1 *= sc;
+#pragma unroll
+    for (int u = 0; u < SB; ++u) {
+      const float ms = __uint_as_float((uint32_t)mlv[u]);
+      const float wgt = ms == -INFINITY ? 0.f : fast_exp2(ms - Mc);
+      L = fmaf(wgt, __uint_as_float((uint32_t)(mlv[u] >> 32)), L);
+      acc0 = fmaf(wgt, __uint_as_float((uint32_t)ov[u]), acc0);
+      acc1 = fmaf(wgt, __uint_as_float((uint32_t)(ov[u] >> 32)), acc1);
+    }
+    M = Mc;
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
   uint32_t* o = reinterpret_cast<uint32_t*>(out + (((size_t)r * a.H + h) * 128 + d) * 2);
@@ -1030,10 +993,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   const uint32_t tag0 = ld_dev(a.ctl + W_EPOCH) + 1u;
   const uint32_t tag = tag0 == 0u ? 1u : tag0;
   const int rounds = a.rounds;
-  // Work units in dependency order: [score chunks | row selections | CSA groups
-  // | CSA window splits | HCA splits | HCA merges | CSA merges].  The score
-  // chunks stream first on every workgroup; the HCA stream then runs beside the
-  // latency-bound selection chain on a limited number of workgroups.  Units
+  // Work units in dependency order: [score chunks | CSA groups | CSA window
+  // splits | HCA splits | HCA merges | CSA merges].  The score chunks stream
+  // first on every workgroup; the HCA stream then runs beside the
+  // latency-bound selection chain.  Units
   // are handed out in that order, the first grid-size ones by workgroup id
   // (workgroups are dispatched in id order) and the rest through one returning
   // atomic, and a unit only waits for units of lower number, whose holders are
@@ -1047,7 +1010,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     KArgs& A = *ap;
     const FCtx x{ap, smem, scr, tag, make_coh(A.ctl)};
     const int R = A.R, nM = A.H / 4;
-    const int64_t u_sel = (int64_t)R * A.n_sc, u_grp = u_sel + R;
+    const int64_t u_grp = (int64_t)R * A.n_sc;
     const int64_t u_win = u_grp + (int64_t)R * A.n_cs_sel, u_hca = u_win + (int64_t)R * A.n_cs_win;
     const int64_t u_mh = u_hca + (int64_t)R * A.n_hs, u_mc = u_mh + (int64_t)R * nM;
     const int64_t total = u_mc + (int64_t)R * nM;
@@ -1061,16 +1024,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     }
     if (it >= total) {
       // nothing to do this round
-    } else if (it < u_sel) {
+    } else if (it < u_grp) {
       const int r = (int)(it / A.n_sc), c = (int)(it % A.n_sc);
       const FRow f = row_info(A, r);
       int64_t j0 = (int64_t)c * A.C, j1 = j0 + A.C;
       if (j1 > f.n_vis) j1 = f.n_vis;
       if (j0 > j1) j0 = j1;
       phase_score(x, r, c, f, j0, j1);
-    } else if (it < u_grp) {
-      const int r = (int)(it - u_sel);
-      (void)select_row(x, r, row_info(A, r));
     } else if (it >= u_mh) {
       const bool hca = it < u_mc;
       const int64_t m = it - (hca ? u_mh : u_mc);
@@ -1079,10 +1039,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
       const int64_t q = it - u_grp;
       const int r = (int)(q % R), g = (int)(q / R);
       const FRow f = row_info(A, r);
-      const int n_sel = group_select(x, r, g, f);
+      uint32_t off = 0, base = 0;
+      const int n_sel = group_select(x, r, g, f, &off, &base);
       if (n_sel >= 0) {
-        attend_item(x, r, 0, g, f, n_sel);
-        (void)group_write_idx(x, r, g, n_sel);
+        attend_item(x, r, 0, g, f, n_sel, base);
+        group_write_idx(x, r, off, n_sel, base);
       }
     } else {
       // attention: kind 1 = CSA window split, 2 = HCA split
@@ -1176,10 +1137,8 @@ FusedPlan plan_fused(int64_t R, int64_t max_pool, int64_t max_hpool, int H, int 
   s += al(W_CTL * 4);
   s += al((size_t)R * p.key_stride * 4);
   s += al(slots * 8);
+  s += al(slots * p.lst * 16);
   s += al(slots * 8);
-  s += al(slots * p.lst * 8);
-  s += al(slots * p.lst * 4);
-  s += al(slots * 4);
   s += al((size_t)R * 8);
   s += al((size_t)R * 8);
   s += al((size_t)R * p.n_cs_sel * 8);
@@ -1232,17 +1191,15 @@ int launch_fused(int R, const int64_t* tok_off, const int64_t* q_pos, const int6
   a.hs = pl.hs; a.n_hs = pl.n_hs;
   a.lst_min = pl.lst_min; a.lst = pl.lst; a.key_stride = pl.key_stride;
   {
-    const int64_t units = (int64_t)R * pl.n_sc + R + (int64_t)R * (pl.n_cs_sel + pl.n_cs_win + pl.n_hs) +
+    const int64_t units = (int64_t)R * pl.n_sc + (int64_t)R * (pl.n_cs_sel + pl.n_cs_win + pl.n_hs) +
                           2 * (int64_t)R * (H / 4);
     a.rounds = (int)((units + pl.grid - 1) / pl.grid);
   }
   a.ctl = (uint32_t*)take(W_CTL * 4);
   a.keys = (uint32_t*)take((size_t)R * pl.key_stride * 4);
-  a.ent_hdr = (uint64_t*)take(slots * 8);
   a.key_hdr = (uint64_t*)take(slots * 8);
-  a.ent = (uint64_t*)take(slots * pl.lst * 8);
-  a.lkey = (uint32_t*)take(slots * pl.lst * 4);
-  a.ltau = (uint32_t*)take(slots * 4);
+  a.lent = (v4u_t*)take(slots * pl.lst * 16);
+  a.ltau = (uint64_t*)take(slots * 8);
   a.row_k = (uint64_t*)take((size_t)R * 8);
   a.row_cut = (uint64_t*)take((size_t)R * 8);
   a.grp_off = (uint64_t*)take((size_t)R * pl.n_cs_sel * 8);
