@@ -67,7 +67,7 @@ constexpr int kOffHist = kOffU + kFEntLds * 4;              // uint32 [2][kFHist
 constexpr int kSelEnd = kOffHist + (2 * kFHist + 64) * 4;
 constexpr int kAttnEnd = kOffU + kAttnLdsBytes;
 constexpr int kFusedLds = kSelEnd > kAttnEnd ? kSelEnd : kAttnEnd;
-static_assert(kOffSel + kFMaxSel * 4 <= kOffScr, "a group's selected rows fit the key region");
+static_assert(kOffSel + (kFMaxSel + 64) * 4 <= kOffScr, "a group's selected rows (+ 64 dummy slots) fit the key region");
 static_assert(kOffU % 16 == 0 && kOffHist % 16 == 0, "LDS regions must be 16-byte aligned");
 static_assert(kFMaxC * 8 <= kAttnLdsBytes, "a score chunk's staged list fits the union region");
 static_assert(2 * kFEntLds * 4 <= kAttnLdsBytes, "a row's keys and indices by position fit the union region");
@@ -799,10 +799,13 @@ __device__ __forceinline__ int group_select(const FCtx& x, int r, int g, const F
       ck[4 * e4] = kk.x; ck[4 * e4 + 1] = kk.y; ck[4 * e4 + 2] = kk.z; ck[4 * e4 + 3] = kk.w;
       ci[4 * e4] = ii.x; ci[4 * e4 + 1] = ii.y; ci[4 * e4 + 2] = ii.z; ci[4 * e4 + 3] = ii.w;
     }
+    // empty positions hold kNoKey, which is -1 as a signed value: below every
+    // key (finite scores are >= 0) and never equal to K*
+    const int32_t ks = (int32_t)kstar;
     uint32_t cgt = 0, ceq = 0;
 #pragma unroll
     for (int e = 0; e < kFEPT; ++e) {
-      cgt += ck[e] != kNoKey && ck[e] > kstar ? 1u : 0u;
+      cgt += (int32_t)ck[e] > ks ? 1u : 0u;
       ceq += ck[e] == kstar ? 1u : 0u;
     }
     uint32_t tot;
@@ -819,16 +822,20 @@ __device__ __forceinline__ int group_select(const FCtx& x, int r, int g, const F
     const uint32_t pcut = uni(x.scr[S_CUT]);
     // each taken entry's output rank: the taken entries before this thread,
     // then its own in position order; the group's entries go to sel_s[rank]
-    uint32_t rank = pre_gt + (pre_eq < r_eq ? pre_eq : r_eq);
+    const uint32_t rank0 = pre_gt + (pre_eq < r_eq ? pre_eq : r_eq);
+    uint32_t rank = rank0, tkm = 0;
+    int32_t* const dummy = sel_s + kFMaxSel + (tid & 63);  // the stores of entries not taken
 #pragma unroll
     for (int e = 0; e < kFEPT; ++e) {
       const uint32_t p = m0 + (uint32_t)e;
-      if (p == P0) x.scr[S_OFF] = rank;
-      if (p == P1) x.scr[S_END] = rank;
-      const bool tk = ck[e] != kNoKey && (ck[e] > kstar || (ck[e] == kstar && p <= pcut));
-      if (tk && p >= P0 && p < P1) sel_s[rank] = (int32_t)ci[e];
-      rank += tk ? 1u : 0u;
+      const uint32_t tk = ((int32_t)ck[e] > ks ? 1u : 0u) | (ck[e] == kstar && p <= pcut ? 1u : 0u);
+      const bool mine = tk != 0u && p >= P0 && p < P1;
+      *(mine ? sel_s + rank : dummy) = (int32_t)ci[e];
+      tkm |= tk << e;
+      rank += tk;
     }
+    if (P0 - m0 < M) x.scr[S_OFF] = rank0 + (uint32_t)__builtin_popcount(tkm & ((1u << (P0 - m0)) - 1u));
+    if (P1 - m0 < M) x.scr[S_END] = rank0 + (uint32_t)__builtin_popcount(tkm & ((1u << (P1 - m0)) - 1u));
     if (tid == 0 && P1 >= npos) x.scr[S_END] = (uint32_t)k_eff;
     __syncthreads();
     const uint32_t off = uni(x.scr[S_OFF]);
@@ -996,14 +1003,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   // Work units in dependency order: [score chunks | CSA groups | CSA window
   // splits | HCA splits | HCA merges | CSA merges].  The score chunks stream
   // first on every workgroup; the HCA stream then runs beside the
-  // latency-bound selection chain.  Units
-  // are handed out in that order, the first grid-size ones by workgroup id
-  // (workgroups are dispatched in id order) and the rest through one returning
-  // atomic, and a unit only waits for units of lower number, whose holders are
-  // already running: every wait ends whatever the residency of the grid.
-  // Every workgroup runs the same number of rounds (rounds * grid >= total), so
-  // the loop bound is uniform; a round whose unit number is past the end (or
-  // that follows a reported error) does nothing.
+  // latency-bound selection chain.  Units are handed out in that order, the
+  // first grid-size ones by workgroup id and the rest through one returning
+  // atomic, claimed one round ahead; a workgroup runs its units in the order
+  // it claimed them, and a unit only waits for units of lower number.  The
+  // lowest unfinished unit therefore never waits, and its workgroup is either
+  // running it or running a unit of lower number still: every wait ends,
+  // whatever the residency of the grid.  Every workgroup runs the same number
+  // of rounds (rounds * grid >= total), so the loop bound is uniform; a round
+  // whose unit number is past the end does nothing.
+  uint32_t next_ticket = 0;  // lane 0: the unit number of the next round, fetched one round ahead
   for (int round = 0; round < rounds; ++round) {
     KArgs* ap = (KArgs*)__builtin_amdgcn_kernarg_segment_ptr();
     asm volatile("" : "+s"(ap));
@@ -1016,12 +1025,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     const int64_t total = u_mc + (int64_t)R * nM;
     int64_t it = (int64_t)blockIdx.x;
     if (round > 0) {
-      if (lane_tid() == 0)
-        scr[S_TICKET] = error_seen(x) ? 0xffffffffu : (uint32_t)gridDim.x + atomicAdd(A.ctl + W_TICKET, 1u);
+      if (lane_tid() == 0) scr[S_TICKET] = (uint32_t)gridDim.x + next_ticket;
       __syncthreads();
       it = uni(scr[S_TICKET]);
       __syncthreads();
     }
+    // claim the next round's unit now: the returning atomic's latency overlaps
+    // this round's work.  A workgroup still runs its units in claim order.
+    if (round + 1 < rounds && lane_tid() == 0) next_ticket = atomicAdd(A.ctl + W_TICKET, 1u);
     if (it >= total) {
       // nothing to do this round
     } else if (it < u_grp) {
