@@ -43,7 +43,7 @@ namespace csa {
 
 constexpr int kPfRowsT = 8;        // queries per threshold block (one MFMA A operand)
 constexpr int kPfRows = 16;        // queries per score block (two MFMA A operands)
-constexpr int kPfKeysWG = 2048;    // keys per scoring workgroup
+constexpr int kPfKeysWG = 4096;    // keys per scoring workgroup, at least (a multiple of 128)
 constexpr int kPfSampleMax = 2048;  // sample keys per query
 constexpr int kPfCand = 2048;      // candidates per query held in a wave's LDS
 constexpr int kPfBins = 1024;      // wave radix-select bins
@@ -55,6 +55,7 @@ struct PfArgs {
   const int64_t* q_pos;
   const int64_t* pool_off;
   int n_seq, bps, bps_t, m, k, stride, ns_max, bw;
+  int kw;  // keys per scoring workgroup (a multiple of 128: 32-key tiles, 4 waves)
   int64_t n_q, max_pool;
   const uint8_t* q_codes;
   const uint8_t* q_scales;
@@ -313,7 +314,7 @@ __global__ __launch_bounds__(256) void k_pf_score(PfArgs a) {
   const int nrows = (int)(row0 >= row_end ? 0 : (row_end - row0 < kPfRows ? row_end - row0 : kPfRows));
   if (nrows == 0) return;
   const int64_t pbase = a.pool_off[b], P = a.pool_off[b + 1] - pbase;
-  const int64_t jr0 = (int64_t)blockIdx.x * kPfKeysWG;
+  const int64_t jr0 = (int64_t)blockIdx.x * a.kw;
   // this lane's 16 queries: slot 8u + 2s + lane/32 of A operand u, score index s
   constexpr int kE = kPfRows / 2;
   uint32_t tq[kE];
@@ -342,8 +343,8 @@ __global__ __launch_bounds__(256) void k_pf_score(PfArgs a) {
   for (int u = 0; u < kPfRows / 8; ++u) pf_load_a(a, row0 + 8 * u, nrows - 8 * u, lane, av[u], asc[u]);
   // word lane L < kPfRows holds the bits of query L (= 8u + 2s + h for ballot (u, s), half h)
   uint32_t* bm_row = a.bitmap + (size_t)(row0 + ((lane & 31) < nrows ? (lane & 31) : 0)) * a.bw;
-  constexpr int kT = kPfKeysWG / 32 / 4;  // tiles per wave
-  constexpr int kB = 8;                   // tiles per wave in flight
+  const int kT = a.kw / 32 / 4;  // tiles per wave
+  constexpr int kB = 8;          // tiles per wave in flight
 #pragma unroll 1
   for (int ub = 0; ub < kT; ub += kB) {
     uint4 kc[kB];
@@ -351,12 +352,12 @@ __global__ __launch_bounds__(256) void k_pf_score(PfArgs a) {
 #pragma unroll
     for (int u = 0; u < kB; ++u) {
       const int64_t j = jr0 + (int64_t)(wave + 4 * (ub + u)) * 32 + (lane & 31);
-      pf_load_b(a, pbase + j, j < nvis_max, kb, kc[u], ks[u]);
+      pf_load_b(a, pbase + j, ub + u < kT && j < nvis_max, kb, kc[u], ks[u]);
     }
 #pragma unroll
     for (int u = 0; u < kB; ++u) {
       const int64_t jt = jr0 + (int64_t)(wave + 4 * (ub + u)) * 32;
-      if (jt >= nvis_max) break;
+      if (ub + u >= kT || jt >= nvis_max) break;
       const int j = (int)jt + (lane & 31);
       const bool whole = jt + 32 <= (int64_t)nmin;  // every query sees the whole tile
       static_assert(kPfRows == 16, "two MFMA A operands");
@@ -560,6 +561,40 @@ __global__ __launch_bounds__(128) void k_pf_select(PfArgs a) {
 // ---------------------------------------------------------------------------
 int prefill_path(int64_t max_q_per_seq) { return max_q_per_seq >= kPfMinQ ? 1 : 0; }
 
+// keys per scoring workgroup: the grid (key blocks x query blocks) is sized to
+// a whole number of rounds of resident workgroups, so no last round runs the
+// chip partly empty
+static int pf_keys_per_wg(int64_t max_pool, int64_t qblocks) {
+  static int capacity = 0;
+  if (capacity == 0) {
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)k_pf_score, 256, 0) == hipSuccess &&
+        cus > 0 && per_cu > 0)
+      capacity = cus * per_cu;
+    else
+      capacity = 1024;
+  }
+  const int64_t quads = (max_pool + 127) / 128;  // 128-key units
+  if (quads <= 0 || qblocks <= 0) return kPfKeysWG;
+  // fewest key blocks that reach a whole round, then as many rounds as keep >= kPfKeysWG keys per block
+  int64_t rounds = 1;
+  for (;;) {
+    const int64_t nx = (rounds * capacity + qblocks - 1) / qblocks;
+    const int64_t per = (quads + nx - 1) / nx;
+    if (per * 128 < kPfKeysWG || nx >= quads) break;
+    const int64_t nx2 = ((rounds + 1) * capacity + qblocks - 1) / qblocks;
+    const int64_t per2 = (quads + nx2 - 1) / nx2;
+    if (per2 * 128 < kPfKeysWG) break;
+    ++rounds;
+  }
+  const int64_t nx = (rounds * capacity + qblocks - 1) / qblocks;
+  int64_t per = (quads + nx - 1) / nx;
+  if (per < 1) per = 1;
+  return (int)(per * 128);
+}
+
 static int pf_stride(int64_t max_pool) {
   int64_t s = (max_pool + kPfSampleMax - 1) / kPfSampleMax;
   return (int)(s < 16 ? 16 : s);
@@ -605,7 +640,8 @@ int launch_prefill_topk(int n_seq, int64_t n_q, int64_t max_q_per_seq, const int
   prof_begin(7, stream);
   hipLaunchKernelGGL(k_pf_thresh, dim3((unsigned)(n_seq * a.bps_t)), dim3(256), lds1, stream, a);
   prof_end(7, stream);
-  dim3 g2((unsigned)((max_pool + kPfKeysWG - 1) / kPfKeysWG), nblk);
+  a.kw = pf_keys_per_wg(max_pool, (int64_t)nblk);
+  dim3 g2((unsigned)((max_pool + a.kw - 1) / a.kw), nblk);
   if (g2.x == 0) g2.x = 1;
   prof_begin(0, stream);
   hipLaunchKernelGGL(k_pf_score, g2, dim3(256), 0, stream, a);
