@@ -267,6 +267,12 @@ def main():
         "compress": compress,
     }
 
+    # ---- streaming cache upkeep (appends at the end of the 1M-token caches) -----
+    try:
+        result["cache_append"] = bench_cache_append(torch, csa, layer, wl, host, log)
+    except Exception as e:  # reported, never silently replaced
+        result["cache_append"] = {"error": repr(e)}
+
     # ---- prefill indexer (4096-token chunk on a 64K cache) ----------------------
     if not args.no_prefill:
         try:
@@ -332,6 +338,56 @@ def counted_traffic(kernel: str, workload: str):
                     return None
                 return int(rec["traffic_bytes_per_launch"])
     return None
+
+
+def bench_cache_append(torch, csa, layer, wl, host, log, reps: int = 50):
+    """csa_cache_append at the end of the resident 1M-token caches: (a) one
+    decode step, one new token for each of the 4 sequences, each completing a
+    CSA and an HCA block; (b) a 4096-token chunk on one sequence.  The appended
+    rows are the caches' own last rows, so every call rewrites identical data;
+    lengths and tail rings are reset between calls, outside the timed region
+    (HIP events around the call's two kernels, on their stream)."""
+    dev = "cuda"
+    B, L = wl.B, np.array(wl.lengths, dtype=np.int64)
+    tok_off = host["tok_off"]
+    ring = wl.m_hca
+    es = 2 if wl.dtype == "bf16" else 4
+    row = 2 * wl.d * es
+    cases = {"decode_step": np.ones(B, dtype=np.int64),
+             "prefill_chunk": np.array([4096] + [0] * (B - 1), dtype=np.int64)}
+    out = {}
+    for name, n in cases.items():
+        L0 = L - n
+        rows = np.concatenate([np.arange(tok_off[b] + L0[b], tok_off[b] + L[b]) for b in range(B)]).astype(np.int64)
+        r = torch.from_numpy(rows).to(dev)
+        x_new, z_new = layer.kv[r].contiguous(), layer.z[r].contiguous()
+        new_off = torch.from_numpy(np.concatenate([[0], np.cumsum(n)]).astype(np.int64)).to(dev)
+        tail_rows = np.array([[tok_off[b] + (p if p >= 0 else 0) for p in
+                               [L0[b] - ring + ((s - (L0[b] - ring)) % ring) for s in range(ring)]]
+                              for b in range(B)], dtype=np.int64)
+        tail0 = layer.z[torch.from_numpy(tail_rows.reshape(-1)).to(dev)].reshape(B, ring, 2, wl.d).contiguous()
+        len0 = torch.from_numpy(L0).to(dev)
+        length, z_tail = len0.clone(), tail0.clone()
+        args = (x_new, z_new, new_off, int(n.max()), layer.tok_off, length, layer.kv, z_tail, layer.pool_off, wl.m,
+                layer.pooled, layer.hpool_off, wl.m_hca, layer.hpooled)
+        csa.csa_cache_append(*args)
+        torch.cuda.synchronize()
+        ev = [(csa.HipEvent(), csa.HipEvent()) for _ in range(reps)]
+        for i in range(reps):
+            length.copy_(len0)
+            z_tail.copy_(tail0)
+            csa.csa_profile_events(csa.CSA_K_APPEND, ev[i][0], ev[i][1])
+            csa.csa_cache_append(*args)
+            csa.csa_profile_events(csa.CSA_K_APPEND)
+        torch.cuda.synchronize()
+        us = float(np.mean([a.elapsed_ms(b) for a, b in ev])) * 1e3
+        blocks = int(((L // wl.m) - (L0 // wl.m)).sum() + ((L // wl.m_hca) - (L0 // wl.m_hca)).sum())
+        # new rows in (values and logits), raw rows out, ring rows out, pooled rows out
+        nbytes = int(n.sum()) * 3 * row + int(np.minimum(n, ring).sum()) * row + blocks * row
+        out[name] = {"tokens": int(n.sum()), "blocks_pooled": blocks, "us": round(us, 2),
+                     "bytes": nbytes, "GB/s": round(nbytes / (us * 1e-6) / 1e9, 1)}
+    log(f"cache append: {out}")
+    return out
 
 
 def bench_prefill_indexer(torch, csa, synth, to_device, log, reps: int = 10):

@@ -103,6 +103,39 @@ int csa_compress(int dtype, int32_t n_seq, const int64_t* tok_off, const int64_t
                  void* stream);
 
 /* ------------------------------------------------------------------------
+ * csa_cache_append — streaming cache upkeep: append each sequence's new
+ * tokens and pool every block the append completes.
+ * Pages: sigco.tistory.com KV-cache section (the cache is split into the
+ * compressed entries CSA/HCA read, the recent tokens the sliding window reads,
+ * and the state of the tail tokens not yet numerous enough to compress);
+ * pooling rule as csa_compress.  For sequence b with L = len[b] tokens cached
+ * and n = new_off[b+1] - new_off[b] new ones:
+ *   - raw row tok_off[b] + L + i <- x_new row new_off[b] + i   (i < n); the
+ *     raw rows [tok_off[b], tok_off[b+1]) are the sequence's capacity and the
+ *     window reads the last W of them;
+ *   - every block j of m tokens with L < (j+1)*m <= L + n is pooled into
+ *     pooled row pool_off[b] + j, and likewise every block of m_hca tokens
+ *     into hpooled row hpool_off[b] + j (m_hca = 0: no HCA pooling); the rows
+ *     are bit-identical to csa_compress over the whole sequence;
+ *   - the tail state z_tail [n_seq][ring][width] keeps the pooling logits of
+ *     the latest `ring` tokens (token p at slot p % ring): it must hold them
+ *     for the tokens cached so far before the call, and does after it;
+ *   - len[b] += n.
+ * x_new, z_new [sum n][width] (values; pooling logits) in `dtype`; kv_raw
+ * [capacity][width]; pooled / hpooled [rows][width].  Writes past a
+ * sequence's raw or pooled capacity are skipped.  Launches two kernels on
+ * `stream`; calls on one set of caches must be ordered (one stream).  The
+ * indexer keys of new CSA rows are not produced here (given as inputs).
+ * Errors: CSA_ERR_INVALID for null pointers, width not a positive multiple of
+ * 8, m < 1, m_hca < 0, ring < max(m, m_hca), max_new < 0, unaligned rows;
+ * CSA_ERR_UNSUPPORTED for other dtypes.
+ * ---------------------------------------------------------------------- */
+int csa_cache_append(int dtype, int32_t n_seq, int width, const int64_t* tok_off, int64_t* len,
+                     const int64_t* new_off, int64_t max_new, const void* x_new, const void* z_new, void* kv_raw,
+                     void* z_tail, int ring, const int64_t* pool_off, int m, void* pooled,
+                     const int64_t* hpool_off, int m_hca, void* hpooled, void* stream);
+
+/* ------------------------------------------------------------------------
  * csa_index_topk — lightning-indexer scores and per-query top-k.
  * Pages: jyp-garden IDEAS (KV compressed to 1/4, the Lightning Indexer keeps
  * only the top-k); sigco CSA/HCA section (the indexer finds relevant blocks,
@@ -240,7 +273,8 @@ int csa_hca_decode_fallbacks(const void* ws, void* stream, uint32_t* rows);
  * CSA_K_IDX_FINAL (top-k passes of decode batches), CSA_K_ATTN (attention
  * main kernel, CSA or HCA), CSA_K_ATTN_COMBINE (split merge), CSA_K_COMPRESS,
  * CSA_K_FUSED, CSA_K_PF_THRESH and CSA_K_PF_SELECT (threshold and selection
- * kernels of prefill batches; their scoring kernel is CSA_K_IDX_SCORE).
+ * kernels of prefill batches; their scoring kernel is CSA_K_IDX_SCORE),
+ * CSA_K_APPEND (both kernels of csa_cache_append).
  * Errors: CSA_ERR_INVALID for an unknown id or exactly one NULL event.
  * ---------------------------------------------------------------------- */
 enum {
@@ -253,7 +287,8 @@ enum {
   CSA_K_FUSED = 6,
   CSA_K_PF_THRESH = 7,
   CSA_K_PF_SELECT = 8,
-  CSA_K_COUNT = 9
+  CSA_K_APPEND = 9,
+  CSA_K_COUNT = 10
 };
 int csa_profile_events(int kernel_id, void* start, void* stop);
 

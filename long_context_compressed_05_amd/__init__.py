@@ -21,12 +21,12 @@ LIB_PATH = os.path.join(_HERE, "libcsa.so")
 CSA_OK, CSA_ERR_INVALID, CSA_ERR_UNSUPPORTED, CSA_ERR_WORKSPACE, CSA_ERR_DEVICE = 0, -1, -2, -3, -4
 CSA_F32, CSA_BF16 = 0, 1
 
-EXPORTS = ("csa_status_string", "csa_last_error", "csa_compress", "csa_index_topk_workspace",
+EXPORTS = ("csa_status_string", "csa_last_error", "csa_compress", "csa_cache_append", "csa_index_topk_workspace",
            "csa_index_topk", "csa_sparse_attn_workspace", "csa_sparse_attn", "hca_attn_workspace",
            "hca_attn", "csa_hca_decode_workspace", "csa_hca_decode", "csa_hca_decode_check",
            "csa_hca_decode_fallbacks", "csa_profile_events")
 (CSA_K_IDX_SCORE, CSA_K_IDX_SELECT, CSA_K_IDX_FINAL, CSA_K_ATTN, CSA_K_ATTN_COMBINE, CSA_K_COMPRESS,
- CSA_K_FUSED, CSA_K_PF_THRESH, CSA_K_PF_SELECT) = range(9)
+ CSA_K_FUSED, CSA_K_PF_THRESH, CSA_K_PF_SELECT, CSA_K_APPEND) = range(10)
 
 
 class CsaBatch(ctypes.Structure):
@@ -54,6 +54,7 @@ def lib():
     L.csa_last_error.restype = ctypes.c_char_p
     L.csa_last_error.argtypes = []
     L.csa_compress.argtypes = [ci, i32, vp, vp, i64, ci, ci, vp, vp, vp, vp]
+    L.csa_cache_append.argtypes = [ci, i32, ci, vp, vp, vp, i64, vp, vp, vp, vp, ci, vp, ci, vp, vp, ci, vp, vp]
     L.csa_index_topk_workspace.argtypes = [bp, i64, ci, ctypes.POINTER(sz)]
     L.csa_index_topk.argtypes = [bp, vp, i64, ci, ci, ci, ci, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.csa_sparse_attn_workspace.argtypes = [ci, bp, ci, ci, ci, ci, ctypes.POINTER(sz)]
@@ -162,6 +163,24 @@ def csa_compress(x: torch.Tensor, z: torch.Tensor, tok_off: torch.Tensor, pool_o
                               max_len, m, width, _ptr(x), _ptr(z), _ptr(out), _stream(stream)),
            "csa_compress")
     return out
+
+
+def csa_cache_append(x_new: torch.Tensor, z_new: torch.Tensor, new_off: torch.Tensor, max_new: int,
+                     tok_off: torch.Tensor, length: torch.Tensor, kv_raw: torch.Tensor, z_tail: torch.Tensor,
+                     pool_off: torch.Tensor, m: int, pooled: torch.Tensor,
+                     hpool_off: Optional[torch.Tensor] = None, m_hca: int = 0,
+                     hpooled: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Append each sequence's new rows (x_new, z_new [sum n][...], new_off [B+1]) to
+    the raw cache, pool the blocks they complete into `pooled` (and `hpooled`),
+    keep the latest tokens' logits in `z_tail` [B][ring][...] and advance
+    `length` [B] (int64, device) in place."""
+    width = kv_raw[0].numel()
+    ring = z_tail.shape[1]
+    _check(lib().csa_cache_append(_dtype_code(kv_raw), new_off.numel() - 1, width, _ptr(tok_off), _ptr(length),
+                                  _ptr(new_off), max_new, _ptr(x_new), _ptr(z_new), _ptr(kv_raw), _ptr(z_tail),
+                                  ring, _ptr(pool_off), m, _ptr(pooled), _ptr(hpool_off), m_hca, _ptr(hpooled),
+                                  _stream(stream)),
+           "csa_cache_append")
 
 
 def csa_index_topk_workspace(batch: Batch, max_pool: int, k: int) -> int:

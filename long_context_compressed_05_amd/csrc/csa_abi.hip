@@ -218,6 +218,32 @@ int csa_compress(int dtype, int32_t n_seq, const int64_t* tok_off, const int64_t
                                        width, x, z, out, (hipStream_t)stream));
 }
 
+int csa_cache_append(int dtype, int32_t n_seq, int width, const int64_t* tok_off, int64_t* len,
+                     const int64_t* new_off, int64_t max_new, const void* x_new, const void* z_new, void* kv_raw,
+                     void* z_tail, int ring, const int64_t* pool_off, int m, void* pooled,
+                     const int64_t* hpool_off, int m_hca, void* hpooled, void* stream) {
+  if (dtype != CSA_F32 && dtype != CSA_BF16) return fail(CSA_ERR_UNSUPPORTED, "dtype %d", dtype);
+  if (n_seq < 1) return fail(CSA_ERR_INVALID, "n_seq must be >= 1");
+  if (width < 1 || width % 8 != 0) return fail(CSA_ERR_INVALID, "width must be a positive multiple of 8");
+  if (m < 1) return fail(CSA_ERR_INVALID, "block size m must be >= 1 (got %d)", m);
+  if (m_hca < 0) return fail(CSA_ERR_INVALID, "m_hca must be >= 0 (got %d)", m_hca);
+  if (max_new < 0) return fail(CSA_ERR_INVALID, "max_new must be >= 0");
+  if (ring < m || ring < m_hca)
+    return fail(CSA_ERR_INVALID, "ring (%d) must be >= m (%d) and >= m_hca (%d)", ring, m, m_hca);
+  if (!tok_off || !len || !new_off || !x_new || !z_new || !kv_raw || !z_tail || !pool_off || !pooled)
+    return fail(CSA_ERR_INVALID, "NULL pointer argument");
+  if (m_hca > 0 && (!hpool_off || !hpooled)) return fail(CSA_ERR_INVALID, "m_hca > 0 needs hpool_off and hpooled");
+  if (!aligned16(x_new) || !aligned16(z_new) || !aligned16(kv_raw) || !aligned16(z_tail) || !aligned16(pooled) ||
+      (m_hca > 0 && !aligned16(hpooled)))
+    return fail(CSA_ERR_INVALID, "row buffers must be 16-byte aligned");
+  if (max_new == 0) return CSA_OK;
+  int rc = check_device();
+  if (rc) return rc;
+  return launched(csa::launch_append(dtype == CSA_BF16, n_seq, width, tok_off, len, new_off, max_new, x_new, z_new,
+                                     kv_raw, z_tail, ring, pool_off, m, pooled, hpool_off, m_hca, hpooled,
+                                     (hipStream_t)stream));
+}
+
 int csa_index_topk_workspace(const csa_batch* b, int64_t max_pool, int k, size_t* bytes) {
   int rc = check_batch(b);
   if (rc) return rc;

@@ -14,6 +14,11 @@ int launch_compress(bool bf16, int n_seq, const int64_t* tok_off, const int64_t*
                     int64_t max_len, int m, int width, const void* x, const void* z, void* out,
                     hipStream_t stream);
 
+int launch_append(bool bf16, int n_seq, int width, const int64_t* tok_off, int64_t* len, const int64_t* new_off,
+                  int64_t max_new, const void* x_new, const void* z_new, void* kv_raw, void* z_tail, int ring,
+                  const int64_t* pool_off, int m, void* pooled, const int64_t* hpool_off, int m_hca, void* hpooled,
+                  hipStream_t stream);
+
 size_t index_ws_bytes(int64_t n_q, int64_t max_q_per_seq, int64_t max_pool, int k);
 int prefill_path(int64_t max_q_per_seq);
 size_t prefill_ws_bytes(int64_t n_q, int64_t max_pool);

@@ -67,6 +67,33 @@ def test_compress_validation():
         assert call() == csa.CSA_ERR_DEVICE
 
 
+def test_cache_append_validation():
+    L = csa.lib()
+    args = dict(dtype=1, n_seq=2, width=256, tok=FAKE, ln=FAKE, new=FAKE, max_new=8, x=FAKE, z=FAKE, raw=FAKE,
+                tail=FAKE, ring=128, pool=FAKE, m=4, pooled=FAKE, hpool=FAKE, m_hca=128, hpooled=FAKE)
+
+    def call(**kw):
+        a = {**args, **kw}
+        return L.csa_cache_append(a["dtype"], a["n_seq"], a["width"], a["tok"], a["ln"], a["new"], a["max_new"],
+                                  a["x"], a["z"], a["raw"], a["tail"], a["ring"], a["pool"], a["m"], a["pooled"],
+                                  a["hpool"], a["m_hca"], a["hpooled"], None)
+    assert call(dtype=3) == csa.CSA_ERR_UNSUPPORTED
+    assert call(n_seq=0) == csa.CSA_ERR_INVALID
+    assert call(width=100) == csa.CSA_ERR_INVALID
+    assert call(m=0) == csa.CSA_ERR_INVALID
+    assert call(m_hca=-1) == csa.CSA_ERR_INVALID
+    assert call(max_new=-1) == csa.CSA_ERR_INVALID
+    assert call(ring=127) == csa.CSA_ERR_INVALID and "ring" in L.csa_last_error().decode()
+    assert call(ring=3, m_hca=0) == csa.CSA_ERR_INVALID  # the ring holds at least one block of m
+    assert call(ln=None) == csa.CSA_ERR_INVALID
+    assert call(hpooled=None) == csa.CSA_ERR_INVALID  # m_hca > 0 needs the HCA cache
+    assert call(tail=FAKE + 8) == csa.CSA_ERR_INVALID  # misaligned
+    assert call(max_new=0) == csa.CSA_OK  # nothing to append: no launch
+    import torch
+    if not torch.cuda.is_available():
+        assert call(m_hca=0, hpool=None, hpooled=None, ring=4) == csa.CSA_ERR_DEVICE
+
+
 def test_index_topk_validation_and_workspace():
     L = csa.lib()
     b = _batch()

@@ -86,6 +86,80 @@ def test_compress_parity(dtype, m):
         assert np.all(np.abs(g - want) <= bound)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_cache_append_builds_the_bulk_caches(dtype):
+    """Caches grown by ragged appends (prefill chunks, single decode tokens,
+    sequences with nothing new) equal the raw rows and the bulk pooling of the
+    whole sequences: raw rows and pooled rows bit for bit (the same pooling
+    arithmetic), pooled rows within one rounding of the oracle's exact pooling,
+    the tail ring holding the latest tokens' logits, and the lengths advanced."""
+    csa = _lib()
+    m, m_hca, ring = 4, 128, 128
+    wl = small_wl("append", [1, 131, 517, 1030, 2050], [1] * 5, dtype=dtype, m=m, m_hca=m_hca, seed=23)
+    host = synth.make_inputs(wl)
+    B, L = wl.B, np.array(wl.lengths)
+    es = torch.float32 if dtype == "f32" else torch.bfloat16
+    rng = np.random.default_rng(5)
+    # the append schedule: chunks per sequence, ragged, with zero-length and single-token steps
+    steps = []
+    done = np.zeros(B, dtype=np.int64)
+    while (done < L).any():
+        n = np.minimum(L - done, rng.choice([0, 1, 1, 3, 64, 200, 777], size=B))
+        if n.sum() == 0:
+            n = np.minimum(L - done, 1)
+        steps.append(n)
+        done += n
+    cap = L + 5
+    tok_off = synth.offsets(list(cap))
+    pool_off, hpool_off = synth.offsets(list(cap // m)), synth.offsets(list(cap // m_hca))
+    dev = "cuda"
+    kv_raw = torch.zeros((int(tok_off[-1]), 2, wl.d), dtype=es, device=dev)
+    pooled = torch.zeros((int(pool_off[-1]), 2, wl.d), dtype=es, device=dev)
+    hpooled = torch.zeros((int(hpool_off[-1]), 2, wl.d), dtype=es, device=dev)
+    z_tail = torch.zeros((B, ring, 2, wl.d), dtype=es, device=dev)
+    length = torch.zeros(B, dtype=torch.int64, device=dev)
+    from long_context_compressed_05_amd.step import to_device
+    dd = to_device({"kv": host["kv"], "z": host["z"]})
+    kv, z = dd["kv"], dd["z"]
+    t_tok, t_pool, t_hpool = (torch.from_numpy(a).to(dev) for a in (tok_off, pool_off, hpool_off))
+    done[:] = 0
+    for n in steps:
+        rows = np.concatenate([np.arange(host["tok_off"][b] + done[b], host["tok_off"][b] + done[b] + n[b])
+                               for b in range(B)]).astype(np.int64)
+        r = torch.from_numpy(rows).to(dev)
+        new_off = torch.from_numpy(synth.offsets(list(n))).to(dev)
+        csa.csa_cache_append(kv[r].contiguous(), z[r].contiguous(), new_off, int(n.max()), t_tok, length, kv_raw,
+                             z_tail, t_pool, m, pooled, t_hpool, m_hca, hpooled)
+        done += n
+    torch.cuda.synchronize()
+    assert P.torch_to_np(length).tolist() == L.tolist()
+    # the bulk path over the whole sequences, for comparison
+    bulk = torch.empty((int(synth.offsets([l // m for l in L])[-1]), 2, wl.d), dtype=es, device=dev)
+    hbulk = torch.empty((int(synth.offsets([l // m_hca for l in L])[-1]), 2, wl.d), dtype=es, device=dev)
+    bp, hbp = synth.offsets([l // m for l in L]), synth.offsets([l // m_hca for l in L])
+    csa.csa_compress(kv, z, torch.from_numpy(host["tok_off"]).to(dev), torch.from_numpy(bp).to(dev), int(L.max()),
+                     m, bulk)
+    csa.csa_compress(kv, z, torch.from_numpy(host["tok_off"]).to(dev), torch.from_numpy(hbp).to(dev), int(L.max()),
+                     m_hca, hbulk)
+    torch.cuda.synchronize()
+    raw_np, pooled_np, hpooled_np = P.torch_to_np(kv_raw), P.torch_to_np(pooled), P.torch_to_np(hpooled)
+    kv_np, z_np, bulk_np, hbulk_np = P.torch_to_np(kv), P.torch_to_np(z), P.torch_to_np(bulk), P.torch_to_np(hbulk)
+    tail_np = P.torch_to_np(z_tail)
+    for b in range(B):
+        t0 = int(host["tok_off"][b])
+        np.testing.assert_array_equal(raw_np[tok_off[b]:tok_off[b] + L[b]], kv_np[t0:t0 + L[b]])
+        for mm, got, off, ref, roff in ((m, pooled_np, pool_off, bulk_np, bp), (m_hca, hpooled_np, hpool_off,
+                                                                                 hbulk_np, hbp)):
+            nb = L[b] // mm
+            g = got[off[b]:off[b] + nb]
+            np.testing.assert_array_equal(g, ref[roff[b]:roff[b] + nb], err_msg=f"seq {b} m={mm}")
+            want = oracle.pool(host["kv"][t0:t0 + L[b]], host["z"][t0:t0 + L[b]], mm).reshape(-1, 2, wl.d)
+            bound = (2.0 ** -8 if dtype == "bf16" else 2.0 ** -20) * np.abs(want) + 1e-6
+            assert np.all(np.abs(P.as_f64(g) - want) <= bound), f"seq {b} m={mm} vs the oracle"
+        for p in range(max(0, L[b] - ring), L[b]):
+            np.testing.assert_array_equal(tail_np[b, p % ring], z_np[t0 + p], err_msg=f"tail slot of token {p}")
+
+
 @pytest.mark.parametrize("name", list(WORKLOADS))
 def test_index_topk_bit_exact(name):
     csa = _lib()
