@@ -43,6 +43,7 @@ def _load():
     lib.orc_e8m0_value.restype = cd
     lib.orc_e8m0_value.argtypes = [ci]
     lib.orc_pool.argtypes = [ci, i64, ci, ci, vp, vp, vp]
+    lib.orc_mxfp4_quantize.argtypes = [i64, ci, ci, vp, vp, vp]
     lib.orc_index_scores.argtypes = [i64, ci, ci, vp, vp, vp, vp, vp, vp, vp]
     lib.orc_topk.argtypes = [i64, vp, ci, vp]
     lib.orc_attend.argtypes = [ci, ci, cd, vp, i64, vp, vp, vp, vp]
@@ -83,6 +84,18 @@ def e2m1_value(code: int) -> float:
 
 def e8m0_value(byte: int) -> float:
     return _load().orc_e8m0_value(byte)
+
+
+def mxfp4_quantize(x: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """Rows of x ([..., dim] fp32, or bf16 bit patterns as uint16) -> MXFP4
+    (codes [..., dim/2] uint8, E8M0 scales [..., dim/32] uint8)."""
+    x = np.ascontiguousarray(x)
+    dim = x.shape[-1]
+    rows = int(np.prod(x.shape[:-1])) if x.ndim > 1 else 1
+    codes = np.zeros(x.shape[:-1] + (dim // 2,), dtype=np.uint8)
+    scales = np.zeros(x.shape[:-1] + (dim // 32,), dtype=np.uint8)
+    _check(_load().orc_mxfp4_quantize(rows, dim, _dt(x), _p(x), _p(codes), _p(scales)), "mxfp4_quantize")
+    return codes, scales
 
 
 def pool(x: np.ndarray, z: np.ndarray, m: int) -> np.ndarray:

@@ -377,4 +377,54 @@ int orc_hca_attend_given(int dt, int d, int H, int m_h, int W_h, double scale, i
   return 0;
 }
 
+/* MXFP4 quantisation of rows of `dim` elements (dim a multiple of 32), the
+ * step before the indexer: the pages put the indexer's QK path in MXFP4
+ * (pytorch.kr, FP4 QAT paragraph) but give no conversion rule; the reading
+ * taken is the OCP MX one, written out here from its definition:
+ *  - per block of 32 elements, the shared scale is 2^e with
+ *    e = floor(log2(amax)) - 2, 2 being the largest exponent of an e2m1
+ *    value (6 = 1.5 * 2^2), amax the block's largest magnitude; stored as the
+ *    E8M0 byte e + 127, clamped to [0, 254]; a block of zeros takes byte 0;
+ *  - each element x becomes the e2m1 value nearest to x / 2^e, ties going to
+ *    the code with an even mantissa bit, magnitudes above 6 saturating to 6;
+ *    the sign bit is set only for a non-zero negative result, so zero is
+ *    always code 0;
+ *  - codes are packed two per byte, the even element in the low nibble.
+ * x: [rows][dim] in dtype dt; codes [rows][dim/2]; scales [rows][dim/32]. */
+int orc_mxfp4_quantize(int64_t rows, int dim, int dt, const void* x, uint8_t* codes, uint8_t* scales) {
+  if (rows < 0 || dim < 32 || dim % 32 != 0) return -1;
+  for (int64_t r = 0; r < rows; ++r) {
+    for (int blk = 0; blk < dim / 32; ++blk) {
+      const int64_t base = r * dim + blk * 32;
+      double amax = 0.0;
+      for (int i = 0; i < 32; ++i) amax = std::max(amax, std::fabs(load_elem(dt, x, base + i)));
+      int e = -127;
+      if (amax > 0.0) {
+        int ex;
+        (void)std::frexp(amax, &ex);  /* amax = f * 2^ex with f in [0.5, 1): floor(log2 amax) = ex - 1 */
+        e = std::max(-127, std::min(127, (ex - 1) - 2));
+      }
+      scales[r * (dim / 32) + blk] = (uint8_t)(e + 127);
+      for (int i = 0; i < 32; ++i) {
+        const double v = std::ldexp(load_elem(dt, x, base + i), -e);
+        const double mag = std::fabs(v);
+        int best = 0;
+        double best_err = std::numeric_limits<double>::infinity();
+        for (int c = 0; c < 8; ++c) {  /* nearest magnitude; a tie keeps the even code */
+          const double err = std::fabs(mag - e2m1_value(c));
+          if (err < best_err || (err == best_err && (c & 1) == 0)) {
+            best = c;
+            best_err = err;
+          }
+        }
+        const int code = best | ((v < 0.0 && best != 0) ? 8 : 0);
+        const int64_t byte = r * (dim / 2) + blk * 16 + i / 2;
+        if (i % 2 == 0) codes[byte] = (uint8_t)code;
+        else codes[byte] = (uint8_t)(codes[byte] | (code << 4));
+      }
+    }
+  }
+  return 0;
+}
+
 }  // extern "C"

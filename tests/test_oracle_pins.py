@@ -50,6 +50,71 @@ def decode_vec(packed, scales):
 
 
 # ----------------------------------------------------------------------------
+# MXFP4 quantiser (the step before the indexer)
+# ----------------------------------------------------------------------------
+def _nibbles(codes_row):
+    out = []
+    for b in codes_row:
+        out += [int(b) & 15, int(b) >> 4]
+    return out
+
+
+def test_mxfp4_quantize_golden_hand_cases():
+    g = json.load(open(os.path.join(GOLD, "mxfp4_quant_hand.json")))
+    for c in g["cases"]:
+        x = np.zeros((1, 32), np.float32)
+        x[0, :len(c["x"])] = c["x"]
+        codes, scales = oracle.mxfp4_quantize(x)
+        nib = _nibbles(codes[0])
+        assert int(scales[0, 0]) == c["scale_byte"], c["what"]
+        assert nib[:len(c["codes"])] == c["codes"], c["what"]
+        assert all(v == 0 for v in nib[len(c["codes"]):]), c["what"]
+
+
+def test_mxfp4_quantize_round_trips_representable_blocks():
+    """A block built from e2m1 values times one power of two, with its largest
+    magnitude in [4, 6], comes back exactly: same codes (zero canonical), same scale."""
+    rng = np.random.default_rng(3)
+    for e in (-20, -3, 0, 5, 30):
+        codes = rng.integers(0, 16, size=(64, 32))
+        codes[:, 0] = rng.choice([6, 7, 14, 15], size=64)  # magnitude 4 or 6 sets the scale
+        vals = np.array([[E2M1[int(c)] for c in row] for row in codes]) * 2.0 ** e
+        q, sc = oracle.mxfp4_quantize(vals.astype(np.float32))
+        assert (sc == e + 127).all()
+        got = np.array([_nibbles(r) for r in q])
+        want = np.where(codes == 8, 0, codes)  # -0 quantises to +0
+        np.testing.assert_array_equal(got, want)
+        np.testing.assert_array_equal(np.stack([decode_vec(q[i], sc[i]) for i in range(64)]), vals)
+
+
+def test_mxfp4_quantize_sign_scale_and_error_bound():
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal((200, 64)).astype(np.float32) * np.float32(3.0)
+    q, sc = oracle.mxfp4_quantize(x)
+    # sign symmetry: -x flips the sign bit of every non-zero code
+    qn, scn = oracle.mxfp4_quantize(-x)
+    np.testing.assert_array_equal(scn, sc)
+    a, b = np.array([_nibbles(r) for r in q]), np.array([_nibbles(r) for r in qn])
+    np.testing.assert_array_equal(b, np.where(a == 0, 0, a ^ 8))
+    # a power-of-two rescale moves only the scale byte
+    q2, sc2 = oracle.mxfp4_quantize(x * np.float32(2.0 ** 9))
+    np.testing.assert_array_equal(q2, q)
+    np.testing.assert_array_equal(sc2.astype(int), sc.astype(int) + 9)
+    # error bound: within half the gap between the neighbouring e2m1 values
+    # (the largest gap, between 4 and 6, is 2), in units of the block scale;
+    # the block maximum lies in [4, 8) units and may saturate (error < 2)
+    deq = np.stack([decode_vec(q[i], sc[i]) for i in range(len(x))])
+    unit = np.repeat(2.0 ** (sc.astype(np.float64) - 127), 32, axis=1)
+    v = np.abs(x.astype(np.float64)) / unit
+    mags = np.array(sorted(set(abs(E2M1[c]) for c in range(16))))
+    gap = np.array([[np.diff(mags)[min(np.searchsorted(mags, t, side="right") - 1, len(mags) - 2)] for t in row]
+                    for row in v])
+    err = np.abs(deq - x.astype(np.float64)) / unit
+    assert np.all(err <= np.where(v <= 6.0, gap / 2, 2.0) + 1e-12)
+    assert np.all(np.where(v > 6.0, err < 2.0, True))
+
+
+# ----------------------------------------------------------------------------
 # codec
 # ----------------------------------------------------------------------------
 def test_e2m1_matches_golden_table():
