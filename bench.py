@@ -273,6 +273,12 @@ def main():
     except Exception as e:  # reported, never silently replaced
         result["cache_append"] = {"error": repr(e)}
 
+    # ---- MXFP4 quantiser and the recall of the FP4 indexer's top-k -------------
+    try:
+        result["mxfp4_indexer"] = bench_mxfp4_recall(torch, csa, log)
+    except Exception as e:  # reported, never silently replaced
+        result["mxfp4_indexer"] = {"error": repr(e)}
+
     # ---- prefill indexer (4096-token chunk on a 64K cache) ----------------------
     if not args.no_prefill:
         try:
@@ -387,6 +393,57 @@ def bench_cache_append(torch, csa, layer, wl, host, log, reps: int = 50):
         out[name] = {"tokens": int(n.sum()), "blocks_pooled": blocks, "us": round(us, 2),
                      "bytes": nbytes, "GB/s": round(nbytes / (us * 1e-6) / 1e9, 1)}
     log(f"cache append: {out}")
+    return out
+
+
+def bench_mxfp4_recall(torch, csa, log, n_seq: int = 4, n_keys: int = 262144, k: int = 1024, reps: int = 20):
+    """fp32 indexer queries (4 heads x 64) and keys (64), quantised on the GPU
+    with csa_mxfp4_quantize and selected with csa_index_topk, against the exact
+    top-k of the unquantised scores (fp64 on the host): recall = the share of
+    the exact top-k the FP4 path returns.  Two synthetic data models: i.i.d.
+    normal, and keys of which 2k per query carry a planted component along the
+    query's heads.  Also the quantiser's throughput on the 1M-context key set."""
+    dev = "cuda"
+    rng = np.random.default_rng(20260424)
+    w = np.array([0.5, 1.0, 2.0, 1.0], np.float32)
+    out = {"n_keys": n_keys, "k": k, "queries": n_seq}
+    for model in ("iid_normal", "planted"):
+        q = rng.standard_normal((n_seq, 4, 64)).astype(np.float32)
+        kf = rng.standard_normal((n_seq * n_keys, 64)).astype(np.float32)
+        if model == "planted":
+            for b in range(n_seq):
+                sel = rng.choice(n_keys, size=2 * k, replace=False) + b * n_keys
+                u = q[b].sum(axis=0)
+                kf[sel] += (0.5 * u / np.linalg.norm(u) * np.sqrt(64)).astype(np.float32)
+        exact = []
+        for b in range(n_seq):
+            d = kf[b * n_keys:(b + 1) * n_keys].astype(np.float64) @ q[b].astype(np.float64).T  # [n][4]
+            S = (np.maximum(d, 0.0) * w.astype(np.float64)).sum(axis=1)
+            exact.append(set(np.argpartition(-S, k - 1)[:k].tolist()))
+        qd, kd = torch.from_numpy(q).to(dev), torch.from_numpy(kf).to(dev)
+        wd = torch.from_numpy(np.tile(w, (n_seq, 1))).to(dev)
+        qc, qs = csa.csa_mxfp4_quantize(qd)
+        kc, ks = csa.csa_mxfp4_quantize(kd)
+        pool_off = torch.from_numpy(np.arange(n_seq + 1, dtype=np.int64) * n_keys).to(dev)
+        lengths = np.full(n_seq, 4 * n_keys, dtype=np.int64)
+        batch = csa.Batch.from_host(np.concatenate([[0], np.cumsum(lengths)]), np.arange(n_seq + 1), lengths - 1)
+        idx = csa.csa_index_topk(batch, pool_off, n_keys, 4, k, qc, qs, wd, kc, ks)
+        got = idx.cpu().numpy()
+        rec = [len(exact[b] & set(got[b].tolist())) / k for b in range(n_seq)]
+        out[model] = {"recall_mean": round(float(np.mean(rec)), 4), "recall_min": round(float(np.min(rec)), 4)}
+        if model == "iid_normal":  # quantiser throughput on the key set
+            ev = [(csa.HipEvent(), csa.HipEvent()) for _ in range(reps)]
+            for i in range(reps):
+                csa.csa_profile_events(csa.CSA_K_QUANT, ev[i][0], ev[i][1])
+                csa.csa_mxfp4_quantize(kd, kc, ks)
+                csa.csa_profile_events(csa.CSA_K_QUANT)
+            torch.cuda.synchronize()
+            us = float(np.mean([a.elapsed_ms(b) for a, b in ev])) * 1e3
+            nbytes = kf.nbytes + kc.numel() + ks.numel()
+            out["quantize_keys"] = {"rows": int(kf.shape[0]), "dtype": "f32", "us": round(us, 2),
+                                    "bytes": int(nbytes), "GB/s": round(nbytes / (us * 1e-6) / 1e9, 1)}
+        del qd, kd, kc, ks
+    log(f"mxfp4 indexer: {out}")
     return out
 
 

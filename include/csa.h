@@ -136,6 +136,26 @@ int csa_cache_append(int dtype, int32_t n_seq, int width, const int64_t* tok_off
                      const int64_t* hpool_off, int m_hca, void* hpooled, void* stream);
 
 /* ------------------------------------------------------------------------
+ * csa_mxfp4_quantize — MXFP4 encoding of indexer vectors (the input format of
+ * csa_index_topk and csa_hca_decode).
+ * Pages: pytorch.kr FP4 QAT section (the indexer QK path is MXFP4).  The pages
+ * give no conversion rule; the OCP MX one is taken: per block of 32 elements
+ * the scale is 2^e with e = floor(log2(amax)) - 2, stored as the E8M0 byte
+ * e + 127 clamped to [0, 254] (0 for an all-zero block); each element becomes
+ * the e2m1 value nearest to x / 2^e, ties to the code with an even mantissa
+ * bit, magnitudes above 6 saturating to 6; zero is code 0 whatever its sign.
+ *   x       [rows][dim] in `dtype` (dim a multiple of 32), 16-byte aligned
+ *   codes   [rows][dim/2] (two codes per byte, even element in the low
+ *           nibble), 16-byte aligned; scales [rows][dim/32]
+ * Indexer queries are rows of n_heads * 64, keys rows of 64.  Deterministic;
+ * bit-identical to the definition above for every finite input.
+ * Errors: CSA_ERR_INVALID for null pointers, rows < 0, dim not a positive
+ * multiple of 32, unaligned x or codes; CSA_ERR_UNSUPPORTED for other dtypes.
+ * ---------------------------------------------------------------------- */
+int csa_mxfp4_quantize(int dtype, int64_t rows, int dim, const void* x, uint8_t* codes, uint8_t* scales,
+                       void* stream);
+
+/* ------------------------------------------------------------------------
  * csa_index_topk — lightning-indexer scores and per-query top-k.
  * Pages: jyp-garden IDEAS (KV compressed to 1/4, the Lightning Indexer keeps
  * only the top-k); sigco CSA/HCA section (the indexer finds relevant blocks,
@@ -274,7 +294,8 @@ int csa_hca_decode_fallbacks(const void* ws, void* stream, uint32_t* rows);
  * main kernel, CSA or HCA), CSA_K_ATTN_COMBINE (split merge), CSA_K_COMPRESS,
  * CSA_K_FUSED, CSA_K_PF_THRESH and CSA_K_PF_SELECT (threshold and selection
  * kernels of prefill batches; their scoring kernel is CSA_K_IDX_SCORE),
- * CSA_K_APPEND (both kernels of csa_cache_append).
+ * CSA_K_APPEND (both kernels of csa_cache_append), CSA_K_QUANT
+ * (csa_mxfp4_quantize).
  * Errors: CSA_ERR_INVALID for an unknown id or exactly one NULL event.
  * ---------------------------------------------------------------------- */
 enum {
@@ -288,7 +309,8 @@ enum {
   CSA_K_PF_THRESH = 7,
   CSA_K_PF_SELECT = 8,
   CSA_K_APPEND = 9,
-  CSA_K_COUNT = 10
+  CSA_K_QUANT = 10,
+  CSA_K_COUNT = 11
 };
 int csa_profile_events(int kernel_id, void* start, void* stop);
 

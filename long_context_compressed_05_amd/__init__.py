@@ -21,12 +21,12 @@ LIB_PATH = os.path.join(_HERE, "libcsa.so")
 CSA_OK, CSA_ERR_INVALID, CSA_ERR_UNSUPPORTED, CSA_ERR_WORKSPACE, CSA_ERR_DEVICE = 0, -1, -2, -3, -4
 CSA_F32, CSA_BF16 = 0, 1
 
-EXPORTS = ("csa_status_string", "csa_last_error", "csa_compress", "csa_cache_append", "csa_index_topk_workspace",
+EXPORTS = ("csa_status_string", "csa_last_error", "csa_compress", "csa_cache_append", "csa_mxfp4_quantize", "csa_index_topk_workspace",
            "csa_index_topk", "csa_sparse_attn_workspace", "csa_sparse_attn", "hca_attn_workspace",
            "hca_attn", "csa_hca_decode_workspace", "csa_hca_decode", "csa_hca_decode_check",
            "csa_hca_decode_fallbacks", "csa_profile_events")
 (CSA_K_IDX_SCORE, CSA_K_IDX_SELECT, CSA_K_IDX_FINAL, CSA_K_ATTN, CSA_K_ATTN_COMBINE, CSA_K_COMPRESS,
- CSA_K_FUSED, CSA_K_PF_THRESH, CSA_K_PF_SELECT, CSA_K_APPEND) = range(10)
+ CSA_K_FUSED, CSA_K_PF_THRESH, CSA_K_PF_SELECT, CSA_K_APPEND, CSA_K_QUANT) = range(11)
 
 
 class CsaBatch(ctypes.Structure):
@@ -54,6 +54,7 @@ def lib():
     L.csa_last_error.restype = ctypes.c_char_p
     L.csa_last_error.argtypes = []
     L.csa_compress.argtypes = [ci, i32, vp, vp, i64, ci, ci, vp, vp, vp, vp]
+    L.csa_mxfp4_quantize.argtypes = [ci, i64, ci, vp, vp, vp, vp]
     L.csa_cache_append.argtypes = [ci, i32, ci, vp, vp, vp, i64, vp, vp, vp, vp, ci, vp, ci, vp, vp, ci, vp, vp]
     L.csa_index_topk_workspace.argtypes = [bp, i64, ci, ctypes.POINTER(sz)]
     L.csa_index_topk.argtypes = [bp, vp, i64, ci, ci, ci, ci, vp, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -181,6 +182,21 @@ def csa_cache_append(x_new: torch.Tensor, z_new: torch.Tensor, new_off: torch.Te
                                   ring, _ptr(pool_off), m, _ptr(pooled), _ptr(hpool_off), m_hca, _ptr(hpooled),
                                   _stream(stream)),
            "csa_cache_append")
+
+
+def csa_mxfp4_quantize(x: torch.Tensor, codes: Optional[torch.Tensor] = None,
+                       scales: Optional[torch.Tensor] = None, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Rows of x ([..., dim], fp32 or bf16, dim a multiple of 32) -> MXFP4 codes
+    [..., dim/2] and E8M0 scales [..., dim/32] (uint8)."""
+    dim = x.shape[-1]
+    rows = x.numel() // dim if dim else 0
+    if codes is None:
+        codes = torch.empty(x.shape[:-1] + (dim // 2,), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty(x.shape[:-1] + (dim // 32,), dtype=torch.uint8, device=x.device)
+    _check(lib().csa_mxfp4_quantize(_dtype_code(x), rows, dim, _ptr(x), _ptr(codes), _ptr(scales), _stream(stream)),
+           "csa_mxfp4_quantize")
+    return codes, scales
 
 
 def csa_index_topk_workspace(batch: Batch, max_pool: int, k: int) -> int:

@@ -244,6 +244,19 @@ int csa_cache_append(int dtype, int32_t n_seq, int width, const int64_t* tok_off
                                      (hipStream_t)stream));
 }
 
+int csa_mxfp4_quantize(int dtype, int64_t rows, int dim, const void* x, uint8_t* codes, uint8_t* scales,
+                       void* stream) {
+  if (dtype != CSA_F32 && dtype != CSA_BF16) return fail(CSA_ERR_UNSUPPORTED, "dtype %d", dtype);
+  if (rows < 0) return fail(CSA_ERR_INVALID, "rows must be >= 0");
+  if (dim < 32 || dim % 32 != 0) return fail(CSA_ERR_INVALID, "dim must be a positive multiple of 32 (got %d)", dim);
+  if (!x || !codes || !scales) return fail(CSA_ERR_INVALID, "NULL pointer argument");
+  if (!aligned16(x) || !aligned16(codes)) return fail(CSA_ERR_INVALID, "x and codes must be 16-byte aligned");
+  if (rows == 0) return CSA_OK;
+  int rc = check_device();
+  if (rc) return rc;
+  return launched(csa::launch_mxfp4_quant(dtype == CSA_BF16, rows, dim, x, codes, scales, (hipStream_t)stream));
+}
+
 int csa_index_topk_workspace(const csa_batch* b, int64_t max_pool, int k, size_t* bytes) {
   int rc = check_batch(b);
   if (rc) return rc;

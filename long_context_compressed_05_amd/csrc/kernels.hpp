@@ -19,6 +19,9 @@ int launch_append(bool bf16, int n_seq, int width, const int64_t* tok_off, int64
                   const int64_t* pool_off, int m, void* pooled, const int64_t* hpool_off, int m_hca, void* hpooled,
                   hipStream_t stream);
 
+int launch_mxfp4_quant(bool bf16, int64_t rows, int dim, const void* x, uint8_t* codes, uint8_t* scales,
+                       hipStream_t stream);
+
 size_t index_ws_bytes(int64_t n_q, int64_t max_q_per_seq, int64_t max_pool, int k);
 int prefill_path(int64_t max_q_per_seq);
 size_t prefill_ws_bytes(int64_t n_q, int64_t max_pool);

@@ -94,6 +94,23 @@ def test_cache_append_validation():
         assert call(m_hca=0, hpool=None, hpooled=None, ring=4) == csa.CSA_ERR_DEVICE
 
 
+def test_mxfp4_quantize_validation():
+    L = csa.lib()
+
+    def call(dtype=0, rows=4, dim=64, x=FAKE, codes=FAKE, scales=FAKE):
+        return L.csa_mxfp4_quantize(dtype, rows, dim, x, codes, scales, None)
+    assert call(dtype=5) == csa.CSA_ERR_UNSUPPORTED
+    assert call(rows=-1) == csa.CSA_ERR_INVALID
+    assert call(dim=48) == csa.CSA_ERR_INVALID and "multiple of 32" in L.csa_last_error().decode()
+    assert call(dim=0) == csa.CSA_ERR_INVALID
+    assert call(scales=None) == csa.CSA_ERR_INVALID
+    assert call(codes=FAKE + 1) == csa.CSA_ERR_INVALID
+    assert call(rows=0) == csa.CSA_OK
+    import torch
+    if not torch.cuda.is_available():
+        assert call() == csa.CSA_ERR_DEVICE
+
+
 def test_index_topk_validation_and_workspace():
     L = csa.lib()
     b = _batch()

@@ -160,6 +160,70 @@ def test_cache_append_builds_the_bulk_caches(dtype):
             np.testing.assert_array_equal(tail_np[b, p % ring], z_np[t0 + p], err_msg=f"tail slot of token {p}")
 
 
+def _quant_inputs(dtype, rows, dim, seed):
+    rng = np.random.default_rng(seed)
+    x = (rng.standard_normal((rows, dim)) * np.exp(rng.uniform(-8, 8, size=(rows, 1)))).astype(np.float32)
+    # special blocks: zeros, exact midpoints and saturation, tiny (subnormal) and huge magnitudes
+    x[0] = 0.0
+    mids = np.array([6, 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5, -0.25, -0.75, -1.25, -1.75, -2.5, -3.5, -5, 7.9],
+                    np.float32)
+    x[1, :32] = np.resize(mids, 32) * np.float32(2.0 ** -40)
+    x[2, :32] = np.float32(1e-42)
+    x[3, :32] = np.resize(mids, 32) * np.float32(2.0 ** 100)
+    x[4, :] = -x[4, :]
+    if dtype == "bf16":  # the same values rounded to bf16 (nearest even), as bit patterns
+        u = x.view(np.uint32).astype(np.uint64)
+        return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+    return x
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("rows,dim", [(1, 32), (37, 64), (300, 256), (4096, 64)])
+def test_mxfp4_quantize_bit_exact(dtype, rows, dim):
+    csa = _lib()
+    x = np.ascontiguousarray(_quant_inputs(dtype, max(rows, 5), dim, seed=rows + dim)[:rows])
+    from long_context_compressed_05_amd.step import to_device
+    xd = to_device({"x": x})["x"]
+    codes, scales = csa.csa_mxfp4_quantize(xd)
+    torch.cuda.synchronize()
+    want_c, want_s = oracle.mxfp4_quantize(x)
+    np.testing.assert_array_equal(P.torch_to_np(scales), want_s)
+    np.testing.assert_array_equal(P.torch_to_np(codes), want_c)
+
+
+def test_mxfp4_quantize_then_index_matches_the_oracle_pipeline():
+    """fp32 indexer queries and keys quantised on the GPU and selected with
+    csa_index_topk give the same indices as the oracle's quantiser followed by
+    its exact scores and full sort."""
+    csa = _lib()
+    rng = np.random.default_rng(9)
+    lengths, k, m = [4096 + 3, 1031, 9000], 64, 4
+    B = len(lengths)
+    P_b = [L // m for L in lengths]
+    pool_off = synth.offsets(P_b)
+    q = rng.standard_normal((B, 4, 64)).astype(np.float32)
+    kf = rng.standard_normal((int(pool_off[-1]), 64)).astype(np.float32)
+    w = np.array([[0.5, 1.0, 2.0, 1.0]] * B, np.float32)
+    qc, qs = oracle.mxfp4_quantize(q)
+    kc, ks = oracle.mxfp4_quantize(kf)
+    from long_context_compressed_05_amd.step import to_device
+    d = to_device({"q": q, "k": kf, "w": w, "pool_off": pool_off})
+    gqc, gqs = csa.csa_mxfp4_quantize(d["q"])
+    gkc, gks = csa.csa_mxfp4_quantize(d["k"])
+    batch = csa.Batch.from_host(synth.offsets(lengths), np.arange(B + 1), np.array(lengths) - 1)
+    idx = csa.csa_index_topk(batch, d["pool_off"], max(P_b), m, k, gqc, gqs, d["w"], gkc, gks)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(P.torch_to_np(gqc), qc)
+    np.testing.assert_array_equal(P.torch_to_np(gkc), kc)
+    got = P.torch_to_np(idx)
+    for b in range(B):
+        p0, p1 = int(pool_off[b]), int(pool_off[b + 1])
+        S, exact = oracle.index_scores(qc[b], qs[b], w[b], kc[p0:p1], ks[p0:p1])
+        assert exact.all()
+        want = oracle.topk(S, k)
+        np.testing.assert_array_equal(got[b], want)
+
+
 @pytest.mark.parametrize("name", list(WORKLOADS))
 def test_index_topk_bit_exact(name):
     csa = _lib()
