@@ -2,7 +2,7 @@
 //
 // The whole decode hot path runs in one kernel whose workgroups (one per CU)
 // take work units in dependency order:
-//   score   chunk c of row r: C pooled entries of the query's visible range,
+//   score   chunk c of row r: one of n_sc equal parts of the query's visible range,
 //           MXFP4 MFMA scores -> u32 sort keys in LDS; one adaptive radix pass
 //           finds a threshold tau so that about lst entries have key >= tau;
 //           every entry with key >= tau (at most lst of them) is written to the
@@ -148,6 +148,14 @@ __device__ __forceinline__ FRow row_info(KArgs& a, int r) {
   f.n_vis = v < P ? v : P;
   f.n_vis_h = vh < Ph ? vh : Ph;
   return f;
+}
+
+// Entries per score chunk of a row: the row's visible range is split evenly
+// into the plan's n_sc chunks (a multiple of 32, at most the plan's C), so a
+// short row's top-k spreads over its chunks like a long row's does.
+__device__ __forceinline__ int64_t row_chunk(KArgs& a, const FRow& f) {
+  const int64_t c = ((f.n_vis + a.n_sc - 1) / a.n_sc + 31) & ~(int64_t)31;
+  return c < 32 ? 32 : (c > a.C ? a.C : c);
 }
 
 __device__ __forceinline__ uint32_t ld_dev(const uint32_t* p) {
@@ -548,7 +556,7 @@ __device__ __forceinline__ void phase_score(const FCtx& x, int r, int c, const F
   // the listed (key, index) pairs in ascending index order -> LDS (the
   // histograms are no longer needed), then every list position -> workspace
   uint2* lst_s = reinterpret_cast<uint2*>(x.smem + kOffU);
-  const uint32_t jbase = (uint32_t)c * (uint32_t)a.C + (uint32_t)e0;
+  const uint32_t jbase = (uint32_t)(c * row_chunk(a, f)) + (uint32_t)e0;
 #pragma unroll
   for (int i = 0; i < kFKPT; ++i)
     if (i < nv && kv[i] >= tau) lst_s[pos++] = make_uint2(kv[i], jbase + (uint32_t)i);
@@ -657,7 +665,7 @@ __device__ __forceinline__ bool row_fallback(const FCtx& x, int r, const FRow& f
   }
   const uint64_t cstar = ((uint64_t)kstar << 32) | njstar;
   // selected count per chunk -> offsets at the group starts
-  const uint32_t C = (uint32_t)a.C;
+  const uint32_t C = (uint32_t)row_chunk(a, f);
   uint32_t* e_sel = row_taus(x);
   for (int sl = tid; sl < nsc; sl += 256) {
     uint32_t cnt = 0;
@@ -865,7 +873,7 @@ __device__ __forceinline__ int group_select(const FCtx& x, int r, int g, const F
   if (!all_ok(x, kfail)) return -1;
   const uint64_t cstar = ((uint64_t)kstar_f << 32) | (uint32_t)~jstar;
   const uint32_t* rowkeys = a.keys + (size_t)r * a.key_stride;
-  const uint32_t C = (uint32_t)a.C, nvis = n_vis_u32(f);
+  const uint32_t C = (uint32_t)row_chunk(a, f), nvis = n_vis_u32(f);
   const uint32_t jb = (uint32_t)c0 * C, je = (uint32_t)c1 * C < nvis ? (uint32_t)c1 * C : nvis;
   const uint32_t n = je > jb ? je - jb : 0u;
   const uint32_t M = (n + 255) >> 8, m0 = (uint32_t)tid * M;
@@ -1038,7 +1046,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     } else if (it < u_grp) {
       const int r = (int)(it / A.n_sc), c = (int)(it % A.n_sc);
       const FRow f = row_info(A, r);
-      int64_t j0 = (int64_t)c * A.C, j1 = j0 + A.C;
+      const int64_t Cr = row_chunk(A, f);
+      int64_t j0 = (int64_t)c * Cr, j1 = j0 + Cr;
       if (j1 > f.n_vis) j1 = f.n_vis;
       if (j0 > j1) j0 = j1;
       phase_score(x, r, c, f, j0, j1);
