@@ -150,12 +150,33 @@ __device__ __forceinline__ FRow row_info(KArgs& a, int r) {
   return f;
 }
 
-// Entries per score chunk of a row: the row's visible range is split evenly
-// into the plan's n_sc chunks (a multiple of 32, at most the plan's C), so a
-// short row's top-k spreads over its chunks like a long row's does.
-__device__ __forceinline__ int64_t row_chunk(KArgs& a, const FRow& f) {
-  const int64_t c = ((f.n_vis + a.n_sc - 1) / a.n_sc + 31) & ~(int64_t)31;
-  return c < 32 ? 32 : (c > a.C ? a.C : c);
+// A row's score chunks and lists.  The row's visible range is split evenly
+// into as few chunks as keep each at most the plan's C entries (nsc <= the
+// plan's n_sc; a multiple of 32 entries each), and the row's n_sc * lst list
+// positions are shared by its chunks: L positions per chunk, at least Lm of
+// them filled when the chunk has that many entries.  A short row thus has few
+// chunks with long lists, and every row's per-chunk share of the top-k is
+// covered the same way.
+struct RowLayout {
+  int nsc;
+  int64_t C;
+  uint32_t L, Lm, npos;
+};
+__device__ __forceinline__ RowLayout row_layout(KArgs& a, const FRow& f) {
+  RowLayout o;
+  const int64_t nv = f.n_vis > 0 ? f.n_vis : 1;
+  int64_t n = (nv + a.C - 1) / a.C;
+  o.nsc = (int)(n < 1 ? 1 : (n > a.n_sc ? a.n_sc : n));
+  int64_t c = ((nv + o.nsc - 1) / o.nsc + 31) & ~(int64_t)31;
+  o.C = c > a.C ? a.C : c;
+  uint32_t L = (uint32_t)(((int64_t)a.n_sc * a.lst / o.nsc) & ~(int64_t)3);
+  if (L > (uint32_t)o.C) L = (uint32_t)o.C;
+  o.L = L;
+  const uint32_t share = (uint32_t)((a.k + o.nsc - 1) / o.nsc);
+  const uint32_t Lm = 2 * share + 16;
+  o.Lm = Lm < L ? Lm : L;
+  o.npos = (uint32_t)o.nsc * L;
+  return o;
 }
 
 __device__ __forceinline__ uint32_t ld_dev(const uint32_t* p) {
@@ -533,7 +554,8 @@ __device__ __forceinline__ void phase_score(const FCtx& x, int r, int c, const F
   // histogram bin holding the chunk's lst_min-th largest key, or of the bin
   // above it when listing that bin would pass lst entries (one radix pass over
   // the chunk's own key range).  Chunks with at most lst entries list them all.
-  const uint32_t L = (uint32_t)a.lst;
+  const RowLayout lay = row_layout(a, f);
+  const uint32_t L = lay.L;
   const bool trunc = (uint32_t)n > L;
   uint32_t tau = 0;
   if (trunc) {
@@ -542,7 +564,7 @@ __device__ __forceinline__ void phase_score(const FCtx& x, int r, int c, const F
     key_range<kFKPT>(kv, vm, hist, x.scr, &lo, &hi);
     if (lo != hi) {
       uint32_t blo, bhi, above, cnt;
-      radix_pass<kFKPT>(kv, vm, (uint32_t)a.lst_min, hist, hist + 2 * kFHist, x.scr, lo, hi, &blo, &bhi, &above, &cnt);
+      radix_pass<kFKPT>(kv, vm, lay.Lm, hist, hist + 2 * kFHist, x.scr, lo, hi, &blo, &bhi, &above, &cnt);
       tau = above + cnt <= L ? blo : bhi + 1u;
     } else {
       tau = lo + 1u;  // n > L equal keys: list none (the row then takes the exact fallback)
@@ -556,13 +578,13 @@ __device__ __forceinline__ void phase_score(const FCtx& x, int r, int c, const F
   // the listed (key, index) pairs in ascending index order -> LDS (the
   // histograms are no longer needed), then every list position -> workspace
   uint2* lst_s = reinterpret_cast<uint2*>(x.smem + kOffU);
-  const uint32_t jbase = (uint32_t)(c * row_chunk(a, f)) + (uint32_t)e0;
+  const uint32_t jbase = (uint32_t)(c * lay.C) + (uint32_t)e0;
 #pragma unroll
   for (int i = 0; i < kFKPT; ++i)
     if (i < nv && kv[i] >= tau) lst_s[pos++] = make_uint2(kv[i], jbase + (uint32_t)i);
   __syncthreads();
   const size_t slot = (size_t)r * a.n_sc + c;
-  v4u_t* dst = a.lent + slot * L;
+  v4u_t* dst = a.lent + (size_t)r * a.n_sc * a.lst + (size_t)c * L;
   for (uint32_t t = (uint32_t)tid; t < L; t += 256) {
     const uint2 e = t < n_list ? lst_s[t] : make_uint2(kNoKey, kNoKey);
     coh_st128(x.coh, dst + t, v4u_t{x.tag, e.x, x.tag, e.y});
@@ -641,12 +663,14 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t b) {
 __device__ __forceinline__ bool row_fallback(const FCtx& x, int r, const FRow& f, int k_eff) {
   KArgs& a = *x.a;
   const int tid = lane_tid();
-  const int nsc = a.n_sc, ngrp = a.n_cs_sel, cgs = a.cg;
+  const int ngrp = a.n_cs_sel, cgs = a.cg;
+  const RowLayout lay = row_layout(a, f);
+  const int nsc = lay.nsc;
   uint32_t* hist = reinterpret_cast<uint32_t*>(x.smem + kOffHist);
   if (tid == 0) atomicAdd(a.ctl + W_FALLBACK, 1u);
   {
     bool kfail = false;
-    for (int sl = tid; sl < nsc && !kfail; sl += 256) (void)poll_word(x, a.key_hdr + (size_t)r * nsc + sl, &kfail, 64u);
+    for (int sl = tid; sl < nsc && !kfail; sl += 256) (void)poll_word(x, a.key_hdr + (size_t)r * a.n_sc + sl, &kfail, 64u);
     if (!all_ok(x, kfail)) return false;
   }
   const uint32_t* rowkeys = a.keys + (size_t)r * a.key_stride;
@@ -665,7 +689,7 @@ __device__ __forceinline__ bool row_fallback(const FCtx& x, int r, const FRow& f
   }
   const uint64_t cstar = ((uint64_t)kstar << 32) | njstar;
   // selected count per chunk -> offsets at the group starts
-  const uint32_t C = (uint32_t)row_chunk(a, f);
+  const uint32_t C = (uint32_t)lay.C;
   uint32_t* e_sel = row_taus(x);
   for (int sl = tid; sl < nsc; sl += 256) {
     uint32_t cnt = 0;
@@ -703,10 +727,17 @@ __device__ __forceinline__ int group_select(const FCtx& x, int r, int g, const F
                                             uint32_t* base_out) {
   KArgs& a = *x.a;
   const int tid = lane_tid();
-  const int nsc = a.n_sc, L = a.lst, cgs = a.cg;
+  const int cgs = a.cg;
   const int k_eff = (int)(f.n_vis < a.k ? f.n_vis : a.k);
+  // the group's share of the row's list positions: the plan's chunks [g*cg, g*cg + cg)
+  // times lst (positions past the row's npos hold nothing)
+  const int pc0 = g * cgs < a.n_sc ? g * cgs : a.n_sc, pc1 = pc0 + cgs < a.n_sc ? pc0 + cgs : a.n_sc;
+  const uint32_t P0 = (uint32_t)(pc0 * a.lst), P1 = (uint32_t)(pc1 * a.lst);
+  const RowLayout lay = row_layout(a, f);
+  const int nsc = lay.nsc;
+  const uint32_t npos = lay.npos;
+  // in the exact fallback the group takes the row's chunks [c0, c1)
   const int c0 = g * cgs < nsc ? g * cgs : nsc, c1 = c0 + cgs < nsc ? c0 + cgs : nsc;
-  const uint32_t P0 = (uint32_t)(c0 * L), P1 = (uint32_t)(c1 * L), npos = (uint32_t)(nsc * L);
   int32_t* sel_s = reinterpret_cast<int32_t*>(x.smem + kOffSel);
   uint32_t* e_tau = row_taus(x);
   uint32_t* hist = reinterpret_cast<uint32_t*>(x.smem + kOffHist);
@@ -721,8 +752,8 @@ __device__ __forceinline__ int group_select(const FCtx& x, int r, int g, const F
   }
   // the row's lists: thread t holds positions u * 256 + t (keys and indices in
   // registers), and the chunks' thresholds -> LDS
-  const v4u_t* lrow = a.lent + (size_t)r * npos;
-  const uint64_t* trow = a.ltau + (size_t)r * nsc;
+  const v4u_t* lrow = a.lent + (size_t)r * a.n_sc * a.lst;
+  const uint64_t* trow = a.ltau + (size_t)r * a.n_sc;  // chunk c's word at r * n_sc + c (the plan's n_sc)
   uint32_t kv[kFEPT], ix[kFEPT];
   uint32_t vm = 0;
   bool fail = false;
@@ -844,6 +875,7 @@ __device__ __forceinline__ int group_select(const FCtx& x, int r, int g, const F
     }
     if (P0 - m0 < M) x.scr[S_OFF] = rank0 + (uint32_t)__builtin_popcount(tkm & ((1u << (P0 - m0)) - 1u));
     if (P1 - m0 < M) x.scr[S_END] = rank0 + (uint32_t)__builtin_popcount(tkm & ((1u << (P1 - m0)) - 1u));
+    if (tid == 0 && P0 >= npos) x.scr[S_OFF] = (uint32_t)k_eff;
     if (tid == 0 && P1 >= npos) x.scr[S_END] = (uint32_t)k_eff;
     __syncthreads();
     const uint32_t off = uni(x.scr[S_OFF]);
@@ -869,11 +901,11 @@ __device__ __forceinline__ int group_select(const FCtx& x, int r, int g, const F
   *off_out = uni(x.scr[S_DIGIT]);
   // the order key (key, ~index) of every visible entry of the group's chunks
   bool kfail = false;
-  for (int sl = c0 + tid; sl < c1 && !kfail; sl += 256) (void)poll_word(x, a.key_hdr + (size_t)r * nsc + sl, &kfail, 64u);
+  for (int sl = c0 + tid; sl < c1 && !kfail; sl += 256) (void)poll_word(x, a.key_hdr + (size_t)r * a.n_sc + sl, &kfail, 64u);
   if (!all_ok(x, kfail)) return -1;
   const uint64_t cstar = ((uint64_t)kstar_f << 32) | (uint32_t)~jstar;
   const uint32_t* rowkeys = a.keys + (size_t)r * a.key_stride;
-  const uint32_t C = (uint32_t)row_chunk(a, f), nvis = n_vis_u32(f);
+  const uint32_t C = (uint32_t)lay.C, nvis = n_vis_u32(f);
   const uint32_t jb = (uint32_t)c0 * C, je = (uint32_t)c1 * C < nvis ? (uint32_t)c1 * C : nvis;
   const uint32_t n = je > jb ? je - jb : 0u;
   const uint32_t M = (n + 255) >> 8, m0 = (uint32_t)tid * M;
@@ -919,6 +951,7 @@ __device__ __forceinline__ void attend_item(const FCtx& x, int r, int kind, int 
     const int64_t list_len = a.max_hpool + a.W_hca;
     p_begin = (int64_t)s * a.hs;
     p_end = p_begin + a.hs < list_len ? p_begin + a.hs : list_len;
+    if (a.W_hca == 0 && p_end > f.n_vis_h) p_end = f.n_vis_h > p_begin ? f.n_vis_h : p_begin;  // past the row's rows
   }
   const int32_t* idx_s = reinterpret_cast<const int32_t*>(x.smem + kOffSel) + sel_base;
   constexpr uint64_t RB = 2 * 128 * 2;
@@ -1044,13 +1077,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     if (it >= total) {
       // nothing to do this round
     } else if (it < u_grp) {
-      const int r = (int)(it / A.n_sc), c = (int)(it % A.n_sc);
+      // chunk-major: every row's first chunks come first (a short row uses fewer chunks)
+      const int c = (int)(it / R), r = (int)(it % R);
       const FRow f = row_info(A, r);
-      const int64_t Cr = row_chunk(A, f);
-      int64_t j0 = (int64_t)c * Cr, j1 = j0 + Cr;
-      if (j1 > f.n_vis) j1 = f.n_vis;
-      if (j0 > j1) j0 = j1;
-      phase_score(x, r, c, f, j0, j1);
+      const RowLayout lay = row_layout(A, f);
+      if (c < lay.nsc) {
+        int64_t j0 = (int64_t)c * lay.C, j1 = j0 + lay.C;
+        if (j1 > f.n_vis) j1 = f.n_vis;
+        if (j0 > j1) j0 = j1;
+        phase_score(x, r, c, f, j0, j1);
+      }
     } else if (it >= u_mh) {
       const bool hca = it < u_mc;
       const int64_t m = it - (hca ? u_mh : u_mc);
