@@ -457,14 +457,15 @@ __device__ __forceinline__ void radix_pass(const uint32_t (&kv)[NK], uint32_t vm
 // when bit i of vm is set): radix select over the keys' own range, each pass narrowing it to one
 // of at most 2048 bins (so keys spread over the bins whatever their
 // magnitude), at most 3 passes.  Returns the key; *gt = the keys above it.
-// A pass that leaves one key in the range ends the search.  hist: 2 x 2048 +
-// 64 words of LDS, 16-byte aligned.
+// A pass that leaves one key in the range ends the search.  *eq = the keys
+// equal to it (n_valid when they are all equal).  hist: 2 x 2048 + 64 words of
+// LDS, 16-byte aligned.
 template <int NK>
-__device__ __forceinline__ uint32_t kth_key(const uint32_t (&kv)[NK], uint32_t vm, uint32_t need, uint32_t* hist,
-                                            uint32_t* scr, uint32_t* gt) {
+__device__ __forceinline__ uint32_t kth_key(const uint32_t (&kv)[NK], uint32_t vm, uint32_t need, uint32_t n_valid,
+                                            uint32_t* hist, uint32_t* scr, uint32_t* gt, uint32_t* eq) {
   uint32_t lo, hi;
   key_range<NK>(kv, vm, hist, scr, &lo, &hi);
-  uint32_t above_all = 0;
+  uint32_t above_all = 0, in_range = n_valid;
 #pragma unroll 1
   for (int pass = 0; pass < 3 && lo != hi; ++pass) {
     uint32_t blo, bhi, above, cnt;
@@ -474,6 +475,7 @@ __device__ __forceinline__ uint32_t kth_key(const uint32_t (&kv)[NK], uint32_t v
     above_all += above;
     lo = blo;
     hi = bhi;
+    in_range = cnt;
     if (cnt == 1u && lo != hi) {  // the one key in [lo, hi]
 #pragma unroll
       for (int i = 0; i < NK; ++i)
@@ -481,9 +483,40 @@ __device__ __forceinline__ uint32_t kth_key(const uint32_t (&kv)[NK], uint32_t v
       __syncthreads();
       lo = hi = uni(scr[S_KEY]);
       __syncthreads();
+    } else if (cnt <= 64u && lo != hi) {
+      // few keys left in [lo, hi]: gather them (in no particular order) and
+      // rank each against the others instead of another pass; the key with
+      // (greater < need <= greater + equal) is the answer
+      uint32_t* cand = hist + (pass & 1 ? 0 : kFHist);  // the idle histogram: zeroed
+      uint32_t* ncand = cand + 64;
+#pragma unroll
+      for (int i = 0; i < NK; ++i)
+        if (((vm >> i) & 1u) && kv[i] >= lo && kv[i] <= hi) cand[atomicAdd(ncand, 1u)] = kv[i];
+      __syncthreads();
+      const int tid = lane_tid();
+      if (tid < (int)cnt) {
+        const uint32_t mine = cand[tid];
+        uint32_t g = 0, e = 0;
+        for (uint32_t j = 0; j < cnt; ++j) {
+          const uint32_t o = cand[j];
+          g += o > mine ? 1u : 0u;
+          e += o == mine ? 1u : 0u;
+        }
+        if (g < need && g + e >= need) {  // equal keys write the same words
+          scr[S_KEY] = mine;
+          scr[S_ABOVE] = g;
+          scr[S_CNT] = e;
+        }
+      }
+      __syncthreads();
+      lo = hi = uni(scr[S_KEY]);
+      above_all += uni(scr[S_ABOVE]);
+      in_range = uni(scr[S_CNT]);
+      __syncthreads();
     }
   }
   *gt = above_all;
+  *eq = in_range;
   return lo;
 }
 
@@ -798,7 +831,7 @@ __device__ __forceinline__ int group_select(const FCtx& x, int r, int g, const F
   uint32_t n_ent;
   (void)block_exscan_val((uint32_t)__builtin_popcount(vm), x.scr, &n_ent);
   bool exact = n_ent >= (uint32_t)k_eff;
-  uint32_t kstar = 0, gt_all = 0;
+  uint32_t kstar = 0, gt_all = 0, eq_all = 0;
   uint32_t* lk = reinterpret_cast<uint32_t*>(x.smem + kOffU);  // [npos] keys by position
   uint32_t* li = lk + kFEntLds;                                 // [npos] indices by position
   if (exact) {
@@ -806,12 +839,48 @@ __device__ __forceinline__ int group_select(const FCtx& x, int r, int g, const F
       uint32_t kv16[16];
 #pragma unroll
       for (int u = 0; u < 16; ++u) kv16[u] = kv[u];
-      kstar = kth_key<16>(kv16, vm & 0xffffu, (uint32_t)k_eff, hist, x.scr, &gt_all);
+      kstar = kth_key<16>(kv16, vm & 0xffffu, (uint32_t)k_eff, n_ent, hist, x.scr, &gt_all, &eq_all);
     } else {
-      kstar = kth_key<kFEPT>(kv, vm, (uint32_t)k_eff, hist, x.scr, &gt_all);
+      kstar = kth_key<kFEPT>(kv, vm, (uint32_t)k_eff, n_ent, hist, x.scr, &gt_all, &eq_all);
     }
     for (int sl = tid; sl < nsc; sl += 256)
       if (e_tau[sl] > kstar) x.scr[S_BAD] = 1;
+    if (gt_all + eq_all == (uint32_t)k_eff) {
+      // every listed entry equal to K* is taken, so the row takes exactly the
+      // listed entries with key >= K*: one scan in position order (slot u,
+      // then thread) ranks the group's own positions, and its first field
+      // counts the taken positions below P0 (the group's output offset)
+      const int32_t ks = (int32_t)kstar;
+      uint32_t pre = 0;
+#pragma unroll
+      for (int u = 0; u < kFEPT; ++u) pre += ((int32_t)kv[u] >= ks && (uint32_t)(u * 256 + tid) < P0) ? 1u : 0u;
+      const int u0 = (int)(P0 >> 8), u1r = (int)((P1 + 255u) >> 8), u1 = u1r > u0 ? u1r : u0 + 1;
+      uint32_t off = 0, run = 0;
+      for (int u = u0; u < u1; ++u) {  // uniform; one slot when the group's positions are one 256-aligned run
+        uint32_t ku = kNoKey, iu = 0;
+#pragma unroll
+        for (int v = 0; v < kFEPT; ++v) {
+          ku = v == u ? kv[v] : ku;
+          iu = v == u ? ix[v] : iu;
+        }
+        const uint32_t p = (uint32_t)(u * 256 + tid);
+        const bool take = (int32_t)ku >= ks && p >= P0 && p < P1;
+        uint32_t tot;
+        const uint32_t ex = block_exscan_val((take ? 1u : 0u) | (u == u0 ? pre << 16 : 0u), x.scr, &tot);
+        if (u == u0) off = tot >> 16;
+        if (take) sel_s[off + run + (ex & 0xffffu)] = (int32_t)iu;
+        run += tot & 0xffffu;
+      }
+      exact = uni(x.scr[S_BAD]) == 0u;  // the scans' barriers ordered the threshold checks
+      __syncthreads();
+      if (exact) {
+        *off_out = off;
+        *base_out = off;
+        return (int)run;
+      }
+    }
+  }
+  if (exact) {
     // to contiguous ownership (the histograms are free again): thread t takes
     // positions [t*M, t*M + M), so position order is thread order
 #pragma unroll
