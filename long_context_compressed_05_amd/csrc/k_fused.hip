@@ -59,9 +59,12 @@ enum { W_EPOCH = 0, W_EXIT = 1, W_ERROR = 2, W_TICKET = 3, W_FALLBACK = 4, W_CTL
 // per-chunk arrays of a row (counts, thresholds) and a CSA group's selected
 // rows; the union region holds the attention stages, or the radix histograms,
 // or a score chunk's staged list.
-constexpr int kOffKeys = 0;                                 // uint32 [kFMaxC]
+constexpr int kFKeyPad = kFMaxC + kFMaxC / 16;  // key slots: entry j at j + j/16 (runs of 16 start on distinct banks)
+constexpr int kFBins = 4096;                    // fixed score bins: a key's bits 30..19 (16 bins per octave)
+constexpr int kFBinPad = kFBins + kFBins / 16;  // bin b at b + b/16
+constexpr int kOffKeys = 0;                                 // uint32 [kFKeyPad]
 constexpr int kOffSel = kOffKeys + 3 * (kFMaxSlots + 8) * 4;  // int32 [kFMaxSel] (aliases the chunk keys)
-constexpr int kOffScr = kOffKeys + kFMaxC * 4;              // uint32 [64]
+constexpr int kOffScr = kOffKeys + kFKeyPad * 4;            // uint32 [64]
 constexpr int kOffU = kOffScr + 64 * 4;                     // union region
 constexpr int kOffHist = kOffU + kFEntLds * 4;              // uint32 [2][kFHist] + [64] lane trash words
 constexpr int kSelEnd = kOffHist + (2 * kFHist + 64) * 4;
@@ -70,6 +73,7 @@ constexpr int kFusedLds = kSelEnd > kAttnEnd ? kSelEnd : kAttnEnd;
 static_assert(kOffSel + (kFMaxSel + 64) * 4 <= kOffScr, "a group's selected rows (+ 64 dummy slots) fit the key region");
 static_assert(kOffU % 16 == 0 && kOffHist % 16 == 0, "LDS regions must be 16-byte aligned");
 static_assert(kFMaxC * 8 <= kAttnLdsBytes, "a score chunk's staged list fits the union region");
+static_assert(kFBinPad * 4 <= kOffHist - kOffU && kFBinPad % 4 == 0, "a score chunk's fixed bins fit below the radix histograms");
 static_assert(2 * kFEntLds * 4 <= kAttnLdsBytes, "a row's keys and indices by position fit the union region");
 static_assert(kFEPT % 4 == 0 && kFEntLds % 4 == 0, "positions are read 16 bytes at a time");
 static_assert(kFusedLds <= 160 * 1024, "one workgroup per CU");
@@ -543,6 +547,12 @@ __device__ __forceinline__ void phase_score(const FCtx& x, int r, int c, const F
   // 32-entry MFMA tiles; wave w takes tiles w, w+4, ...; 16 tiles per wave per batch of loads
   const int n = (int)(j1 - j0);
   const int ntiles = (n + 31) >> 5;
+  const RowLayout lay = row_layout(a, f);
+  const uint32_t L = lay.L;
+  const bool trunc = (uint32_t)n > L;
+  // a truncated chunk counts its keys into fixed bins as they are made (the
+  // LDS atomics hide under the key stream)
+  uint32_t* fh = reinterpret_cast<uint32_t*>(x.smem + kOffU);
   for (int tb = 0; tb < ntiles; tb += 64) {
     uint4 kcv[16];
     int ksv[16];
@@ -556,6 +566,10 @@ __device__ __forceinline__ void phase_score(const FCtx& x, int r, int c, const F
         kcv[u] = *reinterpret_cast<const uint4*>(a.k_codes + (f.pbase + j) * 32 + kb * 16);
         ksv[u] = a.k_scales[(f.pbase + j) * 2 + kb];
       }
+    }
+    if (tb == 0 && trunc) {  // cleared while the first loads are in flight
+      for (int i = tid; i < kFBinPad / 4; i += 256) reinterpret_cast<uint4*>(fh)[i] = make_uint4(0u, 0u, 0u, 0u);
+      __syncthreads();
     }
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
@@ -571,7 +585,9 @@ __device__ __forceinline__ void phase_score(const FCtx& x, int r, int c, const F
         const float r1 = __int_as_float(max(__float_as_int(acc[1]), 0));
         const float r2 = __int_as_float(max(__float_as_int(acc[2]), 0));
         const float r3 = __int_as_float(max(__float_as_int(acc[3]), 0));
-        keys_s[jl] = __float_as_uint((r0 + r1) + (r2 + r3));
+        const uint32_t key = __float_as_uint((r0 + r1) + (r2 + r3));
+        keys_s[jl + (jl >> 4)] = key;
+        if (trunc) atomicAdd(fh + (key >> 19) + (key >> 23), 1u);  // bin key >> 19, padded
       }
     }
   }
@@ -582,25 +598,62 @@ __device__ __forceinline__ void phase_score(const FCtx& x, int r, int c, const F
   const int nv = n - e0 < 0 ? 0 : (n - e0 < M ? n - e0 : M);
   uint32_t kv[kFKPT];
 #pragma unroll
-  for (int i = 0; i < kFKPT; ++i) kv[i] = i < nv ? keys_s[e0 + i] : 0u;
+  for (int i = 0; i < kFKPT; ++i) kv[i] = i < nv ? keys_s[e0 + i + ((e0 + i) >> 4)] : 0u;
   // The list: every entry with key >= tau, where tau is the lower edge of the
-  // histogram bin holding the chunk's lst_min-th largest key, or of the bin
-  // above it when listing that bin would pass lst entries (one radix pass over
-  // the chunk's own key range).  Chunks with at most lst entries list them all.
-  const RowLayout lay = row_layout(a, f);
-  const uint32_t L = lay.L;
-  const bool trunc = (uint32_t)n > L;
+  // fixed bin holding the chunk's lst_min-th largest key when listing that bin
+  // stays within lst entries; otherwise one radix pass over that bin's key
+  // range places tau at the lower edge of the sub-bin holding it, or of the
+  // sub-bin above it when listing that one would pass lst entries.  Chunks with
+  // at most lst entries list them all.
   uint32_t tau = 0;
   if (trunc) {
-    uint32_t lo, hi;
-    const uint32_t vm = (1u << nv) - 1u;
-    key_range<kFKPT>(kv, vm, hist, x.scr, &lo, &hi);
-    if (lo != hi) {
-      uint32_t blo, bhi, above, cnt;
-      radix_pass<kFKPT>(kv, vm, lay.Lm, hist, hist + 2 * kFHist, x.scr, lo, hi, &blo, &bhi, &above, &cnt);
-      tau = above + cnt <= L ? blo : bhi + 1u;
+    const uint32_t need = lay.Lm;  // <= L < n
+    // thread t: bins [16t, 16t + 16), in keys-descending order from the top thread
+    uint32_t hc[16], tot = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      hc[i] = fh[17 * tid + i];
+      tot += hc[i];
+    }
+    const uint32_t incl = wave_incl_add(tot);
+    if (lane == 63) x.scr[wave] = incl;
+    __syncthreads();
+    const uint4 wt = *reinterpret_cast<const uint4*>(x.scr);
+    const uint32_t all = wt.x + wt.y + wt.z + wt.w;
+    const uint32_t below = incl - tot + (wave > 0 ? wt.x : 0u) + (wave > 1 ? wt.y : 0u) + (wave > 2 ? wt.z : 0u);
+    const uint32_t sup = all - below - tot;  // keys in the bins above this thread's
+    if (sup < need && sup + tot >= need) {
+      uint32_t cum = sup, asel = 0, bsel = 0, csel = 0;
+      bool found = false;
+#pragma unroll
+      for (int b = 15; b >= 0; --b) {
+        if (!found) {
+          if (cum + hc[b] >= need) {
+            found = true;
+            bsel = (uint32_t)b;
+            asel = cum;
+            csel = hc[b];
+          } else {
+            cum += hc[b];
+          }
+        }
+      }
+      x.scr[S_DIGIT] = 16u * (uint32_t)tid + bsel;
+      x.scr[S_ABOVE] = asel;
+      x.scr[S_CNT] = csel;
+    }
+    __syncthreads();
+    const uint32_t bin = uni(x.scr[S_DIGIT]), above = uni(x.scr[S_ABOVE]), cnt = uni(x.scr[S_CNT]);
+    if (above + cnt <= L) {
+      tau = bin << 19;
     } else {
-      tau = lo + 1u;  // n > L equal keys: list none (the row then takes the exact fallback)
+      const uint32_t vm = (1u << nv) - 1u;
+      for (int i = tid; i < kFHist / 4; i += 256) reinterpret_cast<uint4*>(hist)[i] = make_uint4(0u, 0u, 0u, 0u);
+      __syncthreads();
+      uint32_t blo, bhi, ab2, cnt2;
+      radix_pass<kFKPT>(kv, vm, need - above, hist, hist + 2 * kFHist, x.scr, bin << 19, ((bin + 1u) << 19) - 1u, &blo,
+                        &bhi, &ab2, &cnt2);
+      tau = above + ab2 + cnt2 <= L ? blo : bhi + 1u;
     }
   }
   uint32_t cg = 0;
@@ -629,11 +682,12 @@ __device__ __forceinline__ void phase_score(const FCtx& x, int r, int c, const F
     uint32_t* gk = a.keys + (size_t)r * a.key_stride + j0;
     for (int i = 4 * tid; i < n; i += 1024) {
       if (i + 3 < n) {
-        const v4u_t u = {keys_s[i], keys_s[i + 1], keys_s[i + 2], keys_s[i + 3]};
+        const uint32_t* k4 = keys_s + i + (i >> 4);  // i % 16 <= 12: the four share one run
+        const v4u_t u = {k4[0], k4[1], k4[2], k4[3]};
         coh_st128(x.coh, gk + i, u);
       } else {
         for (int e = i; e < n; ++e)
-          __builtin_amdgcn_raw_buffer_store_b32(keys_s[e], x.coh.r, coh_off(x.coh, gk + e), 0, kSc1);
+          __builtin_amdgcn_raw_buffer_store_b32(keys_s[e + (e >> 4)], x.coh.r, coh_off(x.coh, gk + e), 0, kSc1);
       }
     }
   }
@@ -826,6 +880,27 @@ __device__ __forceinline__ int group_select(const FCtx& x, int r, int g, const F
     if (tid < nsc) e_tau[tid] = (uint32_t)tw0;
     if (tid + 256 < nsc) e_tau[tid + 256] = (uint32_t)tw1;
   }
+  // Warm the caches with the rows listed at the group's first 256 positions
+  // (its selected rows are among them when P1 - P0 <= 256) while K* is found:
+  // one word of each 128-byte line, consumed only once the ranks are known.
+  uint32_t warm0 = 0, warm1 = 0, warm2 = 0, warm3 = 0;
+  {
+    const int uw = (int)(P0 >> 8);
+    uint32_t kw = kNoKey, iw = 0;
+#pragma unroll
+    for (int v = 0; v < kFEPT; ++v) {
+      kw = v == uw ? kv[v] : kw;
+      iw = v == uw ? ix[v] : iw;
+    }
+    const uint32_t p = (uint32_t)(uw * 256 + tid);
+    if (kw != kNoKey && p >= P0 && p < P1) {  // a listed entry: iw < the row's visible count
+      const uint32_t* row = reinterpret_cast<const uint32_t*>(a.kv_pool + ((size_t)f.pbase + iw) * 512u);
+      warm0 = row[0];
+      warm1 = row[32];
+      warm2 = row[64];
+      warm3 = row[96];
+    }
+  }
   if (tid == 0) x.scr[S_BAD] = 0;
   if (!all_ok(x, fail)) return -1;
   uint32_t n_ent;
@@ -874,6 +949,7 @@ __device__ __forceinline__ int group_select(const FCtx& x, int r, int g, const F
       exact = uni(x.scr[S_BAD]) == 0u;  // the scans' barriers ordered the threshold checks
       __syncthreads();
       if (exact) {
+        asm volatile("" ::"v"(warm0), "v"(warm1), "v"(warm2), "v"(warm3));
         *off_out = off;
         *base_out = off;
         return (int)run;
