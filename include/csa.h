@@ -271,6 +271,41 @@ int csa_hca_decode(const csa_batch* b, const int64_t* pool_off, int64_t max_pool
                    float* csa_lse, void* hca_out, float* hca_lse, void* ws, size_t ws_bytes,
                    void* stream);
 
+/* ------------------------------------------------------------------------
+ * csa_hca_decode_shared — csa_hca_decode over caches whose leading part is
+ * shared with another sequence (a prefix cache).
+ * Pages: sigco.tistory.com KV-cache section (requests with a common prefix
+ * reuse the cache already computed for it, so several questions over one long
+ * document do not rebuild it); the shared part here is device-resident.
+ * Sequence b with p = prefix_seq[b] >= 0 and T = prefix_tokens[b] > 0 reads
+ * the first T tokens of its logical sequence from sequence p's cache: its
+ * logical pooled row j (indexer key row j alike) is pooled row pool_off[p] + j
+ * when j < T/m, else pool_off[b] + (j - T/m); its HCA row j is hpool_off[p] + j
+ * when j < T/m_hca, else hpool_off[b] + (j - T/m_hca); its raw token u (window
+ * rows) is tok_off[p] + u when u < T, else tok_off[b] + (u - T).  So b stores
+ * only its own rows after the prefix, and its logical pooled count is
+ * T/m + (pool_off[b+1] - pool_off[b]) (HCA alike).  q_pos, idx (indices into
+ * the logical pooled rows) and every output are those of csa_hca_decode on
+ * the logical sequence; the result is bit-identical to csa_hca_decode over
+ * caches holding each logical sequence contiguously.
+ *   prefix_seq [n_seq] int32 device (-1: no prefix); prefix_tokens [n_seq]
+ *   int64 device.  T should be a multiple of m and m_hca, p's cache should
+ *   hold at least T tokens' rows and p should have no prefix of its own; the
+ *   kernel clamps each count to what p stores (reads never leave p's rows)
+ *   and ignores p outside [0, n_seq) or p == b, but the result is only
+ *   meaningful when these hold.  max_pool / max_hpool bound the logical
+ *   counts.  Other arguments, workspace and errors as csa_hca_decode;
+ *   CSA_ERR_INVALID also for a NULL prefix array.
+ * ---------------------------------------------------------------------- */
+int csa_hca_decode_shared(const csa_batch* b, const int32_t* prefix_seq, const int64_t* prefix_tokens,
+                          const int64_t* pool_off, int64_t max_pool, const int64_t* hpool_off, int64_t max_hpool,
+                          int m, int m_hca, int H, int d, float scale, int k, int W, int W_hca,
+                          const uint8_t* q_codes, const uint8_t* q_scales, const float* w,
+                          const uint8_t* k_codes, const uint8_t* k_scales, const void* q, const void* kv_pool,
+                          const void* kv_pool_hca, const void* kv_raw, int32_t* idx, void* csa_out,
+                          float* csa_lse, void* hca_out, float* hca_lse, void* ws, size_t ws_bytes,
+                          void* stream);
+
 /* Synchronises `stream`, then returns CSA_OK if no csa_hca_decode launch on
  * workspace `ws` hit its wait bound since the last check, else
  * CSA_ERR_DEVICE; clears the word.  (The only synchronising call.) */

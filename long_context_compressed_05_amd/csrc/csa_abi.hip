@@ -102,14 +102,13 @@ int csa_hca_decode_workspace(const csa_batch* b, int64_t max_pool, int64_t max_h
   return CSA_OK;
 }
 
-int csa_hca_decode(const csa_batch* b, const int64_t* pool_off, int64_t max_pool,
-                   const int64_t* hpool_off, int64_t max_hpool, int m, int m_hca, int H, int d,
-                   float scale, int k, int W, int W_hca, const uint8_t* q_codes,
-                   const uint8_t* q_scales, const float* w, const uint8_t* k_codes,
-                   const uint8_t* k_scales, const void* q, const void* kv_pool,
-                   const void* kv_pool_hca, const void* kv_raw, int32_t* idx, void* csa_out,
-                   float* csa_lse, void* hca_out, float* hca_lse, void* ws, size_t ws_bytes,
-                   void* stream) {
+static int hca_decode_impl(const csa_batch* b, const int32_t* pre_seq, const int64_t* pre_tok,
+                           const int64_t* pool_off, int64_t max_pool, const int64_t* hpool_off, int64_t max_hpool,
+                           int m, int m_hca, int H, int d, float scale, int k, int W, int W_hca,
+                           const uint8_t* q_codes, const uint8_t* q_scales, const float* w, const uint8_t* k_codes,
+                           const uint8_t* k_scales, const void* q, const void* kv_pool, const void* kv_pool_hca,
+                           const void* kv_raw, int32_t* idx, void* csa_out, float* csa_lse, void* hca_out,
+                           float* hca_lse, void* ws, size_t ws_bytes, void* stream) {
   int rc = check_batch(b);
   if (rc) return rc;
   if (b->n_q != b->n_seq || b->max_q_per_seq != 1)
@@ -132,13 +131,41 @@ int csa_hca_decode(const csa_batch* b, const int64_t* pool_off, int64_t max_pool
   const size_t need = csa::plan_fused(b->n_q, max_pool, max_hpool, H, k, W, W_hca).ws_bytes;
   if (!ws || ws_bytes < need)
     return fail(CSA_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need, ws_bytes);
-  if (csa::launch_fused((int)b->n_q, b->tok_off, b->q_pos, pool_off, hpool_off, max_pool, max_hpool, m, m_hca, H,
+  if (csa::launch_fused((int)b->n_q, b->tok_off, b->q_pos, pool_off, hpool_off, pre_seq, pre_tok, max_pool,
+                        max_hpool, m, m_hca, H,
                         scale, k, W, W_hca, q_codes, q_scales, w, k_codes, k_scales, q, kv_pool, kv_pool_hca,
                         kv_raw, idx, csa_out, csa_lse, hca_out, hca_lse, ws, (hipStream_t)stream) != 0) {
     (void)hipGetLastError();
     return fail(CSA_ERR_DEVICE, "cooperative launch of the fused decode kernel failed");
   }
   return CSA_OK;
+}
+
+int csa_hca_decode(const csa_batch* b, const int64_t* pool_off, int64_t max_pool,
+                   const int64_t* hpool_off, int64_t max_hpool, int m, int m_hca, int H, int d,
+                   float scale, int k, int W, int W_hca, const uint8_t* q_codes,
+                   const uint8_t* q_scales, const float* w, const uint8_t* k_codes,
+                   const uint8_t* k_scales, const void* q, const void* kv_pool,
+                   const void* kv_pool_hca, const void* kv_raw, int32_t* idx, void* csa_out,
+                   float* csa_lse, void* hca_out, float* hca_lse, void* ws, size_t ws_bytes,
+                   void* stream) {
+  return hca_decode_impl(b, nullptr, nullptr, pool_off, max_pool, hpool_off, max_hpool, m, m_hca, H, d, scale, k, W,
+                         W_hca, q_codes, q_scales, w, k_codes, k_scales, q, kv_pool, kv_pool_hca, kv_raw, idx,
+                         csa_out, csa_lse, hca_out, hca_lse, ws, ws_bytes, stream);
+}
+
+int csa_hca_decode_shared(const csa_batch* b, const int32_t* prefix_seq, const int64_t* prefix_tokens,
+                          const int64_t* pool_off, int64_t max_pool, const int64_t* hpool_off, int64_t max_hpool,
+                          int m, int m_hca, int H, int d, float scale, int k, int W, int W_hca,
+                          const uint8_t* q_codes, const uint8_t* q_scales, const float* w,
+                          const uint8_t* k_codes, const uint8_t* k_scales, const void* q, const void* kv_pool,
+                          const void* kv_pool_hca, const void* kv_raw, int32_t* idx, void* csa_out,
+                          float* csa_lse, void* hca_out, float* hca_lse, void* ws, size_t ws_bytes,
+                          void* stream) {
+  if (!prefix_seq || !prefix_tokens) return fail(CSA_ERR_INVALID, "NULL prefix array");
+  return hca_decode_impl(b, prefix_seq, prefix_tokens, pool_off, max_pool, hpool_off, max_hpool, m, m_hca, H, d,
+                         scale, k, W, W_hca, q_codes, q_scales, w, k_codes, k_scales, q, kv_pool, kv_pool_hca,
+                         kv_raw, idx, csa_out, csa_lse, hca_out, hca_lse, ws, ws_bytes, stream);
 }
 
 int csa_hca_decode_check(const csa_batch* b, const void* ws, void* stream) {

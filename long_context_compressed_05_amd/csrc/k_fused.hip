@@ -90,6 +90,8 @@ struct FusedArgs {
   const int64_t* q_pos;
   const int64_t* pool_off;
   const int64_t* hpool_off;
+  const int32_t* pre_seq;  // [R] or null: the sequence whose cache holds this one's prefix (-1: none)
+  const int64_t* pre_tok;  // [R] or null: the shared prefix's length in tokens
   int R, m, m_hca, H, k, W, W_hca;
   float scale_log2;
   int64_t max_pool, max_hpool;
@@ -137,9 +139,18 @@ struct FusedArgs {
 // where it is used instead of being held in registers across the whole loop.
 using KArgs = const __attribute__((address_space(4))) FusedArgs;
 
+// A row's logical cache entries: a shared prefix (pre_p pooled rows, pre_h
+// HCA rows, pre_t raw tokens, held in another sequence's cache from ppbase /
+// phbase / ptbase), then the row's own segment (from pbase / hbase /
+// tok_base).  Without a prefix the pre_ counts are 0.
 struct FRow {
   int64_t t, n_vis, n_vis_h, pbase, hbase, tok_base;
+  int64_t pre_p, pre_h, pre_t, ppbase, phbase, ptbase;
 };
+// physical pooled row (and indexer key row) of logical pooled entry j
+__device__ __forceinline__ int64_t pool_row(const FRow& f, int64_t j) {
+  return j < f.pre_p ? f.ppbase + j : f.pbase + (j - f.pre_p);
+}
 
 __device__ __forceinline__ FRow row_info(KArgs& a, int r) {
   FRow f;
@@ -147,7 +158,24 @@ __device__ __forceinline__ FRow row_info(KArgs& a, int r) {
   f.pbase = a.pool_off[r];
   f.hbase = a.hpool_off[r];
   f.tok_base = a.tok_off[r];
-  const int64_t P = a.pool_off[r + 1] - f.pbase, Ph = a.hpool_off[r + 1] - f.hbase;
+  f.pre_p = f.pre_h = f.pre_t = 0;
+  f.ppbase = f.phbase = f.ptbase = 0;
+  if (a.pre_seq) {
+    const int32_t s = a.pre_seq[r];
+    const int64_t T = a.pre_tok[r];
+    if (s >= 0 && s < a.R && s != r && T > 0) {
+      // clamped to what the holder stores, so every read stays in its segment
+      f.ppbase = a.pool_off[s];
+      f.phbase = a.hpool_off[s];
+      f.ptbase = a.tok_off[s];
+      const int64_t sp = a.pool_off[s + 1] - f.ppbase, sh = a.hpool_off[s + 1] - f.phbase;
+      const int64_t st = a.tok_off[s + 1] - f.ptbase;
+      f.pre_p = T / a.m < sp ? T / a.m : sp;
+      f.pre_h = T / a.m_hca < sh ? T / a.m_hca : sh;
+      f.pre_t = T < st ? T : st;
+    }
+  }
+  const int64_t P = f.pre_p + a.pool_off[r + 1] - f.pbase, Ph = f.pre_h + a.hpool_off[r + 1] - f.hbase;
   const int64_t v = (f.t + 1) / a.m, vh = (f.t + 1) / a.m_hca;
   f.n_vis = v < P ? v : P;
   f.n_vis_h = vh < Ph ? vh : Ph;
@@ -563,8 +591,9 @@ __device__ __forceinline__ void phase_score(const FCtx& x, int r, int c, const F
       kcv[u] = make_uint4(0, 0, 0, 0);
       ksv[u] = 127;
       if (tile < ntiles && j < j1) {
-        kcv[u] = *reinterpret_cast<const uint4*>(a.k_codes + (f.pbase + j) * 32 + kb * 16);
-        ksv[u] = a.k_scales[(f.pbase + j) * 2 + kb];
+        const int64_t pj = pool_row(f, j);
+        kcv[u] = *reinterpret_cast<const uint4*>(a.k_codes + pj * 32 + kb * 16);
+        ksv[u] = a.k_scales[pj * 2 + kb];
       }
     }
     if (tb == 0 && trunc) {  // cleared while the first loads are in flight
@@ -894,7 +923,7 @@ __device__ __forceinline__ int group_select(const FCtx& x, int r, int g, const F
     }
     const uint32_t p = (uint32_t)(uw * 256 + tid);
     if (kw != kNoKey && p >= P0 && p < P1) {  // a listed entry: iw < the row's visible count
-      const uint32_t* row = reinterpret_cast<const uint32_t*>(a.kv_pool + ((size_t)f.pbase + iw) * 512u);
+      const uint32_t* row = reinterpret_cast<const uint32_t*>(a.kv_pool + (size_t)pool_row(f, iw) * 512u);
       warm0 = row[0];
       warm1 = row[32];
       warm2 = row[64];
@@ -1102,22 +1131,32 @@ __device__ __forceinline__ void attend_item(const FCtx& x, int r, int kind, int 
   constexpr uint64_t RB = 2 * 128 * 2;
   // Row addresses from 32-bit offsets against per-row bases: list positions
   // below `split` are pooled rows (selected ones for kind 0, HCA rows for
-  // kind 2), the rest are window tokens t - W + 1 + (p - split).
+  // kind 2), the rest are window tokens t - W + 1 + (p - split).  Logical
+  // rows below the shared prefix's count come from the prefix holder.
   const uint8_t* pool_base = kind == 0 ? a.kv_pool + (size_t)f.pbase * RB : a.kv_hpool + (size_t)f.hbase * RB;
+  const uint8_t* pre_pool = kind == 0 ? a.kv_pool + (size_t)f.ppbase * RB : a.kv_hpool + (size_t)f.phbase * RB;
+  const int32_t pre_pool_n = (int32_t)(kind == 0 ? f.pre_p : f.pre_h);
   const uint8_t* raw_base = a.kv_raw + (size_t)f.tok_base * RB;
+  const uint8_t* pre_raw = a.kv_raw + (size_t)f.ptbase * RB;
+  const int32_t pre_raw_n = (int32_t)f.pre_t;
   const int32_t pb32 = (int32_t)p_begin;
   const int32_t split = kind == 1 ? 0 : (int32_t)a.max_hpool;
   const int32_t hi_pool = (int32_t)f.n_vis_h;
   const int32_t win_off = (int32_t)(f.t + 1 - (kind == 1 ? a.W : a.W_hca)) - split;
+  auto pooled = [&](int32_t j) -> const uint8_t* {
+    return j < pre_pool_n ? pre_pool + (uint64_t)(uint32_t)j * RB
+                          : pool_base + (uint64_t)(uint32_t)(j - pre_pool_n) * RB;
+  };
   auto rowptr = [&](int64_t p64) -> const uint8_t* {
     const int32_t p = (int32_t)p64;
     if (kind == 0) {
       const int32_t j = idx_s[p - pb32];
-      return j >= 0 ? pool_base + (uint64_t)(uint32_t)j * RB : nullptr;
+      return j >= 0 ? pooled(j) : nullptr;
     }
-    if (p < split) return p < hi_pool ? pool_base + (uint64_t)(uint32_t)p * RB : nullptr;
+    if (p < split) return p < hi_pool ? pooled(p) : nullptr;
     const int32_t u = p + win_off;
-    return u >= 0 ? raw_base + (uint64_t)(uint32_t)u * RB : nullptr;
+    if (u < 0) return nullptr;
+    return u < pre_raw_n ? pre_raw + (uint64_t)(uint32_t)u * RB : raw_base + (uint64_t)(uint32_t)(u - pre_raw_n) * RB;
   };
   AttnState<1> st;
   attn_init<1>(st, a.q + (size_t)r * a.H * 128 * 2, a.H);
@@ -1364,7 +1403,7 @@ size_t fused_error_word_offset() { return W_ERROR * 4; }
 size_t fused_fallback_word_offset() { return W_FALLBACK * 4; }
 
 int launch_fused(int R, const int64_t* tok_off, const int64_t* q_pos, const int64_t* pool_off,
-                 const int64_t* hpool_off, int64_t max_pool, int64_t max_hpool, int m, int m_hca, int H,
+                 const int64_t* hpool_off, const int32_t* pre_seq, const int64_t* pre_tok, int64_t max_pool, int64_t max_hpool, int m, int m_hca, int H,
                  float scale, int k, int W, int W_hca, const uint8_t* q_codes, const uint8_t* q_scales,
                  const float* w, const uint8_t* k_codes, const uint8_t* k_scales, const void* q,
                  const void* kv_pool, const void* kv_hpool, const void* kv_raw, int32_t* idx, void* csa_out,
@@ -1381,6 +1420,7 @@ int launch_fused(int R, const int64_t* tok_off, const int64_t* q_pos, const int6
   const int n_cs = pl.n_cs_sel + pl.n_cs_win;
   FusedArgs a;
   a.tok_off = tok_off; a.q_pos = q_pos; a.pool_off = pool_off; a.hpool_off = hpool_off;
+  a.pre_seq = pre_seq; a.pre_tok = pre_tok;
   a.R = R; a.m = m; a.m_hca = m_hca; a.H = H; a.k = k; a.W = W; a.W_hca = W_hca;
   a.scale_log2 = scale * kLog2e;
   a.max_pool = max_pool; a.max_hpool = max_hpool;

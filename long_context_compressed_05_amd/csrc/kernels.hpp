@@ -63,7 +63,7 @@ int fused_supported(int64_t R, int64_t max_pool, int64_t max_hpool, int H, int k
 size_t fused_error_word_offset();
 size_t fused_fallback_word_offset();
 int launch_fused(int R, const int64_t* tok_off, const int64_t* q_pos, const int64_t* pool_off,
-                 const int64_t* hpool_off, int64_t max_pool, int64_t max_hpool, int m, int m_hca, int H,
+                 const int64_t* hpool_off, const int32_t* pre_seq, const int64_t* pre_tok, int64_t max_pool, int64_t max_hpool, int m, int m_hca, int H,
                  float scale, int k, int W, int W_hca, const uint8_t* q_codes, const uint8_t* q_scales,
                  const float* w, const uint8_t* k_codes, const uint8_t* k_scales, const void* q,
                  const void* kv_pool, const void* kv_hpool, const void* kv_raw, int32_t* idx, void* csa_out,

@@ -172,3 +172,19 @@ def test_profile_events_validation():
     assert L.csa_profile_events(99, None, None) == csa.CSA_ERR_INVALID
     assert L.csa_profile_events(0, FAKE, None) == csa.CSA_ERR_INVALID
     assert L.csa_profile_events(0, None, None) == 0
+
+
+def test_decode_shared_validation():
+    L = csa.lib()
+    b = _batch(n_seq=4, n_q=4, maxq=1)
+
+    def call(pre=FAKE, pre_tok=FAKE, m=4):
+        return L.csa_hca_decode_shared(ctypes.byref(b), pre, pre_tok, FAKE, 1000, FAKE, 100, m, 128, 64, 128,
+                                       0.088, 64, 128, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                       FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, None)
+    assert call(pre=None) == csa.CSA_ERR_INVALID and "prefix" in L.csa_last_error().decode()
+    assert call(pre_tok=None) == csa.CSA_ERR_INVALID
+    assert call(m=0) == csa.CSA_ERR_INVALID  # the shared entry point checks as csa_hca_decode does
+    import torch
+    if not torch.cuda.is_available():
+        assert call() == csa.CSA_ERR_DEVICE
