@@ -279,6 +279,13 @@ def main():
     except Exception as e:  # reported, never silently replaced
         result["mxfp4_indexer"] = {"error": repr(e)}
 
+    # ---- shared-prefix decode: 4 questions over one ~1M-token document ----------
+    if args.workload == "decode_b4_t1m" and args.path == "fused":
+        try:
+            result["shared_prefix"] = bench_shared_prefix(torch, csa, synth, to_device, log, score_ms)
+        except Exception as e:  # reported, never silently replaced
+            result["shared_prefix"] = {"error": repr(e)}
+
     # ---- prefill indexer (4096-token chunk on a 64K cache) ----------------------
     if not args.no_prefill:
         try:
@@ -393,6 +400,76 @@ def bench_cache_append(torch, csa, layer, wl, host, log, reps: int = 50):
         out[name] = {"tokens": int(n.sum()), "blocks_pooled": blocks, "us": round(us, 2),
                      "bytes": nbytes, "GB/s": round(nbytes / (us * 1e-6) / 1e9, 1)}
     log(f"cache append: {out}")
+    return out
+
+
+def bench_shared_prefix(torch, csa, synth, to_device, log, contiguous_kernel_ms, steps: int = 100, n_rot: int = 8):
+    """csa_hca_decode_shared on 4 questions over one document: sequence 0 holds
+    a 1,048,576-token cache, sequences 1..3 store only their own 8192, 4096 and
+    1024 tokens after a shared prefix of T = 1,032,192 tokens (so every row
+    attends to about a million tokens, like decode_b4_t1m).  Eager launches,
+    HIP events around each, n_rot input sets (queries, indexer keys, HCA cache)
+    rotated as in the main decode timing."""
+    from long_context_compressed_05_amd.step import Layer, Params
+    T, own = 1032192, [8192, 4096, 1024]
+    lengths = [1 << 20] + own
+    wl = synth.Workload("decode_shared_1m", lengths, [L - 1 for L in lengths], k=1024, seed=1006)
+    host = synth.make_inputs(wl)
+    q_pos = np.array([(1 << 20) - 1] + [T + s - 1 for s in own], dtype=np.int64)
+    host["q_pos"] = q_pos
+    p = Params(H=wl.H, d=wl.d, m=wl.m, k=wl.k, W=wl.W, m_hca=wl.m_hca, W_hca=wl.W_hca)
+    layer = Layer.from_host(p, host, "cuda")
+    layer.build_caches()
+    B = len(lengths)
+    logical_pool = [((1 << 20) // wl.m)] + [(T + s) // wl.m for s in own]
+    logical_hpool = [((1 << 20) // wl.m_hca)] + [(T + s) // wl.m_hca for s in own]
+    max_pool, max_hpool = max(logical_pool), max(logical_hpool)
+    pre_seq = torch.tensor([-1, 0, 0, 0], dtype=torch.int32, device="cuda")
+    pre_tok = torch.tensor([0, T, T, T], dtype=torch.int64, device="cuda")
+    P_tot = int(host["pool_off"][-1])
+    sets = []
+    for r in range(n_rot):
+        s = wl.seed + 7919 * (r + 1)
+        hs = {"q": synth.normal(s, synth.S_Q, B * wl.H * wl.d, wl.dtype).reshape(B, wl.H, wl.d),
+              "qc": synth.codes4(s, synth.S_QCODE, B * 128, wl.codeset).reshape(B, 4, 32),
+              "qs": synth.exp_bytes(s, synth.S_QSCALE, B * 8, *wl.scale_exp).reshape(B, 4, 2),
+              "w": synth.pow2(s, synth.S_W, B * 4, *wl.w_exp).reshape(B, 4),
+              "kc": synth.codes4(s, synth.S_KCODE, P_tot * 32, wl.codeset).reshape(P_tot, 32),
+              "ks": synth.exp_bytes(s, synth.S_KSCALE, P_tot * 2, *wl.scale_exp).reshape(P_tot, 2)}
+        d = to_device(hs)
+        d["hp"] = layer.hpooled.clone()
+        sets.append(d)
+    ws = csa.Workspace()
+
+    def step(i):
+        d = sets[i % n_rot]
+        return csa.csa_hca_decode_shared(layer.batch, pre_seq, pre_tok, layer.pool_off, max_pool, layer.hpool_off,
+                                         max_hpool, wl.m, wl.m_hca, wl.k, wl.W, wl.W_hca, 1.0 / math.sqrt(wl.d),
+                                         d["qc"], d["qs"], d["w"], d["kc"], d["ks"], d["q"], layer.pooled, d["hp"],
+                                         layer.kv, ws=ws)
+    for i in range(2 * n_rot):
+        step(i)
+    torch.cuda.synchronize()
+    ev = [(csa.HipEvent(), csa.HipEvent()) for _ in range(steps)]
+    for i in range(steps):
+        csa.csa_profile_events(csa.CSA_K_FUSED, ev[i][0], ev[i][1])
+        step(i)
+    torch.cuda.synchronize()
+    csa.csa_profile_events(csa.CSA_K_FUSED)
+    csa.csa_hca_decode_check(layer.batch, ws)
+    us = float(np.mean([a.elapsed_ms(b) for a, b in ev])) * 1e3
+    es = 2
+    step_bytes = sum(decode_bytes_per_query(logical_pool[b], wl.k, wl.W, int(q_pos[b]) + 1, logical_hpool[b], wl.H,
+                                            wl.d, es) for b in range(B))
+    row = 2 * wl.d * es
+    stored = int(host["tok_off"][-1]) * row + P_tot * (row + 34) + int(host["hpool_off"][-1]) * row
+    logical = (sum(int(x) + 1 for x in q_pos)) * row + sum(logical_pool) * (row + 34) + sum(logical_hpool) * row
+    out = {"workload": wl.name, "prefix_tokens": T, "own_tokens": own, "us_per_step": round(us, 2),
+           "queries_per_s": round(B / (us * 1e-6), 1), "logical_step_bytes": int(step_bytes),
+           "logical_GB/s": round(step_bytes / (us * 1e-6) / 1e9, 1),
+           "contiguous_b4_t1m_kernel_us": round(contiguous_kernel_ms * 1e3, 2),
+           "cache_bytes_stored": stored, "cache_bytes_if_contiguous": logical}
+    log(f"shared prefix: {out}")
     return out
 
 
