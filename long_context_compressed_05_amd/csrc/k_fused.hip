@@ -1335,7 +1335,7 @@ FusedPlan plan_fused(int64_t R, int64_t max_pool, int64_t max_hpool, int H, int 
   FusedPlan p{};
   const int G = fused_grid();
   p.grid = G;
-  p.cs = 64;
+  p.cs = 128;
   p.n_cs_win = split_count(W, p.cs);
   p.hs = 256;
   p.n_hs = split_count(max_hpool + W_hca, p.hs);
@@ -1349,8 +1349,11 @@ FusedPlan plan_fused(int64_t R, int64_t max_pool, int64_t max_hpool, int H, int 
   }
   p.C = (int)(C > kFMaxC ? kFMaxC : C);
   p.n_sc = max_pool > 0 ? (int)((max_pool + p.C - 1) / p.C) : 1;
-  // CSA groups: consecutive chunks holding about 64 selected entries each
-  const int64_t want = split_count(k, 64) > 0 ? split_count(k, 64) : 1;
+  // CSA groups: consecutive chunks holding about 64 selected entries each for
+  // up to 8 rows, 128 for more (measured: fewer, longer groups pay off once
+  // the rows' groups would take more than a quarter of the grid)
+  const int per_group = R > 8 ? 128 : 64;
+  const int64_t want = split_count(k, per_group) > 0 ? split_count(k, per_group) : 1;
   p.cg = (int)((p.n_sc + want - 1) / want);
   if (p.cg < 1) p.cg = 1;
   p.n_cs_sel = (p.n_sc + p.cg - 1) / p.cg;
