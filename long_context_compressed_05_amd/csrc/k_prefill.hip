@@ -111,38 +111,54 @@ __device__ __forceinline__ uint32_t pf_key(const v16f& acc, int s) {
   return __float_as_uint((r0 + r1) + (r2 + r3));
 }
 
-// candidate bits of score index E & 3 of MFMA output c (this lane's query
-// E = 4 o + s) -> lanes 2E (the query of lanes 0-31) and 2E + 1 of word;
+// candidate mask of score index E & 3 of MFMA output c (this lane's query
+// E = 4 o + s: the query of lanes 0-31 is slot 2E, of lanes 32-63 slot 2E + 1);
 // WHOLE: every query sees the tile's 32 keys
 template <int E, bool WHOLE>
-__device__ __forceinline__ void pf_word(uint32_t& word, const v16f& c, int j, const int (&nq)[kPfRows / 2],
-                                        const uint32_t (&tq)[kPfRows / 2]) {
+__device__ __forceinline__ uint64_t pf_mask(const v16f& c, int j, const int (&nq)[kPfRows / 2],
+                                            const uint32_t (&tq)[kPfRows / 2]) {
   const uint32_t key = pf_key(c, E & 3);
-  const uint64_t m = __builtin_amdgcn_ballot_w64(WHOLE ? key >= tq[E] : (j < nq[E] && key >= tq[E]));
-  const int lane = lane_tid() & 63;
-  word = lane == 2 * E ? (uint32_t)m : word;
-  word = lane == 2 * E + 1 ? (uint32_t)(m >> 32) : word;
+  return __builtin_amdgcn_ballot_w64(WHOLE ? key >= tq[E] : (j < nq[E] && key >= tq[E]));
 }
 
+// one tile's 16 candidate words (query slot L in lane L): the 8 ballots' halves
+// go straight from the scalar masks into lanes 0..15 with v_writelane; the
+// masks are written by VALU compares, so the block starts with the wait states
+// a VALU-written SGPR needs before v_writelane may read it
 template <bool WHOLE>
 __device__ __forceinline__ uint32_t pf_tile_word(const v8i (&av)[2], const int (&asc)[2], const uint4& kc, int ks,
                                                  int j, const int (&nq)[kPfRows / 2],
                                                  const uint32_t (&tq)[kPfRows / 2]) {
-  uint32_t word = 0u;
+  uint64_t m[8];
   {
     const v16f c = pf_mfma(av[0], asc[0], kc, ks);
-    pf_word<0, WHOLE>(word, c, j, nq, tq);
-    pf_word<1, WHOLE>(word, c, j, nq, tq);
-    pf_word<2, WHOLE>(word, c, j, nq, tq);
-    pf_word<3, WHOLE>(word, c, j, nq, tq);
+    m[0] = pf_mask<0, WHOLE>(c, j, nq, tq);
+    m[1] = pf_mask<1, WHOLE>(c, j, nq, tq);
+    m[2] = pf_mask<2, WHOLE>(c, j, nq, tq);
+    m[3] = pf_mask<3, WHOLE>(c, j, nq, tq);
   }
   {
     const v16f c = pf_mfma(av[1], asc[1], kc, ks);
-    pf_word<4, WHOLE>(word, c, j, nq, tq);
-    pf_word<5, WHOLE>(word, c, j, nq, tq);
-    pf_word<6, WHOLE>(word, c, j, nq, tq);
-    pf_word<7, WHOLE>(word, c, j, nq, tq);
+    m[4] = pf_mask<4, WHOLE>(c, j, nq, tq);
+    m[5] = pf_mask<5, WHOLE>(c, j, nq, tq);
+    m[6] = pf_mask<6, WHOLE>(c, j, nq, tq);
+    m[7] = pf_mask<7, WHOLE>(c, j, nq, tq);
   }
+  uint32_t word = 0u;
+  asm("s_nop 4\n\t"
+      "v_writelane_b32 %0, %1, 0\n\tv_writelane_b32 %0, %2, 1\n\t"
+      "v_writelane_b32 %0, %3, 2\n\tv_writelane_b32 %0, %4, 3\n\t"
+      "v_writelane_b32 %0, %5, 4\n\tv_writelane_b32 %0, %6, 5\n\t"
+      "v_writelane_b32 %0, %7, 6\n\tv_writelane_b32 %0, %8, 7\n\t"
+      "v_writelane_b32 %0, %9, 8\n\tv_writelane_b32 %0, %10, 9\n\t"
+      "v_writelane_b32 %0, %11, 10\n\tv_writelane_b32 %0, %12, 11\n\t"
+      "v_writelane_b32 %0, %13, 12\n\tv_writelane_b32 %0, %14, 13\n\t"
+      "v_writelane_b32 %0, %15, 14\n\tv_writelane_b32 %0, %16, 15"
+      : "+v"(word)
+      : "s"((uint32_t)m[0]), "s"((uint32_t)(m[0] >> 32)), "s"((uint32_t)m[1]), "s"((uint32_t)(m[1] >> 32)),
+        "s"((uint32_t)m[2]), "s"((uint32_t)(m[2] >> 32)), "s"((uint32_t)m[3]), "s"((uint32_t)(m[3] >> 32)),
+        "s"((uint32_t)m[4]), "s"((uint32_t)(m[4] >> 32)), "s"((uint32_t)m[5]), "s"((uint32_t)(m[5] >> 32)),
+        "s"((uint32_t)m[6]), "s"((uint32_t)(m[6] >> 32)), "s"((uint32_t)m[7]), "s"((uint32_t)(m[7] >> 32)));
   return word;
 }
 
