@@ -58,6 +58,7 @@ def main():
     ap.add_argument("--rotate", type=int, default=20, help="input sets cycled through the timed steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-shared", action="store_true", help="skip the shared-prefix decode section")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of a captured HIP graph")
     ap.add_argument("--path", choices=["fused", "separate"], default="fused",
                     help="fused: one csa_hca_decode launch per step; separate: csa_index_topk + csa_sparse_attn + hca_attn")
@@ -280,7 +281,7 @@ def main():
         result["mxfp4_indexer"] = {"error": repr(e)}
 
     # ---- shared-prefix decode: 4 questions over one ~1M-token document ----------
-    if args.workload == "decode_b4_t1m" and args.path == "fused":
+    if args.workload == "decode_b4_t1m" and args.path == "fused" and not args.no_shared:
         try:
             result["shared_prefix"] = bench_shared_prefix(torch, csa, synth, to_device, log, score_ms)
         except Exception as e:  # reported, never silently replaced
