@@ -2,21 +2,24 @@
 //
 // The whole decode hot path runs in one kernel whose workgroups (one per CU)
 // take work units in dependency order:
-//   score   chunk c of row r: one of n_sc equal parts of the query's visible range,
-//           MXFP4 MFMA scores -> u32 sort keys in LDS; one adaptive radix pass
-//           finds a threshold tau so that about lst entries have key >= tau;
-//           every entry with key >= tau (at most lst of them) is written to the
-//           chunk's lst list positions in ascending index order, each position
-//           a tagged entry (empty ones included), with tau beside them; then
-//           the chunk's keys are stored for the exact fallback
+//   score   chunk c of row r: one of the row's nsc equal parts of the query's
+//           visible range (nsc <= n_sc), MXFP4 MFMA scores -> u32 sort keys
+//           in LDS, each counted into fixed bins as it is made; the bin
+//           holding the chunk's Lm-th largest key (refined by one radix pass
+//           when that bin is crowded) gives a threshold tau; every entry with
+//           key >= tau (at most L of them) is written to the chunk's L list
+//           positions in ascending index order, each position a tagged entry
+//           (empty ones included), with tau beside them; then the chunk's
+//           keys are stored for the exact fallback
 //   group   CSA group g of row r (cg consecutive chunks, about 64 selected
-//           entries): reads the whole row's lists (one round of loads), finds
-//           K* = the k_eff-th largest listed key (radix select in LDS), checks
-//           that every truncated chunk has tau <= K* (else the row's first
-//           group runs an exact radix select over the stored keys and
-//           publishes it), cuts the ties in list (= index) order, takes its own
-//           chunks' selected entries, attends over those pooled rows, writes
-//           its partial and its slice of idx
+//           entries, 128 beyond 8 rows): reads the whole row's lists (one
+//           round of loads), warms the caches with the rows listed at its own
+//           positions, finds K* = the k_eff-th largest listed key (radix
+//           select in LDS), checks that every truncated chunk has tau <= K*
+//           (else the row's first group runs an exact radix select over the
+//           stored keys and publishes it), ranks its own positions' taken
+//           entries (cutting ties in list = index order), attends over those
+//           pooled rows, writes its partial and its slice of idx
 //   window / HCA split: attention over raw window rows / pooled HCA rows
 //   merge   log-sum-exp merge of a row's split partials, 4 heads per unit
 // (units: [score chunks | CSA groups | window splits | HCA splits | HCA
