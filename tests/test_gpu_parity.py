@@ -650,3 +650,30 @@ def test_shared_prefix_decode_is_bit_identical_to_contiguous_caches(name):
         P.check_close(co[r:r + 1], o[None], wl.dtype, f"csa output of row {r}")
         ho_r, hl_r = oracle.hca_query(host["kv"][t0:t1], host["z"][t0:t1], host["q"][r], t, wl.m_hca, wl.W_hca, scale)
         P.check_close(hop[r:r + 1], ho_r[None], wl.dtype, f"hca output of row {r}")
+
+
+def test_shared_prefix_entry_without_prefixes_equals_plain_decode():
+    """csa_hca_decode_shared with no prefix (-1, or a holder out of range, or
+    the sequence itself, or T = 0) reads each sequence's own rows only and
+    gives csa_hca_decode's outputs bit for bit."""
+    csa = _lib()
+    wl = small_wl("decode_shared_none", [3001, 2998, 4097, 5003], [1] * 4, k=128, seed=34)
+    host = synth.make_inputs(wl)
+    from long_context_compressed_05_amd.step import Layer, to_device
+    layer = Layer.from_host(_params(wl), host)
+    layer.build_caches()
+    dq = to_device({k: host[k] for k in ("q", "qc", "qs", "w")})
+    want = [P.torch_to_np(t) for t in layer.decode_fused(dq["q"], dq["qc"], dq["qs"], dq["w"])]
+    layer.check_fused()
+    p = layer.p
+    pre_seq = torch.tensor([-1, 7, 2, 0], dtype=torch.int32, device="cuda")  # none, out of range, itself, T = 0
+    pre_tok = torch.tensor([4096, 1024, 1024, 0], dtype=torch.int64, device="cuda")
+    ws = csa.Workspace()
+    got = [P.torch_to_np(t) for t in csa.csa_hca_decode_shared(
+        layer.batch, pre_seq, pre_tok, layer.pool_off, layer.max_pool, layer.hpool_off, layer.max_hpool, p.m,
+        p.m_hca, p.k, p.W, p.W_hca, p.sm_scale, dq["qc"], dq["qs"], dq["w"], layer.kc, layer.ks, dq["q"],
+        layer.pooled, layer.hpooled, layer.kv, ws=ws)]
+    csa.csa_hca_decode_check(layer.batch, ws)
+    torch.cuda.synchronize()
+    for what, x, y in zip(("idx", "csa_out", "csa_lse", "hca_out", "hca_lse"), got, want):
+        assert np.array_equal(x, y), f"{what} differs from csa_hca_decode"
