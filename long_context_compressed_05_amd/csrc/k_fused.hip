@@ -522,11 +522,15 @@ __device__ __forceinline__ uint32_t kth_key(const uint32_t (&kv)[NK], uint32_t v
       // few keys left in [lo, hi]: gather them (in no particular order) and
       // rank each against the others instead of another pass; the key with
       // (greater < need <= greater + equal) is the answer
-      uint32_t* cand = hist + (pass & 1 ? 0 : kFHist);  // the idle histogram: zeroed
-      uint32_t* ncand = cand + 64;
+      uint32_t* cand = hist + (pass & 1 ? 0 : kFHist);  // the idle histogram
+      uint32_t inr = 0;  // this thread's keys in [lo, hi]
+#pragma unroll
+      for (int i = 0; i < NK; ++i) inr |= (((vm >> i) & 1u) && kv[i] >= lo && kv[i] <= hi) ? (1u << i) : 0u;
+      uint32_t n_in;
+      uint32_t at = block_exscan_val((uint32_t)__builtin_popcount(inr), scr, &n_in);  // n_in == cnt
 #pragma unroll
       for (int i = 0; i < NK; ++i)
-        if (((vm >> i) & 1u) && kv[i] >= lo && kv[i] <= hi) cand[atomicAdd(ncand, 1u)] = kv[i];
+        if ((inr >> i) & 1u) cand[at++] = kv[i];
       __syncthreads();
       const int tid = lane_tid();
       if (tid < (int)cnt) {
@@ -991,13 +995,12 @@ __device__ __forceinline__ int group_select(const FCtx& x, int r, int g, const F
   if (exact) {
     // to contiguous ownership (the histograms are free again): thread t takes
     // positions [t*M, t*M + M), so position order is thread order
+    // (unconditional: kFEPT * 256 = kFEntLds, and positions past npos hold kNoKey)
 #pragma unroll
     for (int u = 0; u < kFEPT; ++u) {
       const uint32_t p = (uint32_t)(u * 256 + tid);
-      if (p < npos) {
-        lk[p] = kv[u];
-        li[p] = ix[u];
-      }
+      lk[p] = kv[u];
+      li[p] = ix[u];
     }
     __syncthreads();
     exact = uni(x.scr[S_BAD]) == 0u;
