@@ -414,6 +414,8 @@ FUSED_CASES = {
                                              W=200, m=4, m_hca=64, W_hca=64, seed=15),
     "decode_bf16_long": lambda: small_wl("decode_bf16_long", [160001, 200003, 150002, 99999], [1] * 4, k=1024,
                                          seed=16),
+    # one long row: 74 chunks of 1024, 4440 list positions (the 24-slot selection)
+    "decode_bf16_single_300k": lambda: small_wl("decode_bf16_single_300k", [300001], [1], k=1024, seed=18),
 }
 
 
