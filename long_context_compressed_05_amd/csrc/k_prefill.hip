@@ -41,7 +41,7 @@
 
 namespace csa {
 
-constexpr int kPfRowsT = 8;        // queries per threshold block (one MFMA A operand)
+constexpr int kPfRowsT = 4;        // queries per threshold block: one per wave (half an MFMA A operand)
 constexpr int kPfRows = 16;        // queries per score block (two MFMA A operands)
 constexpr int kPfKeysWG = 4096;    // keys per scoring workgroup, at least (a multiple of 128)
 constexpr int kPfSampleMax = 2048;  // sample keys per query
