@@ -15,7 +15,8 @@
  *    token, attention over the top candidates, a sliding window of recent
  *    tokens; HCA attends to every compressed entry.  KV-cache section: the
  *    cache is split into compressed entries, the window, and the tail of
- *    tokens not yet numerous enough to form a block.
+ *    tokens not yet numerous enough to form a block; a cache computed for a
+ *    shared prefix is kept and reused by later requests over it.
  *  - jyp-garden EP 95 notes, IDEAS: multi-query attention (one shared KV head).
  *
  * Conventions for every entry point
