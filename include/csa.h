@@ -307,6 +307,43 @@ int csa_hca_decode_shared(const csa_batch* b, const int32_t* prefix_seq, const i
                           float* csa_lse, void* hca_out, float* hca_lse, void* ws, size_t ws_bytes,
                           void* stream);
 
+/* ------------------------------------------------------------------------
+ * csa_hca_decode_paged — csa_hca_decode over paged pooled caches.
+ * Pages: sigco.tistory.com KV-cache section (the compressed caches are kept
+ * apart from the window and the tail, and a prefix's cache is reused by later
+ * requests): here the compressed caches live in fixed-size pages that
+ * sequences map through page tables, so pages can be allocated one at a time
+ * as a sequence grows and a shared prefix's pages can appear in several
+ * tables (see also csa_hca_decode_shared).
+ * Sequence b's pooled row j (block m; and its indexer key row, paged the same
+ * way) is row page_table[b][j / page_rows] * page_rows + j % page_rows of
+ * kv_pool / k_codes / k_scales, for j < pooled_rows[b]; its HCA row j (block
+ * m_hca) is row hca_page_table[b][j / hca_page_rows] * hca_page_rows +
+ * j % hca_page_rows of kv_pool_hca, for j < hca_pooled_rows[b].  Raw rows
+ * (window) stay contiguous: tok_off[b] + u.  Outputs, idx (indices into the
+ * logical pooled rows) and exactness are those of csa_hca_decode over the
+ * same logical caches, bit for bit.
+ *   page_table [n_seq][max_pages] int32 device, hca_page_table
+ *   [n_seq][max_hca_pages]; pooled_rows, hca_pooled_rows [n_seq] int64
+ *   device.  page_rows and hca_page_rows: powers of two, >= 32.  The kernel
+ *   clamps each count to what its table maps; page ids are trusted.
+ *   max_pool / max_hpool bound the pooled counts (and the tables must map
+ *   them).  Other arguments, workspace and errors as csa_hca_decode (its
+ *   pool_off / hpool_off are replaced by the tables); CSA_ERR_INVALID also for
+ *   NULL tables or counts, page sizes that are not powers of two >= 32,
+ *   tables with no column, or tables mapping fewer rows than max_pool /
+ *   max_hpool.
+ * ---------------------------------------------------------------------- */
+int csa_hca_decode_paged(const csa_batch* b, int page_rows, const int32_t* page_table, int max_pages,
+                         const int64_t* pooled_rows, int hca_page_rows, const int32_t* hca_page_table,
+                         int max_hca_pages, const int64_t* hca_pooled_rows, int64_t max_pool, int64_t max_hpool,
+                         int m, int m_hca, int H, int d, float scale, int k, int W, int W_hca,
+                         const uint8_t* q_codes, const uint8_t* q_scales, const float* w,
+                         const uint8_t* k_codes, const uint8_t* k_scales, const void* q, const void* kv_pool,
+                         const void* kv_pool_hca, const void* kv_raw, int32_t* idx, void* csa_out,
+                         float* csa_lse, void* hca_out, float* hca_lse, void* ws, size_t ws_bytes,
+                         void* stream);
+
 /* Synchronises `stream`, then returns CSA_OK if no csa_hca_decode launch on
  * workspace `ws` hit its wait bound since the last check, else
  * CSA_ERR_DEVICE; clears the word.  (The only synchronising call.) */

@@ -23,7 +23,8 @@ CSA_F32, CSA_BF16 = 0, 1
 
 EXPORTS = ("csa_status_string", "csa_last_error", "csa_compress", "csa_cache_append", "csa_mxfp4_quantize", "csa_index_topk_workspace",
            "csa_index_topk", "csa_sparse_attn_workspace", "csa_sparse_attn", "hca_attn_workspace",
-           "hca_attn", "csa_hca_decode_workspace", "csa_hca_decode", "csa_hca_decode_shared", "csa_hca_decode_check",
+           "hca_attn", "csa_hca_decode_workspace", "csa_hca_decode", "csa_hca_decode_shared", "csa_hca_decode_paged",
+           "csa_hca_decode_check",
            "csa_hca_decode_fallbacks", "csa_profile_events")
 (CSA_K_IDX_SCORE, CSA_K_IDX_SELECT, CSA_K_IDX_FINAL, CSA_K_ATTN, CSA_K_ATTN_COMBINE, CSA_K_COMPRESS,
  CSA_K_FUSED, CSA_K_PF_THRESH, CSA_K_PF_SELECT, CSA_K_APPEND, CSA_K_QUANT) = range(11)
@@ -69,6 +70,8 @@ def lib():
                                  vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.csa_hca_decode_shared.argtypes = [bp, vp, vp, vp, i64, vp, i64, ci, ci, ci, ci, ctypes.c_float, ci, ci, ci, vp,
                                         vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.csa_hca_decode_paged.argtypes = [bp, ci, vp, ci, vp, ci, vp, ci, vp, i64, i64, ci, ci, ci, ci, ctypes.c_float, ci,
+                                       ci, ci, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.csa_hca_decode_check.argtypes = [bp, vp, vp]
     L.csa_hca_decode_fallbacks.argtypes = [vp, vp, ctypes.POINTER(ctypes.c_uint32)]
     L.csa_profile_events.argtypes = [ci, vp, vp]
@@ -393,6 +396,38 @@ def csa_hca_decode_shared(batch: Batch, prefix_seq, prefix_tokens, pool_off, max
                                        _ptr(q), _ptr(kv_pool), _ptr(kv_pool_hca), _ptr(kv_raw), _ptr(idx),
                                        _ptr(csa_out), _ptr(csa_lse), _ptr(hca_out), _ptr(hca_lse), _ptr(buf),
                                        nbytes, _stream(stream)), "csa_hca_decode_shared")
+    return idx, csa_out, csa_lse, hca_out, hca_lse
+
+
+def csa_hca_decode_paged(batch: Batch, page_rows: int, page_table, pooled_rows, hca_page_rows: int, hca_page_table,
+                         hca_pooled_rows, max_pool: int, max_hpool: int, m: int, m_hca: int, k: int, W: int,
+                         W_hca: int, scale: float, q_codes, q_scales, w, k_codes, k_scales, q, kv_pool, kv_pool_hca,
+                         kv_raw, idx=None, csa_out=None, csa_lse=None, hca_out=None, hca_lse=None,
+                         ws: Optional[Workspace] = None, stream=None):
+    """csa_hca_decode over paged pooled caches (page tables [n_seq][pages] int32, row counts [n_seq] int64)."""
+    H, d = q.shape[-2], q.shape[-1]
+    dev = q.device
+    if idx is None:
+        idx = torch.empty((batch.n_q, k), dtype=torch.int32, device=dev)
+    if csa_out is None:
+        csa_out = torch.empty_like(q)
+    if hca_out is None:
+        hca_out = torch.empty_like(q)
+    if csa_lse is None:
+        csa_lse = torch.empty((batch.n_q, H), dtype=torch.float32, device=dev)
+    if hca_lse is None:
+        hca_lse = torch.empty((batch.n_q, H), dtype=torch.float32, device=dev)
+    ws = ws or Workspace(dev)
+    nbytes = csa_hca_decode_workspace(batch, max_pool, max_hpool, H, d, k, W, W_hca)
+    buf = ws.get(nbytes)
+    b = batch.c()
+    _check(lib().csa_hca_decode_paged(ctypes.byref(b), page_rows, _ptr(page_table), page_table.shape[-1],
+                                      _ptr(pooled_rows), hca_page_rows, _ptr(hca_page_table),
+                                      hca_page_table.shape[-1], _ptr(hca_pooled_rows), max_pool, max_hpool, m, m_hca,
+                                      H, d, scale, k, W, W_hca, _ptr(q_codes), _ptr(q_scales), _ptr(w),
+                                      _ptr(k_codes), _ptr(k_scales), _ptr(q), _ptr(kv_pool), _ptr(kv_pool_hca),
+                                      _ptr(kv_raw), _ptr(idx), _ptr(csa_out), _ptr(csa_lse), _ptr(hca_out),
+                                      _ptr(hca_lse), _ptr(buf), nbytes, _stream(stream)), "csa_hca_decode_paged")
     return idx, csa_out, csa_lse, hca_out, hca_lse
 
 

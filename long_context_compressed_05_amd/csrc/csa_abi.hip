@@ -103,6 +103,7 @@ int csa_hca_decode_workspace(const csa_batch* b, int64_t max_pool, int64_t max_h
 }
 
 static int hca_decode_impl(const csa_batch* b, const int32_t* pre_seq, const int64_t* pre_tok,
+                           const csa::FusedPaging* paging,
                            const int64_t* pool_off, int64_t max_pool, const int64_t* hpool_off, int64_t max_hpool,
                            int m, int m_hca, int H, int d, float scale, int k, int W, int W_hca,
                            const uint8_t* q_codes, const uint8_t* q_scales, const float* w, const uint8_t* k_codes,
@@ -122,7 +123,7 @@ static int hca_decode_impl(const csa_batch* b, const int32_t* pre_seq, const int
     return fail(CSA_ERR_UNSUPPORTED, "fused decode needs d = 128, 16 <= H <= 64 with H %% 16 == 0, "
                                      "max_pool <= 262144, 1..64 queries and n_q * max_pool <= 3072 * (resident "
                                      "workgroups)");
-  if (!pool_off || !hpool_off || !q_codes || !q_scales || !w || !k_codes || !k_scales || !q || !kv_pool ||
+  if ((!paging && (!pool_off || !hpool_off)) || !q_codes || !q_scales || !w || !k_codes || !k_scales || !q || !kv_pool ||
       (max_hpool > 0 && !kv_pool_hca) || ((W > 0 || W_hca > 0) && !kv_raw) || !idx || !csa_out || !hca_out)
     return fail(CSA_ERR_INVALID, "NULL pointer argument");
   if (!aligned16(q_codes) || !aligned16(k_codes) || !aligned16(q) || !aligned16(kv_pool) ||
@@ -131,7 +132,7 @@ static int hca_decode_impl(const csa_batch* b, const int32_t* pre_seq, const int
   const size_t need = csa::plan_fused(b->n_q, max_pool, max_hpool, H, k, W, W_hca).ws_bytes;
   if (!ws || ws_bytes < need)
     return fail(CSA_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need, ws_bytes);
-  if (csa::launch_fused((int)b->n_q, b->tok_off, b->q_pos, pool_off, hpool_off, pre_seq, pre_tok, max_pool,
+  if (csa::launch_fused((int)b->n_q, b->tok_off, b->q_pos, pool_off, hpool_off, pre_seq, pre_tok, paging, max_pool,
                         max_hpool, m, m_hca, H,
                         scale, k, W, W_hca, q_codes, q_scales, w, k_codes, k_scales, q, kv_pool, kv_pool_hca,
                         kv_raw, idx, csa_out, csa_lse, hca_out, hca_lse, ws, (hipStream_t)stream) != 0) {
@@ -149,7 +150,7 @@ int csa_hca_decode(const csa_batch* b, const int64_t* pool_off, int64_t max_pool
                    const void* kv_pool_hca, const void* kv_raw, int32_t* idx, void* csa_out,
                    float* csa_lse, void* hca_out, float* hca_lse, void* ws, size_t ws_bytes,
                    void* stream) {
-  return hca_decode_impl(b, nullptr, nullptr, pool_off, max_pool, hpool_off, max_hpool, m, m_hca, H, d, scale, k, W,
+  return hca_decode_impl(b, nullptr, nullptr, nullptr, pool_off, max_pool, hpool_off, max_hpool, m, m_hca, H, d, scale, k, W,
                          W_hca, q_codes, q_scales, w, k_codes, k_scales, q, kv_pool, kv_pool_hca, kv_raw, idx,
                          csa_out, csa_lse, hca_out, hca_lse, ws, ws_bytes, stream);
 }
@@ -163,9 +164,33 @@ int csa_hca_decode_shared(const csa_batch* b, const int32_t* prefix_seq, const i
                           float* csa_lse, void* hca_out, float* hca_lse, void* ws, size_t ws_bytes,
                           void* stream) {
   if (!prefix_seq || !prefix_tokens) return fail(CSA_ERR_INVALID, "NULL prefix array");
-  return hca_decode_impl(b, prefix_seq, prefix_tokens, pool_off, max_pool, hpool_off, max_hpool, m, m_hca, H, d,
+  return hca_decode_impl(b, prefix_seq, prefix_tokens, nullptr, pool_off, max_pool, hpool_off, max_hpool, m, m_hca, H, d,
                          scale, k, W, W_hca, q_codes, q_scales, w, k_codes, k_scales, q, kv_pool, kv_pool_hca,
                          kv_raw, idx, csa_out, csa_lse, hca_out, hca_lse, ws, ws_bytes, stream);
+}
+
+int csa_hca_decode_paged(const csa_batch* b, int page_rows, const int32_t* page_table, int max_pages,
+                         const int64_t* pooled_rows, int hca_page_rows, const int32_t* hca_page_table,
+                         int max_hca_pages, const int64_t* hca_pooled_rows, int64_t max_pool, int64_t max_hpool,
+                         int m, int m_hca, int H, int d, float scale, int k, int W, int W_hca,
+                         const uint8_t* q_codes, const uint8_t* q_scales, const float* w,
+                         const uint8_t* k_codes, const uint8_t* k_scales, const void* q, const void* kv_pool,
+                         const void* kv_pool_hca, const void* kv_raw, int32_t* idx, void* csa_out,
+                         float* csa_lse, void* hca_out, float* hca_lse, void* ws, size_t ws_bytes,
+                         void* stream) {
+  if (!page_table || !pooled_rows || !hca_page_table || !hca_pooled_rows)
+    return fail(CSA_ERR_INVALID, "NULL page table or pooled-row count");
+  auto pow2 = [](int v) { return v >= 32 && (v & (v - 1)) == 0; };
+  if (!pow2(page_rows) || !pow2(hca_page_rows))
+    return fail(CSA_ERR_INVALID, "page sizes must be powers of two of at least 32 rows");
+  if (max_pages < 1 || max_hca_pages < 1) return fail(CSA_ERR_INVALID, "page tables need at least one column");
+  if ((int64_t)max_pages * page_rows < max_pool || (int64_t)max_hca_pages * hca_page_rows < max_hpool)
+    return fail(CSA_ERR_INVALID, "the page tables map fewer rows than max_pool / max_hpool");
+  const csa::FusedPaging pg{page_table, pooled_rows, max_pages, page_rows,
+                            hca_page_table, hca_pooled_rows, max_hca_pages, hca_page_rows};
+  return hca_decode_impl(b, nullptr, nullptr, &pg, nullptr, max_pool, nullptr, max_hpool, m, m_hca, H, d, scale, k, W,
+                         W_hca, q_codes, q_scales, w, k_codes, k_scales, q, kv_pool, kv_pool_hca, kv_raw, idx,
+                         csa_out, csa_lse, hca_out, hca_lse, ws, ws_bytes, stream);
 }
 
 int csa_hca_decode_check(const csa_batch* b, const void* ws, void* stream) {

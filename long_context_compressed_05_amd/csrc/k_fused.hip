@@ -73,10 +73,13 @@ constexpr int kOffHist = kOffU + kFEntLds * 4;              // uint32 [2][kFHist
 constexpr int kSelEnd = kOffHist + (2 * kFHist + 64) * 4;
 constexpr int kAttnEnd = kOffU + kAttnLdsBytes;
 constexpr int kFusedLds = kSelEnd > kAttnEnd ? kSelEnd : kAttnEnd;
+constexpr int kOffSelP = kOffSel + (kFMaxSel + 64) * 4;    // int32 [kFMaxSel] physical rows (paged caches)
 static_assert(kOffSel + (kFMaxSel + 64) * 4 <= kOffScr, "a group's selected rows (+ 64 dummy slots) fit the key region");
+static_assert(kOffSelP + kFMaxSel * 4 <= kOffScr, "the selected rows' physical rows fit the key region");
 static_assert(kOffU % 16 == 0 && kOffHist % 16 == 0, "LDS regions must be 16-byte aligned");
 static_assert(kFMaxC * 8 <= kAttnLdsBytes, "a score chunk's staged list fits the union region");
 static_assert(kFBinPad * 4 <= kOffHist - kOffU && kFBinPad % 4 == 0, "a score chunk's fixed bins fit below the radix histograms");
+static_assert((kFBinPad + kFMaxC / 32 + 1) * 4 <= kOffHist - kOffU, "a score chunk's page ids (pages of >= 32 rows) fit after its bins");
 static_assert(2 * kFEntLds * 4 <= kAttnLdsBytes, "a row's keys and indices by position fit the union region");
 static_assert(kFEPT % 4 == 0 && kFEntLds % 4 == 0, "positions are read 16 bytes at a time");
 static_assert(kFusedLds <= 160 * 1024, "one workgroup per CU");
@@ -95,6 +98,14 @@ struct FusedArgs {
   const int64_t* hpool_off;
   const int32_t* pre_seq;  // [R] or null: the sequence whose cache holds this one's prefix (-1: none)
   const int64_t* pre_tok;  // [R] or null: the shared prefix's length in tokens
+  // paged pooled caches (ptab null: contiguous, by pool_off / hpool_off): pooled
+  // row j of row r is row ptab[r][j >> lg_page] << lg_page | (j & page mask) of
+  // kv_pool (and of the indexer keys); HCA rows likewise through hptab
+  const int32_t* ptab;     // [R][max_pages]
+  const int64_t* plen;     // [R] pooled rows per row
+  const int32_t* hptab;    // [R][max_hpages]
+  const int64_t* hplen;    // [R]
+  int max_pages, max_hpages, lg_page, lg_hpage;
   int R, m, m_hca, H, k, W, W_hca;
   float scale_log2;
   int64_t max_pool, max_hpool;
@@ -154,15 +165,28 @@ struct FRow {
 __device__ __forceinline__ int64_t pool_row(const FRow& f, int64_t j) {
   return j < f.pre_p ? f.ppbase + j : f.pbase + (j - f.pre_p);
 }
+// the same through row r's page table (paged caches)
+__device__ __forceinline__ int64_t paged_row(const int32_t* tab_row, int lg, int64_t j) {
+  return ((int64_t)tab_row[j >> lg] << lg) | (j & (((int64_t)1 << lg) - 1));
+}
 
-__device__ __forceinline__ FRow row_info(KArgs& a, int r) {
+__device__ __forceinline__ FRow row_info(KArgs& a, int r, bool paged) {
   FRow f;
   f.t = a.q_pos[r];
-  f.pbase = a.pool_off[r];
-  f.hbase = a.hpool_off[r];
   f.tok_base = a.tok_off[r];
   f.pre_p = f.pre_h = f.pre_t = 0;
   f.ppbase = f.phbase = f.ptbase = 0;
+  if (paged) {  // pooled rows through the page tables, counts clamped to what they map
+    f.pbase = f.hbase = 0;
+    const int64_t cp = (int64_t)a.max_pages << a.lg_page, ch = (int64_t)a.max_hpages << a.lg_hpage;
+    const int64_t P = a.plen[r] < cp ? a.plen[r] : cp, Ph = a.hplen[r] < ch ? a.hplen[r] : ch;
+    const int64_t v = (f.t + 1) / a.m, vh = (f.t + 1) / a.m_hca;
+    f.n_vis = v < P ? v : P;
+    f.n_vis_h = vh < Ph ? vh : Ph;
+    return f;
+  }
+  f.pbase = a.pool_off[r];
+  f.hbase = a.hpool_off[r];
   if (a.pre_seq) {
     const int32_t s = a.pre_seq[r];
     const int64_t T = a.pre_tok[r];
@@ -271,6 +295,7 @@ struct FCtx {
   uint32_t* scr;
   uint32_t tag;
   Coh coh;
+  bool paged;  // pooled caches through page tables (a compile-time constant of the kernel)
 };
 
 // error word: bit 0 = a wait hit its bound, bits 1.. = which wait (see the callers)
@@ -588,6 +613,18 @@ __device__ __forceinline__ void phase_score(const FCtx& x, int r, int c, const F
   // a truncated chunk counts its keys into fixed bins as they are made (the
   // LDS atomics hide under the key stream)
   uint32_t* fh = reinterpret_cast<uint32_t*>(x.smem + kOffU);
+  // paged caches: the chunk's page ids -> LDS first (the key loads need them)
+  const bool paged = x.paged;
+  const int lg = a.lg_page;
+  uint32_t* pg_s = fh + kFBinPad;
+  int64_t pfirst = 0;
+  if (paged) {
+    const int32_t* trow = a.ptab + (size_t)r * a.max_pages;
+    pfirst = j0 >> lg;
+    const int64_t npg = j1 > j0 ? ((j1 - 1) >> lg) - pfirst + 1 : 0;  // j1 <= n_vis <= max_pages << lg
+    for (int64_t i = tid; i < npg; i += 256) pg_s[i] = (uint32_t)trow[pfirst + i];
+    __syncthreads();
+  }
   for (int tb = 0; tb < ntiles; tb += 64) {
     uint4 kcv[16];
     int ksv[16];
@@ -598,7 +635,8 @@ __device__ __forceinline__ void phase_score(const FCtx& x, int r, int c, const F
       kcv[u] = make_uint4(0, 0, 0, 0);
       ksv[u] = 127;
       if (tile < ntiles && j < j1) {
-        const int64_t pj = pool_row(f, j);
+        const int64_t pj = paged ? (((int64_t)pg_s[(j >> lg) - pfirst] << lg) | (j & (((int64_t)1 << lg) - 1)))
+                                 : pool_row(f, j);
         kcv[u] = *reinterpret_cast<const uint4*>(a.k_codes + pj * 32 + kb * 16);
         ksv[u] = a.k_scales[pj * 2 + kb];
       }
@@ -930,7 +968,8 @@ __device__ __forceinline__ int group_select(const FCtx& x, int r, int g, const F
     }
     const uint32_t p = (uint32_t)(uw * 256 + tid);
     if (kw != kNoKey && p >= P0 && p < P1) {  // a listed entry: iw < the row's visible count
-      const uint32_t* row = reinterpret_cast<const uint32_t*>(a.kv_pool + (size_t)pool_row(f, iw) * 512u);
+      const int64_t pr = x.paged ? paged_row(a.ptab + (size_t)r * a.max_pages, a.lg_page, iw) : pool_row(f, iw);
+      const uint32_t* row = reinterpret_cast<const uint32_t*>(a.kv_pool + (size_t)pr * 512u);
       warm0 = row[0];
       warm1 = row[32];
       warm2 = row[64];
@@ -1153,13 +1192,33 @@ __device__ __forceinline__ void attend_item(const FCtx& x, int r, int kind, int 
     return j < pre_pool_n ? pre_pool + (uint64_t)(uint32_t)j * RB
                           : pool_base + (uint64_t)(uint32_t)(j - pre_pool_n) * RB;
   };
+  // paged caches: CSA groups read the physical rows their selection was
+  // translated to; an HCA split takes its range's page ids into LDS first
+  const bool paged = x.paged;
+  const int32_t* idx_p = reinterpret_cast<const int32_t*>(x.smem + kOffSelP) + sel_base;
+  uint32_t* hpg_s = reinterpret_cast<uint32_t*>(x.smem + kOffSel);
+  const int hlg = a.lg_hpage;
+  const int32_t hfirst = (int32_t)(p_begin >> hlg);
+  if (paged && kind == 2) {
+    const int64_t pe = p_end < f.n_vis_h ? p_end : f.n_vis_h;  // <= max_hpages << hlg
+    const int64_t npg = pe > p_begin ? ((pe - 1) >> hlg) - hfirst + 1 : 0;
+    const int32_t* trow = a.hptab + (size_t)r * a.max_hpages;
+    for (int64_t i = lane_tid(); i < npg; i += 256) hpg_s[i] = (uint32_t)trow[hfirst + i];
+    __syncthreads();
+  }
   auto rowptr = [&](int64_t p64) -> const uint8_t* {
     const int32_t p = (int32_t)p64;
     if (kind == 0) {
       const int32_t j = idx_s[p - pb32];
-      return j >= 0 ? pooled(j) : nullptr;
+      if (j < 0) return nullptr;
+      return paged ? a.kv_pool + (uint64_t)(uint32_t)idx_p[p - pb32] * RB : pooled(j);
     }
-    if (p < split) return p < hi_pool ? pooled(p) : nullptr;
+    if (p < split) {
+      if (p >= hi_pool) return nullptr;
+      if (!paged) return pooled(p);
+      const uint32_t pr = (hpg_s[(p >> hlg) - hfirst] << hlg) | ((uint32_t)p & ((1u << hlg) - 1u));
+      return a.kv_hpool + (uint64_t)pr * RB;
+    }
     const int32_t u = p + win_off;
     if (u < 0) return nullptr;
     return u < pre_raw_n ? pre_raw + (uint64_t)(uint32_t)u * RB : raw_base + (uint64_t)(uint32_t)(u - pre_raw_n) * RB;
@@ -1223,6 +1282,8 @@ __device__ __forceinline__ void item_merge(const FCtx& x, bool hca, int r, int h
 }
 
 // ---------------------------------------------------------------------------
+// kPaged: the pooled caches are read through page tables (csa_hca_decode_paged)
+template <bool kPaged>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_decode_fused(FusedArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
   uint32_t* scr = reinterpret_cast<uint32_t*>(smem + kOffScr);
@@ -1239,8 +1300,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   // atomic, claimed one round ahead; a workgroup runs its units in the order
   // it claimed them, and a unit only waits for units of lower number.  The
   // lowest unfinished unit therefore never waits, and its workgroup is either
-  // running it or running a unit of lower number still: every wait ends,
-  // whatever the residency of the grid.  Every workgroup runs the same number
+  // running it or running a unit of lower number still: every wait ends while
+  // the grid's workgroups are resident (one per CU, as the launch sizes it).  Every workgroup runs the same number
   // of rounds (rounds * grid >= total), so the loop bound is uniform; a round
   // whose unit number is past the end does nothing.
   uint32_t next_ticket = 0;  // lane 0: the unit number of the next round, fetched one round ahead
@@ -1248,7 +1309,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     KArgs* ap = (KArgs*)__builtin_amdgcn_kernarg_segment_ptr();
     asm volatile("" : "+s"(ap));
     KArgs& A = *ap;
-    const FCtx x{ap, smem, scr, tag, make_coh(A.ctl)};
+    const FCtx x{ap, smem, scr, tag, make_coh(A.ctl), kPaged};
     const int R = A.R, nM = A.H / 4;
     const int64_t u_grp = (int64_t)R * A.n_sc;
     const int64_t u_win = u_grp + (int64_t)R * A.n_cs_sel, u_hca = u_win + (int64_t)R * A.n_cs_win;
@@ -1269,7 +1330,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     } else if (it < u_grp) {
       // chunk-major: every row's first chunks come first (a short row uses fewer chunks)
       const int c = (int)(it / R), r = (int)(it % R);
-      const FRow f = row_info(A, r);
+      const FRow f = row_info(A, r, kPaged);
       const RowLayout lay = row_layout(A, f);
       if (c < lay.nsc) {
         int64_t j0 = (int64_t)c * lay.C, j1 = j0 + lay.C;
@@ -1284,10 +1345,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     } else if (it < u_win) {
       const int64_t q = it - u_grp;
       const int r = (int)(q % R), g = (int)(q / R);
-      const FRow f = row_info(A, r);
+      const FRow f = row_info(A, r, kPaged);
       uint32_t off = 0, base = 0;
       const int n_sel = group_select(x, r, g, f, &off, &base);
       if (n_sel >= 0) {
+        if (kPaged) {  // paged caches: the selected rows' physical rows -> LDS
+          const int32_t* sel_s = reinterpret_cast<const int32_t*>(smem + kOffSel) + base;
+          int32_t* sel_p = reinterpret_cast<int32_t*>(smem + kOffSelP) + base;
+          const int32_t* trow = A.ptab + (size_t)r * A.max_pages;
+          for (int i = lane_tid(); i < n_sel; i += 256) sel_p[i] = (int32_t)paged_row(trow, A.lg_page, sel_s[i]);
+          __syncthreads();
+        }
         attend_item(x, r, 0, g, f, n_sel, base);
         group_write_idx(x, r, off, n_sel, base);
       }
@@ -1296,7 +1364,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
       const int kind = it < u_hca ? 1 : 2;
       const int64_t q = it - (kind == 1 ? u_win : u_hca);
       const int r = (int)(q % R), s = (int)(q / R);
-      attend_item(x, r, kind, s, row_info(A, r), 0);
+      attend_item(x, r, kind, s, row_info(A, r, kPaged), 0);
     }
   }
   const int G = (int)gridDim.x;
@@ -1322,10 +1390,13 @@ static int fused_grid() {
   int dev = 0, cus = 0, per_cu = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-  if (hipFuncSetAttribute((const void*)k_decode_fused, hipFuncAttributeMaxDynamicSharedMemorySize, kFusedLds) !=
-      hipSuccess)
+  if (hipFuncSetAttribute((const void*)k_decode_fused<false>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                          kFusedLds) != hipSuccess ||
+      hipFuncSetAttribute((const void*)k_decode_fused<true>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                          kFusedLds) != hipSuccess)
     return 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)k_decode_fused, 256, kFusedLds) != hipSuccess)
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)k_decode_fused<false>, 256, kFusedLds) !=
+      hipSuccess)
     return 0;
   if (per_cu < 1) return 0;
   // One workgroup per CU: two score workgroups sharing a CU's memory pipeline
@@ -1412,7 +1483,8 @@ size_t fused_error_word_offset() { return W_ERROR * 4; }
 size_t fused_fallback_word_offset() { return W_FALLBACK * 4; }
 
 int launch_fused(int R, const int64_t* tok_off, const int64_t* q_pos, const int64_t* pool_off,
-                 const int64_t* hpool_off, const int32_t* pre_seq, const int64_t* pre_tok, int64_t max_pool, int64_t max_hpool, int m, int m_hca, int H,
+                 const int64_t* hpool_off, const int32_t* pre_seq, const int64_t* pre_tok, const FusedPaging* paging,
+                 int64_t max_pool, int64_t max_hpool, int m, int m_hca, int H,
                  float scale, int k, int W, int W_hca, const uint8_t* q_codes, const uint8_t* q_scales,
                  const float* w, const uint8_t* k_codes, const uint8_t* k_scales, const void* q,
                  const void* kv_pool, const void* kv_hpool, const void* kv_raw, int32_t* idx, void* csa_out,
@@ -1430,6 +1502,14 @@ int launch_fused(int R, const int64_t* tok_off, const int64_t* q_pos, const int6
   FusedArgs a;
   a.tok_off = tok_off; a.q_pos = q_pos; a.pool_off = pool_off; a.hpool_off = hpool_off;
   a.pre_seq = pre_seq; a.pre_tok = pre_tok;
+  a.ptab = nullptr; a.plen = nullptr; a.hptab = nullptr; a.hplen = nullptr;
+  a.max_pages = a.max_hpages = 0; a.lg_page = a.lg_hpage = 0;
+  if (paging) {
+    a.ptab = paging->ptab; a.plen = paging->plen; a.max_pages = paging->max_pages;
+    a.hptab = paging->hptab; a.hplen = paging->hplen; a.max_hpages = paging->max_hpages;
+    a.lg_page = __builtin_ctz((unsigned)paging->page_rows);
+    a.lg_hpage = __builtin_ctz((unsigned)paging->hpage_rows);
+  }
   a.R = R; a.m = m; a.m_hca = m_hca; a.H = H; a.k = k; a.W = W; a.W_hca = W_hca;
   a.scale_log2 = scale * kLog2e;
   a.max_pool = max_pool; a.max_hpool = max_hpool;
@@ -1460,9 +1540,10 @@ int launch_fused(int R, const int64_t* tok_off, const int64_t* q_pos, const int6
   a.hca_pml = (float*)take((size_t)R * pl.n_hs * H * 2 * 4);
   void* args[] = {&a};
   prof_begin(6, stream);
-  // an ordinary launch: correctness does not depend on all workgroups being resident
+  // an ordinary launch of one workgroup per CU (all resident at once)
   const hipError_t e =
-      hipLaunchKernel((const void*)k_decode_fused, dim3((unsigned)pl.grid), dim3(256), args, kFusedLds, stream);
+      hipLaunchKernel(paging ? (const void*)k_decode_fused<true> : (const void*)k_decode_fused<false>,
+                      dim3((unsigned)pl.grid), dim3(256), args, kFusedLds, stream);
   prof_end(6, stream);
   if (e != hipSuccess) return -1;
   return hipGetLastError() == hipSuccess ? 0 : -1;

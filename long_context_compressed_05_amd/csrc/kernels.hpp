@@ -62,8 +62,18 @@ FusedPlan plan_fused(int64_t R, int64_t max_pool, int64_t max_hpool, int H, int 
 int fused_supported(int64_t R, int64_t max_pool, int64_t max_hpool, int H, int k, int W, int W_hca);
 size_t fused_error_word_offset();
 size_t fused_fallback_word_offset();
+// paged pooled caches for the fused decode (page_rows / hpage_rows powers of two >= 32)
+struct FusedPaging {
+  const int32_t* ptab;
+  const int64_t* plen;
+  int max_pages, page_rows;
+  const int32_t* hptab;
+  const int64_t* hplen;
+  int max_hpages, hpage_rows;
+};
 int launch_fused(int R, const int64_t* tok_off, const int64_t* q_pos, const int64_t* pool_off,
-                 const int64_t* hpool_off, const int32_t* pre_seq, const int64_t* pre_tok, int64_t max_pool, int64_t max_hpool, int m, int m_hca, int H,
+                 const int64_t* hpool_off, const int32_t* pre_seq, const int64_t* pre_tok, const FusedPaging* paging,
+                 int64_t max_pool, int64_t max_hpool, int m, int m_hca, int H,
                  float scale, int k, int W, int W_hca, const uint8_t* q_codes, const uint8_t* q_scales,
                  const float* w, const uint8_t* k_codes, const uint8_t* k_scales, const void* q,
                  const void* kv_pool, const void* kv_hpool, const void* kv_raw, int32_t* idx, void* csa_out,

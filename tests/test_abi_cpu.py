@@ -188,3 +188,23 @@ def test_decode_shared_validation():
     import torch
     if not torch.cuda.is_available():
         assert call() == csa.CSA_ERR_DEVICE
+
+
+def test_decode_paged_validation():
+    L = csa.lib()
+    b = _batch(n_seq=4, n_q=4, maxq=1)
+
+    def call(pr=64, tab=FAKE, npg=16, rows=FAKE, hpr=64, htab=FAKE, nhpg=2, hrows=FAKE, max_pool=1000, max_hpool=100):
+        return L.csa_hca_decode_paged(ctypes.byref(b), pr, tab, npg, rows, hpr, htab, nhpg, hrows, max_pool, max_hpool,
+                                      4, 128, 64, 128, 0.088, 64, 128, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                      FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, None)
+    assert call(tab=None) == csa.CSA_ERR_INVALID and "page" in L.csa_last_error().decode()
+    assert call(hrows=None) == csa.CSA_ERR_INVALID
+    assert call(pr=48) == csa.CSA_ERR_INVALID      # not a power of two
+    assert call(hpr=16) == csa.CSA_ERR_INVALID     # below 32 rows
+    assert call(npg=0) == csa.CSA_ERR_INVALID
+    assert call(npg=8) == csa.CSA_ERR_INVALID      # 8 x 64 rows < max_pool
+    assert call(max_hpool=129) == csa.CSA_ERR_INVALID
+    import torch
+    if not torch.cuda.is_available():
+        assert call() == csa.CSA_ERR_DEVICE

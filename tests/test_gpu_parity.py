@@ -679,3 +679,86 @@ def test_shared_prefix_entry_without_prefixes_equals_plain_decode():
     torch.cuda.synchronize()
     for what, x, y in zip(("idx", "csa_out", "csa_lse", "hca_out", "hca_lse"), got, want):
         assert np.array_equal(x, y), f"{what} differs from csa_hca_decode"
+
+
+# name -> (workload, CSA page rows, HCA page rows, prefix tokens shared by sequence 1 with sequence 0 or 0)
+PAGED_CASES = {
+    "paged_p64_h32": (lambda: small_wl("decode_paged", [20003, 9001, 4099, 70001], [1] * 4, k=256, seed=41),
+                      64, 32, 0),
+    "paged_p256_h64_shared": (lambda: small_wl("decode_paged_sh", [30000, 8192 + 6001, 2050], [1] * 3, H=32, k=300,
+                                               W=200, m_hca=64, W_hca=64, seed=42), 256, 64, 8192),
+    "paged_long": (lambda: small_wl("decode_paged_long", [262147, 131075], [1] * 2, k=1024, seed=43), 128, 32, 0),
+}
+
+
+def _pages(rows_per_seq, page_rows, rng, shared=None):
+    """A page table for sequences of the given row counts over one shuffled
+    pool of pages (plus spare pages); shared = (seq, n_pages): that sequence's
+    first pages are sequence 0's.  Returns (table [n_seq][max_pages], n_pool_pages)."""
+    need = [(n + page_rows - 1) // page_rows for n in rows_per_seq]
+    total = sum(need) + 3
+    perm = rng.permutation(total)
+    table = np.zeros((len(need), max(1, max(need))), dtype=np.int32)
+    nxt = 0
+    for b, n in enumerate(need):
+        for i in range(n):
+            if shared is not None and b == shared[0] and i < shared[1]:
+                table[b, i] = table[0, i]
+            else:
+                table[b, i] = perm[nxt]
+                nxt += 1
+    return table, total
+
+
+def _scatter(src, off, table, page_rows, n_pages):
+    """Rows [off[b], off[b+1]) of a contiguous cache -> their pages."""
+    dst = torch.zeros((n_pages * page_rows, *src.shape[1:]), dtype=src.dtype, device=src.device)
+    for b in range(len(off) - 1):
+        n = int(off[b + 1] - off[b])
+        for i in range((n + page_rows - 1) // page_rows):
+            r0, r1 = i * page_rows, min(n, (i + 1) * page_rows)
+            p = int(table[b, i])
+            dst[p * page_rows:p * page_rows + (r1 - r0)] = src[int(off[b]) + r0:int(off[b]) + r1]
+    return dst
+
+
+@pytest.mark.parametrize("name", list(PAGED_CASES))
+def test_paged_decode_is_bit_identical_to_contiguous_caches(name):
+    """csa_hca_decode_paged over pooled caches scattered into shuffled pages
+    (one case with a sequence whose first pages are another's, over equal
+    data) gives exactly csa_hca_decode's outputs on the contiguous caches."""
+    csa = _lib()
+    make, pr, hpr, T = PAGED_CASES[name]
+    wl = make()
+    host = synth.make_inputs(wl)
+    if T:
+        to, po = host["tok_off"], host["pool_off"]
+        for nm in ("kv", "z"):
+            host[nm][to[1]:to[1] + T] = host[nm][to[0]:to[0] + T]
+        for nm in ("kc", "ks"):
+            host[nm][po[1]:po[1] + T // wl.m] = host[nm][po[0]:po[0] + T // wl.m]
+    from long_context_compressed_05_amd.step import Layer, to_device
+    layer = Layer.from_host(_params(wl), host)
+    layer.build_caches()
+    dq = to_device({k: host[k] for k in ("q", "qc", "qs", "w")})
+    want = [P.torch_to_np(t) for t in layer.decode_fused(dq["q"], dq["qc"], dq["qs"], dq["w"])]
+    layer.check_fused()
+    rng = np.random.default_rng(7)
+    po, ho = host["pool_off"], host["hpool_off"]
+    P_b, Ph_b = np.diff(po), np.diff(ho)
+    tab, npg = _pages(P_b, pr, rng, (1, T // wl.m // pr) if T else None)
+    htab, nhpg = _pages(Ph_b, hpr, rng, (1, T // wl.m_hca // hpr) if T else None)
+    pooled2 = _scatter(layer.pooled, po, tab, pr, npg)
+    kc2, ks2 = _scatter(layer.kc, po, tab, pr, npg), _scatter(layer.ks, po, tab, pr, npg)
+    hpooled2 = _scatter(layer.hpooled, ho, htab, hpr, nhpg)
+    p = layer.p
+    ws = csa.Workspace()
+    dev = lambda a, t: torch.from_numpy(np.ascontiguousarray(a, dtype=t)).cuda()
+    got = [P.torch_to_np(t) for t in csa.csa_hca_decode_paged(
+        layer.batch, pr, dev(tab, np.int32), dev(P_b, np.int64), hpr, dev(htab, np.int32), dev(Ph_b, np.int64),
+        layer.max_pool, layer.max_hpool, p.m, p.m_hca, p.k, p.W, p.W_hca, p.sm_scale, dq["qc"], dq["qs"], dq["w"],
+        kc2, ks2, dq["q"], pooled2, hpooled2, layer.kv, ws=ws)]
+    csa.csa_hca_decode_check(layer.batch, ws)
+    torch.cuda.synchronize()
+    for what, x, y in zip(("idx", "csa_out", "csa_lse", "hca_out", "hca_lse"), got, want):
+        assert np.array_equal(x, y), f"{what} differs from the contiguous layout"
