@@ -286,6 +286,10 @@ def main():
             result["shared_prefix"] = bench_shared_prefix(torch, csa, synth, to_device, log, score_ms)
         except Exception as e:  # reported, never silently replaced
             result["shared_prefix"] = {"error": repr(e)}
+        try:
+            result["paged"] = bench_paged(torch, csa, layer, wl, host, sets, log, score_ms)
+        except Exception as e:  # reported, never silently replaced
+            result["paged"] = {"error": repr(e)}
 
     # ---- prefill indexer (4096-token chunk on a 64K cache) ----------------------
     if not args.no_prefill:
@@ -471,6 +475,68 @@ def bench_shared_prefix(torch, csa, synth, to_device, log, contiguous_kernel_ms,
            "contiguous_b4_t1m_kernel_us": round(contiguous_kernel_ms * 1e3, 2),
            "cache_bytes_stored": stored, "cache_bytes_if_contiguous": logical}
     log(f"shared prefix: {out}")
+    return out
+
+
+def bench_paged(torch, csa, layer, wl, host, sets, log, contiguous_kernel_ms, steps: int = 100,
+                page_rows: int = 256, hca_page_rows: int = 64):
+    """csa_hca_decode_paged on the 4 x 1M workload with its pooled caches and
+    indexer keys scattered into shuffled pages (page_rows CSA rows,
+    hca_page_rows HCA rows a page): event-timed launches over the same
+    rotated queries and keys as the contiguous step."""
+    dev = "cuda"
+    rng = np.random.default_rng(2024)
+    P_b, Ph_b = np.diff(host["pool_off"]), np.diff(host["hpool_off"])
+
+    def layout(rows, pr):
+        need = (rows + pr - 1) // pr
+        perm = rng.permutation(int(need.sum()))
+        tab = np.zeros((len(rows), int(need.max())), dtype=np.int32)
+        src = []  # physical row of each contiguous row
+        k = 0
+        for b in range(len(rows)):
+            tab[b, :need[b]] = perm[k:k + need[b]]
+            k += need[b]
+            j = np.arange(rows[b])
+            src.append(tab[b, j // pr].astype(np.int64) * pr + j % pr)
+        return tab, int(need.sum()), torch.from_numpy(np.concatenate(src)).to(dev)
+
+    tab, npg, rows_p = layout(P_b, page_rows)
+    htab, nhpg, rows_h = layout(Ph_b, hca_page_rows)
+
+    def scatter(t, n_rows, rows):
+        out = torch.zeros((n_rows, *t.shape[1:]), dtype=t.dtype, device=dev)
+        out[rows] = t
+        return out
+    pooled = scatter(layer.pooled, npg * page_rows, rows_p)
+    psets = [{"kc": scatter(d["kc"], npg * page_rows, rows_p), "ks": scatter(d["ks"], npg * page_rows, rows_p),
+              "hp": scatter(d["hpooled"], nhpg * hca_page_rows, rows_h)} for d in sets]
+    t_tab, t_htab = torch.from_numpy(tab).to(dev), torch.from_numpy(htab).to(dev)
+    t_P, t_Ph = torch.from_numpy(P_b.astype(np.int64)).to(dev), torch.from_numpy(Ph_b.astype(np.int64)).to(dev)
+    ws = csa.Workspace()
+    R = len(sets)
+
+    def step(i):
+        d, pd = sets[i % R], psets[i % R]
+        return csa.csa_hca_decode_paged(layer.batch, page_rows, t_tab, t_P, hca_page_rows, t_htab, t_Ph,
+                                        layer.max_pool, layer.max_hpool, wl.m, wl.m_hca, wl.k, wl.W, wl.W_hca,
+                                        1.0 / math.sqrt(wl.d), d["qc"], d["qs"], d["w"], pd["kc"], pd["ks"], d["q"],
+                                        pooled, pd["hp"], layer.kv, ws=ws)
+    for i in range(2 * R):
+        step(i)
+    torch.cuda.synchronize()
+    ev = [(csa.HipEvent(), csa.HipEvent()) for _ in range(steps)]
+    for i in range(steps):
+        csa.csa_profile_events(csa.CSA_K_FUSED, ev[i][0], ev[i][1])
+        step(i)
+    torch.cuda.synchronize()
+    csa.csa_profile_events(csa.CSA_K_FUSED)
+    csa.csa_hca_decode_check(layer.batch, ws)
+    us = float(np.mean([a.elapsed_ms(b) for a, b in ev])) * 1e3
+    out = {"workload": wl.name, "page_rows": page_rows, "hca_page_rows": hca_page_rows, "pages": npg,
+           "hca_pages": nhpg, "us_per_step": round(us, 2), "queries_per_s": round(wl.n_q / (us * 1e-6), 1),
+           "contiguous_kernel_us": round(contiguous_kernel_ms * 1e3, 2)}
+    log(f"paged: {out}")
     return out
 
 
