@@ -688,6 +688,9 @@ PAGED_CASES = {
     "paged_p256_h64_shared": (lambda: small_wl("decode_paged_sh", [30000, 8192 + 6001, 2050], [1] * 3, H=32, k=300,
                                                W=200, m_hca=64, W_hca=64, seed=42), 256, 64, 8192),
     "paged_long": (lambda: small_wl("decode_paged_long", [262147, 131075], [1] * 2, k=1024, seed=43), 128, 32, 0),
+    # every row takes the exact fallback (its entries come from the stored keys)
+    "paged_concentrated": (lambda: small_wl("decode_paged_conc", [40001, 30002], [1, 1], k=1024, seed=17), 64, 32, 0,
+                           "concentrate"),
 }
 
 
@@ -728,9 +731,11 @@ def test_paged_decode_is_bit_identical_to_contiguous_caches(name):
     (one case with a sequence whose first pages are another's, over equal
     data) gives exactly csa_hca_decode's outputs on the contiguous caches."""
     csa = _lib()
-    make, pr, hpr, T = PAGED_CASES[name]
+    make, pr, hpr, T = PAGED_CASES[name][:4]
     wl = make()
     host = synth.make_inputs(wl)
+    if PAGED_CASES[name][4:] == ("concentrate",):
+        host = _concentrate(host)
     if T:
         to, po = host["tok_off"], host["pool_off"]
         for nm in ("kv", "z"):
