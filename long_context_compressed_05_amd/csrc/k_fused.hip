@@ -884,8 +884,10 @@ __device__ __forceinline__ bool row_fallback(const FCtx& x, int r, const FRow& f
 // ascending order -> LDS, their count (or -1 on a failed wait), and their
 // output offset in the row's idx -> *off_out; the entries sit at
 // sel_s[*base_out ..] (the exact path stores them at their output rank).
+// (*phys_out: with paged caches, whether the selected rows' physical rows are
+// already in LDS beside them)
 __device__ __forceinline__ int group_select(const FCtx& x, int r, int g, const FRow& f, uint32_t* off_out,
-                                            uint32_t* base_out) {
+                                            uint32_t* base_out, bool* phys_out) {
   KArgs& a = *x.a;
   const int tid = lane_tid();
   const int cgs = a.cg;
@@ -958,8 +960,10 @@ __device__ __forceinline__ int group_select(const FCtx& x, int r, int g, const F
   // (its selected rows are among them when P1 - P0 <= 256) while K* is found:
   // one word of each 128-byte line, consumed only once the ranks are known.
   uint32_t warm0 = 0, warm1 = 0, warm2 = 0, warm3 = 0;
+  const int uw = (int)(P0 >> 8);
+  int32_t pr_w = 0;  // the physical row of this thread's entry at slot uw (when it is listed)
+  *phys_out = false;
   {
-    const int uw = (int)(P0 >> 8);
     uint32_t kw = kNoKey, iw = 0;
 #pragma unroll
     for (int v = 0; v < kFEPT; ++v) {
@@ -969,6 +973,7 @@ __device__ __forceinline__ int group_select(const FCtx& x, int r, int g, const F
     const uint32_t p = (uint32_t)(uw * 256 + tid);
     if (kw != kNoKey && p >= P0 && p < P1) {  // a listed entry: iw < the row's visible count
       const int64_t pr = x.paged ? paged_row(a.ptab + (size_t)r * a.max_pages, a.lg_page, iw) : pool_row(f, iw);
+      pr_w = (int32_t)pr;
       const uint32_t* row = reinterpret_cast<const uint32_t*>(a.kv_pool + (size_t)pr * 512u);
       warm0 = row[0];
       warm1 = row[32];
@@ -1018,7 +1023,12 @@ __device__ __forceinline__ int group_select(const FCtx& x, int r, int g, const F
         uint32_t tot;
         const uint32_t ex = block_exscan_val((take ? 1u : 0u) | (u == u0 ? pre << 16 : 0u), x.scr, &tot);
         if (u == u0) off = tot >> 16;
-        if (take) sel_s[off + run + (ex & 0xffffu)] = (int32_t)iu;
+        if (take) {
+          sel_s[off + run + (ex & 0xffffu)] = (int32_t)iu;
+          if (x.paged)  // the physical row beside it: from the warm-up at slot uw, else looked up
+            reinterpret_cast<int32_t*>(x.smem + kOffSelP)[off + run + (ex & 0xffffu)] =
+                u == uw ? pr_w : (int32_t)paged_row(a.ptab + (size_t)r * a.max_pages, a.lg_page, iu);
+        }
         run += tot & 0xffffu;
       }
       exact = uni(x.scr[S_BAD]) == 0u;  // the scans' barriers ordered the threshold checks
@@ -1027,6 +1037,7 @@ __device__ __forceinline__ int group_select(const FCtx& x, int r, int g, const F
         asm volatile("" ::"v"(warm0), "v"(warm1), "v"(warm2), "v"(warm3));
         *off_out = off;
         *base_out = off;
+        *phys_out = x.paged;
         return (int)run;
       }
     }
@@ -1347,9 +1358,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
       const int r = (int)(q % R), g = (int)(q / R);
       const FRow f = row_info(A, r, kPaged);
       uint32_t off = 0, base = 0;
-      const int n_sel = group_select(x, r, g, f, &off, &base);
+      bool phys = false;
+      const int n_sel = group_select(x, r, g, f, &off, &base, &phys);
       if (n_sel >= 0) {
-        if (kPaged) {  // paged caches: the selected rows' physical rows -> LDS
+        if (kPaged && !phys) {  // paged caches: the selected rows' physical rows -> LDS
           const int32_t* sel_s = reinterpret_cast<const int32_t*>(smem + kOffSel) + base;
           int32_t* sel_p = reinterpret_cast<int32_t*>(smem + kOffSelP) + base;
           const int32_t* trow = A.ptab + (size_t)r * A.max_pages;
