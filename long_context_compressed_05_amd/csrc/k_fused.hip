@@ -1294,8 +1294,10 @@ __device__ __forceinline__ void item_merge(const FCtx& x, bool hca, int r, int h
 
 // ---------------------------------------------------------------------------
 // kPaged: the pooled caches are read through page tables (csa_hca_decode_paged)
+// (one workgroup per CU, so one wave per SIMD: the compiler is told so and
+// schedules without a second wave's register budget in mind)
 template <bool kPaged>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_decode_fused(FusedArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_decode_fused(FusedArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
   uint32_t* scr = reinterpret_cast<uint32_t*>(smem + kOffScr);
   // the launch's tag: every thread loads the epoch word; the load is waited for
