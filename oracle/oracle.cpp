@@ -147,23 +147,37 @@ ScoreResult index_score(int H_I, int d_I, const uint8_t* qc, const uint8_t* qs, 
   int tot_e = 0;
   bool have = false, all_pow2 = true;
   double min_unit_all = std::numeric_limits<double>::infinity();
+  std::vector<long long> blk((size_t)nb);
+  std::vector<int> bexp((size_t)nb);
+  std::vector<char> nonzero((size_t)nb);
   for (int h = 0; h < H_I; ++h) {
     int we;
     if (!is_pow2(w[h], &we)) { all_pow2 = false; we = 0; }
+    /* per block: the integer sum of its products (2a)(2b), their exponent
+     * eq+ek-256, and whether any product is non-zero.  A block whose
+     * products are all zero adds exactly nothing, whatever its scales, so it
+     * takes no part in the dot's unit 2^emin. */
     int emin = 1 << 30;
-    for (int b = 0; b < nb; ++b) emin = std::min(emin, (int)qs[h * nb + b] + (int)ks[b] - 256);
-    __int128 dot = 0;
     double abs_sum = 0.0;
     for (int b = 0; b < nb; ++b) {
-      long long blk = 0;
+      blk[b] = 0;
+      nonzero[b] = 0;
+      bexp[b] = (int)qs[h * nb + b] + (int)ks[b] - 256;
       for (int c = b * 32; c < b * 32 + 32; ++c) {
         int pa = e2m1_twice(nibble(qc + h * (d_I / 2), c)) * e2m1_twice(nibble(kc, c));
-        blk += pa;
-        abs_sum += std::ldexp((double)std::abs(pa), (int)qs[h * nb + b] + (int)ks[b] - 256);
+        blk[b] += pa;
+        if (pa != 0) nonzero[b] = 1;
+        abs_sum += std::ldexp((double)std::abs(pa), bexp[b]);
       }
-      int sh = (int)qs[h * nb + b] + (int)ks[b] - 256 - emin;
+      if (nonzero[b]) emin = std::min(emin, bexp[b]);
+    }
+    if (emin == (1 << 30)) continue; /* every product is zero: the dot is 0 */
+    __int128 dot = 0;
+    for (int b = 0; b < nb; ++b) {
+      if (!nonzero[b]) continue;
+      int sh = bexp[b] - emin;
       if (sh > 90) { r.ok = false; sh = 90; } /* beyond what 128 bits can check */
-      dot += (__int128)blk * ((__int128)1 << sh);
+      dot += (__int128)blk[b] * ((__int128)1 << sh);
     }
     /* fp32 exactness of this head's dot in any order: every partial sum is a
      * multiple of 2^emin bounded by abs_sum, so it needs abs_sum < 2^(24+emin) */

@@ -298,6 +298,32 @@ def test_index_exactness_flag_detects_wide_scale_spread():
     assert S[0] == 4 * 32 * 36.0 * (2.0 ** 12 + 2.0 ** -12)
 
 
+def test_index_zero_block_scale_does_not_matter():
+    """A query block whose codes are all zero (+0 and -0) adds nothing to the
+    head's dot whatever its scale byte, from 0 (2^-127) to 254: the scores
+    equal those with the block's scale at 2^0, they equal the matmul of the
+    decoded values, and the fp32-exactness flag is not lost to the unused
+    scale."""
+    qc, qs, w, kc, ks = _random_index(8, 300)
+    qc[0, :16] = np.where(np.arange(16) % 2 == 0, 0x80, 0x08).astype(np.uint8)
+    qc[2, 16:] = 0x00
+    base = qs.copy()
+    base[0, 0] = 127
+    base[2, 1] = 127
+    S_ref, ex_ref = oracle.index_scores(qc, base, w, kc, ks)
+    Q = np.stack([decode_vec(qc[h], base[h]) for h in range(4)])
+    K = np.stack([decode_vec(kc[j], ks[j]) for j in range(kc.shape[0])])
+    assert np.array_equal(S_ref, np.maximum(K @ Q.T, 0) @ w.astype(np.float64))
+    assert ex_ref.all()
+    for b0, b2 in ((0, 0), (254, 254), (0, 254)):
+        q2 = qs.copy()
+        q2[0, 0] = b0
+        q2[2, 1] = b2
+        S, ex = oracle.index_scores(qc, q2, w, kc, ks)
+        assert np.array_equal(S, S_ref)
+        assert ex.all()
+
+
 # ----------------------------------------------------------------------------
 # top-k
 # ----------------------------------------------------------------------------
