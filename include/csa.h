@@ -171,12 +171,22 @@ int csa_mxfp4_quantize(int dtype, int64_t rows, int dim, const void* x, uint8_t*
  * min(k, visible), and idx[i][k_eff..k) = -1.  Indices are relative to the
  * sequence's first pooled row pool_off[b].
  *   q_codes  [n_q][n_heads][dim/2]   q_scales [n_q][n_heads][dim/32]
- *   w        [n_q][n_heads] fp32, each an exact power of two
+ *   w        [n_q][n_heads] fp32, each an exact positive power of two or
+ *            zero; it is folded into the query's block scales (byte + log2 w),
+ *            so for a block with a non-zero code the folded byte must stay in
+ *            E8M0's finite range [0, 254] (else it is clamped there and the
+ *            scores are no longer those of the definition).  A block whose
+ *            codes are all zero (+0 or -0) may carry any scale byte, 0
+ *            included, and a zero weight drops its head.  Negative weights
+ *            are not supported (the sign would be dropped).
  *   k_codes  [sum P][dim/2]          k_scales [sum P][dim/32]
  *   idx      [n_q][k] int32 (output)
  *   ws       workspace of >= csa_index_topk_workspace() bytes, ZERO-FILLED
- *            before its first use; every successful call leaves it zero-filled
- *            again (a failed launch may not: re-zero it then).
+ *            before its first use.  Every successful call returns the parts
+ *            that must start at zero (histograms, counters, candidate bitmaps)
+ *            to zero, so later calls reuse it without clearing; the rest is
+ *            scratch that each call writes before reading (a failed launch may
+ *            leave it dirty: re-zero it then).
  * Exactness: scores are formed in fp32 and compared as bit patterns.  They
  * are exact, and the selection therefore matches exact arithmetic bit for
  * bit, when every per-head dot and the head sum are representable, e.g. all
@@ -246,9 +256,9 @@ int hca_attn(int dtype, const csa_batch* b, const int64_t* hpool_off, int64_t ma
  * outputs as the three separate calls (pages as cited there); bit-identical
  * top-k.  Decode batches only: one query per sequence (n_q == n_seq,
  * q_off[b] == b), bf16, H % 16 == 0 and 16 <= H <= 64, d = 128, indexer
- * 4 x 64, k <= 1024, max_pool <= 262144, at most 64 queries, and a plan whose
- * score chunks fit (at most 4096 entries per chunk, 512 chunks per row);
- * otherwise CSA_ERR_UNSUPPORTED (use the separate calls).
+ * 4 x 64, k <= 1024, max_pool <= 262144 and at most 64 queries; otherwise
+ * CSA_ERR_UNSUPPORTED (use the separate calls).  Indexer inputs (w included)
+ * as csa_index_topk.
  *   kv_pool [sum P][2][d] (block m), kv_pool_hca [sum P'][2][d] (block m_hca),
  *   kv_raw [sum L][2][d]; idx [n_q][k]; csa_out/hca_out [n_q][H][d] bf16;
  *   csa_lse/hca_lse [n_q][H] fp32 or NULL.
@@ -256,10 +266,12 @@ int hca_attn(int dtype, const csa_batch* b, const int64_t* hpool_off, int64_t ma
  *       reusable by later launches of the same shapes (a launch-epoch tag in
  *       ws tells one launch's words from another's); re-zero it when the
  *       shapes change.  Launches sharing a ws must be ordered (one stream).
- * The kernel's internal waits are bounded: if one ever times out (a wait only
- * depends on work units handed out before it, so it is not expected) the
- * step's outputs are invalid and an error word in ws is set, which
- * csa_hca_decode_check() reports.
+ * The launch's workgroups take their work units from a counter in arrival
+ * order, and a unit only waits for units handed out before it, so every wait
+ * ends even when only some of the workgroups are resident at a time (another
+ * kernel holding compute units only delays the step).  The waits are bounded
+ * all the same: if one ever runs out the step's outputs are invalid and an
+ * error word in ws is set, which csa_hca_decode_check() reports.
  * ---------------------------------------------------------------------- */
 int csa_hca_decode_workspace(const csa_batch* b, int64_t max_pool, int64_t max_hpool, int H, int d,
                              int k, int W, int W_hca, size_t* bytes);
@@ -290,10 +302,12 @@ int csa_hca_decode(const csa_batch* b, const int64_t* pool_off, int64_t max_pool
  * the logical sequence; the result is bit-identical to csa_hca_decode over
  * caches holding each logical sequence contiguously.
  *   prefix_seq [n_seq] int32 device (-1: no prefix); prefix_tokens [n_seq]
- *   int64 device.  T should be a multiple of m and m_hca, p's cache should
- *   hold at least T tokens' rows and p should have no prefix of its own; the
- *   kernel clamps each count to what p stores (reads never leave p's rows)
- *   and ignores p outside [0, n_seq) or p == b, but the result is only
+ *   int64 device.  T need not be a multiple of m or m_hca: a block that
+ *   straddles T is b's own first pooled row (b's cache pools it from the
+ *   prefix's last tokens and its own first ones).  p's cache should hold at
+ *   least T tokens' rows and p should have no prefix of its own; the kernel
+ *   clamps each count to what p stores (reads never leave p's rows) and
+ *   ignores p outside [0, n_seq) or p == b, but the result is only
  *   meaningful when these hold.  max_pool / max_hpool bound the logical
  *   counts.  Other arguments, workspace and errors as csa_hca_decode;
  *   CSA_ERR_INVALID also for a NULL prefix array.
@@ -358,9 +372,11 @@ int csa_hca_decode_fallbacks(const void* ws, void* stream, uint32_t* rows);
 
 /* ------------------------------------------------------------------------
  * csa_profile_events — tracing hook (host).  Until cleared, every launch of
- * internal kernel `kernel_id` made by the calling thread is bracketed by
- * hipEventRecord(start) / hipEventRecord(stop) on the launch stream, so a
- * caller can time one kernel of a multi-kernel call with its own events.
+ * internal kernel `kernel_id` made by the calling thread carries the two
+ * events: they are attached to the dispatch itself (hipExtLaunchKernel), so
+ * hipEventElapsedTime(start, stop) is the kernel's execution time on the GPU,
+ * as a kernel trace reports it, without the enqueue (for an id that covers
+ * two kernels, from the first one's start to the second one's end).
  * start/stop are hipEvent_t handles owned by the caller; pass NULL, NULL to
  * clear.  Kernel ids: CSA_K_IDX_SCORE (indexer scoring), CSA_K_IDX_SELECT,
  * CSA_K_IDX_FINAL (top-k passes of decode batches), CSA_K_ATTN (attention

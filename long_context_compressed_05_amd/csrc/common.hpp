@@ -34,6 +34,24 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Head weight folded into a query block's E8M0 scale: w = 2^e multiplies
+// every product of the block, so the block's scale byte becomes qscale + e.
+// `u` holds the block's 32 e2m1 codes.  A block whose codes are all zero (or
+// -0), or a zero weight, adds nothing to the dot whatever its scale: its codes
+// are zeroed and the scale is set to 2^0, so no out-of-range byte (0xFF is
+// E8M0's NaN) can reach the MFMA.  Otherwise the byte is clamped to the
+// finite range [0, 254]; a fold that leaves it is outside the exactness
+// precondition of the indexer (scales within a few octaves of each other).
+__device__ __forceinline__ int fold_head_weight(uint4& u, int qscale, float w) {
+  const int wexp = (int)((__float_as_uint(w) >> 23) & 255u);
+  if (wexp == 0 || ((u.x | u.y | u.z | u.w) & 0x77777777u) == 0u) {
+    u = make_uint4(0u, 0u, 0u, 0u);
+    return 127;
+  }
+  const int e = qscale + wexp - 127;
+  return e < 0 ? 0 : (e > 254 ? 254 : e);
+}
+
 // Wave-wide inclusive scans on DPP lane moves (row shifts within 16-lane rows,
 // then the row broadcasts of lanes 15 and 31): a few VALU operations instead
 // of LDS permutes.  Lanes whose source is outside the row take the identity.

@@ -76,12 +76,7 @@ int launched(int rc) {
 }  // namespace
 
 namespace csa {
-void prof_begin(int id, hipStream_t stream) {
-  if (g_prof[id][0]) (void)hipEventRecord(g_prof[id][0], stream);
-}
-void prof_end(int id, hipStream_t stream) {
-  if (g_prof[id][1]) (void)hipEventRecord(g_prof[id][1], stream);
-}
+hipEvent_t prof_event(int id, int stop) { return g_prof[id][stop ? 1 : 0]; }
 }  // namespace csa
 
 extern "C" {
@@ -95,9 +90,8 @@ int csa_hca_decode_workspace(const csa_batch* b, int64_t max_pool, int64_t max_h
   rc = check_device();
   if (rc) return rc;
   if (d != 128 || !csa::fused_supported(b->n_q, max_pool, max_hpool, H, k, W, W_hca))
-    return fail(CSA_ERR_UNSUPPORTED, "fused decode needs d = 128, 16 <= H <= 64 with H %% 16 == 0, "
-                                     "max_pool <= 262144, 1..64 queries and n_q * max_pool <= 3072 * (resident "
-                                     "workgroups)");
+    return fail(CSA_ERR_UNSUPPORTED, "fused decode needs d = 128, 16 <= H <= 64 with H %% 16 == 0, k <= 1024, "
+                                     "max_pool <= 262144 and 1..64 queries");
   *bytes = csa::plan_fused(b->n_q, max_pool, max_hpool, H, k, W, W_hca).ws_bytes;
   return CSA_OK;
 }
@@ -120,9 +114,8 @@ static int hca_decode_impl(const csa_batch* b, const int32_t* pre_seq, const int
   rc = check_device();
   if (rc) return rc;
   if (d != 128 || !csa::fused_supported(b->n_q, max_pool, max_hpool, H, k, W, W_hca))
-    return fail(CSA_ERR_UNSUPPORTED, "fused decode needs d = 128, 16 <= H <= 64 with H %% 16 == 0, "
-                                     "max_pool <= 262144, 1..64 queries and n_q * max_pool <= 3072 * (resident "
-                                     "workgroups)");
+    return fail(CSA_ERR_UNSUPPORTED, "fused decode needs d = 128, 16 <= H <= 64 with H %% 16 == 0, k <= 1024, "
+                                     "max_pool <= 262144 and 1..64 queries");
   if ((!paging && (!pool_off || !hpool_off)) || !q_codes || !q_scales || !w || !k_codes || !k_scales || !q || !kv_pool ||
       (max_hpool > 0 && !kv_pool_hca) || ((W > 0 || W_hca > 0) && !kv_raw) || !idx || !csa_out || !hca_out)
     return fail(CSA_ERR_INVALID, "NULL pointer argument");
@@ -137,7 +130,7 @@ static int hca_decode_impl(const csa_batch* b, const int32_t* pre_seq, const int
                         scale, k, W, W_hca, q_codes, q_scales, w, k_codes, k_scales, q, kv_pool, kv_pool_hca,
                         kv_raw, idx, csa_out, csa_lse, hca_out, hca_lse, ws, (hipStream_t)stream) != 0) {
     (void)hipGetLastError();
-    return fail(CSA_ERR_DEVICE, "cooperative launch of the fused decode kernel failed");
+    return fail(CSA_ERR_DEVICE, "launch of the fused decode kernel failed");
   }
   return CSA_OK;
 }

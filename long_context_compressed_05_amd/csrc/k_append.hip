@@ -235,13 +235,12 @@ int launch_append(bool bf16, int n_seq, int width, const int64_t* tok_off, int64
   a.wide_par = wide > 0 && lds <= 64 * 1024 ? 1 : 0;
   const size_t lds_launch = a.wide_par ? lds : 0;
   dim3 g1((unsigned)(a.nb_narrow + wide), (unsigned)n_seq);
-  prof_begin(9, stream);
-  if (bf16) hipLaunchKernelGGL(k_append_pool<true>, g1, dim3(256), lds_launch, stream, a);
-  else hipLaunchKernelGGL(k_append_pool<false>, g1, dim3(256), lds_launch, stream, a);
-  if (bf16) hipLaunchKernelGGL(k_append_tail<true>, dim3((unsigned)n_seq), dim3(256), 0, stream, a);
-  else hipLaunchKernelGGL(k_append_tail<false>, dim3((unsigned)n_seq), dim3(256), 0, stream, a);
-  prof_end(9, stream);
-  return hipGetLastError() == hipSuccess ? 0 : -1;
+  hipError_t e = launch(9, kProfStart, bf16 ? k_append_pool<true> : k_append_pool<false>, g1, dim3(256), lds_launch,
+                        stream, a);
+  if (e == hipSuccess)
+    e = launch(9, kProfStop, bf16 ? k_append_tail<true> : k_append_tail<false>, dim3((unsigned)n_seq), dim3(256), 0,
+               stream, a);
+  return e == hipSuccess && hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 }  // namespace csa

@@ -335,26 +335,14 @@ int launch_attn(bool bf16, bool hca, int n_seq, int64_t n_q, const int64_t* tok_
     a.splits = 1;
   }
   dim3 grid((unsigned)a.splits, (unsigned)n_q);
-  prof_begin(3, stream);
-  if (bf16) {
-    if (H > 64) hipLaunchKernelGGL(k_attn_bf16<2>, grid, dim3(256), 0, stream, a);
-    else hipLaunchKernelGGL(k_attn_bf16<1>, grid, dim3(256), 0, stream, a);
-  } else {
-    hipLaunchKernelGGL(k_attn_f32, grid, dim3(256), 0, stream, a);
-  }
-  prof_end(3, stream);
-  if (a.splits > 1) {
-    prof_begin(4, stream);
+  hipError_t e = launch(3, kProfBoth, !bf16 ? k_attn_f32 : (H > 64 ? k_attn_bf16<2> : k_attn_bf16<1>), grid,
+                        dim3(256), 0, stream, a);
+  if (e == hipSuccess && a.splits > 1) {
     dim3 gc((unsigned)n_q, (unsigned)H);
-    if (bf16)
-      hipLaunchKernelGGL(k_attn_combine<true>, gc, dim3(128), 0, stream, a.part_o, a.part_ml, a.splits, H,
-                         a.out, lse);
-    else
-      hipLaunchKernelGGL(k_attn_combine<false>, gc, dim3(128), 0, stream, a.part_o, a.part_ml, a.splits, H,
-                         a.out, lse);
-    prof_end(4, stream);
+    e = launch(4, kProfBoth, bf16 ? k_attn_combine<true> : k_attn_combine<false>, gc, dim3(128), 0, stream,
+               (const float*)a.part_o, (const float*)a.part_ml, a.splits, H, a.out, lse);
   }
-  return hipGetLastError() == hipSuccess ? 0 : -1;
+  return e == hipSuccess && hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 }  // namespace csa

@@ -50,15 +50,9 @@ int launch_compress(bool bf16, int n_seq, const int64_t* tok_off, const int64_t*
   if (max_blocks == 0 || n_seq == 0) return 0;
   const int64_t threads = max_blocks * groups;
   dim3 grid((unsigned)((threads + 255) / 256), (unsigned)n_seq);
-  prof_begin(5, stream);
-  if (bf16)
-    hipLaunchKernelGGL(k_compress<true>, grid, dim3(256), 0, stream, tok_off, pool_off, m, width,
-                       (const uint8_t*)x, (const uint8_t*)z, (uint8_t*)out);
-  else
-    hipLaunchKernelGGL(k_compress<false>, grid, dim3(256), 0, stream, tok_off, pool_off, m, width,
-                       (const uint8_t*)x, (const uint8_t*)z, (uint8_t*)out);
-  prof_end(5, stream);
-  return hipGetLastError() == hipSuccess ? 0 : -1;
+  const hipError_t e = launch(5, kProfBoth, bf16 ? k_compress<true> : k_compress<false>, grid, dim3(256), 0, stream,
+                              tok_off, pool_off, m, width, (const uint8_t*)x, (const uint8_t*)z, (uint8_t*)out);
+  return e == hipSuccess && hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 }  // namespace csa

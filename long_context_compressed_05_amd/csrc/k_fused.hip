@@ -37,6 +37,8 @@
 // are all resident and never wait for a later stage, so every wait ends; the
 // waits are bounded anyway, and hitting the bound sets the error word (read
 // and cleared by csa_hca_decode_check) and skips the workgroup's remaining work.
+#include <atomic>
+
 #include "attn_core.hpp"
 #include "common.hpp"
 #include "kernels.hpp"
@@ -54,6 +56,7 @@ constexpr int kFMaxVisible = 262144;  // visible pooled entries per query (18-bi
 constexpr int kFMaxRows = 64;
 constexpr int kFMaxSlots = 512;      // score chunks per row
 constexpr uint32_t kSpinLimit = 1u << 20;
+static_assert(kFMaxVisible / 1024 <= kFMaxSlots, "every plan's chunk count fits (chunks hold at least 1024 entries)");
 
 // control words at the start of the workspace
 enum { W_EPOCH = 0, W_EXIT = 1, W_ERROR = 2, W_TICKET = 3, W_FALLBACK = 4, W_CTL = 64 };
@@ -599,10 +602,9 @@ __device__ __forceinline__ void phase_score(const FCtx& x, int r, int c, const F
   int asc = 127;
   if ((lane & 31) < 4) {
     const int64_t qrow = (int64_t)r * 4 + (lane & 3);
-    const uint4 u = *reinterpret_cast<const uint4*>(a.q_codes + qrow * 32 + kb * 16);
+    uint4 u = *reinterpret_cast<const uint4*>(a.q_codes + qrow * 32 + kb * 16);
+    asc = fold_head_weight(u, (int)a.q_scales[qrow * 2 + kb], a.w[qrow]);  // w_h folded into the block scale
     av[0] = (int)u.x; av[1] = (int)u.y; av[2] = (int)u.z; av[3] = (int)u.w;
-    const int we = (int)((__float_as_uint(a.w[qrow]) >> 23) & 255u) - 127;
-    asc = (int)a.q_scales[qrow * 2 + kb] + we;  // w_h = 2^we folded into the block scale
   }
   // 32-entry MFMA tiles; wave w takes tiles w, w+4, ...; 16 tiles per wave per batch of loads
   const int n = (int)(j1 - j0);
@@ -1308,16 +1310,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // Work units in dependency order: [score chunks | CSA groups | CSA window
   // splits | HCA splits | HCA merges | CSA merges].  The score chunks stream
   // first on every workgroup; the HCA stream then runs beside the
-  // latency-bound selection chain.  Units are handed out in that order, the
-  // first grid-size ones by workgroup id and the rest through one returning
-  // atomic, claimed one round ahead; a workgroup runs its units in the order
-  // it claimed them, and a unit only waits for units of lower number.  The
-  // lowest unfinished unit therefore never waits, and its workgroup is either
-  // running it or running a unit of lower number still: every wait ends while
-  // the grid's workgroups are resident (one per CU, as the launch sizes it).  Every workgroup runs the same number
-  // of rounds (rounds * grid >= total), so the loop bound is uniform; a round
-  // whose unit number is past the end does nothing.
+  // latency-bound selection chain.  Every unit number comes from one
+  // returning atomic on a ticket counter, taken by a running workgroup (the
+  // first on arrival, each later one a round ahead), so units are handed out
+  // in arrival order and a unit is only ever held by a workgroup that has
+  // started.  A workgroup runs its units in the order it claimed them
+  // (ascending), and a unit only waits for units of lower number.  The
+  // lowest unfinished unit is therefore held by a running workgroup whose
+  // earlier units are all done, so it is being run and never waits: every
+  // wait ends however many of the grid's workgroups are resident at a time
+  // (workgroups that start late simply take later units).  Every workgroup
+  // runs the same number of rounds (rounds * grid >= total), so the loop
+  // bound is uniform; a round whose unit number is past the end does nothing.
   uint32_t next_ticket = 0;  // lane 0: the unit number of the next round, fetched one round ahead
+  if (lane_tid() == 0) next_ticket = atomicAdd(a.ctl + W_TICKET, 1u);
   for (int round = 0; round < rounds; ++round) {
     KArgs* ap = (KArgs*)__builtin_amdgcn_kernarg_segment_ptr();
     asm volatile("" : "+s"(ap));
@@ -1328,13 +1334,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int64_t u_win = u_grp + (int64_t)R * A.n_cs_sel, u_hca = u_win + (int64_t)R * A.n_cs_win;
     const int64_t u_mh = u_hca + (int64_t)R * A.n_hs, u_mc = u_mh + (int64_t)R * nM;
     const int64_t total = u_mc + (int64_t)R * nM;
-    int64_t it = (int64_t)blockIdx.x;
-    if (round > 0) {
-      if (lane_tid() == 0) scr[S_TICKET] = (uint32_t)gridDim.x + next_ticket;
-      __syncthreads();
-      it = uni(scr[S_TICKET]);
-      __syncthreads();
-    }
+    if (lane_tid() == 0) scr[S_TICKET] = next_ticket;
+    __syncthreads();
+    const int64_t it = (int64_t)uni(scr[S_TICKET]);
+    __syncthreads();
     // claim the next round's unit now: the returning atomic's latency overlaps
     // this round's work.  A workgroup still runs its units in claim order.
     if (round + 1 < rounds && lane_tid() == 0) next_ticket = atomicAdd(A.ctl + W_TICKET, 1u);
@@ -1397,12 +1400,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
-static int g_fused_grid = 0;
+// grid size per device (0 = not known yet): the occupancy query runs once
+// per device; concurrent first calls compute the same value, so a relaxed
+// atomic store is enough
+constexpr int kMaxDevices = 64;
+static std::atomic<int> g_fused_grid[kMaxDevices];
 
 static int fused_grid() {
-  if (g_fused_grid > 0) return g_fused_grid;
   int dev = 0, cus = 0, per_cu = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < kMaxDevices) {
+    const int g = g_fused_grid[dev].load(std::memory_order_relaxed);
+    if (g > 0) return g;
+  }
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
   if (hipFuncSetAttribute((const void*)k_decode_fused<false>, hipFuncAttributeMaxDynamicSharedMemorySize,
                           kFusedLds) != hipSuccess ||
@@ -1412,12 +1422,12 @@ static int fused_grid() {
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)k_decode_fused<false>, 256, kFusedLds) !=
       hipSuccess)
     return 0;
-  if (per_cu < 1) return 0;
+  if (per_cu < 1 || cus < 1) return 0;
   // One workgroup per CU: two score workgroups sharing a CU's memory pipeline
   // finish far apart (the second one's stores drain late), and the selection
   // waits for the last chunk of every row.
-  g_fused_grid = cus;
-  return g_fused_grid;
+  if (dev < kMaxDevices) g_fused_grid[dev].store(cus, std::memory_order_relaxed);
+  return cus;
 }
 
 static int split_count(int64_t len, int64_t size) { return len <= 0 ? 0 : (int)((len + size - 1) / size); }
@@ -1488,9 +1498,8 @@ FusedPlan plan_fused(int64_t R, int64_t max_pool, int64_t max_hpool, int H, int 
 int fused_supported(int64_t R, int64_t max_pool, int64_t max_hpool, int H, int k, int W, int W_hca) {
   if (R < 1 || R > kFMaxRows || max_pool > (int64_t)kFMaxVisible || H % 16 != 0 || H > 64 || H < 16 || k > kFMaxSel)
     return 0;
-  const FusedPlan p = plan_fused(R, max_pool, max_hpool, H, k, W, W_hca);
-  if (p.grid <= 0 || p.C > kFMaxC || p.n_sc > kFMaxSlots) return 0;
-  return 1;
+  // the plan always fits: C <= kFMaxC and n_sc <= kFMaxVisible / 1024 <= kFMaxSlots
+  return plan_fused(R, max_pool, max_hpool, H, k, W, W_hca).grid > 0 ? 1 : 0;
 }
 
 size_t fused_error_word_offset() { return W_ERROR * 4; }
@@ -1504,7 +1513,7 @@ int launch_fused(int R, const int64_t* tok_off, const int64_t* q_pos, const int6
                  const void* kv_pool, const void* kv_hpool, const void* kv_raw, int32_t* idx, void* csa_out,
                  float* csa_lse, void* hca_out, float* hca_lse, void* ws, hipStream_t stream) {
   const FusedPlan pl = plan_fused(R, max_pool, max_hpool, H, k, W, W_hca);
-  if (pl.grid <= 0 || pl.C > kFMaxC || pl.n_sc > kFMaxSlots) return -1;
+  if (pl.grid <= 0) return -1;
   uint8_t* p = (uint8_t*)ws;
   auto take = [&](size_t bytes) {
     uint8_t* q0 = p;
@@ -1552,13 +1561,9 @@ int launch_fused(int R, const int64_t* tok_off, const int64_t* q_pos, const int6
   a.csa_pml = (float*)take((size_t)R * n_cs * H * 2 * 4);
   a.hca_po = (float*)take((size_t)R * pl.n_hs * H * 128 * 4);
   a.hca_pml = (float*)take((size_t)R * pl.n_hs * H * 2 * 4);
-  void* args[] = {&a};
-  prof_begin(6, stream);
-  // an ordinary launch of one workgroup per CU (all resident at once)
-  const hipError_t e =
-      hipLaunchKernel(paging ? (const void*)k_decode_fused<true> : (const void*)k_decode_fused<false>,
-                      dim3((unsigned)pl.grid), dim3(256), args, kFusedLds, stream);
-  prof_end(6, stream);
+  // an ordinary launch of one workgroup per CU
+  const hipError_t e = launch(6, kProfBoth, paging ? k_decode_fused<true> : k_decode_fused<false>,
+                              dim3((unsigned)pl.grid), dim3(256), kFusedLds, stream, a);
   if (e != hipSuccess) return -1;
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }

@@ -121,9 +121,8 @@ __global__ __launch_bounds__(256) void k_idx_score(ScoreArgs a) {
   if (slot_a < nrows) {
     const int64_t qrow = (row0 + slot_a) * 4 + head_a;
     uint4 u = *reinterpret_cast<const uint4*>(a.q_codes + qrow * 32 + kb * 16);
+    asc = fold_head_weight(u, (int)a.q_scales[qrow * 2 + kb], a.w[qrow]);  // w_h folded into the block scale
     av[0] = (int)u.x; av[1] = (int)u.y; av[2] = (int)u.z; av[3] = (int)u.w;
-    const int we = (int)((__float_as_uint(a.w[qrow]) >> 23) & 255u) - 127;
-    asc = (int)a.q_scales[qrow * 2 + kb] + we;  // w_h = 2^we folded into the block scale
   }
 
   const int64_t jc0 = (int64_t)blockIdx.x * kScoreChunk;
@@ -402,17 +401,14 @@ int launch_index_topk(int n_seq, int64_t n_q, int64_t max_q_per_seq, const int64
                q_scales, w, k_codes, k_scales, keys, hist};
   dim3 g1((unsigned)((max_pool + kScoreChunk - 1) / kScoreChunk), (unsigned)(n_seq * tiles_per_seq));
   if (g1.x == 0) g1.x = 1;
-  prof_begin(0, stream);
-  hipLaunchKernelGGL(k_idx_score, g1, dim3(256), (size_t)qt * (kNBins / 2) * 4, stream, sa);
-  prof_end(0, stream);
-  hipLaunchKernelGGL(k_idx_threshold, dim3((unsigned)n_q), dim3(256), 0, stream, q_off, q_pos, pool_off,
-                     n_seq, m, k, nrep, (const uint32_t*)hist, info);
+  hipError_t e = launch(0, kProfBoth, k_idx_score, g1, dim3(256), (size_t)qt * (kNBins / 2) * 4, stream, sa);
+  if (e == hipSuccess)
+    e = launch(-1, kProfNone, k_idx_threshold, dim3((unsigned)n_q), dim3(256), 0, stream, q_off, q_pos, pool_off,
+               n_seq, m, k, nrep, (const uint32_t*)hist, info);
   SelectArgs se{q_off, q_pos, pool_off, n_seq, m, k, max_pool, keys, info, counts, def, cand};
   dim3 g2((unsigned)((max_pool + kSelChunk - 1) / kSelChunk), (unsigned)n_q);
   if (g2.x == 0) g2.x = 1;
-  prof_begin(1, stream);
-  hipLaunchKernelGGL(k_idx_select, g2, dim3(256), 0, stream, se);
-  prof_end(1, stream);
+  if (e == hipSuccess) e = launch(1, kProfBoth, k_idx_select, g2, dim3(256), 0, stream, se);
   const size_t bm_bytes = (size_t)((max_pool + 31) / 32) * 4;
   const int use_bitmap = bm_bytes <= (size_t)kBitmapMaxBytes ? 1 : 0;
   FinalArgs fa{q_off, q_pos, pool_off, n_seq, m, k, nrep, use_bitmap, max_pool, counts, hist, def, cand, idx};
@@ -422,10 +418,9 @@ int launch_index_topk(int n_seq, int64_t n_q, int64_t max_q_per_seq, const int64
                               kBitmapMaxBytes);
     lds_attr_set = true;
   }
-  prof_begin(2, stream);
-  hipLaunchKernelGGL(k_idx_final, dim3((unsigned)n_q), dim3(1024), use_bitmap ? bm_bytes : 0, stream, fa);
-  prof_end(2, stream);
-  return hipGetLastError() == hipSuccess ? 0 : -1;
+  if (e == hipSuccess)
+    e = launch(2, kProfBoth, k_idx_final, dim3((unsigned)n_q), dim3(1024), use_bitmap ? bm_bytes : 0, stream, fa);
+  return e == hipSuccess && hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 }  // namespace csa

@@ -79,10 +79,9 @@ __device__ __forceinline__ void pf_load_a(const PfArgs& a, int64_t row0, int nsl
   asc = 127;
   if (slot < nslots) {
     const int64_t qrow = (row0 + slot) * 4 + head;
-    const uint4 u = *reinterpret_cast<const uint4*>(a.q_codes + qrow * 32 + kb * 16);
+    uint4 u = *reinterpret_cast<const uint4*>(a.q_codes + qrow * 32 + kb * 16);
+    asc = fold_head_weight(u, (int)a.q_scales[qrow * 2 + kb], a.w[qrow]);  // w_h folded into the block scale
     av[0] = (int)u.x; av[1] = (int)u.y; av[2] = (int)u.z; av[3] = (int)u.w;
-    const int we = (int)((__float_as_uint(a.w[qrow]) >> 23) & 255u) - 127;
-    asc = (int)a.q_scales[qrow * 2 + kb] + we;  // w_h = 2^we folded into the block scale
   }
 }
 
@@ -653,19 +652,13 @@ int launch_prefill_topk(int n_seq, int64_t n_q, int64_t max_q_per_seq, const int
     attr = true;
   }
   const unsigned nblk = (unsigned)(n_seq * a.bps);
-  prof_begin(7, stream);
-  hipLaunchKernelGGL(k_pf_thresh, dim3((unsigned)(n_seq * a.bps_t)), dim3(256), lds1, stream, a);
-  prof_end(7, stream);
+  hipError_t e = launch(7, kProfBoth, k_pf_thresh, dim3((unsigned)(n_seq * a.bps_t)), dim3(256), lds1, stream, a);
   a.kw = pf_keys_per_wg(max_pool, (int64_t)nblk);
   dim3 g2((unsigned)((max_pool + a.kw - 1) / a.kw), nblk);
   if (g2.x == 0) g2.x = 1;
-  prof_begin(0, stream);
-  hipLaunchKernelGGL(k_pf_score, g2, dim3(256), 0, stream, a);
-  prof_end(0, stream);
-  prof_begin(8, stream);
-  hipLaunchKernelGGL(k_pf_select, dim3((unsigned)((n_q + 1) / 2)), dim3(128), lds3, stream, a);
-  prof_end(8, stream);
-  return hipGetLastError() == hipSuccess ? 0 : -1;
+  if (e == hipSuccess) e = launch(0, kProfBoth, k_pf_score, g2, dim3(256), 0, stream, a);
+  if (e == hipSuccess) e = launch(8, kProfBoth, k_pf_select, dim3((unsigned)((n_q + 1) / 2)), dim3(128), lds3, stream, a);
+  return e == hipSuccess && hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 }  // namespace csa

@@ -79,13 +79,9 @@ int launch_mxfp4_quant(bool bf16, int64_t rows, int dim, const void* x, uint8_t*
   const int64_t nblocks = rows * (dim / 32);
   if (nblocks == 0) return 0;
   const dim3 grid((unsigned)((nblocks + 255) / 256));
-  prof_begin(10, stream);
-  if (bf16)
-    hipLaunchKernelGGL(k_mxfp4_quant<true>, grid, dim3(256), 0, stream, nblocks, (const uint8_t*)x, codes, scales);
-  else
-    hipLaunchKernelGGL(k_mxfp4_quant<false>, grid, dim3(256), 0, stream, nblocks, (const uint8_t*)x, codes, scales);
-  prof_end(10, stream);
-  return hipGetLastError() == hipSuccess ? 0 : -1;
+  const hipError_t e = launch(10, kProfBoth, bf16 ? k_mxfp4_quant<true> : k_mxfp4_quant<false>, grid, dim3(256), 0,
+                              stream, nblocks, (const uint8_t*)x, codes, scales);
+  return e == hipSuccess && hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 }  // namespace csa

@@ -1,14 +1,35 @@
 // Host-side launchers of the libcsa kernels (internal to the library).
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
 
 namespace csa {
 
-// tracing hook: events recorded around one internal kernel (thread-local)
-void prof_begin(int kernel_id, hipStream_t stream);
-void prof_end(int kernel_id, hipStream_t stream);
+// Tracing hook: the caller's events for one internal kernel id (thread-local;
+// null when none are set).  Every kernel is launched through launch() below:
+// when the hook holds events for the launch's id they are handed to
+// hipExtLaunchKernel, which attaches them to the dispatch itself, so they time
+// the kernel's execution on the GPU (as a kernel trace does), not its enqueue;
+// otherwise it is a plain hipLaunchKernel.  `mark` says which of the id's
+// events a launch carries: the start for the first of several launches, the
+// stop for the last, both for a single one.
+hipEvent_t prof_event(int kernel_id, int stop);
+enum { kProfNone = 0, kProfStart = 1, kProfStop = 2, kProfBoth = 3 };
+template <class T>
+struct launch_arg {
+  using type = T;
+};
+template <typename... P>
+inline hipError_t launch(int kernel_id, int mark, void (*k)(P...), dim3 grid, dim3 block, size_t lds,
+                         hipStream_t stream, typename launch_arg<P>::type... args) {
+  void* a[] = {(void*)&args..., nullptr};
+  hipEvent_t e0 = (mark & kProfStart) ? prof_event(kernel_id, 0) : nullptr;
+  hipEvent_t e1 = (mark & kProfStop) ? prof_event(kernel_id, 1) : nullptr;
+  if (e0 || e1) return hipExtLaunchKernel((const void*)k, grid, block, a, lds, stream, e0, e1, 0);
+  return hipLaunchKernel((const void*)k, grid, block, a, lds, stream);
+}
 
 int launch_compress(bool bf16, int n_seq, const int64_t* tok_off, const int64_t* pool_off,
                     int64_t max_len, int m, int width, const void* x, const void* z, void* out,

@@ -378,7 +378,12 @@ def _index_rows(wl, host, rows):
     for row in rows:
         want = P.oracle_topk_row(host, wl, row, seqs[row], wl.k, wl.m)
         assert np.array_equal(got[row], want), f"row {row} (seq {seqs[row]}, t={host['q_pos'][row]})"
-    assert int(torch.count_nonzero(ws.buf)) == 0, "the workspace is not left zero-filled"
+    if batch.max_q_per_seq >= 16:  # the prefill path's workspace is all candidate bitmaps, left zero
+        assert int(torch.count_nonzero(ws.buf)) == 0, "the workspace is not left zero-filled"
+    # reused without clearing, the workspace gives the same selection
+    idx2 = csa.csa_index_topk(batch, d["pool_off"], max_pool, wl.m, wl.k, d["qc"], d["qs"], d["w"], d["kc"],
+                              d["ks"], ws=ws)
+    assert np.array_equal(P.torch_to_np(idx2), got), "a second call on the same workspace differs"
     return got
 
 
@@ -576,6 +581,11 @@ SHARED_CASES = {
                                      W=200, m_hca=64, W_hca=64, seed=32), 2048),
     "shared_long": (lambda: small_wl("decode_shared_long", [262147, 131072 + 4099, 131072 + 77, 131072 + 1030],
                                      [1] * 4, k=1024, seed=33), 131072),
+    # a prefix of 4226 tokens: the CSA block 1056 (tokens 4224..4227) and the HCA block 33
+    # (tokens 4224..4351) straddle its end, so each sharer's own caches pool them from
+    # the prefix's tokens and its own
+    "shared_straddle": (lambda: small_wl("decode_shared_straddle", [20003, 4226 + 5001, 4226 + 77, 4226 + 2],
+                                         [1] * 4, k=256, seed=35), 4226),
 }
 
 
@@ -729,7 +739,8 @@ def _scatter(src, off, table, page_rows, n_pages):
 def test_paged_decode_is_bit_identical_to_contiguous_caches(name):
     """csa_hca_decode_paged over pooled caches scattered into shuffled pages
     (one case with a sequence whose first pages are another's, over equal
-    data) gives exactly csa_hca_decode's outputs on the contiguous caches."""
+    data) gives exactly csa_hca_decode's outputs on the contiguous caches, and
+    the oracle's top-k and outputs on the first and last rows."""
     csa = _lib()
     make, pr, hpr, T = PAGED_CASES[name][:4]
     wl = make()
@@ -767,3 +778,69 @@ def test_paged_decode_is_bit_identical_to_contiguous_caches(name):
     torch.cuda.synchronize()
     for what, x, y in zip(("idx", "csa_out", "csa_lse", "hca_out", "hca_lse"), got, want):
         assert np.array_equal(x, y), f"{what} differs from the contiguous layout"
+    # the oracle on the logical sequences: the first and the last row
+    idx, co, cl, hop, hl = got
+    seqs = P.row_seq(host)
+    scale = 1 / math.sqrt(wl.d)
+    for r in sorted({0, wl.n_q - 1}):
+        b = seqs[r]
+        (t0, t1), (p0, p1), _ = P.seq_slices(host, b)
+        t = int(host["q_pos"][r])
+        o, l, i = oracle.csa_query(host["kv"][t0:t1], host["z"][t0:t1], host["q"][r], t, wl.m, wl.W, wl.k, scale,
+                                   host["qc"][r], host["qs"][r], host["w"][r], host["kc"][p0:p1], host["ks"][p0:p1])
+        assert np.array_equal(idx[r], i), f"top-k of row {r}"
+        P.check_close(co[r:r + 1], o[None], wl.dtype, f"csa output of row {r}")
+        P.check_close(cl[r:r + 1], l[None], "bf16", f"csa lse of row {r}")
+        ho_r, hl_r = oracle.hca_query(host["kv"][t0:t1], host["z"][t0:t1], host["q"][r], t, wl.m_hca, wl.W_hca, scale)
+        P.check_close(hop[r:r + 1], ho_r[None], wl.dtype, f"hca output of row {r}")
+        P.check_close(hl[r:r + 1], hl_r[None], "bf16", f"hca lse of row {r}")
+
+
+def _zero_weight_blocks(host):
+    """Indexer query blocks the fold of a head weight must survive: for every
+    query, head 0's first 32-element block all zero (codes 0 and -0) with
+    scale byte 0, head 1's second block all zero with byte 0, head 2's first
+    block all zero with byte 254, all with weights 0.5 on heads 0 and 1 (a
+    folded byte of -1 would be E8M0's NaN) and 2 on head 2 (255)."""
+    qc, qs, w = host["qc"].copy(), host["qs"].copy(), host["w"].copy()
+    qc[:, 0, :16] = np.where(np.arange(16) % 2 == 0, 0x00, 0x88).astype(np.uint8)
+    qs[:, 0, 0] = 0
+    qc[:, 1, 16:] = 0x08
+    qs[:, 1, 1] = 0
+    qc[:, 2, :16] = 0x80
+    qs[:, 2, 0] = 254
+    w[:, 0] = 0.5
+    w[:, 1] = 0.5
+    w[:, 2] = 2.0
+    host["qc"], host["qs"], host["w"] = qc, qs, w
+    return host
+
+
+@pytest.mark.parametrize("lengths,q_counts", [([3001, 70001, 517], [1, 1, 1]), ([5000, 9001], [40, 100])])
+def test_index_topk_with_zero_query_blocks_and_folded_weights(lengths, q_counts):
+    """csa_index_topk (decode and prefill paths) on queries with all-zero blocks
+    whose scale byte sits at the edge of E8M0's range, under head weights whose
+    fold would leave that range: the same top-k as the oracle's exact scores."""
+    csa = _lib()
+    wl = small_wl("index_zero_blocks", lengths, q_counts, k=128, seed=51)
+    host = _zero_weight_blocks(synth.make_inputs(wl, raw=False))
+    got = _index_rows(wl, host, range(wl.n_q))
+    assert got.shape == (wl.n_q, wl.k)
+
+
+def test_fused_decode_with_zero_query_blocks_and_folded_weights():
+    """The one-launch decode step on the same edge-case queries: top-k equal to
+    the oracle's and to csa_index_topk's."""
+    csa = _lib()
+    wl = small_wl("decode_zero_blocks", [3001, 70001, 517, 40003], [1] * 4, k=256, seed=52)
+    host = _zero_weight_blocks(synth.make_inputs(wl))
+    from long_context_compressed_05_amd.step import Layer, to_device
+    layer = Layer.from_host(_params(wl), host)
+    layer.build_caches()
+    dq = to_device({k: host[k] for k in ("q", "qc", "qs", "w")})
+    idx = P.torch_to_np(layer.decode_fused(dq["q"], dq["qc"], dq["qs"], dq["w"])[0])
+    layer.check_fused()
+    seqs = P.row_seq(host)
+    for r in range(wl.n_q):
+        want = P.oracle_topk_row(host, wl, r, seqs[r], wl.k, wl.m)
+        assert np.array_equal(idx[r], want), f"top-k of row {r}"
