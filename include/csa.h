@@ -285,6 +285,31 @@ int csa_hca_decode(const csa_batch* b, const int64_t* pool_off, int64_t max_pool
                    void* stream);
 
 /* ------------------------------------------------------------------------
+ * csa_hca_decode_noalloc — csa_hca_decode without a workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).  It allocates
+ * nothing: the step's workspace is a static scratch array of 64 MiB that the
+ * library holds on each GPU it runs on until the process ends.  Arguments,
+ * outputs and errors as csa_hca_decode (bit-identical results), plus
+ * CSA_ERR_UNSUPPORTED when the step needs more than the 64 MiB
+ * (csa_hca_decode_workspace() tells the size: 4 x 1M-token sequences need
+ * about 11 MB).  Before the first call on a device, and before a call whose
+ * shapes (n_q, max_pool, max_hpool, H, k, W, W_hca) differ from the previous
+ * call's on that device, a small kernel on `stream` clears the bytes the step
+ * uses.  Every call on a GPU shares that GPU's array and keeps the last
+ * call's contents: calls that overlap on one GPU (different streams or host
+ * threads) race and their results are undefined; order them on one stream.
+ * The wait-bound error word of this variant is not readable by the caller.
+ * ---------------------------------------------------------------------- */
+int csa_hca_decode_noalloc(const csa_batch* b, const int64_t* pool_off, int64_t max_pool,
+                           const int64_t* hpool_off, int64_t max_hpool, int m, int m_hca, int H, int d,
+                           float scale, int k, int W, int W_hca, const uint8_t* q_codes,
+                           const uint8_t* q_scales, const float* w, const uint8_t* k_codes,
+                           const uint8_t* k_scales, const void* q, const void* kv_pool,
+                           const void* kv_pool_hca, const void* kv_raw, int32_t* idx, void* csa_out,
+                           float* csa_lse, void* hca_out, float* hca_lse, void* stream);
+
+/* ------------------------------------------------------------------------
  * csa_hca_decode_shared — csa_hca_decode over caches whose leading part is
  * shared with another sequence (a prefix cache).
  * Pages: sigco.tistory.com KV-cache section (requests with a common prefix

@@ -23,7 +23,8 @@ CSA_F32, CSA_BF16 = 0, 1
 
 EXPORTS = ("csa_status_string", "csa_last_error", "csa_compress", "csa_cache_append", "csa_mxfp4_quantize", "csa_index_topk_workspace",
            "csa_index_topk", "csa_sparse_attn_workspace", "csa_sparse_attn", "hca_attn_workspace",
-           "hca_attn", "csa_hca_decode_workspace", "csa_hca_decode", "csa_hca_decode_shared", "csa_hca_decode_paged",
+           "hca_attn", "csa_hca_decode_workspace", "csa_hca_decode", "csa_hca_decode_noalloc", "csa_hca_decode_shared",
+           "csa_hca_decode_paged",
            "csa_hca_decode_check",
            "csa_hca_decode_fallbacks", "csa_profile_events")
 (CSA_K_IDX_SCORE, CSA_K_IDX_SELECT, CSA_K_IDX_FINAL, CSA_K_ATTN, CSA_K_ATTN_COMBINE, CSA_K_COMPRESS,
@@ -68,6 +69,8 @@ def lib():
     L.csa_hca_decode_workspace.argtypes = [bp, i64, i64, ci, ci, ci, ci, ci, ctypes.POINTER(sz)]
     L.csa_hca_decode.argtypes = [bp, vp, i64, vp, i64, ci, ci, ci, ci, ctypes.c_float, ci, ci, ci, vp, vp, vp, vp,
                                  vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.csa_hca_decode_noalloc.argtypes = [bp, vp, i64, vp, i64, ci, ci, ci, ci, ctypes.c_float, ci, ci, ci, vp, vp, vp,
+                                         vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     L.csa_hca_decode_shared.argtypes = [bp, vp, vp, vp, i64, vp, i64, ci, ci, ci, ci, ctypes.c_float, ci, ci, ci, vp,
                                         vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.csa_hca_decode_paged.argtypes = [bp, ci, vp, ci, vp, ci, vp, ci, vp, i64, i64, ci, ci, ci, ci, ctypes.c_float, ci,
@@ -366,6 +369,21 @@ def csa_hca_decode(batch: Batch, pool_off, max_pool: int, hpool_off, max_hpool: 
                                 _ptr(k_scales), _ptr(q), _ptr(kv_pool), _ptr(kv_pool_hca), _ptr(kv_raw), _ptr(idx),
                                 _ptr(csa_out), _ptr(csa_lse), _ptr(hca_out), _ptr(hca_lse), _ptr(buf), nbytes,
                                 _stream(stream)), "csa_hca_decode")
+    return idx, csa_out, csa_lse, hca_out, hca_lse
+
+
+def csa_hca_decode_noalloc(batch: Batch, pool_off, max_pool: int, hpool_off, max_hpool: int, m: int, m_hca: int,
+                           k: int, W: int, W_hca: int, scale: float, q_codes, q_scales, w, k_codes, k_scales, q,
+                           kv_pool, kv_pool_hca, kv_raw, idx, csa_out, csa_lse, hca_out, hca_lse, stream=None):
+    """csa_hca_decode on the library's static scratch: no workspace, and no
+    allocation in the call (the outputs are the caller's)."""
+    H, d = q.shape[-2], q.shape[-1]
+    b = batch.c()
+    _check(lib().csa_hca_decode_noalloc(ctypes.byref(b), _ptr(pool_off), max_pool, _ptr(hpool_off), max_hpool, m,
+                                        m_hca, H, d, scale, k, W, W_hca, _ptr(q_codes), _ptr(q_scales), _ptr(w),
+                                        _ptr(k_codes), _ptr(k_scales), _ptr(q), _ptr(kv_pool), _ptr(kv_pool_hca),
+                                        _ptr(kv_raw), _ptr(idx), _ptr(csa_out), _ptr(csa_lse), _ptr(hca_out),
+                                        _ptr(hca_lse), _stream(stream)), "csa_hca_decode_noalloc")
     return idx, csa_out, csa_lse, hca_out, hca_lse
 
 

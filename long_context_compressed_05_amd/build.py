@@ -15,7 +15,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libcsa.so")
-SOURCES = ["csa_abi.hip", "k_compress.hip", "k_append.hip", "k_quant.hip", "k_index.hip", "k_prefill.hip", "k_attn.hip", "k_fused.hip"]
+SOURCES = ["csa_abi.hip", "k_compress.hip", "k_append.hip", "k_quant.hip", "k_index.hip", "k_prefill.hip", "k_attn.hip", "k_fused.hip", "noalloc.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

@@ -103,7 +103,7 @@ static int hca_decode_impl(const csa_batch* b, const int32_t* pre_seq, const int
                            const uint8_t* q_codes, const uint8_t* q_scales, const float* w, const uint8_t* k_codes,
                            const uint8_t* k_scales, const void* q, const void* kv_pool, const void* kv_pool_hca,
                            const void* kv_raw, int32_t* idx, void* csa_out, float* csa_lse, void* hca_out,
-                           float* hca_lse, void* ws, size_t ws_bytes, void* stream) {
+                           float* hca_lse, void* ws, size_t ws_bytes, void* stream, bool noalloc = false) {
   int rc = check_batch(b);
   if (rc) return rc;
   if (b->n_q != b->n_seq || b->max_q_per_seq != 1)
@@ -122,6 +122,12 @@ static int hca_decode_impl(const csa_batch* b, const int32_t* pre_seq, const int
   if (!aligned16(q_codes) || !aligned16(k_codes) || !aligned16(q) || !aligned16(kv_pool) ||
       !aligned16(kv_pool_hca) || !aligned16(kv_raw) || !aligned16(csa_out) || !aligned16(hca_out))
     return fail(CSA_ERR_INVALID, "codes, q, caches and outputs must be 16-byte aligned");
+  if (noalloc) {  // the library's static scratch (cleared here when the layout changes)
+    const char* err = "";
+    rc = csa::noalloc_prepare((int)b->n_q, max_pool, max_hpool, H, k, W, W_hca, (hipStream_t)stream, &ws, &ws_bytes,
+                              &err);
+    if (rc) return fail(rc, "%s", err);
+  }
   const size_t need = csa::plan_fused(b->n_q, max_pool, max_hpool, H, k, W, W_hca).ws_bytes;
   if (!ws || ws_bytes < need)
     return fail(CSA_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need, ws_bytes);
@@ -146,6 +152,18 @@ int csa_hca_decode(const csa_batch* b, const int64_t* pool_off, int64_t max_pool
   return hca_decode_impl(b, nullptr, nullptr, nullptr, pool_off, max_pool, hpool_off, max_hpool, m, m_hca, H, d, scale, k, W,
                          W_hca, q_codes, q_scales, w, k_codes, k_scales, q, kv_pool, kv_pool_hca, kv_raw, idx,
                          csa_out, csa_lse, hca_out, hca_lse, ws, ws_bytes, stream);
+}
+
+int csa_hca_decode_noalloc(const csa_batch* b, const int64_t* pool_off, int64_t max_pool,
+                           const int64_t* hpool_off, int64_t max_hpool, int m, int m_hca, int H, int d,
+                           float scale, int k, int W, int W_hca, const uint8_t* q_codes,
+                           const uint8_t* q_scales, const float* w, const uint8_t* k_codes,
+                           const uint8_t* k_scales, const void* q, const void* kv_pool,
+                           const void* kv_pool_hca, const void* kv_raw, int32_t* idx, void* csa_out,
+                           float* csa_lse, void* hca_out, float* hca_lse, void* stream) {
+  return hca_decode_impl(b, nullptr, nullptr, nullptr, pool_off, max_pool, hpool_off, max_hpool, m, m_hca, H, d, scale, k,
+                         W, W_hca, q_codes, q_scales, w, k_codes, k_scales, q, kv_pool, kv_pool_hca, kv_raw, idx,
+                         csa_out, csa_lse, hca_out, hca_lse, nullptr, 0, stream, true);
 }
 
 int csa_hca_decode_shared(const csa_batch* b, const int32_t* prefix_seq, const int64_t* prefix_tokens,

@@ -92,6 +92,11 @@ struct FusedPaging {
   const int64_t* hplen;
   int max_hpages, hpage_rows;
 };
+// the static scratch of the no-allocation decode entry point (noalloc.hip):
+// its device address on the current device, cleared first when the layout
+// differs from the last launch's on this device
+int noalloc_prepare(int R, int64_t max_pool, int64_t max_hpool, int H, int k, int W, int W_hca, hipStream_t stream,
+                    void** ws, size_t* ws_bytes, const char** err);
 int launch_fused(int R, const int64_t* tok_off, const int64_t* q_pos, const int64_t* pool_off,
                  const int64_t* hpool_off, const int32_t* pre_seq, const int64_t* pre_tok, const FusedPaging* paging,
                  int64_t max_pool, int64_t max_hpool, int m, int m_hca, int H,

@@ -208,3 +208,21 @@ def test_decode_paged_validation():
     import torch
     if not torch.cuda.is_available():
         assert call() == csa.CSA_ERR_DEVICE
+
+
+def test_decode_noalloc_validation():
+    """The no-allocation decode entry point validates as csa_hca_decode does,
+    before it touches the device or its scratch."""
+    L = csa.lib()
+    b = _batch(n_seq=4, n_q=4, maxq=1)
+
+    def call(m=4, k=64, H=64, d=128, idx=FAKE, bb=b):
+        return L.csa_hca_decode_noalloc(ctypes.byref(bb), FAKE, 1000, FAKE, 100, m, 128, H, d, 0.088, k, 128, 0, FAKE,
+                                        FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, idx, FAKE, FAKE, FAKE, FAKE, None)
+    assert call(m=0) == csa.CSA_ERR_INVALID
+    assert call(k=0) == csa.CSA_ERR_INVALID
+    assert call(bb=_batch(n_seq=4, n_q=8, maxq=2)) == csa.CSA_ERR_UNSUPPORTED  # decode batches only
+    import torch
+    if not torch.cuda.is_available():
+        assert call() == csa.CSA_ERR_DEVICE
+        assert call(idx=None) == csa.CSA_ERR_DEVICE  # the device check comes before the pointer checks
