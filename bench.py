@@ -1,5 +1,5 @@
 #!/usr/bin/env python3
-"""CSA + HCA decode benchmark on one MI355X (gfx950).
+"""CSA + HCA decode and prefill benchmark on one MI355X (gfx950).
 
 One step = one pass of the whole decode hot path over one batch: indexer
 scoring, exact top-k, CSA sparse attention over the top-k pooled rows plus the
@@ -10,11 +10,15 @@ Pooled caches are built once with csa_compress before timing (its throughput
 is reported apart).  --copy-calibration runs only a 1 GiB device copy, the
 scale reference for the HBM byte counters.
 
-Default workload: 4 sequences x 1,048,576 tokens, 64 query heads on one bf16
+Headline workload: 4 sequences x 1,048,576 tokens, 64 query heads on one bf16
 KV head, d = 128, m = 4 (262,144 pooled entries), top-k 1024, window 128,
 m' = 128 (8192 entries), indexer 4 heads x 64 in MXFP4.  Inputs are seeded
 synthetic data already resident in HBM; R input sets are rotated so that
-consecutive steps do not hit the 256 MB Infinity Cache.
+consecutive steps do not hit the 256 MB Infinity Cache.  Also reported: the
+other decode configurations (4096-token fp32, 16 x 64K, 32 ragged sequences),
+HCA with a window, the prefill step of a 4096-token chunk on a 64K cache, the
+measured peaks of the part (HBM read, FP4 and bf16 MFMA), cache upkeep,
+shared-prefix and paged decode, and the CPU oracle beside them.
 
 Prints ONE JSON line on stdout; progress goes to stderr.
 """
@@ -49,6 +53,172 @@ def decode_bytes_per_query(n_vis, k, W, L, n_hvis, H, d, es):
             + 4 * H * d * es + 4 * k + (4 * 34 + 4 * 4))
 
 
+def pct(xs):
+    """median, p10 and p90 of a list of durations (microseconds)."""
+    a = np.asarray(xs, dtype=np.float64)
+    return {"median": round(float(np.median(a)), 3), "p10": round(float(np.percentile(a, 10)), 3),
+            "p90": round(float(np.percentile(a, 90)), 3), "mean": round(float(a.mean()), 3), "n": int(a.size)}
+
+
+def step_bytes_of(wl, host):
+    """Algorithmic bytes of one decode step over every query of the batch."""
+    es = 2 if wl.dtype == "bf16" else 4
+    q_pos = host["q_pos"]
+    q_seq = np.repeat(np.arange(wl.B), np.diff(host["q_off"]))
+    P_b, Ph_b = np.diff(host["pool_off"]), np.diff(host["hpool_off"])
+    tot = 0
+    for i in range(wl.n_q):
+        b, t = q_seq[i], int(q_pos[i])
+        n_vis = min((t + 1) // wl.m, int(P_b[b]))
+        n_hvis = min((t + 1) // wl.m_hca, int(Ph_b[b]))
+        tot += decode_bytes_per_query(n_vis, wl.k, wl.W, t + 1, n_hvis, wl.H, wl.d, es)
+    return int(tot)
+
+
+class DecodeBench:
+    """One decode workload resident on the GPU: raw KV, pooled caches (built
+    with csa_compress, timed apart) and R rotated input sets (queries, indexer
+    codes, scales and weights, indexer keys, HCA cache) so that consecutive
+    steps do not find their data in the 256 MB Infinity Cache."""
+
+    def __init__(self, torch, csa, synth, to_device, wl, R, path):
+        from long_context_compressed_05_amd.step import Layer, Params
+        self.torch, self.csa, self.wl, self.R = torch, csa, wl, max(1, R)
+        self.path = path
+        dev = "cuda"
+        self.host = host = synth.make_inputs(wl)
+        self.es = 2 if wl.dtype == "bf16" else 4
+        p = Params(H=wl.H, d=wl.d, m=wl.m, k=wl.k, W=wl.W, m_hca=wl.m_hca, W_hca=wl.W_hca)
+        self.layer = layer = Layer.from_host(p, host, dev)
+        n_pool, n_hpool = int(host["pool_off"][-1]), int(host["hpool_off"][-1])
+        layer.pooled = torch.empty((n_pool, 2, wl.d), dtype=layer.kv.dtype, device=dev)
+        layer.hpooled = torch.empty((n_hpool, 2, wl.d), dtype=layer.kv.dtype, device=dev)
+        self.compress = {}
+        for name, m, off, out, kid in (("csa", wl.m, layer.pool_off, layer.pooled, csa.CSA_K_COMPRESS),
+                                       ("hca", wl.m_hca, layer.hpool_off, layer.hpooled, csa.CSA_K_COMPRESS)):
+            csa.csa_compress(layer.kv, layer.z, layer.tok_off, off, layer.batch.max_len, m, out)  # warm
+            e0, e1 = csa.HipEvent(), csa.HipEvent()
+            csa.csa_profile_events(kid, e0, e1)
+            csa.csa_compress(layer.kv, layer.z, layer.tok_off, off, layer.batch.max_len, m, out)
+            csa.csa_profile_events(kid)
+            ms = e0.elapsed_ms(e1)
+            rows = sum((L // m) * m for L in wl.lengths)
+            nbytes = 2 * rows * 2 * wl.d * self.es + (rows // m) * 2 * wl.d * self.es
+            self.compress[name] = {"m": m, "us": round(ms * 1e3, 2), "GB/s": round(nbytes / ms / 1e6, 1)}
+        self.sets = []
+        P_tot = n_pool
+        for r in range(self.R):
+            if r == 0:
+                hs = {k: host[k] for k in ("q", "qc", "qs", "w", "kc", "ks")}
+            else:
+                s_ = wl.seed + 7919 * r
+                hs = {"q": synth.normal(s_, synth.S_Q, wl.n_q * wl.H * wl.d, wl.dtype).reshape(wl.n_q, wl.H, wl.d),
+                      "qc": synth.codes4(s_, synth.S_QCODE, wl.n_q * 128, wl.codeset).reshape(wl.n_q, 4, 32),
+                      "qs": synth.exp_bytes(s_, synth.S_QSCALE, wl.n_q * 8, *wl.scale_exp).reshape(wl.n_q, 4, 2),
+                      "w": synth.pow2(s_, synth.S_W, wl.n_q * 4, *wl.w_exp).reshape(wl.n_q, 4),
+                      "kc": synth.codes4(s_, synth.S_KCODE, P_tot * 32, wl.codeset).reshape(P_tot, 32),
+                      "ks": synth.exp_bytes(s_, synth.S_KSCALE, P_tot * 2, *wl.scale_exp).reshape(P_tot, 2)}
+            d = to_device(hs, dev)
+            d["hpooled"] = layer.hpooled if r == 0 else layer.hpooled.clone()
+            d["idx"] = torch.empty((wl.n_q, wl.k), dtype=torch.int32, device=dev)
+            d["co"] = torch.empty((wl.n_q, wl.H, wl.d), dtype=layer.kv.dtype, device=dev)
+            d["cl"] = torch.empty((wl.n_q, wl.H), dtype=torch.float32, device=dev)
+            d["ho"] = torch.empty_like(d["co"])
+            d["hl"] = torch.empty_like(d["cl"])
+            self.sets.append(d)
+        self.step_bytes = step_bytes_of(wl, host)
+        self.scale = 1.0 / math.sqrt(wl.d)
+
+    def step(self, r):
+        d, layer, wl, csa = self.sets[r % self.R], self.layer, self.wl, self.csa
+        if self.path == "fused":
+            layer.decode_fused(d["q"], d["qc"], d["qs"], d["w"], idx=d["idx"], csa_out=d["co"], csa_lse=d["cl"],
+                               hca_out=d["ho"], hca_lse=d["hl"], kc=d["kc"], ks=d["ks"], hpooled=d["hpooled"])
+        else:
+            b = layer.batch
+            csa.csa_index_topk(b, layer.pool_off, layer.max_pool, wl.m, wl.k, d["qc"], d["qs"], d["w"], d["kc"],
+                               d["ks"], idx=d["idx"], ws=layer.ws_idx)
+            csa.csa_sparse_attn(b, layer.pool_off, d["q"], layer.pooled, layer.kv, d["idx"], wl.W, self.scale,
+                                out=d["co"], lse=d["cl"], ws=layer.ws_csa)
+            csa.hca_attn(b, layer.hpool_off, layer.max_hpool, wl.m_hca, d["q"], d["hpooled"], layer.kv, wl.W_hca,
+                         self.scale, out=d["ho"], lse=d["hl"], ws=layer.ws_hca)
+
+    def run(self, steps, warmup, graph=True):
+        """Warm-up, then (1) `steps` eager steps with per-launch events (the
+        fused kernel's events ride on its dispatch: kernel execution only; the
+        separate calls' step is bracketed by stream events), (2) a HIP graph of
+        the R rotated steps replayed until at least `steps` steps ran, timed as
+        a whole.  Returns the per-step figures."""
+        torch, csa = self.torch, self.csa
+        for i in range(warmup):
+            self.step(i)
+        torch.cuda.synchronize()
+        per = []
+        if self.path == "fused":
+            ev = [(csa.HipEvent(), csa.HipEvent()) for _ in range(steps)]
+            for i in range(steps):
+                csa.csa_profile_events(csa.CSA_K_FUSED, ev[i][0], ev[i][1])
+                self.step(i)
+            csa.csa_profile_events(csa.CSA_K_FUSED)
+            torch.cuda.synchronize()
+            self.layer.check_fused()
+            per = [a.elapsed_ms(b) * 1e3 for a, b in ev]
+        else:
+            for i in range(steps):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                self.step(i)
+                e1.record()
+                torch.cuda.synchronize()
+                per.append(e0.elapsed_time(e1) * 1e3)
+        g = None
+        if graph:
+            try:
+                g = torch.cuda.CUDAGraph()
+                cap = torch.cuda.Stream()
+                cap.wait_stream(torch.cuda.current_stream())
+                with torch.cuda.stream(cap):
+                    with torch.cuda.graph(g, stream=cap):
+                        for r in range(self.R):
+                            self.step(r)
+                torch.cuda.current_stream().wait_stream(cap)
+                g.replay()
+                torch.cuda.synchronize()
+            except Exception as e:
+                log(f"graph capture unavailable ({e!r}); timing eager launches")
+                g = None
+        reps = max(1, (steps + self.R - 1) // self.R) if g is not None else steps
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0.record()
+        if g is not None:
+            for _ in range(reps):
+                g.replay()
+        else:
+            for i in range(steps):
+                self.step(i)
+        t1.record()
+        torch.cuda.synchronize()
+        n_steps = reps * self.R if g is not None else steps
+        ms_step = t0.elapsed_time(t1) / n_steps
+        if self.path == "fused":
+            self.layer.check_fused()
+        wl = self.wl
+        kern = pct(per)
+        out = {"workload": wl.name, "path": self.path, "rotate_sets": self.R, "steps_timed": n_steps,
+               "us_per_step": round(ms_step * 1e3, 3),
+               "timing": "hip graph of the rotated steps, replayed" if g is not None else "eager launches",
+               "queries_per_s": round(wl.n_q / (ms_step * 1e-3), 1), "step_bytes": self.step_bytes,
+               "GB/s": round(self.step_bytes / (ms_step * 1e-3) / 1e9, 1),
+               "frac_of_8TB/s": round(self.step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+               ("kernel_us" if self.path == "fused" else "eager_step_us"): kern}
+        if self.path == "fused":
+            achieved = self.step_bytes / (kern["median"] * 1e-6) / 1e9
+            out["kernel_GB/s"] = round(achieved, 1)
+            out["kernel_frac_of_8TB/s"] = round(achieved / HBM_PEAK_GBS, 4)
+        return out, ms_step, per
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -58,12 +228,13 @@ def main():
     ap.add_argument("--rotate", type=int, default=20, help="input sets cycled through the timed steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
-    ap.add_argument("--no-shared", action="store_true", help="skip the shared-prefix decode section")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="time the headline decode step only (no other configs, sections, peaks or CPU baseline)")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of a captured HIP graph")
     ap.add_argument("--path", choices=["fused", "separate"], default="fused",
                     help="fused: one csa_hca_decode launch per step; separate: csa_index_topk + csa_sparse_attn + hca_attn")
     ap.add_argument("--prefill-only", action="store_true",
-                    help="only time the prefill indexer (4096 queries over a 65,536-token cache) and print its record")
+                    help="only time the prefill step (4096 queries over a 65,536-token cache) and print its record")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device-to-device copy of known size (the HBM counter calibration)")
     args = ap.parse_args()
@@ -77,14 +248,13 @@ def main():
     import torch
     import synth
     import long_context_compressed_05_amd as csa
-    from long_context_compressed_05_amd.step import Layer, Params, to_device
+    from long_context_compressed_05_amd.step import to_device
 
     assert torch.cuda.is_available(), "bench.py needs a ROCm GPU"
     if args.copy_calibration:
         copy_calibration(torch)
         return
     csa.lib()
-    dev = "cuda"
     torch.cuda.init()
     if args.prefill_only:
         print(json.dumps({"prefill": bench_prefill_chunk(torch, csa, synth, to_device, log)}), flush=True)
@@ -92,162 +262,17 @@ def main():
 
     wl = synth.WORKLOADS[args.workload]()
     log(f"workload {wl.name}: B={wl.B} max_len={max(wl.lengths)} n_q={wl.n_q}; generating inputs")
-    host = synth.make_inputs(wl)
-    es = 2 if wl.dtype == "bf16" else 4
-    p = Params(H=wl.H, d=wl.d, m=wl.m, k=wl.k, W=wl.W, m_hca=wl.m_hca, W_hca=wl.W_hca)
-    layer = Layer.from_host(p, host, dev)
-    log("inputs resident on the GPU; building pooled caches")
-
-    # ---- compress (cache build), timed apart ----------------------------------
-    n_pool, n_hpool = int(host["pool_off"][-1]), int(host["hpool_off"][-1])
-    layer.pooled = torch.empty((n_pool, 2, wl.d), dtype=layer.kv.dtype, device=dev)
-    layer.hpooled = torch.empty((n_hpool, 2, wl.d), dtype=layer.kv.dtype, device=dev)
-    compress = {}
-    for name, m, off, out in (("csa", wl.m, layer.pool_off, layer.pooled), ("hca", wl.m_hca, layer.hpool_off, layer.hpooled)):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        csa.csa_compress(layer.kv, layer.z, layer.tok_off, off, layer.batch.max_len, m, out)  # warm
-        torch.cuda.synchronize()
-        e0.record()
-        csa.csa_compress(layer.kv, layer.z, layer.tok_off, off, layer.batch.max_len, m, out)
-        e1.record()
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1)
-        rows = sum((L // m) * m for L in wl.lengths)
-        nbytes = 2 * rows * 2 * wl.d * es + (rows // m) * 2 * wl.d * es
-        compress[name] = {"m": m, "ms": round(ms, 4), "GB/s": round(nbytes / ms / 1e6, 1)}
-    log(f"compress: {compress}")
-
-    # ---- rotation sets ---------------------------------------------------------
-    R = max(1, args.rotate)
-    sets = []
-    P_tot = int(host["pool_off"][-1])
-    for r in range(R):
-        if r == 0:
-            hs = {k: host[k] for k in ("q", "qc", "qs", "w", "kc", "ks")}
-        else:
-            s = wl.seed + 7919 * r
-            hs = {
-                "q": synth.normal(s, synth.S_Q, wl.n_q * wl.H * wl.d, wl.dtype).reshape(wl.n_q, wl.H, wl.d),
-                "qc": synth.codes4(s, synth.S_QCODE, wl.n_q * 128, wl.codeset).reshape(wl.n_q, 4, 32),
-                "qs": synth.exp_bytes(s, synth.S_QSCALE, wl.n_q * 8, *wl.scale_exp).reshape(wl.n_q, 4, 2),
-                "w": synth.pow2(s, synth.S_W, wl.n_q * 4, *wl.w_exp).reshape(wl.n_q, 4),
-                "kc": synth.codes4(s, synth.S_KCODE, P_tot * 32, wl.codeset).reshape(P_tot, 32),
-                "ks": synth.exp_bytes(s, synth.S_KSCALE, P_tot * 2, *wl.scale_exp).reshape(P_tot, 2),
-            }
-        d = to_device(hs, dev)
-        d["hpooled"] = layer.hpooled if r == 0 else layer.hpooled.clone()
-        d["idx"] = torch.empty((wl.n_q, wl.k), dtype=torch.int32, device=dev)
-        d["co"] = torch.empty((wl.n_q, wl.H, wl.d), dtype=layer.kv.dtype, device=dev)
-        d["cl"] = torch.empty((wl.n_q, wl.H), dtype=torch.float32, device=dev)
-        d["ho"] = torch.empty_like(d["co"])
-        d["hl"] = torch.empty_like(d["cl"])
-        sets.append(d)
-    log(f"{R} rotation sets resident")
-
-    batch = layer.batch
-    scale = 1.0 / math.sqrt(wl.d)
-
-    def step_fused(r):
-        d = sets[r % R]
-        layer.decode_fused(d["q"], d["qc"], d["qs"], d["w"], idx=d["idx"], csa_out=d["co"], csa_lse=d["cl"],
-                           hca_out=d["ho"], hca_lse=d["hl"], kc=d["kc"], ks=d["ks"], hpooled=d["hpooled"])
-
-    def step_separate(r):
-        d = sets[r % R]
-        csa.csa_index_topk(batch, layer.pool_off, layer.max_pool, wl.m, wl.k, d["qc"], d["qs"], d["w"], d["kc"],
-                           d["ks"], idx=d["idx"], ws=layer.ws_idx)
-        csa.csa_sparse_attn(batch, layer.pool_off, d["q"], layer.pooled, layer.kv, d["idx"], wl.W, scale,
-                            out=d["co"], lse=d["cl"], ws=layer.ws_csa)
-        csa.hca_attn(batch, layer.hpool_off, layer.max_hpool, wl.m_hca, d["q"], d["hpooled"], layer.kv, wl.W_hca,
-                     scale, out=d["ho"], lse=d["hl"], ws=layer.ws_hca)
-
-    step = step_fused if args.path == "fused" else step_separate
-    # the kernel whose duration is the roofline figure: the fused step kernel, or the indexer scoring kernel
-    prof_id = csa.CSA_K_FUSED if args.path == "fused" else csa.CSA_K_IDX_SCORE
-    prof_name = "k_decode_fused" if args.path == "fused" else "k_idx_score"
-
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    log(f"warmup {args.warmup} steps done; timing {args.steps} steps")
-
-    K = args.steps
-    # dominant kernel: HIP events around every launch of the indexer scoring kernel
-    # (eager steps, same inputs and rotation)
-    ev = [(csa.HipEvent(), csa.HipEvent()) for _ in range(K)]
-    torch.cuda.synchronize()
-    for i in range(K):
-        csa.csa_profile_events(prof_id, ev[i][0], ev[i][1])
-        step(i)
-    torch.cuda.synchronize()
-    csa.csa_profile_events(prof_id)
-    if args.path == "fused":
-        layer.check_fused()
-    score_ms = float(np.mean([a.elapsed_ms(b) for a, b in ev]))
-
-    graph = None
-    if not args.eager:
-        try:
-            graph = torch.cuda.CUDAGraph()
-            cap = torch.cuda.Stream()
-            cap.wait_stream(torch.cuda.current_stream())
-            with torch.cuda.stream(cap):
-                with torch.cuda.graph(graph, stream=cap):
-                    for r in range(R):
-                        step(r)
-            torch.cuda.current_stream().wait_stream(cap)
-            for _ in range(max(1, args.warmup // R)):
-                graph.replay()
-            torch.cuda.synchronize()
-        except Exception as e:
-            log(f"graph capture unavailable ({e!r}); timing eager launches")
-            graph = None
-    reps = max(1, K // R) if graph is not None else K
-    t_start, t_stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_start.record()
-    if graph is not None:
-        for _ in range(reps):
-            graph.replay()
-    else:
-        for i in range(K):
-            step(i)
-    t_stop.record()
-    torch.cuda.synchronize()
-    total_ms = t_start.elapsed_time(t_stop)
-    K = reps * R if graph is not None else K
-    ms_step = total_ms / K
-    if args.path == "fused":
-        layer.check_fused()
-    log(f"timed ({'graph' if graph is not None else 'eager'}, {args.path}): {ms_step * 1e3:.2f} us/step; "
-        f"profiled kernel {score_ms * 1e3:.2f} us/launch")
-
-    # algorithmic bytes
-    m_, mh = wl.m, wl.m_hca
-    q_pos = host["q_pos"]
-    q_seq = np.repeat(np.arange(wl.B), np.diff(host["q_off"]))
-    P_b = np.diff(host["pool_off"])
-    Ph_b = np.diff(host["hpool_off"])
-    step_bytes = 0
-    score_bytes = 0
-    for i in range(wl.n_q):
-        b = q_seq[i]
-        t = int(q_pos[i])
-        n_vis = min((t + 1) // m_, int(P_b[b]))
-        n_hvis = min((t + 1) // mh, int(Ph_b[b]))
-        step_bytes += decode_bytes_per_query(n_vis, wl.k, wl.W, t + 1, n_hvis, wl.H, wl.d, es)
-        score_bytes += 34 * n_vis + 4 * 34 + 4 * 4
-    qps = wl.n_q / (ms_step * 1e-3)
-    gbs = step_bytes / (ms_step * 1e-3) / 1e9
-    kernel_bytes = step_bytes if args.path == "fused" else score_bytes
-    achieved = kernel_bytes / (score_ms * 1e-3) / 1e9
-
+    db = DecodeBench(torch, csa, synth, to_device, wl, args.rotate, args.path)
+    log(f"inputs and {db.R} rotation sets resident; compress: {db.compress}")
+    head, ms_step, per = db.run(args.steps, args.warmup, graph=not args.eager)
+    log(f"headline: {head}")
+    prof_name = "k_decode_fused" if args.path == "fused" else None
     result = {
         "metric": METRIC,
-        "value": round(qps, 1),
+        "value": round(wl.n_q / (ms_step * 1e-3), 1),
         "unit": "queries/s",
         "n_gpus": 1,
-        "steps": K,
+        "steps": head["steps_timed"],
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 5),
         "higher_is_better": True,
@@ -255,22 +280,64 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if wl.dtype == "bf16" else "f32",
         "data": "synthetic",
-        "config": {**wl.describe(), "indexer": "mxfp4 4x64", "rotate_sets": R, "path": args.path,
-                   "timing": "hip graph of the rotated steps, replayed" if graph is not None else "eager launches"},
-        "hbm_gbps": round(gbs, 1),
-        "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
-        "step_bytes": int(step_bytes),
-        "roofline": {"bound": "hbm", "kernel": prof_name,
-                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": counted_traffic(prof_name, wl.name),
-                     "bytes_per_launch": int(kernel_bytes), "avg_launch_us": round(score_ms * 1e3, 3)},
-        "compress": compress,
+        "config": {**wl.describe(), "indexer": "mxfp4 4x64", "rotate_sets": db.R, "path": args.path,
+                   "timing": head["timing"]},
+        "hbm_gbps": head["GB/s"],
+        "hbm_frac": head["frac_of_8TB/s"],
+        "step_bytes": db.step_bytes,
+        "decode": head,
+        "compress": db.compress,
     }
+    if prof_name:
+        kern = head["kernel_us"]
+        achieved = db.step_bytes / (kern["median"] * 1e-6) / 1e9
+        result["roofline"] = {"bound": "hbm", "kernel": prof_name, "achieved": round(achieved, 1),
+                              "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                              "traffic": counted_traffic(prof_name, wl.name), "bytes_per_launch": db.step_bytes,
+                              "launch_us": kern,
+                              "duration": "median kernel execution per launch (events attached to each dispatch)"}
+    if args.no_extras:
+        print(json.dumps(result), flush=True)
+        return
+
+    # ---- measured peaks of this part ---------------------------------------------
+    try:
+        result["peaks"] = bench_peaks(torch, db.step_bytes, log)
+        if "roofline" in result and "hbm_read_GB/s" in result["peaks"]:
+            mp = result["peaks"]["hbm_read_GB/s"]
+            result["roofline"]["measured_peak"] = mp
+            result["roofline"]["frac_of_measured_peak"] = round(result["roofline"]["achieved"] / mp, 4)
+    except Exception as e:  # reported, never silently replaced
+        result["peaks"] = {"error": repr(e)}
+
+    # ---- the other decode configurations, each in its own launch configuration ---
+    result["configs"] = {}
+    cfgs = [("decode_t4096_fp32", "separate", 4), ("decode_b16_t64k", "fused", 60), ("decode_ragged_b32", "fused", 12)]
+    for name, path, R in cfgs:
+        try:
+            cdb = DecodeBench(torch, csa, synth, to_device, synth.WORKLOADS[name](), R, path)
+            result["configs"][name], _, _ = cdb.run(max(args.steps, 20), args.warmup)
+            del cdb
+            torch.cuda.empty_cache()
+        except Exception as e:  # reported, never silently replaced
+            result["configs"][name] = {"error": repr(e)}
+        log(f"config {name}: {result['configs'][name]}")
+    # reading D5's alternative: HCA with the same 128-token window as CSA
+    try:
+        wl_w = synth.WORKLOADS[args.workload]()
+        wl_w.W_hca = wl_w.W
+        wdb = DecodeBench(torch, csa, synth, to_device, wl_w, args.rotate, args.path)
+        rec, _, _ = wdb.run(max(args.steps, 20), args.warmup)
+        rec["W_hca"] = wl_w.W_hca
+        result["configs"][args.workload + "_hca_window"] = rec
+        del wdb
+        torch.cuda.empty_cache()
+    except Exception as e:  # reported, never silently replaced
+        result["configs"][args.workload + "_hca_window"] = {"error": repr(e)}
 
     # ---- streaming cache upkeep (appends at the end of the 1M-token caches) -----
     try:
-        result["cache_append"] = bench_cache_append(torch, csa, layer, wl, host, log)
+        result["cache_append"] = bench_cache_append(torch, csa, db.layer, wl, db.host, log)
     except Exception as e:  # reported, never silently replaced
         result["cache_append"] = {"error": repr(e)}
 
@@ -280,27 +347,36 @@ def main():
     except Exception as e:  # reported, never silently replaced
         result["mxfp4_indexer"] = {"error": repr(e)}
 
-    # ---- shared-prefix decode: 4 questions over one ~1M-token document ----------
-    if args.workload == "decode_b4_t1m" and args.path == "fused" and not args.no_shared:
+    # ---- shared-prefix and paged decode over ~1M-token caches --------------------
+    if args.workload == "decode_b4_t1m" and args.path == "fused":
+        kernel_ms = head["kernel_us"]["median"] * 1e-3
         try:
-            result["shared_prefix"] = bench_shared_prefix(torch, csa, synth, to_device, log, score_ms)
+            result["shared_prefix"] = bench_shared_prefix(torch, csa, synth, to_device, log, kernel_ms)
         except Exception as e:  # reported, never silently replaced
             result["shared_prefix"] = {"error": repr(e)}
         try:
-            result["paged"] = bench_paged(torch, csa, layer, wl, host, sets, log, score_ms)
+            result["paged"] = bench_paged(torch, csa, db.layer, wl, db.host, db.sets, log, kernel_ms)
         except Exception as e:  # reported, never silently replaced
             result["paged"] = {"error": repr(e)}
 
-    # ---- prefill indexer (4096-token chunk on a 64K cache) ----------------------
+    # ---- the prefill step (4096-token chunk on a 64K cache) ----------------------
     if not args.no_prefill:
         try:
-            result["prefill_indexer"] = bench_prefill_indexer(torch, csa, synth, to_device, log)
+            result["prefill"] = bench_prefill_chunk(torch, csa, synth, to_device, log)
+            if "peaks" in result and "bf16_mfma_TFLOP/s" in result["peaks"]:
+                for part in ("csa_attn", "hca_attn"):
+                    rec = result["prefill"][part]
+                    rec["frac_of_measured_peak"] = round(rec["tflops"] / result["peaks"]["bf16_mfma_TFLOP/s"], 4)
+            if "peaks" in result and "fp4_mfma_TFLOP/s" in result["peaks"]:
+                rec = result["prefill"]["indexer"]
+                rec["scoring_frac_of_measured_peak"] = round(rec["scoring_tflops"] /
+                                                             result["peaks"]["fp4_mfma_TFLOP/s"], 4)
         except Exception as e:  # reported, never silently replaced
-            result["prefill_indexer"] = {"error": repr(e)}
+            result["prefill"] = {"error": repr(e)}
 
     # ---- CPU oracle baseline --------------------------------------------------
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(wl, host, log)
+        result["cpu_baseline"] = cpu_baseline(wl, db.host, log)
 
     print(json.dumps(result), flush=True)
 
@@ -591,49 +667,6 @@ def bench_mxfp4_recall(torch, csa, log, n_seq: int = 4, n_keys: int = 262144, k:
     return out
 
 
-def bench_prefill_indexer(torch, csa, synth, to_device, log, reps: int = 10):
-    """The prefill indexer on a 4096-query chunk over a 65,536-token cache
-    (17,408 pooled keys, top-512): the scoring kernel computes every visible
-    score exactly once (the algorithmic FLOPs are counted over visible scores
-    only); the threshold and selection kernels are timed beside it."""
-    wl = synth.prefill_4k_on_64k()
-    host = synth.make_inputs(wl, raw=False)
-    d = to_device({k: host[k] for k in ("qc", "qs", "w", "kc", "ks", "pool_off")})
-    batch = csa.Batch.from_host(host["tok_off"], host["q_off"], host["q_pos"])
-    max_pool = int(np.diff(host["pool_off"]).max())
-    ws = csa.Workspace()
-    idx = torch.empty((wl.n_q, wl.k), dtype=torch.int32, device="cuda")
-    call = lambda: csa.csa_index_topk(batch, d["pool_off"], max_pool, wl.m, wl.k, d["qc"], d["qs"], d["w"],
-                                      d["kc"], d["ks"], idx=idx, ws=ws)
-    call()
-    torch.cuda.synchronize()
-    kernels = {"score": csa.CSA_K_IDX_SCORE, "threshold": csa.CSA_K_PF_THRESH, "select": csa.CSA_K_PF_SELECT}
-    ev = {name: [(csa.HipEvent(), csa.HipEvent()) for _ in range(reps)] for name in kernels}
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0.record()
-    for i in range(reps):
-        for name, kid in kernels.items():
-            csa.csa_profile_events(kid, ev[name][i][0], ev[name][i][1])
-        call()
-    t1.record()
-    torch.cuda.synchronize()
-    for kid in kernels.values():
-        csa.csa_profile_events(kid)
-    us = {name: float(np.mean([a.elapsed_ms(b) for a, b in ev[name]])) * 1e3 for name in kernels}
-    call_ms = t0.elapsed_time(t1) / reps
-    n_vis = np.minimum((host["q_pos"] + 1) // wl.m, int(host["pool_off"][-1]))
-    flops = 2.0 * 4 * 64 * float(n_vis.sum())
-    tf = flops / (us["score"] * 1e-6) / 1e12
-    log(f"prefill indexer: scoring {us['score']:.1f} us ({tf:.1f} TFLOP/s), threshold {us['threshold']:.1f} us, "
-        f"select {us['select']:.1f} us, whole index_topk {call_ms * 1e3:.1f} us")
-    return {"workload": wl.name, "scoring_kernel": "k_pf_score", "scoring_kernel_us": round(us["score"], 2),
-            "threshold_kernel_us": round(us["threshold"], 2), "select_kernel_us": round(us["select"], 2),
-            "algorithmic_flop": flops, "tflops": round(tf, 2), "peak_tflops": FP4_PEAK_TFLOPS,
-            "frac": round(tf / FP4_PEAK_TFLOPS, 5), "index_topk_us": round(call_ms * 1e3, 2),
-            "queries_per_s": round(wl.n_q / (call_ms * 1e-3), 1),
-            "overhead_flop": {"threshold_sample": flops / 16, "select_rescore": "about 2 k keys per query"}}
-
-
 BF16_PEAK_TFLOPS = 2500.0
 
 
@@ -780,7 +813,7 @@ def bench_prefill_chunk(torch, csa, synth, to_device, log, reps: int = 10, oracl
         for r in rows:
             one(r)
         dt1 = time.time() - t0_
-        nthr = os.cpu_count() or 1
+        nthr = host_threads()
         t0_ = time.time()
         with ThreadPoolExecutor(max_workers=nthr) as ex:
             list(ex.map(one, [rows[i % len(rows)] for i in range(max(nthr, len(rows)))]))
@@ -797,21 +830,114 @@ def bench_prefill_chunk(torch, csa, synth, to_device, log, reps: int = 10, oracl
     return out
 
 
-def cpu_baseline(wl, host, log, min_seconds: float = 12.0):
-    """The oracle, as it stands, on the decode queries of the same workload
-    (one thread per query).  The oracle's fp64 HCA caches are built first and
-    not timed, as the GPU's pooled caches are not."""
+def bench_peaks(torch, csa, step_bytes, log, R: int = 20):
+    """Measured peaks of this part (the peaks/ reference kernels, events on
+    each dispatch): (1) HBM read of the decode step's byte count, R buffers
+    read in turn so that no launch finds its data in the Infinity Cache, best
+    median over grid sizes and loads in flight, and the sustained rate of a
+    1 GiB read; (2) dense FP4 MFMA (32x32x64, block-scaled) and bf16 MFMA
+    (16x16x32 and 32x32x16) rates, best over grid sizes."""
+    import peaks
+    L = peaks.lib()
+    dev = "cuda"
+    stream = torch.cuda.current_stream().cuda_stream
+    nbytes = (int(step_bytes) + 15) // 16 * 16
+    bufs = [torch.full((nbytes,), r, dtype=torch.uint8, device=dev) for r in range(R)]
+    sink = torch.zeros(1 << 20, dtype=torch.int32, device=dev)
+    out = {"read_bytes": nbytes, "read_buffers": R}
+    sweep = {}
+    best = None
+    for grid in (256, 512, 1024, 2048, 4096):
+        for unroll in (8, 16):
+            ev = [(csa.HipEvent(), csa.HipEvent()) for _ in range(3 * R)]
+            for i, (e0, e1) in enumerate(ev):
+                rc = L.peak_read(bufs[i % R].data_ptr(), nbytes, grid, unroll, sink.data_ptr(), e0.handle, e1.handle,
+                                 stream)
+                assert rc == 0, "peak_read launch failed"
+            torch.cuda.synchronize()
+            us = float(np.median([a.elapsed_ms(b) * 1e3 for a, b in ev[R:]]))
+            sweep[f"grid{grid}_u{unroll}"] = round(us, 2)
+            if best is None or us < best[0]:
+                best = (us, grid, unroll)
+    out["read_us"] = {"best": round(best[0], 2), "grid": best[1], "unroll": best[2], "sweep": sweep}
+    out["hbm_read_GB/s"] = round(nbytes / (best[0] * 1e-6) / 1e9, 1)
+    del bufs
+    big = torch.full((1 << 30,), 7, dtype=torch.uint8, device=dev)
+    ev = [(csa.HipEvent(), csa.HipEvent()) for _ in range(6)]
+    for e0, e1 in ev:
+        assert L.peak_read(big.data_ptr(), 1 << 30, 4096, 8, sink.data_ptr(), e0.handle, e1.handle, stream) == 0
+    torch.cuda.synchronize()
+    us = float(np.median([a.elapsed_ms(b) * 1e3 for a, b in ev[1:]]))
+    out["hbm_read_1GiB_GB/s"] = round((1 << 30) / (us * 1e-6) / 1e9, 1)
+    del big
+    fsink = torch.zeros(4096 * 256, dtype=torch.float32, device=dev)
+
+    def mfma_rate(fn, flop_per_inst, iters=4000):
+        best_tf, best_grid = 0.0, 0
+        for grid in (256, 512, 1024, 2048):
+            ev = [(csa.HipEvent(), csa.HipEvent()) for _ in range(3)]
+            for e0, e1 in ev:
+                assert fn(grid, iters, e0, e1) == 0, "MFMA peak launch failed"
+            torch.cuda.synchronize()
+            ms = float(np.median([a.elapsed_ms(b) for a, b in ev[1:]]))
+            tf = grid * 4 * iters * 4 * flop_per_inst / (ms * 1e-3) / 1e12
+            if tf > best_tf:
+                best_tf, best_grid = tf, grid
+        return round(best_tf, 1), best_grid
+    fp4, g4 = mfma_rate(lambda g, it, e0, e1: L.peak_mfma_fp4(g, it, fsink.data_ptr(), e0.handle, e1.handle, stream),
+                        peaks.FLOP_FP4_MFMA)
+    b16s, gs = mfma_rate(lambda g, it, e0, e1: L.peak_mfma_bf16(g, it, 0, fsink.data_ptr(), e0.handle, e1.handle,
+                                                                stream), peaks.FLOP_BF16_SMALL)
+    b16b, gb = mfma_rate(lambda g, it, e0, e1: L.peak_mfma_bf16(g, it, 1, fsink.data_ptr(), e0.handle, e1.handle,
+                                                                stream), peaks.FLOP_BF16_BIG)
+    out["fp4_mfma_TFLOP/s"] = fp4
+    out["bf16_mfma_16x16x32_TFLOP/s"] = b16s
+    out["bf16_mfma_32x32x16_TFLOP/s"] = b16b
+    out["bf16_mfma_TFLOP/s"] = max(b16s, b16b)
+    out["mfma_grids"] = {"fp4": g4, "bf16_16x16x32": gs, "bf16_32x32x16": gb}
+    out["datasheet"] = {"hbm_GB/s": HBM_PEAK_GBS, "fp4_TFLOP/s": FP4_PEAK_TFLOPS, "bf16_TFLOP/s": BF16_PEAK_TFLOPS}
+    log(f"measured peaks: {out}")
+    return out
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def host_threads() -> int:
+    """Threads the oracle may use: the CPUs this process may run on, at most 16
+    (a one-GPU machine's share)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def cpu_baseline(wl, host, log, min_seconds: float = 10.0, single_seconds: float = 4.0):
+    """The oracle, as it stands, on the decode queries of the same workload:
+    every host thread this process may use (the 4 queries repeated to fill
+    them), then one thread alone.  The oracle's fp64 HCA caches are built first
+    and not timed, as the GPU's pooled caches are not."""
     import oracle
     n = wl.n_q
     seqs = np.repeat(np.arange(wl.B), np.diff(host["q_off"]))
     scale = 1.0 / math.sqrt(wl.d)
+    threads = host_threads()
 
     def seq_rows(b):
         t0, t1 = int(host["tok_off"][b]), int(host["tok_off"][b + 1])
         return host["kv"][t0:t1], host["z"][t0:t1]
 
     log(f"cpu baseline: building oracle HCA caches for {n} queries")
-    with ThreadPoolExecutor(max_workers=n) as ex:
+    with ThreadPoolExecutor(max_workers=min(threads, n)) as ex:
         hp = list(ex.map(lambda r: oracle.pool(*seq_rows(seqs[r]), wl.m_hca), range(n)))
 
     def one(r):
@@ -823,20 +949,29 @@ def cpu_baseline(wl, host, log, min_seconds: float = 12.0):
                          host["w"][r], host["kc"][p0:p1], host["ks"][p0:p1])
         oracle.hca_query(kv, z, host["q"][r], t, wl.m_hca, wl.W_hca, scale, hpooled=hp[r])
 
-    log(f"cpu baseline: timing the oracle on {n} queries with {n} threads, repeated for at least {min_seconds} s")
+    tasks = [i % n for i in range(max(threads, n))]
+    log(f"cpu baseline: the oracle on {len(tasks)} query tasks with {threads} threads, at least {min_seconds} s")
     t = time.time()
-    passes = 0
-    with ThreadPoolExecutor(max_workers=n) as ex:
-        while passes == 0 or time.time() - t < min_seconds:
-            list(ex.map(one, range(n)))
-            passes += 1
+    done = 0
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        while done == 0 or time.time() - t < min_seconds:
+            list(ex.map(one, tasks))
+            done += len(tasks)
     dt = time.time() - t
-    log(f"cpu baseline: {passes} passes in {dt:.2f} s")
-    return {"value": round(passes * n / dt, 4), "unit": "queries/s", "cores": n, "kind": "oracle",
-            "sample": f"{passes} passes over all {n} decode queries of {wl.name} (CSA: exact MXFP4 scores of every "
-                      f"visible pooled entry, full-sort top-{wl.k}, fp64 pooling of the selected blocks, attention; "
-                      f"HCA: attention over the oracle's prebuilt fp64 cache), one thread per query",
-            "seconds": round(dt, 3), "host_cpus": os.cpu_count()}
+    t = time.time()
+    single = 0
+    while single == 0 or time.time() - t < single_seconds:
+        one(single % n)
+        single += 1
+    dt1 = time.time() - t
+    log(f"cpu baseline: {done} queries in {dt:.2f} s on {threads} threads; {single} in {dt1:.2f} s on one")
+    return {"value": round(done / dt, 4), "unit": "queries/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} decode queries of {wl.name} ({n} distinct, repeated to fill {threads} threads; CSA: "
+                      f"exact MXFP4 scores of every visible pooled entry, full-sort top-{wl.k}, fp64 pooling of the "
+                      f"selected blocks, attention; HCA: attention over the oracle's prebuilt fp64 cache)",
+            "seconds": round(dt, 3), "single_thread": {"value": round(single / dt1, 4), "queries": single,
+                                                        "seconds": round(dt1, 3)},
+            "cpu_model": cpu_model(), "host_cpus": os.cpu_count()}
 
 
 if __name__ == "__main__":

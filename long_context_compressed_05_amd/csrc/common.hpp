@@ -36,18 +36,16 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 
 // Head weight folded into a query block's E8M0 scale: w = 2^e multiplies
 // every product of the block, so the block's scale byte becomes qscale + e.
-// `u` holds the block's 32 e2m1 codes.  A block whose codes are all zero (or
-// -0), or a zero weight, adds nothing to the dot whatever its scale: its codes
-// are zeroed and the scale is set to 2^0, so no out-of-range byte (0xFF is
-// E8M0's NaN) can reach the MFMA.  Otherwise the byte is clamped to the
-// finite range [0, 254]; a fold that leaves it is outside the exactness
-// precondition of the indexer (scales within a few octaves of each other).
+// `u` holds the block's 32 e2m1 codes.  The byte is clamped to E8M0's finite
+// range [0, 254], so no 0xFF (NaN) reaches the MFMA: a block whose codes are
+// all zero then still adds exactly 0, and a fold of a block with a non-zero
+// code that leaves the range is outside the indexer's exactness precondition
+// (scales within a few octaves of each other).  A zero weight zeroes the
+// codes (its head adds nothing).  The scale depends on the scale byte and the
+// weight only, not on the codes, so it never waits for the code load.
 __device__ __forceinline__ int fold_head_weight(uint4& u, int qscale, float w) {
   const int wexp = (int)((__float_as_uint(w) >> 23) & 255u);
-  if (wexp == 0 || ((u.x | u.y | u.z | u.w) & 0x77777777u) == 0u) {
-    u = make_uint4(0u, 0u, 0u, 0u);
-    return 127;
-  }
+  if (wexp == 0) u = make_uint4(0u, 0u, 0u, 0u);
   const int e = qscale + wexp - 127;
   return e < 0 ? 0 : (e > 254 ? 254 : e);
 }

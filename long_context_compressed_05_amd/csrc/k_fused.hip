@@ -38,6 +38,7 @@
 // waits are bounded anyway, and hitting the bound sets the error word (read
 // and cleared by csa_hca_decode_check) and skips the workgroup's remaining work.
 #include <atomic>
+#include <cstdlib>
 
 #include "attn_core.hpp"
 #include "common.hpp"
@@ -92,7 +93,7 @@ typedef unsigned int v4u_t __attribute__((ext_vector_type(4)));
 constexpr uint32_t kNoKey = 0xffffffffu;  // empty list position (scores are finite and >= 0)
 
 // scratch word indices (0..19 are used by the block scans and searches)
-enum { S_TAG = 40, S_FLAG, S_DIGIT, S_ABOVE, S_CNT, S_BAD, S_TICKET, S_KEY, S_CUT, S_OFF, S_END };
+enum { S_TAG = 40, S_FLAG, S_DIGIT, S_ABOVE, S_CNT, S_BAD, S_TICKET, S_KEY, S_CUT, S_OFF, S_STEAL, S_END };
 
 struct FusedArgs {
   const int64_t* tok_off;
@@ -131,6 +132,8 @@ struct FusedArgs {
   int cs, n_cs_sel, n_cs_win;  // window split size; CSA groups and window splits per row
   int cg;                      // score chunks per CSA group
   int rounds;                  // work units taken per workgroup (rounds * grid >= all units)
+  int first_units;             // first-round score chunks assigned by workgroup id (min(score chunks, grid))
+  int steal_polls;             // list polls after which a group computes a missing score chunk itself
   int hs, n_hs;                // HCA split size, splits per row
   int lst_min, lst;            // per chunk: listed entries, at least lst_min (when it has them), at most lst (4 | lst)
   int64_t key_stride;          // keys row stride (multiple of 4)
@@ -883,7 +886,8 @@ __device__ __forceinline__ bool row_fallback(const FCtx& x, int r, const FRow& f
 // row's, ties included.  Otherwise the row's first group runs the exact
 // selection over the stored keys (row_fallback) and every group takes its
 // entries from the stored keys.  Result: the group's selected indices in
-// ascending order -> LDS, their count (or -1 on a failed wait), and their
+// ascending order -> LDS, their count (or -1 on a failed wait, or -2 with the
+// number of a score chunk of the row to compute first in *off_out), and their
 // output offset in the row's idx -> *off_out; the entries sit at
 // sel_s[*base_out ..] (the exact path stores them at their output rank).
 // (*phys_out: with paged caches, whether the selected rows' physical rows are
@@ -932,12 +936,17 @@ __device__ __forceinline__ int group_select(const FCtx& x, int r, int g, const F
     uint64_t tw0 = tid < nsc ? coh_ld64(x.coh, trow + tid) : tagged(x.tag, 0u);
     uint64_t tw1 = tid + 256 < nsc ? coh_ld64(x.coh, trow + tid + 256) : tagged(x.tag, 0u);
     // entries not written yet are all read again together (one bounded retry loop)
+    bool steal = false;
     for (uint32_t n = 0;;) {
       bool late = (uint32_t)(tw0 >> 32) != x.tag || (uint32_t)(tw1 >> 32) != x.tag;
 #pragma unroll
       for (int u = 0; u < kFEPT; ++u) late |= e[u][0] != x.tag || e[u][2] != x.tag;
       if (!late) break;
-      if (++n >= kSpinLimit || ((n & 1023u) == 0 && error_seen(x))) {
+      if (++n >= (uint32_t)a.steal_polls) {  // far longer than a running chunk takes
+        steal = true;
+        break;
+      }
+      if (n >= kSpinLimit || ((n & 1023u) == 0 && error_seen(x))) {
         if (n >= kSpinLimit) set_error(x, 2u);
         fail = true;
         break;
@@ -949,6 +958,38 @@ __device__ __forceinline__ int group_select(const FCtx& x, int r, int g, const F
       if ((uint32_t)(tw0 >> 32) != x.tag) tw0 = coh_ld64(x.coh, trow + tid);
       if ((uint32_t)(tw1 >> 32) != x.tag) tw1 = coh_ld64(x.coh, trow + tid + 256);
     }
+    // A chunk whose list is still missing after that long may belong to a
+    // first-round workgroup that has not started (another kernel holds its CU):
+    // the group has the lowest such chunk computed by its own workgroup and is
+    // run again.  A score chunk is a pure function of the inputs, so a second
+    // run of it (by a late owner) rewrites identical words.
+    if (tid == 0) {
+      x.scr[S_FLAG] = 0;
+      x.scr[S_STEAL] = 0xffffffffu;
+    }
+    __syncthreads();
+    if (fail || steal) x.scr[S_FLAG] = fail ? 1u : 2u;
+    __syncthreads();
+    const uint32_t wflag = uni(x.scr[S_FLAG]);
+    if (wflag == 1u) return -1;  // a failed wait (every thread returns here)
+    if (wflag == 2u) {
+      if (steal) {
+        uint32_t cmin = 0xffffffffu;
+        if ((uint32_t)(tw0 >> 32) != x.tag) cmin = (uint32_t)tid;
+        if ((uint32_t)(tw1 >> 32) != x.tag && (uint32_t)tid + 256u < cmin) cmin = (uint32_t)tid + 256u;
+#pragma unroll
+        for (int u = 0; u < kFEPT; ++u) {
+          const uint32_t c = (uint32_t)(u * 256 + tid) / lay.L;
+          if ((e[u][0] != x.tag || e[u][2] != x.tag) && c < cmin) cmin = c;
+        }
+        if (cmin != 0xffffffffu) atomicMin(&x.scr[S_STEAL], cmin);
+      }
+      __syncthreads();
+      *off_out = uni(x.scr[S_STEAL]);
+      __syncthreads();
+      return -2;
+    }
+    __syncthreads();
 #pragma unroll
     for (int u = 0; u < kFEPT; ++u) {
       kv[u] = fail ? kNoKey : e[u][1];
@@ -984,7 +1025,7 @@ __device__ __forceinline__ int group_select(const FCtx& x, int r, int g, const F
     }
   }
   if (tid == 0) x.scr[S_BAD] = 0;
-  if (!all_ok(x, fail)) return -1;
+  __syncthreads();
   uint32_t n_ent;
   (void)block_exscan_val((uint32_t)__builtin_popcount(vm), x.scr, &n_ent);
   bool exact = n_ent >= (uint32_t)k_eff;
@@ -1310,21 +1351,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // Work units in dependency order: [score chunks | CSA groups | CSA window
   // splits | HCA splits | HCA merges | CSA merges].  The score chunks stream
   // first on every workgroup; the HCA stream then runs beside the
-  // latency-bound selection chain.  Every unit number comes from one
-  // returning atomic on a ticket counter, taken by a running workgroup (the
-  // first on arrival, each later one a round ahead), so units are handed out
-  // in arrival order and a unit is only ever held by a workgroup that has
-  // started.  A workgroup runs its units in the order it claimed them
-  // (ascending), and a unit only waits for units of lower number.  The
-  // lowest unfinished unit is therefore held by a running workgroup whose
-  // earlier units are all done, so it is being run and never waits: every
-  // wait ends however many of the grid's workgroups are resident at a time
-  // (workgroups that start late simply take later units).  Every workgroup
-  // runs the same number of rounds (rounds * grid >= total), so the loop
-  // bound is uniform; a round whose unit number is past the end does nothing.
-  uint32_t next_ticket = 0;  // lane 0: the unit number of the next round, fetched one round ahead
-  if (lane_tid() == 0) next_ticket = atomicAdd(a.ctl + W_TICKET, 1u);
-  for (int round = 0; round < rounds; ++round) {
+  // latency-bound selection chain.  The first-round score chunks (the first
+  // min(score chunks, grid) units) are taken by workgroup id, so their key
+  // streams start at once; every other unit number comes from one returning
+  // atomic on a ticket counter, taken by a running workgroup one round ahead,
+  // so those units are handed out in arrival order and are only ever held by
+  // workgroups that have started.  A workgroup runs its units in the order it
+  // holds them (ascending), and a unit only waits for units of lower number.
+  // The only units a workgroup can hold before it starts are first-round
+  // score chunks, and nothing waits for them blindly: a CSA group that has
+  // waited far longer than a running chunk takes (steal_polls polls) computes
+  // the missing chunk itself (a chunk is a pure function of the inputs, so
+  // its late owner only rewrites the same words) and runs again.  So the
+  // lowest unfinished unit is either such a chunk, computed by whoever waits
+  // for it, or held by a running workgroup whose earlier units are done and
+  // never waits: every wait ends however many of the grid's workgroups are
+  // resident at a time.  Every workgroup runs the same number of rounds
+  // (rounds * grid >= total), plus two for every chunk it computes for one
+  // of its groups; a round whose unit number is past the end does nothing.
+  const uint32_t first = (uint32_t)a.first_units;
+  const bool by_id = blockIdx.x < first;
+  uint32_t next_ticket = 0;  // lane 0: the unit number of the next ticket, fetched one unit ahead
+  if (!by_id && lane_tid() == 0) next_ticket = first + atomicAdd(a.ctl + W_TICKET, 1u);
+  int tickets = rounds - 1;       // claims still to make after the first unit's
+  int n_rounds = rounds;          // grows by 2 for every chunk a group has this workgroup compute
+  int64_t pend_chunk = -1, pend_group = -1;
+  for (int round = 0; round < n_rounds; ++round) {
     KArgs* ap = (KArgs*)__builtin_amdgcn_kernarg_segment_ptr();
     asm volatile("" : "+s"(ap));
     KArgs& A = *ap;
@@ -1334,13 +1386,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int64_t u_win = u_grp + (int64_t)R * A.n_cs_sel, u_hca = u_win + (int64_t)R * A.n_cs_win;
     const int64_t u_mh = u_hca + (int64_t)R * A.n_hs, u_mc = u_mh + (int64_t)R * nM;
     const int64_t total = u_mc + (int64_t)R * nM;
-    if (lane_tid() == 0) scr[S_TICKET] = next_ticket;
-    __syncthreads();
-    const int64_t it = (int64_t)uni(scr[S_TICKET]);
-    __syncthreads();
-    // claim the next round's unit now: the returning atomic's latency overlaps
-    // this round's work.  A workgroup still runs its units in claim order.
-    if (round + 1 < rounds && lane_tid() == 0) next_ticket = atomicAdd(A.ctl + W_TICKET, 1u);
+    int64_t it;
+    if (pend_chunk >= 0) {  // a chunk a group of this workgroup found missing, then that group again
+      it = pend_chunk;
+      pend_chunk = -1;
+    } else if (pend_group >= 0) {
+      it = pend_group;
+      pend_group = -1;
+    } else {
+      if (round == 0 && by_id) {
+        it = (int64_t)blockIdx.x;
+      } else {
+        if (lane_tid() == 0) scr[S_TICKET] = next_ticket;
+        __syncthreads();
+        it = (int64_t)uni(scr[S_TICKET]);
+        __syncthreads();
+      }
+      // claim the next unit now: the returning atomic's latency overlaps this
+      // unit's work.  A workgroup still runs its units in claim order.
+      if (tickets > 0 && lane_tid() == 0) next_ticket = first + atomicAdd(A.ctl + W_TICKET, 1u);
+      --tickets;
+    }
     if (it >= total) {
       // nothing to do this round
     } else if (it < u_grp) {
@@ -1354,6 +1420,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         if (j0 > j1) j0 = j1;
         phase_score(x, r, c, f, j0, j1);
       }
+      if (pend_group >= 0) {
+        vm_drain();  // the computed chunk's words are out before the group reads them back
+        __syncthreads();
+      }
     } else if (it >= u_mh) {
       const bool hca = it < u_mc;
       const int64_t m = it - (hca ? u_mh : u_mc);
@@ -1365,7 +1435,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       uint32_t off = 0, base = 0;
       bool phys = false;
       const int n_sel = group_select(x, r, g, f, &off, &base, &phys);
-      if (n_sel >= 0) {
+      if (n_sel == -2) {  // run the row's missing chunk `off`, then this group again
+        pend_chunk = (int64_t)off * R + r;
+        pend_group = it;
+        n_rounds += 2;
+      } else if (n_sel >= 0) {
         if (kPaged && !phys) {  // paged caches: the selected rows' physical rows -> LDS
           const int32_t* sel_s = reinterpret_cast<const int32_t*>(smem + kOffSel) + base;
           int32_t* sel_p = reinterpret_cast<int32_t*>(smem + kOffSelP) + base;
@@ -1428,6 +1502,20 @@ static int fused_grid() {
   // waits for the last chunk of every row.
   if (dev < kMaxDevices) g_fused_grid[dev].store(cus, std::memory_order_relaxed);
   return cus;
+}
+
+// Polls of a CSA group's list wait after which it computes a missing score
+// chunk itself: far longer than a running chunk takes (each poll is a
+// device-coherent load), so it only happens when the chunk's workgroup has not
+// started.  CSA_FUSED_STEAL_POLLS (1 .. 2^19) overrides it; a small value
+// makes groups compute chunks that are merely late, which changes no output.
+static int steal_polls() {
+  const char* e = std::getenv("CSA_FUSED_STEAL_POLLS");
+  if (e && *e) {
+    const long v = std::strtol(e, nullptr, 10);
+    if (v >= 1 && v < (long)kSpinLimit) return (int)v;
+  }
+  return 4096;
 }
 
 static int split_count(int64_t len, int64_t size) { return len <= 0 ? 0 : (int)((len + size - 1) / size); }
@@ -1547,6 +1635,9 @@ int launch_fused(int R, const int64_t* tok_off, const int64_t* q_pos, const int6
     const int64_t units = (int64_t)R * pl.n_sc + (int64_t)R * (pl.n_cs_sel + pl.n_cs_win + pl.n_hs) +
                           2 * (int64_t)R * (H / 4);
     a.rounds = (int)((units + pl.grid - 1) / pl.grid);
+    const int64_t chunks = (int64_t)R * pl.n_sc;
+    a.first_units = (int)(chunks < pl.grid ? chunks : pl.grid);
+    a.steal_polls = steal_polls();
   }
   a.ctl = (uint32_t*)take(W_CTL * 4);
   a.keys = (uint32_t*)take((size_t)R * pl.key_stride * 4);

@@ -844,3 +844,30 @@ def test_fused_decode_with_zero_query_blocks_and_folded_weights():
     for r in range(wl.n_q):
         want = P.oracle_topk_row(host, wl, r, seqs[r], wl.k, wl.m)
         assert np.array_equal(idx[r], want), f"top-k of row {r}"
+
+
+@pytest.mark.parametrize("name", ["decode_bf16_long", "decode_bf16_ragged"])
+def test_fused_decode_groups_compute_late_chunks_themselves(name, monkeypatch):
+    """With the steal threshold at one poll, a CSA group that finds any list of
+    its row not yet written computes that score chunk itself (the path that
+    keeps the step going when a first-round workgroup has not started) and a
+    chunk may run twice: the outputs are bit-identical to a normal launch and
+    the top-k equals the oracle's."""
+    csa = _lib()
+    wl = FUSED_CASES[name]()
+    host = synth.make_inputs(wl)
+    from long_context_compressed_05_amd.step import Layer, to_device
+    layer = Layer.from_host(_params(wl), host)
+    layer.build_caches()
+    dq = to_device({k: host[k] for k in ("q", "qc", "qs", "w")})
+    want = [P.torch_to_np(t) for t in layer.decode_fused(dq["q"], dq["qc"], dq["qs"], dq["w"])]
+    layer.check_fused()
+    monkeypatch.setenv("CSA_FUSED_STEAL_POLLS", "1")
+    for _ in range(3):
+        got = [P.torch_to_np(t) for t in layer.decode_fused(dq["q"], dq["qc"], dq["qs"], dq["w"])]
+        layer.check_fused()
+        for what, x, y in zip(("idx", "csa_out", "csa_lse", "hca_out", "hca_lse"), got, want):
+            assert np.array_equal(x, y), f"{what} differs when groups compute late chunks"
+    seqs = P.row_seq(host)
+    for r in range(wl.n_q):
+        assert np.array_equal(got[0][r], P.oracle_topk_row(host, wl, r, seqs[r], wl.k, wl.m)), f"top-k of row {r}"
