@@ -302,7 +302,7 @@ def main():
 
     # ---- measured peaks of this part ---------------------------------------------
     try:
-        result["peaks"] = bench_peaks(torch, db.step_bytes, log)
+        result["peaks"] = bench_peaks(torch, csa, db.step_bytes, log)
         if "roofline" in result and "hbm_read_GB/s" in result["peaks"]:
             mp = result["peaks"]["hbm_read_GB/s"]
             result["roofline"]["measured_peak"] = mp

@@ -93,7 +93,7 @@ typedef unsigned int v4u_t __attribute__((ext_vector_type(4)));
 constexpr uint32_t kNoKey = 0xffffffffu;  // empty list position (scores are finite and >= 0)
 
 // scratch word indices (0..19 are used by the block scans and searches)
-enum { S_TAG = 40, S_FLAG, S_DIGIT, S_ABOVE, S_CNT, S_BAD, S_TICKET, S_KEY, S_CUT, S_OFF, S_STEAL, S_END };
+enum { S_TAG = 40, S_FLAG, S_DIGIT, S_ABOVE, S_CNT, S_BAD, S_TICKET, S_KEY, S_CUT, S_OFF, S_STEAL, S_PENDC, S_PENDG, S_END };
 
 struct FusedArgs {
   const int64_t* tok_off;
@@ -133,6 +133,7 @@ struct FusedArgs {
   int cg;                      // score chunks per CSA group
   int rounds;                  // work units taken per workgroup (rounds * grid >= all units)
   int first_units;             // first-round score chunks assigned by workgroup id (min(score chunks, grid))
+  int hpm;                     // heads per merge unit (4, or 16 beyond 8 rows)
   int steal_polls;             // list polls after which a group computes a missing score chunk itself
   int hs, n_hs;                // HCA split size, splits per row
   int lst_min, lst;            // per chunk: listed entries, at least lst_min (when it has them), at most lst (4 | lst)
@@ -925,7 +926,8 @@ __device__ __forceinline__ int group_select(const FCtx& x, int r, int g, const F
   const uint64_t* trow = a.ltau + (size_t)r * a.n_sc;  // chunk c's word at r * n_sc + c (the plan's n_sc)
   uint32_t kv[kFEPT], ix[kFEPT];
   uint32_t vm = 0;
-  bool fail = false;
+  bool fail = false, steal = false;
+  uint32_t steal_c = 0xffffffffu;  // the lowest chunk this thread found missing (when it gave up waiting)
   {
     v4u_t e[kFEPT];
 #pragma unroll
@@ -936,7 +938,6 @@ __device__ __forceinline__ int group_select(const FCtx& x, int r, int g, const F
     uint64_t tw0 = tid < nsc ? coh_ld64(x.coh, trow + tid) : tagged(x.tag, 0u);
     uint64_t tw1 = tid + 256 < nsc ? coh_ld64(x.coh, trow + tid + 256) : tagged(x.tag, 0u);
     // entries not written yet are all read again together (one bounded retry loop)
-    bool steal = false;
     for (uint32_t n = 0;;) {
       bool late = (uint32_t)(tw0 >> 32) != x.tag || (uint32_t)(tw1 >> 32) != x.tag;
 #pragma unroll
@@ -958,41 +959,18 @@ __device__ __forceinline__ int group_select(const FCtx& x, int r, int g, const F
       if ((uint32_t)(tw0 >> 32) != x.tag) tw0 = coh_ld64(x.coh, trow + tid);
       if ((uint32_t)(tw1 >> 32) != x.tag) tw1 = coh_ld64(x.coh, trow + tid + 256);
     }
-    // A chunk whose list is still missing after that long may belong to a
-    // first-round workgroup that has not started (another kernel holds its CU):
-    // the group has the lowest such chunk computed by its own workgroup and is
-    // run again.  A score chunk is a pure function of the inputs, so a second
-    // run of it (by a late owner) rewrites identical words.
-    if (tid == 0) {
-      x.scr[S_FLAG] = 0;
-      x.scr[S_STEAL] = 0xffffffffu;
-    }
-    __syncthreads();
-    if (fail || steal) x.scr[S_FLAG] = fail ? 1u : 2u;
-    __syncthreads();
-    const uint32_t wflag = uni(x.scr[S_FLAG]);
-    if (wflag == 1u) return -1;  // a failed wait (every thread returns here)
-    if (wflag == 2u) {
-      if (steal) {
-        uint32_t cmin = 0xffffffffu;
-        if ((uint32_t)(tw0 >> 32) != x.tag) cmin = (uint32_t)tid;
-        if ((uint32_t)(tw1 >> 32) != x.tag && (uint32_t)tid + 256u < cmin) cmin = (uint32_t)tid + 256u;
+    if (steal) {
+      if ((uint32_t)(tw0 >> 32) != x.tag) steal_c = (uint32_t)tid;
+      if ((uint32_t)(tw1 >> 32) != x.tag && (uint32_t)tid + 256u < steal_c) steal_c = (uint32_t)tid + 256u;
 #pragma unroll
-        for (int u = 0; u < kFEPT; ++u) {
-          const uint32_t c = (uint32_t)(u * 256 + tid) / lay.L;
-          if ((e[u][0] != x.tag || e[u][2] != x.tag) && c < cmin) cmin = c;
-        }
-        if (cmin != 0xffffffffu) atomicMin(&x.scr[S_STEAL], cmin);
+      for (int u = 0; u < kFEPT; ++u) {
+        const uint32_t c = (uint32_t)(u * 256 + tid) / lay.L;
+        if ((e[u][0] != x.tag || e[u][2] != x.tag) && c < steal_c) steal_c = c;
       }
-      __syncthreads();
-      *off_out = uni(x.scr[S_STEAL]);
-      __syncthreads();
-      return -2;
     }
-    __syncthreads();
 #pragma unroll
     for (int u = 0; u < kFEPT; ++u) {
-      kv[u] = fail ? kNoKey : e[u][1];
+      kv[u] = fail || steal ? kNoKey : e[u][1];
       ix[u] = e[u][3];
       vm |= kv[u] != kNoKey ? (1u << u) : 0u;
     }
@@ -1024,8 +1002,27 @@ __device__ __forceinline__ int group_select(const FCtx& x, int r, int g, const F
       warm3 = row[96];
     }
   }
-  if (tid == 0) x.scr[S_BAD] = 0;
+  // A chunk whose list is still missing after that long may belong to a
+  // first-round workgroup that has not started (another kernel holds its CU):
+  // the group has the lowest such chunk computed by its own workgroup and is
+  // run again.  A score chunk is a pure function of the inputs, so a second
+  // run of it (by a late owner) rewrites identical words.
+  if (tid == 0) {
+    x.scr[S_BAD] = 0;
+    x.scr[S_FLAG] = 0;
+    x.scr[S_STEAL] = 0xffffffffu;
+  }
   __syncthreads();
+  if (fail) x.scr[S_FLAG] = 1u;
+  if (steal) atomicMin(&x.scr[S_STEAL], steal_c);
+  __syncthreads();
+  const uint32_t wfail = uni(x.scr[S_FLAG]), wsteal = uni(x.scr[S_STEAL]);
+  __syncthreads();
+  if (wfail) return -1;
+  if (wsteal != 0xffffffffu) {
+    *off_out = wsteal;
+    return -2;
+  }
   uint32_t n_ent;
   (void)block_exscan_val((uint32_t)__builtin_popcount(vm), x.scr, &n_ent);
   bool exact = n_ent >= (uint32_t)k_eff;
@@ -1284,6 +1281,67 @@ __device__ __forceinline__ void attend_item(const FCtx& x, int r, int kind, int 
 }
 
 // merge of 4 heads (h0 .. h0+3) of one row: thread = (head, 2 dims)
+// HPM (8 or 16) heads of row r from head h0: 256 / HPM threads per head,
+// HPM / 2 output dims per thread
+template <int HPM>
+__device__ __forceinline__ void merge_heads(const FCtx& x, bool hca, int r, int h0) {
+  KArgs& a = *x.a;
+  const int tid = lane_tid();
+  const int n_cs = a.n_cs_sel + a.n_cs_win;
+  const int n = hca ? a.n_hs : n_cs;
+  const float* po = hca ? a.hca_po : a.csa_po;
+  const float* pml = hca ? a.hca_pml : a.csa_pml;
+  uint8_t* out = hca ? a.hca_out : a.csa_out;
+  float* lse = hca ? a.hca_lse : a.csa_lse;
+  // every split's (m, l) of this thread's head and its output values, all
+  // loaded at once (one round of loads per SB splits), merged online
+  constexpr int TPH = 256 / HPM, DPT = 128 / TPH;  // threads per head, dims per thread
+  const int hh = tid / TPH, h = h0 + hh, d = (tid % TPH) * DPT;
+  constexpr int SB = HPM == 8 ? 16 : 8;
+  float M = -INFINITY, L = 0.f, acc[DPT];
+#pragma unroll
+  for (int i = 0; i < DPT; ++i) acc[i] = 0.f;
+  for (int s0 = 0; s0 < n; s0 += SB) {
+    uint64_t mlv[SB];
+    uint32_t ov[SB][DPT];
+#pragma unroll
+    for (int u = 0; u < SB; ++u) {
+      const int s = s0 + u;
+      const size_t pb = ((size_t)r * n + s) * a.H + h;
+      mlv[u] = s < n ? coh_ld64(x.coh, pml + pb * 2) : (uint64_t)__float_as_uint(-INFINITY);
+#pragma unroll
+      for (int i = 0; i < DPT; i += 2) {
+        const uint64_t v = s < n ? coh_ld64(x.coh, po + pb * 128 + d + i) : 0ull;
+        ov[u][i] = (uint32_t)v;
+        ov[u][i + 1] = (uint32_t)(v >> 32);
+      }
+    }
+    float Mc = M;
+#pragma unroll
+    for (int u = 0; u < SB; ++u) Mc = fmaxf(Mc, __uint_as_float((uint32_t)mlv[u]));
+    if (Mc == -INFINITY) continue;
+    const float sc = M == -INFINITY ? 0.f : fast_exp2(M - Mc);
+    L *= sc;
+#pragma unroll
+    for (int i = 0; i < DPT; ++i) acc[i] *= sc;
+#pragma unroll
+    for (int u = 0; u < SB; ++u) {
+      const float ms = __uint_as_float((uint32_t)mlv[u]);
+      const float wgt = ms == -INFINITY ? 0.f : fast_exp2(ms - Mc);
+      L = fmaf(wgt, __uint_as_float((uint32_t)(mlv[u] >> 32)), L);
+#pragma unroll
+      for (int i = 0; i < DPT; ++i) acc[i] = fmaf(wgt, __uint_as_float(ov[u][i]), acc[i]);
+    }
+    M = Mc;
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  uint32_t* o = reinterpret_cast<uint32_t*>(out + (((size_t)r * a.H + h) * 128 + d) * 2);
+#pragma unroll
+  for (int i = 0; i < DPT; i += 2) o[i / 2] = f32_to_bf16(acc[i] * inv) | (f32_to_bf16(acc[i + 1] * inv) << 16);
+  if (lse && d == 0) lse[(size_t)r * a.H + h] = L > 0.f ? (M + __log2f(L)) * kLn2 : -INFINITY;
+}
+
+// merge unit: a.hpm heads of row r from head h0 (4, or 16 for batches of many rows)
 __device__ __forceinline__ void item_merge(const FCtx& x, bool hca, int r, int h0) {
   KArgs& a = *x.a;
   const int tid = lane_tid();
@@ -1293,12 +1351,19 @@ __device__ __forceinline__ void item_merge(const FCtx& x, bool hca, int r, int h
   bool fail = false;
   for (int s = tid; s < n && !fail; s += 256) (void)poll_word(x, hdr + s, &fail, hca ? 8u : 4u);
   if (!all_ok(x, fail)) return;
+  if (a.hpm == 16) {
+    merge_heads<16>(x, hca, r, h0);
+    return;
+  }
+  if (a.hpm == 8) {
+    merge_heads<8>(x, hca, r, h0);
+    return;
+  }
+  // 4 heads: a thread per head and 2 dims, 24 splits per round of loads
   const float* po = hca ? a.hca_po : a.csa_po;
   const float* pml = hca ? a.hca_pml : a.csa_pml;
   uint8_t* out = hca ? a.hca_out : a.csa_out;
   float* lse = hca ? a.hca_lse : a.csa_lse;
-  // every split's (m, l) of this thread's head and its two output values, all
-  // loaded at once (one round of loads per 24 splits), merged online
   const int hh = tid >> 6, h = h0 + hh, d = (tid & 63) * 2;
   constexpr int SB = 24;
   float M = -INFINITY, L = 0.f, acc0 = 0.f, acc1 = 0.f;
@@ -1369,30 +1434,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // resident at a time.  Every workgroup runs the same number of rounds
   // (rounds * grid >= total), plus two for every chunk it computes for one
   // of its groups; a round whose unit number is past the end does nothing.
+  // (Unit numbers fit 32 bits: the plan bounds them far below.)
   const uint32_t first = (uint32_t)a.first_units;
   const bool by_id = blockIdx.x < first;
-  uint32_t next_ticket = 0;  // lane 0: the unit number of the next ticket, fetched one unit ahead
+  // lane 0: the unit number of the next ticket (fetched one unit ahead) and the
+  // claims still to make; a group that has its workgroup compute a missing
+  // chunk leaves the chunk and itself in two LDS words, taken before the next
+  // ticket (no other state is carried from round to round)
+  uint32_t next_ticket = 0;  // lane 0: the unit number of the next round, fetched one round ahead
   if (!by_id && lane_tid() == 0) next_ticket = first + atomicAdd(a.ctl + W_TICKET, 1u);
-  int tickets = rounds - 1;       // claims still to make after the first unit's
-  int n_rounds = rounds;          // grows by 2 for every chunk a group has this workgroup compute
-  int64_t pend_chunk = -1, pend_group = -1;
-  for (int round = 0; round < n_rounds; ++round) {
+  // 1: run the chunk in scr[S_PENDC] (for a group of this workgroup), 2: then
+  // that group (scr[S_PENDG]) again; such rounds claim nothing and do not count
+  int pend = 0;
+  for (int round = 0; round < rounds; ++round) {
     KArgs* ap = (KArgs*)__builtin_amdgcn_kernarg_segment_ptr();
     asm volatile("" : "+s"(ap));
     KArgs& A = *ap;
     const FCtx x{ap, smem, scr, tag, make_coh(A.ctl), kPaged};
-    const int R = A.R, nM = A.H / 4;
+    const int R = A.R, nM = A.H / A.hpm;
     const int64_t u_grp = (int64_t)R * A.n_sc;
     const int64_t u_win = u_grp + (int64_t)R * A.n_cs_sel, u_hca = u_win + (int64_t)R * A.n_cs_win;
     const int64_t u_mh = u_hca + (int64_t)R * A.n_hs, u_mc = u_mh + (int64_t)R * nM;
     const int64_t total = u_mc + (int64_t)R * nM;
     int64_t it;
-    if (pend_chunk >= 0) {  // a chunk a group of this workgroup found missing, then that group again
-      it = pend_chunk;
-      pend_chunk = -1;
-    } else if (pend_group >= 0) {
-      it = pend_group;
-      pend_group = -1;
+    if (pend != 0) {
+      it = (int64_t)uni(scr[pend == 1 ? S_PENDC : S_PENDG]);
     } else {
       if (round == 0 && by_id) {
         it = (int64_t)blockIdx.x;
@@ -1402,10 +1468,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         it = (int64_t)uni(scr[S_TICKET]);
         __syncthreads();
       }
-      // claim the next unit now: the returning atomic's latency overlaps this
-      // unit's work.  A workgroup still runs its units in claim order.
-      if (tickets > 0 && lane_tid() == 0) next_ticket = first + atomicAdd(A.ctl + W_TICKET, 1u);
-      --tickets;
+      // claim the next round's unit now: the returning atomic's latency overlaps
+      // this round's work.  A workgroup still runs its units in claim order.
+      if (round + 1 < rounds && lane_tid() == 0) next_ticket = first + atomicAdd(A.ctl + W_TICKET, 1u);
     }
     if (it >= total) {
       // nothing to do this round
@@ -1420,14 +1485,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         if (j0 > j1) j0 = j1;
         phase_score(x, r, c, f, j0, j1);
       }
-      if (pend_group >= 0) {
-        vm_drain();  // the computed chunk's words are out before the group reads them back
+      if (pend == 1) {  // computed for a group of this workgroup: out before it reads them back
+        vm_drain();
         __syncthreads();
+        pend = 2;
       }
     } else if (it >= u_mh) {
       const bool hca = it < u_mc;
       const int64_t m = it - (hca ? u_mh : u_mc);
-      item_merge(x, hca, (int)(m / nM), (int)(m % nM) * 4);
+      item_merge(x, hca, (int)(m / nM), (int)(m % nM) * A.hpm);
     } else if (it < u_win) {
       const int64_t q = it - u_grp;
       const int r = (int)(q % R), g = (int)(q / R);
@@ -1435,10 +1501,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       uint32_t off = 0, base = 0;
       bool phys = false;
       const int n_sel = group_select(x, r, g, f, &off, &base, &phys);
+      pend = 0;
       if (n_sel == -2) {  // run the row's missing chunk `off`, then this group again
-        pend_chunk = (int64_t)off * R + r;
-        pend_group = it;
-        n_rounds += 2;
+        if (lane_tid() == 0) {
+          scr[S_PENDC] = (uint32_t)((int64_t)off * R + r);
+          scr[S_PENDG] = (uint32_t)it;
+        }
+        __syncthreads();
+        pend = 1;
+        round -= 2;  // two rounds of their own (the chunk, the group again): no claims, not counted
       } else if (n_sel >= 0) {
         if (kPaged && !phys) {  // paged caches: the selected rows' physical rows -> LDS
           const int32_t* sel_s = reinterpret_cast<const int32_t*>(smem + kOffSel) + base;
@@ -1546,6 +1617,14 @@ FusedPlan plan_fused(int64_t R, int64_t max_pool, int64_t max_hpool, int H, int 
   p.cg = (int)((p.n_sc + want - 1) / want);
   if (p.cg < 1) p.cg = 1;
   p.n_cs_sel = (p.n_sc + p.cg - 1) / p.cg;
+  // heads per merge unit: as many as keep a unit's partials near 66 KB (at
+  // most 128 partials of one head), so batches of many short rows need fewer
+  // units (each unit is one claim on the ticket counter, whose returning
+  // atomics are served one at a time) while long rows keep their merges spread
+  {
+    const int nmax = p.n_cs_sel + p.n_cs_win > p.n_hs ? p.n_cs_sel + p.n_cs_win : p.n_hs;
+    p.hpm = nmax * 16 <= 128 && H % 16 == 0 ? 16 : (nmax * 8 <= 128 && H % 8 == 0 ? 8 : 4);
+  }
   // listed per chunk: about twice a chunk's expected share of the top-k plus
   // slack, and room for 16 more (a threshold bin's worth); the stride is a
   // multiple of 4, so lists are read 16 bytes at a time, and the row's listed
@@ -1629,11 +1708,11 @@ int launch_fused(int R, const int64_t* tok_off, const int64_t* q_pos, const int6
   a.kv_raw = (const uint8_t*)kv_raw;
   a.idx = idx; a.csa_out = (uint8_t*)csa_out; a.csa_lse = csa_lse; a.hca_out = (uint8_t*)hca_out; a.hca_lse = hca_lse;
   a.C = pl.C; a.n_sc = pl.n_sc; a.cs = pl.cs; a.n_cs_sel = pl.n_cs_sel; a.n_cs_win = pl.n_cs_win; a.cg = pl.cg;
-  a.hs = pl.hs; a.n_hs = pl.n_hs;
+  a.hs = pl.hs; a.n_hs = pl.n_hs; a.hpm = pl.hpm;
   a.lst_min = pl.lst_min; a.lst = pl.lst; a.key_stride = pl.key_stride;
   {
     const int64_t units = (int64_t)R * pl.n_sc + (int64_t)R * (pl.n_cs_sel + pl.n_cs_win + pl.n_hs) +
-                          2 * (int64_t)R * (H / 4);
+                          2 * (int64_t)R * (H / pl.hpm);
     a.rounds = (int)((units + pl.grid - 1) / pl.grid);
     const int64_t chunks = (int64_t)R * pl.n_sc;
     a.first_units = (int)(chunks < pl.grid ? chunks : pl.grid);

@@ -76,6 +76,7 @@ struct FusedPlan {
   int cg;                       // score chunks per CSA group
   int hs, n_hs;                 // HCA split size, splits per row
   int lst_min, lst;             // per score chunk: entries listed, at least lst_min, at most lst
+  int hpm;                      // heads per merge unit
   int64_t key_stride;
   size_t ws_bytes;
 };
