@@ -412,12 +412,9 @@ int launch_index_topk(int n_seq, int64_t n_q, int64_t max_q_per_seq, const int64
   const size_t bm_bytes = (size_t)((max_pool + 31) / 32) * 4;
   const int use_bitmap = bm_bytes <= (size_t)kBitmapMaxBytes ? 1 : 0;
   FinalArgs fa{q_off, q_pos, pool_off, n_seq, m, k, nrep, use_bitmap, max_pool, counts, hist, def, cand, idx};
-  static bool lds_attr_set = false;  // allow the bitmap beyond the default dynamic LDS limit
-  if (!lds_attr_set) {
-    (void)hipFuncSetAttribute((const void*)k_idx_final, hipFuncAttributeMaxDynamicSharedMemorySize,
-                              kBitmapMaxBytes);
-    lds_attr_set = true;
-  }
+  // allow the bitmap beyond the default dynamic LDS limit (idempotent, per call:
+  // it holds for whichever device is current)
+  (void)hipFuncSetAttribute((const void*)k_idx_final, hipFuncAttributeMaxDynamicSharedMemorySize, kBitmapMaxBytes);
   if (e == hipSuccess)
     e = launch(2, kProfBoth, k_idx_final, dim3((unsigned)n_q), dim3(1024), use_bitmap ? bm_bytes : 0, stream, fa);
   return e == hipSuccess && hipGetLastError() == hipSuccess ? 0 : -1;

@@ -36,6 +36,8 @@
 // product and partial sum is a small dyadic rational, so the fp32 sums are
 // exact and the score bit pattern (ReLU as an integer max, which also maps -0
 // to +0) is an exact sort key.
+#include <atomic>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -48,6 +50,11 @@ constexpr int kPfSampleMax = 2048;  // sample keys per query
 constexpr int kPfCand = 2048;      // candidates per query held in a wave's LDS
 constexpr int kPfBins = 1024;      // wave radix-select bins
 constexpr int kPfWaveHist = kPfBins + 64;  // + one trash word per lane
+// the selection kernel's per-wave histogram: 256 bins (+ trash), so that a
+// wave's LDS (2048 candidates + histogram) stays under 10 KB and every
+// two-wave workgroup of a 4096-query chunk is resident at once (8 per CU)
+constexpr int kSelBins = 256;
+constexpr int kSelWaveHist = kSelBins + 64;
 constexpr int kPfMinQ = 16;        // queries per sequence from which this path is used
 
 struct PfArgs {
@@ -168,9 +175,11 @@ __device__ __forceinline__ uint32_t pf_tile_word(const v8i (&av)[2], const int (
 // are looked at.  No barriers.  *gt = the keys above the result.  With
 // MAXPASS < 4 the result is the lower edge of the last bin found, a value
 // with at least `need` keys at or above it.
-template <int NK, int MAXPASS = 4>
+template <int NK, int MAXPASS = 4, int BINS = kPfBins>
 __device__ __forceinline__ uint32_t wave_kth(const uint32_t (&kv)[NK], uint32_t vm, int nk, uint32_t need,
                                              uint32_t* hist, uint32_t* gt) {
+  static_assert(BINS == 1024 || BINS == 256, "1024 or 256 bins");
+  constexpr int LOGB = BINS == 1024 ? 10 : 8, BPL = BINS / 64;  // bins per lane
   const int lane = lane_tid() & 63;
   uint32_t lo = 0xffffffffu, hi = 0u;
 #pragma unroll
@@ -186,18 +195,18 @@ __device__ __forceinline__ uint32_t wave_kth(const uint32_t (&kv)[NK], uint32_t 
   for (int pass = 0; pass < MAXPASS && lo != hi; ++pass) {
     const uint32_t span = hi - lo;
     const int nbits = 32 - __clz((int)span);
-    const int shift = nbits > 10 ? nbits - 10 : 0;
+    const int shift = nbits > LOGB ? nbits - LOGB : 0;
 #pragma unroll
     for (int i = 0; i < NK; ++i) {
       if (i >= nk) break;
       const bool in = ((vm >> i) & 1u) && kv[i] >= lo && kv[i] <= hi;
-      atomicAdd(in ? hist + ((kv[i] - lo) >> shift) : hist + kPfBins + lane, 1u);
+      atomicAdd(in ? hist + ((kv[i] - lo) >> shift) : hist + BINS + lane, 1u);
     }
-    // lane l owns bins [1024 - 16 (l + 1), 1024 - 16 l): lane 0 the top ones
-    const int base = kPfBins - 16 * (lane + 1);
-    uint32_t c[16], tot = 0;
+    // lane l owns bins [BINS - BPL (l + 1), BINS - BPL l): lane 0 the top ones
+    const int base = BINS - BPL * (lane + 1);
+    uint32_t c[BPL], tot = 0;
 #pragma unroll
-    for (int b = 0; b < 16; ++b) {
+    for (int b = 0; b < BPL; ++b) {
       c[b] = hist[base + b];
       hist[base + b] = 0u;
       tot += c[b];
@@ -206,7 +215,7 @@ __device__ __forceinline__ uint32_t wave_kth(const uint32_t (&kv)[NK], uint32_t 
     uint32_t cum = excl, asel = 0, cb = 0;
     int bsel = -1;
 #pragma unroll
-    for (int b = 15; b >= 0; --b) {
+    for (int b = BPL - 1; b >= 0; --b) {
       if (bsel < 0) {
         if (cum + c[b] >= need || b == 0) {
           bsel = b;
@@ -404,7 +413,7 @@ __device__ void pf_select_all(const PfArgs& a, int64_t row, int64_t pbase, int64
       pf_load_b(a, pbase + j, j < nvis, kb, kc, ks);
       const uint32_t key = pf_key(pf_mfma(av, asc, kc, ks), 0);
       const bool in = lane < 32 && j < nvis && (key & pmask) == prefix;
-      atomicAdd(in ? hist + ((key >> shift) & 255u) : hist + kPfBins + lane, 1u);
+      atomicAdd(in ? hist + ((key >> shift) & 255u) : hist + kSelBins + lane, 1u);
     }
     // 256 bins: lane l owns bins [252 - 4 l, 256 - 4 l)
     const int base = 252 - 4 * lane;
@@ -461,9 +470,9 @@ __global__ __launch_bounds__(128) void k_pf_select(PfArgs a) {
   extern __shared__ __align__(16) uint32_t pf_sm[];
   const int tid = threadIdx.x, lane = tid & 63, kb = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
-  uint32_t* cand_j = pf_sm + (size_t)wave * (kPfCand + kPfWaveHist);
+  uint32_t* cand_j = pf_sm + (size_t)wave * (kPfCand + kSelWaveHist);
   uint32_t* hist = cand_j + kPfCand;
-  for (int i = lane; i < kPfWaveHist; i += 64) hist[i] = 0u;
+  for (int i = lane; i < kSelWaveHist; i += 64) hist[i] = 0u;
   const int64_t row = (int64_t)blockIdx.x * 2 + wave;
   if (row >= a.n_q) return;  // wave-level work only: no block barriers below
   const int b = seq_of_row(a.q_off, a.n_seq, row);
@@ -550,7 +559,7 @@ __global__ __launch_bounds__(128) void k_pf_select(PfArgs a) {
     }
   }
   uint32_t gt;
-  const uint32_t kstar = wave_kth<NK>(kv, vm, nk, k_eff, hist, &gt);
+  const uint32_t kstar = wave_kth<NK, 4, kSelBins>(kv, vm, nk, k_eff, hist, &gt);
   const uint32_t r_eq = k_eff - gt;
   // candidates are in ascending index order: a selected one goes to the count of
   // selected ones before it
@@ -579,17 +588,21 @@ int prefill_path(int64_t max_q_per_seq) { return max_q_per_seq >= kPfMinQ ? 1 : 
 // keys per scoring workgroup: the grid (key blocks x query blocks) is sized to
 // a whole number of rounds of resident workgroups, so no last round runs the
 // chip partly empty
+static std::atomic<int> g_pf_capacity[64];  // resident scoring workgroups per device (0 = not known yet)
+
 static int pf_keys_per_wg(int64_t max_pool, int64_t qblocks) {
-  static int capacity = 0;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+  int capacity = dev < 64 ? g_pf_capacity[dev].load(std::memory_order_relaxed) : 0;
   if (capacity == 0) {
-    int dev = 0, cus = 0, per_cu = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
         hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)k_pf_score, 256, 0) == hipSuccess &&
         cus > 0 && per_cu > 0)
       capacity = cus * per_cu;
     else
       capacity = 1024;
+    if (dev < 64) g_pf_capacity[dev].store(capacity, std::memory_order_relaxed);
   }
   const int64_t quads = (max_pool + 127) / 128;  // 128-key units
   if (quads <= 0 || qblocks <= 0) return kPfKeysWG;
@@ -643,14 +656,12 @@ int launch_prefill_topk(int n_seq, int64_t n_q, int64_t max_q_per_seq, const int
   a.bitmap = (uint32_t*)(p + (((size_t)n_q * 4 + 255) & ~(size_t)255));
   a.idx = idx;
   const size_t lds1 = ((size_t)kPfRowsT * a.ns_max + 4 * kPfWaveHist) * 4;
-  const size_t lds3 = (size_t)2 * (kPfCand + kPfWaveHist) * 4;
-  static bool attr = false;
-  if (!attr) {
-    (void)hipFuncSetAttribute((const void*)k_pf_thresh, hipFuncAttributeMaxDynamicSharedMemorySize,
-                              (int)(((size_t)kPfRowsT * kPfSampleMax + 4 * kPfWaveHist) * 4));
-    (void)hipFuncSetAttribute((const void*)k_pf_select, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds3);
-    attr = true;
-  }
+  const size_t lds3 = (size_t)2 * (kPfCand + kSelWaveHist) * 4;
+  static_assert((size_t)2 * (kPfCand + kSelWaveHist) * 4 * 8 <= 160 * 1024, "8 selection workgroups per CU");
+  // the threshold kernel's LDS can exceed the default dynamic limit (idempotent,
+  // so concurrent first calls need no ordering)
+  (void)hipFuncSetAttribute((const void*)k_pf_thresh, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)(((size_t)kPfRowsT * kPfSampleMax + 4 * kPfWaveHist) * 4));
   const unsigned nblk = (unsigned)(n_seq * a.bps);
   hipError_t e = launch(7, kProfBoth, k_pf_thresh, dim3((unsigned)(n_seq * a.bps_t)), dim3(256), lds1, stream, a);
   a.kw = pf_keys_per_wg(max_pool, (int64_t)nblk);
