@@ -437,10 +437,12 @@ def counted_traffic(kernel: str, workload: str):
 def bench_cache_append(torch, csa, layer, wl, host, log, reps: int = 50):
     """csa_cache_append at the end of the resident 1M-token caches: (a) one
     decode step, one new token for each of the 4 sequences, each completing a
-    CSA and an HCA block; (b) a 4096-token chunk on one sequence.  The appended
-    rows are the caches' own last rows, so every call rewrites identical data;
-    lengths and tail rings are reset between calls, outside the timed region
-    (HIP events around the call's two kernels, on their stream)."""
+    CSA and an HCA block (one launch); (b) a 4096-token chunk on one sequence
+    (two launches).  Each completed CSA block's 64-element indexer vector is
+    encoded into the MXFP4 key cache in the same call.  The appended rows are
+    the caches' own last rows, so every call rewrites identical data; lengths
+    and tail rings are reset between calls, outside the timed region (events
+    attached to the call's kernels)."""
     dev = "cuda"
     B, L = wl.B, np.array(wl.lengths, dtype=np.int64)
     tok_off = host["tok_off"]
@@ -462,8 +464,13 @@ def bench_cache_append(torch, csa, layer, wl, host, log, reps: int = 50):
         tail0 = layer.z[torch.from_numpy(tail_rows.reshape(-1)).to(dev)].reshape(B, ring, 2, wl.d).contiguous()
         len0 = torch.from_numpy(L0).to(dev)
         length, z_tail = len0.clone(), tail0.clone()
+        nblk = (L // wl.m) - (L0 // wl.m)
+        kvec = torch.randn((max(1, int(nblk.sum())), 64), device=dev).to(layer.kv.dtype)
+        kvec_off = torch.from_numpy(np.concatenate([[0], np.cumsum(nblk)]).astype(np.int64)).to(dev)
+        kc_scr = torch.zeros((int(host["pool_off"][-1]), 32), dtype=torch.uint8, device=dev)
+        ks_scr = torch.zeros((int(host["pool_off"][-1]), 2), dtype=torch.uint8, device=dev)
         args = (x_new, z_new, new_off, int(n.max()), layer.tok_off, length, layer.kv, z_tail, layer.pool_off, wl.m,
-                layer.pooled, layer.hpool_off, wl.m_hca, layer.hpooled)
+                layer.pooled, layer.hpool_off, wl.m_hca, layer.hpooled, kvec_off, kvec, kc_scr, ks_scr)
         csa.csa_cache_append(*args)
         torch.cuda.synchronize()
         ev = [(csa.HipEvent(), csa.HipEvent()) for _ in range(reps)]
@@ -476,9 +483,11 @@ def bench_cache_append(torch, csa, layer, wl, host, log, reps: int = 50):
         torch.cuda.synchronize()
         us = float(np.mean([a.elapsed_ms(b) for a, b in ev])) * 1e3
         blocks = int(((L // wl.m) - (L0 // wl.m)).sum() + ((L // wl.m_hca) - (L0 // wl.m_hca)).sum())
-        # new rows in (values and logits), raw rows out, ring rows out, pooled rows out
-        nbytes = int(n.sum()) * 3 * row + int(np.minimum(n, ring).sum()) * row + blocks * row
-        out[name] = {"tokens": int(n.sum()), "blocks_pooled": blocks, "us": round(us, 2),
+        # new rows in (values and logits), raw rows out, ring rows out, pooled rows out, key vectors in, keys out
+        nbytes = (int(n.sum()) * 3 * row + int(np.minimum(n, ring).sum()) * row + blocks * row
+                  + int(nblk.sum()) * (64 * es + 34))
+        out[name] = {"tokens": int(n.sum()), "blocks_pooled": blocks, "keys_encoded": int(nblk.sum()),
+                     "launches": 1 if int(n.max()) <= 64 else 2, "us": round(us, 2),
                      "bytes": nbytes, "GB/s": round(nbytes / (us * 1e-6) / 1e9, 1)}
     log(f"cache append: {out}")
     return out

@@ -121,20 +121,30 @@ int csa_compress(int dtype, int32_t n_seq, const int64_t* tok_off, const int64_t
  *   - the tail state z_tail [n_seq][ring][width] keeps the pooling logits of
  *     the latest `ring` tokens (token p at slot p % ring): it must hold them
  *     for the tokens cached so far before the call, and does after it;
+ *   - the indexer key of each CSA block j the append completes (c0 <= j <
+ *     c0 + nc, c0 = floor(L/m), nc = floor((L+n)/m) - c0) is the caller's
+ *     vector kvec row kvec_off[b] + (j - c0) (kdim elements in `dtype`; the
+ *     pages give no source for it, so it is an input), encoded in MXFP4 as
+ *     csa_mxfp4_quantize does into k_codes / k_scales row pool_off[b] + j
+ *     (at most kvec_off[b+1] - kvec_off[b] blocks); kvec = NULL: no keys;
  *   - len[b] += n.
  * x_new, z_new [sum n][width] (values; pooling logits) in `dtype`; kv_raw
- * [capacity][width]; pooled / hpooled [rows][width].  Writes past a
- * sequence's raw or pooled capacity are skipped.  Launches two kernels on
- * `stream`; calls on one set of caches must be ordered (one stream).  The
- * indexer keys of new CSA rows are not produced here (given as inputs).
+ * [capacity][width]; pooled / hpooled [rows][width]; kvec [sum nc][kdim],
+ * kvec_off [B+1] device; k_codes [sum P][kdim/2], k_scales [sum P][kdim/32].
+ * Writes past a sequence's raw or pooled capacity are skipped.  An append of
+ * at most 64 tokens per sequence is one launch (a workgroup per sequence);
+ * a longer one takes two.  Calls on one set of caches must be ordered (one
+ * stream).
  * Errors: CSA_ERR_INVALID for null pointers, width not a positive multiple of
- * 8, m < 1, m_hca < 0, ring < max(m, m_hca), max_new < 0, unaligned rows;
- * CSA_ERR_UNSUPPORTED for other dtypes.
+ * 8, m < 1, m_hca < 0, ring < max(m, m_hca), max_new < 0, unaligned rows,
+ * kvec without kvec_off / k_codes / k_scales, kdim not a positive multiple
+ * of 32; CSA_ERR_UNSUPPORTED for other dtypes.
  * ---------------------------------------------------------------------- */
 int csa_cache_append(int dtype, int32_t n_seq, int width, const int64_t* tok_off, int64_t* len,
                      const int64_t* new_off, int64_t max_new, const void* x_new, const void* z_new, void* kv_raw,
                      void* z_tail, int ring, const int64_t* pool_off, int m, void* pooled,
-                     const int64_t* hpool_off, int m_hca, void* hpooled, void* stream);
+                     const int64_t* hpool_off, int m_hca, void* hpooled, const int64_t* kvec_off, const void* kvec,
+                     int kdim, uint8_t* k_codes, uint8_t* k_scales, void* stream);
 
 /* ------------------------------------------------------------------------
  * csa_mxfp4_quantize — MXFP4 encoding of indexer vectors (the input format of

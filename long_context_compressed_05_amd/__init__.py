@@ -57,7 +57,8 @@ def lib():
     L.csa_last_error.argtypes = []
     L.csa_compress.argtypes = [ci, i32, vp, vp, i64, ci, ci, vp, vp, vp, vp]
     L.csa_mxfp4_quantize.argtypes = [ci, i64, ci, vp, vp, vp, vp]
-    L.csa_cache_append.argtypes = [ci, i32, ci, vp, vp, vp, i64, vp, vp, vp, vp, ci, vp, ci, vp, vp, ci, vp, vp]
+    L.csa_cache_append.argtypes = [ci, i32, ci, vp, vp, vp, i64, vp, vp, vp, vp, ci, vp, ci, vp, vp, ci, vp, vp, vp,
+                                   ci, vp, vp, vp]
     L.csa_index_topk_workspace.argtypes = [bp, i64, ci, ctypes.POINTER(sz)]
     L.csa_index_topk.argtypes = [bp, vp, i64, ci, ci, ci, ci, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.csa_sparse_attn_workspace.argtypes = [ci, bp, ci, ci, ci, ci, ctypes.POINTER(sz)]
@@ -178,17 +179,22 @@ def csa_cache_append(x_new: torch.Tensor, z_new: torch.Tensor, new_off: torch.Te
                      tok_off: torch.Tensor, length: torch.Tensor, kv_raw: torch.Tensor, z_tail: torch.Tensor,
                      pool_off: torch.Tensor, m: int, pooled: torch.Tensor,
                      hpool_off: Optional[torch.Tensor] = None, m_hca: int = 0,
-                     hpooled: Optional[torch.Tensor] = None, stream=None) -> None:
+                     hpooled: Optional[torch.Tensor] = None, kvec_off: Optional[torch.Tensor] = None,
+                     kvec: Optional[torch.Tensor] = None, k_codes: Optional[torch.Tensor] = None,
+                     k_scales: Optional[torch.Tensor] = None, stream=None) -> None:
     """Append each sequence's new rows (x_new, z_new [sum n][...], new_off [B+1]) to
     the raw cache, pool the blocks they complete into `pooled` (and `hpooled`),
-    keep the latest tokens' logits in `z_tail` [B][ring][...] and advance
-    `length` [B] (int64, device) in place."""
+    encode the completed CSA blocks' indexer vectors (kvec [sum blocks][kdim],
+    kvec_off [B+1]) into the MXFP4 key cache (k_codes, k_scales), keep the
+    latest tokens' logits in `z_tail` [B][ring][...] and advance `length` [B]
+    (int64, device) in place."""
     width = kv_raw[0].numel()
     ring = z_tail.shape[1]
+    kdim = kvec.shape[-1] if kvec is not None else 0
     _check(lib().csa_cache_append(_dtype_code(kv_raw), new_off.numel() - 1, width, _ptr(tok_off), _ptr(length),
                                   _ptr(new_off), max_new, _ptr(x_new), _ptr(z_new), _ptr(kv_raw), _ptr(z_tail),
                                   ring, _ptr(pool_off), m, _ptr(pooled), _ptr(hpool_off), m_hca, _ptr(hpooled),
-                                  _stream(stream)),
+                                  _ptr(kvec_off), _ptr(kvec), kdim, _ptr(k_codes), _ptr(k_scales), _stream(stream)),
            "csa_cache_append")
 
 

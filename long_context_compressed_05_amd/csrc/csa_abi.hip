@@ -284,7 +284,8 @@ int csa_compress(int dtype, int32_t n_seq, const int64_t* tok_off, const int64_t
 int csa_cache_append(int dtype, int32_t n_seq, int width, const int64_t* tok_off, int64_t* len,
                      const int64_t* new_off, int64_t max_new, const void* x_new, const void* z_new, void* kv_raw,
                      void* z_tail, int ring, const int64_t* pool_off, int m, void* pooled,
-                     const int64_t* hpool_off, int m_hca, void* hpooled, void* stream) {
+                     const int64_t* hpool_off, int m_hca, void* hpooled, const int64_t* kvec_off, const void* kvec,
+                     int kdim, uint8_t* k_codes, uint8_t* k_scales, void* stream) {
   if (dtype != CSA_F32 && dtype != CSA_BF16) return fail(CSA_ERR_UNSUPPORTED, "dtype %d", dtype);
   if (n_seq < 1) return fail(CSA_ERR_INVALID, "n_seq must be >= 1");
   if (width < 1 || width % 8 != 0) return fail(CSA_ERR_INVALID, "width must be a positive multiple of 8");
@@ -299,12 +300,17 @@ int csa_cache_append(int dtype, int32_t n_seq, int width, const int64_t* tok_off
   if (!aligned16(x_new) || !aligned16(z_new) || !aligned16(kv_raw) || !aligned16(z_tail) || !aligned16(pooled) ||
       (m_hca > 0 && !aligned16(hpooled)))
     return fail(CSA_ERR_INVALID, "row buffers must be 16-byte aligned");
+  if (kvec) {
+    if (!kvec_off || !k_codes || !k_scales) return fail(CSA_ERR_INVALID, "kvec needs kvec_off, k_codes and k_scales");
+    if (kdim < 32 || kdim % 32 != 0) return fail(CSA_ERR_INVALID, "kdim must be a positive multiple of 32 (got %d)", kdim);
+    if (!aligned16(kvec) || !aligned16(k_codes)) return fail(CSA_ERR_INVALID, "kvec and k_codes must be 16-byte aligned");
+  }
   if (max_new == 0) return CSA_OK;
   int rc = check_device();
   if (rc) return rc;
   return launched(csa::launch_append(dtype == CSA_BF16, n_seq, width, tok_off, len, new_off, max_new, x_new, z_new,
-                                     kv_raw, z_tail, ring, pool_off, m, pooled, hpool_off, m_hca, hpooled,
-                                     (hipStream_t)stream));
+                                     kv_raw, z_tail, ring, pool_off, m, pooled, hpool_off, m_hca, hpooled, kvec_off,
+                                     kvec, kvec ? kdim : 0, k_codes, k_scales, (hipStream_t)stream));
 }
 
 int csa_mxfp4_quantize(int dtype, int64_t rows, int dim, const void* x, uint8_t* codes, uint8_t* scales,

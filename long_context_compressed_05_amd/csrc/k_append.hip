@@ -12,7 +12,15 @@
 // the bulk pooling kernel (pool_core.hpp), so a cache built by appends equals
 // one pooled in bulk bit for bit.
 //
-// Two kernels, in stream order:
+// The indexer key of each CSA block the append completes (an input vector of
+// kdim elements, the block's key given by the caller: reading D9) is encoded
+// in MXFP4 (quant_core.hpp) into the key cache row pool_off[b] + j.
+//
+// A short append (every sequence's new tokens fit the ring beside a block's
+// older tokens: the decode step) is one launch, k_append_one: a workgroup per
+// sequence copies the rows, pools the completed blocks, encodes their keys,
+// and only then (after a barrier) writes the ring and advances the length.
+// A longer one takes two kernels, in stream order:
 //   k_append_pool  copies the new rows into the raw cache and pools the
 //                  completed blocks: a block's older tokens come from the raw
 //                  cache and the logit ring, its new tokens straight from the
@@ -21,11 +29,15 @@
 //                  channels; a long one by a workgroup whose threads pool its
 //                  16-row segments in parallel and then fold them in order
 //                  (the bulk kernel's order, so the bits agree)
-//   k_append_tail  one workgroup per sequence: the newest min(n, ring) tokens'
-//                  logits -> the ring, then the sequence's length advances
+//                  (and its last workgroups encode the completed blocks'
+//                  keys, a thread per 32-element part)
+//   k_append_tail  one workgroup per sequence: the newest min(n, ring)
+//                  tokens' logits -> the ring, then the sequence's length
+//                  advances
 #include "common.hpp"
 #include "kernels.hpp"
 #include "pool_core.hpp"
+#include "quant_core.hpp"
 
 namespace csa {
 
@@ -41,9 +53,15 @@ struct AppendArgs {
   const int64_t* hpool_off;
   uint8_t* pooled;
   uint8_t* hpooled;
+  const int64_t* kvec_off;  // [B+1] rows of kvec per sequence (null: no keys to encode)
+  const uint8_t* kvec;      // [sum completed CSA blocks][kdim], KV dtype
+  uint8_t* k_codes;         // [sum P][kdim / 2]
+  uint8_t* k_scales;        // [sum P][kdim / 32]
+  int kdim;
   int width, ring, m, m_hca;
   int64_t narrow_items;  // per sequence, at most: rows to copy + blocks of at most kPoolSeg rows
   int nb_narrow;         // workgroups of the narrow items; each later workgroup pools one long block
+  int nb_wide;           // workgroups of long blocks; the workgroups after them encode keys (a thread per part)
   int wide_par;          // long blocks: segments pooled in parallel (1) or in one thread each (0)
 };
 
@@ -146,6 +164,20 @@ __global__ __launch_bounds__(256) void k_append_pool(AppendArgs a) {
             (size_t)g * 16);
     return;
   }
+  if ((int)blockIdx.x >= a.nb_narrow + a.nb_wide) {  // keys: a thread per 32-element part of a completed block
+    if (!a.kvec) return;
+    const int parts = a.kdim / 32;
+    const int64_t t = (int64_t)(blockIdx.x - a.nb_narrow - a.nb_wide) * blockDim.x + threadIdx.x;
+    const int64_t i = t / parts;
+    const int p = (int)(t - i * parts);
+    const int64_t r0 = a.kvec_off[b];
+    const int64_t nk = a.kvec_off[b + 1] - r0 < q.nc ? a.kvec_off[b + 1] - r0 : q.nc;
+    if (i >= nk || q.c0 + i >= a.pool_off[b + 1] - a.pool_off[b]) return;
+    const size_t kr = (size_t)(a.pool_off[b] + q.c0 + i);
+    mxfp4_block<BF16>(a.kvec + ((size_t)(r0 + i) * a.kdim + (size_t)p * 32) * ES,
+                      a.k_codes + kr * (a.kdim / 2) + (size_t)p * 16, a.k_scales + kr * parts + p);
+    return;
+  }
   // one long block per workgroup: [long CSA blocks | long HCA blocks]
   int64_t w = (int64_t)blockIdx.x - a.nb_narrow;
   bool hca;
@@ -188,6 +220,27 @@ __global__ __launch_bounds__(256) void k_append_pool(AppendArgs a) {
   }
 }
 
+// the indexer keys of sequence b's completed CSA blocks (blocks j = c0 .. c0 + nc
+// of the append) -> MXFP4 rows pool_off[b] + j, a thread per 32-element part
+template <bool BF16>
+__device__ __forceinline__ void append_keys(const AppendArgs& a, int b, const AppendSeq& q) {
+  if (!a.kvec) return;
+  constexpr int ES = BF16 ? 2 : 4;
+  const int parts = a.kdim / 32;
+  const int64_t r0 = a.kvec_off[b];
+  const int64_t nk = a.kvec_off[b + 1] - r0 < q.nc ? a.kvec_off[b + 1] - r0 : q.nc;  // vectors given
+  const int64_t pcap = a.pool_off[b + 1] - a.pool_off[b];
+  for (int64_t t = threadIdx.x; t < nk * parts; t += blockDim.x) {
+    const int64_t i = t / parts;
+    const int p = (int)(t - i * parts);
+    const int64_t j = q.c0 + i;
+    if (j >= pcap) continue;
+    const size_t kr = (size_t)(a.pool_off[b] + j);
+    mxfp4_block<BF16>(a.kvec + ((size_t)(r0 + i) * a.kdim + (size_t)p * 32) * ES,
+                      a.k_codes + kr * (a.kdim / 2) + (size_t)p * 16, a.k_scales + kr * parts + p);
+  }
+}
+
 template <bool BF16>
 __global__ __launch_bounds__(256) void k_append_tail(AppendArgs a) {
   constexpr int N = Vec16<BF16>::N;
@@ -210,12 +263,206 @@ __global__ __launch_bounds__(256) void k_append_tail(AppendArgs a) {
   if (threadIdx.x == 0) a.len[b] = L0 + n;
 }
 
+// The whole append of sequence b in one workgroup: rows, completed blocks
+// (short ones a thread per channel group, long ones by parallel segments
+// folded in order, as k_append_pool), their keys; then, after every read of
+// the ring and of len[b] is done, the ring and the length.
+template <bool BF16>
+__global__ __launch_bounds__(256) void k_append_one(AppendArgs a) {
+  constexpr int N = Vec16<BF16>::N;
+  constexpr int ES = BF16 ? 2 : 4;
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int groups = a.width / N;
+  const size_t row = (size_t)a.width * ES;
+  const AppendSeq q = append_seq(a, b);
+  for (int64_t t = tid; t < q.n * groups; t += blockDim.x) {
+    const int64_t i = t / groups;
+    const int g = (int)(t - i * groups);
+    if (q.L0 + i < q.cap)
+      *reinterpret_cast<uint4*>(a.kv_raw + (size_t)(q.r0 + q.L0 + i) * row + (size_t)g * 16) =
+          *reinterpret_cast<const uint4*>(a.x_new + (size_t)(a.new_off[b] + i) * row + (size_t)g * 16);
+  }
+  extern __shared__ __align__(16) uint8_t ap_sm[];
+  PoolState<BF16>* part = reinterpret_cast<PoolState<BF16>*>(ap_sm);
+  for (int kind = 0; kind < 2; ++kind) {
+    const bool hca = kind == 1;
+    const int m = hca ? a.m_hca : a.m;
+    if (m == 0) continue;
+    const int64_t j0 = hca ? q.h0 : q.c0, nb = hca ? q.nh : q.nc;
+    const int64_t pcap = hca ? a.hpool_off[b + 1] - a.hpool_off[b] : a.pool_off[b + 1] - a.pool_off[b];
+    uint8_t* dst = hca ? a.hpooled + (size_t)a.hpool_off[b] * row : a.pooled + (size_t)a.pool_off[b] * row;
+    if (m <= kPoolSeg) {
+      for (int64_t t = tid; t < nb * groups; t += blockDim.x) {
+        const int64_t j = j0 + t / groups;
+        const int g = (int)(t % groups);
+        if (j >= pcap || (j + 1) * m > q.cap) continue;
+        const BlockRows<BF16> br = block_rows<BF16>(a, b, q, j, m, g);
+        pool_block<BF16>(m, [&](int i) { return br.x(i); }, [&](int i) { return br.z(i); },
+                         dst + (size_t)j * row + (size_t)g * 16);
+      }
+      continue;
+    }
+    const int segs = (m + kPoolSeg - 1) / kPoolSeg;
+    for (int64_t j = j0; j < j0 + nb; ++j) {  // uniform
+      if (j >= pcap || (j + 1) * m > q.cap) continue;
+      for (int t = tid; t < segs * groups; t += blockDim.x) {
+        const int sg = t / groups, g = t - sg * groups;
+        const BlockRows<BF16> br = block_rows<BF16>(a, b, q, j, m, g);
+        const int i0 = sg * kPoolSeg, i1 = i0 + kPoolSeg < m ? i0 + kPoolSeg : m;
+        pool_segment<BF16>(i0, i1, [&](int i) { return br.x(i); }, [&](int i) { return br.z(i); }, part[t]);
+      }
+      __syncthreads();
+      for (int g = tid; g < groups; g += blockDim.x) {
+        PoolState<BF16> st = part[g];
+        for (int sg = 1; sg < segs; ++sg) pool_fold<BF16>(st, part[sg * groups + g]);
+        pool_store<BF16>(st, dst + (size_t)j * row + (size_t)g * 16);
+      }
+      __syncthreads();
+    }
+  }
+  append_keys<BF16>(a, b, q);
+  __syncthreads();  // every read of the ring and of len[b] is done
+  const int64_t first = q.n > a.ring ? q.n - a.ring : 0;
+  for (int64_t t = tid; t < (q.n - first) * groups; t += blockDim.x) {
+    const int64_t i = first + t / groups;
+    const int g = (int)(t % groups);
+    const int64_t p = q.L0 + i;
+    *reinterpret_cast<uint4*>(a.z_tail + ((size_t)b * a.ring + (size_t)(p % a.ring)) * row + (size_t)g * 16) =
+        *reinterpret_cast<const uint4*>(a.z_new + (size_t)(a.new_off[b] + i) * row + (size_t)g * 16);
+  }
+  if (tid == 0) a.len[b] = q.L0 + q.n;
+}
+
+// A decode-sized append (kernel k_append_step): every thread issues all of its
+// loads first, so the sequence's append costs one round of memory latency after
+// its length is read: thread t pools segment t / groups of the sequence's one
+// long (HCA) block for channel group t % groups, one short (CSA) block's
+// channel group, one part of a completed block's key, and one new row's
+// channel group (copy to the raw cache and, after the barrier that ends every
+// read of the ring, to the ring).  The host takes this path when all of that
+// fits one task of each kind per thread (at most one long block, m <= 8).
+template <bool BF16>
+__global__ __launch_bounds__(256) void k_append_step(AppendArgs a) {
+  constexpr int N = Vec16<BF16>::N;
+  constexpr int ES = BF16 ? 2 : 4;
+  constexpr int kMaxM = 8;  // short blocks (CSA) of at most 8 rows on this path
+  const int b = blockIdx.x, t = threadIdx.x;
+  const int groups = a.width / N;
+  const size_t row = (size_t)a.width * ES;
+  const AppendSeq q = append_seq(a, b);
+  const uint8_t* xnew = a.x_new + (size_t)a.new_off[b] * row;
+  const uint8_t* znew = a.z_new + (size_t)a.new_off[b] * row;
+  const uint8_t* xold = a.kv_raw + (size_t)q.r0 * row;
+  const uint8_t* zring = a.z_tail + (size_t)b * a.ring * row;
+  // ---- issue every load
+  // (1) the long block's segment: rows [i0, i0 + ns) of block h0 (values, logits)
+  const int segs = a.m_hca > 0 ? (a.m_hca + kPoolSeg - 1) / kPoolSeg : 0;
+  const int64_t hcap = a.m_hca > 0 ? a.hpool_off[b + 1] - a.hpool_off[b] : 0;
+  const bool h_do = q.nh > 0 && t < segs * groups && q.h0 < hcap && (q.h0 + 1) * a.m_hca <= q.cap;
+  const int hs = h_do ? t / groups : 0, hg = h_do ? t - hs * groups : 0;
+  const int i0 = hs * kPoolSeg;
+  const int ns = h_do ? (a.m_hca - i0 < kPoolSeg ? a.m_hca - i0 : kPoolSeg) : 0;
+  uint4 hx[kPoolSeg], hz[kPoolSeg];
+  {
+    const int64_t p0 = q.h0 * a.m_hca + i0;
+    int64_t slot = p0 % a.ring;
+#pragma unroll
+    for (int i = 0; i < kPoolSeg; ++i) {
+      const int64_t p = p0 + i;
+      if (i < ns) {
+        const bool old = p < q.L0;
+        hx[i] = *reinterpret_cast<const uint4*>((old ? xold + (size_t)p * row : xnew + (size_t)(p - q.L0) * row) +
+                                                (size_t)hg * 16);
+        hz[i] = *reinterpret_cast<const uint4*>((old ? zring + (size_t)slot * row : znew + (size_t)(p - q.L0) * row) +
+                                                (size_t)hg * 16);
+      }
+      slot = slot + 1 == a.ring ? 0 : slot + 1;
+    }
+  }
+  // (2) one short block's channel group: block c0 + t / groups
+  const int64_t cj = q.c0 + t / groups;
+  const int cg = t % groups;
+  const int64_t ccap = a.pool_off[b + 1] - a.pool_off[b];
+  const bool c_do = t / groups < q.nc && cj < ccap && (cj + 1) * a.m <= q.cap;
+  uint4 cx[kMaxM], cz[kMaxM];
+  if (c_do) {
+    const int64_t p0 = cj * a.m;
+    int64_t slot = p0 % a.ring;
+#pragma unroll
+    for (int i = 0; i < kMaxM; ++i) {
+      const int64_t p = p0 + i;
+      if (i < a.m) {
+        const bool old = p < q.L0;
+        cx[i] = *reinterpret_cast<const uint4*>((old ? xold + (size_t)p * row : xnew + (size_t)(p - q.L0) * row) +
+                                                (size_t)cg * 16);
+        cz[i] = *reinterpret_cast<const uint4*>((old ? zring + (size_t)slot * row : znew + (size_t)(p - q.L0) * row) +
+                                                (size_t)cg * 16);
+      }
+      slot = slot + 1 == a.ring ? 0 : slot + 1;
+    }
+  }
+  // (3) one 32-element part of a completed block's key vector
+  const int parts = a.kvec ? a.kdim / 32 : 0;
+  const int64_t kvr = a.kvec ? a.kvec_off[b] : 0;
+  const int64_t nk = a.kvec ? (a.kvec_off[b + 1] - kvr < q.nc ? a.kvec_off[b + 1] - kvr : q.nc) : 0;
+  const int64_t ki = parts > 0 ? t / parts : 0;
+  const int kp = parts > 0 ? t % parts : 0;
+  const bool k_do = parts > 0 && ki < nk && q.c0 + ki < ccap;
+  // (4) one new row's channel group
+  const int64_t ri = t / groups;
+  const int rg = t % groups;
+  const bool r_do = ri < q.n;
+  uint4 rx = make_uint4(0u, 0u, 0u, 0u), rz = make_uint4(0u, 0u, 0u, 0u);
+  if (r_do) {
+    rx = *reinterpret_cast<const uint4*>(xnew + (size_t)ri * row + (size_t)rg * 16);
+    rz = *reinterpret_cast<const uint4*>(znew + (size_t)ri * row + (size_t)rg * 16);
+  }
+  // ---- compute and store
+  extern __shared__ __align__(16) uint8_t ap_sm[];
+  PoolState<BF16>* part = reinterpret_cast<PoolState<BF16>*>(ap_sm);
+  if (h_do) pool_segment_loaded<BF16>(ns, hz, hx, part[t]);
+  if (c_do) {
+    PoolState<BF16> st;
+    pool_reset<BF16>(st);
+    float zz[8][N], xx[8][N];
+#pragma unroll
+    for (int i = 0; i < kMaxM; ++i) {
+      Vec16<BF16>::load(&cz[i], zz[i]);
+      Vec16<BF16>::load(&cx[i], xx[i]);
+    }
+    pool_chunk<BF16>(st, zz, xx, a.m);
+    pool_store<BF16>(st, a.pooled + (size_t)(a.pool_off[b] + cj) * row + (size_t)cg * 16);
+  }
+  if (k_do) {
+    const size_t kr = (size_t)(a.pool_off[b] + q.c0 + ki);
+    mxfp4_block<BF16>(a.kvec + ((size_t)(kvr + ki) * a.kdim + (size_t)kp * 32) * ES,
+                      a.k_codes + kr * (a.kdim / 2) + (size_t)kp * 16, a.k_scales + kr * parts + kp);
+  }
+  if (r_do && q.L0 + ri < q.cap)
+    *reinterpret_cast<uint4*>(a.kv_raw + (size_t)(q.r0 + q.L0 + ri) * row + (size_t)rg * 16) = rx;
+  __syncthreads();  // every segment state is in LDS; every read of the ring and of len[b] is done
+  if (q.nh > 0 && q.h0 < hcap && (q.h0 + 1) * a.m_hca <= q.cap) {
+    for (int g = t; g < groups; g += blockDim.x) {
+      PoolState<BF16> st = part[g];
+      for (int sg = 1; sg < segs; ++sg) pool_fold<BF16>(st, part[sg * groups + g]);
+      pool_store<BF16>(st, a.hpooled + (size_t)(a.hpool_off[b] + q.h0) * row + (size_t)g * 16);
+    }
+  }
+  if (r_do) {
+    const int64_t p = q.L0 + ri;
+    *reinterpret_cast<uint4*>(a.z_tail + ((size_t)b * a.ring + (size_t)(p % a.ring)) * row + (size_t)rg * 16) = rz;
+  }
+  if (t == 0) a.len[b] = q.L0 + q.n;
+}
+
 int launch_append(bool bf16, int n_seq, int width, const int64_t* tok_off, int64_t* len, const int64_t* new_off,
                   int64_t max_new, const void* x_new, const void* z_new, void* kv_raw, void* z_tail, int ring,
                   const int64_t* pool_off, int m, void* pooled, const int64_t* hpool_off, int m_hca, void* hpooled,
+                  const int64_t* kvec_off, const void* kvec, int kdim, uint8_t* k_codes, uint8_t* k_scales,
                   hipStream_t stream) {
   if (n_seq == 0) return 0;
   AppendArgs a{};
+  a.kvec_off = kvec_off; a.kvec = (const uint8_t*)kvec; a.kdim = kdim; a.k_codes = k_codes; a.k_scales = k_scales;
   a.tok_off = tok_off; a.len = len; a.new_off = new_off;
   a.x_new = (const uint8_t*)x_new; a.z_new = (const uint8_t*)z_new;
   a.kv_raw = (uint8_t*)kv_raw; a.z_tail = (uint8_t*)z_tail;
@@ -234,7 +481,31 @@ int launch_append(bool bf16, int n_seq, int width, const int64_t* tok_off, int64
   const size_t lds = (size_t)((max_m + kPoolSeg - 1) / kPoolSeg) * groups * state;
   a.wide_par = wide > 0 && lds <= 64 * 1024 ? 1 : 0;
   const size_t lds_launch = a.wide_par ? lds : 0;
-  dim3 g1((unsigned)(a.nb_narrow + wide), (unsigned)n_seq);
+  // a short append (at most kOneMax new tokens per sequence, long blocks' segment
+  // states in 64 KB): one launch, a workgroup per sequence
+  constexpr int64_t kOneMax = 64;
+  {
+    // one task of each kind per thread: new rows and short blocks' channel
+    // groups, the long block's segments, the keys' parts
+    const int64_t nc_max = max_new / m + 1;
+    const int segs = m_hca > 0 ? (m_hca + kPoolSeg - 1) / kPoolSeg : 0;
+    const bool fits = m <= 8 && m_hca > kPoolSeg && max_new <= m_hca && max_new * groups <= 256 &&
+                      nc_max * groups <= 256 && (int64_t)segs * groups <= 256 && nc_max * (kdim / 32) <= 256 &&
+                      (size_t)segs * groups * state <= 64 * 1024;
+    if (fits) {
+      const hipError_t e1 = launch(9, kProfBoth, bf16 ? k_append_step<true> : k_append_step<false>,
+                                   dim3((unsigned)n_seq), dim3(256), (size_t)segs * groups * state, stream, a);
+      return e1 == hipSuccess && hipGetLastError() == hipSuccess ? 0 : -1;
+    }
+  }
+  if (max_new <= kOneMax && (wide == 0 || a.wide_par)) {
+    const hipError_t e1 = launch(9, kProfBoth, bf16 ? k_append_one<true> : k_append_one<false>, dim3((unsigned)n_seq),
+                                 dim3(256), wide > 0 ? lds : 0, stream, a);
+    return e1 == hipSuccess && hipGetLastError() == hipSuccess ? 0 : -1;
+  }
+  a.nb_wide = (int)wide;
+  const int64_t nb_keys = kvec ? (nb_c * (kdim / 32) + 255) / 256 : 0;
+  dim3 g1((unsigned)(a.nb_narrow + wide + nb_keys), (unsigned)n_seq);
   hipError_t e = launch(9, kProfStart, bf16 ? k_append_pool<true> : k_append_pool<false>, g1, dim3(256), lds_launch,
                         stream, a);
   if (e == hipSuccess)

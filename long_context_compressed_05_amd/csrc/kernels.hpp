@@ -38,6 +38,7 @@ int launch_compress(bool bf16, int n_seq, const int64_t* tok_off, const int64_t*
 int launch_append(bool bf16, int n_seq, int width, const int64_t* tok_off, int64_t* len, const int64_t* new_off,
                   int64_t max_new, const void* x_new, const void* z_new, void* kv_raw, void* z_tail, int ring,
                   const int64_t* pool_off, int m, void* pooled, const int64_t* hpool_off, int m_hca, void* hpooled,
+                  const int64_t* kvec_off, const void* kvec, int kdim, uint8_t* k_codes, uint8_t* k_scales,
                   hipStream_t stream);
 
 int launch_mxfp4_quant(bool bf16, int64_t rows, int dim, const void* x, uint8_t* codes, uint8_t* scales,

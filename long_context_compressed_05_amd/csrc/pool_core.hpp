@@ -57,13 +57,44 @@ struct PoolState {
 // both give the same bits.
 constexpr int kPoolSeg = 16;
 
+template <bool BF16>
+__device__ __forceinline__ void pool_reset(PoolState<BF16>& st) {
+#pragma unroll
+  for (int c = 0; c < PoolState<BF16>::N; ++c) { st.mx[c] = -INFINITY; st.den[c] = 0.f; st.acc[c] = 0.f; }
+}
+
+// one chunk of n <= 8 rows (logits zz, values xx) into the state: the online
+// softmax step every pooling path uses, so all of them give the same bits
+template <bool BF16>
+__device__ __forceinline__ void pool_chunk(PoolState<BF16>& st, const float (&zz)[8][Vec16<BF16>::N],
+                                           const float (&xx)[8][Vec16<BF16>::N], int n) {
+  constexpr int N = Vec16<BF16>::N;
+#pragma unroll
+  for (int c = 0; c < N; ++c) {
+    float cm = st.mx[c];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (i < n) cm = fmaxf(cm, zz[i][c]);
+    const float alpha = fast_exp2((st.mx[c] - cm) * kLog2e);  // exp2(-inf) = 0 on the first chunk
+    float d = st.den[c] * alpha, a = st.acc[c] * alpha;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (i < n) {
+        const float e = fast_exp2((zz[i][c] - cm) * kLog2e);
+        d += e;
+        a = fmaf(e, xx[i][c], a);
+      }
+    }
+    st.mx[c] = cm; st.den[c] = d; st.acc[c] = a;
+  }
+}
+
 // rows [i0, i1) of the block (1 <= i1 - i0 <= kPoolSeg) -> a fresh state
 template <bool BF16, class XRow, class ZRow>
 __device__ __forceinline__ void pool_segment(int i0, int i1, XRow xrow, ZRow zrow, PoolState<BF16>& st) {
   using V = Vec16<BF16>;
   constexpr int N = V::N;
-#pragma unroll
-  for (int c = 0; c < N; ++c) { st.mx[c] = -INFINITY; st.den[c] = 0.f; st.acc[c] = 0.f; }
+  pool_reset<BF16>(st);
   for (int c0 = i0; c0 < i1; c0 += 8) {
     const int n = (i1 - c0) < 8 ? (i1 - c0) : 8;
     float zz[8][N], xx[8][N];
@@ -74,24 +105,29 @@ __device__ __forceinline__ void pool_segment(int i0, int i1, XRow xrow, ZRow zro
         V::load(xrow(c0 + i), xx[i]);
       }
     }
+    pool_chunk<BF16>(st, zz, xx, n);
+  }
+}
+
+// The same segment from rows already loaded (raw 16-byte words of up to
+// kPoolSeg rows, loaded together by the caller so their latencies overlap).
+template <bool BF16>
+__device__ __forceinline__ void pool_segment_loaded(int n, const uint4 (&zr)[kPoolSeg], const uint4 (&xr)[kPoolSeg],
+                                                    PoolState<BF16>& st) {
+  using V = Vec16<BF16>;
+  constexpr int N = V::N;
+  pool_reset<BF16>(st);
 #pragma unroll
-    for (int c = 0; c < N; ++c) {
-      float cm = st.mx[c];
+  for (int c0 = 0; c0 < kPoolSeg; c0 += 8) {
+    if (c0 >= n) break;
+    const int k = (n - c0) < 8 ? (n - c0) : 8;
+    float zz[8][N], xx[8][N];
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        if (i < n) cm = fmaxf(cm, zz[i][c]);
-      const float alpha = fast_exp2((st.mx[c] - cm) * kLog2e);  // exp2(-inf) = 0 on the first chunk
-      float d = st.den[c] * alpha, a = st.acc[c] * alpha;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        if (i < n) {
-          const float e = fast_exp2((zz[i][c] - cm) * kLog2e);
-          d += e;
-          a = fmaf(e, xx[i][c], a);
-        }
-      }
-      st.mx[c] = cm; st.den[c] = d; st.acc[c] = a;
+    for (int i = 0; i < 8; ++i) {
+      V::load(&zr[c0 + i], zz[i]);
+      V::load(&xr[c0 + i], xx[i]);
     }
+    pool_chunk<BF16>(st, zz, xx, k);
   }
 }
 

@@ -70,13 +70,21 @@ def test_compress_validation():
 def test_cache_append_validation():
     L = csa.lib()
     args = dict(dtype=1, n_seq=2, width=256, tok=FAKE, ln=FAKE, new=FAKE, max_new=8, x=FAKE, z=FAKE, raw=FAKE,
-                tail=FAKE, ring=128, pool=FAKE, m=4, pooled=FAKE, hpool=FAKE, m_hca=128, hpooled=FAKE)
+                tail=FAKE, ring=128, pool=FAKE, m=4, pooled=FAKE, hpool=FAKE, m_hca=128, hpooled=FAKE, koff=None,
+                kvec=None, kdim=0, kc=None, ks=None)
 
     def call(**kw):
         a = {**args, **kw}
         return L.csa_cache_append(a["dtype"], a["n_seq"], a["width"], a["tok"], a["ln"], a["new"], a["max_new"],
                                   a["x"], a["z"], a["raw"], a["tail"], a["ring"], a["pool"], a["m"], a["pooled"],
-                                  a["hpool"], a["m_hca"], a["hpooled"], None)
+                                  a["hpool"], a["m_hca"], a["hpooled"], a["koff"], a["kvec"], a["kdim"], a["kc"],
+                                  a["ks"], None)
+    keys = dict(koff=FAKE, kvec=FAKE, kdim=64, kc=FAKE, ks=FAKE)
+    assert call(**{**keys, "kc": None}) == csa.CSA_ERR_INVALID and "kvec" in L.csa_last_error().decode()
+    assert call(**{**keys, "koff": None}) == csa.CSA_ERR_INVALID
+    assert call(**{**keys, "kdim": 48}) == csa.CSA_ERR_INVALID
+    assert call(**{**keys, "kvec": FAKE + 4}) == csa.CSA_ERR_INVALID  # misaligned
+    assert call(**{**keys, "max_new": 0}) == csa.CSA_OK
     assert call(dtype=3) == csa.CSA_ERR_UNSUPPORTED
     assert call(n_seq=0) == csa.CSA_ERR_INVALID
     assert call(width=100) == csa.CSA_ERR_INVALID

@@ -89,10 +89,14 @@ def test_compress_parity(dtype, m):
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_cache_append_builds_the_bulk_caches(dtype):
     """Caches grown by ragged appends (prefill chunks, single decode tokens,
-    sequences with nothing new) equal the raw rows and the bulk pooling of the
-    whole sequences: raw rows and pooled rows bit for bit (the same pooling
-    arithmetic), pooled rows within one rounding of the oracle's exact pooling,
-    the tail ring holding the latest tokens' logits, and the lengths advanced."""
+    sequences with nothing new; decode-sized steps take the one-launch path
+    that issues all loads first, steps of at most 64 tokens the one-launch
+    workgroup-per-sequence path, longer ones two kernels) equal the raw rows and the bulk
+    pooling of the whole sequences: raw rows and pooled rows bit for bit (the
+    same pooling arithmetic), pooled rows within one rounding of the oracle's
+    exact pooling, the completed blocks' indexer keys bit for bit equal to the
+    oracle's MXFP4 encoding of their vectors, the tail ring holding the latest
+    tokens' logits, and the lengths advanced."""
     csa = _lib()
     m, m_hca, ring = 4, 128, 128
     wl = small_wl("append", [1, 131, 517, 1030, 2050], [1] * 5, dtype=dtype, m=m, m_hca=m_hca, seed=23)
@@ -100,9 +104,14 @@ def test_cache_append_builds_the_bulk_caches(dtype):
     B, L = wl.B, np.array(wl.lengths)
     es = torch.float32 if dtype == "f32" else torch.bfloat16
     rng = np.random.default_rng(5)
-    # the append schedule: chunks per sequence, ragged, with zero-length and single-token steps
+    # the append schedule: two single-token steps for every sequence, then chunks per
+    # sequence, ragged, with zero-length and single-token steps
     steps = []
     done = np.zeros(B, dtype=np.int64)
+    for _ in range(2):
+        n = np.minimum(L - done, 1)
+        steps.append(n)
+        done += n
     while (done < L).any():
         n = np.minimum(L - done, rng.choice([0, 1, 1, 3, 64, 200, 777], size=B))
         if n.sum() == 0:
@@ -113,6 +122,14 @@ def test_cache_append_builds_the_bulk_caches(dtype):
     tok_off = synth.offsets(list(cap))
     pool_off, hpool_off = synth.offsets(list(cap // m)), synth.offsets(list(cap // m_hca))
     dev = "cuda"
+    # the indexer vector of every CSA block of each sequence (64 elements, the KV dtype)
+    kdim = 64
+    kf = [rng.standard_normal((int(l) // m, kdim)).astype(np.float32) for l in L]
+    if dtype == "bf16":
+        kf = [((v.view(np.uint32).astype(np.uint64) + 0x7FFF + ((v.view(np.uint32) >> 16) & 1)) >> 16)
+              .astype(np.uint16) for v in kf]
+    k_codes = torch.zeros((int(pool_off[-1]), kdim // 2), dtype=torch.uint8, device=dev)
+    k_scales = torch.zeros((int(pool_off[-1]), kdim // 32), dtype=torch.uint8, device=dev)
     kv_raw = torch.zeros((int(tok_off[-1]), 2, wl.d), dtype=es, device=dev)
     pooled = torch.zeros((int(pool_off[-1]), 2, wl.d), dtype=es, device=dev)
     hpooled = torch.zeros((int(hpool_off[-1]), 2, wl.d), dtype=es, device=dev)
@@ -123,14 +140,25 @@ def test_cache_append_builds_the_bulk_caches(dtype):
     kv, z = dd["kv"], dd["z"]
     t_tok, t_pool, t_hpool = (torch.from_numpy(a).to(dev) for a in (tok_off, pool_off, hpool_off))
     done[:] = 0
+    saw_step = saw_short = saw_long = False
     for n in steps:
         rows = np.concatenate([np.arange(host["tok_off"][b] + done[b], host["tok_off"][b] + done[b] + n[b])
                                for b in range(B)]).astype(np.int64)
         r = torch.from_numpy(rows).to(dev)
         new_off = torch.from_numpy(synth.offsets(list(n))).to(dev)
+        c0, c1 = done // m, (done + n) // m
+        kv_np = np.concatenate([kf[b][c0[b]:c1[b]] for b in range(B)]) if (c1 > c0).any() else kf[0][:0]
+        kvec = to_device({"k": np.ascontiguousarray(kv_np.reshape(-1, kdim) if kv_np.size else
+                                                    np.zeros((1, kdim), kf[0].dtype))})["k"]
+        kvec_off = torch.from_numpy(synth.offsets(list(c1 - c0))).to(dev)
         csa.csa_cache_append(kv[r].contiguous(), z[r].contiguous(), new_off, int(n.max()), t_tok, length, kv_raw,
-                             z_tail, t_pool, m, pooled, t_hpool, m_hca, hpooled)
+                             z_tail, t_pool, m, pooled, t_hpool, m_hca, hpooled, kvec_off=kvec_off, kvec=kvec,
+                             k_codes=k_codes, k_scales=k_scales)
+        saw_step |= 0 < int(n.max()) <= (8 if dtype == "bf16" else 4)
+        saw_short |= (8 if dtype == "bf16" else 4) < int(n.max()) <= 64
+        saw_long |= int(n.max()) > 64
         done += n
+    assert saw_step and saw_short and saw_long, "the schedule should take every append path"
     torch.cuda.synchronize()
     assert P.torch_to_np(length).tolist() == L.tolist()
     # the bulk path over the whole sequences, for comparison
@@ -158,6 +186,14 @@ def test_cache_append_builds_the_bulk_caches(dtype):
             assert np.all(np.abs(P.as_f64(g) - want) <= bound), f"seq {b} m={mm} vs the oracle"
         for p in range(max(0, L[b] - ring), L[b]):
             np.testing.assert_array_equal(tail_np[b, p % ring], z_np[t0 + p], err_msg=f"tail slot of token {p}")
+        # the completed blocks' keys against the oracle's encoding of their vectors
+        nb = L[b] // m
+        if nb:
+            want_c, want_s = oracle.mxfp4_quantize(kf[b])
+            np.testing.assert_array_equal(P.torch_to_np(k_codes)[pool_off[b]:pool_off[b] + nb], want_c,
+                                          err_msg=f"key codes of sequence {b}")
+            np.testing.assert_array_equal(P.torch_to_np(k_scales)[pool_off[b]:pool_off[b] + nb], want_s,
+                                          err_msg=f"key scales of sequence {b}")
 
 
 def _quant_inputs(dtype, rows, dim, seed):
