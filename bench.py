@@ -626,16 +626,37 @@ def bench_paged(torch, csa, layer, wl, host, sets, log, contiguous_kernel_ms, st
 
 
 def bench_mxfp4_recall(torch, csa, log, n_seq: int = 4, n_keys: int = 262144, k: int = 1024, reps: int = 20):
-    """fp32 indexer queries (4 heads x 64) and keys (64), quantised on the GPU
-    with csa_mxfp4_quantize and selected with csa_index_topk, against the exact
-    top-k of the unquantised scores (fp64 on the host): recall = the share of
-    the exact top-k the FP4 path returns.  Two synthetic data models: i.i.d.
-    normal, and keys of which 2k per query carry a planted component along the
-    query's heads.  Also the quantiser's throughput on the 1M-context key set."""
+    """The MXFP4 indexer against a bf16 one and against exact scores.  fp32
+    indexer queries (4 heads x 64) and keys (64) are quantised on the GPU with
+    csa_mxfp4_quantize and selected with csa_index_topk; the same values
+    rounded to bf16 are selected with csa_index_topk_bf16.  Recall = the share
+    of a reference top-k a path returns: each path against the exact top-k of
+    the unquantised fp64 scores (host), and FP4 against bf16.  Two synthetic
+    data models: i.i.d. normal, and keys of which 2k per query carry a planted
+    component along the query's heads.  Times (median of `reps`, kernel-only
+    from the tracing hook for the scoring kernel, events around the call for
+    the whole selection) give the FP4 path's speed-up.  Also the quantiser's
+    throughput on the key set."""
     dev = "cuda"
     rng = np.random.default_rng(20260424)
     w = np.array([0.5, 1.0, 2.0, 1.0], np.float32)
-    out = {"n_keys": n_keys, "k": k, "queries": n_seq}
+    out = {"n_keys_per_query": n_keys, "k": k, "queries": n_seq}
+
+    def timed(call):
+        ev = [(csa.HipEvent(), csa.HipEvent()) for _ in range(reps)]
+        tot = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        call()
+        for i in range(reps):
+            csa.csa_profile_events(csa.CSA_K_IDX_SCORE, ev[i][0], ev[i][1])
+            tot[i][0].record()
+            call()
+            tot[i][1].record()
+            csa.csa_profile_events(csa.CSA_K_IDX_SCORE)
+        torch.cuda.synchronize()
+        score = float(np.median([a.elapsed_ms(b) for a, b in ev])) * 1e3
+        whole = float(np.median([a.elapsed_time(b) for a, b in tot])) * 1e3
+        return score, whole
+
     for model in ("iid_normal", "planted"):
         q = rng.standard_normal((n_seq, 4, 64)).astype(np.float32)
         kf = rng.standard_normal((n_seq * n_keys, 64)).astype(np.float32)
@@ -650,29 +671,50 @@ def bench_mxfp4_recall(torch, csa, log, n_seq: int = 4, n_keys: int = 262144, k:
             S = (np.maximum(d, 0.0) * w.astype(np.float64)).sum(axis=1)
             exact.append(set(np.argpartition(-S, k - 1)[:k].tolist()))
         qd, kd = torch.from_numpy(q).to(dev), torch.from_numpy(kf).to(dev)
+        qb, kb = qd.to(torch.bfloat16), kd.to(torch.bfloat16)
         wd = torch.from_numpy(np.tile(w, (n_seq, 1))).to(dev)
         qc, qs = csa.csa_mxfp4_quantize(qd)
         kc, ks = csa.csa_mxfp4_quantize(kd)
         pool_off = torch.from_numpy(np.arange(n_seq + 1, dtype=np.int64) * n_keys).to(dev)
         lengths = np.full(n_seq, 4 * n_keys, dtype=np.int64)
         batch = csa.Batch.from_host(np.concatenate([[0], np.cumsum(lengths)]), np.arange(n_seq + 1), lengths - 1)
-        idx = csa.csa_index_topk(batch, pool_off, n_keys, 4, k, qc, qs, wd, kc, ks)
-        got = idx.cpu().numpy()
+        ws = csa.Workspace()
+        idx = torch.empty((n_seq, k), dtype=torch.int32, device=dev)
+        idx_b = torch.empty_like(idx)
+        fp4 = lambda: csa.csa_index_topk(batch, pool_off, n_keys, 4, k, qc, qs, wd, kc, ks, idx=idx, ws=ws)
+        bf16 = lambda: csa.csa_index_topk_bf16(batch, pool_off, n_keys, 4, k, qb, wd, kb, idx=idx_b, ws=ws)
+        fp4()
+        bf16()
+        got, got_b = idx.cpu().numpy(), idx_b.cpu().numpy()
+        sets_b = [set(got_b[b].tolist()) for b in range(n_seq)]
         rec = [len(exact[b] & set(got[b].tolist())) / k for b in range(n_seq)]
-        out[model] = {"recall_mean": round(float(np.mean(rec)), 4), "recall_min": round(float(np.min(rec)), 4)}
-        if model == "iid_normal":  # quantiser throughput on the key set
+        rec_b = [len(exact[b] & sets_b[b]) / k for b in range(n_seq)]
+        rec_fb = [len(sets_b[b] & set(got[b].tolist())) / k for b in range(n_seq)]
+        r = lambda v: {"mean": round(float(np.mean(v)), 4), "min": round(float(np.min(v)), 4)}
+        out[model] = {"fp4_vs_exact": r(rec), "bf16_vs_exact": r(rec_b), "fp4_vs_bf16": r(rec_fb)}
+        if model == "iid_normal":
+            s4, w4 = timed(fp4)
+            s16, w16 = timed(bf16)
+            kb4 = kc.numel() + ks.numel()
+            kb16 = kb.numel() * 2
+            out["time_us"] = {
+                "fp4_score": round(s4, 2), "bf16_score": round(s16, 2),
+                "fp4_call": round(w4, 2), "bf16_call": round(w16, 2),
+                "score_speedup": round(s16 / s4, 2), "call_speedup": round(w16 / w4, 2),
+                "key_bytes": {"fp4": int(kb4), "bf16": int(kb16)},
+                "score_GB/s": {"fp4": round(kb4 / (s4 * 1e-6) / 1e9, 1), "bf16": round(kb16 / (s16 * 1e-6) / 1e9, 1)}}
             ev = [(csa.HipEvent(), csa.HipEvent()) for _ in range(reps)]
-            for i in range(reps):
+            for i in range(reps):  # quantiser throughput on the key set
                 csa.csa_profile_events(csa.CSA_K_QUANT, ev[i][0], ev[i][1])
                 csa.csa_mxfp4_quantize(kd, kc, ks)
                 csa.csa_profile_events(csa.CSA_K_QUANT)
             torch.cuda.synchronize()
-            us = float(np.mean([a.elapsed_ms(b) for a, b in ev])) * 1e3
+            us = float(np.median([a.elapsed_ms(b) for a, b in ev])) * 1e3
             nbytes = kf.nbytes + kc.numel() + ks.numel()
-            out["quantize_keys"] = {"rows": int(kf.shape[0]), "dtype": "f32", "us": round(us, 2),
+            out["quantize_keys"] = {"rows": int(kf.shape[0]), "dtype": "f32", "us_median": round(us, 2),
                                     "bytes": int(nbytes), "GB/s": round(nbytes / (us * 1e-6) / 1e9, 1)}
-        del qd, kd, kc, ks
-    log(f"mxfp4 indexer: {out}")
+        del qd, kd, qb, kb, kc, ks
+    log(f"indexer fp4 vs bf16: {out}")
     return out
 
 

@@ -213,6 +213,27 @@ int csa_index_topk(const csa_batch* b, const int64_t* pool_off, int64_t max_pool
                    void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * csa_index_topk_bf16 — the same indexer with bf16 operands: the
+ * higher-precision indexer the MXFP4 path is measured against.
+ * Pages: pytorch.kr FP4 QAT section (the indexer QK path is FP4, with a
+ * speed-up over a higher-precision selector at high recall).  Score of pooled
+ * entry j for query i: S = sum_h w[i][h] * max(0, sum_c q[i][h][c] * key[j][c])
+ * with bf16 q and keys, fp32 products and accumulation (exact when every
+ * partial sum is representable, e.g. small-integer multiples of one power of
+ * two); same visibility, order (S descending, j ascending), output layout and
+ * workspace rules as csa_index_topk.  Decode batches only (max_q_per_seq < 16).
+ *   q     [n_q][4][64] bf16     w [n_q][4] fp32 (exact powers of two keep
+ *                               the products exact)
+ *   keys  [sum P][64] bf16      idx [n_q][k] int32 (output)
+ *   ws    >= csa_index_topk_workspace() bytes for the same batch, zero-filled
+ *         before first use (left so by every successful call).
+ * Errors: as csa_index_topk; CSA_ERR_UNSUPPORTED also for prefill batches.
+ * ---------------------------------------------------------------------- */
+int csa_index_topk_bf16(const csa_batch* b, const int64_t* pool_off, int64_t max_pool, int m, int n_heads, int dim,
+                        int k, const void* q, const float* w, const void* keys, int32_t* idx, void* ws,
+                        size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * csa_sparse_attn — MQA attention over the selected pooled rows plus the
  * sliding window, with ONE softmax.
  * Pages: pytorch.kr CSA/HCA section (attend to the top-k compressed entries;

@@ -22,7 +22,7 @@ CSA_OK, CSA_ERR_INVALID, CSA_ERR_UNSUPPORTED, CSA_ERR_WORKSPACE, CSA_ERR_DEVICE 
 CSA_F32, CSA_BF16 = 0, 1
 
 EXPORTS = ("csa_status_string", "csa_last_error", "csa_compress", "csa_cache_append", "csa_mxfp4_quantize", "csa_index_topk_workspace",
-           "csa_index_topk", "csa_sparse_attn_workspace", "csa_sparse_attn", "hca_attn_workspace",
+           "csa_index_topk", "csa_index_topk_bf16", "csa_sparse_attn_workspace", "csa_sparse_attn", "hca_attn_workspace",
            "hca_attn", "csa_hca_decode_workspace", "csa_hca_decode", "csa_hca_decode_noalloc", "csa_hca_decode_shared",
            "csa_hca_decode_paged",
            "csa_hca_decode_check",
@@ -61,6 +61,7 @@ def lib():
                                    ci, vp, vp, vp]
     L.csa_index_topk_workspace.argtypes = [bp, i64, ci, ctypes.POINTER(sz)]
     L.csa_index_topk.argtypes = [bp, vp, i64, ci, ci, ci, ci, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.csa_index_topk_bf16.argtypes = [bp, vp, i64, ci, ci, ci, ci, vp, vp, vp, vp, vp, sz, vp]
     L.csa_sparse_attn_workspace.argtypes = [ci, bp, ci, ci, ci, ci, ctypes.POINTER(sz)]
     L.csa_sparse_attn.argtypes = [ci, bp, vp, ci, ci, ctypes.c_float, ci, ci, vp, vp, vp, vp, vp, vp,
                                   vp, sz, vp]
@@ -235,6 +236,22 @@ def csa_index_topk(batch: Batch, pool_off: torch.Tensor, max_pool: int, m: int, 
     _check(lib().csa_index_topk(ctypes.byref(b), _ptr(pool_off), max_pool, m, n_heads, dim, k,
                                 _ptr(q_codes), _ptr(q_scales), _ptr(w), _ptr(k_codes), _ptr(k_scales),
                                 _ptr(idx), _ptr(buf), nbytes, _stream(stream)), "csa_index_topk")
+    return idx
+
+
+def csa_index_topk_bf16(batch: Batch, pool_off: torch.Tensor, max_pool: int, m: int, k: int, q: torch.Tensor,
+                        w: torch.Tensor, keys: torch.Tensor, idx: Optional[torch.Tensor] = None,
+                        ws: Optional[Workspace] = None, stream=None) -> torch.Tensor:
+    """The indexer with bf16 operands: q [n_q][4][64], keys [sum P][64] (bf16), w [n_q][4]."""
+    if idx is None:
+        idx = torch.empty((batch.n_q, k), dtype=torch.int32, device=q.device)
+    ws = ws or Workspace(q.device)
+    nbytes = csa_index_topk_workspace(batch, max_pool, k)
+    buf = ws.get(nbytes)
+    b = batch.c()
+    _check(lib().csa_index_topk_bf16(ctypes.byref(b), _ptr(pool_off), max_pool, m, q.shape[-2], q.shape[-1], k,
+                                     _ptr(q), _ptr(w), _ptr(keys), _ptr(idx), _ptr(buf), nbytes, _stream(stream)),
+           "csa_index_topk_bf16")
     return idx
 
 

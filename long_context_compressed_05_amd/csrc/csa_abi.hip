@@ -361,6 +361,30 @@ int csa_index_topk(const csa_batch* b, const int64_t* pool_off, int64_t max_pool
                                          k_scales, idx, ws, (hipStream_t)stream));
 }
 
+int csa_index_topk_bf16(const csa_batch* b, const int64_t* pool_off, int64_t max_pool, int m, int n_heads, int dim,
+                        int k, const void* q, const float* w, const void* keys, int32_t* idx, void* ws,
+                        size_t ws_bytes, void* stream) {
+  int rc = check_batch(b);
+  if (rc) return rc;
+  if (n_heads != 4 || dim != 64)
+    return fail(CSA_ERR_UNSUPPORTED, "indexer shape %d heads x %d dims (supported: 4 x 64)", n_heads, dim);
+  if (csa::prefill_path(b->max_q_per_seq))
+    return fail(CSA_ERR_UNSUPPORTED, "the bf16 indexer takes decode batches only (max_q_per_seq < 16)");
+  if (m < 1) return fail(CSA_ERR_INVALID, "block size m must be >= 1");
+  if (k < 1 || k > 4096) return fail(CSA_ERR_INVALID, "k must be in [1, 4096] (got %d)", k);
+  if (max_pool < 0 || max_pool > (1LL << 30)) return fail(CSA_ERR_INVALID, "max_pool out of range");
+  if (!pool_off || !q || !w || !keys || !idx) return fail(CSA_ERR_INVALID, "NULL pointer argument");
+  if (!aligned16(q) || !aligned16(keys)) return fail(CSA_ERR_INVALID, "q and keys must be 16-byte aligned");
+  const size_t need = csa::index_ws_bytes(b->n_q, b->max_q_per_seq, max_pool, k);
+  if (!ws || ws_bytes < need)
+    return fail(CSA_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need, ws_bytes);
+  rc = check_device();
+  if (rc) return rc;
+  return launched(csa::launch_index_topk_bf16(b->n_seq, b->n_q, b->max_q_per_seq, b->q_off, b->q_pos, pool_off,
+                                              max_pool, m, k, (const uint16_t*)q, w, (const uint16_t*)keys, idx, ws,
+                                              (hipStream_t)stream));
+}
+
 static int check_attn_shape(int dtype, int H, int d) {
   if (dtype != CSA_F32 && dtype != CSA_BF16) return fail(CSA_ERR_UNSUPPORTED, "dtype %d", dtype);
   if (d != 128) return fail(CSA_ERR_UNSUPPORTED, "head dim %d (supported: 128)", d);

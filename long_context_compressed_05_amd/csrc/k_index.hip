@@ -176,6 +176,111 @@ __global__ __launch_bounds__(256) void k_idx_score(ScoreArgs a) {
   }
 }
 
+// The same scores from bf16 indexer vectors (the higher-precision indexer
+// the FP4 path is compared with; same definition, S = sum_h w_h * max(0,
+// q_h . k), with bf16 operands and fp32 accumulation): v_mfma_f32_32x32x16_bf16,
+// A = up to 8 queries x 4 heads (lane & 31 = slot * 4 + head), B = 32 keys,
+// K = 64 in four steps of 16; the output layout is the FP4 kernel's, so the
+// epilogue, the keys and the histogram are the same and the selection kernels
+// that follow are shared.  The head weights multiply the ReLU'd dots in fp32.
+struct ScoreArgsBf16 {
+  const int64_t* q_off;
+  const int64_t* q_pos;
+  const int64_t* pool_off;
+  int n_seq, tiles_per_seq, qt, m, nrep;
+  int64_t max_pool;
+  const uint16_t* q;  // [n_q][4][64]
+  const float* w;     // [n_q][4]
+  const uint16_t* k;  // [sum P][64]
+  uint32_t* keys;
+  uint32_t* hist;
+};
+
+__global__ __launch_bounds__(256) void k_idx_score_bf16(ScoreArgsBf16 a) {
+  extern __shared__ uint32_t lhist[];  // qt * kNBins/2 words, two 16-bit counters per word
+  __shared__ int64_t nvis_s[8];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tile = blockIdx.y;
+  const int b = tile / a.tiles_per_seq;
+  const int64_t row0 = a.q_off[b] + (int64_t)(tile % a.tiles_per_seq) * a.qt;
+  const int64_t row_end_seq = a.q_off[b + 1];
+  const int nrows = (int)(row0 >= row_end_seq ? 0 : (row_end_seq - row0 < a.qt ? row_end_seq - row0 : a.qt));
+  if (nrows == 0) return;
+  const int64_t pbase = a.pool_off[b];
+  const int64_t P = a.pool_off[b + 1] - pbase;
+  if (tid < 8) nvis_s[tid] = tid < nrows ? n_visible(a.q_pos[row0 + tid], a.m, P) : 0;
+  for (int i = tid; i < a.qt * (kNBins / 2); i += 256) lhist[i] = 0;
+  __syncthreads();
+  int64_t nvis_max = 0;
+  for (int r = 0; r < nrows; ++r) nvis_max = nvis_s[r] > nvis_max ? nvis_s[r] : nvis_max;
+  // A operand, k-step s: row (lane & 31) = slot * 4 + head, dims 16 s + 8 (lane >> 5) .. + 8
+  const int slot_a = (lane & 31) >> 2, head_a = lane & 3, half = lane >> 5;
+  v8bf av[4];
+#pragma unroll
+  for (int st = 0; st < 4; ++st) {
+    av[st] = v8bf{};
+    if (slot_a < nrows)
+      av[st] = *reinterpret_cast<const v8bf*>(a.q + ((row0 + slot_a) * 4 + head_a) * 64 + 16 * st + 8 * half);
+  }
+  // this lane's output rows: slot 2 s + half, head h -> weight
+  float wq[4][4];
+#pragma unroll
+  for (int s2 = 0; s2 < 4; ++s2)
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const int slot = 2 * s2 + half;
+      wq[s2][h] = slot < nrows ? a.w[(row0 + slot) * 4 + h] : 0.f;
+    }
+  const int64_t jc0 = (int64_t)blockIdx.x * kScoreChunk;
+  if (jc0 < nvis_max) {
+#pragma unroll 1
+    for (int it0 = 0; it0 < kScoreIter; it0 += 4) {  // 4 key tiles (16 KB per wave) in flight
+      v8bf kv[4][4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int64_t j = jc0 + (int64_t)(wave * kScoreIter + it0 + u) * 32 + (lane & 31);
+#pragma unroll
+        for (int st = 0; st < 4; ++st)
+          kv[u][st] = j < nvis_max ? *reinterpret_cast<const v8bf*>(a.k + (pbase + j) * 64 + 16 * st + 8 * half)
+                                   : v8bf{};
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int64_t jbase = jc0 + (int64_t)(wave * kScoreIter + it0 + u) * 32;
+        if (jbase >= nvis_max) break;
+        v16f acc = {};
+#pragma unroll
+        for (int st = 0; st < 4; ++st) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[st], kv[u][st], acc, 0, 0, 0);
+        const int64_t j = jbase + (lane & 31);
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2) {
+          const int slot = 2 * s2 + half;
+          if (slot < nrows && j < nvis_s[slot]) {
+            const float r0 = wq[s2][0] * __int_as_float(max(__float_as_int(acc[4 * s2 + 0]), 0));
+            const float r1 = wq[s2][1] * __int_as_float(max(__float_as_int(acc[4 * s2 + 1]), 0));
+            const float r2 = wq[s2][2] * __int_as_float(max(__float_as_int(acc[4 * s2 + 2]), 0));
+            const float r3 = wq[s2][3] * __int_as_float(max(__float_as_int(acc[4 * s2 + 3]), 0));
+            const uint32_t key = __float_as_uint((r0 + r1) + (r2 + r3));
+            a.keys[(row0 + slot) * a.max_pool + j] = key;
+            const uint32_t bin = key >> kBinShift;
+            atomicAdd(&lhist[slot * (kNBins / 2) + (bin >> 1)], 1u << ((bin & 1u) * 16));
+          }
+        }
+      }
+    }
+  }
+  __syncthreads();
+  const int rep = (int)((blockIdx.x + (int64_t)gridDim.x * blockIdx.y) % a.nrep);
+  for (int r = 0; r < nrows; ++r) {
+    uint32_t* gh = a.hist + ((row0 + r) * a.nrep + rep) * kNBins;
+    for (int wi = tid; wi < kNBins / 2; wi += 256) {
+      const uint32_t v = lhist[r * (kNBins / 2) + wi];
+      if (v & 0xffffu) atomicAdd(gh + 2 * wi, v & 0xffffu);
+      if (v >> 16) atomicAdd(gh + 2 * wi + 1, v >> 16);
+    }
+  }
+}
+
 // threshold bin of every query (one workgroup per query); runs after the
 // scoring kernel so its histogram merges are complete and visible
 __global__ __launch_bounds__(256) void k_idx_threshold(const int64_t* q_off, const int64_t* q_pos,
@@ -376,14 +481,12 @@ size_t index_ws_bytes(int64_t n_q, int64_t max_q_per_seq, int64_t max_pool, int 
   return s;
 }
 
-int launch_index_topk(int n_seq, int64_t n_q, int64_t max_q_per_seq, const int64_t* q_off,
-                      const int64_t* q_pos, const int64_t* pool_off, int64_t max_pool, int m,
-                      int k, const uint8_t* q_codes, const uint8_t* q_scales, const float* w,
-                      const uint8_t* k_codes, const uint8_t* k_scales, int32_t* idx, void* ws,
-                      hipStream_t stream) {
-  if (prefill_path(max_q_per_seq))
-    return launch_prefill_topk(n_seq, n_q, max_q_per_seq, q_off, q_pos, pool_off, max_pool, m, k, q_codes, q_scales,
-                               w, k_codes, k_scales, idx, ws, stream);
+// the decode-batch chain: scoring (FP4, or bf16 when q_bf16 is set), threshold,
+// selection, final
+static int decode_topk(int n_seq, int64_t n_q, int64_t max_q_per_seq, const int64_t* q_off, const int64_t* q_pos,
+                       const int64_t* pool_off, int64_t max_pool, int m, int k, const uint8_t* q_codes,
+                       const uint8_t* q_scales, const float* w, const uint8_t* k_codes, const uint8_t* k_scales,
+                       const uint16_t* q_bf16, const uint16_t* k_bf16, int32_t* idx, void* ws, hipStream_t stream) {
   const int nrep = hist_replicas(n_q, max_pool);
   uint8_t* p = (uint8_t*)ws;
   auto take = [&](size_t bytes) { uint8_t* r = p; p += (bytes + 255) & ~(size_t)255; return r; };
@@ -397,11 +500,17 @@ int launch_index_topk(int n_seq, int64_t n_q, int64_t max_q_per_seq, const int64
 
   const int qt = max_q_per_seq > 1 ? 8 : 1;
   const int tiles_per_seq = (int)((max_q_per_seq + qt - 1) / qt);
-  ScoreArgs sa{q_off, q_pos, pool_off, n_seq, tiles_per_seq, qt, m, nrep, max_pool, q_codes,
-               q_scales, w, k_codes, k_scales, keys, hist};
   dim3 g1((unsigned)((max_pool + kScoreChunk - 1) / kScoreChunk), (unsigned)(n_seq * tiles_per_seq));
   if (g1.x == 0) g1.x = 1;
-  hipError_t e = launch(0, kProfBoth, k_idx_score, g1, dim3(256), (size_t)qt * (kNBins / 2) * 4, stream, sa);
+  hipError_t e;
+  if (q_bf16) {
+    ScoreArgsBf16 sb{q_off, q_pos, pool_off, n_seq, tiles_per_seq, qt, m, nrep, max_pool, q_bf16, w, k_bf16, keys, hist};
+    e = launch(0, kProfBoth, k_idx_score_bf16, g1, dim3(256), (size_t)qt * (kNBins / 2) * 4, stream, sb);
+  } else {
+    ScoreArgs sa{q_off, q_pos, pool_off, n_seq, tiles_per_seq, qt, m, nrep, max_pool, q_codes,
+                 q_scales, w, k_codes, k_scales, keys, hist};
+    e = launch(0, kProfBoth, k_idx_score, g1, dim3(256), (size_t)qt * (kNBins / 2) * 4, stream, sa);
+  }
   if (e == hipSuccess)
     e = launch(-1, kProfNone, k_idx_threshold, dim3((unsigned)n_q), dim3(256), 0, stream, q_off, q_pos, pool_off,
                n_seq, m, k, nrep, (const uint32_t*)hist, info);
@@ -418,6 +527,25 @@ int launch_index_topk(int n_seq, int64_t n_q, int64_t max_q_per_seq, const int64
   if (e == hipSuccess)
     e = launch(2, kProfBoth, k_idx_final, dim3((unsigned)n_q), dim3(1024), use_bitmap ? bm_bytes : 0, stream, fa);
   return e == hipSuccess && hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int launch_index_topk(int n_seq, int64_t n_q, int64_t max_q_per_seq, const int64_t* q_off,
+                      const int64_t* q_pos, const int64_t* pool_off, int64_t max_pool, int m,
+                      int k, const uint8_t* q_codes, const uint8_t* q_scales, const float* w,
+                      const uint8_t* k_codes, const uint8_t* k_scales, int32_t* idx, void* ws,
+                      hipStream_t stream) {
+  if (prefill_path(max_q_per_seq))
+    return launch_prefill_topk(n_seq, n_q, max_q_per_seq, q_off, q_pos, pool_off, max_pool, m, k, q_codes, q_scales,
+                               w, k_codes, k_scales, idx, ws, stream);
+  return decode_topk(n_seq, n_q, max_q_per_seq, q_off, q_pos, pool_off, max_pool, m, k, q_codes, q_scales, w, k_codes,
+                     k_scales, nullptr, nullptr, idx, ws, stream);
+}
+
+int launch_index_topk_bf16(int n_seq, int64_t n_q, int64_t max_q_per_seq, const int64_t* q_off, const int64_t* q_pos,
+                           const int64_t* pool_off, int64_t max_pool, int m, int k, const uint16_t* q, const float* w,
+                           const uint16_t* keys, int32_t* idx, void* ws, hipStream_t stream) {
+  return decode_topk(n_seq, n_q, max_q_per_seq, q_off, q_pos, pool_off, max_pool, m, k, nullptr, nullptr, w, nullptr,
+                     nullptr, q, keys, idx, ws, stream);
 }
 
 }  // namespace csa

@@ -58,6 +58,12 @@ int launch_index_topk(int n_seq, int64_t n_q, int64_t max_q_per_seq, const int64
                       const uint8_t* k_codes, const uint8_t* k_scales, int32_t* idx, void* ws,
                       hipStream_t stream);
 
+// decode batches only (max_q_per_seq below the prefill threshold); workspace as
+// launch_index_topk's for such batches
+int launch_index_topk_bf16(int n_seq, int64_t n_q, int64_t max_q_per_seq, const int64_t* q_off, const int64_t* q_pos,
+                           const int64_t* pool_off, int64_t max_pool, int m, int k, const uint16_t* q, const float* w,
+                           const uint16_t* keys, int32_t* idx, void* ws, hipStream_t stream);
+
 struct AttnPlan {
   int splits;
   int ks;

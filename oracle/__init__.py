@@ -46,6 +46,7 @@ def _load():
     lib.orc_mxfp4_quantize.argtypes = [i64, ci, ci, vp, vp, vp]
     lib.orc_index_scores.argtypes = [i64, ci, ci, vp, vp, vp, vp, vp, vp, vp]
     lib.orc_topk.argtypes = [i64, vp, ci, vp]
+    lib.orc_index_scores_bf16.argtypes = [i64, ci, ci, vp, vp, vp, vp]
     lib.orc_attend.argtypes = [ci, ci, cd, vp, i64, vp, vp, vp, vp]
     lib.orc_csa_query.argtypes = [ci, ci, ci, ci, ci, ci, cd, i64, vp, vp, vp, vp,
                                   ci, ci, vp, vp, vp, vp, vp, vp, vp, vp]
@@ -122,6 +123,18 @@ def index_scores(qc, qs, w, kc, ks) -> Tuple[np.ndarray, np.ndarray]:
     _check(_load().orc_index_scores(n, H_I, 2 * half, _p(qc), _p(qs), _p(w), _p(kc), _p(ks), _p(S), _p(ex)),
            "index_scores")
     return S, ex.astype(bool)
+
+
+def index_scores_bf16(q, w, keys) -> np.ndarray:
+    """Scores of keys [n][d_I] (bf16 bit patterns, uint16) for one query
+    q [H_I][d_I] (bf16 bits) with head weights w [H_I]: fp64, exact products."""
+    q = np.ascontiguousarray(q, np.uint16)
+    keys = np.ascontiguousarray(keys, np.uint16)
+    w = np.ascontiguousarray(w, np.float32)
+    H_I, d_I = q.shape
+    S = np.empty(keys.shape[0], dtype=np.float64)
+    _check(_load().orc_index_scores_bf16(keys.shape[0], H_I, d_I, _p(q), _p(w), _p(keys), _p(S)), "index_scores_bf16")
+    return S
 
 
 def topk(S: np.ndarray, k: int) -> np.ndarray:

@@ -259,6 +259,29 @@ int orc_index_scores(int64_t n_keys, int H_I, int d_I, const uint8_t* qc, const 
   return rc;
 }
 
+/* The indexer score with bf16 operands (the higher-precision indexer the
+ * MXFP4 one is compared with; pytorch.kr FP4 QAT section: the FP4 indexer is
+ * set against a higher-precision selector):
+ *   S = sum_h w_h * max(0, sum_c q[h][c] * k[c])
+ * q [H_I][d_I] and keys [n][d_I] as bf16 bit patterns.  Every product of two
+ * bf16 values is exact in fp64 (8 + 8 significand bits); the sum runs in fp64
+ * in index order. */
+int orc_index_scores_bf16(int64_t n_keys, int H_I, int d_I, const uint16_t* q, const float* w,
+                          const uint16_t* keys, double* S) {
+  if (H_I < 1 || d_I < 1 || n_keys < 0) return -1;
+  for (int64_t j = 0; j < n_keys; ++j) {
+    double s = 0.0;
+    for (int h = 0; h < H_I; ++h) {
+      double dot = 0.0;
+      for (int c = 0; c < d_I; ++c)
+        dot += load_elem(1, q, (int64_t)h * d_I + c) * load_elem(1, keys, j * d_I + c);
+      s += (double)w[h] * std::max(0.0, dot);
+    }
+    S[j] = s;
+  }
+  return 0;
+}
+
 int orc_topk(int64_t n, const double* S, int k, int32_t* idx) {
   if (k < 1 || n < 0) return -1;
   topk(n, S, k, idx);

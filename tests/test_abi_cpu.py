@@ -147,6 +147,27 @@ def test_index_topk_validation_and_workspace():
         assert call() == csa.CSA_ERR_DEVICE
 
 
+def test_index_topk_bf16_validation():
+    L = csa.lib()
+    b = _batch()
+
+    def call(b=b, n_heads=4, dim=64, k=64, ws=FAKE, ws_bytes=1 << 40, keys=FAKE, m=4):
+        return L.csa_index_topk_bf16(ctypes.byref(b), FAKE, 1000, m, n_heads, dim, k, FAKE, FAKE, keys, FAKE,
+                                     ws, ws_bytes, None)
+    assert call(n_heads=8) == csa.CSA_ERR_UNSUPPORTED
+    assert call(dim=128) == csa.CSA_ERR_UNSUPPORTED
+    assert call(b=_batch(n_q=16, maxq=16)) == csa.CSA_ERR_UNSUPPORTED  # prefill batches
+    assert call(k=0) == csa.CSA_ERR_INVALID
+    assert call(k=4097) == csa.CSA_ERR_INVALID
+    assert call(m=0) == csa.CSA_ERR_INVALID
+    assert call(keys=None) == csa.CSA_ERR_INVALID
+    assert call(ws_bytes=16) == csa.CSA_ERR_WORKSPACE
+    assert call(ws=None) == csa.CSA_ERR_WORKSPACE
+    import torch
+    if not torch.cuda.is_available():
+        assert call() == csa.CSA_ERR_DEVICE
+
+
 def test_attention_validation():
     L = csa.lib()
     b = _batch()

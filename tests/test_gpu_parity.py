@@ -907,3 +907,45 @@ def test_fused_decode_groups_compute_late_chunks_themselves(name, monkeypatch):
     seqs = P.row_seq(host)
     for r in range(wl.n_q):
         assert np.array_equal(got[0][r], P.oracle_topk_row(host, wl, r, seqs[r], wl.k, wl.m)), f"top-k of row {r}"
+
+
+def _bf16_exact_inputs(rng, lengths, m):
+    """Decode indexer inputs on which fp32 accumulation is exact: bf16 queries
+    in {-4..4}/4, keys in {-3..3}/2, head weights powers of two (every partial
+    sum a multiple of 1/8 below 2^10).  Small ranges give many tied scores."""
+    B = len(lengths)
+    P_b = [L // m for L in lengths]
+    pool_off = synth.offsets(P_b)
+    q = (rng.integers(-4, 5, size=(B, 4, 64)) * 0.25).astype(np.float32)
+    keys = (rng.integers(-3, 4, size=(int(pool_off[-1]), 64)) * 0.5).astype(np.float32)
+    w = np.exp2(rng.integers(-1, 2, size=(B, 4))).astype(np.float32)
+    bits = lambda a: (a.view(np.uint32) >> 16).astype(np.uint16)
+    return P_b, pool_off, bits(q), bits(keys), w
+
+
+@pytest.mark.parametrize("lengths,k", [
+    ([1, 3, 130, 517, 1030, 2049, 4099], 64),    # ragged, k above the visible count, empty sequences
+    ([160001, 200003], 1000),                    # large ranges, heavy ties
+    ([3200003], 2048),                           # visible range beyond the LDS bitmap
+])
+def test_index_topk_bf16_matches_the_oracle(lengths, k):
+    """csa_index_topk_bf16 against the oracle's fp64 bf16 scores and full sort,
+    bit for bit, on inputs where the kernel's fp32 arithmetic is exact."""
+    csa = _lib()
+    m = 4
+    P_b, pool_off, qb, kb, w = _bf16_exact_inputs(np.random.default_rng(41), lengths, m)
+    B = len(lengths)
+    as_bf16 = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    q_pos = np.array(lengths) - 1
+    batch = csa.Batch.from_host(synth.offsets(lengths), np.arange(B + 1), q_pos)
+    ws = csa.Workspace()
+    args = (batch, torch.from_numpy(pool_off).cuda(), max(P_b), m, k, as_bf16(qb),
+            torch.from_numpy(w).cuda(), as_bf16(kb))
+    got = P.torch_to_np(csa.csa_index_topk_bf16(*args, ws=ws))
+    for b in range(B):
+        p0 = int(pool_off[b])
+        n_vis = min((int(q_pos[b]) + 1) // m, P_b[b])
+        S = oracle.index_scores_bf16(qb[b], w[b], kb[p0:p0 + n_vis])
+        np.testing.assert_array_equal(got[b], oracle.topk(S, k), err_msg=f"sequence {b}")
+    again = P.torch_to_np(csa.csa_index_topk_bf16(*args, ws=ws))
+    assert np.array_equal(again, got), "a second call on the same workspace differs"

@@ -324,6 +324,47 @@ def test_index_zero_block_scale_does_not_matter():
         assert ex.all()
 
 
+def _to_bf16_bits(v):
+    """fp64 values exactly representable in bf16 -> bf16 bit patterns (checked)."""
+    f = np.asarray(v, np.float32)
+    assert np.array_equal(f.astype(np.float64), np.asarray(v, np.float64))
+    b = (f.view(np.uint32) >> 16).astype(np.uint16)
+    assert np.array_equal((b.astype(np.uint32) << 16).view(np.float32), f), "not a bf16 value"
+    return b
+
+
+def test_index_bf16_scores_equal_the_mxfp4_scores_of_the_same_values():
+    """Every MXFP4 value (an e2m1 value times 2^e) is a bf16 value: the bf16
+    score of the decoded vectors equals the exact MXFP4 score, for the whole
+    set, ties and zeros included."""
+    for seed, codeset in ((10, synth.E2M1_ALL_CODES), (11, synth.E2M1_TIE_CODES)):
+        qc, qs, w, kc, ks = _random_index(seed, 400, codeset)
+        S, _ = oracle.index_scores(qc, qs, w, kc, ks)
+        qb = _to_bf16_bits(np.stack([decode_vec(qc[h], qs[h]) for h in range(4)]))
+        kb = _to_bf16_bits(np.stack([decode_vec(kc[j], ks[j]) for j in range(kc.shape[0])]))
+        assert np.array_equal(oracle.index_scores_bf16(qb, w, kb), S)
+
+
+def test_index_bf16_relu_identities_and_hand_case():
+    """S(k) - S(-k) = sum_h w_h D_h, S(k) + S(-k) = sum_h w_h |D_h| with D from
+    a numpy matmul; and one worked case: q_0 = e_0, q_1 = -e_1, k = (3, 2, 0..),
+    w = (0.5, 2, 1, 1): S = 0.5 * 3 + 2 * max(0, -2) = 1.5."""
+    rng = np.random.default_rng(12)
+    Q = rng.integers(-5, 6, size=(4, 64)) * 0.25
+    K = rng.integers(-5, 6, size=(300, 64)) * 0.5
+    w = np.array([0.5, 1.0, 2.0, 1.0], np.float32)
+    qb, kb, knb = _to_bf16_bits(Q), _to_bf16_bits(K), _to_bf16_bits(-K)
+    D = K @ Q.T
+    Sp, Sn = oracle.index_scores_bf16(qb, w, kb), oracle.index_scores_bf16(qb, w, knb)
+    assert np.array_equal(Sp - Sn, D @ w.astype(np.float64))
+    assert np.array_equal(Sp + Sn, np.abs(D) @ w.astype(np.float64))
+    q = np.zeros((4, 64))
+    q[0, 0], q[1, 1] = 1.0, -1.0
+    k = np.zeros((1, 64))
+    k[0, 0], k[0, 1] = 3.0, 2.0
+    assert oracle.index_scores_bf16(_to_bf16_bits(q), np.array([0.5, 2, 1, 1], np.float32), _to_bf16_bits(k))[0] == 1.5
+
+
 # ----------------------------------------------------------------------------
 # top-k
 # ----------------------------------------------------------------------------
