@@ -435,26 +435,31 @@ def counted_traffic(kernel: str, workload: str):
 
 
 def bench_cache_append(torch, csa, layer, wl, host, log, reps: int = 50):
-    """csa_cache_append at the end of the resident 1M-token caches: (a) one
-    decode step, one new token for each of the 4 sequences, each completing a
-    CSA and an HCA block (one launch); (b) a 4096-token chunk on one sequence
-    (two launches).  Each completed CSA block's 64-element indexer vector is
-    encoded into the MXFP4 key cache in the same call.  The appended rows are
-    the caches' own last rows, so every call rewrites identical data; lengths
-    and tail rings are reset between calls, outside the timed region (events
-    attached to the call's kernels)."""
+    """csa_cache_append at the end of the resident 1M-token caches.  Decode
+    steps (one new token for each of the 4 sequences, one launch) in the three
+    cases a step meets: the token completes no block, a CSA block (1 step in
+    m), or a CSA and an HCA block (1 step in m'); their mean over a cycle of
+    m' steps is the amortised cost per step.  Then a 4096-token chunk on one
+    sequence (two launches).  Each completed CSA block's 64-element indexer
+    vector is encoded into the MXFP4 key cache in the same call.  The appended
+    rows are the caches' own rows, so every call rewrites identical data;
+    lengths and tail rings are reset between calls, outside the timed region
+    (events attached to the call's kernels; medians)."""
     dev = "cuda"
     B, L = wl.B, np.array(wl.lengths, dtype=np.int64)
     tok_off = host["tok_off"]
     ring = wl.m_hca
     es = 2 if wl.dtype == "bf16" else 4
     row = 2 * wl.d * es
-    cases = {"decode_step": np.ones(B, dtype=np.int64),
-             "prefill_chunk": np.array([4096] + [0] * (B - 1), dtype=np.int64)}
+    # (tokens per sequence, how far before the cache end the append ends)
+    cases = {"decode_none": (np.ones(B, dtype=np.int64), 2), "decode_csa": (np.ones(B, dtype=np.int64), wl.m),
+             "decode_csa_hca": (np.ones(B, dtype=np.int64), 0),
+             "prefill_chunk": (np.array([4096] + [0] * (B - 1), dtype=np.int64), 0)}
     out = {}
-    for name, n in cases.items():
-        L0 = L - n
-        rows = np.concatenate([np.arange(tok_off[b] + L0[b], tok_off[b] + L[b]) for b in range(B)]).astype(np.int64)
+    for name, (n, back) in cases.items():
+        L1 = L - back
+        L0 = L1 - n
+        rows = np.concatenate([np.arange(tok_off[b] + L0[b], tok_off[b] + L1[b]) for b in range(B)]).astype(np.int64)
         r = torch.from_numpy(rows).to(dev)
         x_new, z_new = layer.kv[r].contiguous(), layer.z[r].contiguous()
         new_off = torch.from_numpy(np.concatenate([[0], np.cumsum(n)]).astype(np.int64)).to(dev)
@@ -464,7 +469,8 @@ def bench_cache_append(torch, csa, layer, wl, host, log, reps: int = 50):
         tail0 = layer.z[torch.from_numpy(tail_rows.reshape(-1)).to(dev)].reshape(B, ring, 2, wl.d).contiguous()
         len0 = torch.from_numpy(L0).to(dev)
         length, z_tail = len0.clone(), tail0.clone()
-        nblk = (L // wl.m) - (L0 // wl.m)
+        nblk = (L1 // wl.m) - (L0 // wl.m)
+        hblk = (L1 // wl.m_hca) - (L0 // wl.m_hca)
         kvec = torch.randn((max(1, int(nblk.sum())), 64), device=dev).to(layer.kv.dtype)
         kvec_off = torch.from_numpy(np.concatenate([[0], np.cumsum(nblk)]).astype(np.int64)).to(dev)
         kc_scr = torch.zeros((int(host["pool_off"][-1]), 32), dtype=torch.uint8, device=dev)
@@ -481,14 +487,23 @@ def bench_cache_append(torch, csa, layer, wl, host, log, reps: int = 50):
             csa.csa_cache_append(*args)
             csa.csa_profile_events(csa.CSA_K_APPEND)
         torch.cuda.synchronize()
-        us = float(np.mean([a.elapsed_ms(b) for a, b in ev])) * 1e3
-        blocks = int(((L // wl.m) - (L0 // wl.m)).sum() + ((L // wl.m_hca) - (L0 // wl.m_hca)).sum())
+        t_us = np.array([a.elapsed_ms(b) for a, b in ev]) * 1e3
+        blocks = int(nblk.sum() + hblk.sum())
         # new rows in (values and logits), raw rows out, ring rows out, pooled rows out, key vectors in, keys out
         nbytes = (int(n.sum()) * 3 * row + int(np.minimum(n, ring).sum()) * row + blocks * row
                   + int(nblk.sum()) * (64 * es + 34))
-        out[name] = {"tokens": int(n.sum()), "blocks_pooled": blocks, "keys_encoded": int(nblk.sum()),
-                     "launches": 1 if int(n.max()) <= 64 else 2, "us": round(us, 2),
-                     "bytes": nbytes, "GB/s": round(nbytes / (us * 1e-6) / 1e9, 1)}
+        us = float(np.median(t_us))
+        out[name] = {"tokens": int(n.sum()), "csa_blocks": int(nblk.sum()), "hca_blocks": int(hblk.sum()),
+                     "keys_encoded": int(nblk.sum()), "launches": 1 if int(n.max()) <= 64 else 2,
+                     "us_median": round(us, 2), "us_p10": round(float(np.percentile(t_us, 10)), 2),
+                     "us_p90": round(float(np.percentile(t_us, 90)), 2),
+                     "bytes_written_or_read_new": nbytes}
+    c = wl.m_hca // wl.m  # CSA completions per HCA cycle
+    amort = ((wl.m_hca - c) * out["decode_none"]["us_median"] + (c - 1) * out["decode_csa"]["us_median"]
+             + out["decode_csa_hca"]["us_median"]) / wl.m_hca
+    out["decode_amortised_us_per_step"] = round(amort, 2)
+    out["note"] = ("a decode step's append reads the completed HCA block's 128 rows (values and logits); "
+                   "its floor is one launch (peaks.empty_kernel_us)")
     log(f"cache append: {out}")
     return out
 
@@ -941,6 +956,11 @@ def bench_peaks(torch, csa, step_bytes, log, R: int = 20):
                                                                 stream), peaks.FLOP_BF16_SMALL)
     b16b, gb = mfma_rate(lambda g, it, e0, e1: L.peak_mfma_bf16(g, it, 1, fsink.data_ptr(), e0.handle, e1.handle,
                                                                 stream), peaks.FLOP_BF16_BIG)
+    ev = [(csa.HipEvent(), csa.HipEvent()) for _ in range(21)]
+    for e0, e1 in ev:  # the floor of a launch's measured duration (4 workgroups of 1024 threads)
+        assert L.peak_empty(4, 1024, sink.data_ptr(), e0.handle, e1.handle, stream) == 0
+    torch.cuda.synchronize()
+    out["empty_kernel_us"] = round(float(np.median([a.elapsed_ms(b) * 1e3 for a, b in ev[1:]])), 2)
     out["fp4_mfma_TFLOP/s"] = fp4
     out["bf16_mfma_16x16x32_TFLOP/s"] = b16s
     out["bf16_mfma_32x32x16_TFLOP/s"] = b16b

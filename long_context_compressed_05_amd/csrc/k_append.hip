@@ -16,10 +16,11 @@
 // kdim elements, the block's key given by the caller: reading D9) is encoded
 // in MXFP4 (quant_core.hpp) into the key cache row pool_off[b] + j.
 //
-// A short append (every sequence's new tokens fit the ring beside a block's
-// older tokens: the decode step) is one launch, k_append_one: a workgroup per
-// sequence copies the rows, pools the completed blocks, encodes their keys,
-// and only then (after a barrier) writes the ring and advances the length.
+// A short append is one launch: k_append_step for a decode-sized one (a few
+// tokens per sequence, each task one per thread), else k_append_one (up to 64
+// tokens per sequence): a workgroup per sequence copies the rows, pools the
+// completed blocks, encodes their keys, and only then (after a barrier)
+// writes the ring and advances the length.
 // A longer one takes two kernels, in stream order:
 //   k_append_pool  copies the new rows into the raw cache and pools the
 //                  completed blocks: a block's older tokens come from the raw
@@ -215,7 +216,7 @@ __global__ __launch_bounds__(256) void k_append_pool(AppendArgs a) {
   __syncthreads();
   for (int g = threadIdx.x; g < groups; g += blockDim.x) {
     PoolState<BF16> st = part[g];
-    for (int sg = 1; sg < segs; ++sg) pool_fold<BF16>(st, part[sg * groups + g]);
+    for (int sg = 1; sg < segs; ++sg) pool_fold(st, part[sg * groups + g]);
     pool_store<BF16>(st, out + (size_t)g * 16);
   }
 }
@@ -314,7 +315,7 @@ __global__ __launch_bounds__(256) void k_append_one(AppendArgs a) {
       __syncthreads();
       for (int g = tid; g < groups; g += blockDim.x) {
         PoolState<BF16> st = part[g];
-        for (int sg = 1; sg < segs; ++sg) pool_fold<BF16>(st, part[sg * groups + g]);
+        for (int sg = 1; sg < segs; ++sg) pool_fold(st, part[sg * groups + g]);
         pool_store<BF16>(st, dst + (size_t)j * row + (size_t)g * 16);
       }
       __syncthreads();
@@ -333,124 +334,181 @@ __global__ __launch_bounds__(256) void k_append_one(AppendArgs a) {
   if (tid == 0) a.len[b] = q.L0 + q.n;
 }
 
-// A decode-sized append (kernel k_append_step): every thread issues all of its
-// loads first, so the sequence's append costs one round of memory latency after
-// its length is read: thread t pools segment t / groups of the sequence's one
-// long (HCA) block for channel group t % groups, one short (CSA) block's
-// channel group, one part of a completed block's key, and one new row's
-// channel group (copy to the raw cache and, after the barrier that ends every
-// read of the ring, to the ring).  The host takes this path when all of that
-// fits one task of each kind per thread (at most one long block, m <= 8).
+// A decode-sized append (kernel k_append_step): one workgroup of 1024 threads
+// per sequence.  A wave issues about one vector instruction every few cycles,
+// so the launch is bounded by the longest instruction stream of any wave, not
+// by its few kilobytes of data: every thread pools 4 bytes of channels of one
+// 16-row segment of the sequence's one long (HCA) block (segment t / units),
+// and the other tasks go to distinct waves: 4 bytes of a short (CSA) block
+// (threads from 0), one element of a completed block's key (from 256; the 32
+// lanes of a key part find its scale together), 16 bytes of a new row (from
+// 512; they also write the ring), and the long block's fold, 4 bytes of
+// channels each (from 768).  Every load is issued before any arithmetic.
+// After the barrier that ends every read of the ring and of len[b], the fold
+// threads fold the segment states in order and the row threads write the
+// ring.  The host takes this path when every task fits (at most one long
+// block, m <= 8, at most 256 threads per task kind).
+constexpr int kStepKeys = 256, kStepRows = 512, kStepFold = 768;  // first threads of the task kinds
+
 template <bool BF16>
-__global__ __launch_bounds__(256) void k_append_step(AppendArgs a) {
-  constexpr int N = Vec16<BF16>::N;
+__global__ __launch_bounds__(1024) void k_append_step(AppendArgs a) {
+  constexpr int N = Vec4<BF16>::N;
   constexpr int ES = BF16 ? 2 : 4;
   constexpr int kMaxM = 8;  // short blocks (CSA) of at most 8 rows on this path
   const int b = blockIdx.x, t = threadIdx.x;
-  const int groups = a.width / N;
   const size_t row = (size_t)a.width * ES;
+  const int units = (int)(row / 4), groups = (int)(row / 16);
   const AppendSeq q = append_seq(a, b);
   const uint8_t* xnew = a.x_new + (size_t)a.new_off[b] * row;
   const uint8_t* znew = a.z_new + (size_t)a.new_off[b] * row;
   const uint8_t* xold = a.kv_raw + (size_t)q.r0 * row;
   const uint8_t* zring = a.z_tail + (size_t)b * a.ring * row;
   // ---- issue every load
-  // (1) the long block's segment: rows [i0, i0 + ns) of block h0 (values, logits)
+  // (1) the long block: rows [i0, i0 + ns) of segment t / units, unit t % units
   const int segs = a.m_hca > 0 ? (a.m_hca + kPoolSeg - 1) / kPoolSeg : 0;
   const int64_t hcap = a.m_hca > 0 ? a.hpool_off[b + 1] - a.hpool_off[b] : 0;
-  const bool h_do = q.nh > 0 && t < segs * groups && q.h0 < hcap && (q.h0 + 1) * a.m_hca <= q.cap;
-  const int hs = h_do ? t / groups : 0, hg = h_do ? t - hs * groups : 0;
+  const bool h_blk = q.nh > 0 && q.h0 < hcap && (q.h0 + 1) * a.m_hca <= q.cap;
+  const bool h_do = h_blk && t < segs * units;
+  const int hs = t / units, hu = t - hs * units;
   const int i0 = hs * kPoolSeg;
   const int ns = h_do ? (a.m_hca - i0 < kPoolSeg ? a.m_hca - i0 : kPoolSeg) : 0;
-  uint4 hx[kPoolSeg], hz[kPoolSeg];
-  {
+  uint32_t hx[kPoolSeg], hz[kPoolSeg];
+  // ring slots: a block's first slot (uniform) plus the row's offset in the
+  // block, which is below m_hca <= ring, so one wrap at most
+  const int hslot0 = a.m_hca > 0 ? (int)((q.h0 * a.m_hca) % a.ring) : 0;
+  if (h_do) {
     const int64_t p0 = q.h0 * a.m_hca + i0;
-    int64_t slot = p0 % a.ring;
 #pragma unroll
     for (int i = 0; i < kPoolSeg; ++i) {
-      const int64_t p = p0 + i;
-      if (i < ns) {
-        const bool old = p < q.L0;
-        hx[i] = *reinterpret_cast<const uint4*>((old ? xold + (size_t)p * row : xnew + (size_t)(p - q.L0) * row) +
-                                                (size_t)hg * 16);
-        hz[i] = *reinterpret_cast<const uint4*>((old ? zring + (size_t)slot * row : znew + (size_t)(p - q.L0) * row) +
-                                                (size_t)hg * 16);
-      }
-      slot = slot + 1 == a.ring ? 0 : slot + 1;
+      const int ii = i < ns ? i : ns - 1;  // rows past the segment load its last row (unused)
+      const int64_t p = p0 + ii;
+      const int so = hslot0 + i0 + ii;
+      const int slot = so < a.ring ? so : so - a.ring;
+      const bool old = p < q.L0;
+      hx[i] = *reinterpret_cast<const uint32_t*>((old ? xold + (size_t)p * row : xnew + (size_t)(p - q.L0) * row) +
+                                                 (size_t)hu * 4);
+      hz[i] = *reinterpret_cast<const uint32_t*>((old ? zring + (size_t)slot * row : znew + (size_t)(p - q.L0) * row) +
+                                                 (size_t)hu * 4);
     }
   }
-  // (2) one short block's channel group: block c0 + t / groups
-  const int64_t cj = q.c0 + t / groups;
-  const int cg = t % groups;
+  // (2) one short block's unit: block c0 + t / units (threads from 0)
+  const int64_t cj = q.c0 + t / units;
+  const int cu = t % units;
   const int64_t ccap = a.pool_off[b + 1] - a.pool_off[b];
-  const bool c_do = t / groups < q.nc && cj < ccap && (cj + 1) * a.m <= q.cap;
-  uint4 cx[kMaxM], cz[kMaxM];
+  const bool c_do = t / units < q.nc && cj < ccap && (cj + 1) * a.m <= q.cap;
+  uint32_t cx[kMaxM], cz[kMaxM];
+  // the first short block's first slot (uniform); the blocks this append
+  // completes span fewer than max_new + m <= 2 * ring rows from it
+  const int cslot0 = (int)((q.c0 * a.m) % a.ring);
   if (c_do) {
     const int64_t p0 = cj * a.m;
-    int64_t slot = p0 % a.ring;
+    int cs = cslot0 + (t / units) * a.m;
+    cs = cs < a.ring ? cs : cs - a.ring;
 #pragma unroll
     for (int i = 0; i < kMaxM; ++i) {
-      const int64_t p = p0 + i;
-      if (i < a.m) {
-        const bool old = p < q.L0;
-        cx[i] = *reinterpret_cast<const uint4*>((old ? xold + (size_t)p * row : xnew + (size_t)(p - q.L0) * row) +
-                                                (size_t)cg * 16);
-        cz[i] = *reinterpret_cast<const uint4*>((old ? zring + (size_t)slot * row : znew + (size_t)(p - q.L0) * row) +
-                                                (size_t)cg * 16);
-      }
-      slot = slot + 1 == a.ring ? 0 : slot + 1;
+      const int ii = i < a.m ? i : a.m - 1;
+      const int64_t p = p0 + ii;
+      int slot = cs + ii;
+      slot = slot < a.ring ? slot : slot - a.ring;
+      slot = slot < a.ring ? slot : slot - a.ring;
+      const bool old = p < q.L0;
+      cx[i] = *reinterpret_cast<const uint32_t*>((old ? xold + (size_t)p * row : xnew + (size_t)(p - q.L0) * row) +
+                                                 (size_t)cu * 4);
+      cz[i] = *reinterpret_cast<const uint32_t*>((old ? zring + (size_t)slot * row : znew + (size_t)(p - q.L0) * row) +
+                                                 (size_t)cu * 4);
     }
   }
-  // (3) one 32-element part of a completed block's key vector
-  const int parts = a.kvec ? a.kdim / 32 : 0;
-  const int64_t kvr = a.kvec ? a.kvec_off[b] : 0;
-  const int64_t nk = a.kvec ? (a.kvec_off[b + 1] - kvr < q.nc ? a.kvec_off[b + 1] - kvr : q.nc) : 0;
-  const int64_t ki = parts > 0 ? t / parts : 0;
-  const int kp = parts > 0 ? t % parts : 0;
-  const bool k_do = parts > 0 && ki < nk && q.c0 + ki < ccap;
-  // (4) one new row's channel group
-  const int64_t ri = t / groups;
-  const int rg = t % groups;
-  const bool r_do = ri < q.n;
+  // (3) 16 bytes of one new row (threads from 512)
+  const int tr = t - kStepRows;
+  const int64_t ri = tr >= 0 ? tr / groups : 0;
+  const int rg = tr >= 0 ? tr % groups : 0;
+  const bool r_do = tr >= 0 && ri < q.n;
   uint4 rx = make_uint4(0u, 0u, 0u, 0u), rz = make_uint4(0u, 0u, 0u, 0u);
   if (r_do) {
     rx = *reinterpret_cast<const uint4*>(xnew + (size_t)ri * row + (size_t)rg * 16);
     rz = *reinterpret_cast<const uint4*>(znew + (size_t)ri * row + (size_t)rg * 16);
   }
+  // (4, issued last: its lanes
+  // exchange values, which waits for every load) one element of a completed block's key vector (threads from 256: key
+  // tk / kdim, element tk % kdim)
+  const int tk = t - kStepKeys;
+  const int64_t kvr = a.kvec ? a.kvec_off[b] : 0;
+  const int64_t nk = a.kvec ? (a.kvec_off[b + 1] - kvr < q.nc ? a.kvec_off[b + 1] - kvr : q.nc) : 0;
+  const int ki = a.kvec && tk >= 0 ? tk / a.kdim : 0, ke = a.kvec && tk >= 0 ? tk - ki * a.kdim : 0;
+  const bool k_do = a.kvec && tk >= 0 && ki < nk && q.c0 + ki < ccap;  // the same for the 32 lanes of a part
+  float kval = 0.f;
+  if (k_do) {
+    const uint8_t* src = a.kvec + ((size_t)(kvr + ki) * a.kdim + (size_t)ke) * ES;
+    kval = BF16 ? __uint_as_float((uint32_t)*reinterpret_cast<const uint16_t*>(src) << 16)
+                : *reinterpret_cast<const float*>(src);
+  }
   // ---- compute and store
   extern __shared__ __align__(16) uint8_t ap_sm[];
-  PoolState<BF16>* part = reinterpret_cast<PoolState<BF16>*>(ap_sm);
-  if (h_do) pool_segment_loaded<BF16>(ns, hz, hx, part[t]);
+  PoolSt<N>* part = reinterpret_cast<PoolSt<N>*>(ap_sm);
+  if (h_do) {
+    PoolSt<N> st;
+    pool_reset(st);
+#pragma unroll
+    for (int c0 = 0; c0 < kPoolSeg; c0 += 8) {
+      if (c0 < ns) {
+        float zz[8][N], xx[8][N];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          Vec4<BF16>::load(hz[c0 + i], zz[i]);
+          Vec4<BF16>::load(hx[c0 + i], xx[i]);
+        }
+        pool_chunk(st, zz, xx, ns - c0 < 8 ? ns - c0 : 8);
+      }
+    }
+    part[t] = st;
+  }
   if (c_do) {
-    PoolState<BF16> st;
-    pool_reset<BF16>(st);
+    PoolSt<N> st;
+    pool_reset(st);
     float zz[8][N], xx[8][N];
 #pragma unroll
     for (int i = 0; i < kMaxM; ++i) {
-      Vec16<BF16>::load(&cz[i], zz[i]);
-      Vec16<BF16>::load(&cx[i], xx[i]);
+      Vec4<BF16>::load(cz[i], zz[i]);
+      Vec4<BF16>::load(cx[i], xx[i]);
     }
-    pool_chunk<BF16>(st, zz, xx, a.m);
-    pool_store<BF16>(st, a.pooled + (size_t)(a.pool_off[b] + cj) * row + (size_t)cg * 16);
-  }
-  if (k_do) {
-    const size_t kr = (size_t)(a.pool_off[b] + q.c0 + ki);
-    mxfp4_block<BF16>(a.kvec + ((size_t)(kvr + ki) * a.kdim + (size_t)kp * 32) * ES,
-                      a.k_codes + kr * (a.kdim / 2) + (size_t)kp * 16, a.k_scales + kr * parts + kp);
+    pool_chunk(st, zz, xx, a.m);
+    float o[N];
+    pool_result(st, o);
+    *reinterpret_cast<uint32_t*>(a.pooled + (size_t)(a.pool_off[b] + cj) * row + (size_t)cu * 4) = Vec4<BF16>::pack(o);
   }
   if (r_do && q.L0 + ri < q.cap)
     *reinterpret_cast<uint4*>(a.kv_raw + (size_t)(q.r0 + q.L0 + ri) * row + (size_t)rg * 16) = rx;
+  if (k_do) {
+    uint32_t amax = __float_as_uint(kval) & 0x7fffffffu;
+#pragma unroll
+    for (int o = 16; o >= 1; o >>= 1) {
+      const uint32_t v = (uint32_t)__shfl_xor((int)amax, o, 32);
+      amax = v > amax ? v : amax;
+    }
+    const int e = mxfp4_exponent(amax);
+    uint32_t w = mxfp4_code(kval, mxfp4_inverse(e)) << (4 * (ke & 7));
+#pragma unroll
+    for (int o = 4; o >= 1; o >>= 1) w |= (uint32_t)__shfl_xor((int)w, o, 32);
+    const size_t kr = (size_t)(a.pool_off[b] + q.c0 + ki);
+    if ((ke & 7) == 0) *reinterpret_cast<uint32_t*>(a.k_codes + kr * (a.kdim / 2) + (size_t)(ke >> 3) * 4) = w;
+    if ((ke & 31) == 0) a.k_scales[kr * (a.kdim / 32) + (ke >> 5)] = (uint8_t)(e + 127);
+  }
   __syncthreads();  // every segment state is in LDS; every read of the ring and of len[b] is done
-  if (q.nh > 0 && q.h0 < hcap && (q.h0 + 1) * a.m_hca <= q.cap) {
-    for (int g = t; g < groups; g += blockDim.x) {
-      PoolState<BF16> st = part[g];
-      for (int sg = 1; sg < segs; ++sg) pool_fold<BF16>(st, part[sg * groups + g]);
-      pool_store<BF16>(st, a.hpooled + (size_t)(a.hpool_off[b] + q.h0) * row + (size_t)g * 16);
+  if (h_blk && t >= kStepFold && t < kStepFold + units) {
+    {
+      const int u = t - kStepFold;
+      PoolSt<N> st = part[u];
+      for (int sg = 1; sg < segs; ++sg) pool_fold(st, part[sg * units + u]);
+      float o[N];
+      pool_result(st, o);
+      *reinterpret_cast<uint32_t*>(a.hpooled + (size_t)(a.hpool_off[b] + q.h0) * row + (size_t)u * 4) =
+          Vec4<BF16>::pack(o);
     }
   }
-  if (r_do) {
-    const int64_t p = q.L0 + ri;
-    *reinterpret_cast<uint4*>(a.z_tail + ((size_t)b * a.ring + (size_t)(p % a.ring)) * row + (size_t)rg * 16) = rz;
+  if (r_do) {  // new row ri < max_new <= ring: one wrap at most
+    const int rs0 = (int)(q.L0 % a.ring) + (int)ri;
+    const int slot = rs0 < a.ring ? rs0 : rs0 - a.ring;
+    *reinterpret_cast<uint4*>(a.z_tail + ((size_t)b * a.ring + (size_t)slot) * row + (size_t)rg * 16) = rz;
   }
   if (t == 0) a.len[b] = q.L0 + q.n;
 }
@@ -485,16 +543,19 @@ int launch_append(bool bf16, int n_seq, int width, const int64_t* tok_off, int64
   // states in 64 KB): one launch, a workgroup per sequence
   constexpr int64_t kOneMax = 64;
   {
-    // one task of each kind per thread: new rows and short blocks' channel
-    // groups, the long block's segments, the keys' parts
+    // at most one task of each kind per thread of a 1024-thread workgroup: the
+    // long block's segment units, the short blocks' units, key elements and
+    // new rows' 16-byte groups
     const int64_t nc_max = max_new / m + 1;
+    const int units = groups * 4;
     const int segs = m_hca > 0 ? (m_hca + kPoolSeg - 1) / kPoolSeg : 0;
-    const bool fits = m <= 8 && m_hca > kPoolSeg && max_new <= m_hca && max_new * groups <= 256 &&
-                      nc_max * groups <= 256 && (int64_t)segs * groups <= 256 && nc_max * (kdim / 32) <= 256 &&
-                      (size_t)segs * groups * state <= 64 * 1024;
+    const size_t step_lds = (size_t)segs * units * (bf16 ? sizeof(PoolSt<2>) : sizeof(PoolSt<1>));
+    const bool fits = m <= 8 && (m_hca == 0 || max_new <= m_hca) && max_new <= ring && max_new * groups <= 256 &&
+                      nc_max * units <= 256 && (int64_t)segs * units <= 1024 && nc_max * kdim <= 256 &&
+                      units <= 256 && step_lds <= 64 * 1024;
     if (fits) {
       const hipError_t e1 = launch(9, kProfBoth, bf16 ? k_append_step<true> : k_append_step<false>,
-                                   dim3((unsigned)n_seq), dim3(256), (size_t)segs * groups * state, stream, a);
+                                   dim3((unsigned)n_seq), dim3(1024), step_lds, stream, a);
       return e1 == hipSuccess && hipGetLastError() == hipSuccess ? 0 : -1;
     }
   }

@@ -43,32 +43,51 @@ struct Vec16 {
   }
 };
 
-// Pooling state of one thread's channels: running max, denominator, weighted sum.
+// 4 bytes of a row (2 bf16 channels or 1 fp32 channel), as a raw word
 template <bool BF16>
-struct PoolState {
-  static constexpr int N = Vec16<BF16>::N;
+struct Vec4 {
+  static constexpr int N = BF16 ? 2 : 1;
+  __device__ static void load(uint32_t u, float* v) {
+    if constexpr (BF16) {
+      v[0] = __uint_as_float(u << 16);
+      v[1] = __uint_as_float(u & 0xffff0000u);
+    } else {
+      v[0] = __uint_as_float(u);
+    }
+  }
+  __device__ static uint32_t pack(const float* v) {
+    if constexpr (BF16) return f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16);
+    else return __float_as_uint(v[0]);
+  }
+};
+
+// Pooling state of N channels: running max, denominator, weighted sum.
+template <int N>
+struct PoolSt {
   float mx[N], den[N], acc[N];
 };
+template <bool BF16>
+using PoolState = PoolSt<Vec16<BF16>::N>;
 
 // A block is pooled in segments of kPoolSeg rows: each segment with an online
 // softmax over chunks of up to 8 rows, then the segments folded left to right.
 // The bulk kernel folds them in one thread; the streaming append pools the
 // segments of a long block in parallel and folds them in the same order, so
-// both give the same bits.
+// both give the same bits.  Every operation is per channel, so a thread
+// holding N channels computes each of them exactly as a thread holding any
+// other number of them does.
 constexpr int kPoolSeg = 16;
 
-template <bool BF16>
-__device__ __forceinline__ void pool_reset(PoolState<BF16>& st) {
+template <int N>
+__device__ __forceinline__ void pool_reset(PoolSt<N>& st) {
 #pragma unroll
-  for (int c = 0; c < PoolState<BF16>::N; ++c) { st.mx[c] = -INFINITY; st.den[c] = 0.f; st.acc[c] = 0.f; }
+  for (int c = 0; c < N; ++c) { st.mx[c] = -INFINITY; st.den[c] = 0.f; st.acc[c] = 0.f; }
 }
 
 // one chunk of n <= 8 rows (logits zz, values xx) into the state: the online
 // softmax step every pooling path uses, so all of them give the same bits
-template <bool BF16>
-__device__ __forceinline__ void pool_chunk(PoolState<BF16>& st, const float (&zz)[8][Vec16<BF16>::N],
-                                           const float (&xx)[8][Vec16<BF16>::N], int n) {
-  constexpr int N = Vec16<BF16>::N;
+template <int N>
+__device__ __forceinline__ void pool_chunk(PoolSt<N>& st, const float (&zz)[8][N], const float (&xx)[8][N], int n) {
 #pragma unroll
   for (int c = 0; c < N; ++c) {
     float cm = st.mx[c];
@@ -94,7 +113,7 @@ template <bool BF16, class XRow, class ZRow>
 __device__ __forceinline__ void pool_segment(int i0, int i1, XRow xrow, ZRow zrow, PoolState<BF16>& st) {
   using V = Vec16<BF16>;
   constexpr int N = V::N;
-  pool_reset<BF16>(st);
+  pool_reset(st);
   for (int c0 = i0; c0 < i1; c0 += 8) {
     const int n = (i1 - c0) < 8 ? (i1 - c0) : 8;
     float zz[8][N], xx[8][N];
@@ -105,37 +124,15 @@ __device__ __forceinline__ void pool_segment(int i0, int i1, XRow xrow, ZRow zro
         V::load(xrow(c0 + i), xx[i]);
       }
     }
-    pool_chunk<BF16>(st, zz, xx, n);
-  }
-}
-
-// The same segment from rows already loaded (raw 16-byte words of up to
-// kPoolSeg rows, loaded together by the caller so their latencies overlap).
-template <bool BF16>
-__device__ __forceinline__ void pool_segment_loaded(int n, const uint4 (&zr)[kPoolSeg], const uint4 (&xr)[kPoolSeg],
-                                                    PoolState<BF16>& st) {
-  using V = Vec16<BF16>;
-  constexpr int N = V::N;
-  pool_reset<BF16>(st);
-#pragma unroll
-  for (int c0 = 0; c0 < kPoolSeg; c0 += 8) {
-    if (c0 >= n) break;
-    const int k = (n - c0) < 8 ? (n - c0) : 8;
-    float zz[8][N], xx[8][N];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      V::load(&zr[c0 + i], zz[i]);
-      V::load(&xr[c0 + i], xx[i]);
-    }
-    pool_chunk<BF16>(st, zz, xx, k);
+    pool_chunk(st, zz, xx, n);
   }
 }
 
 // st <- st folded with the next segment t
-template <bool BF16>
-__device__ __forceinline__ void pool_fold(PoolState<BF16>& st, const PoolState<BF16>& t) {
+template <int N>
+__device__ __forceinline__ void pool_fold(PoolSt<N>& st, const PoolSt<N>& t) {
 #pragma unroll
-  for (int c = 0; c < PoolState<BF16>::N; ++c) {
+  for (int c = 0; c < N; ++c) {
     const float M = fmaxf(st.mx[c], t.mx[c]);
     const float a1 = fast_exp2((st.mx[c] - M) * kLog2e), a2 = fast_exp2((t.mx[c] - M) * kLog2e);
     st.den[c] = st.den[c] * a1 + t.den[c] * a2;
@@ -144,11 +141,16 @@ __device__ __forceinline__ void pool_fold(PoolState<BF16>& st, const PoolState<B
   }
 }
 
+// the pooled values of the state's channels
+template <int N>
+__device__ __forceinline__ void pool_result(const PoolSt<N>& st, float (&o)[N]) {
+#pragma unroll
+  for (int c = 0; c < N; ++c) o[c] = st.acc[c] / st.den[c];
+}
 template <bool BF16>
 __device__ __forceinline__ void pool_store(const PoolState<BF16>& st, uint8_t* out) {
-  float o[PoolState<BF16>::N];
-#pragma unroll
-  for (int c = 0; c < PoolState<BF16>::N; ++c) o[c] = st.acc[c] / st.den[c];
+  float o[Vec16<BF16>::N];
+  pool_result(st, o);
   Vec16<BF16>::store(out, o);
 }
 
@@ -161,7 +163,7 @@ __device__ __forceinline__ void pool_block(int m, XRow xrow, ZRow zrow, uint8_t*
   for (int s0 = kPoolSeg; s0 < m; s0 += kPoolSeg) {
     PoolState<BF16> t;
     pool_segment<BF16>(s0, m - s0 < kPoolSeg ? m : s0 + kPoolSeg, xrow, zrow, t);
-    pool_fold<BF16>(st, t);
+    pool_fold(st, t);
   }
   pool_store<BF16>(st, out);
 }

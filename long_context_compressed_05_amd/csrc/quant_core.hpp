@@ -26,6 +26,21 @@ __device__ __forceinline__ uint32_t e2m1_code_of(float m) {
   return (m > 0.25f) + (m >= 0.75f) + (m > 1.25f) + (m >= 1.75f) + (m > 2.5f) + (m >= 3.5f) + (m > 5.0f);
 }
 
+// the block's scale exponent e from the bits of its largest magnitude (the
+// biased exponent field: 0 for zero or a subnormal, which clamps e to -127)
+__device__ __forceinline__ int mxfp4_exponent(uint32_t amax_bits) {
+  const int E = (int)(amax_bits >> 23);
+  return E == 0 ? -127 : (E - 129 < -127 ? -127 : E - 129);
+}
+// 2^-e, a normal float for e in [-127, 125]
+__device__ __forceinline__ float mxfp4_inverse(int e) { return __uint_as_float((uint32_t)(127 - e) << 23); }
+// the 4-bit code of element v given 2^-e
+__device__ __forceinline__ uint32_t mxfp4_code(float v, float inv) {
+  const float t = v * inv;
+  const uint32_t mag = e2m1_code_of(fabsf(t));
+  return mag | ((t < 0.f && mag != 0u) ? 8u : 0u);
+}
+
 // x: the block's 32 elements (64 bytes of bf16 or 128 of fp32, 16-byte
 // aligned) -> 16 code bytes at codes (16-byte aligned) and the E8M0 byte at *scale
 template <bool BF16>
@@ -58,17 +73,11 @@ __device__ __forceinline__ void mxfp4_block(const uint8_t* x, uint8_t* codes, ui
     const uint32_t a = __float_as_uint(v[i]) & 0x7fffffffu;
     amax_bits = a > amax_bits ? a : amax_bits;
   }
-  const int E = (int)(amax_bits >> 23);  // biased exponent of amax; 0 for zero or a subnormal
-  const int e = E == 0 ? -127 : (E - 129 < -127 ? -127 : E - 129);
-  const float inv = __uint_as_float((uint32_t)(127 - e) << 23);  // 2^-e, a normal float for e in [-127, 125]
+  const int e = mxfp4_exponent(amax_bits);
+  const float inv = mxfp4_inverse(e);
   uint32_t w[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    const float t = v[i] * inv;
-    const uint32_t mag = e2m1_code_of(fabsf(t));
-    const uint32_t code = mag | ((t < 0.f && mag != 0u) ? 8u : 0u);
-    w[i >> 3] |= code << (4 * (i & 7));
-  }
+  for (int i = 0; i < 32; ++i) w[i >> 3] |= mxfp4_code(v[i], inv) << (4 * (i & 7));
   *reinterpret_cast<uint4*>(codes) = make_uint4(w[0], w[1], w[2], w[3]);
   *scale = (uint8_t)(e + 127);
 }

@@ -1,4 +1,5 @@
-"""Measured-peak kernels (HBM streaming read, FP4 and bf16 MFMA loops) -
+"""Measured-peak kernels (HBM streaming read, FP4 and bf16 MFMA loops, an
+empty kernel for the launch floor) -
 MEASUREMENT INFRASTRUCTURE ONLY: bench.py loads it to report every roofline
 fraction against this part's sustained rates as well as the datasheet's.
 The product library (long_context_compressed_05_amd) does not use it."""
@@ -41,7 +42,8 @@ def lib():
     L.peak_read.argtypes = [vp, sz, ci, ci, vp, vp, vp, vp]
     L.peak_mfma_fp4.argtypes = [ci, ci, vp, vp, vp, vp]
     L.peak_mfma_bf16.argtypes = [ci, ci, ci, vp, vp, vp, vp]
-    for f in (L.peak_read, L.peak_mfma_fp4, L.peak_mfma_bf16):
+    L.peak_empty.argtypes = [ci, ci, vp, vp, vp, vp]
+    for f in (L.peak_read, L.peak_mfma_fp4, L.peak_mfma_bf16, L.peak_empty):
         f.restype = ci
     _lib = L
     return L

@@ -11,7 +11,9 @@
 //                    indexer's instruction), four independent accumulators
 //                    per wave;
 //  - peak_mfma_bf16: back-to-back bf16 MFMAs (16x16x32, the attention's
-//                    instruction, or 32x32x16).
+//                    instruction, or 32x32x16);
+//  - peak_empty:     a kernel that does nothing (the floor of any launch's
+//                    measured duration: dispatch, wave launch, end of kernel).
 // Each call launches one kernel on `stream`; when start/stop are non-null
 // they are attached to the dispatch (hipExtLaunchKernel) and time the kernel
 // alone.  Returns 0 or -1 (launch failure).
@@ -100,6 +102,10 @@ __global__ __launch_bounds__(256) void k_peak_bf16(int iters, float* sink) {
   sink[blockIdx.x * 256 + threadIdx.x] = s;
 }
 
+__global__ __launch_bounds__(1024) void k_peak_empty(uint32_t* sink) {
+  if (threadIdx.x == 1023u && blockIdx.x == 0xffffffu) sink[0] = 1u;
+}
+
 template <typename... P>
 static int go(void (*k)(P...), dim3 grid, void* start, void* stop, void* stream, P... args) {
   void* a[] = {(void*)&args..., nullptr};
@@ -109,6 +115,15 @@ static int go(void (*k)(P...), dim3 grid, void* start, void* stop, void* stream,
 }
 
 extern "C" {
+
+// sink: device word (never written); workgroups of `block` threads (<= 1024)
+int peak_empty(int grid, int block, uint32_t* sink, void* start, void* stop, void* stream) {
+  if (grid < 1 || block < 1 || block > 1024 || !sink) return -1;
+  void* a[] = {(void*)&sink, nullptr};
+  const hipError_t e = hipExtLaunchKernel((const void*)k_peak_empty, dim3(grid), dim3(block), a, 0,
+                                          (hipStream_t)stream, (hipEvent_t)start, (hipEvent_t)stop, 0);
+  return e == hipSuccess ? 0 : -1;
+}
 
 // buf: device, bytes a multiple of 16; sink: device, >= grid words; unroll 4, 8 or 16
 int peak_read(const void* buf, size_t bytes, int grid, int unroll, uint32_t* sink, void* start, void* stop,
