@@ -1,7 +1,11 @@
 // MQA attention tile loop on bf16 MFMA, shared by the attention kernels.
 //
 // One workgroup of 4 waves; wave w owns query-head groups w, w+4, ... (16
-// heads each, GPW groups per wave).  A list of key rows ([2][128] bf16: K then
+// heads each, GPW groups per wave).  attn_run_q2 serves two queries of one
+// sequence over one key list instead: wave w owns head group w of both, and
+// each K and V fragment read from LDS feeds both queries' MFMAs (half the
+// LDS reads per FLOP); per-query limits mask the list positions beyond each
+// query's visible range.  A list of key rows ([2][128] bf16: K then
 // V, 512 B) is walked in 64-key tiles.  Tiles go from memory straight into LDS
 // (global_load_lds_dwordx4, no register staging) through NST stages: while
 // tile t is computed, tiles t+1 .. t+NST-1 are in flight.
@@ -107,6 +111,106 @@ __device__ __forceinline__ void attn_init(AttnState<GPW>& st, const uint8_t* q_r
       } else {
         st.qf[gi][kq] = v8bf{};
       }
+    }
+  }
+}
+
+// DMA of tile t of list positions [p_begin, p_end) into stage s: wave w
+// stages rows 16w .. 16w+15 (lane: row 16w + lane/4, chunks 4i + lane%4 of
+// instruction i) and writes their validity bits to the stage's mask word.
+template <class RowPtr>
+__device__ __forceinline__ void attn_issue_tile(int64_t p_begin, int64_t p_end, int64_t t, int s, RowPtr& rowptr,
+                                                uint32_t lds_base, uint64_t* masks) {
+  const int lane = lane_tid() & 63, wave = lane_tid() >> 6;
+  const int row = 16 * wave + (lane >> 2);
+  const int64_t p = p_begin + t * kTileKeys + row;
+  const uint8_t* rp = p < p_end ? rowptr(p) : nullptr;
+  const uint64_t vb = __ballot(rp != nullptr);
+  const uint8_t* src = (rp ? rp : g_zero_row) + 16 * (lane & 3);
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_base + (uint32_t)(s * kStageBytes + wave * 1024));
+  dma16<0>(src, m0);
+  dma16<64>(src, m0 + 4 * 1024 - 64);
+  dma16<128>(src, m0 + 8 * 1024 - 128);
+  dma16<192>(src, m0 + 12 * 1024 - 192);
+  dma16<256>(src, m0 + 16 * 1024 - 256);
+  dma16<320>(src, m0 + 20 * 1024 - 320);
+  dma16<384>(src, m0 + 24 * 1024 - 384);
+  dma16<448>(src, m0 + 28 * 1024 - 448);
+  // rows 16w .. 16w+15 valid bits: lanes 4j
+  uint32_t m16 = 0;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) m16 |= (uint32_t)((vb >> (4 * j)) & 1ull) << j;
+  if (lane == 0) reinterpret_cast<uint16_t*>(masks + s)[wave] = (uint16_t)m16;
+}
+
+// the tile's V^T fragments (lane (l16, g): see the layout notes above)
+__device__ __forceinline__ void attn_vt(const uint8_t* cur, int l16, int g, v4s_t (&vt)[8][2][2]) {
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+    for (int kq = 0; kq < 2; ++kq)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int a3 = l16 & 3;
+        const int off = ((4 + (mt >> 1)) * 4 + 2 * kq + hh) * 1024 + (4 * g + (l16 >> 2)) * 64 +
+                        (2 * (mt & 1) + (a3 >> 1)) * 16 + (a3 & 1) * 8;
+        vt[mt][kq][hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4s_t*)(const_cast<uint8_t*>(cur) + off));
+      }
+}
+
+// masked online softmax of one tile's scores and O^T += V^T P^T for one
+// group (the same steps as attn_run's, for attn_run_q2)
+__device__ __forceinline__ void attn_softmax_pv(float& m_run, float& l_run, v4f (&O)[8], float (&s_)[4][4],
+                                                const v4s_t (&vt)[8][2][2], uint64_t vmask, int g,
+                                                float scale_log2) {
+  if (vmask != ~0ull) {
+    const uint64_t my = vmask >> (4 * g);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        if (!((my >> (16 * mt + v)) & 1ull)) s_[mt][v] = -INFINITY;
+  }
+  float tmax = -INFINITY;
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) tmax = fmaxf(tmax, s_[mt][v]);
+  tmax = xor32_max(xor16_max(tmax)) * scale_log2;
+  if (__ballot(tmax > m_run + (float)kLazyRescale) != 0ull) {
+    const float mnew = fmaxf(m_run, tmax);
+    const float alpha = fast_exp2(m_run - mnew);  // 0 while nothing was valid
+    m_run = mnew;
+    l_run *= alpha;
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) O[mt] *= alpha;
+  }
+  if (m_run == -INFINITY) return;  // nothing valid so far (uniform: validity is per key)
+  const float mneg = -m_run;
+  float psum = 0.f;
+  float pv[4][4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      pv[mt][v] = fast_exp2(fmaf(s_[mt][v], scale_log2, mneg));
+      psum += pv[mt][v];
+    }
+  l_run += psum;
+#pragma unroll
+  for (int kq = 0; kq < 2; ++kq) {
+    v8bf pf;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      pf[i] = (__bf16)pv[2 * kq][i];
+      pf[4 + i] = (__bf16)pv[2 * kq + 1][i];
+    }
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) {
+      const v4s_t both[2] = {vt[mt][kq][0], vt[mt][kq][1]};
+      const v8bf vf = *reinterpret_cast<const v8bf*>(both);
+      O[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, O[mt], 0, 0, 0);
     }
   }
 }
@@ -255,6 +359,69 @@ __device__ __forceinline__ void attn_run(AttnState<GPW>& st, int H, float scale_
     }
   }
   __syncthreads();  // LDS free for the caller
+}
+
+// Two queries of one sequence over one key list (positions [0, p_end)): group
+// gi of `st` is query gi's head group `wave`; query gi sees positions < lim[gi]
+// only.  Each K fragment feeds both queries' S^T MFMAs and each V^T fragment
+// both PV products.  Same entry conditions as attn_run.
+template <int NST = kAttnStages, class RowPtr>
+__device__ __forceinline__ void attn_run_q2(AttnState<2>& st, float scale_log2, int64_t p_end, const int64_t (&lim)[2],
+                                            RowPtr rowptr, uint8_t* lds) {
+  static_assert(NST == 2 || NST == 3, "two or three stages");
+  const int lane = lane_tid() & 63;
+  const int l16 = lane & 15, g = lane >> 4;
+  if (p_end <= 0) return;
+  const int64_t n_tiles = (p_end + kTileKeys - 1) / kTileKeys;
+  const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
+  uint64_t* masks = reinterpret_cast<uint64_t*>(lds + NST * kStageBytes);
+  auto issue = [&](int64_t t, int s) { attn_issue_tile(0, p_end, t, s, rowptr, lds_base, masks); };
+  issue(0, 0);
+  if (n_tiles > 1) issue(1, 1);
+  if (NST == 3 && n_tiles > 2) issue(2, 2);
+  for (int64_t t = 0; t < n_tiles; ++t) {
+    const int s = (int)(t % NST);
+    const int64_t ahead = n_tiles - 1 - t < NST - 1 ? n_tiles - 1 - t : NST - 1;
+    if (ahead >= 2) attn_wait_dma<16>();
+    else if (ahead == 1) attn_wait_dma<8>();
+    else attn_wait_dma<0>();
+    __syncthreads();
+    const uint8_t* cur = lds + s * kStageBytes;
+    const uint64_t vmask = masks[s];
+    const int64_t t0 = t * kTileKeys;
+    uint64_t vm[2];
+#pragma unroll
+    for (int gi = 0; gi < 2; ++gi)
+      vm[gi] = lim[gi] <= t0 ? 0ull : (lim[gi] < t0 + kTileKeys ? vmask & ((1ull << (lim[gi] - t0)) - 1ull) : vmask);
+    float s0[4][4], s1[4][4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      v8bf kf[4];
+#pragma unroll
+      for (int kq = 0; kq < 4; ++kq)
+        kf[kq] = *reinterpret_cast<const v8bf*>(cur + (kq * 4 + mt) * 1024 + l16 * 64 + g * 16);
+      v4f a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kq = 0; kq < 4; ++kq) {
+        a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kq], st.qf[0][kq], a0, 0, 0, 0);
+        a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kq], st.qf[1][kq], a1, 0, 0, 0);
+      }
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        s0[mt][v] = a0[v];
+        s1[mt][v] = a1[v];
+      }
+    }
+    v4s_t vt[8][2][2];
+    attn_vt(cur, l16, g, vt);
+    attn_softmax_pv(st.m_run[0], st.l_run[0], st.O[0], s0, vt, vm[0], g, scale_log2);
+    attn_softmax_pv(st.m_run[1], st.l_run[1], st.O[1], s1, vt, vm[1], g, scale_log2);
+    if (t + NST < n_tiles) {
+      __syncthreads();
+      issue(t + NST, s);
+    }
+  }
+  __syncthreads();
 }
 
 // Finish: normalised bf16 output [H][128] and lse (natural log), or, when

@@ -128,6 +128,69 @@ __global__ __launch_bounds__(256) void k_attn_bf16(AttnArgs a) {
                    a.splits > 1, false);
 }
 
+// HCA without a window over a prefill batch (H = 64, one split per query):
+// workgroup y serves rows 2y and 2y+1 of one sequence over the union of their
+// visible pooled rows (attn_run_q2: every K and V fragment read from LDS feeds
+// both rows; each row masks the positions beyond its own visible count).  A
+// pair that straddles two sequences (at most one per sequence boundary), or
+// the unpaired last row, is served one row at a time (attn_run).
+__global__ __launch_bounds__(256) void k_attn_bf16_pair(AttnArgs a, int64_t n_q) {
+  __shared__ __align__(16) uint8_t lds[kAttnLdsBytes];
+  const int64_t r0 = 2 * (int64_t)blockIdx.y;
+  const bool has1 = r0 + 1 < n_q;
+  const RowCtx c0 = row_ctx(a, r0);
+  const RowCtx c1 = row_ctx(a, has1 ? r0 + 1 : r0);
+  constexpr size_t RB = 2 * 128 * 2;
+  if (has1 && c1.b == c0.b) {
+    const int64_t n_union = c0.n_vis_a > c1.n_vis_a ? c0.n_vis_a : c1.n_vis_a;
+    auto rowptr = [&](int64_t p) -> const uint8_t* {
+      return p < n_union ? a.kv_pool + (size_t)(c0.pool_base + p) * RB : nullptr;
+    };
+    AttnState<2> st;
+    {
+      const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, l16 = lane & 15, g = lane >> 4;
+#pragma unroll
+      for (int gi = 0; gi < 2; ++gi) {
+        st.m_run[gi] = -INFINITY;
+        st.l_run[gi] = 0.f;
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt) st.O[gi][mt] = v4f{0.f, 0.f, 0.f, 0.f};
+        const uint8_t* qrow = a.q + (size_t)(r0 + gi) * a.H * 128 * 2;
+#pragma unroll
+        for (int kq = 0; kq < 4; ++kq)
+          st.qf[gi][kq] = *reinterpret_cast<const v8bf*>(qrow + ((size_t)(16 * wave + l16) * 128 + 32 * kq + 8 * g) * 2);
+      }
+    }
+    const int64_t lim[2] = {c0.n_vis_a, c1.n_vis_a};
+    attn_run_q2(st, a.scale_log2, n_union, lim, rowptr, lds);
+    // each row's head group `wave`: the one-group finish on a copy of its state
+#pragma unroll
+    for (int gi = 0; gi < 2; ++gi) {
+      AttnState<1> one;
+      one.m_run[0] = st.m_run[gi];
+      one.l_run[0] = st.l_run[gi];
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt) one.O[0][mt] = st.O[gi][mt];
+      const int64_t row = r0 + gi;
+      attn_finish<1>(one, a.H, a.out + (size_t)row * a.H * 128 * 2, a.lse ? a.lse + row * a.H : nullptr, nullptr,
+                     nullptr, false, false);
+    }
+    return;
+  }
+  for (int j = 0; j < (has1 ? 2 : 1); ++j) {  // uniform
+    const RowCtx& c = j == 0 ? c0 : c1;
+    const int64_t row = r0 + j;
+    auto rowptr = [&](int64_t p) -> const uint8_t* {
+      return p < c.n_vis_a ? a.kv_pool + (size_t)(c.pool_base + p) * RB : nullptr;
+    };
+    AttnState<1> st;
+    attn_init<1>(st, a.q + (size_t)row * a.H * 128 * 2, a.H);
+    attn_run<1>(st, a.H, a.scale_log2, 0, a.seg_a, rowptr, lds);
+    attn_finish<1>(st, a.H, a.out + (size_t)row * a.H * 128 * 2, a.lse ? a.lse + row * a.H : nullptr, nullptr,
+                   nullptr, false, false);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // fp32, VALU (small head counts; exact fp32 FMAs)
 // ---------------------------------------------------------------------------
@@ -333,6 +396,11 @@ int launch_attn(bool bf16, bool hca, int n_seq, int64_t n_q, const int64_t* tok_
   a.splits = pl.splits; a.ks = pl.ks;
   if (list_len == 0) {  // every list is empty: the combine writes zeros and -inf
     a.splits = 1;
+  }
+  if (bf16 && hca && W == 0 && H == 64 && a.splits == 1 && n_q >= 512) {  // prefill HCA: two rows per workgroup
+    const hipError_t e = launch(3, kProfBoth, k_attn_bf16_pair, dim3(1u, (unsigned)((n_q + 1) / 2)), dim3(256), 0,
+                                stream, a, n_q);
+    return e == hipSuccess && hipGetLastError() == hipSuccess ? 0 : -1;
   }
   dim3 grid((unsigned)a.splits, (unsigned)n_q);
   hipError_t e = launch(3, kProfBoth, !bf16 ? k_attn_f32 : (H > 64 ? k_attn_bf16<2> : k_attn_bf16<1>), grid,

@@ -43,6 +43,11 @@ WORKLOADS = {
                                               W=200, m=4, m_hca=64, W_hca=64, seed=15),
     "prefill_bf16_ties": lambda: small_wl("prefill_bf16_ties", [5000, 9001], [64, 200], k=128,
                                           codeset=synth.E2M1_TIE_CODES, seed=18),
+    # 635 prefill queries over three sequences: HCA serves two rows per workgroup,
+    # with pairs across sequence boundaries, rows whose visible counts differ by
+    # one, and an unpaired last row
+    "prefill_bf16_pairs": lambda: small_wl("prefill_bf16_pairs", [2000, 1500, 900], [301, 256, 78], k=64, W=64,
+                                           m_hca=32, seed=19),
 }
 
 
@@ -313,7 +318,7 @@ def test_sparse_attn_stagewise(name):
 
 
 @pytest.mark.parametrize("name", ["decode_fp32_t4096_h8", "decode_bf16_ragged", "prefill_bf16_chunks",
-                                  "decode_fp32_k1_h24", "decode_bf16_kbig_whca"])
+                                  "decode_fp32_k1_h24", "decode_bf16_kbig_whca", "prefill_bf16_pairs"])
 def test_hca_attn_stagewise(name):
     csa = _lib()
     wl = WORKLOADS[name]()
