@@ -961,6 +961,19 @@ def bench_peaks(torch, csa, step_bytes, log, R: int = 20):
         assert L.peak_empty(4, 1024, sink.data_ptr(), e0.handle, e1.handle, stream) == 0
     torch.cuda.synchronize()
     out["empty_kernel_us"] = round(float(np.median([a.elapsed_ms(b) * 1e3 for a, b in ev[1:]])), 2)
+    # VALU issue: 64 x 256 adds per wave, one workgroup per CU of 1, 4 or 16 waves
+    valu = {}
+    for block in (64, 256, 1024):
+        ev = [(csa.HipEvent(), csa.HipEvent()) for _ in range(6)]
+        for e0, e1 in ev:
+            assert L.peak_valu(256, block, 64, sink.data_ptr(), e0.handle, e1.handle, stream) == 0
+        torch.cuda.synchronize()
+        us = float(np.median([a.elapsed_ms(b) * 1e3 for a, b in ev[1:]]))
+        per_wave = 64 * 256
+        valu[f"waves_per_cu_{block // 64}"] = {
+            "us": round(us, 2),
+            "ns_per_instr_per_wave": round((us - out["empty_kernel_us"]) * 1e3 / per_wave, 3)}
+    out["valu_issue"] = valu
     out["fp4_mfma_TFLOP/s"] = fp4
     out["bf16_mfma_16x16x32_TFLOP/s"] = b16s
     out["bf16_mfma_32x32x16_TFLOP/s"] = b16b

@@ -33,10 +33,14 @@
 // workgroup to finish (a returning atomic on the exit count) advances it.
 // Attention partials are plain data: the producer drains its stores
 // (s_waitcnt vmcnt(0)) before it publishes the partial's tagged header.
-// Every wait depends only on work of an earlier stage done by workgroups that
-// are all resident and never wait for a later stage, so every wait ends; the
-// waits are bounded anyway, and hitting the bound sets the error word (read
-// and cleared by csa_hca_decode_check) and skips the workgroup's remaining work.
+// Forward progress: units wait only for units of lower number.  Every unit
+// after the first round is claimed from the ticket counter by a workgroup
+// that is running; a first-round score chunk (assigned by workgroup id) may
+// belong to a workgroup not yet dispatched, so a CSA group that finds a chunk's
+// list missing for steal_polls polls computes that chunk itself and then runs
+// again.  Every wait therefore ends whatever the residency; the waits are
+// bounded anyway, and hitting the bound sets the error word (read and cleared
+// by csa_hca_decode_check) and skips the workgroup's remaining work.
 #include <atomic>
 #include <cstdlib>
 

@@ -1,5 +1,5 @@
 """Measured-peak kernels (HBM streaming read, FP4 and bf16 MFMA loops, an
-empty kernel for the launch floor) -
+empty kernel for the launch floor, a VALU loop for the per-wave issue rate) -
 MEASUREMENT INFRASTRUCTURE ONLY: bench.py loads it to report every roofline
 fraction against this part's sustained rates as well as the datasheet's.
 The product library (long_context_compressed_05_amd) does not use it."""
@@ -43,7 +43,8 @@ def lib():
     L.peak_mfma_fp4.argtypes = [ci, ci, vp, vp, vp, vp]
     L.peak_mfma_bf16.argtypes = [ci, ci, ci, vp, vp, vp, vp]
     L.peak_empty.argtypes = [ci, ci, vp, vp, vp, vp]
-    for f in (L.peak_read, L.peak_mfma_fp4, L.peak_mfma_bf16, L.peak_empty):
+    L.peak_valu.argtypes = [ci, ci, ci, vp, vp, vp, vp]
+    for f in (L.peak_read, L.peak_mfma_fp4, L.peak_mfma_bf16, L.peak_empty, L.peak_valu):
         f.restype = ci
     _lib = L
     return L

@@ -13,7 +13,10 @@
 //  - peak_mfma_bf16: back-to-back bf16 MFMAs (16x16x32, the attention's
 //                    instruction, or 32x32x16);
 //  - peak_empty:     a kernel that does nothing (the floor of any launch's
-//                    measured duration: dispatch, wave launch, end of kernel).
+//                    measured duration: dispatch, wave launch, end of kernel);
+//  - peak_valu:      `iters` x 256 independent 32-bit VALU adds per wave (four
+//                    chains), waves per workgroup as given: the instruction
+//                    issue rate of one wave, and of several sharing a SIMD.
 // Each call launches one kernel on `stream`; when start/stop are non-null
 // they are attached to the dispatch (hipExtLaunchKernel) and time the kernel
 // alone.  Returns 0 or -1 (launch failure).
@@ -106,6 +109,20 @@ __global__ __launch_bounds__(1024) void k_peak_empty(uint32_t* sink) {
   if (threadIdx.x == 1023u && blockIdx.x == 0xffffffu) sink[0] = 1u;
 }
 
+#define PK_ADD4                                                                                  \
+  asm volatile("v_add_u32 %0, %0, %4\n\tv_add_u32 %1, %1, %4\n\tv_add_u32 %2, %2, %4\n\tv_add_u32 %3, %3, %4" \
+               : "+v"(x0), "+v"(x1), "+v"(x2), "+v"(x3)                                           \
+               : "v"(y));
+#define PK_ADD16 PK_ADD4 PK_ADD4 PK_ADD4 PK_ADD4
+#define PK_ADD64 PK_ADD16 PK_ADD16 PK_ADD16 PK_ADD16
+__global__ __launch_bounds__(1024) void k_peak_valu(int iters, uint32_t y, uint32_t* sink) {
+  uint32_t x0 = threadIdx.x, x1 = x0 + 1u, x2 = x0 + 2u, x3 = x0 + 3u;
+  for (int i = 0; i < iters; ++i) {
+    PK_ADD64 PK_ADD64 PK_ADD64 PK_ADD64
+  }
+  if ((x0 ^ x1 ^ x2 ^ x3) == 0xdeadbeefu) sink[0] = x0;
+}
+
 template <typename... P>
 static int go(void (*k)(P...), dim3 grid, void* start, void* stop, void* stream, P... args) {
   void* a[] = {(void*)&args..., nullptr};
@@ -115,6 +132,16 @@ static int go(void (*k)(P...), dim3 grid, void* start, void* stop, void* stream,
 }
 
 extern "C" {
+
+// sink: device word (written only if an impossible value comes out)
+int peak_valu(int grid, int block, int iters, uint32_t* sink, void* start, void* stop, void* stream) {
+  if (grid < 1 || block < 1 || block > 1024 || iters < 1 || !sink) return -1;
+  uint32_t y = 1u;
+  void* a[] = {(void*)&iters, (void*)&y, (void*)&sink, nullptr};
+  const hipError_t e = hipExtLaunchKernel((const void*)k_peak_valu, dim3(grid), dim3(block), a, 0,
+                                          (hipStream_t)stream, (hipEvent_t)start, (hipEvent_t)stop, 0);
+  return e == hipSuccess ? 0 : -1;
+}
 
 // sink: device word (never written); workgroups of `block` threads (<= 1024)
 int peak_empty(int grid, int block, uint32_t* sink, void* start, void* stop, void* stream) {
