@@ -9,10 +9,11 @@
 // the k largest under (S descending, j ascending), indices in ascending order.
 //
 // Three kernels:
-//  1. k_pf_thresh: per block of 8 queries of one sequence, the scores of a
+//  1. k_pf_thresh: per block of 4 queries of one sequence, the scores of a
 //     strided sample of the visible keys (every stride-th) -> LDS; per query
-//     (one wave, two radix passes over the sample's own range) tau = the lower
-//     edge of the bin holding the need_s-th largest sample score, need_s =
+//     (one wave, one radix pass over the range of the sample's nonzero
+//     scores) tau = the lower edge of the bin holding the need_s-th largest
+//     sample score, need_s =
 //     ceil(2 k / stride), so that about 2 k keys are >= tau; tau = 0 when the
 //     query sees at most k keys or too few samples.
 //  2. k_pf_score: every visible score exactly once on the block-scaled FP4
@@ -318,10 +319,22 @@ __global__ __launch_bounds__(256) void k_pf_thresh(PfArgs a) {
         kv[e] = v ? ss[(size_t)q * a.ns_max + c] : 0u;
         vm |= v ? (1u << e) : 0u;
       }
-      // two radix passes: the lower edge of the sample bin holding the need_s-th largest
-      // (at least need_s samples are >= it; the exact order statistic is not needed)
-      uint32_t gt;
-      tau = wave_kth<kPfSampleMax / 64, 2>(kv, vm, (nsq + 63) >> 6, (uint32_t)need_s, hist, &gt);
+      // One radix pass over the range of the sample's nonzero scores (a score
+      // is 0 when every head's dot product is <= 0): the lower edge of the
+      // sample bin holding the need_s-th largest, so at least need_s samples
+      // are >= it (the exact order statistic is not needed).  With 1024 bins
+      // over that range a bin spans a few percent of a score, so the bin
+      // edge adds few candidates.  When fewer than need_s samples are
+      // nonzero, tau = 0 (every visible key is a candidate).
+#pragma unroll
+      for (int e = 0; e < kPfSampleMax / 64; ++e) vm &= kv[e] != 0u ? 0xffffffffu : ~(1u << e);
+      uint32_t nz = (uint32_t)__builtin_popcount(vm);
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) nz += (uint32_t)__shfl_xor((int)nz, o);
+      if (nz >= (uint32_t)need_s) {
+        uint32_t gt;
+        tau = wave_kth<kPfSampleMax / 64, 1>(kv, vm, (nsq + 63) >> 6, (uint32_t)need_s, hist, &gt);
+      }
     }
     if (lane == 0) a.tau[row] = tau;
   }
