@@ -22,7 +22,11 @@
  * Conventions for every entry point
  *  - Pointers are DEVICE pointers unless a comment says "host".  The caller
  *    owns all memory, including workspaces; the library allocates and frees
- *    nothing and keeps no pointer after a call returns.
+ *    nothing and keeps no pointer after a call returns.  Its only state is
+ *    per-device caches (whether the device is a gfx950, workgroups resident
+ *    per CU; computed once per device, race-free atomics), the profiling
+ *    hook's events, and for csa_hca_decode_noalloc a static scratch array
+ *    per device.
  *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
  *    default stream).  The library never synchronises.  Calls on different
  *    streams may run concurrently if they do not share a workspace.
