@@ -125,6 +125,15 @@ struct ScoreResult {
 /* Lightning-indexer score of one key for one query:
  *   S = sum_h w_h * max(0, sum_c q[h][c] * k[c])
  * over MXFP4 values (code value times the 2^(e-127) scale of its 32-block). */
+/* whether v << sh (v >= 0) stays below 2^125, so that a few such terms still
+ * add up inside a signed 128-bit integer */
+bool shl_fits(__int128 v, int sh) {
+  if (v < 0 || sh < 0) return false;
+  int bits = 0;
+  for (__int128 t = v; t != 0; t >>= 1) ++bits;
+  return bits + sh <= 125;
+}
+
 ScoreResult index_score(int H_I, int d_I, const uint8_t* qc, const uint8_t* qs, const float* w,
                         const uint8_t* kc, const uint8_t* ks) {
   ScoreResult r{0.0, true, true};
@@ -186,8 +195,14 @@ ScoreResult index_score(int H_I, int d_I, const uint8_t* qc, const uint8_t* qs, 
     int e = emin + we;
     min_unit_all = std::min(min_unit_all, std::ldexp(1.0, e));
     if (!have) { tot = dot; tot_e = e; have = true; }
-    else if (e >= tot_e) tot += dot << (e - tot_e);
-    else { tot = (tot << (tot_e - e)) + dot; tot_e = e; }
+    else if (!r.ok) continue; /* already beyond what 128 bits can check */
+    else if (e >= tot_e) {
+      if (!shl_fits(dot, e - tot_e)) r.ok = false;
+      else tot += dot << (e - tot_e);
+    } else {
+      if (!shl_fits(tot, tot_e - e)) r.ok = false;
+      else { tot = (tot << (tot_e - e)) + dot; tot_e = e; }
+    }
   }
   if (all_pow2) { /* the integer route needs power-of-two head weights */
     double sint = have ? std::ldexp((double)tot, tot_e) : 0.0;
