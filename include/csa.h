@@ -83,6 +83,19 @@ const char* csa_status_string(int status);
 /* Thread-local description of the last failed call on this thread (host). */
 const char* csa_last_error(void);
 
+/* Debug builds only.  In a library compiled with CSA_DEBUG (libcsa_debug.so,
+ * `python -m long_context_compressed_05_amd.build --debug`), the kernels check
+ * device-side indices before using them (every CSA list index given to
+ * csa_sparse_attn against its sequence's pooled rows; every row a fused
+ * decode step's selection gathers against the query's visible entries) and
+ * count each violation instead of reading out of range (the entry is then
+ * treated as padding).  csa_debug_checks stores the count since the last
+ * call in *violations and clears it; it synchronises the current device.
+ * Errors: CSA_ERR_INVALID for a NULL pointer, CSA_ERR_UNSUPPORTED in a
+ * release build (no checks compiled), CSA_ERR_DEVICE when the counters
+ * cannot be read. */
+int csa_debug_checks(uint64_t* violations);
+
 /* ------------------------------------------------------------------------
  * csa_compress — pooling of m consecutive raw rows into one row.
  * Pages: pytorch.kr CSA/HCA section (m consecutive KV entries become one;

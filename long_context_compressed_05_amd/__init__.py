@@ -16,7 +16,9 @@ from typing import Optional, Tuple
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libcsa.so")
+# CSA_LIBRARY=debug loads libcsa_debug.so (the same kernels with device-side
+# index checks, see csa_debug_checks); anything else loads libcsa.so
+LIB_PATH = os.path.join(_HERE, "libcsa_debug.so" if os.environ.get("CSA_LIBRARY") == "debug" else "libcsa.so")
 
 CSA_OK, CSA_ERR_INVALID, CSA_ERR_UNSUPPORTED, CSA_ERR_WORKSPACE, CSA_ERR_DEVICE = 0, -1, -2, -3, -4
 CSA_F32, CSA_BF16 = 0, 1
@@ -26,7 +28,7 @@ EXPORTS = ("csa_status_string", "csa_last_error", "csa_compress", "csa_cache_app
            "hca_attn", "csa_hca_decode_workspace", "csa_hca_decode", "csa_hca_decode_noalloc", "csa_hca_decode_shared",
            "csa_hca_decode_paged",
            "csa_hca_decode_check",
-           "csa_hca_decode_fallbacks", "csa_profile_events")
+           "csa_hca_decode_fallbacks", "csa_profile_events", "csa_debug_checks")
 (CSA_K_IDX_SCORE, CSA_K_IDX_SELECT, CSA_K_IDX_FINAL, CSA_K_ATTN, CSA_K_ATTN_COMBINE, CSA_K_COMPRESS,
  CSA_K_FUSED, CSA_K_PF_THRESH, CSA_K_PF_SELECT, CSA_K_APPEND, CSA_K_QUANT) = range(11)
 
@@ -55,6 +57,7 @@ def lib():
     L.csa_status_string.argtypes = [ci]
     L.csa_last_error.restype = ctypes.c_char_p
     L.csa_last_error.argtypes = []
+    L.csa_debug_checks.argtypes = [vp]
     L.csa_compress.argtypes = [ci, i32, vp, vp, i64, ci, ci, vp, vp, vp, vp]
     L.csa_mxfp4_quantize.argtypes = [ci, i64, ci, vp, vp, vp, vp]
     L.csa_cache_append.argtypes = [ci, i32, ci, vp, vp, vp, i64, vp, vp, vp, vp, ci, vp, ci, vp, vp, ci, vp, vp, vp,
@@ -197,6 +200,14 @@ def csa_cache_append(x_new: torch.Tensor, z_new: torch.Tensor, new_off: torch.Te
                                   ring, _ptr(pool_off), m, _ptr(pooled), _ptr(hpool_off), m_hca, _ptr(hpooled),
                                   _ptr(kvec_off), _ptr(kvec), kdim, _ptr(k_codes), _ptr(k_scales), _stream(stream)),
            "csa_cache_append")
+
+
+def csa_debug_checks() -> int:
+    """Violations counted by a debug library's device-side index checks since
+    the last call (then cleared); raises on a release library."""
+    n = ctypes.c_uint64(0)
+    _check(lib().csa_debug_checks(ctypes.byref(n)), "csa_debug_checks")
+    return int(n.value)
 
 
 def csa_mxfp4_quantize(x: torch.Tensor, codes: Optional[torch.Tensor] = None,

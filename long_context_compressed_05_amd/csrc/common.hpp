@@ -34,6 +34,22 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+#ifdef CSA_DEBUG
+// Debug builds (libcsa_debug.so): kernels check device-side indices before
+// they use them and count each violation here (one counter per translation
+// unit) instead of reading out of range; csa_debug_checks reads and clears
+// the counters.  Release builds compile none of this.
+static __device__ unsigned long long g_debug_violations;
+__device__ __forceinline__ void debug_violation() { atomicAdd(&g_debug_violations, 1ull); }
+// this translation unit's count since the last call, then cleared (synchronous)
+static inline unsigned long long debug_take_here() {
+  unsigned long long v = 0, z = 0;
+  if (hipMemcpyFromSymbol(&v, HIP_SYMBOL(g_debug_violations), sizeof(v)) != hipSuccess) return ~0ull;
+  if (hipMemcpyToSymbol(HIP_SYMBOL(g_debug_violations), &z, sizeof(z)) != hipSuccess) return ~0ull;
+  return v;
+}
+#endif
+
 // Head weight folded into a query block's E8M0 scale: w = 2^e multiplies
 // every product of the block, so the block's scale byte becomes qscale + e.
 // `u` holds the block's 32 e2m1 codes.  The byte is clamped to E8M0's finite

@@ -264,6 +264,19 @@ const char* csa_status_string(int status) {
 
 const char* csa_last_error(void) { return g_err; }
 
+int csa_debug_checks(uint64_t* violations) {
+  if (!violations) return fail(CSA_ERR_INVALID, "violations must not be NULL");
+#ifdef CSA_DEBUG
+  const unsigned long long a = csa::debug_take_attn(), f = csa::debug_take_fused();
+  if (a == ~0ull || f == ~0ull) return fail(CSA_ERR_DEVICE, "could not read the debug counters");
+  *violations = (uint64_t)(a + f);
+  return CSA_OK;
+#else
+  *violations = 0;
+  return fail(CSA_ERR_UNSUPPORTED, "a release build: no device-side checks compiled (build with --debug)");
+#endif
+}
+
 int csa_compress(int dtype, int32_t n_seq, const int64_t* tok_off, const int64_t* pool_off,
                  int64_t max_len, int m, int width, const void* x, const void* z, void* out,
                  void* stream) {

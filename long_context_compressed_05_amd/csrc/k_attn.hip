@@ -55,6 +55,9 @@ struct AttnArgs {
 struct RowCtx {
   int b;
   int64_t t, n_vis_a, pool_base, tok_base;
+#ifdef CSA_DEBUG
+  int64_t P;  // pooled rows of the sequence (the range a CSA index must fall in)
+#endif
 };
 
 __device__ __forceinline__ RowCtx row_ctx(const AttnArgs& a, int64_t row) {
@@ -63,6 +66,9 @@ __device__ __forceinline__ RowCtx row_ctx(const AttnArgs& a, int64_t row) {
   c.t = a.q_pos[row];
   c.pool_base = a.pool_off[c.b];
   c.tok_base = a.tok_off[c.b];
+#ifdef CSA_DEBUG
+  c.P = a.pool_off[c.b + 1] - c.pool_base;
+#endif
   if (a.hca) {
     const int64_t P = a.pool_off[c.b + 1] - c.pool_base;
     const int64_t v = (c.t + 1) / a.m_pool;
@@ -79,6 +85,12 @@ __device__ __forceinline__ const uint8_t* key_row(const AttnArgs& a, const RowCt
   if (p < a.seg_a) {
     if (a.hca) return p < c.n_vis_a ? a.kv_pool + (size_t)(c.pool_base + p) * row_bytes : nullptr;
     const int32_t j = a.idx[row * a.seg_a + p];
+#ifdef CSA_DEBUG
+    if (j >= c.P) {
+      debug_violation();
+      return nullptr;
+    }
+#endif
     return j >= 0 ? a.kv_pool + (size_t)(c.pool_base + j) * row_bytes : nullptr;
   }
   const int64_t u = c.t - a.W + 1 + (p - a.seg_a);
@@ -114,6 +126,12 @@ __global__ __launch_bounds__(256) void k_attn_bf16(AttnArgs a) {
     if (p < a.seg_a) {
       if (a.hca) return p < c.n_vis_a ? a.kv_pool + (size_t)(c.pool_base + p) * RB : nullptr;
       const int32_t j = idx_s[p - p_begin];
+#ifdef CSA_DEBUG
+      if (j >= c.P) {
+        debug_violation();
+        return nullptr;
+      }
+#endif
       return j >= 0 ? a.kv_pool + (size_t)(c.pool_base + j) * RB : nullptr;
     }
     const int64_t u = c.t - a.W + 1 + (p - a.seg_a);
@@ -376,6 +394,10 @@ AttnPlan plan_attn(int64_t n_q, int64_t list_len, int H) {
   p.ws_bytes = s > 1 ? (size_t)n_q * s * H * (128 + 2) * 4 + 256 : 0;
   return p;
 }
+
+#ifdef CSA_DEBUG
+unsigned long long debug_take_attn() { return debug_take_here(); }
+#endif
 
 int launch_attn(bool bf16, bool hca, int n_seq, int64_t n_q, const int64_t* tok_off,
                 const int64_t* q_off, const int64_t* q_pos, const int64_t* pool_off, int m_pool,

@@ -1266,6 +1266,12 @@ __device__ __forceinline__ void attend_item(const FCtx& x, int r, int kind, int 
     if (kind == 0) {
       const int32_t j = idx_s[p - pb32];
       if (j < 0) return nullptr;
+#ifdef CSA_DEBUG
+      if (j >= (int32_t)f.n_vis) {
+        debug_violation();
+        return nullptr;
+      }
+#endif
       return paged ? a.kv_pool + (uint64_t)(uint32_t)idx_p[p - pb32] * RB : pooled(j);
     }
     if (p < split) {
@@ -1594,6 +1600,10 @@ static int steal_polls() {
 }
 
 static int split_count(int64_t len, int64_t size) { return len <= 0 ? 0 : (int)((len + size - 1) / size); }
+
+#ifdef CSA_DEBUG
+unsigned long long debug_take_fused() { return debug_take_here(); }
+#endif
 
 FusedPlan plan_fused(int64_t R, int64_t max_pool, int64_t max_hpool, int H, int k, int W, int W_hca) {
   FusedPlan p{};

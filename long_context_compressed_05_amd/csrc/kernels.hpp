@@ -113,4 +113,10 @@ int launch_fused(int R, const int64_t* tok_off, const int64_t* q_pos, const int6
                  const void* kv_pool, const void* kv_hpool, const void* kv_raw, int32_t* idx, void* csa_out,
                  float* csa_lse, void* hca_out, float* hca_lse, void* ws, hipStream_t stream);
 
+#ifdef CSA_DEBUG
+// violations counted by the debug checks since the last call, cleared (synchronous)
+unsigned long long debug_take_attn();
+unsigned long long debug_take_fused();
+#endif
+
 }  // namespace csa

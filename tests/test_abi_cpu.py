@@ -147,6 +147,20 @@ def test_index_topk_validation_and_workspace():
         assert call() == csa.CSA_ERR_DEVICE
 
 
+def test_debug_checks_need_a_debug_build():
+    L = csa.lib()
+    n = ctypes.c_uint64(7)
+    assert L.csa_debug_checks(None) == csa.CSA_ERR_INVALID
+    if csa.LIB_PATH.endswith("libcsa.so"):
+        assert L.csa_debug_checks(ctypes.byref(n)) == csa.CSA_ERR_UNSUPPORTED
+        assert n.value == 0
+    dbg = os.path.join(os.path.dirname(csa.LIB_PATH), "libcsa_debug.so")
+    if os.path.exists(dbg):  # the debug build exports the same symbols
+        D = ctypes.CDLL(dbg)
+        for name in declared_functions():
+            assert hasattr(D, name), f"libcsa_debug.so does not export {name}"
+
+
 def test_index_topk_bf16_validation():
     L = csa.lib()
     b = _batch()
