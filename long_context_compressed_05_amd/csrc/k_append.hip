@@ -27,9 +27,10 @@
 //                  cache and the logit ring, its new tokens straight from the
 //                  inputs (nothing this kernel reads is written by it).  A
 //                  short block is pooled by one thread per 16 bytes of
-//                  channels; a long one by a workgroup whose threads pool its
-//                  16-row segments in parallel and then fold them in order
-//                  (the bulk kernel's order, so the bits agree)
+//                  channels; a long one by several workgroups, each holding a
+//                  slice of the channels, whose threads pool its 16-row
+//                  segments in parallel and then fold them in order (the bulk
+//                  kernel's order, so the bits agree)
 //                  (and its last workgroups encode the completed blocks'
 //                  keys, a thread per 32-element part)
 //   k_append_tail  one workgroup per sequence: the newest min(n, ring)
@@ -64,6 +65,8 @@ struct AppendArgs {
   int nb_narrow;         // workgroups of the narrow items; each later workgroup pools one long block
   int nb_wide;           // workgroups of long blocks; the workgroups after them encode keys (a thread per part)
   int wide_par;          // long blocks: segments pooled in parallel (1) or in one thread each (0)
+  int wide_slices;       // k_append_pool: workgroups per long block (channel slices)
+  int wide_units;        // k_append_pool: 4-byte channel units per slice
 };
 
 __device__ __forceinline__ int64_t floordiv_blocks(int64_t p, int m) { return m > 0 ? p / m : 0; }
@@ -179,8 +182,13 @@ __global__ __launch_bounds__(256) void k_append_pool(AppendArgs a) {
                       a.k_codes + kr * (a.kdim / 2) + (size_t)p * 16, a.k_scales + kr * parts + p);
     return;
   }
-  // one long block per workgroup: [long CSA blocks | long HCA blocks]
-  int64_t w = (int64_t)blockIdx.x - a.nb_narrow;
+  // long blocks: [long CSA blocks | long HCA blocks], each split into
+  // wide_slices workgroups by 4-byte channel units; a workgroup pools every
+  // 16-row segment of its units in parallel (each thread loading all of its
+  // segment's rows before any arithmetic), then folds them in order
+  const int64_t wb = (int64_t)blockIdx.x - a.nb_narrow;
+  int64_t w = wb / a.wide_slices;
+  const int slice = (int)(wb - w * a.wide_slices);
   bool hca;
   int64_t j;
   if (!csa_narrow && w < q.nc) {
@@ -195,29 +203,61 @@ __global__ __launch_bounds__(256) void k_append_pool(AppendArgs a) {
   const int m = hca ? a.m_hca : a.m;
   const int64_t pcap = hca ? a.hpool_off[b + 1] - a.hpool_off[b] : a.pool_off[b + 1] - a.pool_off[b];
   if (j >= pcap || (j + 1) * m > q.cap) return;  // uniform over the workgroup
+  constexpr int N4 = Vec4<BF16>::N;
+  const int units = (int)(row / 4);
+  const int u0 = slice * a.wide_units;
+  const int nu = units - u0 < a.wide_units ? units - u0 : a.wide_units;
+  if (nu <= 0) return;
   uint8_t* out = hca ? a.hpooled + (size_t)(a.hpool_off[b] + j) * row : a.pooled + (size_t)(a.pool_off[b] + j) * row;
   const int segs = (m + kPoolSeg - 1) / kPoolSeg;
-  if (!a.wide_par) {
-    for (int g = threadIdx.x; g < groups; g += blockDim.x) {
-      const BlockRows<BF16> br = block_rows<BF16>(a, b, q, j, m, g);
-      pool_block<BF16>(m, [&](int i) { return br.x(i); }, [&](int i) { return br.z(i); }, out + (size_t)g * 16);
-    }
-    return;
-  }
-  // every segment's state -> LDS [segs][groups], then each channel group folds them in order
+  const uint8_t* xold = a.kv_raw + (size_t)q.r0 * row;
+  const uint8_t* zring = a.z_tail + (size_t)b * a.ring * row;
+  const uint8_t* xnew = a.x_new + (size_t)a.new_off[b] * row;
+  const uint8_t* znew = a.z_new + (size_t)a.new_off[b] * row;
+  const int64_t p_blk = j * m;
+  const int slot0 = (int)(p_blk % a.ring);  // rows of the block are < m <= ring apart: one wrap at most
   extern __shared__ __align__(16) uint8_t ap_sm[];
-  PoolState<BF16>* part = reinterpret_cast<PoolState<BF16>*>(ap_sm);
-  for (int t = threadIdx.x; t < segs * groups; t += blockDim.x) {
-    const int sg = t / groups, g = t - sg * groups;
-    const BlockRows<BF16> br = block_rows<BF16>(a, b, q, j, m, g);
-    const int i0 = sg * kPoolSeg, i1 = i0 + kPoolSeg < m ? i0 + kPoolSeg : m;
-    pool_segment<BF16>(i0, i1, [&](int i) { return br.x(i); }, [&](int i) { return br.z(i); }, part[t]);
+  PoolSt<N4>* part = reinterpret_cast<PoolSt<N4>*>(ap_sm);
+  for (int task = threadIdx.x; task < segs * nu; task += blockDim.x) {
+    const int sg = task / nu, u = u0 + (task - sg * nu);
+    const int i0 = sg * kPoolSeg;
+    const int ns = m - i0 < kPoolSeg ? m - i0 : kPoolSeg;
+    uint32_t xr[kPoolSeg], zr[kPoolSeg];
+#pragma unroll
+    for (int i = 0; i < kPoolSeg; ++i) {
+      const int ii = i0 + (i < ns ? i : ns - 1);  // rows past the segment load its last row (unused)
+      const int64_t p = p_blk + ii;
+      const int so = slot0 + ii;
+      const int slot = so < a.ring ? so : so - a.ring;
+      const bool old = p < q.L0;
+      xr[i] = *reinterpret_cast<const uint32_t*>((old ? xold + (size_t)p * row : xnew + (size_t)(p - q.L0) * row) +
+                                                 (size_t)u * 4);
+      zr[i] = *reinterpret_cast<const uint32_t*>((old ? zring + (size_t)slot * row : znew + (size_t)(p - q.L0) * row) +
+                                                 (size_t)u * 4);
+    }
+    PoolSt<N4> st;
+    pool_reset(st);
+#pragma unroll
+    for (int c0 = 0; c0 < kPoolSeg; c0 += 8) {
+      if (c0 < ns) {
+        float zz[8][N4], xx[8][N4];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          Vec4<BF16>::load(zr[c0 + i], zz[i]);
+          Vec4<BF16>::load(xr[c0 + i], xx[i]);
+        }
+        pool_chunk(st, zz, xx, ns - c0 < 8 ? ns - c0 : 8);
+      }
+    }
+    part[task] = st;
   }
   __syncthreads();
-  for (int g = threadIdx.x; g < groups; g += blockDim.x) {
-    PoolState<BF16> st = part[g];
-    for (int sg = 1; sg < segs; ++sg) pool_fold(st, part[sg * groups + g]);
-    pool_store<BF16>(st, out + (size_t)g * 16);
+  for (int uu = threadIdx.x; uu < nu; uu += blockDim.x) {
+    PoolSt<N4> st = part[uu];
+    for (int sg = 1; sg < segs; ++sg) pool_fold(st, part[sg * nu + uu]);
+    float o[N4];
+    pool_result(st, o);
+    *reinterpret_cast<uint32_t*>(out + (size_t)(u0 + uu) * 4) = Vec4<BF16>::pack(o);
   }
 }
 
@@ -538,7 +578,6 @@ int launch_append(bool bf16, int n_seq, int width, const int64_t* tok_off, int64
   const size_t state = bf16 ? sizeof(PoolState<true>) : sizeof(PoolState<false>);
   const size_t lds = (size_t)((max_m + kPoolSeg - 1) / kPoolSeg) * groups * state;
   a.wide_par = wide > 0 && lds <= 64 * 1024 ? 1 : 0;
-  const size_t lds_launch = a.wide_par ? lds : 0;
   // a short append (at most kOneMax new tokens per sequence, long blocks' segment
   // states in 64 KB): one launch, a workgroup per sequence
   constexpr int64_t kOneMax = 64;
@@ -564,10 +603,22 @@ int launch_append(bool bf16, int n_seq, int width, const int64_t* tok_off, int64
                                  dim3(256), wide > 0 ? lds : 0, stream, a);
     return e1 == hipSuccess && hipGetLastError() == hipSuccess ? 0 : -1;
   }
-  a.nb_wide = (int)wide;
+  // long blocks: slices of wide_units channel units, segs x units tasks per
+  // 256-thread workgroup (more segments than 256: a loop)
+  {
+    const int units = groups * 4;
+    const int segs_max = (max_m + kPoolSeg - 1) / kPoolSeg;
+    int U = 256 / segs_max;
+    U = U < 1 ? 1 : (U > units ? units : U);
+    a.wide_units = U;
+    a.wide_slices = (units + U - 1) / U;
+  }
+  a.nb_wide = (int)(wide * a.wide_slices);
+  const size_t wide_lds = wide > 0 ? (size_t)((max_m + kPoolSeg - 1) / kPoolSeg) * a.wide_units *
+                                         (bf16 ? sizeof(PoolSt<2>) : sizeof(PoolSt<1>)) : 0;
   const int64_t nb_keys = kvec ? (nb_c * (kdim / 32) + 255) / 256 : 0;
-  dim3 g1((unsigned)(a.nb_narrow + wide + nb_keys), (unsigned)n_seq);
-  hipError_t e = launch(9, kProfStart, bf16 ? k_append_pool<true> : k_append_pool<false>, g1, dim3(256), lds_launch,
+  dim3 g1((unsigned)(a.nb_narrow + a.nb_wide + nb_keys), (unsigned)n_seq);
+  hipError_t e = launch(9, kProfStart, bf16 ? k_append_pool<true> : k_append_pool<false>, g1, dim3(256), wide_lds,
                         stream, a);
   if (e == hipSuccess)
     e = launch(9, kProfStop, bf16 ? k_append_tail<true> : k_append_tail<false>, dim3((unsigned)n_seq), dim3(256), 0,
