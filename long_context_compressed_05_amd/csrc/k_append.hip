@@ -283,9 +283,10 @@ __device__ __forceinline__ void append_keys(const AppendArgs& a, int b, const Ap
 }
 
 template <bool BF16>
-__global__ __launch_bounds__(256) void k_append_tail(AppendArgs a) {
+__global__ __launch_bounds__(1024) void k_append_tail(AppendArgs a) {
   constexpr int N = Vec16<BF16>::N;
   constexpr int ES = BF16 ? 2 : 4;
+  constexpr int kPer = 4;  // 16-byte pieces per thread and pass, all loaded before any store
   const int b = blockIdx.x;
   const int groups = a.width / N;
   const size_t row = (size_t)a.width * ES;
@@ -293,12 +294,28 @@ __global__ __launch_bounds__(256) void k_append_tail(AppendArgs a) {
   const int64_t n = a.new_off[b + 1] - a.new_off[b];
   const int64_t first = n > a.ring ? n - a.ring : 0;  // older new tokens are overwritten in the ring anyway
   const int64_t work = (n - first) * groups;
-  for (int64_t t = threadIdx.x; t < work; t += blockDim.x) {
-    const int64_t i = first + t / groups;
-    const int g = (int)(t % groups);
-    const int64_t p = L0 + i;
-    *reinterpret_cast<uint4*>(a.z_tail + ((size_t)b * a.ring + (size_t)(p % a.ring)) * row + (size_t)g * 16) =
-        *reinterpret_cast<const uint4*>(a.z_new + (size_t)(a.new_off[b] + i) * row + (size_t)g * 16);
+  const int ring_slot0 = (int)((L0 + first) % a.ring);  // piece t: token first + t / groups, slot one wrap away
+  const uint8_t* src = a.z_new + (size_t)(a.new_off[b] + first) * row;
+  uint8_t* ring = a.z_tail + (size_t)b * a.ring * row;
+  for (int64_t t0 = threadIdx.x; t0 < work; t0 += (int64_t)kPer * blockDim.x) {
+    uint4 v[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int64_t t = t0 + (int64_t)k * blockDim.x;
+      const int64_t tt = t < work ? t : work - 1;
+      const int64_t i = tt / groups;
+      v[k] = *reinterpret_cast<const uint4*>(src + (size_t)i * row + (size_t)(tt - i * groups) * 16);
+    }
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int64_t t = t0 + (int64_t)k * blockDim.x;
+      if (t < work) {
+        const int64_t i = t / groups;
+        const int64_t so = ring_slot0 + i;  // i < ring: one wrap at most
+        const int64_t slot = so < a.ring ? so : so - a.ring;
+        *reinterpret_cast<uint4*>(ring + (size_t)slot * row + (size_t)(t - i * groups) * 16) = v[k];
+      }
+    }
   }
   __syncthreads();  // every thread has read len[b]
   if (threadIdx.x == 0) a.len[b] = L0 + n;
@@ -621,7 +638,7 @@ int launch_append(bool bf16, int n_seq, int width, const int64_t* tok_off, int64
   hipError_t e = launch(9, kProfStart, bf16 ? k_append_pool<true> : k_append_pool<false>, g1, dim3(256), wide_lds,
                         stream, a);
   if (e == hipSuccess)
-    e = launch(9, kProfStop, bf16 ? k_append_tail<true> : k_append_tail<false>, dim3((unsigned)n_seq), dim3(256), 0,
+    e = launch(9, kProfStop, bf16 ? k_append_tail<true> : k_append_tail<false>, dim3((unsigned)n_seq), dim3(1024), 0,
                stream, a);
   return e == hipSuccess && hipGetLastError() == hipSuccess ? 0 : -1;
 }
