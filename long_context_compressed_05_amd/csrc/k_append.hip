@@ -61,8 +61,9 @@ struct AppendArgs {
   uint8_t* k_scales;        // [sum P][kdim / 32]
   int kdim;
   int width, ring, m, m_hca;
-  int64_t narrow_items;  // per sequence, at most: rows to copy + blocks of at most kPoolSeg rows
-  int nb_narrow;         // workgroups of the narrow items; each later workgroup pools one long block
+  int64_t narrow_items;  // per sequence, at most: blocks of at most kPoolSeg rows (k_append_one: + rows to copy)
+  int nb_copy;           // k_append_pool: workgroups copying the new rows (first in the grid)
+  int nb_narrow;         // workgroups of the short blocks; then the long blocks' and the keys' workgroups
   int nb_wide;           // workgroups of long blocks; the workgroups after them encode keys (a thread per part)
   int wide_par;          // long blocks: segments pooled in parallel (1) or in one thread each (0)
   int wide_slices;       // k_append_pool: workgroups per long block (channel slices)
@@ -134,19 +135,37 @@ __global__ __launch_bounds__(256) void k_append_pool(AppendArgs a) {
   const size_t row = (size_t)a.width * ES;
   const AppendSeq q = append_seq(a, b);
   const bool csa_narrow = a.m <= kPoolSeg, hca_narrow = a.m_hca <= kPoolSeg;
-  if ((int)blockIdx.x < a.nb_narrow) {
-    // narrow items: [rows to copy | short CSA blocks | short HCA blocks], a thread per 16 bytes
-    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if ((int)blockIdx.x < a.nb_copy) {
+    // the new rows -> the raw cache: kCopyPer 16-byte pieces per thread, all loaded before any store
+    constexpr int kCopyPer = 4;
+    const int64_t pieces = q.n * groups;
+    const int64_t t0 = (int64_t)blockIdx.x * blockDim.x * kCopyPer + threadIdx.x;
+    if (t0 >= pieces) return;
+    const uint8_t* src = a.x_new + (size_t)a.new_off[b] * row;
+    uint8_t* dst = a.kv_raw + (size_t)(q.r0 + q.L0) * row;
+    uint4 v[kCopyPer];
+#pragma unroll
+    for (int k = 0; k < kCopyPer; ++k) {
+      const int64_t t = t0 + (int64_t)k * blockDim.x;
+      const int64_t tt = t < pieces ? t : pieces - 1;
+      const int64_t i = tt / groups;
+      v[k] = *reinterpret_cast<const uint4*>(src + (size_t)i * row + (size_t)(tt - i * groups) * 16);
+    }
+#pragma unroll
+    for (int k = 0; k < kCopyPer; ++k) {
+      const int64_t t = t0 + (int64_t)k * blockDim.x;
+      const int64_t i = t / groups;
+      if (t < pieces && q.L0 + i < q.cap)
+        *reinterpret_cast<uint4*>(dst + (size_t)i * row + (size_t)(t - i * groups) * 16) = v[k];
+    }
+    return;
+  }
+  if ((int)blockIdx.x < a.nb_copy + a.nb_narrow) {
+    // short blocks: [short CSA blocks | short HCA blocks], a thread per 16 bytes
+    const int64_t gid = (int64_t)(blockIdx.x - a.nb_copy) * blockDim.x + threadIdx.x;
     int64_t item = gid / groups;
     const int g = (int)(gid - item * groups);
     if (item >= a.narrow_items) return;
-    if (item < q.n) {
-      if (q.L0 + item < q.cap)
-        *reinterpret_cast<uint4*>(a.kv_raw + (size_t)(q.r0 + q.L0 + item) * row + (size_t)g * 16) =
-            *reinterpret_cast<const uint4*>(a.x_new + (size_t)(a.new_off[b] + item) * row + (size_t)g * 16);
-      return;
-    }
-    item -= q.n;
     bool hca;
     int64_t j;
     if (csa_narrow && item < q.nc) {
@@ -168,10 +187,10 @@ __global__ __launch_bounds__(256) void k_append_pool(AppendArgs a) {
             (size_t)g * 16);
     return;
   }
-  if ((int)blockIdx.x >= a.nb_narrow + a.nb_wide) {  // keys: a thread per 32-element part of a completed block
+  if ((int)blockIdx.x >= a.nb_copy + a.nb_narrow + a.nb_wide) {  // keys: a thread per 32-element part
     if (!a.kvec) return;
     const int parts = a.kdim / 32;
-    const int64_t t = (int64_t)(blockIdx.x - a.nb_narrow - a.nb_wide) * blockDim.x + threadIdx.x;
+    const int64_t t = (int64_t)(blockIdx.x - a.nb_copy - a.nb_narrow - a.nb_wide) * blockDim.x + threadIdx.x;
     const int64_t i = t / parts;
     const int p = (int)(t - i * parts);
     const int64_t r0 = a.kvec_off[b];
@@ -186,7 +205,7 @@ __global__ __launch_bounds__(256) void k_append_pool(AppendArgs a) {
   // wide_slices workgroups by 4-byte channel units; a workgroup pools every
   // 16-row segment of its units in parallel (each thread loading all of its
   // segment's rows before any arithmetic), then folds them in order
-  const int64_t wb = (int64_t)blockIdx.x - a.nb_narrow;
+  const int64_t wb = (int64_t)blockIdx.x - a.nb_copy - a.nb_narrow;
   int64_t w = wb / a.wide_slices;
   const int slice = (int)(wb - w * a.wide_slices);
   bool hca;
@@ -631,10 +650,15 @@ int launch_append(bool bf16, int n_seq, int width, const int64_t* tok_off, int64
     a.wide_slices = (units + U - 1) / U;
   }
   a.nb_wide = (int)(wide * a.wide_slices);
+  // the multi-kernel path copies rows in workgroups of their own (4 pieces per thread)
+  // and numbers the short blocks alone
+  a.narrow_items -= max_new;
+  a.nb_narrow = (int)((a.narrow_items * groups + 255) / 256);
+  a.nb_copy = (int)((max_new * groups + 1023) / 1024);
   const size_t wide_lds = wide > 0 ? (size_t)((max_m + kPoolSeg - 1) / kPoolSeg) * a.wide_units *
                                          (bf16 ? sizeof(PoolSt<2>) : sizeof(PoolSt<1>)) : 0;
   const int64_t nb_keys = kvec ? (nb_c * (kdim / 32) + 255) / 256 : 0;
-  dim3 g1((unsigned)(a.nb_narrow + a.nb_wide + nb_keys), (unsigned)n_seq);
+  dim3 g1((unsigned)(a.nb_copy + a.nb_narrow + a.nb_wide + nb_keys), (unsigned)n_seq);
   hipError_t e = launch(9, kProfStart, bf16 ? k_append_pool<true> : k_append_pool<false>, g1, dim3(256), wide_lds,
                         stream, a);
   if (e == hipSuccess)
