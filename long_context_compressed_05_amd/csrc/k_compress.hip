@@ -41,6 +41,60 @@ __global__ __launch_bounds__(256) void k_compress(const int64_t* __restrict__ to
       out + (size_t)(pool_off[b] + j) * row_bytes + (size_t)g * 16);
 }
 
+// Short blocks (m <= MAXM <= 8): each thread pools the same 16 bytes of
+// channels of BPT consecutive blocks, loading all of their rows before any
+// arithmetic, so a thread keeps BPT * 2m loads in flight and the grid needs
+// BPT times fewer workgroups.  Same per-channel arithmetic as pool_block
+// (pool_core.hpp).
+template <bool BF16, int BPT, int MAXM>
+__global__ __launch_bounds__(256) void k_compress_short(const int64_t* __restrict__ tok_off,
+                                                        const int64_t* __restrict__ pool_off, int m, int width,
+                                                        const uint8_t* __restrict__ x, const uint8_t* __restrict__ z,
+                                                        uint8_t* __restrict__ out) {
+  constexpr int N = Vec16<BF16>::N;
+  constexpr int ES = BF16 ? 2 : 4;
+  const int b = blockIdx.y;
+  const int64_t r0 = tok_off[b];
+  const int64_t L = tok_off[b + 1] - r0;
+  const int64_t cap = pool_off[b + 1] - pool_off[b];
+  const int64_t P = (L / m) < cap ? (L / m) : cap;
+  const int groups = width / N;
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t jq = gid / groups;
+  const int g = (int)(gid - jq * groups);
+  const int64_t j0 = jq * BPT;
+  if (j0 >= P) return;
+  const size_t row_bytes = (size_t)width * ES;
+  const uint8_t* xp = x + (size_t)r0 * row_bytes + (size_t)g * 16;
+  const uint8_t* zp = z + (size_t)r0 * row_bytes + (size_t)g * 16;
+  uint4 xr[BPT][MAXM], zr[BPT][MAXM];
+#pragma unroll
+  for (int k = 0; k < BPT; ++k) {
+    const int64_t j = j0 + k < P ? j0 + k : P - 1;  // blocks past P load the last one (not stored)
+#pragma unroll
+    for (int i = 0; i < MAXM; ++i) {
+      const int ii = i < m ? i : m - 1;
+      const size_t off = (size_t)(j * m + ii) * row_bytes;
+      xr[k][i] = *reinterpret_cast<const uint4*>(xp + off);
+      zr[k][i] = *reinterpret_cast<const uint4*>(zp + off);
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < BPT; ++k) {
+    if (j0 + k >= P) break;
+    PoolState<BF16> st;
+    pool_reset(st);
+    float zz[8][N], xx[8][N];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      Vec16<BF16>::load(&zr[k][i < MAXM ? i : MAXM - 1], zz[i]);
+      Vec16<BF16>::load(&xr[k][i < MAXM ? i : MAXM - 1], xx[i]);
+    }
+    pool_chunk(st, zz, xx, m);
+    pool_store<BF16>(st, out + (size_t)(pool_off[b] + j0 + k) * row_bytes + (size_t)g * 16);
+  }
+}
+
 int launch_compress(bool bf16, int n_seq, const int64_t* tok_off, const int64_t* pool_off,
                     int64_t max_len, int m, int width, const void* x, const void* z, void* out,
                     hipStream_t stream) {
@@ -48,10 +102,21 @@ int launch_compress(bool bf16, int n_seq, const int64_t* tok_off, const int64_t*
   const int64_t groups = width / N;
   const int64_t max_blocks = max_len / m;
   if (max_blocks == 0 || n_seq == 0) return 0;
-  const int64_t threads = max_blocks * groups;
-  dim3 grid((unsigned)((threads + 255) / 256), (unsigned)n_seq);
-  const hipError_t e = launch(5, kProfBoth, bf16 ? k_compress<true> : k_compress<false>, grid, dim3(256), 0, stream,
-                              tok_off, pool_off, m, width, (const uint8_t*)x, (const uint8_t*)z, (uint8_t*)out);
+  hipError_t e;
+  if (m <= 8) {
+    constexpr int BPT = 2;
+    const int64_t threads = (max_blocks + BPT - 1) / BPT * groups;
+    dim3 grid((unsigned)((threads + 255) / 256), (unsigned)n_seq);
+    auto k = m <= 4 ? (bf16 ? k_compress_short<true, BPT, 4> : k_compress_short<false, BPT, 4>)
+                    : (bf16 ? k_compress_short<true, BPT, 8> : k_compress_short<false, BPT, 8>);
+    e = launch(5, kProfBoth, k, grid, dim3(256), 0, stream, tok_off, pool_off, m, width, (const uint8_t*)x,
+               (const uint8_t*)z, (uint8_t*)out);
+  } else {
+    const int64_t threads = max_blocks * groups;
+    dim3 grid((unsigned)((threads + 255) / 256), (unsigned)n_seq);
+    e = launch(5, kProfBoth, bf16 ? k_compress<true> : k_compress<false>, grid, dim3(256), 0, stream, tok_off,
+               pool_off, m, width, (const uint8_t*)x, (const uint8_t*)z, (uint8_t*)out);
+  }
   return e == hipSuccess && hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
