@@ -401,18 +401,40 @@ def copy_calibration(torch):
     print(json.dumps({"copy_bytes": COPY_BYTES, "launches": 5}), flush=True)
 
 
+def release_lines(lines, name="<source>"):
+    """The lines of a kernel source that can change its release build: not
+    blank, not whole-line comments, not inside #ifdef CSA_DEBUG blocks (code
+    compiled only into the debug library)."""
+    skip = 0  # depth inside a CSA_DEBUG block
+    for line in lines:
+        t = line.strip()
+        if skip:
+            if t.startswith("#if"):
+                skip += 1
+            elif t.startswith("#endif"):
+                skip -= 1
+            elif t.startswith("#el") and skip == 1:
+                raise ValueError(f"{name}: #else or #elif in a CSA_DEBUG block")
+            continue
+        if t == "#ifdef CSA_DEBUG":
+            skip = 1
+            continue
+        if t and not t.startswith("//"):
+            yield line.rstrip()
+    if skip:
+        raise ValueError(f"{name}: unterminated CSA_DEBUG block")
+
+
 def kernel_source_digest(kernel: str) -> str:
+    """sha256 over the release lines of the sources `kernel` is built from."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)), "long_context_compressed_05_amd", "csrc")
     for f in KERNEL_SOURCES[kernel]:
         with open(os.path.join(csrc, f)) as fh:
-            # whole-line comments and blank lines do not change the kernel
-            for line in fh:
-                t = line.strip()
-                if t and not t.startswith("//"):
-                    h.update(line.rstrip().encode())
-                    h.update(b"\n")
+            for line in release_lines(fh, f):
+                h.update(line.encode())
+                h.update(b"\n")
     return h.hexdigest()
 
 
