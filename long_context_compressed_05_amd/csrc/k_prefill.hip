@@ -118,14 +118,35 @@ __device__ __forceinline__ uint32_t pf_key(const v16f& acc, int s) {
   return __float_as_uint((r0 + r1) + (r2 + r3));
 }
 
+// The candidate test key >= tau of score index s, in 7 operations instead of
+// the key's 8.  For reals, max(a, 0) + max(b, 0) = max(a + b, a, b) whenever
+// that is positive, and the sum is 0 otherwise; the same holds for the rounded
+// sums (rounding is monotonic, and a + b rounds to a when b is 0), so
+//   v = max3(p01 + p23, p01, p23),  p01 = max3(x0 + x1, x0, x1)  (p23 alike)
+// equals the key's value (x0 + x1 ... in the key's order) when it is positive
+// and is <= 0 exactly when the key is 0.  The maxima compare bit patterns as
+// signed integers: right whenever one operand is positive, and a non-positive
+// result is all that matters otherwise.  The test is then v >= tau as signed
+// bit patterns, with tau = 0 (every key passes) mapped to INT_MIN
+// (pf_tau_signed).
+__device__ __forceinline__ int pf_tau_signed(uint32_t tau) {
+  return tau == 0u ? (int)0x80000000u : (int)(tau < 0x7fffffffu ? tau : 0x7fffffffu);
+}
+__device__ __forceinline__ int pf_relu_sum_bits(const v16f& acc, int s) {
+  const float x0 = acc[4 * s + 0], x1 = acc[4 * s + 1], x2 = acc[4 * s + 2], x3 = acc[4 * s + 3];
+  const int p01 = max(max(__float_as_int(x0 + x1), __float_as_int(x0)), __float_as_int(x1));
+  const int p23 = max(max(__float_as_int(x2 + x3), __float_as_int(x2)), __float_as_int(x3));
+  return max(max(__float_as_int(__int_as_float(p01) + __int_as_float(p23)), p01), p23);
+}
+
 // candidate mask of score index E & 3 of MFMA output c (this lane's query
 // E = 4 o + s: the query of lanes 0-31 is slot 2E, of lanes 32-63 slot 2E + 1);
-// WHOLE: every query sees the tile's 32 keys
+// WHOLE: every query sees the tile's 32 keys; tq: thresholds by pf_tau_signed
 template <int E, bool WHOLE>
 __device__ __forceinline__ uint64_t pf_mask(const v16f& c, int j, const int (&nq)[kPfRows / 2],
-                                            const uint32_t (&tq)[kPfRows / 2]) {
-  const uint32_t key = pf_key(c, E & 3);
-  return __builtin_amdgcn_ballot_w64(WHOLE ? key >= tq[E] : (j < nq[E] && key >= tq[E]));
+                                            const int (&tq)[kPfRows / 2]) {
+  const int v = pf_relu_sum_bits(c, E & 3);
+  return __builtin_amdgcn_ballot_w64(WHOLE ? v >= tq[E] : (j < nq[E] && v >= tq[E]));
 }
 
 // one tile's 16 candidate words (query slot L in lane L): the 8 ballots' halves
@@ -135,7 +156,7 @@ __device__ __forceinline__ uint64_t pf_mask(const v16f& c, int j, const int (&nq
 template <bool WHOLE>
 __device__ __forceinline__ uint32_t pf_tile_word(const v8i (&av)[2], const int (&asc)[2], const uint4& kc, int ks,
                                                  int j, const int (&nq)[kPfRows / 2],
-                                                 const uint32_t (&tq)[kPfRows / 2]) {
+                                                 const int (&tq)[kPfRows / 2]) {
   uint64_t m[8];
   {
     const v16f c = pf_mfma(av[0], asc[0], kc, ks);
@@ -354,14 +375,14 @@ __global__ __launch_bounds__(256) void k_pf_score(PfArgs a) {
   const int64_t jr0 = (int64_t)blockIdx.x * a.kw;
   // this lane's 16 queries: slot 8u + 2s + lane/32 of A operand u, score index s
   constexpr int kE = kPfRows / 2;
-  uint32_t tq[kE];
+  int tq[kE];  // thresholds by pf_tau_signed
   int nq[kE];
   int nmax = 0, nmin = 0x7fffffff;
 #pragma unroll
   for (int e = 0; e < kE; ++e) {
     const int q = 8 * (e >> 2) + 2 * (e & 3) + (lane >> 5);
     const bool v = q < nrows;
-    tq[e] = v ? a.tau[row0 + q] : 0xffffffffu;
+    tq[e] = pf_tau_signed(v ? a.tau[row0 + q] : 0xffffffffu);
     nq[e] = v ? (int)pf_nvis(a.q_pos[row0 + q], a.m, P) : 0;
     nmax = nq[e] > nmax ? nq[e] : nmax;
     nmin = v && nq[e] < nmin ? nq[e] : nmin;
@@ -386,6 +407,29 @@ __global__ __launch_bounds__(256) void k_pf_score(PfArgs a) {
   for (int ub = 0; ub < kT; ub += kB) {
     uint4 kc[kB];
     int ks[kB];
+    // a batch whose tiles every query sees whole: straight-line code (no
+    // branch between its tiles, so one tile's MFMAs overlap the previous
+    // tile's epilogue), its 16 words per tile stored after the batch
+    const int64_t jlast = jr0 + (int64_t)(wave + 4 * (ub + kB - 1)) * 32;
+    if (ub + kB <= kT && jlast + 32 <= (int64_t)nmin) {  // uniform per wave
+#pragma unroll
+      for (int u = 0; u < kB; ++u) {
+        const int64_t j = jr0 + (int64_t)(wave + 4 * (ub + u)) * 32 + (lane & 31);
+        kc[u] = *reinterpret_cast<const uint4*>(a.k_codes + (pbase + j) * 32 + kb * 16);
+        ks[u] = a.k_scales[(pbase + j) * 2 + kb];
+      }
+      uint32_t words[kB];
+#pragma unroll
+      for (int u = 0; u < kB; ++u) {
+        const int j = (int)(jr0 + (int64_t)(wave + 4 * (ub + u)) * 32) + (lane & 31);
+        words[u] = pf_tile_word<true>(av, asc, kc[u], ks[u], j, nq, tq);
+      }
+      if (lane < nrows && lane < kPfRows) {
+#pragma unroll
+        for (int u = 0; u < kB; ++u) bm_row[(jr0 >> 5) + wave + 4 * (ub + u)] = words[u];
+      }
+      continue;
+    }
 #pragma unroll
     for (int u = 0; u < kB; ++u) {
       const int64_t j = jr0 + (int64_t)(wave + 4 * (ub + u)) * 32 + (lane & 31);
