@@ -68,7 +68,7 @@ def _run_path(wl, host):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("m", [1, 3, 4, 128])
+@pytest.mark.parametrize("m", [1, 3, 4, 16, 48, 64, 128])
 def test_compress_parity(dtype, m):
     csa = _lib()
     wl = small_wl("compress", [5, 130, 517, 1030, 2049], [1] * 5, dtype=dtype, m=m, seed=21)
