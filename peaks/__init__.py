@@ -40,11 +40,12 @@ def lib():
     L = ctypes.CDLL(_SO)
     vp, ci, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
     L.peak_read.argtypes = [vp, sz, ci, ci, vp, vp, vp, vp]
+    L.peak_read_chunked.argtypes = [vp, sz, ci, ci, vp, vp, vp, vp]
     L.peak_mfma_fp4.argtypes = [ci, ci, vp, vp, vp, vp]
     L.peak_mfma_bf16.argtypes = [ci, ci, ci, vp, vp, vp, vp]
     L.peak_empty.argtypes = [ci, ci, vp, vp, vp, vp]
     L.peak_valu.argtypes = [ci, ci, ci, vp, vp, vp, vp]
-    for f in (L.peak_read, L.peak_mfma_fp4, L.peak_mfma_bf16, L.peak_empty, L.peak_valu):
+    for f in (L.peak_read, L.peak_read_chunked, L.peak_mfma_fp4, L.peak_mfma_bf16, L.peak_empty, L.peak_valu):
         f.restype = ci
     _lib = L
     return L

@@ -7,6 +7,8 @@
 //  - peak_read:      one pass over a buffer with 16-byte loads, each thread
 //                    keeping `unroll` loads in flight, a reduction kept live
 //                    through one word per workgroup (HBM read bandwidth);
+//                    peak_read_chunked: the same, each workgroup streaming a
+//                    contiguous span of the buffer;
 //  - peak_mfma_fp4:  back-to-back block-scaled FP4 MFMAs (32x32x64, the
 //                    indexer's instruction), four independent accumulators
 //                    per wave;
@@ -46,6 +48,35 @@ __global__ __launch_bounds__(256) void k_peak_read(const uint4* __restrict__ p, 
     acc ^= v.x ^ v.y ^ v.z ^ v.w;
   }
   // keep the loads live: one word per workgroup (lanes folded with atomics in LDS)
+  __shared__ uint32_t red;
+  if (threadIdx.x == 0) red = 0;
+  __syncthreads();
+  atomicXor(&red, acc);
+  __syncthreads();
+  if (threadIdx.x == 0) sink[blockIdx.x] = red;
+}
+
+// The same pass with each workgroup streaming its own contiguous span of
+// `chunk16` elements (the access pattern of the pooling kernels): per step a
+// thread loads U elements 256 apart, so a workgroup reads U x 4 KB in order.
+template <int U>
+__global__ __launch_bounds__(256) void k_peak_read_chunk(const uint4* __restrict__ p, size_t n16, size_t chunk16,
+                                                         uint32_t* sink) {
+  const size_t begin = (size_t)blockIdx.x * chunk16;
+  const size_t end = begin + chunk16 < n16 ? begin + chunk16 : n16;
+  uint32_t acc = 0;
+  size_t i = begin + threadIdx.x;
+  for (; i + (size_t)(U - 1) * 256 < end; i += (size_t)U * 256) {
+    uint4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = p[i + (size_t)u * 256];
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  for (; i < end; i += 256) {
+    const uint4 v = p[i];
+    acc ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
   __shared__ uint32_t red;
   if (threadIdx.x == 0) red = 0;
   __syncthreads();
@@ -161,6 +192,19 @@ int peak_read(const void* buf, size_t bytes, int grid, int unroll, uint32_t* sin
   if (unroll == 4) return go(k_peak_read<4>, dim3(grid), start, stop, stream, p, n16, sink);
   if (unroll == 16) return go(k_peak_read<16>, dim3(grid), start, stop, stream, p, n16, sink);
   return go(k_peak_read<8>, dim3(grid), start, stop, stream, p, n16, sink);
+}
+
+// the same with each workgroup reading its own contiguous span (bytes / grid,
+// rounded up to 4 KB)
+int peak_read_chunked(const void* buf, size_t bytes, int grid, int unroll, uint32_t* sink, void* start, void* stop,
+                      void* stream) {
+  if (!buf || !sink || bytes % 16 != 0 || grid < 1) return -1;
+  const uint4* p = (const uint4*)buf;
+  const size_t n16 = bytes / 16;
+  const size_t chunk16 = ((n16 + grid - 1) / grid + 255) / 256 * 256;
+  if (unroll == 4) return go(k_peak_read_chunk<4>, dim3(grid), start, stop, stream, p, n16, chunk16, sink);
+  if (unroll == 16) return go(k_peak_read_chunk<16>, dim3(grid), start, stop, stream, p, n16, chunk16, sink);
+  return go(k_peak_read_chunk<8>, dim3(grid), start, stop, stream, p, n16, chunk16, sink);
 }
 
 // sink: device, >= grid * 256 floats.  FLOPs = grid * 4 waves * iters * 4 * 2*32*32*64.
