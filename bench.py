@@ -854,6 +854,41 @@ def bench_prefill_chunk(torch, csa, synth, to_device, log, reps: int = 10, oracl
         step_ms.append(e0.elapsed_time(e1))
     us = {nm: float(np.median([a.elapsed_ms(b) for a, b in ev[nm]])) * 1e3 for nm in names if used[nm]}
     step_us = float(np.median(step_ms)) * 1e3
+    # the same step captured once in a HIP graph and replayed (no launch gaps
+    # between its kernels); every replay's outputs must equal the eager step's
+    graph = {}
+    try:
+        reset()
+        step()
+        torch.cuda.synchronize()
+        ref = [t_.clone() for t_ in (idx, co, cl, ho, hl)]
+        g = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        reset()
+        cap.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(g, stream=cap):
+                step()
+        torch.cuda.current_stream().wait_stream(cap)
+        torch.cuda.synchronize()
+        g_ms = []
+        for i in range(reps):
+            reset()
+            for t_ in (idx, co, cl, ho, hl):
+                t_.fill_(0)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            g_ms.append(e0.elapsed_time(e1))
+            if not all(torch.equal(a_, b_) for a_, b_ in zip((idx, co, cl, ho, hl), ref)):
+                raise RuntimeError(f"graph replay {i} differs from the eager step")
+        g_us = float(np.median(g_ms)) * 1e3
+        graph = {"step_us": round(g_us, 2), "prefill_tokens_per_s": round(n / (g_us * 1e-6), 1),
+                 "replays": reps, "check": "every replay's top-k, outputs and LSEs equal the eager step's"}
+    except Exception as e:  # reported, never silently replaced
+        graph = {"error": repr(e)}
     # algorithmic FLOPs
     q_pos = host["q_pos"]
     k_eff = np.minimum(wl.k, np.minimum((q_pos + 1) // wl.m, P_cap))
@@ -888,6 +923,7 @@ def bench_prefill_chunk(torch, csa, synth, to_device, log, reps: int = 10, oracl
                     "index_topk_us": round(index_us, 2),
                     "index_topk_queries_per_s": round(wl.n_q / (index_us * 1e-6), 1)},
         "timing": "median of %d eager steps; kernel times from events attached to each dispatch" % reps,
+        "graph": graph,
     }
     # the oracle beside it, on a few of the same queries (fp64 pooled caches prebuilt, not timed)
     try:

@@ -129,3 +129,78 @@ def test_prefill_chunk_ragged_small_end_to_end():
     host = synth.make_inputs(wl)
     res = run_prefill_chunk(csa, wl, host, T0)
     check_prefill_rows(wl, host, res, range(wl.n_q))
+
+
+def test_prefill_step_replays_from_a_hip_graph():
+    """The prefill step (append, index, CSA and HCA attention) captured once in
+    a HIP graph and replayed three times, with the caches' lengths and tail
+    rings reset and unrelated eager work between the replays: every replay's
+    top-k is bit-identical and its outputs and LSEs equal to the eager step's
+    (nothing in the step records a memset or allocates)."""
+    csa = _lib()
+    from long_context_compressed_05_amd.step import to_device
+    T0, n = 1030, 301
+    wl = synth.Workload("prefill_graph", [T0 + n], [T0], k=64, seed=62)
+    host = synth.make_inputs(wl)
+    dev = "cuda"
+    L = wl.lengths[0]
+    d = to_device({k: host[k] for k in ("kv", "z", "q", "qc", "qs", "w", "kc", "ks")})
+    kv_raw = torch.zeros_like(d["kv"])
+    kv_raw[:T0] = d["kv"][:T0]
+    P_cap, Ph_cap = L // wl.m, L // wl.m_hca
+    pooled = torch.zeros((P_cap, 2, wl.d), dtype=d["kv"].dtype, device=dev)
+    hpooled = torch.zeros((Ph_cap, 2, wl.d), dtype=d["kv"].dtype, device=dev)
+    t = lambda a: torch.from_numpy(np.asarray(a, dtype=np.int64)).to(dev)
+    tok0, pool_off, hpool_off, tok_off = t([0, T0]), t([0, P_cap]), t([0, Ph_cap]), t([0, L])
+    csa.csa_compress(d["kv"], d["z"], tok0, pool_off, T0, wl.m, pooled)
+    csa.csa_compress(d["kv"], d["z"], tok0, hpool_off, T0, wl.m_hca, hpooled)
+    ring = wl.m_hca
+    slots = np.array([T0 - ring + ((s - (T0 - ring)) % ring) for s in range(ring)])
+    tail0 = d["z"][t(slots)].reshape(1, ring, 2, wl.d).contiguous()
+    z_tail, len0 = tail0.clone(), t([T0])
+    length = len0.clone()
+    x_new, z_new, new_off = d["kv"][T0:].contiguous(), d["z"][T0:].contiguous(), t([0, n])
+    batch = csa.Batch.from_host(host["tok_off"], host["q_off"], host["q_pos"])
+    scale = 1 / math.sqrt(wl.d)
+    idx = torch.empty((wl.n_q, wl.k), dtype=torch.int32, device=dev)
+    co, ho = torch.empty_like(d["q"]), torch.empty_like(d["q"])
+    cl = torch.empty((wl.n_q, wl.H), dtype=torch.float32, device=dev)
+    hl = torch.empty_like(cl)
+    ws_i, ws_c, ws_h = csa.Workspace(), csa.Workspace(), csa.Workspace()
+
+    def step():
+        csa.csa_cache_append(x_new, z_new, new_off, n, tok_off, length, kv_raw, z_tail, pool_off, wl.m, pooled,
+                             hpool_off, wl.m_hca, hpooled)
+        csa.csa_index_topk(batch, pool_off, P_cap, wl.m, wl.k, d["qc"], d["qs"], d["w"], d["kc"], d["ks"], idx=idx,
+                           ws=ws_i)
+        csa.csa_sparse_attn(batch, pool_off, d["q"], pooled, kv_raw, idx, wl.W, scale, out=co, lse=cl, ws=ws_c)
+        csa.hca_attn(batch, hpool_off, Ph_cap, wl.m_hca, d["q"], hpooled, kv_raw, wl.W_hca, scale, out=ho, lse=hl,
+                     ws=ws_h)
+
+    def reset():
+        length.copy_(len0)
+        z_tail.copy_(tail0)
+
+    step()
+    torch.cuda.synchronize()
+    ref = [x.clone() for x in (idx, co, cl, ho, hl, length, z_tail)]
+    reset()
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(g, stream=cap):
+            step()
+    torch.cuda.current_stream().wait_stream(cap)
+    torch.cuda.synchronize()
+    junk = torch.randn(1 << 20, device=dev)
+    for rep in range(3):
+        reset()
+        for x in (idx, co, cl, ho, hl):
+            x.fill_(0)
+        junk = junk * 1.0001 + 1.0  # eager work between replays
+        g.replay()
+        torch.cuda.synchronize()
+        for name, got, want in zip(("idx", "csa out", "csa lse", "hca out", "hca lse", "length", "tail ring"),
+                                   (idx, co, cl, ho, hl, length, z_tail), ref):
+            assert torch.equal(got, want), f"replay {rep}: {name} differs from the eager step"
