@@ -408,8 +408,9 @@ __global__ __launch_bounds__(256) void k_pf_score(PfArgs a) {
     uint4 kc[kB];
     int ks[kB];
     // a batch whose tiles every query sees whole: straight-line code (no
-    // branch between its tiles, so one tile's MFMAs overlap the previous
-    // tile's epilogue), its 16 words per tile stored after the batch
+    // branch between its tiles, so the compiler schedules across them and
+    // each tile waits only for its own loads), its 16 words per tile stored
+    // after the batch
     const int64_t jlast = jr0 + (int64_t)(wave + 4 * (ub + kB - 1)) * 32;
     if (ub + kB <= kT && jlast + 32 <= (int64_t)nmin) {  // uniform per wave
 #pragma unroll
