@@ -268,6 +268,11 @@ __global__ __launch_bounds__(256) void k_append_pool(AppendArgs a) {
         pool_chunk(st, zz, xx, ns - c0 < 8 ? ns - c0 : 8);
       }
     }
+#pragma unroll
+    for (int i = 8; i < kPoolSeg; ++i) {  // rows of a second chunk the segment does not have
+      consume_load(xr[i]);
+      consume_load(zr[i]);
+    }
     part[task] = st;
   }
   __syncthreads();
@@ -536,6 +541,11 @@ __global__ __launch_bounds__(1024) void k_append_step(AppendArgs a) {
         pool_chunk(st, zz, xx, ns - c0 < 8 ? ns - c0 : 8);
       }
     }
+#pragma unroll
+    for (int i = 8; i < kPoolSeg; ++i) {  // rows of a second chunk the segment does not have
+      consume_load(hx[i]);
+      consume_load(hz[i]);
+    }
     part[t] = st;
   }
   if (c_do) {
@@ -554,6 +564,10 @@ __global__ __launch_bounds__(1024) void k_append_step(AppendArgs a) {
   }
   if (r_do && q.L0 + ri < q.cap)
     *reinterpret_cast<uint4*>(a.kv_raw + (size_t)(q.r0 + q.L0 + ri) * row + (size_t)rg * 16) = rx;
+  if (r_do) {  // a row past the capacity is loaded but not stored
+    consume_load(rx.x);
+    consume_load(rz.x);
+  }
   if (k_do) {
     uint32_t amax = __float_as_uint(kval) & 0x7fffffffu;
 #pragma unroll

@@ -70,7 +70,7 @@ __global__ __launch_bounds__(256) void k_compress_short(const int64_t* __restric
   uint4 xr[BPT][MAXM], zr[BPT][MAXM];
 #pragma unroll
   for (int k = 0; k < BPT; ++k) {
-    const int64_t j = j0 + k < P ? j0 + k : P - 1;  // blocks past P load the last one (not stored)
+    const int64_t j = j0 + k < P ? j0 + k : P - 1;  // blocks past P load the last one (consumed, not stored)
 #pragma unroll
     for (int i = 0; i < MAXM; ++i) {
       const int ii = i < m ? i : m - 1;
@@ -81,7 +81,14 @@ __global__ __launch_bounds__(256) void k_compress_short(const int64_t* __restric
   }
 #pragma unroll
   for (int k = 0; k < BPT; ++k) {
-    if (j0 + k >= P) break;
+    if (j0 + k >= P) {  // loaded (the last block again) but not pooled
+#pragma unroll
+      for (int i = 0; i < MAXM; ++i) {
+        consume_load(xr[k][i].x);
+        consume_load(zr[k][i].x);
+      }
+      continue;
+    }
     PoolState<BF16> st;
     pool_reset(st);
     float zz[8][N], xx[8][N];

@@ -61,6 +61,11 @@ struct Vec4 {
   }
 };
 
+// A loaded value that a path does not use is still consumed here (the empty
+// asm reads the register, so the compiler waits for the load), so that no
+// load is left in flight with its result unused.
+__device__ __forceinline__ void consume_load(uint32_t v) { asm volatile("" ::"v"(v)); }
+
 // Pooling state of N channels: running max, denominator, weighted sum.
 template <int N>
 struct PoolSt {

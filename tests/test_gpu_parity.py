@@ -91,7 +91,7 @@ def test_compress_parity(dtype, m):
         assert np.all(np.abs(g - want) <= bound)
 
 
-@pytest.mark.parametrize("dtype,m,m_hca", [("f32", 4, 128), ("bf16", 4, 128), ("bf16", 32, 64)])
+@pytest.mark.parametrize("dtype,m,m_hca", [("f32", 4, 128), ("bf16", 4, 128), ("bf16", 32, 64), ("bf16", 4, 40)])
 def test_cache_append_builds_the_bulk_caches(dtype, m, m_hca):
     """Caches grown by ragged appends (prefill chunks, single decode tokens,
     sequences with nothing new; decode-sized steps take the one-launch path
@@ -102,7 +102,8 @@ def test_cache_append_builds_the_bulk_caches(dtype, m, m_hca):
     exact pooling, the completed blocks' indexer keys bit for bit equal to the
     oracle's MXFP4 encoding of their vectors, the tail ring holding the latest
     tokens' logits, and the lengths advanced.  m = 32 makes the CSA blocks
-    long too (pooled by channel-slice workgroups in the multi-kernel path)."""
+    long too (pooled by channel-slice workgroups in the multi-kernel path);
+    m' = 40 ends every HCA block with a segment of 8 rows."""
     csa = _lib()
     ring = m_hca
     wl = small_wl("append", [1, 131, 517, 1030, 2050], [1] * 5, dtype=dtype, m=m, m_hca=m_hca, seed=23)
