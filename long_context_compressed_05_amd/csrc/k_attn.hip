@@ -212,13 +212,24 @@ __global__ __launch_bounds__(256) void k_attn_bf16_pair(AttnArgs a, int64_t n_q)
 // ---------------------------------------------------------------------------
 // fp32, VALU (small head counts; exact fp32 FMAs)
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ float wave_sum_f(float v) {
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// QLDS (H <= 64): the query's heads are staged in LDS once, so the score
+// loop reads them from LDS (a wave's lanes share one head: a broadcast)
+// instead of from global memory in the loop.  The softmax of a tile runs one
+// wave per head, a lane per key.
+template <bool QLDS>
 __global__ __launch_bounds__(256) void k_attn_f32(AttnArgs a) {
   __shared__ float Ks[64][129];
   __shared__ float Vs[64][128];
   __shared__ float Ps[128][65];
   __shared__ float m_s[128], l_s[128], al_s[128];
   __shared__ const uint8_t* rowp[64];
-  const int tid = threadIdx.x;
+  extern __shared__ float qs[];  // [H][128] with QLDS
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t row = blockIdx.y;
   const int split = blockIdx.x;
   const RowCtx c = row_ctx(a, row);
@@ -234,6 +245,10 @@ __global__ __launch_bounds__(256) void k_attn_f32(AttnArgs a) {
 #pragma unroll
   for (int e = 0; e < MAXE; ++e) O[e] = 0.f;
   for (int h = tid; h < H; h += 256) { m_s[h] = -INFINITY; l_s[h] = 0.f; }
+  if constexpr (QLDS) {
+    for (int i = tid; i < H * 32; i += 256)
+      reinterpret_cast<float4*>(qs)[i] = reinterpret_cast<const float4*>(qrow)[i];
+  }
 
   for (int64_t p0 = p_begin; p0 < p_end; p0 += 64) {
     if (tid < 64) {
@@ -241,41 +256,53 @@ __global__ __launch_bounds__(256) void k_attn_f32(AttnArgs a) {
       rowp[tid] = p < p_end ? key_row(a, c, row, p, RB) : nullptr;
     }
     __syncthreads();
-    for (int i = tid; i < 64 * 64; i += 256) {  // 64 keys x 64 float4 (K then V)
-      const int key = i >> 6, q4 = i & 63;
-      const uint8_t* rp = rowp[key];
-      float4 v = rp ? *reinterpret_cast<const float4*>(rp + q4 * 16) : make_float4(0, 0, 0, 0);
-      if (q4 < 32) {
-        Ks[key][4 * q4 + 0] = v.x; Ks[key][4 * q4 + 1] = v.y;
-        Ks[key][4 * q4 + 2] = v.z; Ks[key][4 * q4 + 3] = v.w;
-      } else {
-        *reinterpret_cast<float4*>(&Vs[key][4 * (q4 - 32)]) = v;
+    {  // 64 keys x 64 float4 (K then V): all 16 of a thread's loads, then the stores
+      float4 v[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const int i = tid + 256 * u, key = i >> 6, q4 = i & 63;
+        const uint8_t* rp = rowp[key];
+        v[u] = rp ? *reinterpret_cast<const float4*>(rp + q4 * 16) : make_float4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const int i = tid + 256 * u, key = i >> 6, q4 = i & 63;
+        if (q4 < 32) {
+          Ks[key][4 * q4 + 0] = v[u].x; Ks[key][4 * q4 + 1] = v[u].y;
+          Ks[key][4 * q4 + 2] = v[u].z; Ks[key][4 * q4 + 3] = v[u].w;
+        } else {
+          *reinterpret_cast<float4*>(&Vs[key][4 * (q4 - 32)]) = v[u];
+        }
       }
     }
     __syncthreads();
-    for (int i = tid; i < H * 64; i += 256) {
+    for (int i = tid; i < H * 64; i += 256) {  // a wave's 64 lanes: one head, 64 keys
       const int h = i >> 6, j = i & 63;
       float s = 0.f;
-      const float* qh = qrow + h * 128;
+      const float* qh = QLDS ? qs + h * 128 : qrow + h * 128;
+#pragma unroll 8
       for (int d = 0; d < 128; ++d) s = fmaf(qh[d], Ks[j][d], s);
       Ps[h][j] = rowp[j] ? s * a.scale_log2 : -INFINITY;
     }
     __syncthreads();
-    for (int h = tid; h < H; h += 256) {
-      float tmax = -INFINITY;
-      for (int j = 0; j < 64; ++j) tmax = fmaxf(tmax, Ps[h][j]);
-      const float mnew = fmaxf(m_s[h], tmax);
-      if (mnew == -INFINITY) { al_s[h] = 1.f; continue; }
-      const float alpha = fast_exp2(m_s[h] - mnew);
-      float sum = 0.f;
-      for (int j = 0; j < 64; ++j) {
-        const float pj = fast_exp2(Ps[h][j] - mnew);
-        Ps[h][j] = pj;
-        sum += pj;
+    for (int h = wave; h < H; h += 4) {  // wave per head, lane per key
+      const float pv = Ps[h][lane];
+      const float tmax = wave_max(pv);
+      const float mold = m_s[h];
+      const float mnew = fmaxf(mold, tmax);
+      if (mnew == -INFINITY) {  // nothing valid so far (uniform)
+        if (lane == 0) al_s[h] = 1.f;
+        continue;
       }
-      m_s[h] = mnew;
-      l_s[h] = l_s[h] * alpha + sum;
-      al_s[h] = alpha;
+      const float pj = fast_exp2(pv - mnew);
+      Ps[h][lane] = pj;
+      const float sum = wave_sum_f(pj);
+      if (lane == 0) {
+        const float alpha = fast_exp2(mold - mnew);
+        m_s[h] = mnew;
+        l_s[h] = l_s[h] * alpha + sum;
+        al_s[h] = alpha;
+      }
     }
     __syncthreads();
 #pragma unroll
@@ -425,8 +452,12 @@ int launch_attn(bool bf16, bool hca, int n_seq, int64_t n_q, const int64_t* tok_
     return e == hipSuccess && hipGetLastError() == hipSuccess ? 0 : -1;
   }
   dim3 grid((unsigned)a.splits, (unsigned)n_q);
-  hipError_t e = launch(3, kProfBoth, !bf16 ? k_attn_f32 : (H > 64 ? k_attn_bf16<2> : k_attn_bf16<1>), grid,
-                        dim3(256), 0, stream, a);
+  hipError_t e;
+  if (!bf16 && H <= 64)  // the query's heads staged in LDS
+    e = launch(3, kProfBoth, k_attn_f32<true>, grid, dim3(256), (size_t)H * 128 * 4, stream, a);
+  else
+    e = launch(3, kProfBoth, !bf16 ? k_attn_f32<false> : (H > 64 ? k_attn_bf16<2> : k_attn_bf16<1>), grid,
+               dim3(256), 0, stream, a);
   if (e == hipSuccess && a.splits > 1) {
     dim3 gc((unsigned)n_q, (unsigned)H);
     e = launch(4, kProfBoth, bf16 ? k_attn_combine<true> : k_attn_combine<false>, gc, dim3(128), 0, stream,
