@@ -453,6 +453,23 @@ def test_prefill_topk_full_size_sampled():
     _index_rows(wl, host, rows)
 
 
+
+def test_prefill_topk_two_sequences_mixed_batches():
+    """4096 queries over two sequences (16,384 and 12,000 cached tokens, the
+    second sequence's queries starting at a position off a block boundary):
+    up to 4,608 pooled keys per sequence, so the scoring workgroups hold 1,152
+    keys (9 tiles per wave): a first batch of 8 tiles that every query of a
+    block sees whole (the straight-line path), a last batch of 1 (the
+    per-tile path), and blocks at each query's visible edge.  The first and
+    last rows of each sequence and 250 spread rows against the oracle, bit for
+    bit."""
+    wl = small_wl("prefill_mixed_batches", [16384 + 2048, 12001 + 2048], [2048, 2048], k=256, seed=63)
+    host = synth.make_inputs(wl, raw=False)
+    q_off = host["q_off"]
+    ends = [0, int(q_off[1]) - 1, int(q_off[1]), wl.n_q - 1]
+    rows = sorted(set(ends + list(np.random.default_rng(9).choice(wl.n_q, 250, replace=False))))
+    _index_rows(wl, host, rows)
+
 FUSED_CASES = {
     "decode_bf16_ragged": lambda: small_wl("decode_bf16_ragged", [1, 3, 130, 517, 1030, 2049, 4099], [1] * 7,
                                            k=64, seed=11),
