@@ -101,11 +101,97 @@ __device__ __forceinline__ const uint8_t* key_row(const AttnArgs& a, const RowCt
 // ---------------------------------------------------------------------------
 // bf16, MFMA (tile loop in attn_core.hpp)
 // ---------------------------------------------------------------------------
+// One query's head group per wave over list positions [p_begin, p_end), with
+// 48 KB of LDS instead of two 32 KB stages: K single-buffered, V
+// double-buffered (kKv1LdsBytes).  Per tile t: wait for K(t) and V(t), read
+// the K fragments (S^T MFMAs) and the V^T fragments into registers, barrier,
+// DMA of K(t+1) (hidden behind the softmax and PV) and of V(t+2) (a whole
+// tile ahead), then the softmax and PV from registers.  So three workgroups
+// fit a CU's LDS.  Same arithmetic as attn_run (attn_softmax_pv); same entry
+// conditions.
+constexpr int kKv1LdsBytes = 3 * 16 * 1024 + 16;
+
+template <class RowPtr>
+__device__ __forceinline__ void attn_run_kv1(AttnState<1>& st, float scale_log2, int64_t p_begin, int64_t p_end,
+                                             RowPtr rowptr, uint8_t* lds) {
+  const int lane = lane_tid() & 63, wave = lane_tid() >> 6;
+  const int l16 = lane & 15, g = lane >> 4;
+  if (p_begin >= p_end) return;
+  const int64_t n_tiles = (p_end - p_begin + kTileKeys - 1) / kTileKeys;
+  const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
+  uint64_t* masks = reinterpret_cast<uint64_t*>(lds + 3 * 16 * 1024);  // by tile parity
+  // row of this lane in tile t (nullptr: masked) and its source address
+  auto src_of = [&](int64_t t, const uint8_t** rp_out) {
+    const int row = 16 * wave + (lane >> 2);
+    const int64_t p = p_begin + t * kTileKeys + row;
+    const uint8_t* rp = p < p_end ? rowptr(p) : nullptr;
+    *rp_out = rp;
+    return (rp ? rp : g_zero_row) + 16 * (lane & 3);
+  };
+  auto issue_k = [&](int64_t t) {  // K chunks 0..15 -> [0, 16 KB), and the tile's validity word
+    const uint8_t* rp;
+    const uint8_t* src = src_of(t, &rp);
+    const uint64_t vb = __ballot(rp != nullptr);
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_base + (uint32_t)(wave * 1024));
+    dma16<0>(src, m0);
+    dma16<64>(src, m0 + 4 * 1024 - 64);
+    dma16<128>(src, m0 + 8 * 1024 - 128);
+    dma16<192>(src, m0 + 12 * 1024 - 192);
+    uint32_t m16 = 0;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) m16 |= (uint32_t)((vb >> (4 * j)) & 1ull) << j;
+    if (lane == 0) reinterpret_cast<uint16_t*>(masks + (t & 1))[wave] = (uint16_t)m16;
+  };
+  auto issue_v = [&](int64_t t) {  // V chunks 16..31 -> buffer t & 1 at 16 KB (t & 1 ? 2 : 1)
+    const uint8_t* rp;
+    const uint8_t* src = src_of(t, &rp);
+    const uint32_t vb0 = lds_base + (uint32_t)((1 + (t & 1)) * 16 * 1024);
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(vb0 + (uint32_t)(wave * 1024));
+    dma16<256>(src, m0 - 256);
+    dma16<320>(src, m0 + 4 * 1024 - 320);
+    dma16<384>(src, m0 + 8 * 1024 - 384);
+    dma16<448>(src, m0 + 12 * 1024 - 448);
+  };
+  issue_k(0);
+  issue_v(0);
+  if (n_tiles > 1) issue_v(1);
+  for (int64_t t = 0; t < n_tiles; ++t) {
+    // issued after K(t): only V(t+1) (V(t) was issued before K(t))
+    if (t + 1 < n_tiles) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();  // K(t), V(t) and the validity word in LDS
+    const uint64_t vmask = masks[t & 1];
+    float s_[4][4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      v8bf kf[4];
+#pragma unroll
+      for (int kq = 0; kq < 4; ++kq)
+        kf[kq] = *reinterpret_cast<const v8bf*>(lds + (kq * 4 + mt) * 1024 + l16 * 64 + g * 16);
+      v4f acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kq = 0; kq < 4; ++kq) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kq], st.qf[0][kq], acc, 0, 0, 0);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) s_[mt][v] = acc[v];
+    }
+    // V^T of tile t: attn_vt addresses V at +16 KB of its base
+    v4s_t vt[8][2][2];
+    attn_vt(lds + (t & 1) * 16 * 1024, l16, g, vt);
+    __syncthreads();  // every wave has read K(t) and V(t) (the barrier waits for its LDS reads)
+    if (t + 1 < n_tiles) issue_k(t + 1);
+    if (t + 2 < n_tiles) issue_v(t + 2);
+    attn_softmax_pv(st.m_run[0], st.l_run[0], st.O[0], s_, vt, vmask, g, scale_log2);
+  }
+  __syncthreads();
+}
+
 constexpr int kMaxSplitKeys = 1024;
 
 template <int GPW>
 __global__ __launch_bounds__(256) void k_attn_bf16(AttnArgs a) {
-  __shared__ __align__(16) uint8_t lds[kAttnLdsBytes];
+  // one head group per wave (H <= 64): the 48 KB K/V staging (three
+  // workgroups per CU); two groups per wave: two 32 KB stages
+  __shared__ __align__(16) uint8_t lds[GPW == 1 ? kKv1LdsBytes : kAttnLdsBytes];
   __shared__ int32_t idx_s[kMaxSplitKeys];
   const int tid = threadIdx.x;
   const int64_t row = blockIdx.y;
@@ -139,7 +225,8 @@ __global__ __launch_bounds__(256) void k_attn_bf16(AttnArgs a) {
   };
   AttnState<GPW> st;
   attn_init<GPW>(st, a.q + (size_t)row * a.H * 128 * 2, a.H);
-  attn_run<GPW>(st, a.H, a.scale_log2, p_begin, p_end, rowptr, lds);
+  if constexpr (GPW == 1) attn_run_kv1(st, a.scale_log2, p_begin, p_end, rowptr, lds);
+  else attn_run<GPW>(st, a.H, a.scale_log2, p_begin, p_end, rowptr, lds);
   const size_t pbase = (size_t)(row * a.splits + split) * a.H;
   attn_finish<GPW>(st, a.H, a.out + (size_t)row * a.H * 128 * 2, a.lse ? a.lse + row * a.H : nullptr,
                    a.part_o ? a.part_o + pbase * 128 : nullptr, a.part_ml ? a.part_ml + pbase * 2 : nullptr,
