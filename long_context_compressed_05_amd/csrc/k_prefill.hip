@@ -298,16 +298,19 @@ __global__ __launch_bounds__(256) void k_pf_thresh(PfArgs a) {
   const int64_t st = a.stride;
   const int ns = (int)((nvis_max + st - 1) / st);  // <= ns_max
   const int ntiles = (ns + 31) >> 5;
-  for (int tb = wave; tb < ntiles; tb += 4 * 8) {  // 8 tiles per wave in flight
-    uint4 kc[8];
-    int ks[8];
+  // 16 tiles per wave in flight: a sample of up to 64 tiles (2048 keys) takes
+  // one round of loads
+  constexpr int kTB = 16;
+  for (int tb = wave; tb < ntiles; tb += 4 * kTB) {
+    uint4 kc[kTB];
+    int ks[kTB];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < kTB; ++u) {
       const int64_t j = (int64_t)((tb + 4 * u) * 32 + (lane & 31)) * st;
       pf_load_b(a, pbase + j, tb + 4 * u < ntiles && j < nvis_max, kb, kc[u], ks[u]);
     }
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < kTB; ++u) {
       const int tile = tb + 4 * u;
       if (tile >= ntiles) break;
       const int i = tile * 32 + (lane & 31);
@@ -543,44 +546,56 @@ __global__ __launch_bounds__(128) void k_pf_select(PfArgs a) {
     if (lane == 0) a.tau[row] = 0u;
     return;
   }
-  // candidates: the bitmap's set bits, lane l owning words [l * wpl, l * wpl + wpl),
-  // read 16 at a time (all loads of a batch in flight)
+  // candidates: the bitmap's set bits.  Word g * 64 + l goes to lane l (words
+  // of a group of 64 are adjacent, so a run of dense words spreads over the
+  // lanes and a group's extraction takes as many steps as its densest word
+  // has bits); groups read 16 at a time (all loads of a batch in flight)
   const uint32_t* bm = a.bitmap + (size_t)row * a.bw;
   uint32_t* bmw = a.bitmap + (size_t)row * a.bw;
-  const int nw = (int)((nvis + 31) >> 5), wpl = (nw + 63) >> 6, w0 = lane * wpl;
+  const int nw = (int)((nvis + 31) >> 5), ng = (nw + 63) >> 6;
   constexpr int kWB = 16;
   uint32_t wv[kWB];
   uint32_t cnt = 0;
-  for (int b0 = 0; b0 < wpl; b0 += kWB) {
+  for (int g0 = 0; g0 < ng; g0 += kWB) {
 #pragma unroll
-    for (int i = 0; i < kWB; ++i) wv[i] = (b0 + i < wpl && w0 + b0 + i < nw) ? bm[w0 + b0 + i] : 0u;
+    for (int i = 0; i < kWB; ++i) {
+      const int w = (g0 + i) * 64 + lane;
+      wv[i] = (g0 + i < ng && w < nw) ? bm[w] : 0u;
+    }
 #pragma unroll
     for (int i = 0; i < kWB; ++i) cnt += (uint32_t)__popc(wv[i]);
   }
-  const uint32_t incl = wave_incl_add(cnt);
-  const uint32_t n_c = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+  const uint32_t n_c = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_add(cnt), 63);
   // the workspace is left zero-filled: this query's threshold and bitmap words
   if (lane == 0) a.tau[row] = 0u;
   if (n_c < k_eff || n_c > (uint32_t)kPfCand) {
-    for (int i = 0; i < wpl; ++i)
-      if (w0 + i < nw) bmw[w0 + i] = 0u;
+    for (int w = lane; w < nw; w += 64) bmw[w] = 0u;
     pf_select_all(a, row, pbase, nvis, k_eff, hist, idx);
     return;
   }
-  uint32_t pos = incl - cnt;
-  for (int b0 = 0; b0 < wpl; b0 += kWB) {
-    if (wpl > kWB) {  // more than one batch: read this one again
+  uint32_t run = 0;  // candidates of the groups before
+  for (int g0 = 0; g0 < ng; g0 += kWB) {
+    if (ng > kWB) {  // more than one batch: read this one again
 #pragma unroll
-      for (int i = 0; i < kWB; ++i) wv[i] = (b0 + i < wpl && w0 + b0 + i < nw) ? bm[w0 + b0 + i] : 0u;
+      for (int i = 0; i < kWB; ++i) {
+        const int w = (g0 + i) * 64 + lane;
+        wv[i] = (g0 + i < ng && w < nw) ? bm[w] : 0u;
+      }
     }
 #pragma unroll
     for (int i = 0; i < kWB; ++i) {
-      if (b0 + i < wpl && w0 + b0 + i < nw) bmw[w0 + b0 + i] = 0u;
+      if (g0 + i >= ng) break;  // uniform
+      const int w = (g0 + i) * 64 + lane;
+      if (w < nw) bmw[w] = 0u;
+      const uint32_t c = (uint32_t)__popc(wv[i]);
+      const uint32_t incl = wave_incl_add(c);
+      uint32_t pos = run + incl - c;
+      run += (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
       uint32_t bits = wv[i];
       while (bits) {
         const int bpos = __ffs(bits) - 1;
         bits &= bits - 1u;
-        cand_j[pos++] = (uint32_t)((w0 + b0 + i) * 32 + bpos);
+        cand_j[pos++] = (uint32_t)(w * 32 + bpos);
       }
     }
   }
