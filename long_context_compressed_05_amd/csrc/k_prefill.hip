@@ -10,12 +10,13 @@
 //
 // Three kernels:
 //  1. k_pf_thresh: per block of 4 queries of one sequence, the scores of a
-//     strided sample of the visible keys (every stride-th) -> LDS; per query
-//     (one wave, one radix pass over the range of the sample's nonzero
-//     scores) tau = the lower edge of the bin holding the need_s-th largest
-//     sample score, need_s =
-//     ceil(2 k / stride), so that about 2 k keys are >= tau; tau = 0 when the
-//     query sees at most k keys or too few samples.
+//     sample of the keys (runs of 32 consecutive keys, one run every
+//     32 * stride keys: 1 key in stride, each run one coalesced tile) -> LDS;
+//     per query (one wave, one radix pass over the range of its visible
+//     samples' nonzero scores) tau = the lower edge of the bin holding the
+//     need_s-th largest sample score, need_s = ceil(2 k / stride), so that
+//     about 2 k keys are >= tau; tau = 0 when the query sees at most k keys or
+//     too few samples.
 //  2. k_pf_score: every visible score exactly once on the block-scaled FP4
 //     MFMA (8 queries x 4 heads x 32 keys per MFMA, two MFMAs per key tile),
 //     compared with its query's tau: the output is a candidate bitmap, one bit
@@ -273,7 +274,7 @@ __device__ __forceinline__ uint32_t wave_kth(const uint32_t (&kv)[NK], uint32_t 
 }
 
 // ---------------------------------------------------------------------------
-// 1. thresholds from a strided sample
+// 1. thresholds from a sample of key runs
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_pf_thresh(PfArgs a) {
   extern __shared__ __align__(16) uint32_t pf_sm[];
@@ -286,28 +287,25 @@ __global__ __launch_bounds__(256) void k_pf_thresh(PfArgs a) {
   const int nrows = (int)(row0 >= row_end ? 0 : (row_end - row0 < kPfRowsT ? row_end - row0 : kPfRowsT));
   if (nrows == 0) return;
   const int64_t pbase = a.pool_off[b], P = a.pool_off[b + 1] - pbase;
-  int64_t nvis_max = 0;
-  for (int q = 0; q < nrows; ++q) {
-    const int64_t v = pf_nvis(a.q_pos[row0 + q], a.m, P);
-    nvis_max = v > nvis_max ? v : nvis_max;
-  }
   for (int i = tid; i < 4 * kPfWaveHist; i += 256) wh[i] = 0u;
   v8i a0;
   int s0;
   pf_load_a(a, row0, nrows, lane, a0, s0);
-  const int64_t st = a.stride;
-  const int ns = (int)((nvis_max + st - 1) / st);  // <= ns_max
-  const int ntiles = (ns + 31) >> 5;
-  // 16 tiles per wave in flight: a sample of up to 64 tiles (2048 keys) takes
-  // one round of loads
+  // sample tile u: keys [u * span, u * span + 32) of the sequence's P (the
+  // queries' own visible limits are applied per query below, so the loads do
+  // not wait for the positions); at most 64 tiles (the stride is >= P / 2048)
+  const int64_t st = a.stride, span = 32 * st;
+  const int ntiles = (int)((P + span - 1) / span);  // ntiles * 32 <= ns_max
+  // 16 tiles per wave in flight: the whole sample takes one round of loads
   constexpr int kTB = 16;
   for (int tb = wave; tb < ntiles; tb += 4 * kTB) {
     uint4 kc[kTB];
     int ks[kTB];
 #pragma unroll
     for (int u = 0; u < kTB; ++u) {
-      const int64_t j = (int64_t)((tb + 4 * u) * 32 + (lane & 31)) * st;
-      pf_load_b(a, pbase + j, tb + 4 * u < ntiles && j < nvis_max, kb, kc[u], ks[u]);
+      // 32-bit: P <= max_pool <= 2^30 (checked at the boundary), so j < 2^31
+      const int j = (tb + 4 * u) * (int)span + (lane & 31);
+      pf_load_b(a, pbase + j, tb + 4 * u < ntiles && j < (int)P, kb, kc[u], ks[u]);
     }
 #pragma unroll
     for (int u = 0; u < kTB; ++u) {
@@ -315,12 +313,10 @@ __global__ __launch_bounds__(256) void k_pf_thresh(PfArgs a) {
       if (tile >= ntiles) break;
       const int i = tile * 32 + (lane & 31);
       const v16f c0 = pf_mfma(a0, s0, kc[u], ks[u]);
-      if (i < ns) {
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const int q = 2 * s + (lane >> 5);
-          if (q < nrows) ss[(size_t)q * a.ns_max + i] = pf_key(c0, s);
-        }
+      for (int s = 0; s < 4; ++s) {
+        const int q = 2 * s + (lane >> 5);
+        if (q < nrows) ss[(size_t)q * a.ns_max + i] = pf_key(c0, s);
       }
     }
   }
@@ -330,7 +326,10 @@ __global__ __launch_bounds__(256) void k_pf_thresh(PfArgs a) {
     const int64_t row = row0 + q;
     const int64_t nvis = pf_nvis(a.q_pos[row], a.m, P);
     const int64_t k_eff = nvis < a.k ? nvis : a.k;
-    const int nsq = (int)((nvis + st - 1) / st);
+    // samples of keys < nvis: the runs below nvis / span whole, then the first
+    // min(32, nvis % span) of the next, so slots [0, nsq)
+    const int64_t rem = nvis % span;
+    const int nsq = (int)(nvis / span * 32 + (rem < 32 ? rem : 32));
     const int64_t need_s = (2 * k_eff + st - 1) / st;
     uint32_t tau = 0u;
     if (k_eff < nvis && need_s >= 1 && need_s <= nsq) {
@@ -719,8 +718,10 @@ int launch_prefill_topk(int n_seq, int64_t n_q, int64_t max_q_per_seq, const int
   a.bps_t = (int)((max_q_per_seq + kPfRowsT - 1) / kPfRowsT);
   a.m = m; a.k = k;
   a.stride = pf_stride(max_pool);
-  a.ns_max = (int)((max_pool + a.stride - 1) / a.stride);
-  if (a.ns_max < 1) a.ns_max = 1;
+  // sample slots: 32 per run of the longest sequence (<= kPfSampleMax, since
+  // stride >= max_pool / kPfSampleMax)
+  a.ns_max = (int)((max_pool + 32 * (int64_t)a.stride - 1) / (32 * (int64_t)a.stride)) * 32;
+  if (a.ns_max < 32) a.ns_max = 32;
   a.bw = (int)((max_pool + 31) / 32);
   a.n_q = n_q; a.max_pool = max_pool;
   a.q_codes = q_codes; a.q_scales = q_scales; a.w = w; a.k_codes = k_codes; a.k_scales = k_scales;

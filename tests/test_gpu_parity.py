@@ -470,6 +470,22 @@ def test_prefill_topk_two_sequences_mixed_batches():
     rows = sorted(set(ends + list(np.random.default_rng(9).choice(wl.n_q, 250, replace=False))))
     _index_rows(wl, host, rows)
 
+
+@pytest.mark.parametrize("codeset", [synth.E2M1_ALL_CODES, synth.E2M1_TIE_CODES])
+def test_prefill_topk_long_caches(codeset):
+    """Prefill batches on long caches: up to 50,000 pooled keys per query, so a
+    query's bitmap has more than 16 groups of 64 words (the selection reads its
+    words in several batches), the threshold sample stride exceeds 16 and the
+    sample fills its 2048 slots.  With tie-heavy codes the candidates
+    overflow and the exact path over all visible keys runs at that length.
+    The first and last row of each sequence and every fourth row against the
+    oracle, bit for bit."""
+    wl = small_wl("prefill_long", [200003, 140001], [32, 20], k=512, codeset=codeset, seed=71)
+    host = synth.make_inputs(wl, raw=False)
+    q_off = host["q_off"]
+    rows = sorted(set([0, int(q_off[1]) - 1, int(q_off[1]), wl.n_q - 1] + list(range(0, wl.n_q, 4))))
+    _index_rows(wl, host, rows)
+
 FUSED_CASES = {
     "decode_bf16_ragged": lambda: small_wl("decode_bf16_ragged", [1, 3, 130, 517, 1030, 2049, 4099], [1] * 7,
                                            k=64, seed=11),
