@@ -407,6 +407,14 @@ __global__ __launch_bounds__(256) void k_pf_score(PfArgs a) {
   constexpr int kB = 8;          // tiles per wave in flight
 #pragma unroll 1
   for (int ub = 0; ub < kT; ub += kB) {
+    {  // a wave further along issues after those behind it (waves of a SIMD
+       // otherwise issue oldest first, and the youngest one finishes alone)
+      const int pb = ub / kB;
+      if (pb == 0) __builtin_amdgcn_s_setprio(3);
+      else if (pb == 1) __builtin_amdgcn_s_setprio(2);
+      else if (pb == 2) __builtin_amdgcn_s_setprio(1);
+      else __builtin_amdgcn_s_setprio(0);
+    }
     uint4 kc[kB];
     int ks[kB];
     // a batch whose tiles every query sees whole: straight-line code (no
