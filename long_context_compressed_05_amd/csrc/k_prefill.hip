@@ -287,6 +287,7 @@ __global__ __launch_bounds__(256) void k_pf_thresh(PfArgs a) {
   const int nrows = (int)(row0 >= row_end ? 0 : (row_end - row0 < kPfRowsT ? row_end - row0 : kPfRowsT));
   if (nrows == 0) return;
   const int64_t pbase = a.pool_off[b], P = a.pool_off[b + 1] - pbase;
+  __builtin_amdgcn_s_setprio(3);  // lowered for the radix pass (waves of a SIMD progress together)
   for (int i = tid; i < 4 * kPfWaveHist; i += 256) wh[i] = 0u;
   v8i a0;
   int s0;
@@ -321,6 +322,7 @@ __global__ __launch_bounds__(256) void k_pf_thresh(PfArgs a) {
     }
   }
   __syncthreads();
+  __builtin_amdgcn_s_setprio(1);
   uint32_t* hist = wh + wave * kPfWaveHist;
   for (int q = wave; q < nrows; q += 4) {
     const int64_t row = row0 + q;
@@ -572,6 +574,9 @@ __global__ __launch_bounds__(128) void k_pf_select(PfArgs a) {
 #pragma unroll
     for (int i = 0; i < kWB; ++i) cnt += (uint32_t)__popc(wv[i]);
   }
+  // issue priority falls as a wave's phases complete (count, re-score, K*),
+  // so the waves of a SIMD progress together rather than oldest first
+  __builtin_amdgcn_s_setprio(3);
   const uint32_t n_c = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_add(cnt), 63);
   // the workspace is left zero-filled: this query's threshold and bitmap words
   if (lane == 0) a.tau[row] = 0u;
@@ -606,6 +611,7 @@ __global__ __launch_bounds__(128) void k_pf_select(PfArgs a) {
       }
     }
   }
+  __builtin_amdgcn_s_setprio(2);
   // the candidates' scores again: query slot 0 of the MFMA, 32 candidates per tile;
   // tiles 2e and 2e + 1 fill register slot e (lanes 0-31 and 32-63)
   v8i av;
@@ -639,7 +645,9 @@ __global__ __launch_bounds__(128) void k_pf_select(PfArgs a) {
     }
   }
   uint32_t gt;
+  __builtin_amdgcn_s_setprio(1);
   const uint32_t kstar = wave_kth<NK, 4, kSelBins>(kv, vm, nk, k_eff, hist, &gt);
+  __builtin_amdgcn_s_setprio(0);
   const uint32_t r_eq = k_eff - gt;
   // candidates are in ascending index order: a selected one goes to the count of
   // selected ones before it
