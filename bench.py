@@ -856,22 +856,6 @@ def bench_prefill_chunk(torch, csa, synth, to_device, log, reps: int = 10, oracl
     step_us = float(np.median(step_ms)) * 1e3
     # the same step captured once in a HIP graph and replayed (no launch gaps
     # between its kernels); every replay's outputs must equal the eager step's
-    side = torch.cuda.Stream()
-
-    def step_two_streams():
-        """HCA attention needs only the appended caches, not the top-k: it runs
-        on a second stream beside the indexer and the CSA attention."""
-        csa.csa_cache_append(x_new, z_new, new_off, n, tok_off, length, kv_raw, z_tail, pool_off, wl.m, pooled,
-                             hpool_off, wl.m_hca, hpooled)
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            csa.hca_attn(batch, hpool_off, Ph_cap, wl.m_hca, d["q"], hpooled, kv_raw, wl.W_hca, scale, out=ho,
-                         lse=hl, ws=ws_h)
-        csa.csa_index_topk(batch, pool_off, P_cap, wl.m, wl.k, d["qc"], d["qs"], d["w"], d["kc"], d["ks"], idx=idx,
-                           ws=ws_i)
-        csa.csa_sparse_attn(batch, pool_off, d["q"], pooled, kv_raw, idx, wl.W, scale, out=co, lse=cl, ws=ws_c)
-        torch.cuda.current_stream().wait_stream(side)
-
     def graph_of(fn):
         try:
             reset()
@@ -906,8 +890,6 @@ def bench_prefill_chunk(torch, csa, synth, to_device, log, reps: int = 10, oracl
         except Exception as e:  # reported, never silently replaced
             return {"error": repr(e)}
     graph = graph_of(step)
-    graph2 = graph_of(step_two_streams)
-    graph2["streams"] = "HCA attention on a second stream after the append, beside the indexer and CSA attention"
     # algorithmic FLOPs
     q_pos = host["q_pos"]
     k_eff = np.minimum(wl.k, np.minimum((q_pos + 1) // wl.m, P_cap))
@@ -943,7 +925,6 @@ def bench_prefill_chunk(torch, csa, synth, to_device, log, reps: int = 10, oracl
                     "index_topk_queries_per_s": round(wl.n_q / (index_us * 1e-6), 1)},
         "timing": "median of %d eager steps; kernel times from events attached to each dispatch" % reps,
         "graph": graph,
-        "graph_two_streams": graph2,
     }
     # the oracle beside it, on a few of the same queries (fp64 pooled caches prebuilt, not timed)
     try:
