@@ -306,13 +306,18 @@ __device__ __forceinline__ float wave_sum_f(float v) {
 
 // QLDS (H <= 64): the query's heads are staged in LDS once, so the score
 // loop reads them from LDS (a wave's lanes share one head: a broadcast)
-// instead of from global memory in the loop.  The softmax of a tile runs one
-// wave per head, a lane per key.
-template <bool QLDS>
+// instead of from global memory.  E (a power of two >= H / 2): the outputs a
+// thread owns, dims tid & 127 of heads (tid >> 7) + 2e.  A tile's scores
+// come from four independent partial dot products per (head, key) over
+// 16-byte LDS reads, the softmax runs one wave per head and a lane per key,
+// and PV reads each V element once for all of the thread's heads (E
+// independent FMA chains), so no step is a long chain of dependent LDS reads.
+template <bool QLDS, int E>
 __global__ __launch_bounds__(256) void k_attn_f32(AttnArgs a) {
-  __shared__ float Ks[64][129];
-  __shared__ float Vs[64][128];
-  __shared__ float Ps[128][65];
+  constexpr int KS = 132, PS = 68;  // row strides (floats): 16-byte aligned rows
+  __shared__ __align__(16) float Ks[64][KS];
+  __shared__ __align__(16) float Vs[64][128];
+  __shared__ __align__(16) float Ps[128][PS];
   __shared__ float m_s[128], l_s[128], al_s[128];
   __shared__ const uint8_t* rowp[64];
   extern __shared__ float qs[];  // [H][128] with QLDS
@@ -326,11 +331,10 @@ __global__ __launch_bounds__(256) void k_attn_f32(AttnArgs a) {
   const int H = a.H;
   constexpr size_t RB = 2 * 128 * 4;
   const float* qrow = reinterpret_cast<const float*>(a.q) + (size_t)row * H * 128;
-  constexpr int MAXE = 64;  // H*128/256 outputs per thread at H = 128
-  const int n_el = (H * 128 + 255) / 256;
-  float O[MAXE];
+  const int d_own = tid & 127, h_own = tid >> 7;  // output e: head h_own + 2e, dim d_own
+  float O[E];
 #pragma unroll
-  for (int e = 0; e < MAXE; ++e) O[e] = 0.f;
+  for (int e = 0; e < E; ++e) O[e] = 0.f;
   for (int h = tid; h < H; h += 256) { m_s[h] = -INFINITY; l_s[h] = 0.f; }
   if constexpr (QLDS) {
     for (int i = tid; i < H * 32; i += 256)
@@ -354,22 +358,25 @@ __global__ __launch_bounds__(256) void k_attn_f32(AttnArgs a) {
 #pragma unroll
       for (int u = 0; u < 16; ++u) {
         const int i = tid + 256 * u, key = i >> 6, q4 = i & 63;
-        if (q4 < 32) {
-          Ks[key][4 * q4 + 0] = v[u].x; Ks[key][4 * q4 + 1] = v[u].y;
-          Ks[key][4 * q4 + 2] = v[u].z; Ks[key][4 * q4 + 3] = v[u].w;
-        } else {
-          *reinterpret_cast<float4*>(&Vs[key][4 * (q4 - 32)]) = v[u];
-        }
+        if (q4 < 32) *reinterpret_cast<float4*>(&Ks[key][4 * q4]) = v[u];
+        else *reinterpret_cast<float4*>(&Vs[key][4 * (q4 - 32)]) = v[u];
       }
     }
     __syncthreads();
     for (int i = tid; i < H * 64; i += 256) {  // a wave's 64 lanes: one head, 64 keys
       const int h = i >> 6, j = i & 63;
-      float s = 0.f;
       const float* qh = QLDS ? qs + h * 128 : qrow + h * 128;
+      float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
 #pragma unroll 8
-      for (int d = 0; d < 128; ++d) s = fmaf(qh[d], Ks[j][d], s);
-      Ps[h][j] = rowp[j] ? s * a.scale_log2 : -INFINITY;
+      for (int d = 0; d < 128; d += 4) {
+        const float4 q = *reinterpret_cast<const float4*>(qh + d);
+        const float4 k = *reinterpret_cast<const float4*>(&Ks[j][d]);
+        s0 = fmaf(q.x, k.x, s0);
+        s1 = fmaf(q.y, k.y, s1);
+        s2 = fmaf(q.z, k.z, s2);
+        s3 = fmaf(q.w, k.w, s3);
+      }
+      Ps[h][j] = rowp[j] ? ((s0 + s1) + (s2 + s3)) * a.scale_log2 : -INFINITY;
     }
     __syncthreads();
     for (int h = wave; h < H; h += 4) {  // wave per head, lane per key
@@ -377,7 +384,8 @@ __global__ __launch_bounds__(256) void k_attn_f32(AttnArgs a) {
       const float tmax = wave_max(pv);
       const float mold = m_s[h];
       const float mnew = fmaxf(mold, tmax);
-      if (mnew == -INFINITY) {  // nothing valid so far (uniform)
+      if (mnew == -INFINITY) {  // nothing valid so far (uniform): adds nothing
+        Ps[h][lane] = 0.f;
         if (lane == 0) al_s[h] = 1.f;
         continue;
       }
@@ -392,33 +400,41 @@ __global__ __launch_bounds__(256) void k_attn_f32(AttnArgs a) {
       }
     }
     __syncthreads();
+    {  // O[e] = O[e] * alpha + sum_j P[h][j] V[j][d], four keys a step
 #pragma unroll
-    for (int e = 0; e < MAXE; ++e) {
-      const int o = tid + 256 * e;
-      if (e < n_el && o < H * 128) {
-        const int h = o >> 7, d = o & 127;
-        if (m_s[h] != -INFINITY) {
-          float acc = O[e] * al_s[h];
-          for (int j = 0; j < 64; ++j) acc = fmaf(Ps[h][j], Vs[j][d], acc);
-          O[e] = acc;
+      for (int e = 0; e < E; ++e)
+        if (h_own + 2 * e < H) O[e] *= al_s[h_own + 2 * e];
+#pragma unroll 2
+      for (int j = 0; j < 64; j += 4) {
+        const float v0 = Vs[j][d_own], v1 = Vs[j + 1][d_own], v2 = Vs[j + 2][d_own], v3 = Vs[j + 3][d_own];
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const int h = h_own + 2 * e;
+          if (h < H) {
+            const float4 pp = *reinterpret_cast<const float4*>(&Ps[h][j]);
+            O[e] = fmaf(pp.x, v0, O[e]);
+            O[e] = fmaf(pp.y, v1, O[e]);
+            O[e] = fmaf(pp.z, v2, O[e]);
+            O[e] = fmaf(pp.w, v3, O[e]);
+          }
         }
       }
     }
     __syncthreads();
   }
 #pragma unroll
-  for (int e = 0; e < MAXE; ++e) {
-    const int o = tid + 256 * e;
-    if (e >= n_el || o >= H * 128) continue;
-    const int h = o >> 7, d = o & 127;
+  for (int e = 0; e < E; ++e) {
+    const int h = h_own + 2 * e;
+    if (h >= H) continue;
+    const int o = h * 128 + d_own;
     const float l = l_s[h];
     if (a.splits == 1) {
       reinterpret_cast<float*>(a.out)[(size_t)row * H * 128 + o] = l > 0.f ? O[e] / l : 0.f;
-      if (a.lse && d == 0) a.lse[row * H + h] = l > 0.f ? (m_s[h] + __log2f(l)) * kLn2 : -INFINITY;
+      if (a.lse && d_own == 0) a.lse[row * H + h] = l > 0.f ? (m_s[h] + __log2f(l)) * kLn2 : -INFINITY;
     } else {
       const size_t base = (size_t)(row * a.splits + split) * H + h;
-      a.part_o[base * 128 + d] = O[e];
-      if (d == 0) { a.part_ml[base * 2] = m_s[h]; a.part_ml[base * 2 + 1] = l; }
+      a.part_o[base * 128 + d_own] = O[e];
+      if (d_own == 0) { a.part_ml[base * 2] = m_s[h]; a.part_ml[base * 2 + 1] = l; }
     }
   }
 }
@@ -540,11 +556,16 @@ int launch_attn(bool bf16, bool hca, int n_seq, int64_t n_q, const int64_t* tok_
   }
   dim3 grid((unsigned)a.splits, (unsigned)n_q);
   hipError_t e;
-  if (!bf16 && H <= 64)  // the query's heads staged in LDS
-    e = launch(3, kProfBoth, k_attn_f32<true>, grid, dim3(256), (size_t)H * 128 * 4, stream, a);
-  else
-    e = launch(3, kProfBoth, !bf16 ? k_attn_f32<false> : (H > 64 ? k_attn_bf16<2> : k_attn_bf16<1>), grid,
-               dim3(256), 0, stream, a);
+  if (!bf16) {  // outputs per thread: the power of two >= H / 2; the query's heads in LDS when H <= 64
+    const size_t qb = (size_t)H * 128 * 4;
+    if (H <= 8) e = launch(3, kProfBoth, k_attn_f32<true, 4>, grid, dim3(256), qb, stream, a);
+    else if (H <= 16) e = launch(3, kProfBoth, k_attn_f32<true, 8>, grid, dim3(256), qb, stream, a);
+    else if (H <= 32) e = launch(3, kProfBoth, k_attn_f32<true, 16>, grid, dim3(256), qb, stream, a);
+    else if (H <= 64) e = launch(3, kProfBoth, k_attn_f32<true, 32>, grid, dim3(256), qb, stream, a);
+    else e = launch(3, kProfBoth, k_attn_f32<false, 64>, grid, dim3(256), 0, stream, a);
+  } else {
+    e = launch(3, kProfBoth, H > 64 ? k_attn_bf16<2> : k_attn_bf16<1>, grid, dim3(256), 0, stream, a);
+  }
   if (e == hipSuccess && a.splits > 1) {
     dim3 gc((unsigned)n_q, (unsigned)H);
     e = launch(4, kProfBoth, bf16 ? k_attn_combine<true> : k_attn_combine<false>, gc, dim3(128), 0, stream,

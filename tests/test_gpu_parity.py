@@ -39,6 +39,12 @@ WORKLOADS = {
                                          codeset=synth.E2M1_TIE_CODES, seed=13),
     "decode_fp32_k1_h24": lambda: small_wl("decode_fp32_k1_h24", [333, 1024], [2, 3], H=24,
                                            dtype="f32", k=1, W=5, m=3, m_hca=16, seed=14),
+    # fp32 head counts that fill a thread's outputs unevenly (5 heads: 640
+    # outputs over 256 threads) and beyond the staged-query limit (100 > 64)
+    "decode_fp32_h5": lambda: small_wl("decode_fp32_h5", [70, 517, 1030], [1, 2, 1], H=5, dtype="f32", k=40,
+                                       W=96, m=4, m_hca=32, W_hca=16, seed=16),
+    "decode_fp32_h100": lambda: small_wl("decode_fp32_h100", [900, 260], [1, 3], H=100, dtype="f32", k=48,
+                                         W=64, m=4, m_hca=16, seed=17),
     "decode_bf16_kbig_whca": lambda: small_wl("decode_bf16_kbig_whca", [200, 900], [1, 4], H=32, k=4000,
                                               W=200, m=4, m_hca=64, W_hca=64, seed=15),
     "prefill_bf16_ties": lambda: small_wl("prefill_bf16_ties", [5000, 9001], [64, 200], k=128,
