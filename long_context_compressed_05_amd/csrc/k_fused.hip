@@ -80,7 +80,15 @@ constexpr int kOffU = kOffScr + 64 * 4;                     // union region
 constexpr int kOffHist = kOffU + kFEntLds * 4;              // uint32 [2][kFHist] + [64] lane trash words
 constexpr int kSelEnd = kOffHist + (2 * kFHist + 64) * 4;
 constexpr int kAttnEnd = kOffU + kAttnLdsBytes;
-constexpr int kFusedLds = kSelEnd > kAttnEnd ? kSelEnd : kAttnEnd;
+constexpr int kFusedLds0 = kSelEnd > kAttnEnd ? kSelEnd : kAttnEnd;
+// The launch's per-row work counts (built once per workgroup before it decodes
+// its first ticket; no phase writes this region): row-major exclusive starts of
+// the ticket-phase score chunks and of the HCA splits, each row's HCA split
+// count, the two totals and whether every row has all n_hs splits.
+enum { T_EB = 0, T_EH = 64, T_NHS = 128, T_UB = 192, T_UH, T_UNIH, T_WORDS = 196 };
+constexpr int kOffTab = (kFusedLds0 + 15) & ~15;
+constexpr int kFusedLds = kOffTab + T_WORDS * 4;
+static_assert(kFMaxRows <= 64, "the row table holds one row per lane of a wave");
 constexpr int kOffSelP = kOffSel + (kFMaxSel + 64) * 4;    // int32 [kFMaxSel] physical rows (paged caches)
 static_assert(kOffSel + (kFMaxSel + 64) * 4 <= kOffScr, "a group's selected rows (+ 64 dummy slots) fit the key region");
 static_assert(kOffSelP + kFMaxSel * 4 <= kOffScr, "the selected rows' physical rows fit the key region");
@@ -1294,11 +1302,11 @@ __device__ __forceinline__ void attend_item(const FCtx& x, int r, int kind, int 
 // HPM (8 or 16) heads of row r from head h0: 256 / HPM threads per head,
 // HPM / 2 output dims per thread
 template <int HPM>
-__device__ __forceinline__ void merge_heads(const FCtx& x, bool hca, int r, int h0) {
+__device__ __forceinline__ void merge_heads(const FCtx& x, bool hca, int r, int h0, int n) {
   KArgs& a = *x.a;
   const int tid = lane_tid();
   const int n_cs = a.n_cs_sel + a.n_cs_win;
-  const int n = hca ? a.n_hs : n_cs;
+  const int ns = hca ? a.n_hs : n_cs;  // partial slots per row
   const float* po = hca ? a.hca_po : a.csa_po;
   const float* pml = hca ? a.hca_pml : a.csa_pml;
   uint8_t* out = hca ? a.hca_out : a.csa_out;
@@ -1317,7 +1325,7 @@ __device__ __forceinline__ void merge_heads(const FCtx& x, bool hca, int r, int 
 #pragma unroll
     for (int u = 0; u < SB; ++u) {
       const int s = s0 + u;
-      const size_t pb = ((size_t)r * n + s) * a.H + h;
+      const size_t pb = ((size_t)r * ns + s) * a.H + h;
       mlv[u] = s < n ? coh_ld64(x.coh, pml + pb * 2) : (uint64_t)__float_as_uint(-INFINITY);
 #pragma unroll
       for (int i = 0; i < DPT; i += 2) {
@@ -1351,22 +1359,24 @@ __device__ __forceinline__ void merge_heads(const FCtx& x, bool hca, int r, int 
   if (lse && d == 0) lse[(size_t)r * a.H + h] = L > 0.f ? (M + __log2f(L)) * kLn2 : -INFINITY;
 }
 
-// merge unit: a.hpm heads of row r from head h0 (4, or 16 for batches of many rows)
-__device__ __forceinline__ void item_merge(const FCtx& x, bool hca, int r, int h0) {
+// merge unit: a.hpm heads of row r from head h0 (4, or 16 for batches of many
+// rows) over the row's first n partials (its n_cs CSA ones, or the HCA splits
+// that were handed out for it; slots past those are not written)
+__device__ __forceinline__ void item_merge(const FCtx& x, bool hca, int r, int h0, int n) {
   KArgs& a = *x.a;
   const int tid = lane_tid();
   const int n_cs = a.n_cs_sel + a.n_cs_win;
-  const int n = hca ? a.n_hs : n_cs;
+  const int ns = hca ? a.n_hs : n_cs;  // partial slots per row
   const uint64_t* hdr = a.part_hdr + (size_t)r * (n_cs + a.n_hs) + (hca ? n_cs : 0);
   bool fail = false;
   for (int s = tid; s < n && !fail; s += 256) (void)poll_word(x, hdr + s, &fail, hca ? 8u : 4u);
   if (!all_ok(x, fail)) return;
   if (a.hpm == 16) {
-    merge_heads<16>(x, hca, r, h0);
+    merge_heads<16>(x, hca, r, h0, n);
     return;
   }
   if (a.hpm == 8) {
-    merge_heads<8>(x, hca, r, h0);
+    merge_heads<8>(x, hca, r, h0, n);
     return;
   }
   // 4 heads: a thread per head and 2 dims, 24 splits per round of loads
@@ -1382,7 +1392,7 @@ __device__ __forceinline__ void item_merge(const FCtx& x, bool hca, int r, int h
 #pragma unroll
     for (int u = 0; u < SB; ++u) {
       const int s = s0 + u;
-      const size_t pb = ((size_t)r * n + s) * a.H + h;
+      const size_t pb = ((size_t)r * ns + s) * a.H + h;
       mlv[u] = s < n ? coh_ld64(x.coh, pml + pb * 2) : (uint64_t)__float_as_uint(-INFINITY);
       ov[u] = s < n ? coh_ld64(x.coh, po + pb * 128 + d) : 0ull;
     }
@@ -1410,11 +1420,71 @@ __device__ __forceinline__ void item_merge(const FCtx& x, bool hca, int r, int h
   if (lse && d == 0) lse[(size_t)r * a.H + h] = L > 0.f ? (M + __log2f(L)) * kLn2 : -INFINITY;
 }
 
+// The row table, built by a workgroup before it decodes its first ticket when
+// the plan has more score chunks than the first round takes (wave 0, lane r =
+// row r): of row r's score chunks, those not numbered below
+// `first` (the first round's chunks, numbered c * R + r) and its HCA splits
+// (every split of the plan when the HCA list ends in a window, otherwise
+// those that hold visible rows), with their row-major exclusive starts.  The
+// ticket units are numbered over these counts, so the empty chunks and
+// splits of short rows in a ragged batch are never handed out.
+__device__ __forceinline__ void build_row_table(const FCtx& x, uint32_t first) {
+  KArgs& a = *x.a;
+  uint32_t* tab = reinterpret_cast<uint32_t*>(x.smem + kOffTab);
+  const int r = lane_tid();
+  if (r < 64) {
+    const int R = a.R;
+    uint32_t eb = 0, eh = 0;
+    if (r < R) {
+      // the chunk count of row_layout (the visible count is at most
+      // kFMaxVisible, so 32-bit arithmetic is exact) and the splits holding
+      // visible HCA rows (at most the plan's n_hs)
+      const FRow f = row_info(a, r, x.paged);
+      const uint32_t nv = f.n_vis > 1 ? (uint32_t)f.n_vis : 1u, C = (uint32_t)a.C;
+      uint32_t nsc = (nv + C - 1u) / C;
+      nsc = nsc > (uint32_t)a.n_sc ? (uint32_t)a.n_sc : nsc;
+      const uint32_t c0 = first > (uint32_t)r ? (first - (uint32_t)r + (uint32_t)R - 1u) / (uint32_t)R : 0u;
+      eb = nsc > c0 ? nsc - c0 : 0u;
+      if (a.W_hca > 0) {
+        eh = (uint32_t)a.n_hs;
+      } else {
+        const int64_t cap = (int64_t)a.n_hs * a.hs;
+        const uint32_t nh = (uint32_t)(f.n_vis_h < cap ? f.n_vis_h : cap), hs = (uint32_t)a.hs;
+        eh = (nh + hs - 1u) / hs;
+      }
+    }
+    const uint32_t ib = wave_incl_add(eb), ih = wave_incl_add(eh);
+    tab[T_EB + r] = ib - eb;
+    tab[T_EH + r] = ih - eh;
+    tab[T_NHS + r] = eh;
+    const bool uni_h = __ballot(r < R && eh != (uint32_t)a.n_hs) == 0ull;
+    if (r == 63) {
+      tab[T_UB] = ib;
+      tab[T_UH] = ih;
+      tab[T_UNIH] = uni_h ? 1u : 0u;
+    }
+  }
+  __syncthreads();
+}
+
+// The row holding unit j of a row-major count table with exclusive starts
+// `starts` (R rows): the last row whose start is <= j (rows with no units
+// share the next row's start and are passed over).  Each wave computes it
+// (one LDS read per lane and a ballot); the result is the same in all.
+__device__ __forceinline__ int table_row(const uint32_t* starts, int R, uint32_t j) {
+  const int l = lane_tid() & 63;
+  const bool le = l < R && starts[l] <= j;
+  return (int)__builtin_popcountll(__ballot(le)) - 1;
+}
+
 // ---------------------------------------------------------------------------
 // kPaged: the pooled caches are read through page tables (csa_hca_decode_paged)
 // (one workgroup per CU, so one wave per SIMD: the compiler is told so and
 // schedules without a second wave's register budget in mind)
-template <bool kPaged>
+// kCompact: the plan has more score chunks than the first round takes, so the
+// ticket units are numbered over the row table (otherwise the table is
+// compiled out and the plan's numbering is used)
+template <bool kPaged, bool kCompact>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_decode_fused(FusedArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
   uint32_t* scr = reinterpret_cast<uint32_t*>(smem + kOffScr);
@@ -1441,10 +1511,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // lowest unfinished unit is either such a chunk, computed by whoever waits
   // for it, or held by a running workgroup whose earlier units are done and
   // never waits: every wait ends however many of the grid's workgroups are
-  // resident at a time.  Every workgroup runs the same number of rounds
-  // (rounds * grid >= total), plus two for every chunk it computes for one
-  // of its groups; a round whose unit number is past the end does nothing.
-  // (Unit numbers fit 32 bits: the plan bounds them far below.)
+  // resident at a time.  The first-round chunks are numbered c * R + r over
+  // the plan's n_sc chunks per row (those of short rows past the row's own
+  // chunk count do nothing); when the plan has more chunks than the first
+  // round takes, the ticket units are numbered over what each row has (the
+  // row table), so a ragged batch hands out no empty chunk or HCA split.  A
+  // workgroup stops at its first ticket past the last unit;
+  // `rounds` bounds the rounds (rounds * grid covers every unit of the plan),
+  // plus two for every chunk it computes for one of its groups.  (Unit
+  // numbers fit 32 bits: the plan bounds them far below.)
   const uint32_t first = (uint32_t)a.first_units;
   const bool by_id = blockIdx.x < first;
   // lane 0: the unit number of the next ticket (fetched one unit ahead) and the
@@ -1456,22 +1531,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // 1: run the chunk in scr[S_PENDC] (for a group of this workgroup), 2: then
   // that group (scr[S_PENDG]) again; such rounds claim nothing and do not count
   int pend = 0;
+  bool tab_ready = false;  // the row table (uniform: every thread takes the same path)
   for (int round = 0; round < rounds; ++round) {
     KArgs* ap = (KArgs*)__builtin_amdgcn_kernarg_segment_ptr();
     asm volatile("" : "+s"(ap));
     KArgs& A = *ap;
     const FCtx x{ap, smem, scr, tag, make_coh(A.ctl), kPaged};
     const int R = A.R, nM = A.H / A.hpm;
-    const int64_t u_grp = (int64_t)R * A.n_sc;
-    const int64_t u_win = u_grp + (int64_t)R * A.n_cs_sel, u_hca = u_win + (int64_t)R * A.n_cs_win;
-    const int64_t u_mh = u_hca + (int64_t)R * A.n_hs, u_mc = u_mh + (int64_t)R * nM;
-    const int64_t total = u_mc + (int64_t)R * nM;
     int64_t it;
+    // a score chunk numbered c * R + r: the first round's, or one computed for a group
+    bool old_chunk = false;
     if (pend != 0) {
       it = (int64_t)uni(scr[pend == 1 ? S_PENDC : S_PENDG]);
+      old_chunk = pend == 1;
     } else {
       if (round == 0 && by_id) {
         it = (int64_t)blockIdx.x;
+        old_chunk = true;
       } else {
         if (lane_tid() == 0) scr[S_TICKET] = next_ticket;
         __syncthreads();
@@ -1482,31 +1558,84 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       // this round's work.  A workgroup still runs its units in claim order.
       if (round + 1 < rounds && lane_tid() == 0) next_ticket = first + atomicAdd(A.ctl + W_TICKET, 1u);
     }
-    if (it >= total) {
-      // nothing to do this round
-    } else if (it < u_grp) {
+    // Ticket units (t = it - first), in dependency order: [the rows' remaining
+    // score chunks | CSA groups | CSA window splits | HCA splits | HCA merges |
+    // CSA merges]; units only wait for units of lower number.  When every
+    // chunk of the plan ran in the first round (R * n_sc <= first, as in
+    // batches of equal long rows) the units are the plan's (HCA splits
+    // split-major, R * n_hs of them, those past a row's rows doing nothing);
+    // otherwise they are numbered over the row table, which leaves out the
+    // empty chunks and HCA splits of short rows (a ragged batch) at the cost
+    // of building the table (one round of loads) before the first ticket.
+    // The unit is decoded first (kind, row, index), then run from one call
+    // site per kind (each phase is inlined once).
+    int kind;  // 0 score chunk, 1 CSA group, 2 CSA window split, 3 HCA split, 4 HCA merge, 5 CSA merge
+    int r, ui;
+    int n_merge = 0;
+    if (old_chunk) {
       // chunk-major: every row's first chunks come first (a short row uses fewer chunks)
-      const int c = (int)(it / R), r = (int)(it % R);
+      kind = 0;
+      ui = (int)(it / R);
+      r = (int)(it % R);
+    } else {
+      constexpr bool compact = kCompact;
+      if (compact && !tab_ready) {  // once per workgroup
+        build_row_table(x, first);
+        tab_ready = true;
+      }
+      const uint32_t* tab = reinterpret_cast<const uint32_t*>(smem + kOffTab);
+      const int64_t t = it - (int64_t)first;
+      const int64_t t_grp = compact ? (int64_t)tab[T_UB] : 0;
+      const int64_t t_win = t_grp + (int64_t)R * A.n_cs_sel, t_hca = t_win + (int64_t)R * A.n_cs_win;
+      const int64_t t_mh = t_hca + (compact ? (int64_t)tab[T_UH] : (int64_t)R * A.n_hs);
+      const int64_t t_mc = t_mh + (int64_t)R * nM, t_end = t_mc + (int64_t)R * nM;
+      if (t >= t_end) break;  // every unit is handed out: no further claims
+      if (t < t_grp) {
+        kind = 0;
+        r = table_row(tab + T_EB, R, (uint32_t)t);
+        const uint32_t c0 = first > (uint32_t)r ? (first - (uint32_t)r + (uint32_t)R - 1u) / (uint32_t)R : 0u;
+        ui = (int)(c0 + ((uint32_t)t - tab[T_EB + r]));
+      } else if (t >= t_mh) {
+        kind = t < t_mc ? 4 : 5;
+        const int64_t m = t - (kind == 4 ? t_mh : t_mc);
+        r = (int)(m / nM);
+        ui = (int)(m % nM) * A.hpm;
+        n_merge = kind == 4 ? (compact ? (int)tab[T_NHS + r] : A.n_hs) : A.n_cs_sel + A.n_cs_win;
+      } else if (t < t_hca) {
+        kind = t < t_win ? 1 : 2;
+        const int64_t q = t - (kind == 1 ? t_grp : t_win);
+        r = (int)(q % R);
+        ui = (int)(q / R);
+      } else {  // HCA split: split-major when every row has all of them, else row-major
+        kind = 3;
+        const uint32_t j = (uint32_t)(t - t_hca);
+        if (!compact || tab[T_UNIH] != 0u) {
+          r = (int)(j % (uint32_t)R);
+          ui = (int)(j / (uint32_t)R);
+        } else {
+          r = table_row(tab + T_EH, R, j);
+          ui = (int)(j - tab[T_EH + r]);
+        }
+      }
+    }
+    if (kind == 0) {  // score chunk ui of row r
       const FRow f = row_info(A, r, kPaged);
       const RowLayout lay = row_layout(A, f);
-      if (c < lay.nsc) {
-        int64_t j0 = (int64_t)c * lay.C, j1 = j0 + lay.C;
+      if (ui < lay.nsc) {
+        int64_t j0 = (int64_t)ui * lay.C, j1 = j0 + lay.C;
         if (j1 > f.n_vis) j1 = f.n_vis;
         if (j0 > j1) j0 = j1;
-        phase_score(x, r, c, f, j0, j1);
+        phase_score(x, r, ui, f, j0, j1);
       }
       if (pend == 1) {  // computed for a group of this workgroup: out before it reads them back
         vm_drain();
         __syncthreads();
         pend = 2;
       }
-    } else if (it >= u_mh) {
-      const bool hca = it < u_mc;
-      const int64_t m = it - (hca ? u_mh : u_mc);
-      item_merge(x, hca, (int)(m / nM), (int)(m % nM) * A.hpm);
-    } else if (it < u_win) {
-      const int64_t q = it - u_grp;
-      const int r = (int)(q % R), g = (int)(q / R);
+    } else if (kind >= 4) {
+      item_merge(x, kind == 4, r, ui, n_merge);
+    } else if (kind == 1) {
+      const int g = ui;
       const FRow f = row_info(A, r, kPaged);
       uint32_t off = 0, base = 0;
       bool phys = false;
@@ -1532,11 +1661,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         group_write_idx(x, r, off, n_sel, base);
       }
     } else {
-      // attention: kind 1 = CSA window split, 2 = HCA split
-      const int kind = it < u_hca ? 1 : 2;
-      const int64_t q = it - (kind == 1 ? u_win : u_hca);
-      const int r = (int)(q % R), s = (int)(q / R);
-      attend_item(x, r, kind, s, row_info(A, r, kPaged), 0);
+      // a CSA window split (attend_item's kind 1) or an HCA split (its kind 2)
+      attend_item(x, r, kind == 2 ? 1 : 2, ui, row_info(A, r, kPaged), 0);
     }
   }
   const int G = (int)gridDim.x;
@@ -1569,12 +1695,16 @@ static int fused_grid() {
     if (g > 0) return g;
   }
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-  if (hipFuncSetAttribute((const void*)k_decode_fused<false>, hipFuncAttributeMaxDynamicSharedMemorySize,
+  if (hipFuncSetAttribute((const void*)k_decode_fused<false, false>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                          kFusedLds0) != hipSuccess ||
+      hipFuncSetAttribute((const void*)k_decode_fused<true, false>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                          kFusedLds0) != hipSuccess ||
+      hipFuncSetAttribute((const void*)k_decode_fused<false, true>, hipFuncAttributeMaxDynamicSharedMemorySize,
                           kFusedLds) != hipSuccess ||
-      hipFuncSetAttribute((const void*)k_decode_fused<true>, hipFuncAttributeMaxDynamicSharedMemorySize,
+      hipFuncSetAttribute((const void*)k_decode_fused<true, true>, hipFuncAttributeMaxDynamicSharedMemorySize,
                           kFusedLds) != hipSuccess)
     return 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)k_decode_fused<false>, 256, kFusedLds) !=
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)k_decode_fused<false, true>, 256, kFusedLds) !=
       hipSuccess)
     return 0;
   if (per_cu < 1 || cus < 1) return 0;
@@ -1746,8 +1876,13 @@ int launch_fused(int R, const int64_t* tok_off, const int64_t* q_pos, const int6
   a.hca_po = (float*)take((size_t)R * pl.n_hs * H * 128 * 4);
   a.hca_pml = (float*)take((size_t)R * pl.n_hs * H * 2 * 4);
   // an ordinary launch of one workgroup per CU
-  const hipError_t e = launch(6, kProfBoth, paging ? k_decode_fused<true> : k_decode_fused<false>,
-                              dim3((unsigned)pl.grid), dim3(256), kFusedLds, stream, a);
+  // the row table only when some chunks are left past the first round (a.first_units)
+  const bool compact = (int64_t)R * pl.n_sc > (int64_t)a.first_units;
+  const hipError_t e =
+      compact ? launch(6, kProfBoth, paging ? k_decode_fused<true, true> : k_decode_fused<false, true>,
+                       dim3((unsigned)pl.grid), dim3(256), kFusedLds, stream, a)
+              : launch(6, kProfBoth, paging ? k_decode_fused<true, false> : k_decode_fused<false, false>,
+                       dim3((unsigned)pl.grid), dim3(256), kFusedLds0, stream, a);
   if (e != hipSuccess) return -1;
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }

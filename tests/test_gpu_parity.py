@@ -492,6 +492,10 @@ def test_prefill_topk_long_caches(codeset):
     rows = sorted(set([0, int(q_off[1]) - 1, int(q_off[1]), wl.n_q - 1] + list(range(0, wl.n_q, 4))))
     _index_rows(wl, host, rows)
 
+_MANY_ROWS = [1, 2, 3, 5, 17, 64, 100, 127, 128, 129, 200, 255, 256, 257, 300, 511, 512, 513, 700, 1000,
+              30001, 1030, 1500, 2049, 2500, 3001, 3500, 4099, 4500, 5003, 32000, 5555, 6000, 6100, 640, 90, 7,
+              2222, 999, 32771]
+
 FUSED_CASES = {
     "decode_bf16_ragged": lambda: small_wl("decode_bf16_ragged", [1, 3, 130, 517, 1030, 2049, 4099], [1] * 7,
                                            k=64, seed=11),
@@ -503,6 +507,14 @@ FUSED_CASES = {
                                          seed=16),
     # one long row: 74 chunks of 1024, 4440 list positions (the 24-slot selection)
     "decode_bf16_single_300k": lambda: small_wl("decode_bf16_single_300k", [300001], [1], k=1024, seed=18),
+    # 40 rows, two of them long: the plan has 7 chunks of 1280 per row (280 >
+    # 256 first-round units), so rows 30 and 39 have their last chunk handed
+    # out by ticket, and the ticket units are numbered over the row table
+    # (rows without HCA rows get no split and merge zero partials)
+    "decode_bf16_many_rows": lambda: small_wl("decode_bf16_many_rows", _MANY_ROWS, [1] * 40, k=200, seed=19),
+    # the same rows with an HCA window: every row keeps all of its HCA splits
+    "decode_bf16_many_rows_whca": lambda: small_wl("decode_bf16_many_rows_whca", _MANY_ROWS, [1] * 40, k=200,
+                                                   m_hca=64, W_hca=64, seed=20),
 }
 
 
