@@ -45,7 +45,8 @@
 
 namespace csa {
 
-constexpr int kPfRowsT = 4;        // queries per threshold block: one per wave (half an MFMA A operand)
+constexpr int kPfRowsT = 8;        // queries per threshold block: one per wave (one MFMA A operand)
+constexpr int kPfThreads = 64 * kPfRowsT;
 constexpr int kPfRows = 16;        // queries per score block (two MFMA A operands)
 constexpr int kPfKeysWG = 4096;    // keys per scoring workgroup, at least (a multiple of 128)
 constexpr int kPfSampleMax = 2048;  // sample keys per query
@@ -276,10 +277,10 @@ __device__ __forceinline__ uint32_t wave_kth(const uint32_t (&kv)[NK], uint32_t 
 // ---------------------------------------------------------------------------
 // 1. thresholds from a sample of key runs
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_pf_thresh(PfArgs a) {
+__global__ __launch_bounds__(kPfThreads) void k_pf_thresh(PfArgs a) {
   extern __shared__ __align__(16) uint32_t pf_sm[];
   uint32_t* ss = pf_sm;                                          // [kPfRowsT][ns_max]
-  uint32_t* wh = pf_sm + (size_t)kPfRowsT * a.ns_max;            // [4][kPfWaveHist]
+  uint32_t* wh = pf_sm + (size_t)kPfRowsT * a.ns_max;            // [kPfRowsT][kPfWaveHist]
   const int tid = threadIdx.x, lane = tid & 63, kb = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int b = blockIdx.x / a.bps_t, t = blockIdx.x % a.bps_t;
@@ -288,7 +289,7 @@ __global__ __launch_bounds__(256) void k_pf_thresh(PfArgs a) {
   if (nrows == 0) return;
   const int64_t pbase = a.pool_off[b], P = a.pool_off[b + 1] - pbase;
   __builtin_amdgcn_s_setprio(3);  // lowered for the radix pass (waves of a SIMD progress together)
-  for (int i = tid; i < 4 * kPfWaveHist; i += 256) wh[i] = 0u;
+  for (int i = tid; i < kPfRowsT * kPfWaveHist; i += kPfThreads) wh[i] = 0u;
   v8i a0;
   int s0;
   pf_load_a(a, row0, nrows, lane, a0, s0);
@@ -297,20 +298,20 @@ __global__ __launch_bounds__(256) void k_pf_thresh(PfArgs a) {
   // not wait for the positions); at most 64 tiles (the stride is >= P / 2048)
   const int64_t st = a.stride, span = 32 * st;
   const int ntiles = (int)((P + span - 1) / span);  // ntiles * 32 <= ns_max
-  // 16 tiles per wave in flight: the whole sample takes one round of loads
+  // up to 16 tiles per wave in flight: the whole sample takes one round of loads
   constexpr int kTB = 16;
-  for (int tb = wave; tb < ntiles; tb += 4 * kTB) {
+  for (int tb = wave; tb < ntiles; tb += kPfRowsT * kTB) {
     uint4 kc[kTB];
     int ks[kTB];
 #pragma unroll
     for (int u = 0; u < kTB; ++u) {
       // 32-bit: P <= max_pool <= 2^30 (checked at the boundary), so j < 2^31
-      const int j = (tb + 4 * u) * (int)span + (lane & 31);
-      pf_load_b(a, pbase + j, tb + 4 * u < ntiles && j < (int)P, kb, kc[u], ks[u]);
+      const int j = (tb + kPfRowsT * u) * (int)span + (lane & 31);
+      pf_load_b(a, pbase + j, tb + kPfRowsT * u < ntiles && j < (int)P, kb, kc[u], ks[u]);
     }
 #pragma unroll
     for (int u = 0; u < kTB; ++u) {
-      const int tile = tb + 4 * u;
+      const int tile = tb + kPfRowsT * u;
       if (tile >= ntiles) break;
       const int i = tile * 32 + (lane & 31);
       const v16f c0 = pf_mfma(a0, s0, kc[u], ks[u]);
@@ -324,7 +325,7 @@ __global__ __launch_bounds__(256) void k_pf_thresh(PfArgs a) {
   __syncthreads();
   __builtin_amdgcn_s_setprio(1);
   uint32_t* hist = wh + wave * kPfWaveHist;
-  for (int q = wave; q < nrows; q += 4) {
+  for (int q = wave; q < nrows; q += kPfRowsT) {
     const int64_t row = row0 + q;
     const int64_t nvis = pf_nvis(a.q_pos[row], a.m, P);
     const int64_t k_eff = nvis < a.k ? nvis : a.k;
@@ -745,15 +746,17 @@ int launch_prefill_topk(int n_seq, int64_t n_q, int64_t max_q_per_seq, const int
   a.tau = (uint32_t*)p;
   a.bitmap = (uint32_t*)(p + (((size_t)n_q * 4 + 255) & ~(size_t)255));
   a.idx = idx;
-  const size_t lds1 = ((size_t)kPfRowsT * a.ns_max + 4 * kPfWaveHist) * 4;
+  const size_t lds1 = ((size_t)kPfRowsT * a.ns_max + kPfRowsT * kPfWaveHist) * 4;
   const size_t lds3 = (size_t)2 * (kPfCand + kSelWaveHist) * 4;
   static_assert((size_t)2 * (kPfCand + kSelWaveHist) * 4 * 8 <= 160 * 1024, "8 selection workgroups per CU");
   // the threshold kernel's LDS can exceed the default dynamic limit (idempotent,
   // so concurrent first calls need no ordering)
   (void)hipFuncSetAttribute((const void*)k_pf_thresh, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)(((size_t)kPfRowsT * kPfSampleMax + 4 * kPfWaveHist) * 4));
+                            (int)(((size_t)kPfRowsT * kPfSampleMax + kPfRowsT * kPfWaveHist) * 4));
+  static_assert(((size_t)kPfRowsT * kPfSampleMax + kPfRowsT * kPfWaveHist) * 4 <= 160 * 1024,
+                "the threshold block's samples and histograms fit a CU's LDS");
   const unsigned nblk = (unsigned)(n_seq * a.bps);
-  hipError_t e = launch(7, kProfBoth, k_pf_thresh, dim3((unsigned)(n_seq * a.bps_t)), dim3(256), lds1, stream, a);
+  hipError_t e = launch(7, kProfBoth, k_pf_thresh, dim3((unsigned)(n_seq * a.bps_t)), dim3(kPfThreads), lds1, stream, a);
   a.kw = pf_keys_per_wg(max_pool, (int64_t)nblk);
   dim3 g2((unsigned)((max_pool + a.kw - 1) / a.kw), nblk);
   if (g2.x == 0) g2.x = 1;
