@@ -496,6 +496,10 @@ _MANY_ROWS = [1, 2, 3, 5, 17, 64, 100, 127, 128, 129, 200, 255, 256, 257, 300, 5
               30001, 1030, 1500, 2049, 2500, 3001, 3500, 4099, 4500, 5003, 32000, 5555, 6000, 6100, 640, 90, 7,
               2222, 999, 32771]
 
+_SHARED_TAILS = [1, 5, 77, 130, 300, 517, 1000, 2049, 3001, 4099, 5003, 6000, 7, 90, 640, 999, 2222, 1500, 2500,
+                 3500, 4500, 5555, 6100, 700, 200, 255, 256, 257, 511, 512, 513, 1030, 33, 64, 100, 127, 128, 129,
+                 17]
+
 FUSED_CASES = {
     "decode_bf16_ragged": lambda: small_wl("decode_bf16_ragged", [1, 3, 130, 517, 1030, 2049, 4099], [1] * 7,
                                            k=64, seed=11),
@@ -680,6 +684,10 @@ SHARED_CASES = {
     # the prefix's tokens and its own
     "shared_straddle": (lambda: small_wl("decode_shared_straddle", [20003, 4226 + 5001, 4226 + 77, 4226 + 2],
                                          [1] * 4, k=256, seed=35), 4226),
+    # 40 rows over one 8192-token prefix; the longest row's 16,384 pooled entries
+    # give 7 chunks per row (280 > 256 first-round units): the compact form
+    "shared_many_rows": (lambda: small_wl("decode_shared_many", [65539] + [8192 + v for v in _SHARED_TAILS],
+                                          [1] * 40, k=200, seed=36), 8192),
 }
 
 
@@ -792,6 +800,9 @@ PAGED_CASES = {
     "paged_p256_h64_shared": (lambda: small_wl("decode_paged_sh", [30000, 8192 + 6001, 2050], [1] * 3, H=32, k=300,
                                                W=200, m_hca=64, W_hca=64, seed=42), 256, 64, 8192),
     "paged_long": (lambda: small_wl("decode_paged_long", [262147, 131075], [1] * 2, k=1024, seed=43), 128, 32, 0),
+    # 40 rows whose plan leaves chunks past the first round: the compact form
+    # (ticket units over the row table) through page tables
+    "paged_many_rows": (lambda: small_wl("decode_paged_many", _MANY_ROWS, [1] * 40, k=200, seed=44), 64, 32, 0),
     # every row takes the exact fallback (its entries come from the stored keys)
     "paged_concentrated": (lambda: small_wl("decode_paged_conc", [40001, 30002], [1, 1], k=1024, seed=17), 64, 32, 0,
                            "concentrate"),
