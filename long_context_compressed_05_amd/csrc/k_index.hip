@@ -383,9 +383,9 @@ __global__ __launch_bounds__(1024) void k_idx_final(FinalArgs a) {
   extern __shared__ uint32_t bitmap[];  // ceil(max_pool / 32) words when use_bitmap
   __shared__ int32_t outj[4096];
   __shared__ uint2 cand_s[kCandLds];
-  __shared__ uint32_t bins[256];
-  __shared__ uint32_t scratch[24];
-  __shared__ uint32_t n_out;
+  __shared__ uint32_t bins[1024];
+  __shared__ uint32_t scratch[32];
+  __shared__ uint32_t n_out, n_eq;
   const int64_t row = blockIdx.x;
   const int tid = threadIdx.x;
   const int b = seq_of_row(a.q_off, a.n_seq, row);
@@ -403,13 +403,33 @@ __global__ __launch_bounds__(1024) void k_idx_final(FinalArgs a) {
       __syncthreads();
       cand = cand_s;
     }
+    // Every candidate lies in the threshold bin b1 (its key >> kBinShift), so
+    // only the keys' low kBinShift bits are left to resolve (two rounds of
+    // at most 10 bits instead of four of 8 over the whole key).
+    const uint32_t fixed = cand[0].x & ~((1u << kBinShift) - 1u);
     uint32_t r;
-    const uint32_t kstar = radix_select_desc(
-        n_c, need, [&](uint32_t i) { return cand[i].x; }, [&](uint32_t) { return true; }, &r, bins, scratch);
-    uint32_t r2;
-    const uint32_t jstar = radix_select_desc(
-        n_c, r, [&](uint32_t i) { return ~cand[i].y; }, [&](uint32_t i) { return cand[i].x == kstar; }, &r2,
+    const uint32_t kstar = radix_select_desc_low(
+        n_c, need, kBinShift, fixed, [&](uint32_t i) { return cand[i].x; }, [&](uint32_t) { return true; }, &r,
         bins, scratch);
+    // r of the candidates equal to K* are taken: all of them unless ties are
+    // cut, and then the r lowest indices (the largest complements ~j, whose
+    // bits above the index width are all ones)
+    if (tid == 0) n_eq = 0;
+    __syncthreads();
+    {
+      uint32_t e = 0;
+      for (uint32_t i = tid; i < n_c; i += blockDim.x) e += cand[i].x == kstar ? 1u : 0u;
+      if (e) atomicAdd(&n_eq, e);
+    }
+    __syncthreads();
+    uint32_t jstar = 0;  // every tie taken
+    if (n_eq > r) {
+      const int ibits = a.max_pool > 1 ? 64 - __clzll((unsigned long long)(a.max_pool - 1)) : 0;
+      uint32_t r2;
+      jstar = radix_select_desc_low(
+          n_c, r, ibits, ibits >= 32 ? 0u : (~0u << ibits), [&](uint32_t i) { return ~cand[i].y; },
+          [&](uint32_t i) { return cand[i].x == kstar; }, &r2, bins, scratch);
+    }
     auto chosen = [&](uint2 c) { return c.x > kstar || (c.x == kstar && ~c.y >= jstar); };
     if (a.use_bitmap) {
       // ascending order from a bitmap of the visible range
