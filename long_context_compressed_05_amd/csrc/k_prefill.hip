@@ -198,7 +198,8 @@ __device__ __forceinline__ uint32_t pf_tile_word(const v8i (&av)[2], const int (
 // zeroed words, left zeroed, + 64 trash words); only slots i < nk (uniform)
 // are looked at.  No barriers.  *gt = the keys above the result.  With
 // MAXPASS < 4 the result is the lower edge of the last bin found, a value
-// with at least `need` keys at or above it.
+// with at least `need` keys at or above it; otherwise a pass that leaves at
+// most 64 keys in its bin is finished by ranking them against each other.
 template <int NK, int MAXPASS = 4, int BINS = kPfBins>
 __device__ __forceinline__ uint32_t wave_kth(const uint32_t (&kv)[NK], uint32_t vm, int nk, uint32_t need,
                                              uint32_t* hist, uint32_t* gt) {
@@ -267,6 +268,35 @@ __device__ __forceinline__ uint32_t wave_kth(const uint32_t (&kv)[NK], uint32_t 
       for (int i = 0; i < NK; ++i) v = (((vm >> i) & 1u) && kv[i] >= lo && kv[i] <= hi) ? kv[i] : v;
       uint32_t dummy = 0xffffffffu;
       wave_minmax(dummy, v);
+      lo = hi = v;
+    } else if (MAXPASS > 1 && cnt <= 64u && lo != hi) {
+      // at most 64 keys left in [lo, hi]: gather them into the (zeroed) bins
+      // and rank each against the others instead of another pass; the key
+      // with (greater < need <= greater + equal) is the answer
+      uint32_t at = 0;
+      const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+#pragma unroll
+      for (int i = 0; i < NK; ++i) {
+        if (i >= nk) break;
+        const bool in = ((vm >> i) & 1u) && kv[i] >= lo && kv[i] <= hi;
+        const uint64_t m = __ballot(in);
+        if (in) hist[at + (uint32_t)__popcll(m & below)] = kv[i];
+        at += (uint32_t)__popcll(m);
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's stores, before its lanes read them
+      const uint32_t mine = lane < (int)cnt ? hist[lane] : 0u;
+      uint32_t g = 0, e = 0;
+      for (uint32_t j = 0; j < cnt; ++j) {
+        const uint32_t o = hist[j];
+        g += o > mine ? 1u : 0u;
+        e += o == mine ? 1u : 0u;
+      }
+      const uint64_t hit = __ballot(lane < (int)cnt && g < need && g + e >= need);
+      const int src = (int)__builtin_ctzll(hit);
+      const uint32_t v = (uint32_t)__builtin_amdgcn_readlane((int)mine, src);
+      above_all += (uint32_t)__builtin_amdgcn_readlane((int)g, src);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // every lane's reads, before the bins are cleared
+      if (lane < (int)cnt) hist[lane] = 0u;
       lo = hi = v;
     }
   }
