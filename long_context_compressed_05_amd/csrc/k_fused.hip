@@ -104,7 +104,8 @@ typedef unsigned int v2u_t __attribute__((ext_vector_type(2)));
 typedef unsigned int v4u_t __attribute__((ext_vector_type(4)));
 constexpr uint32_t kNoKey = 0xffffffffu;  // empty list position (scores are finite and >= 0)
 
-// scratch word indices (0..19 are used by the block scans and searches)
+// scratch word indices (0..19 are used by the block scans and searches, 20..35
+// by the CSA group's first reduction)
 enum { S_TAG = 40, S_FLAG, S_DIGIT, S_ABOVE, S_CNT, S_BAD, S_TICKET, S_KEY, S_CUT, S_OFF, S_STEAL, S_PENDC, S_PENDG, S_END };
 
 struct FusedArgs {
@@ -540,10 +541,22 @@ __device__ __forceinline__ void radix_pass(const uint32_t (&kv)[NK], uint32_t vm
 // equal to it (n_valid when they are all equal).  hist: 2 x 2048 + 64 words of
 // LDS, 16-byte aligned.
 template <int NK>
+__device__ __forceinline__ uint32_t kth_key_in(const uint32_t (&kv)[NK], uint32_t vm, uint32_t need, uint32_t n_valid,
+                                               uint32_t* hist, uint32_t* scr, uint32_t* gt, uint32_t* eq,
+                                               uint32_t lo, uint32_t hi);
+template <int NK>
 __device__ __forceinline__ uint32_t kth_key(const uint32_t (&kv)[NK], uint32_t vm, uint32_t need, uint32_t n_valid,
                                             uint32_t* hist, uint32_t* scr, uint32_t* gt, uint32_t* eq) {
   uint32_t lo, hi;
   key_range<NK>(kv, vm, hist, scr, &lo, &hi);
+  return kth_key_in<NK>(kv, vm, need, n_valid, hist, scr, gt, eq, lo, hi);
+}
+// The same search when the keys' range [lo, hi] is known and both histograms
+// are zeroed (and a barrier has ordered that before the first pass).
+template <int NK>
+__device__ __forceinline__ uint32_t kth_key_in(const uint32_t (&kv)[NK], uint32_t vm, uint32_t need, uint32_t n_valid,
+                                               uint32_t* hist, uint32_t* scr, uint32_t* gt, uint32_t* eq,
+                                               uint32_t lo, uint32_t hi) {
   uint32_t above_all = 0, in_range = n_valid;
 #pragma unroll 1
   for (int pass = 0; pass < 3 && lo != hi; ++pass) {
@@ -1019,24 +1032,42 @@ __device__ __forceinline__ int group_select(const FCtx& x, int r, int g, const F
   // the group has the lowest such chunk computed by its own workgroup and is
   // run again.  A score chunk is a pure function of the inputs, so a second
   // run of it (by a late owner) rewrites identical words.
-  if (tid == 0) {
-    x.scr[S_BAD] = 0;
-    x.scr[S_FLAG] = 0;
-    x.scr[S_STEAL] = 0xffffffffu;
+  // One round of wave reductions and one barrier give every thread the
+  // failure and steal flags, the number of listed entries and their key
+  // range (K*'s first pass needs no range pass of its own); the radix
+  // histograms are cleared beside them.
+  uint32_t wfail, wsteal, n_ent, klo, khi;
+  {
+    const int lane = tid & 63, wave = tid >> 6;
+    uint32_t mn = 0xffffffffu, mx = 0u;
+#pragma unroll
+    for (int u = 0; u < kFEPT; ++u) {
+      const bool v = (vm >> u) & 1u;
+      mn = v && kv[u] < mn ? kv[u] : mn;
+      mx = v && kv[u] > mx ? kv[u] : mx;
+    }
+    wave_minmax(mn, mx);
+    uint32_t st = steal ? steal_c : 0xffffffffu, st_hi = 0u;
+    wave_minmax(st, st_hi);
+    const uint32_t cnt = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_add((uint32_t)__builtin_popcount(vm)), 63);
+    const bool wf = __ballot(fail) != 0ull;
+    for (int i = tid; i < 2 * kFHist / 4; i += 256) reinterpret_cast<uint4*>(hist)[i] = make_uint4(0u, 0u, 0u, 0u);
+    if (tid == 0) x.scr[S_BAD] = 0;
+    if (lane == 0) *reinterpret_cast<uint4*>(x.scr + 20 + 4 * wave) = make_uint4(cnt, mn, mx, wf ? 0xfffffffeu : st);
+    __syncthreads();
+    const uint4 r0 = *reinterpret_cast<const uint4*>(x.scr + 20), r1 = *reinterpret_cast<const uint4*>(x.scr + 24);
+    const uint4 r2 = *reinterpret_cast<const uint4*>(x.scr + 28), r3 = *reinterpret_cast<const uint4*>(x.scr + 32);
+    n_ent = uni(r0.x + r1.x + r2.x + r3.x);
+    klo = uni(min(min(r0.y, r1.y), min(r2.y, r3.y)));
+    khi = uni(max(max(r0.z, r1.z), max(r2.z, r3.z)));
+    wfail = (r0.w == 0xfffffffeu || r1.w == 0xfffffffeu || r2.w == 0xfffffffeu || r3.w == 0xfffffffeu) ? 1u : 0u;
+    wsteal = uni(min(min(r0.w, r1.w), min(r2.w, r3.w)));
   }
-  __syncthreads();
-  if (fail) x.scr[S_FLAG] = 1u;
-  if (steal) atomicMin(&x.scr[S_STEAL], steal_c);
-  __syncthreads();
-  const uint32_t wfail = uni(x.scr[S_FLAG]), wsteal = uni(x.scr[S_STEAL]);
-  __syncthreads();
   if (wfail) return -1;
   if (wsteal != 0xffffffffu) {
     *off_out = wsteal;
     return -2;
   }
-  uint32_t n_ent;
-  (void)block_exscan_val((uint32_t)__builtin_popcount(vm), x.scr, &n_ent);
   bool exact = n_ent >= (uint32_t)k_eff;
   uint32_t kstar = 0, gt_all = 0, eq_all = 0;
   uint32_t* lk = reinterpret_cast<uint32_t*>(x.smem + kOffU);  // [npos] keys by position
@@ -1046,9 +1077,9 @@ __device__ __forceinline__ int group_select(const FCtx& x, int r, int g, const F
       uint32_t kv16[16];
 #pragma unroll
       for (int u = 0; u < 16; ++u) kv16[u] = kv[u];
-      kstar = kth_key<16>(kv16, vm & 0xffffu, (uint32_t)k_eff, n_ent, hist, x.scr, &gt_all, &eq_all);
+      kstar = kth_key_in<16>(kv16, vm & 0xffffu, (uint32_t)k_eff, n_ent, hist, x.scr, &gt_all, &eq_all, klo, khi);
     } else {
-      kstar = kth_key<kFEPT>(kv, vm, (uint32_t)k_eff, n_ent, hist, x.scr, &gt_all, &eq_all);
+      kstar = kth_key_in<kFEPT>(kv, vm, (uint32_t)k_eff, n_ent, hist, x.scr, &gt_all, &eq_all, klo, khi);
     }
     for (int sl = tid; sl < nsc; sl += 256)
       if (e_tau[sl] > kstar) x.scr[S_BAD] = 1;
@@ -1556,7 +1587,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       }
       // claim the next round's unit now: the returning atomic's latency overlaps
       // this round's work.  A workgroup still runs its units in claim order.
-      if (round + 1 < rounds && lane_tid() == 0) next_ticket = first + atomicAdd(A.ctl + W_TICKET, 1u);
+      // (The compact form claims once the unit is decoded, below.)
+      if (!kCompact && round + 1 < rounds && lane_tid() == 0) next_ticket = first + atomicAdd(A.ctl + W_TICKET, 1u);
     }
     // Ticket units (t = it - first), in dependency order: [the rows' remaining
     // score chunks | CSA groups | CSA window splits | HCA splits | HCA merges |
@@ -1618,6 +1650,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         }
       }
     }
+    // In the compact form (ragged batches) a CSA group's workgroup claims its
+    // next unit only once its group is done: a group ends late, and group
+    // workgroups arrive first for the next round's tickets, so the units they
+    // would hold start last (ragged 32 rows: 65.3 -> 55.6 us; with equal rows
+    // it measured no better).  Every other unit claims the next one now.
+    if (kCompact && pend == 0 && kind != 1 && round + 1 < rounds && lane_tid() == 0)
+      next_ticket = first + atomicAdd(A.ctl + W_TICKET, 1u);
     if (kind == 0) {  // score chunk ui of row r
       const FRow f = row_info(A, r, kPaged);
       const RowLayout lay = row_layout(A, f);
@@ -1660,6 +1699,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         attend_item(x, r, 0, g, f, n_sel, base);
         group_write_idx(x, r, off, n_sel, base);
       }
+      if (kCompact && n_sel != -2 && round + 1 < rounds && lane_tid() == 0)
+        next_ticket = first + atomicAdd(A.ctl + W_TICKET, 1u);
     } else {
       // a CSA window split (attend_item's kind 1) or an HCA split (its kind 2)
       attend_item(x, r, kind == 2 ? 1 : 2, ui, row_info(A, r, kPaged), 0);
