@@ -501,6 +501,136 @@ size_t index_ws_bytes(int64_t n_q, int64_t max_q_per_seq, int64_t max_pool, int 
   return s;
 }
 
+// A query whose sequence has at most kSmallPool pooled entries (a short
+// decode cache) is selected by one workgroup in one launch: its visible keys
+// are scored into LDS (16 waves, 32-key MFMA tiles), K* is found by a radix
+// select over the keys' own range (the bits above it are common to every key),
+// ties at K* are cut at the lowest indices (a second select over the
+// complemented indices, only when some are left out), and the chosen entries
+// are emitted in ascending order from an LDS bitmap.  The workspace is not
+// touched (it stays zero-filled).
+constexpr int kSmallPool = 4096;
+
+struct SmallArgs {
+  const int64_t* q_off;
+  const int64_t* q_pos;
+  const int64_t* pool_off;
+  int n_seq, m, k;
+  const uint8_t* q_codes;
+  const uint8_t* q_scales;
+  const float* w;
+  const uint8_t* k_codes;
+  const uint8_t* k_scales;
+  int32_t* idx;
+};
+
+__global__ __launch_bounds__(1024) void k_idx_small(SmallArgs a) {
+  __shared__ uint32_t keys_s[kSmallPool];
+  __shared__ uint32_t bins[1024];
+  __shared__ uint32_t bitmap[kSmallPool / 32];
+  __shared__ uint32_t scratch[32];
+  __shared__ uint32_t red[2][16];
+  __shared__ uint32_t n_eq;
+  const int64_t row = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int b = seq_of_row(a.q_off, a.n_seq, row);
+  const int64_t pbase = a.pool_off[b], P = a.pool_off[b + 1] - pbase;
+  int64_t nv = n_visible(a.q_pos[row], a.m, P);
+  const int nvis = (int)(nv < kSmallPool ? nv : kSmallPool);  // P <= max_pool <= kSmallPool
+  const int k_eff = nvis < a.k ? nvis : a.k;
+  int32_t* idx = a.idx + row * a.k;
+  for (int i = k_eff + tid; i < a.k; i += blockDim.x) idx[i] = -1;
+  if (k_eff == nvis) {  // every visible entry is taken (none when nothing is visible)
+    for (int i = tid; i < nvis; i += blockDim.x) idx[i] = i;
+    return;
+  }
+  // scores: A = this query's 4 heads (slot 0), B = 32 keys; wave w takes tiles w, w + 16, ...
+  const int kb = lane >> 5;
+  v8i av = {0, 0, 0, 0, 0, 0, 0, 0};
+  int asc = 127;
+  if (((lane & 31) >> 2) == 0) {
+    const int64_t qrow = row * 4 + (lane & 3);
+    uint4 u = *reinterpret_cast<const uint4*>(a.q_codes + qrow * 32 + kb * 16);
+    asc = fold_head_weight(u, (int)a.q_scales[qrow * 2 + kb], a.w[qrow]);  // w_h folded into the block scale
+    av[0] = (int)u.x; av[1] = (int)u.y; av[2] = (int)u.z; av[3] = (int)u.w;
+  }
+  constexpr int kIt = kSmallPool / 32 / 16;  // tiles per wave
+  const int ntiles = (nvis + 31) >> 5;
+  uint4 kcv[kIt];
+  int ksv[kIt];
+#pragma unroll
+  for (int it = 0; it < kIt; ++it) {  // every load of the wave first, then the MFMAs
+    const int j = (wave + 16 * it) * 32 + (lane & 31);
+    kcv[it] = make_uint4(0u, 0u, 0u, 0u);
+    ksv[it] = 127;
+    if (j < nvis) {
+      kcv[it] = *reinterpret_cast<const uint4*>(a.k_codes + (pbase + j) * 32 + kb * 16);
+      ksv[it] = a.k_scales[(pbase + j) * 2 + kb];
+    }
+  }
+  uint32_t mn = 0xffffffffu, mx = 0u;
+#pragma unroll
+  for (int it = 0; it < kIt; ++it) {
+    if (wave + 16 * it >= ntiles) break;  // uniform per wave
+    const v8i bv = {(int)kcv[it].x, (int)kcv[it].y, (int)kcv[it].z, (int)kcv[it].w, 0, 0, 0, 0};
+    v16f acc = {};
+    acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc, 4, 4, 0, asc, 0, ksv[it]);
+    const int j = (wave + 16 * it) * 32 + (lane & 31);
+    if (lane < 32 && j < nvis) {  // slot 0: lanes 0-31, score index 0
+      const float r0 = __int_as_float(max(__float_as_int(acc[0]), 0));
+      const float r1 = __int_as_float(max(__float_as_int(acc[1]), 0));
+      const float r2 = __int_as_float(max(__float_as_int(acc[2]), 0));
+      const float r3 = __int_as_float(max(__float_as_int(acc[3]), 0));
+      const uint32_t key = __float_as_uint((r0 + r1) + (r2 + r3));
+      keys_s[j] = key;
+      mn = key < mn ? key : mn;
+      mx = key > mx ? key : mx;
+    }
+  }
+  wave_minmax(mn, mx);
+  if (lane == 0) {
+    red[0][wave] = mn;
+    red[1][wave] = mx;
+  }
+  if (tid < kSmallPool / 32) bitmap[tid] = 0u;
+  if (tid == 0) n_eq = 0u;
+  __syncthreads();
+  uint32_t lo = 0xffffffffu, hi = 0u;
+  for (int wv = 0; wv < 16; ++wv) {
+    lo = red[0][wv] < lo ? red[0][wv] : lo;
+    hi = red[1][wv] > hi ? red[1][wv] : hi;
+  }
+  // every key lies in [lo, hi], so the bits above the highest one in which lo
+  // and hi differ are common to all of them
+  const int top = lo == hi ? 0 : 32 - __clz((int)(lo ^ hi));
+  const uint32_t fixed = top >= 32 ? 0u : (lo & ~((1u << top) - 1u));
+  uint32_t r;
+  const uint32_t kstar = radix_select_desc_low(
+      (uint32_t)nvis, (uint32_t)k_eff, top, fixed, [&](uint32_t i) { return keys_s[i]; },
+      [&](uint32_t) { return true; }, &r, bins, scratch);
+  {
+    uint32_t e = 0;
+    for (int i = tid; i < nvis; i += blockDim.x) e += keys_s[i] == kstar ? 1u : 0u;
+    if (e) atomicAdd(&n_eq, e);
+  }
+  __syncthreads();
+  // r of the entries equal to K* are taken: all of them, or the r lowest indices
+  uint32_t jstar = 0;
+  if (n_eq > r) {
+    const int ibits = 32 - __clz(nvis - 1);  // nvis >= 2 here
+    uint32_t r2;
+    jstar = radix_select_desc_low(
+        (uint32_t)nvis, r, ibits, ~0u << ibits, [&](uint32_t i) { return ~i; },
+        [&](uint32_t i) { return keys_s[i] == kstar; }, &r2, bins, scratch);
+  }
+  for (int i = tid; i < nvis; i += blockDim.x) {
+    const uint32_t key = keys_s[i];
+    if (key > kstar || (key == kstar && ~(uint32_t)i >= jstar)) atomicOr(&bitmap[i >> 5], 1u << (i & 31));
+  }
+  __syncthreads();
+  bitmap_emit_ascending(bitmap, (nvis + 31) >> 5, scratch, [&](uint32_t pos, int32_t j) { idx[pos] = j; });
+}
+
 // the decode-batch chain: scoring (FP4, or bf16 when q_bf16 is set), threshold,
 // selection, final
 static int decode_topk(int n_seq, int64_t n_q, int64_t max_q_per_seq, const int64_t* q_off, const int64_t* q_pos,
@@ -518,6 +648,11 @@ static int decode_topk(int n_seq, int64_t n_q, int64_t max_q_per_seq, const int6
   uint2* cand = (uint2*)take((size_t)n_q * max_pool * 8);
   if (n_q == 0) return 0;
 
+  if (!q_bf16 && max_pool <= kSmallPool) {  // short caches: one workgroup per query, one launch
+    SmallArgs sm{q_off, q_pos, pool_off, n_seq, m, k, q_codes, q_scales, w, k_codes, k_scales, idx};
+    const hipError_t e = launch(2, kProfBoth, k_idx_small, dim3((unsigned)n_q), dim3(1024), 0, stream, sm);
+    return e == hipSuccess && hipGetLastError() == hipSuccess ? 0 : -1;
+  }
   const int qt = max_q_per_seq > 1 ? 8 : 1;
   const int tiles_per_seq = (int)((max_q_per_seq + qt - 1) / qt);
   dim3 g1((unsigned)((max_pool + kScoreChunk - 1) / kScoreChunk), (unsigned)(n_seq * tiles_per_seq));
