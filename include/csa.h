@@ -452,7 +452,8 @@ int csa_hca_decode_fallbacks(const void* ws, void* stream, uint32_t* rows);
  * two kernels, from the first one's start to the second one's end).
  * start/stop are hipEvent_t handles owned by the caller; pass NULL, NULL to
  * clear.  Kernel ids: CSA_K_IDX_SCORE (indexer scoring), CSA_K_IDX_SELECT,
- * CSA_K_IDX_FINAL (top-k passes of decode batches), CSA_K_ATTN (attention
+ * CSA_K_IDX_FINAL (top-k passes of decode batches; for caches of at most
+ * 4096 pooled entries per sequence the one-launch top-k), CSA_K_ATTN (attention
  * main kernel, CSA or HCA), CSA_K_ATTN_COMBINE (split merge), CSA_K_COMPRESS,
  * CSA_K_FUSED, CSA_K_PF_THRESH and CSA_K_PF_SELECT (threshold and selection
  * kernels of prefill batches; their scoring kernel is CSA_K_IDX_SCORE),
