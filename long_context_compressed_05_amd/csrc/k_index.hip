@@ -503,7 +503,7 @@ size_t index_ws_bytes(int64_t n_q, int64_t max_q_per_seq, int64_t max_pool, int 
 
 // A query whose sequence has at most kSmallPool pooled entries (a short
 // decode cache) is selected by one workgroup in one launch: its visible keys
-// are scored into LDS (16 waves, 32-key MFMA tiles), K* is found by a radix
+// are scored into LDS (4 waves, 32-key MFMA tiles), K* is found by a radix
 // select over the keys' own range (the bits above it are common to every key),
 // ties at K* are cut at the lowest indices (a second select over the
 // complemented indices, only when some are left out), and the chosen entries
@@ -524,12 +524,13 @@ struct SmallArgs {
   int32_t* idx;
 };
 
-__global__ __launch_bounds__(1024) void k_idx_small(SmallArgs a) {
+constexpr int kSmallWaves = 4;
+__global__ __launch_bounds__(64 * kSmallWaves) void k_idx_small(SmallArgs a) {
   __shared__ uint32_t keys_s[kSmallPool];
   __shared__ uint32_t bins[1024];
   __shared__ uint32_t bitmap[kSmallPool / 32];
   __shared__ uint32_t scratch[32];
-  __shared__ uint32_t red[2][16];
+  __shared__ uint32_t red[2][kSmallWaves];
   __shared__ uint32_t n_eq;
   const int64_t row = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -544,7 +545,8 @@ __global__ __launch_bounds__(1024) void k_idx_small(SmallArgs a) {
     for (int i = tid; i < nvis; i += blockDim.x) idx[i] = i;
     return;
   }
-  // scores: A = this query's 4 heads (slot 0), B = 32 keys; wave w takes tiles w, w + 16, ...
+  // scores: A = this query's 4 heads (slot 0), B = 32 keys; wave w takes tiles
+  // w, w + kSmallWaves, ..., in batches of 8 whose loads all go out first
   const int kb = lane >> 5;
   v8i av = {0, 0, 0, 0, 0, 0, 0, 0};
   int asc = 127;
@@ -554,37 +556,40 @@ __global__ __launch_bounds__(1024) void k_idx_small(SmallArgs a) {
     asc = fold_head_weight(u, (int)a.q_scales[qrow * 2 + kb], a.w[qrow]);  // w_h folded into the block scale
     av[0] = (int)u.x; av[1] = (int)u.y; av[2] = (int)u.z; av[3] = (int)u.w;
   }
-  constexpr int kIt = kSmallPool / 32 / 16;  // tiles per wave
+  constexpr int kB = 8;  // tiles per wave in flight
   const int ntiles = (nvis + 31) >> 5;
-  uint4 kcv[kIt];
-  int ksv[kIt];
-#pragma unroll
-  for (int it = 0; it < kIt; ++it) {  // every load of the wave first, then the MFMAs
-    const int j = (wave + 16 * it) * 32 + (lane & 31);
-    kcv[it] = make_uint4(0u, 0u, 0u, 0u);
-    ksv[it] = 127;
-    if (j < nvis) {
-      kcv[it] = *reinterpret_cast<const uint4*>(a.k_codes + (pbase + j) * 32 + kb * 16);
-      ksv[it] = a.k_scales[(pbase + j) * 2 + kb];
-    }
-  }
   uint32_t mn = 0xffffffffu, mx = 0u;
+  for (int t0 = wave; t0 < ntiles; t0 += kSmallWaves * kB) {
+    uint4 kcv[kB];
+    int ksv[kB];
 #pragma unroll
-  for (int it = 0; it < kIt; ++it) {
-    if (wave + 16 * it >= ntiles) break;  // uniform per wave
-    const v8i bv = {(int)kcv[it].x, (int)kcv[it].y, (int)kcv[it].z, (int)kcv[it].w, 0, 0, 0, 0};
-    v16f acc = {};
-    acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc, 4, 4, 0, asc, 0, ksv[it]);
-    const int j = (wave + 16 * it) * 32 + (lane & 31);
-    if (lane < 32 && j < nvis) {  // slot 0: lanes 0-31, score index 0
-      const float r0 = __int_as_float(max(__float_as_int(acc[0]), 0));
-      const float r1 = __int_as_float(max(__float_as_int(acc[1]), 0));
-      const float r2 = __int_as_float(max(__float_as_int(acc[2]), 0));
-      const float r3 = __int_as_float(max(__float_as_int(acc[3]), 0));
-      const uint32_t key = __float_as_uint((r0 + r1) + (r2 + r3));
-      keys_s[j] = key;
-      mn = key < mn ? key : mn;
-      mx = key > mx ? key : mx;
+    for (int it = 0; it < kB; ++it) {
+      const int j = (t0 + kSmallWaves * it) * 32 + (lane & 31);
+      kcv[it] = make_uint4(0u, 0u, 0u, 0u);
+      ksv[it] = 127;
+      if (j < nvis) {
+        kcv[it] = *reinterpret_cast<const uint4*>(a.k_codes + (pbase + j) * 32 + kb * 16);
+        ksv[it] = a.k_scales[(pbase + j) * 2 + kb];
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < kB; ++it) {
+      const int tile = t0 + kSmallWaves * it;
+      if (tile >= ntiles) break;  // uniform per wave
+      const v8i bv = {(int)kcv[it].x, (int)kcv[it].y, (int)kcv[it].z, (int)kcv[it].w, 0, 0, 0, 0};
+      v16f acc = {};
+      acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc, 4, 4, 0, asc, 0, ksv[it]);
+      const int j = tile * 32 + (lane & 31);
+      if (lane < 32 && j < nvis) {  // slot 0: lanes 0-31, score index 0
+        const float r0 = __int_as_float(max(__float_as_int(acc[0]), 0));
+        const float r1 = __int_as_float(max(__float_as_int(acc[1]), 0));
+        const float r2 = __int_as_float(max(__float_as_int(acc[2]), 0));
+        const float r3 = __int_as_float(max(__float_as_int(acc[3]), 0));
+        const uint32_t key = __float_as_uint((r0 + r1) + (r2 + r3));
+        keys_s[j] = key;
+        mn = key < mn ? key : mn;
+        mx = key > mx ? key : mx;
+      }
     }
   }
   wave_minmax(mn, mx);
@@ -592,11 +597,11 @@ __global__ __launch_bounds__(1024) void k_idx_small(SmallArgs a) {
     red[0][wave] = mn;
     red[1][wave] = mx;
   }
-  if (tid < kSmallPool / 32) bitmap[tid] = 0u;
+  for (int i = tid; i < kSmallPool / 32; i += blockDim.x) bitmap[i] = 0u;
   if (tid == 0) n_eq = 0u;
   __syncthreads();
   uint32_t lo = 0xffffffffu, hi = 0u;
-  for (int wv = 0; wv < 16; ++wv) {
+  for (int wv = 0; wv < kSmallWaves; ++wv) {
     lo = red[0][wv] < lo ? red[0][wv] : lo;
     hi = red[1][wv] > hi ? red[1][wv] : hi;
   }
@@ -650,7 +655,7 @@ static int decode_topk(int n_seq, int64_t n_q, int64_t max_q_per_seq, const int6
 
   if (!q_bf16 && max_pool <= kSmallPool) {  // short caches: one workgroup per query, one launch
     SmallArgs sm{q_off, q_pos, pool_off, n_seq, m, k, q_codes, q_scales, w, k_codes, k_scales, idx};
-    const hipError_t e = launch(2, kProfBoth, k_idx_small, dim3((unsigned)n_q), dim3(1024), 0, stream, sm);
+    const hipError_t e = launch(2, kProfBoth, k_idx_small, dim3((unsigned)n_q), dim3(64 * kSmallWaves), 0, stream, sm);
     return e == hipSuccess && hipGetLastError() == hipSuccess ? 0 : -1;
   }
   const int qt = max_q_per_seq > 1 ? 8 : 1;
