@@ -29,6 +29,8 @@
 //      indices among entries equal to K*, then the ascending index order
 //      (an LDS bitmap of the visible range, or a bitonic sort when the range
 //      is too large for LDS).  It also returns the workspace to all-zero.
+// Batches whose sequences have at most kSmallPool pooled entries take one
+// launch instead (k_idx_small, below).
 #include "common.hpp"
 #include "kernels.hpp"
 #include "select_core.hpp"
